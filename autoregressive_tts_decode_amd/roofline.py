@@ -1,0 +1,89 @@
+"""Bytes-per-frame and bandwidth-bound arithmetic for the frame decode.
+
+The pages' own cost model ("Running Qwen3-TTS on an AMD R9700", section
+"Running Qwen3-TTS"): if the decode is bound by memory bandwidth, the time
+per frame is the bytes read per frame -- one Talker pass plus 15
+CodePredictor passes -- divided by the bandwidth; with fp16 sizes 3.483 GB
+and 0.350 GB that is 8.733 GB per frame, i.e. 73.3 frames/s at 640 GB/s.
+
+``pages_crude_bytes_per_frame`` is that formula. ``algorithmic_bytes`` is the
+refined count used for the roofline fraction: only the weights a frame
+actually streams (all Talker layers + the semantic head; per CodePredictor
+step all its layers, one acoustic head and the input projection; the gathered
+embedding rows) plus the KV-cache bytes attention reads. Embedding tables are
+not streamed whole and the 14 idle heads of a step are not read.
+"""
+from __future__ import annotations
+
+from .config import ModelCfg, StackCfg, FRAME_RATE_HZ
+
+HBM_PEAK_BYTES_PER_S = 8.0e12  # MI355X published HBM3E bandwidth
+
+
+def pages_crude_bytes_per_frame(talker_bytes: float, cp_bytes: float, cp_passes: int = 15) -> float:
+    return talker_bytes + cp_passes * cp_bytes
+
+
+def bound_fps(bytes_per_frame: float, bandwidth_bytes_per_s: float) -> float:
+    return bandwidth_bytes_per_s / bytes_per_frame
+
+
+def rtf_from_fps(fps: float) -> float:
+    """Real-time factor = compute time / audio time = 12.5 / fps."""
+    return FRAME_RATE_HZ / fps
+
+
+def _wbytes(cfg: ModelCfg) -> int:
+    return 2 if cfg.weight_dtype == "bf16" else 4
+
+
+def layer_weight_elems(s: StackCfg) -> int:
+    qd, kd = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
+    proj = s.hidden * (qd + 2 * kd) + qd * s.hidden + 3 * s.hidden * s.ffn
+    norms = 2 * s.hidden + 2 * s.head_dim
+    return proj + norms
+
+
+def kv_bytes_per_position(s: StackCfg, kv_elem_bytes: int) -> int:
+    """K and V bytes of one position in one layer."""
+    return 2 * s.n_kv_heads * s.head_dim * kv_elem_bytes
+
+
+def algorithmic_bytes(cfg: ModelCfg, talker_positions_read: float, batch: int = 1) -> dict:
+    """Algorithmic bytes of one frame (per stream batch of ``batch`` lockstep streams).
+
+    talker_positions_read: number of cached positions the Talker's attention
+    reads in this frame (p + 1 at Talker position p). Weights are shared by
+    the batch; embeddings, KV reads scale with it.
+    """
+    t, c = cfg.talker, cfg.codepred
+    b = _wbytes(cfg)
+    kvb = b  # the cache is stored in the weight dtype
+    talker_w = (t.n_layers * layer_weight_elems(t) + t.hidden + t.vocab * t.hidden) * b
+    emb_rows = batch * (1 + cfg.n_acoustic) * t.hidden * b
+    cp_step_w = (c.n_layers * layer_weight_elems(c) + c.hidden + c.vocab * c.hidden) * b
+    if t.hidden != c.hidden:
+        cp_step_w += c.hidden * t.hidden * b
+    cp_rows = batch * (1 + cfg.n_acoustic) * t.hidden * b  # E_sem row + 14 acoustic rows (+h_T) fed to the CodePredictor
+    kv_t = batch * t.n_layers * kv_bytes_per_position(t, kvb) * talker_positions_read
+    # CodePredictor attention over positions 0..j for its 16 positions (0..15).
+    cp_positions = sum(j + 1 for j in range(cfg.n_acoustic + 1))
+    kv_c = batch * c.n_layers * kv_bytes_per_position(c, kvb) * cp_positions
+    weights = talker_w + cfg.n_acoustic * cp_step_w
+    total = weights + emb_rows + cp_rows + kv_t + kv_c
+    return {"talker_weights": talker_w, "cp_step_weights": cp_step_w, "weights": weights,
+            "embedding_rows": emb_rows + cp_rows, "kv_talker": kv_t, "kv_cp": kv_c, "total": total}
+
+
+def frame_bytes_for_run(cfg: ModelCfg, prefill_len: int, first_frame: int, n_frames: int, batch: int = 1) -> float:
+    """Total algorithmic bytes of frames [first_frame, first_frame + n_frames).
+
+    Frame t (t >= 0) samples its semantic token from the pending Talker
+    output, runs the 15 CodePredictor steps and then the Talker step that
+    consumes its codes at position prefill_len + t (reading prefill_len + t + 1
+    cached positions).
+    """
+    tot = 0.0
+    for t in range(first_frame, first_frame + n_frames):
+        tot += algorithmic_bytes(cfg, prefill_len + t + 1, batch)["total"]
+    return tot

@@ -1,0 +1,872 @@
+// Host side of the C ABI in include/tts.h: validation, weight binding,
+// workspace layout, launch sequences of the Talker step / CodePredictor frame
+// / samplers, and the captured per-frame HIP graph.
+//
+// Per frame ("Running Qwen3-TTS on an AMD R9700", section "Running
+// Qwen3-TTS"): the Talker runs once and emits the semantic token, then the
+// CodePredictor runs 15 sequential steps for acoustic tokens 1..15. Here a
+// replayed frame is: draw the semantic token from the pending Talker output,
+// run the 15 CodePredictor steps, write the 16 codes, run the Talker step that
+// consumes them (which leaves the next frame's Talker output pending).
+#include "tts.h"
+#include "tts_device.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+using namespace tts;
+
+namespace {
+
+constexpr int kCpPositions = 16;   // CodePredictor positions 0..15 per frame
+constexpr int kAttnChunk = 64;     // Talker positions per attention split
+constexpr int kMaxGemvM = 8;       // input rows per GEMV launch
+constexpr size_t kGemvLds = 48 * 1024;
+
+struct Layer {
+  const void *attn_norm = nullptr, *wq = nullptr, *wk = nullptr, *wv = nullptr, *q_norm = nullptr, *k_norm = nullptr;
+  const void *wo = nullptr, *mlp_norm = nullptr, *wg = nullptr, *wu = nullptr, *wd = nullptr;
+};
+
+struct StackW {
+  tts_stack_cfg c;
+  std::vector<Layer> layers;
+  const void* final_norm = nullptr;
+};
+
+struct GraphKey {
+  tts_sampling sem, ac;
+  const float* u;
+  int32_t* codes;
+  int batch;
+  bool operator==(const GraphKey& o) const {
+    return std::memcmp(&sem, &o.sem, sizeof sem) == 0 && std::memcmp(&ac, &o.ac, sizeof ac) == 0 && u == o.u &&
+           codes == o.codes && batch == o.batch;
+  }
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace layout, computed identically by tts_workspace_bytes and tts_create.
+struct Layout {
+  size_t st, tk, tv, ck, cv, tcos, tsin, ccos, csin, x, qkv, attn, h, part, logits, hT, cx, clog, next_tok, sem_tok,
+      ac_codes, history, total;
+  int nsplit;
+};
+
+size_t elem_bytes(const tts_config& c) { return c.weight_dtype == TTS_DTYPE_BF16 ? 2 : 4; }
+size_t kv_bytes(const tts_config& c) { return c.kv_dtype == TTS_DTYPE_BF16 ? 2 : 4; }
+
+Layout make_layout(const tts_config& c) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  const auto &t = c.talker, &p = c.codepred;
+  const size_t B = c.max_batch, eb = kv_bytes(c);
+  const size_t cap = c.max_cache_steps;
+  L.nsplit = (int)((cap + kAttnChunk - 1) / kAttnChunk);
+  L.st = take(sizeof(DevState));
+  L.tk = take((size_t)t.n_layers * B * t.n_kv_heads * cap * t.head_dim * eb);
+  L.tv = take((size_t)t.n_layers * B * t.n_kv_heads * cap * t.head_dim * eb);
+  L.ck = take((size_t)p.n_layers * B * p.n_kv_heads * kCpPositions * p.head_dim * eb);
+  L.cv = take((size_t)p.n_layers * B * p.n_kv_heads * kCpPositions * p.head_dim * eb);
+  L.tcos = take(cap * (t.head_dim / 2) * 4);
+  L.tsin = take(cap * (t.head_dim / 2) * 4);
+  L.ccos = take(kCpPositions * (p.head_dim / 2) * 4);
+  L.csin = take(kCpPositions * (p.head_dim / 2) * 4);
+  const size_t rows = 2 * B;  // CodePredictor step 1 runs two positions per stream
+  const size_t hmax = std::max(t.hidden, p.hidden);
+  const size_t qkv_t = (size_t)(t.n_q_heads + 2 * t.n_kv_heads) * t.head_dim;
+  const size_t qkv_c = (size_t)(p.n_q_heads + 2 * p.n_kv_heads) * p.head_dim;
+  L.x = take(B * t.hidden * 4);
+  L.qkv = take(rows * std::max(qkv_t, qkv_c) * 4);
+  L.attn = take(rows * std::max((size_t)t.n_q_heads * t.head_dim, (size_t)p.n_q_heads * p.head_dim) * 4);
+  L.h = take(rows * std::max(t.ffn, p.ffn) * 4);
+  L.part = take(B * t.n_q_heads * (size_t)L.nsplit * (t.head_dim + 2) * 4);
+  L.logits = take(B * t.vocab * 4);
+  L.hT = take(B * t.hidden * 4);
+  L.cx = take(rows * hmax * 4);
+  L.clog = take(B * p.vocab * 4);
+  L.next_tok = take(B * 4);
+  L.sem_tok = take(B * 4);
+  L.ac_codes = take(B * c.n_acoustic * 4);
+  L.history = take(B * t.vocab);
+  L.total = off;
+  return L;
+}
+
+bool units_ok(int K, int E, int* U) {
+  if (K <= 0 || K % (64 * E)) return false;
+  const int u = K / (64 * E);
+  if (!(u == 1 || u == 2 || u == 3 || u == 4 || u == 6 || u == 8 || u == 12 || u == 16)) return false;
+  if (U) *U = u;
+  return true;
+}
+
+// Returns an error text or "" when the config is one the kernels accept.
+std::string check_config(const tts_config* c) {
+  if (!c) return "config is NULL";
+  if (c->weight_dtype != TTS_DTYPE_F32 && c->weight_dtype != TTS_DTYPE_BF16) return "weight_dtype must be TTS_DTYPE_F32 or TTS_DTYPE_BF16";
+  if (c->kv_dtype != TTS_DTYPE_F32 && c->kv_dtype != TTS_DTYPE_BF16) return "kv_dtype must be TTS_DTYPE_F32 or TTS_DTYPE_BF16";
+  if (c->n_acoustic != 15) return "n_acoustic must be 15";
+  if (c->max_batch < 1 || c->max_batch > 64) return "max_batch must be in [1, 64]";
+  if (c->max_cache_steps < 2 || c->max_cache_steps > 65536) return "max_cache_steps must be in [2, 65536]";
+  if (c->max_frames < 1) return "max_frames must be >= 1";
+  if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) return "rms_eps must be > 0 and rope_theta > 1";
+  if (c->text_vocab < 1) return "text_vocab must be >= 1";
+  const int E = c->weight_dtype == TTS_DTYPE_BF16 ? 8 : 4;
+  const tts_stack_cfg* ss[2] = {&c->talker, &c->codepred};
+  for (int i = 0; i < 2; ++i) {
+    const tts_stack_cfg& s = *ss[i];
+    const char* nm = i ? "codepred" : "talker";
+    char buf[256];
+    if (s.n_layers < 1 || s.vocab < 1 || s.n_q_heads < 1 || s.n_kv_heads < 1) {
+      snprintf(buf, sizeof buf, "%s: n_layers, vocab and head counts must be >= 1", nm);
+      return buf;
+    }
+    if (s.head_dim != 64 && s.head_dim != 128) { snprintf(buf, sizeof buf, "%s: head_dim must be 64 or 128", nm); return buf; }
+    if (s.n_q_heads % s.n_kv_heads) { snprintf(buf, sizeof buf, "%s: n_q_heads must be a multiple of n_kv_heads", nm); return buf; }
+    const int G = s.n_q_heads / s.n_kv_heads;
+    if (G != 1 && G != 2 && G != 4) { snprintf(buf, sizeof buf, "%s: n_q_heads / n_kv_heads must be 1, 2 or 4", nm); return buf; }
+    const int ks[3] = {s.hidden, s.n_q_heads * s.head_dim, s.ffn};
+    for (int k : ks)
+      if (!units_ok(k, E, nullptr)) {
+        snprintf(buf, sizeof buf, "%s: hidden, n_q_heads*head_dim and ffn must be %d x {1,2,3,4,6,8,12,16} (got %d)", nm, 64 * E, k);
+        return buf;
+      }
+  }
+  return "";
+}
+
+}  // namespace
+
+struct tts_ctx {
+  tts_config cfg{};
+  hipStream_t stream = nullptr;
+  char* ws = nullptr;
+  Layout L{};
+  int device = 0;
+  // workspace views
+  DevState* st = nullptr;
+  float *x = nullptr, *qkv = nullptr, *attn = nullptr, *h = nullptr, *part = nullptr, *logits = nullptr, *hT = nullptr;
+  float *cx = nullptr, *clog = nullptr;
+  float *tcos = nullptr, *tsin = nullptr, *ccos = nullptr, *csin = nullptr;
+  int32_t *next_tok = nullptr, *sem_tok = nullptr, *ac_codes = nullptr;
+  uint8_t* history = nullptr;
+  // weights
+  StackW talker, cp;
+  const void *embed_text = nullptr, *embed_sem = nullptr, *lm_head = nullptr, *proj = nullptr, *embed_ac = nullptr,
+             *heads = nullptr;
+  bool weights_ok = false;
+  // host mirror of the device counters
+  bool prefilled = false;
+  int batch = 0, pos = 0, frames = 0;
+  // captured frame graph
+  bool have_graph = false;
+  GraphKey gkey{};
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t gexec = nullptr;
+  hipStream_t cap_stream = nullptr;  // private stream used only to record the frame graph
+  std::string err;
+
+  int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    err = buf;
+    return code;
+  }
+  bool bf16() const { return cfg.weight_dtype == TTS_DTYPE_BF16; }
+  bool kv_bf16() const { return cfg.kv_dtype == TTS_DTYPE_BF16; }
+  size_t eb() const { return elem_bytes(cfg); }
+  size_t kvb() const { return kv_bytes(cfg); }
+};
+
+#define HIP_TRY(call)                                                                          \
+  do {                                                                                         \
+    hipError_t e_ = (call);                                                                    \
+    if (e_ != hipSuccess) return ctx->fail(TTS_E_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+#define HIP_LAUNCH_CHECK()                                                                          \
+  do {                                                                                              \
+    hipError_t e_ = hipGetLastError();                                                              \
+    if (e_ != hipSuccess) return ctx->fail(TTS_E_HIP, "kernel launch: %s", hipGetErrorString(e_)); \
+  } while (0)
+
+namespace {
+
+// ---------------------------------------------------------------------------- GEMV dispatch
+
+template <typename WT, int U, int M, bool PAIR>
+int launch_gemv_t(tts_ctx* ctx, const GemvArgs& a) {
+  // only instantiate row counts whose staged input fits the LDS budget
+  if constexpr ((size_t)M * U * 64 * WTraits<WT>::E * 4 > kGemvLds) {
+    return ctx->fail(TTS_E_UNSUPPORTED, "gemv: M=%d with K=%d exceeds the LDS budget", M, a.K);
+  } else {
+  constexpr int RW = GemvShape<U, PAIR>::RW;
+  const int rows_per_block = 4 * RW;
+  const int blocks = (a.N + rows_per_block - 1) / rows_per_block;
+  const size_t lds = (size_t)M * a.K * 4;
+  hipLaunchKernelGGL((k_gemv<WT, U, M, PAIR>), dim3(blocks), dim3(256), lds, ctx->stream, a);
+  HIP_LAUNCH_CHECK();
+  return TTS_OK;
+  }
+}
+
+template <typename WT, int U, bool PAIR>
+int launch_gemv_m(tts_ctx* ctx, const GemvArgs& a) {
+  switch (a.M) {
+    case 1: return launch_gemv_t<WT, U, 1, PAIR>(ctx, a);
+    case 2: return launch_gemv_t<WT, U, 2, PAIR>(ctx, a);
+    case 4: return launch_gemv_t<WT, U, 4, PAIR>(ctx, a);
+    case 8: return launch_gemv_t<WT, U, 8, PAIR>(ctx, a);
+    default: return ctx->fail(TTS_E_UNSUPPORTED, "gemv: M=%d", a.M);
+  }
+}
+
+template <typename WT, bool PAIR>
+int launch_gemv_u(tts_ctx* ctx, const GemvArgs& a) {
+  int U = 0;
+  if (!units_ok(a.K, WTraits<WT>::E, &U)) return ctx->fail(TTS_E_SHAPE, "gemv: K=%d", a.K);
+  switch (U) {
+    case 1: return launch_gemv_m<WT, 1, PAIR>(ctx, a);
+    case 2: return launch_gemv_m<WT, 2, PAIR>(ctx, a);
+    case 3: return launch_gemv_m<WT, 3, PAIR>(ctx, a);
+    case 4: return launch_gemv_m<WT, 4, PAIR>(ctx, a);
+    case 6: return launch_gemv_m<WT, 6, PAIR>(ctx, a);
+    case 8: return launch_gemv_m<WT, 8, PAIR>(ctx, a);
+    case 12: return launch_gemv_m<WT, 12, PAIR>(ctx, a);
+    case 16: return launch_gemv_m<WT, 16, PAIR>(ctx, a);
+  }
+  return ctx->fail(TTS_E_SHAPE, "gemv: K=%d", a.K);
+}
+
+// Launch a GEMV over M input rows, chunked so that each launch stages at most
+// kMaxGemvM rows and 64 KB of input in LDS. Chunks re-stream the weights.
+int gemv(tts_ctx* ctx, GemvArgs a) {
+  const int Mtot = a.M;
+  int chunk = kMaxGemvM;
+  while (chunk > 1 && (size_t)chunk * a.K * 4 > kGemvLds) chunk >>= 1;
+  if (a.src == SRC_VEC_THEN_TABLE && chunk < 2) return ctx->fail(TTS_E_SHAPE, "gemv: K=%d too large for paired rows", a.K);
+  for (int m0 = 0; m0 < Mtot;) {
+    int mc = std::min(chunk, Mtot - m0);
+    while (mc & (mc - 1)) mc &= mc - 1;  // power of two rows per launch
+    GemvArgs c = a;
+    c.M = mc;
+    if (a.src == SRC_VEC_THEN_TABLE) {
+      c.x = a.x + (size_t)(m0 / 2) * a.x_stride;
+      c.tok.offset = a.tok.offset + (m0 / 2) * a.tok.b_stride;
+    } else if (a.src == SRC_TABLE) {
+      c.tok.offset = a.tok.offset + m0 * a.tok.b_stride;
+    } else {
+      c.x = a.x + (size_t)m0 * a.x_stride;
+    }
+    c.y = a.y + (size_t)m0 * a.y_stride;
+    if (a.res) c.res = a.res + (size_t)m0 * a.res_stride;
+    if (a.xn_out) c.xn_out = a.xn_out + (size_t)m0 * a.xn_stride;
+    int rc;
+    const bool pair = a.epi == EPI_SWIGLU;
+    if (ctx->bf16()) rc = pair ? launch_gemv_u<uint16_t, true>(ctx, c) : launch_gemv_u<uint16_t, false>(ctx, c);
+    else rc = pair ? launch_gemv_u<float, true>(ctx, c) : launch_gemv_u<float, false>(ctx, c);
+    if (rc) return rc;
+    m0 += mc;
+  }
+  return TTS_OK;
+}
+
+// ---------------------------------------------------------------------------- attention dispatch
+
+template <typename WT, typename KT, int G, int M, int D>
+int launch_attn_t(tts_ctx* ctx, const AttnArgs& a, int B) {
+  hipLaunchKernelGGL((k_attn<WT, KT, G, M, D>), dim3(a.nsplit, a.nkv, B), dim3(256), 0, ctx->stream, a);
+  HIP_LAUNCH_CHECK();
+  return TTS_OK;
+}
+
+template <typename WT, typename KT, int G, int M>
+int launch_attn_d(tts_ctx* ctx, const AttnArgs& a, int B) {
+  if (a.d == 64) return launch_attn_t<WT, KT, G, M, 64>(ctx, a, B);
+  if (a.d == 128) return launch_attn_t<WT, KT, G, M, 128>(ctx, a, B);
+  return ctx->fail(TTS_E_SHAPE, "attention: head_dim %d", a.d);
+}
+
+template <typename WT, typename KT, int G>
+int launch_attn_m(tts_ctx* ctx, const AttnArgs& a, int B) {
+  if (a.M == 1) return launch_attn_d<WT, KT, G, 1>(ctx, a, B);
+  if (a.M == 2) return launch_attn_d<WT, KT, G, 2>(ctx, a, B);
+  return ctx->fail(TTS_E_SHAPE, "attention: %d new positions", a.M);
+}
+
+template <typename WT, typename KT>
+int launch_attn_g(tts_ctx* ctx, const AttnArgs& a, int B) {
+  const int G = a.nq / a.nkv;
+  if (G == 1) return launch_attn_m<WT, KT, 1>(ctx, a, B);
+  if (G == 2) return launch_attn_m<WT, KT, 2>(ctx, a, B);
+  if (G == 4) return launch_attn_m<WT, KT, 4>(ctx, a, B);
+  return ctx->fail(TTS_E_SHAPE, "attention: %d query heads per KV head", G);
+}
+
+int attention(tts_ctx* ctx, const AttnArgs& a, int B) {
+  if (ctx->bf16()) return ctx->kv_bf16() ? launch_attn_g<uint16_t, uint16_t>(ctx, a, B) : launch_attn_g<uint16_t, float>(ctx, a, B);
+  return ctx->kv_bf16() ? launch_attn_g<float, uint16_t>(ctx, a, B) : launch_attn_g<float, float>(ctx, a, B);
+}
+
+// ---------------------------------------------------------------------------- building blocks
+
+TokRef tokref(const int32_t* base, int b_stride, int f_stride, int offset, int use_frame) {
+  TokRef r;
+  r.base = base; r.b_stride = b_stride; r.f_stride = f_stride; r.offset = offset; r.use_frame = use_frame;
+  return r;
+}
+URef uref(const float* base, int b_stride, int f_stride, int offset, int use_frame) {
+  URef r;
+  r.base = base; r.b_stride = b_stride; r.f_stride = f_stride; r.offset = offset; r.use_frame = use_frame;
+  return r;
+}
+
+GemvArgs gemv_args(tts_ctx* ctx) {
+  GemvArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.nseg = 1;
+  a.eps = ctx->cfg.rms_eps;
+  a.st = ctx->st;
+  return a;
+}
+
+// One pass of a decoder stack over Mp new positions per stream (rows b*Mp+m
+// of x, hidden H). Position of row m: pos_const + m, or the device Talker
+// position when pos_from_state. KV caches [layers][B][nkv][cap][d].
+int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_const, int pos_from_state, void* kc,
+               void* vc, int cap, int nsplit, const float* rc, const float* rs, bool nontemporal) {
+  const tts_stack_cfg& c = S.c;
+  const int rows = B * Mp;
+  const int qd = c.n_q_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
+  const int qkv_n = qd + 2 * kd;
+  // per-layer cache stride uses the allocated stream capacity, not the live batch
+  const size_t layer_cache = (size_t)ctx->cfg.max_batch * c.n_kv_heads * cap * c.head_dim * ctx->kvb();
+  for (int l = 0; l < c.n_layers; ++l) {
+    const Layer& W = S.layers[l];
+    // RMSNorm + QKV
+    GemvArgs a = gemv_args(ctx);
+    a.w[0] = W.wq; a.w[1] = W.wk; a.w[2] = W.wv;
+    a.seg_rows[0] = qd; a.seg_rows[1] = kd; a.seg_rows[2] = kd;
+    a.nseg = 3; a.N = qkv_n; a.K = c.hidden; a.M = rows;
+    a.src = SRC_VEC; a.x = x; a.x_stride = c.hidden;
+    a.gain = W.attn_norm;
+    a.y = ctx->qkv; a.y_stride = qkv_n; a.epi = EPI_STORE; a.nontemporal = nontemporal;
+    if (int rc_ = gemv(ctx, a)) return rc_;
+    // q/k norm + RoPE + KV append + attention
+    AttnArgs t;
+    std::memset(&t, 0, sizeof t);
+    t.qkv = ctx->qkv; t.qkv_stride = qkv_n; t.M = Mp;
+    t.nq = c.n_q_heads; t.nkv = c.n_kv_heads; t.d = c.head_dim;
+    t.q_norm = W.q_norm; t.k_norm = W.k_norm; t.eps = ctx->cfg.rms_eps;
+    t.rope_cos = rc; t.rope_sin = rs;
+    t.pos_const = pos_const; t.pos_from_state = pos_from_state;
+    t.kc = (char*)kc + l * layer_cache; t.vc = (char*)vc + l * layer_cache;
+    t.cap = cap; t.chunk = nsplit == 1 ? cap : kAttnChunk; t.nsplit = nsplit;
+    t.out = ctx->attn; t.out_stride = qd; t.part = ctx->part; t.st = ctx->st;
+    if (int rc_ = attention(ctx, t, B)) return rc_;
+    if (nsplit > 1) {
+      MergeArgs mg;
+      mg.part = ctx->part; mg.nq = c.n_q_heads; mg.d = c.head_dim; mg.nsplit = nsplit; mg.chunk = kAttnChunk;
+      mg.M = Mp; mg.pos_const = pos_const; mg.pos_from_state = pos_from_state;
+      mg.out = ctx->attn; mg.out_stride = qd; mg.st = ctx->st;
+      hipLaunchKernelGGL(k_attn_merge, dim3(c.n_q_heads, rows), dim3(c.head_dim), 0, ctx->stream, mg);
+      HIP_LAUNCH_CHECK();
+    }
+    // O projection + residual
+    a = gemv_args(ctx);
+    a.w[0] = W.wo; a.seg_rows[0] = c.hidden; a.N = c.hidden; a.K = qd; a.M = rows;
+    a.src = SRC_VEC; a.x = ctx->attn; a.x_stride = qd;
+    a.y = x; a.y_stride = c.hidden; a.res = x; a.res_stride = c.hidden; a.epi = EPI_RESID; a.nontemporal = nontemporal;
+    if (int rc_ = gemv(ctx, a)) return rc_;
+    // RMSNorm + gate/up + SwiGLU
+    a = gemv_args(ctx);
+    a.w[0] = W.wg; a.w[1] = W.wu; a.seg_rows[0] = c.ffn; a.seg_rows[1] = c.ffn; a.nseg = 2;
+    a.N = c.ffn; a.K = c.hidden; a.M = rows;
+    a.src = SRC_VEC; a.x = x; a.x_stride = c.hidden; a.gain = W.mlp_norm;
+    a.y = ctx->h; a.y_stride = c.ffn; a.epi = EPI_SWIGLU; a.nontemporal = nontemporal;
+    if (int rc_ = gemv(ctx, a)) return rc_;
+    // down projection + residual
+    a = gemv_args(ctx);
+    a.w[0] = W.wd; a.seg_rows[0] = c.hidden; a.N = c.hidden; a.K = c.ffn; a.M = rows;
+    a.src = SRC_VEC; a.x = ctx->h; a.x_stride = c.ffn;
+    a.y = x; a.y_stride = c.hidden; a.res = x; a.res_stride = c.hidden; a.epi = EPI_RESID; a.nontemporal = nontemporal;
+    if (int rc_ = gemv(ctx, a)) return rc_;
+  }
+  return TTS_OK;
+}
+
+// Talker final norm + semantic head: logits = W_lm RMSNorm(x); the normed
+// hidden (h_T, which conditions the CodePredictor) is written as well.
+int talker_head(tts_ctx* ctx, int B) {
+  const auto& t = ctx->cfg.talker;
+  GemvArgs a = gemv_args(ctx);
+  a.w[0] = ctx->lm_head; a.seg_rows[0] = t.vocab; a.N = t.vocab; a.K = t.hidden; a.M = B;
+  a.src = SRC_VEC; a.x = ctx->x; a.x_stride = t.hidden; a.gain = ctx->talker.final_norm;
+  a.y = ctx->logits; a.y_stride = t.vocab; a.epi = EPI_STORE;
+  a.xn_out = ctx->hT; a.xn_stride = t.hidden; a.nontemporal = 1;
+  return gemv(ctx, a);
+}
+
+int talker_stack(tts_ctx* ctx, int B, int pos_const, int pos_from_state) {
+  const auto& c = ctx->cfg;
+  return stack_step(ctx, ctx->talker, ctx->x, B, 1, pos_const, pos_from_state, ctx->ws + ctx->L.tk, ctx->ws + ctx->L.tv,
+                    c.max_cache_steps, ctx->L.nsplit, ctx->tcos, ctx->tsin, true);
+}
+
+// Talker input from a frame's 16 codes (codebook t of stream b at tok refs).
+int embed_sum(tts_ctx* ctx, int B, const TokRef* refs) {
+  const auto& c = ctx->cfg;
+  EmbedArgs e;
+  std::memset(&e, 0, sizeof e);
+  e.ntab = 1 + c.n_acoustic;
+  e.H = c.talker.hidden;
+  const size_t ac_table = (size_t)c.codepred.vocab * c.talker.hidden * ctx->eb();
+  e.table[0] = ctx->embed_sem;
+  e.rows[0] = c.talker.vocab;
+  e.tok[0] = refs[0];
+  for (int j = 1; j <= c.n_acoustic; ++j) {
+    e.table[j] = (const char*)ctx->embed_ac + (j - 1) * ac_table;
+    e.rows[j] = c.codepred.vocab;
+    e.tok[j] = refs[j];
+  }
+  e.x = ctx->x; e.x_stride = c.talker.hidden; e.st = ctx->st;
+  const int gx = (c.talker.hidden + 255) / 256;
+  if (ctx->bf16()) hipLaunchKernelGGL(k_embed_sum<uint16_t>, dim3(gx, B), dim3(256), 0, ctx->stream, e);
+  else hipLaunchKernelGGL(k_embed_sum<float>, dim3(gx, B), dim3(256), 0, ctx->stream, e);
+  HIP_LAUNCH_CHECK();
+  return TTS_OK;
+}
+
+int gather(tts_ctx* ctx, int src, int M, int H, const float* vec, int vec_stride, const void* table, int table_rows, TokRef tok,
+           float* out, int out_stride) {
+  GatherArgs g;
+  std::memset(&g, 0, sizeof g);
+  g.src = src; g.M = M; g.H = H; g.vec = vec; g.vec_stride = vec_stride; g.table = table; g.table_rows = table_rows; g.tok = tok;
+  g.x = out; g.x_stride = out_stride; g.st = ctx->st;
+  const int gx = (H + 255) / 256;
+  if (ctx->bf16()) hipLaunchKernelGGL(k_gather<uint16_t>, dim3(gx, M), dim3(256), 0, ctx->stream, g);
+  else hipLaunchKernelGGL(k_gather<float>, dim3(gx, M), dim3(256), 0, ctx->stream, g);
+  HIP_LAUNCH_CHECK();
+  return TTS_OK;
+}
+
+int sample(tts_ctx* ctx, const float* logits, int l_stride, int B, int V, const tts_sampling& s, URef u, uint8_t* hist,
+           int h_stride, int mark, int32_t* out, int ob, int of, int oo, int ouf, int32_t* next, const int32_t* forced,
+           int fs, int fo) {
+  SampleArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.logits = logits; a.l_stride = l_stride; a.V = V;
+  a.do_sample = s.do_sample; a.top_k = s.top_k; a.top_p = s.top_p; a.temperature = s.temperature;
+  a.penalty = s.repetition_penalty;
+  a.u = u; a.history = hist; a.h_stride = h_stride; a.mark_history = mark;
+  a.out = out; a.out_b_stride = ob; a.out_f_stride = of; a.out_offset = oo; a.out_use_frame = ouf;
+  a.next = next; a.forced = forced; a.forced_stride = fs; a.forced_offset = fo; a.st = ctx->st;
+  hipLaunchKernelGGL(k_sample, dim3(B), dim3(256), 0, ctx->stream, a);
+  HIP_LAUNCH_CHECK();
+  return TTS_OK;
+}
+
+// The 15 CodePredictor steps. semantic: token ref of the semantic id per
+// stream. Acoustic token j of stream b goes to out (refs with offset j-1);
+// logits (optional) to logits_out + b*15*Va + (j-1)*Va. u: uniform refs with
+// offset of acoustic 1 (incremented per step). forced: [B][15] or nullptr.
+int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac, URef u, const int32_t* forced,
+                   int32_t* out, int ob, int of, int oo, int ouf, float* logits_out) {
+  const auto& c = ctx->cfg;
+  const int Hc = c.codepred.hidden, Ht = c.talker.hidden, Va = c.codepred.vocab;
+  const size_t ac_table = (size_t)Va * Ht * ctx->eb();
+  const size_t head_sz = (size_t)Va * Hc * ctx->eb();
+  void* kc = ctx->ws + ctx->L.ck;
+  void* vc = ctx->ws + ctx->L.cv;
+  for (int j = 1; j <= c.n_acoustic; ++j) {
+    const int Mp = (j == 1) ? 2 : 1;
+    // CodePredictor input rows
+    if (j == 1) {
+      if (ctx->proj) {
+        GemvArgs a = gemv_args(ctx);
+        a.w[0] = ctx->proj; a.seg_rows[0] = Hc; a.N = Hc; a.K = Ht; a.M = 2 * B;
+        a.src = SRC_VEC_THEN_TABLE; a.x = ctx->hT; a.x_stride = Ht; a.table = ctx->embed_sem; a.table_rows = c.talker.vocab;
+        a.tok = semantic;
+        a.y = ctx->cx; a.y_stride = Hc; a.epi = EPI_STORE;
+        if (int rc = gemv(ctx, a)) return rc;
+      } else if (int rc = gather(ctx, SRC_VEC_THEN_TABLE, 2 * B, Hc, ctx->hT, Ht, ctx->embed_sem, c.talker.vocab, semantic, ctx->cx,
+                                 Hc)) {
+        return rc;
+      }
+    } else {
+      const void* table = (const char*)ctx->embed_ac + (size_t)(j - 2) * ac_table;
+      TokRef prev = tokref(ctx->next_tok, 1, 0, 0, 0);
+      if (ctx->proj) {
+        GemvArgs a = gemv_args(ctx);
+        a.w[0] = ctx->proj; a.seg_rows[0] = Hc; a.N = Hc; a.K = Ht; a.M = B;
+        a.src = SRC_TABLE; a.table = table; a.table_rows = Va; a.tok = prev;
+        a.y = ctx->cx; a.y_stride = Hc; a.epi = EPI_STORE;
+        if (int rc = gemv(ctx, a)) return rc;
+      } else if (int rc = gather(ctx, SRC_TABLE, B, Hc, nullptr, 0, table, Va, prev, ctx->cx, Hc)) {
+        return rc;
+      }
+    }
+    if (int rc = stack_step(ctx, ctx->cp, ctx->cx, B, Mp, j == 1 ? 0 : j, 0, kc, vc, kCpPositions, 1, ctx->ccos, ctx->csin,
+                            false))
+      return rc;
+    // final norm + head j on the last position of each stream
+    GemvArgs a = gemv_args(ctx);
+    a.w[0] = (const char*)ctx->heads + (size_t)(j - 1) * head_sz; a.seg_rows[0] = Va; a.N = Va; a.K = Hc; a.M = B;
+    a.src = SRC_VEC; a.x = ctx->cx + (size_t)(Mp - 1) * Hc; a.x_stride = Mp * Hc; a.gain = ctx->cp.final_norm;
+    float* lg = logits_out ? logits_out + (size_t)(j - 1) * Va : ctx->clog;
+    a.y = lg; a.y_stride = logits_out ? c.n_acoustic * Va : Va; a.epi = EPI_STORE;
+    if (int rc = gemv(ctx, a)) return rc;
+    URef uj = u;
+    uj.offset += j - 1;
+    if (int rc = sample(ctx, lg, a.y_stride, B, Va, ac, uj, nullptr, 0, 0, out, ob, of, oo + j - 1, ouf, ctx->next_tok, forced,
+                        c.n_acoustic, j - 1))
+      return rc;
+  }
+  return TTS_OK;
+}
+
+void fill_rope(const tts_config& c, int d, int npos, std::vector<float>& cs, std::vector<float>& sn) {
+  const int half = d / 2;
+  cs.resize((size_t)npos * half);
+  sn.resize((size_t)npos * half);
+  for (int p = 0; p < npos; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double inv = std::pow((double)c.rope_theta, -2.0 * i / d);
+      const double ang = (double)p * inv;
+      cs[(size_t)p * half + i] = (float)std::cos(ang);
+      sn[(size_t)p * half + i] = (float)std::sin(ang);
+    }
+}
+
+int check_sampling(tts_ctx* ctx, const tts_sampling* s, int V, const char* what) {
+  if (!s) return ctx->fail(TTS_E_ARG, "%s sampling is NULL", what);
+  if (s->do_sample) {
+    if (!(s->temperature > 0.f)) return ctx->fail(TTS_E_ARG, "%s temperature must be > 0", what);
+    if (!(s->repetition_penalty > 0.f)) return ctx->fail(TTS_E_ARG, "%s repetition_penalty must be > 0", what);
+    if (!(s->top_p > 0.f)) return ctx->fail(TTS_E_ARG, "%s top_p must be > 0", what);
+    if (V > kSortMax) return ctx->fail(TTS_E_UNSUPPORTED, "%s: sampling supports vocab <= %d (got %d)", what, kSortMax, V);
+  }
+  return TTS_OK;
+}
+
+int enqueue_frame(tts_ctx* ctx, const tts_sampling& sem, const tts_sampling& ac, const float* u, int32_t* codes) {
+  const auto& c = ctx->cfg;
+  const int B = ctx->batch;
+  const int fs = c.max_frames * 16;
+  // greedy never reads u; keep its strides at zero then so no address depends on it
+  const int ub = u ? fs : 0, uf = u ? 16 : 0;
+  if (!u) u = ctx->hT;
+  // semantic token of frame t from the pending Talker logits
+  if (int rc = sample(ctx, ctx->logits, c.talker.vocab, B, c.talker.vocab, sem, uref(u, ub, uf, 0, 1), ctx->history,
+                      c.talker.vocab, 1, codes, fs, 16, 0, 1, ctx->sem_tok, nullptr, 0, 0))
+    return rc;
+  if (int rc = codepred_frame(ctx, B, tokref(ctx->sem_tok, 1, 0, 0, 0), ac, uref(u, ub, uf, u == ctx->hT ? 0 : 1, 1), nullptr, codes,
+                              fs, 16, 1, 1, nullptr))
+    return rc;
+  TokRef refs[16];
+  for (int j = 0; j < 16; ++j) refs[j] = tokref(codes, fs, 16, j, 1);
+  if (int rc = embed_sum(ctx, B, refs)) return rc;
+  if (int rc = talker_stack(ctx, B, 0, 1)) return rc;
+  if (int rc = talker_head(ctx, B)) return rc;
+  hipLaunchKernelGGL(k_bump, dim3(1), dim3(64), 0, ctx->stream, ctx->st, 1, 1);
+  HIP_LAUNCH_CHECK();
+  return TTS_OK;
+}
+
+void drop_graph(tts_ctx* ctx) {
+  if (ctx->gexec) (void)hipGraphExecDestroy(ctx->gexec);
+  if (ctx->graph) (void)hipGraphDestroy(ctx->graph);
+  ctx->gexec = nullptr;
+  ctx->graph = nullptr;
+  ctx->have_graph = false;
+}
+
+}  // namespace
+
+// ============================================================================ C ABI
+
+extern "C" {
+
+int tts_workspace_bytes(const tts_config* cfg, size_t* bytes) {
+  if (!bytes) return TTS_E_ARG;
+  std::string e = check_config(cfg);
+  if (!e.empty()) return cfg ? TTS_E_SHAPE : TTS_E_ARG;
+  *bytes = make_layout(*cfg).total;
+  return TTS_OK;
+}
+
+int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t workspace_bytes, tts_ctx** out) {
+  if (!out) return TTS_E_ARG;
+  *out = nullptr;
+  if (!cfg || !workspace) return TTS_E_ARG;
+  if (!check_config(cfg).empty()) return TTS_E_SHAPE;
+  if (((uintptr_t)workspace) & 255) return TTS_E_ARG;
+  Layout L = make_layout(*cfg);
+  if (workspace_bytes < L.total) return TTS_E_CAPACITY;
+  tts_ctx* ctx = new tts_ctx();
+  ctx->cfg = *cfg;
+  ctx->stream = (hipStream_t)hip_stream;
+  ctx->ws = (char*)workspace;
+  ctx->L = L;
+  if (hipGetDevice(&ctx->device) != hipSuccess) { delete ctx; return TTS_E_HIP; }
+  char* w = ctx->ws;
+  ctx->st = (DevState*)(w + L.st);
+  ctx->x = (float*)(w + L.x); ctx->qkv = (float*)(w + L.qkv); ctx->attn = (float*)(w + L.attn); ctx->h = (float*)(w + L.h);
+  ctx->part = (float*)(w + L.part); ctx->logits = (float*)(w + L.logits); ctx->hT = (float*)(w + L.hT);
+  ctx->cx = (float*)(w + L.cx); ctx->clog = (float*)(w + L.clog);
+  ctx->tcos = (float*)(w + L.tcos); ctx->tsin = (float*)(w + L.tsin); ctx->ccos = (float*)(w + L.ccos); ctx->csin = (float*)(w + L.csin);
+  ctx->next_tok = (int32_t*)(w + L.next_tok); ctx->sem_tok = (int32_t*)(w + L.sem_tok); ctx->ac_codes = (int32_t*)(w + L.ac_codes);
+  ctx->history = (uint8_t*)(w + L.history);
+  ctx->talker.c = cfg->talker;
+  ctx->cp.c = cfg->codepred;
+  // RoPE tables: angles p * theta^(-2i/d) in double, rounded to fp32.
+  std::vector<float> cs, sn;
+  fill_rope(*cfg, cfg->talker.head_dim, cfg->max_cache_steps, cs, sn);
+  hipError_t e1 = hipMemcpy(ctx->tcos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice);
+  hipError_t e2 = hipMemcpy(ctx->tsin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice);
+  fill_rope(*cfg, cfg->codepred.head_dim, kCpPositions, cs, sn);
+  hipError_t e3 = hipMemcpy(ctx->ccos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice);
+  hipError_t e4 = hipMemcpy(ctx->csin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice);
+  if (e1 || e2 || e3 || e4) { delete ctx; return TTS_E_HIP; }
+  hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, 0, 0);
+  if (hipGetLastError() != hipSuccess) { delete ctx; return TTS_E_HIP; }
+  *out = ctx;
+  return TTS_OK;
+}
+
+int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* const* dev_ptrs, const int64_t* shapes,
+                     const int32_t* ranks, const int32_t* dtypes) {
+  if (!ctx) return TTS_E_ARG;
+  if (n < 0 || !names || !dev_ptrs || !shapes || !ranks || !dtypes) return ctx->fail(TTS_E_ARG, "load_weights: NULL argument");
+  const tts_config& c = ctx->cfg;
+  struct Want { std::vector<int64_t> shape; const void** slot; };
+  std::unordered_map<std::string, Want> want;
+  StackW talker, cp;
+  talker.c = c.talker; cp.c = c.codepred;
+  talker.layers.resize(c.talker.n_layers);
+  cp.layers.resize(c.codepred.n_layers);
+  const void *embed_text = nullptr, *embed_sem = nullptr, *lm_head = nullptr, *proj = nullptr, *embed_ac = nullptr, *heads = nullptr;
+  auto add_stack = [&](const char* prefix, StackW& S) {
+    const tts_stack_cfg& s = S.c;
+    const int64_t H = s.hidden, qd = (int64_t)s.n_q_heads * s.head_dim, kd = (int64_t)s.n_kv_heads * s.head_dim;
+    for (int i = 0; i < s.n_layers; ++i) {
+      std::string p = std::string(prefix) + ".layers." + std::to_string(i) + ".";
+      Layer& L = S.layers[i];
+      want[p + "attn_norm"] = {{H}, &L.attn_norm};
+      want[p + "wq"] = {{qd, H}, &L.wq};
+      want[p + "wk"] = {{kd, H}, &L.wk};
+      want[p + "wv"] = {{kd, H}, &L.wv};
+      want[p + "q_norm"] = {{s.head_dim}, &L.q_norm};
+      want[p + "k_norm"] = {{s.head_dim}, &L.k_norm};
+      want[p + "wo"] = {{H, qd}, &L.wo};
+      want[p + "mlp_norm"] = {{H}, &L.mlp_norm};
+      want[p + "wg"] = {{s.ffn, H}, &L.wg};
+      want[p + "wu"] = {{s.ffn, H}, &L.wu};
+      want[p + "wd"] = {{H, s.ffn}, &L.wd};
+    }
+    want[std::string(prefix) + ".final_norm"] = {{H}, &S.final_norm};
+  };
+  add_stack("talker", talker);
+  add_stack("cp", cp);
+  const int64_t Ht = c.talker.hidden, Hc = c.codepred.hidden;
+  want["talker.embed_text"] = {{c.text_vocab, Ht}, &embed_text};
+  want["talker.embed_sem"] = {{c.talker.vocab, Ht}, &embed_sem};
+  want["talker.lm_head"] = {{c.talker.vocab, Ht}, &lm_head};
+  if (Ht != Hc) want["cp.proj"] = {{Hc, Ht}, &proj};
+  want["cp.embed_ac"] = {{c.n_acoustic, c.codepred.vocab, Ht}, &embed_ac};
+  want["cp.heads"] = {{c.n_acoustic, c.codepred.vocab, Hc}, &heads};
+  std::unordered_map<std::string, bool> seen;
+  for (int i = 0; i < n; ++i) {
+    if (!names[i]) return ctx->fail(TTS_E_ARG, "load_weights: name %d is NULL", i);
+    auto it = want.find(names[i]);
+    if (it == want.end()) return ctx->fail(TTS_E_SHAPE, "load_weights: unexpected tensor '%s'", names[i]);
+    if (seen.count(names[i])) return ctx->fail(TTS_E_ARG, "load_weights: tensor '%s' given twice", names[i]);
+    seen[names[i]] = true;
+    const auto& shp = it->second.shape;
+    if (ranks[i] != (int)shp.size()) return ctx->fail(TTS_E_SHAPE, "load_weights: '%s' has rank %d, expected %zu", names[i], ranks[i], shp.size());
+    for (size_t k = 0; k < shp.size(); ++k)
+      if (shapes[i * 4 + k] != shp[k])
+        return ctx->fail(TTS_E_SHAPE, "load_weights: '%s' dim %zu is %lld, expected %lld", names[i], k, (long long)shapes[i * 4 + k],
+                         (long long)shp[k]);
+    if (dtypes[i] != c.weight_dtype) return ctx->fail(TTS_E_SHAPE, "load_weights: '%s' dtype %d, expected %d", names[i], dtypes[i], c.weight_dtype);
+    if (!dev_ptrs[i]) return ctx->fail(TTS_E_ARG, "load_weights: '%s' pointer is NULL", names[i]);
+    if (((uintptr_t)dev_ptrs[i]) & 15) return ctx->fail(TTS_E_ARG, "load_weights: '%s' is not 16-byte aligned", names[i]);
+    *it->second.slot = dev_ptrs[i];
+  }
+  for (auto& kv : want)
+    if (!seen.count(kv.first)) return ctx->fail(TTS_E_SHAPE, "load_weights: tensor '%s' missing", kv.first.c_str());
+  ctx->talker = talker;
+  ctx->cp = cp;
+  ctx->embed_text = embed_text; ctx->embed_sem = embed_sem; ctx->lm_head = lm_head; ctx->proj = proj;
+  ctx->embed_ac = embed_ac; ctx->heads = heads;
+  ctx->weights_ok = true;
+  ctx->prefilled = false;
+  drop_graph(ctx);
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+int tts_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, float* sem_logits) {
+  if (!ctx) return TTS_E_ARG;
+  if (!ctx->weights_ok) return ctx->fail(TTS_E_STATE, "prefill: weights not loaded");
+  if (!ids) return ctx->fail(TTS_E_ARG, "prefill: ids is NULL");
+  if (batch < 1 || batch > ctx->cfg.max_batch) return ctx->fail(TTS_E_ARG, "prefill: batch %d outside [1, %d]", batch, ctx->cfg.max_batch);
+  if (n < 1) return ctx->fail(TTS_E_ARG, "prefill: n must be >= 1");
+  if (n > ctx->cfg.max_cache_steps) return ctx->fail(TTS_E_CAPACITY, "prefill: %d positions exceed max_cache_steps %d", n, ctx->cfg.max_cache_steps);
+  const auto& c = ctx->cfg;
+  drop_graph(ctx);
+  hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, 0, 0);
+  HIP_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_fill_u8, dim3(64), dim3(256), 0, ctx->stream, ctx->history, (size_t)batch * c.talker.vocab, (uint8_t)0);
+  HIP_LAUNCH_CHECK();
+  for (int p = 0; p < n; ++p) {
+    if (int rc = gather(ctx, SRC_TABLE, batch, c.talker.hidden, nullptr, 0, ctx->embed_text, c.text_vocab, tokref(ids, n, 0, p, 0),
+                        ctx->x, c.talker.hidden))
+      return rc;
+    if (int rc = talker_stack(ctx, batch, p, 0)) return rc;
+  }
+  if (int rc = talker_head(ctx, batch)) return rc;
+  hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, n, 0);
+  HIP_LAUNCH_CHECK();
+  if (sem_logits)
+    HIP_TRY(hipMemcpyAsync(sem_logits, ctx->logits, (size_t)batch * c.talker.vocab * 4, hipMemcpyDeviceToDevice, ctx->stream));
+  ctx->batch = batch;
+  ctx->pos = n;
+  ctx->frames = 0;
+  ctx->prefilled = true;
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+int tts_talker_step(tts_ctx* ctx, const int32_t* prev_codes, float* sem_logits) {
+  if (!ctx) return TTS_E_ARG;
+  if (!ctx->prefilled) return ctx->fail(TTS_E_STATE, "talker_step: call tts_prefill first");
+  if (!prev_codes) return ctx->fail(TTS_E_ARG, "talker_step: prev_codes is NULL");
+  if (ctx->pos + 1 > ctx->cfg.max_cache_steps) return ctx->fail(TTS_E_CAPACITY, "talker_step: KV cache full (%d positions)", ctx->pos);
+  const int B = ctx->batch;
+  TokRef refs[16];
+  for (int j = 0; j < 16; ++j) refs[j] = tokref(prev_codes, 16, 0, j, 0);
+  if (int rc = embed_sum(ctx, B, refs)) return rc;
+  if (int rc = talker_stack(ctx, B, 0, 1)) return rc;
+  if (int rc = talker_head(ctx, B)) return rc;
+  hipLaunchKernelGGL(k_bump, dim3(1), dim3(64), 0, ctx->stream, ctx->st, 1, 0);
+  HIP_LAUNCH_CHECK();
+  if (sem_logits)
+    HIP_TRY(hipMemcpyAsync(sem_logits, ctx->logits, (size_t)B * ctx->cfg.talker.vocab * 4, hipMemcpyDeviceToDevice, ctx->stream));
+  ctx->pos += 1;
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+int tts_codepred_frame(tts_ctx* ctx, const int32_t* semantic, const tts_sampling* ac, const float* u, const int32_t* forced,
+                       int32_t* codes, float* logits) {
+  if (!ctx) return TTS_E_ARG;
+  if (!ctx->prefilled) return ctx->fail(TTS_E_STATE, "codepred_frame: call tts_prefill first");
+  if (!semantic || !codes) return ctx->fail(TTS_E_ARG, "codepred_frame: semantic and codes must not be NULL");
+  if (int rc = check_sampling(ctx, ac, ctx->cfg.codepred.vocab, "acoustic")) return rc;
+  if (ac->do_sample && !u) return ctx->fail(TTS_E_ARG, "codepred_frame: u is NULL with do_sample");
+  const int B = ctx->batch;
+  URef ur = uref(u ? u : ctx->hT, u ? 15 : 0, 0, 0, 0);
+  if (int rc = codepred_frame(ctx, B, tokref(semantic, 1, 0, 0, 0), *ac, ur, forced, codes, 15, 0, 0, 0, logits)) return rc;
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+int tts_sample(tts_ctx* ctx, const float* logits, int32_t batch, int32_t vocab, const tts_sampling* s, const float* u,
+               uint8_t* history, int32_t* out) {
+  if (!ctx) return TTS_E_ARG;
+  if (!logits || !out) return ctx->fail(TTS_E_ARG, "sample: logits and out must not be NULL");
+  if (batch < 1 || vocab < 1 || vocab > 65536) return ctx->fail(TTS_E_ARG, "sample: batch %d / vocab %d out of range", batch, vocab);
+  if (int rc = check_sampling(ctx, s, vocab, "sample")) return rc;
+  if (s->do_sample && !u) return ctx->fail(TTS_E_ARG, "sample: u is NULL with do_sample");
+  URef ur = uref(u ? u : logits, u ? 1 : 0, 0, 0, 0);
+  if (int rc = sample(ctx, logits, vocab, batch, vocab, *s, ur, history, vocab, history ? 1 : 0, out, 1, 0, 0, 0, nullptr, nullptr,
+                      0, 0))
+    return rc;
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+int tts_run_frames(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_sampling* ac, const float* u, int32_t* codes) {
+  if (!ctx) return TTS_E_ARG;
+  if (!ctx->prefilled) return ctx->fail(TTS_E_STATE, "run_frames: call tts_prefill first");
+  if (n < 0) return ctx->fail(TTS_E_ARG, "run_frames: n must be >= 0");
+  if (!codes) return ctx->fail(TTS_E_ARG, "run_frames: codes is NULL");
+  if (int rc = check_sampling(ctx, sem, ctx->cfg.talker.vocab, "semantic")) return rc;
+  if (int rc = check_sampling(ctx, ac, ctx->cfg.codepred.vocab, "acoustic")) return rc;
+  if ((sem->do_sample || ac->do_sample) && !u) return ctx->fail(TTS_E_ARG, "run_frames: u is NULL with sampling");
+  if (ctx->frames + n > ctx->cfg.max_frames)
+    return ctx->fail(TTS_E_CAPACITY, "run_frames: %d + %d frames exceed max_frames %d", ctx->frames, n, ctx->cfg.max_frames);
+  if (ctx->pos + n > ctx->cfg.max_cache_steps)
+    return ctx->fail(TTS_E_CAPACITY, "run_frames: %d + %d positions exceed max_cache_steps %d", ctx->pos, n, ctx->cfg.max_cache_steps);
+  if (n == 0) return TTS_OK;
+  GraphKey key{*sem, *ac, u, codes, ctx->batch};
+  if (!ctx->have_graph || !(ctx->gkey == key)) {
+    drop_graph(ctx);
+    // Record on a private stream (the caller's may be the null stream, which
+    // cannot be captured); nothing executes during capture. The graph is
+    // then launched on the caller's stream.
+    if (!ctx->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&ctx->cap_stream, hipStreamNonBlocking));
+    HIP_TRY(hipStreamBeginCapture(ctx->cap_stream, hipStreamCaptureModeThreadLocal));
+    hipStream_t user = ctx->stream;
+    ctx->stream = ctx->cap_stream;
+    int rc = enqueue_frame(ctx, *sem, *ac, u, codes);
+    ctx->stream = user;
+    hipGraph_t g = nullptr;
+    hipError_t ec = hipStreamEndCapture(ctx->cap_stream, &g);
+    if (rc) { if (g) (void)hipGraphDestroy(g); return rc; }
+    if (ec != hipSuccess) return ctx->fail(TTS_E_HIP, "hipStreamEndCapture: %s", hipGetErrorString(ec));
+    ctx->graph = g;
+    HIP_TRY(hipGraphInstantiate(&ctx->gexec, ctx->graph, nullptr, nullptr, 0));
+    ctx->have_graph = true;
+    ctx->gkey = key;
+  }
+  for (int i = 0; i < n; ++i) HIP_TRY(hipGraphLaunch(ctx->gexec, ctx->stream));
+  ctx->frames += n;
+  ctx->pos += n;
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+int tts_get_progress(const tts_ctx* ctx, int32_t* talker_pos, int32_t* frames) {
+  if (!ctx) return TTS_E_ARG;
+  if (talker_pos) *talker_pos = ctx->pos;
+  if (frames) *frames = ctx->frames;
+  return TTS_OK;
+}
+
+int tts_reset(tts_ctx* ctx) {
+  if (!ctx) return TTS_E_ARG;
+  hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, 0, 0);
+  HIP_LAUNCH_CHECK();
+  ctx->prefilled = false;
+  ctx->pos = 0;
+  ctx->frames = 0;
+  ctx->batch = 0;
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+const char* tts_last_error(const tts_ctx* ctx) { return ctx ? ctx->err.c_str() : "context is NULL"; }
+
+void tts_destroy(tts_ctx* ctx) {
+  if (!ctx) return;
+  drop_graph(ctx);
+  if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
+  delete ctx;
+}
+
+}  // extern "C"

@@ -1,0 +1,747 @@
+// Device code of the frame decode: CDNA4 (gfx950, wave64) kernels.
+//
+// Ops (Qwen3-style decoder block; the block internals are a reading, the
+// per-frame schedule is from "Running Qwen3-TTS on an AMD R9700", section
+// "Running Qwen3-TTS"):
+//   gemv      y = W x for M input rows, W bf16/fp32 [out, in] streamed once
+//             with 16-byte loads per lane; optional RMSNorm prologue on x,
+//             residual-add or SwiGLU epilogue; x may be gathered from an
+//             embedding table by token.
+//   embed_sum x = E_sem[c0] + sum_j E_ac[j][cj] (Talker input of a frame).
+//   attn      decode attention over a contiguous GQA KV cache with the
+//             per-head q/k RMSNorm, rotate-half RoPE and the KV append fused
+//             in; positions split across blocks, merged by attn_merge.
+//   sample    greedy argmax, or penalty -> temperature -> top-k -> top-p ->
+//             inverse CDF at a given uniform.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tts {
+
+constexpr int kMaxSeg = 3;
+
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+enum Src : int { SRC_VEC = 0, SRC_TABLE = 1, SRC_VEC_THEN_TABLE = 2 };
+
+// Decode-time counters kept on the device so that a captured frame graph can
+// be replayed: pos = next Talker position to write, frame = frames since prefill.
+struct DevState {
+  int32_t pos;
+  int32_t frame;
+  int32_t pad[62];
+};
+
+// Token / uniform addressing that may depend on the device frame counter:
+// element(b) = base[b * b_stride + (use_frame ? frame * f_stride : 0) + offset]
+struct TokRef {
+  const int32_t* base;
+  int32_t b_stride, f_stride, offset, use_frame;
+};
+struct URef {
+  const float* base;
+  int32_t b_stride, f_stride, offset, use_frame;
+};
+
+__device__ __forceinline__ int tok_at(const TokRef& r, const DevState* st, int b) {
+  long i = (long)b * r.b_stride + r.offset + (r.use_frame ? (long)st->frame * r.f_stride : 0);
+  return r.base[i];
+}
+// Token ids index embedding tables; ids outside [0, rows) are clamped so that a
+// bad caller-supplied id cannot read outside the table.
+__device__ __forceinline__ int clamp_tok(int t, int rows) { return t < 0 ? 0 : (t >= rows ? rows - 1 : t); }
+__device__ __forceinline__ float u_at(const URef& r, const DevState* st, int b) {
+  long i = (long)b * r.b_stride + r.offset + (r.use_frame ? (long)st->frame * r.f_stride : 0);
+  return r.base[i];
+}
+
+// ---------------------------------------------------------------------------- element types
+
+// bf16 weights are carried as their 16-bit patterns; a bf16 is the top half of an fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+
+// fp32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ void store_elem(uint16_t* p, float v) { *p = f32_to_bf16(v); }
+__device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <typename WT> struct WTraits;
+template <> struct WTraits<float> { static constexpr int E = 4; };     // elements per 16-byte lane load
+template <> struct WTraits<uint16_t> { static constexpr int E = 8; };
+
+// Unpack one 16-byte weight chunk into E floats.
+__device__ __forceinline__ void unpack(const u32x4& w, float (&f)[8], uint16_t*) {
+  f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  f[4] = bf16_lo(w.z); f[5] = bf16_hi(w.z); f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
+}
+__device__ __forceinline__ void unpack(const u32x4& w, float (&f)[8], float*) {
+  f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y); f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+}
+
+// ---------------------------------------------------------------------------- wave reductions (DPP)
+
+#define TTS_DPP(v, ctrl) __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, true))
+
+// Sum across the 16 lanes of each DPP row; every lane of the row gets the row sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += TTS_DPP(v, 0xB1);   // quad_perm [1,0,3,2]
+  v += TTS_DPP(v, 0x4E);   // quad_perm [2,3,0,1]
+  v += TTS_DPP(v, 0x124);  // row_ror:4
+  v += TTS_DPP(v, 0x128);  // row_ror:8
+  return v;
+}
+// Full wave64 sum, result uniform across the wave.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  int b = __builtin_bit_cast(int, v);
+  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return (r0 + r1) + (r2 + r3);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, TTS_DPP(v, 0xB1));
+  v = fmaxf(v, TTS_DPP(v, 0x4E));
+  v = fmaxf(v, TTS_DPP(v, 0x124));
+  v = fmaxf(v, TTS_DPP(v, 0x128));
+  int b = __builtin_bit_cast(int, v);
+  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 0));
+  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 16));
+  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 32));
+  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------- GEMV
+
+struct GemvArgs {
+  const void* w[kMaxSeg];   // segments share K; their rows are concatenated
+  int32_t seg_rows[kMaxSeg];
+  int32_t nseg;
+  int32_t N;                // total output rows (SwiGLU: rows per branch)
+  int32_t K;
+  int32_t M;                // input rows (streams x positions)
+  int32_t src;              // enum Src
+  const float* x;           // fp32 input rows
+  int32_t x_stride;
+  const void* table;        // embedding table [table_rows, K] (weight dtype) for gathered rows
+  int32_t table_rows;
+  TokRef tok;               // token of gathered row (indexed by stream)
+  const void* gain;         // RMSNorm gain [K] (weight dtype) or nullptr
+  float eps;
+  float* y;
+  int32_t y_stride;
+  const float* res;         // residual rows (EPI_RESID); may alias y
+  int32_t res_stride;
+  int32_t epi;              // enum Epi
+  float* xn_out;            // optional: block 0 writes the normalised input rows here
+  int32_t xn_stride;
+  int32_t nontemporal;      // stream the weights past the caches (read once per frame)
+  const DevState* st;
+};
+
+// Rows each wave streams, by units per row U (a unit = one 16-byte load per lane).
+template <int U, bool PAIR> struct GemvShape {
+  static constexpr int RW0 = PAIR ? (8 / U) : (16 / U);
+  static constexpr int RW = RW0 < 1 ? 1 : (RW0 > 4 ? 4 : RW0);
+};
+
+// Load input row m (fp32 or gathered from a table) element k.. into LDS, with
+// the optional RMSNorm applied. One block stages all M rows.
+template <typename WT, int M>
+__device__ __forceinline__ void gemv_stage_input(const GemvArgs& a, float* xs) {
+  const int tid = threadIdx.x;
+  const int K = a.K;
+  __shared__ float red[M][4];
+  __shared__ float scale[M];
+  float ss[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    ss[m] = 0.f;
+    const int stream = (a.src == SRC_VEC_THEN_TABLE) ? (m >> 1) : m;
+    const bool from_table = (a.src == SRC_TABLE) || (a.src == SRC_VEC_THEN_TABLE && (m & 1));
+    const float* xv = nullptr;
+    const WT* tv = nullptr;
+    if (from_table) {
+      const int t = clamp_tok(tok_at(a.tok, a.st, stream), a.table_rows);
+      tv = reinterpret_cast<const WT*>(a.table) + (size_t)t * K;
+    } else {
+      xv = a.x + (size_t)((a.src == SRC_VEC_THEN_TABLE) ? stream : m) * a.x_stride;
+    }
+    for (int k = tid * 4; k < K; k += 256 * 4) {
+      float v0, v1, v2, v3;
+      if (from_table) {
+        v0 = to_f32(tv[k]); v1 = to_f32(tv[k + 1]); v2 = to_f32(tv[k + 2]); v3 = to_f32(tv[k + 3]);
+      } else {
+        float4 f = *reinterpret_cast<const float4*>(xv + k);
+        v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
+      }
+      ss[m] += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
+      *reinterpret_cast<float4*>(xs + m * K + k) = make_float4(v0, v1, v2, v3);
+    }
+  }
+  if (a.gain) {
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float s = wave_sum(ss[m]);
+      if (lane == 0) red[m][wave] = s;
+    }
+    __syncthreads();
+    if (tid < M) {
+      float s = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
+      scale[tid] = 1.0f / sqrtf(s / (float)K + a.eps);
+    }
+    __syncthreads();
+    const WT* g = reinterpret_cast<const WT*>(a.gain);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float sc = scale[m];
+      for (int k = tid; k < K; k += 256) {
+        float v = xs[m * K + k] * sc * to_f32(g[k]);
+        xs[m * K + k] = v;
+        if (a.xn_out && blockIdx.x == 0) a.xn_out[(size_t)m * a.xn_stride + k] = v;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <typename WT>
+__device__ __forceinline__ const WT* gemv_row_ptr(const GemvArgs& a, int row) {
+  int s = 0, off = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSeg - 1; ++i) {
+    if (s < a.nseg - 1 && row >= off + a.seg_rows[s]) { off += a.seg_rows[s]; ++s; }
+  }
+  return reinterpret_cast<const WT*>(a.w[s]) + (size_t)(row - off) * a.K;
+}
+
+// One wave streams RW rows (PAIR: RW gate rows + RW up rows) of U units each.
+template <typename WT, int U, int M, bool PAIR>
+__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+  constexpr int E = WTraits<WT>::E;
+  constexpr int CH = 64 * E;
+  constexpr int RW = GemvShape<U, PAIR>::RW;
+  constexpr int NR = PAIR ? 2 * RW : RW;  // weight rows per wave
+  extern __shared__ float xs[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r0 = (blockIdx.x * 4 + wave) * RW;
+
+  // 1. issue every weight load of this wave
+  u32x4 wb[NR][U];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    int row = r0 + (PAIR ? (r % RW) : r);
+    if (row > a.N - 1) row = a.N - 1;
+    const WT* wp;
+    if (PAIR) wp = reinterpret_cast<const WT*>(a.w[r / RW]) + (size_t)row * a.K;
+    else wp = gemv_row_ptr<WT>(a, row);
+    const u32x4* p = reinterpret_cast<const u32x4*>(wp) + lane;
+    if (a.nontemporal) {
+#pragma unroll
+      for (int c = 0; c < U; ++c) wb[r][c] = __builtin_nontemporal_load(p + c * 64);
+    } else {
+#pragma unroll
+      for (int c = 0; c < U; ++c) wb[r][c] = p[c * 64];
+    }
+  }
+
+  // 2. stage (and normalise) the input rows in LDS while the weights stream
+  gemv_stage_input<WT, M>(a, xs);
+
+  // 3. dot products
+  float acc[NR][M];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+#pragma unroll
+  for (int c = 0; c < U; ++c) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float xv[E];
+      const float* xp = xs + m * a.K + c * CH + lane * E;
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        float4 f = *reinterpret_cast<const float4*>(xp + e);
+        xv[e] = f.x; xv[e + 1] = f.y; xv[e + 2] = f.z; xv[e + 3] = f.w;
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        float wf[8];
+        unpack(wb[r][c], wf, (WT*)nullptr);
+        float s = acc[r][m];
+#pragma unroll
+        for (int e = 0; e < E; ++e) s = fmaf(wf[e], xv[e], s);
+        acc[r][m] = s;
+      }
+    }
+  }
+
+  // 4. reduce and write
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int row = r0 + r;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float v = wave_sum(acc[r][m]);
+      if (PAIR) {
+        float u = wave_sum(acc[RW + r][m]);
+        v = silu(v) * u;
+      }
+      if (lane == 0 && row < a.N) {
+        float* yp = a.y + (size_t)m * a.y_stride + row;
+        if (a.epi == EPI_RESID) v += a.res[(size_t)m * a.res_stride + row];
+        *yp = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- embeddings
+
+// x[b] = sum over t of table_t[tok_t(b)], summed in table order (t = 0 first).
+struct EmbedArgs {
+  const void* table[16];
+  int32_t rows[16];
+  TokRef tok[16];
+  int32_t ntab;
+  int32_t H;
+  float* x;
+  int32_t x_stride;
+  const DevState* st;
+};
+
+template <typename WT>
+__global__ __launch_bounds__(256) void k_embed_sum(EmbedArgs a) {
+  const int b = blockIdx.y;
+  __shared__ int toks[16];
+  if (threadIdx.x < a.ntab) toks[threadIdx.x] = clamp_tok(tok_at(a.tok[threadIdx.x], a.st, b), a.rows[threadIdx.x]);
+  __syncthreads();
+  for (int k = blockIdx.x * 256 + threadIdx.x; k < a.H; k += gridDim.x * 256) {
+    float s = to_f32(reinterpret_cast<const WT*>(a.table[0])[(size_t)toks[0] * a.H + k]);
+    for (int t = 1; t < a.ntab; ++t) s += to_f32(reinterpret_cast<const WT*>(a.table[t])[(size_t)toks[t] * a.H + k]);
+    a.x[(size_t)b * a.x_stride + k] = s;
+  }
+}
+
+// Rows m of the CodePredictor input when no projection applies:
+// src VEC: x[m] <- vec row; TABLE: x[m] <- table[tok(m)]; VEC_THEN_TABLE: even m <- vec[m/2], odd m <- table[tok(m/2)].
+struct GatherArgs {
+  int32_t src, M, H;
+  const float* vec;
+  int32_t vec_stride;
+  const void* table;
+  int32_t table_rows;
+  TokRef tok;
+  float* x;
+  int32_t x_stride;
+  const DevState* st;
+};
+
+template <typename WT>
+__global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
+  const int m = blockIdx.y;
+  const int stream = (a.src == SRC_VEC_THEN_TABLE) ? (m >> 1) : m;
+  const bool from_table = (a.src == SRC_TABLE) || (a.src == SRC_VEC_THEN_TABLE && (m & 1));
+  const int t = from_table ? clamp_tok(tok_at(a.tok, a.st, stream), a.table_rows) : 0;
+  for (int k = blockIdx.x * 256 + threadIdx.x; k < a.H; k += gridDim.x * 256) {
+    float v = from_table ? to_f32(reinterpret_cast<const WT*>(a.table)[(size_t)t * a.H + k])
+                         : a.vec[(size_t)stream * a.vec_stride + k];
+    a.x[(size_t)m * a.x_stride + k] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------- attention
+
+struct AttnArgs {
+  const float* qkv;         // rows (stream-major, M per stream) of [q (nq*d) | k (nkv*d) | v (nkv*d)]
+  int32_t qkv_stride;
+  int32_t M;                // new positions per stream
+  int32_t nq, nkv, d;
+  const void* q_norm;       // [d] weight dtype
+  const void* k_norm;
+  float eps;
+  const float* rope_cos;    // [positions][d/2]
+  const float* rope_sin;
+  int32_t pos_const;        // position of row 0 when pos_from_state == 0
+  int32_t pos_from_state;
+  void* kc;                 // cache [B][nkv][cap][d] (KT)
+  void* vc;
+  int32_t cap;
+  int32_t chunk;            // positions per split
+  int32_t nsplit;
+  float* out;               // nsplit == 1: [rows][nq*d]
+  int32_t out_stride;
+  float* part;              // nsplit > 1: [rows][nq][nsplit][d + 2] = (o[d], m, l)
+  const DevState* st;
+};
+
+// Cache element loads of EPL contiguous elements into floats.
+template <int EPL>
+__device__ __forceinline__ void load_row(const uint16_t* p, float (&f)[EPL]) {
+  if constexpr (EPL % 8 == 0) {
+#pragma unroll
+    for (int c = 0; c < EPL / 8; ++c) {
+      const u32x4 w = reinterpret_cast<const u32x4*>(p)[c];
+      f[8 * c + 0] = bf16_lo(w.x); f[8 * c + 1] = bf16_hi(w.x); f[8 * c + 2] = bf16_lo(w.y); f[8 * c + 3] = bf16_hi(w.y);
+      f[8 * c + 4] = bf16_lo(w.z); f[8 * c + 5] = bf16_hi(w.z); f[8 * c + 6] = bf16_lo(w.w); f[8 * c + 7] = bf16_hi(w.w);
+    }
+  } else {
+    static_assert(EPL == 4, "bf16 rows load 4 or a multiple of 8 elements");
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+  }
+}
+template <int EPL>
+__device__ __forceinline__ void load_row(const float* p, float (&f)[EPL]) {
+  static_assert(EPL % 4 == 0, "fp32 rows load 4 elements per 16 bytes");
+#pragma unroll
+  for (int c = 0; c < EPL / 4; ++c) {
+    const float4 w = reinterpret_cast<const float4*>(p)[c];
+    f[4 * c + 0] = w.x; f[4 * c + 1] = w.y; f[4 * c + 2] = w.z; f[4 * c + 3] = w.w;
+  }
+}
+
+constexpr int kAttnMaxD = 256;
+
+// grid (nsplit, nkv, B), 256 threads. G query heads share a KV head; M new
+// positions per stream; D = head_dim; each 16-lane group holds D/16
+// elements per lane and walks positions s0+grp, s0+grp+16, ...
+template <typename WT, typename KT, int G, int M, int D>
+__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+  constexpr int EPL = D / 16;
+  constexpr int PL = D / 64;  // elements per lane in the norm/RoPE stage
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int p0 = a.pos_from_state ? a.st->pos : a.pos_const;
+  const int plast = p0 + M - 1;
+  const int s0 = split * a.chunk;
+  if (s0 > plast) return;  // nothing to attend in this split (the merge ignores it)
+  const int s1 = min(s0 + a.chunk, plast + 1);
+  const int row0 = b * M;
+
+  __shared__ float qs[M][G][D];
+  KT* kcache = reinterpret_cast<KT*>(a.kc) + ((size_t)b * a.nkv + g) * a.cap * D;
+  KT* vcache = reinterpret_cast<KT*>(a.vc) + ((size_t)b * a.nkv + g) * a.cap * D;
+
+  // 1. per-head RMSNorm + RoPE of q and k, then k/v appended at their
+  //    positions by the split that holds them. One wave per vector.
+  for (int vi = wave; vi < M * (G + 2); vi += 4) {
+    const int m = vi / (G + 2), j = vi % (G + 2);  // j < G: q head; G: k; G + 1: v
+    const int p = p0 + m;
+    const float* rowp = a.qkv + (size_t)(row0 + m) * a.qkv_stride;
+    const float* src = (j < G) ? rowp + (size_t)(g * G + j) * D
+                     : (j == G) ? rowp + (size_t)a.nq * D + (size_t)g * D
+                                : rowp + (size_t)(a.nq + a.nkv) * D + (size_t)g * D;
+    float v[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) v[i] = src[lane + 64 * i];
+    if (j <= G) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < PL; ++i) ss += v[i] * v[i];
+      ss = wave_sum(ss);
+      const float sc = 1.0f / sqrtf(ss / (float)D + a.eps);
+      const WT* gn = reinterpret_cast<const WT*>(j < G ? a.q_norm : a.k_norm);
+#pragma unroll
+      for (int i = 0; i < PL; ++i) v[i] = v[i] * sc * to_f32(gn[lane + 64 * i]);
+      constexpr int HALF = D / 2;
+      const float* cs = a.rope_cos + (size_t)p * HALF;
+      const float* sn = a.rope_sin + (size_t)p * HALF;
+      float r[PL];
+      if constexpr (PL == 1) {
+        const float other = __shfl_xor(v[0], 32);
+        const int ii = lane & (HALF - 1);
+        const float c = cs[ii], s = sn[ii];
+        r[0] = (lane < HALF) ? (v[0] * c - other * s) : (v[0] * c + other * s);
+      } else {
+        constexpr int HP = PL / 2;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+          const int ii = (lane + 64 * i) & (HALF - 1);
+          const float c = cs[ii], s = sn[ii];
+          r[i] = (i < HP) ? (v[i] * c - v[i + HP] * s) : (v[i] * c + v[i - HP] * s);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < PL; ++i) v[i] = r[i];
+    }
+    if (j < G) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i) qs[m][j][lane + 64 * i] = v[i];
+    } else if (p >= s0 && p < s0 + a.chunk) {
+      KT* dst = (j == G ? kcache : vcache) + (size_t)p * D;
+#pragma unroll
+      for (int i = 0; i < PL; ++i) store_elem(dst + lane + 64 * i, v[i]);
+    }
+  }
+  __syncthreads();
+
+  // 2. online softmax over this split's positions
+  const int grp = tid >> 4, gl16 = tid & 15;
+  const float scale = 1.0f / sqrtf((float)D);
+  float mrun[M][G], lrun[M][G], o[M][G][EPL], qv[M][G][EPL];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mrun[m][h] = -INFINITY;
+      lrun[m][h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) { o[m][h][e] = 0.f; qv[m][h][e] = qs[m][h][gl16 * EPL + e]; }
+    }
+  for (int t = s0 + grp; t < s1; t += 16) {
+    float kf[EPL], vf[EPL];
+    load_row<EPL>(kcache + (size_t)t * D + gl16 * EPL, kf);
+    load_row<EPL>(vcache + (size_t)t * D + gl16 * EPL, vf);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const bool visible = t <= p0 + m;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) s = fmaf(qv[m][h][e], kf[e], s);
+        s = row16_sum(s) * scale;
+        if (visible) {
+          const float mn = fmaxf(mrun[m][h], s);
+          const float corr = expf(mrun[m][h] - mn);
+          const float pw = expf(s - mn);
+          lrun[m][h] = lrun[m][h] * corr + pw;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[m][h][e] = o[m][h][e] * corr + pw * vf[e];
+          mrun[m][h] = mn;
+        }
+      }
+    }
+  }
+
+  // 3. combine the 16 groups in fixed order, then write the output or the partial
+  __shared__ float gm[16][M][G], gl[16][M][G];
+  __shared__ float ocomb[M][G][D];
+  __shared__ float mtot[M][G], ltot[M][G];
+  if (gl16 == 0) {
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int h = 0; h < G; ++h) { gm[grp][m][h] = mrun[m][h]; gl[grp][m][h] = lrun[m][h]; }
+  }
+  for (int i = tid; i < M * G * D; i += 256) (&ocomb[0][0][0])[i] = 0.f;
+  __syncthreads();
+  if (tid < M * G) {
+    const int m = tid / G, h = tid % G;
+    float mx = -INFINITY;
+    for (int q = 0; q < 16; ++q) mx = fmaxf(mx, gm[q][m][h]);
+    float l = 0.f;
+    for (int q = 0; q < 16; ++q) {
+      const float w = (gm[q][m][h] == -INFINITY) ? 0.f : expf(gm[q][m][h] - mx);
+      gm[q][m][h] = w;
+      l += gl[q][m][h] * w;
+    }
+    mtot[m][h] = mx;
+    ltot[m][h] = l;
+  }
+  __syncthreads();
+  for (int q = 0; q < 16; ++q) {
+    if (grp == q) {
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float w = gm[q][m][h];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) ocomb[m][h][gl16 * EPL + e] += w * o[m][h][e];
+        }
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < M * G * D; i += 256) {
+    const int m = i / (G * D), h = (i / D) % G, e = i % D;
+    const int qh = g * G + h;
+    const int row = row0 + m;
+    if (a.nsplit == 1) {
+      const float l = ltot[m][h];
+      a.out[(size_t)row * a.out_stride + (size_t)qh * D + e] = l > 0.f ? ocomb[m][h][e] / l : 0.f;
+    } else {
+      float* pp = a.part + (((size_t)row * a.nq + qh) * a.nsplit + split) * (D + 2);
+      pp[e] = ocomb[m][h][e];
+      if (e == 0) { pp[D] = mtot[m][h]; pp[D + 1] = ltot[m][h]; }
+    }
+  }
+}
+
+// Merge split partials: grid (nq, rows), d threads.
+struct MergeArgs {
+  const float* part;
+  int32_t nq, d, nsplit, chunk, M, pos_const, pos_from_state;
+  float* out;
+  int32_t out_stride;
+  const DevState* st;
+};
+
+__global__ __launch_bounds__(256) void k_attn_merge(MergeArgs a) {
+  const int qh = blockIdx.x, row = blockIdx.y, e = threadIdx.x;
+  const int p0 = a.pos_from_state ? a.st->pos : a.pos_const;
+  const int m = row % a.M;
+  const int used = min(a.nsplit, (p0 + m) / a.chunk + 1);
+  const float* pp = a.part + ((size_t)row * a.nq + qh) * a.nsplit * (a.d + 2);
+  float mx = -INFINITY;
+  for (int s = 0; s < used; ++s) mx = fmaxf(mx, pp[s * (a.d + 2) + a.d]);
+  float l = 0.f, acc = 0.f;
+  for (int s = 0; s < used; ++s) {
+    const float ms = pp[s * (a.d + 2) + a.d];
+    const float w = (ms == -INFINITY) ? 0.f : expf(ms - mx);
+    l += w * pp[s * (a.d + 2) + a.d + 1];
+    if (e < a.d) acc += w * pp[s * (a.d + 2) + e];
+  }
+  if (e < a.d) a.out[(size_t)row * a.out_stride + (size_t)qh * a.d + e] = l > 0.f ? acc / l : 0.f;
+}
+
+// ---------------------------------------------------------------------------- sampling
+
+struct SampleArgs {
+  const float* logits;
+  int32_t l_stride;
+  int32_t V;
+  int32_t do_sample, top_k;
+  float top_p, temperature, penalty;
+  URef u;
+  uint8_t* history;         // [B][V] or nullptr
+  int32_t h_stride;
+  int32_t mark_history;
+  int32_t* out;             // token (stream b at out[b * out_b_stride + frame * out_f_stride + out_offset])
+  int32_t out_b_stride, out_f_stride, out_offset, out_use_frame;
+  int32_t* next;            // optional: token fed to the next step (forced override)
+  const int32_t* forced;    // optional [B][forced_stride]
+  int32_t forced_stride, forced_offset;
+  const DevState* st;
+};
+
+constexpr int kSortMax = 4096;
+
+__device__ __forceinline__ uint32_t orderable(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One block (256 threads) per stream.
+__global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const float* l = a.logits + (size_t)b * a.l_stride;
+  __shared__ float red_v[256];
+  __shared__ int red_i[256];
+  __shared__ int chosen;
+  if (!a.do_sample) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int i = tid; i < a.V; i += 256) {
+      const float v = l[i];
+      if (bi == 0x7fffffff || v > bv) { bv = v; bi = i; }
+    }
+    red_v[tid] = bv; red_i[tid] = bi;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if (tid < s) {
+        const float v2 = red_v[tid + s];
+        const int i2 = red_i[tid + s];
+        if (v2 > red_v[tid] || (v2 == red_v[tid] && i2 < red_i[tid])) { red_v[tid] = v2; red_i[tid] = i2; }
+      }
+      __syncthreads();
+    }
+    if (tid == 0) chosen = red_i[0];
+  } else {
+    __shared__ unsigned long long keys[kSortMax];
+    __shared__ float vals[kSortMax];
+    int n2 = 1;
+    while (n2 < a.V) n2 <<= 1;
+    const uint8_t* hist = a.history ? a.history + (size_t)b * a.h_stride : nullptr;
+    for (int i = tid; i < n2; i += 256) {
+      if (i < a.V) {
+        float v = l[i];
+        if (hist && a.penalty != 1.0f && hist[i]) v = (v > 0.f) ? v / a.penalty : v * a.penalty;
+        v = v / a.temperature;
+        vals[i] = v;
+        keys[i] = ((unsigned long long)(~orderable(v)) << 32) | (uint32_t)i;
+      } else {
+        keys[i] = ~0ull;
+      }
+    }
+    __syncthreads();
+    // bitonic sort, ascending
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n2; i += 256) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const unsigned long long x = keys[i], y = keys[ixj];
+            const bool up = (i & k) == 0;
+            if ((x > y) == up) { keys[i] = y; keys[ixj] = x; }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    if (tid == 0) {
+      int kk = (a.top_k <= 0 || a.top_k > a.V) ? a.V : a.top_k;
+      const float l0 = vals[(uint32_t)keys[0]];
+      if (a.top_p < 1.0f) {
+        float tot = 0.f;
+        for (int i = 0; i < kk; ++i) tot += expf(vals[(uint32_t)keys[i]] - l0);
+        float cum = 0.f;
+        int m = kk - 1;
+        for (int i = 0; i < kk; ++i) {
+          cum += expf(vals[(uint32_t)keys[i]] - l0) / tot;
+          if (cum >= a.top_p) { m = i; break; }
+        }
+        kk = m + 1;
+      }
+      float tot = 0.f;
+      for (int i = 0; i < kk; ++i) tot += expf(vals[(uint32_t)keys[i]] - l0);
+      const float target = u_at(a.u, a.st, b) * tot;
+      int pick = kk - 1;
+      float cum = 0.f;
+      for (int i = 0; i < kk; ++i) {
+        cum += expf(vals[(uint32_t)keys[i]] - l0);
+        if (cum > target) { pick = i; break; }
+      }
+      chosen = (int)(uint32_t)keys[pick];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int t = chosen;
+    const long fo = a.out_use_frame ? (long)a.st->frame * a.out_f_stride : 0;
+    a.out[(long)b * a.out_b_stride + fo + a.out_offset] = t;
+    if (a.history && a.mark_history) a.history[(size_t)b * a.h_stride + t] = 1;
+    if (a.next) a.next[b] = a.forced ? a.forced[(size_t)b * a.forced_stride + a.forced_offset] : t;
+  }
+}
+
+// ---------------------------------------------------------------------------- counters
+
+__global__ void k_bump(DevState* st, int dpos, int dframe) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) { st->pos += dpos; st->frame += dframe; }
+}
+__global__ void k_set_state(DevState* st, int pos, int frame) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) { st->pos = pos; st->frame = frame; }
+}
+__global__ void k_fill_u8(uint8_t* p, size_t n, uint8_t v) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+}  // namespace tts

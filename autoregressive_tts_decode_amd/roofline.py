@@ -49,7 +49,7 @@ def kv_bytes_per_position(s: StackCfg, kv_elem_bytes: int) -> int:
     return 2 * s.n_kv_heads * s.head_dim * kv_elem_bytes
 
 
-def algorithmic_bytes(cfg: ModelCfg, talker_positions_read: float, batch: int = 1) -> dict:
+def algorithmic_bytes(cfg: ModelCfg, talker_positions_read: float, batch: int = 1, kv_elem_bytes: int | None = None) -> dict:
     """Algorithmic bytes of one frame (per stream batch of ``batch`` lockstep streams).
 
     talker_positions_read: number of cached positions the Talker's attention
@@ -58,7 +58,7 @@ def algorithmic_bytes(cfg: ModelCfg, talker_positions_read: float, batch: int = 
     """
     t, c = cfg.talker, cfg.codepred
     b = _wbytes(cfg)
-    kvb = b  # the cache is stored in the weight dtype
+    kvb = b if kv_elem_bytes is None else kv_elem_bytes
     talker_w = (t.n_layers * layer_weight_elems(t) + t.hidden + t.vocab * t.hidden) * b
     emb_rows = batch * (1 + cfg.n_acoustic) * t.hidden * b
     cp_step_w = (c.n_layers * layer_weight_elems(c) + c.hidden + c.vocab * c.hidden) * b
@@ -75,7 +75,8 @@ def algorithmic_bytes(cfg: ModelCfg, talker_positions_read: float, batch: int = 
             "embedding_rows": emb_rows + cp_rows, "kv_talker": kv_t, "kv_cp": kv_c, "total": total}
 
 
-def frame_bytes_for_run(cfg: ModelCfg, prefill_len: int, first_frame: int, n_frames: int, batch: int = 1) -> float:
+def frame_bytes_for_run(cfg: ModelCfg, prefill_len: int, first_frame: int, n_frames: int, batch: int = 1,
+                        kv_elem_bytes: int | None = None) -> float:
     """Total algorithmic bytes of frames [first_frame, first_frame + n_frames).
 
     Frame t (t >= 0) samples its semantic token from the pending Talker
@@ -85,5 +86,5 @@ def frame_bytes_for_run(cfg: ModelCfg, prefill_len: int, first_frame: int, n_fra
     """
     tot = 0.0
     for t in range(first_frame, first_frame + n_frames):
-        tot += algorithmic_bytes(cfg, prefill_len + t + 1, batch)["total"]
+        tot += algorithmic_bytes(cfg, prefill_len + t + 1, batch, kv_elem_bytes)["total"]
     return tot

@@ -1,0 +1,150 @@
+"""Frame-decode benchmark: acoustic frames/s and RTF at batch 1 (1.7B-class).
+
+A step is one acoustic frame: draw the semantic token, 15 CodePredictor
+steps, and the Talker step that consumes the frame's codes -- one replay of
+the captured frame graph. The workload follows the 1.7B-class config: seeded
+bf16 weights, prefill of 64 random text ids, greedy frames at batch 1.
+
+    python bench.py [--steps K] [--warmup W] [--workload 1.7b] [--reps R]
+
+Prints one JSON line. The oracle (plain NumPy) is timed on a bounded sample of
+the same workload on the host cores as ``cpu_baseline``.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+METRIC = "acoustic frames/sec (RTF) at batch 1, 1.7B-class; % of HBM roofline"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=224, help="timed frames per repetition")
+    p.add_argument("--warmup", type=int, default=16, help="untimed frames before the timed ones")
+    p.add_argument("--reps", type=int, default=3, help="repetitions (prefill + warmup + timed); the median is reported")
+    p.add_argument("--workload", default="1.7b")
+    p.add_argument("--cpu-frames", type=int, default=200, help="frames of the oracle CPU baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--kv-dtype", default="fp32", choices=["fp32", "bf16"])
+    return p.parse_args()
+
+
+def cpu_baseline(wl, weights, frames: int) -> dict:
+    from threadpoolctl import threadpool_info
+    from oracle import OracleModel
+    from autoregressive_tts_decode_amd import synth
+
+    model = wl.model
+    orc = OracleModel(weights, model.as_dict(), np.float32)
+    ids = synth.make_text_ids(wl)[:1, :8]
+    greedy = {"do_sample": False, "top_k": 0, "top_p": 1.0, "temperature": 1.0, "repetition_penalty": 1.0}
+    st = orc.new_state(1, 8 + frames + 1)
+    lg = orc.prefill(st, ids)
+    t0 = time.perf_counter()
+    for _ in range(frames):
+        s = int(np.argmax(lg[0]))
+        a, _ = orc.codepred_frame(st, np.array([s], np.int32), greedy, np.zeros((1, 15), np.float32))
+        lg = orc.talker_step(st, np.concatenate([[[s]], a], axis=1).astype(np.int32))
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(frames / dt, 4), "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{model.name}, batch 1, prefill 8 ids, {frames} greedy frames timed (NumPy fp32, "
+                      f"weights pre-upcast from the same bf16 values), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build decodes on one GPU: a batch-1 frame does not shard usefully and "
+                                   "independent streams are data parallel with no exchange; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    from autoregressive_tts_decode_amd import config, synth, tts, roofline
+
+    wl = config.WORKLOADS[args.workload]
+    model, B = wl.model, wl.batch
+    K, W = args.steps, args.warmup
+    cap = wl.prefill_len + W + K + 1
+    d = torch.device("cuda:0")
+    tts.load_library()  # fails loudly when the HIP library is missing
+
+    weights = synth.make_weights(model, wl.weight_seed)
+    dw = tts.weights_to_device(weights, model, d)
+    dec = tts.TTSDecoder(model, B, cap, W + K, kv_dtype=args.kv_dtype)
+    dec.load_weights(dw)
+    ids = torch.from_numpy(synth.make_text_ids(wl)).to(d)
+    u = torch.from_numpy(synth.make_uniforms(wl, frames=W + K)).to(d)
+    codes = torch.zeros((B, W + K, 16), dtype=torch.int32, device=d)
+    stream = dec.stream
+
+    times, prefill_ms = [], []
+    for _ in range(args.reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        dec.prefill(ids)
+        torch.cuda.synchronize()
+        prefill_ms.append((time.perf_counter() - t0) * 1e3)
+        if W:
+            dec.run_frames(W, wl.semantic, wl.acoustic, u, codes)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dec.run_frames(K, wl.semantic, wl.acoustic, u, codes)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    t = statistics.median(times)
+    fps = B * K / t
+    ms_per_step = t / K * 1e3
+    kvb = 2 if dec.kv_dtype == "bf16" else 4
+    bytes_avg = roofline.frame_bytes_for_run(model, wl.prefill_len, W, K, batch=B, kv_elem_bytes=kvb) / K
+    achieved = bytes_avg / (t / K) / 1e9
+    peak = roofline.HBM_PEAK_BYTES_PER_S / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(fps, 3),
+        "unit": "frames/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if model.weight_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{model.name}: Talker 28x2048 (16q/8kv heads, d128, FFN 6144, Vs 3072) + "
+                               f"CodePredictor 5x1024 (FFN 3072, 15 heads x 2048); batch {B}, prefill "
+                               f"{wl.prefill_len} ids, {W + K} frames ({'sampled' if wl.semantic.do_sample else 'greedy'})"
+                   if args.workload.startswith("1.7b") else f"{model.name}; batch {B}, prefill {wl.prefill_len}, {W + K} frames",
+                   "batch": B, "prefill_len": wl.prefill_len, "frames": W + K, "timed_frames": K,
+                   "kv_cache": dec.kv_dtype},
+        "rtf": round(roofline.rtf_from_fps(fps / B), 6),
+        "prefill_ms": round(statistics.median(prefill_ms), 2),
+        "ms_per_step_all_reps": [round(x / K * 1e3, 4) for x in times],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit_of_work": "one frame graph replay (all kernels of a frame)",
+                     "algorithmic_bytes_per_frame": int(bytes_avg)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, weights, args.cpu_frames)
+    dec.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

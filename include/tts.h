@@ -1,0 +1,166 @@
+/*
+ * tts.h -- C ABI of the MI355X per-frame Talker + CodePredictor decode.
+ *
+ * The method ("Running Qwen3-TTS on an AMD R9700", section "Running
+ * Qwen3-TTS"): audio is generated one acoustic frame (80 ms, 16 codebook
+ * tokens [semantic, acoustic 1..15]) at a time. Per frame the Talker decoder
+ * runs one step and emits the semantic token; the CodePredictor decoder then
+ * runs 15 sequential steps and emits acoustic tokens 1..15. Sampling controls
+ * follow the "qwen3-tts-hip" README, section "Library Usage" (do_sample,
+ * top_k, top_p, temperature, repetition_penalty; the acoustic set has no
+ * repetition penalty); a fixed KV-cache capacity independent of a request's
+ * frame count follows the same section (max_cache_steps).
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers (HIP device memory owned by the
+ *    caller), except the config/sampling structs and the name/shape tables of
+ *    tts_load_weights, which are host memory.
+ *  - The library never allocates or frees device memory. The caller
+ *    allocates the workspace (size from tts_workspace_bytes) and the weights;
+ *    the context borrows them until tts_destroy.
+ *  - Every call is asynchronous on the stream given to tts_create. Results
+ *    are valid after the caller synchronises that stream. A context belongs to
+ *    one host thread at a time.
+ *  - Host-side validation happens before anything is enqueued: on an error
+ *    return nothing was enqueued and the device state is unchanged. The text
+ *    of the last error is available from tts_last_error.
+ *  - Tokens are int32. Logits are fp32. Weights are row-major [out, in],
+ *    all fp32 (TTS_DTYPE_F32) or all bf16 (TTS_DTYPE_BF16).
+ *  - B (batch) streams run in lockstep: same prefill length, same positions.
+ */
+#ifndef TTS_H
+#define TTS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTS_ABI_VERSION 1
+
+typedef struct tts_ctx tts_ctx;
+
+enum tts_status {
+  TTS_OK = 0,
+  TTS_E_ARG = -1,        /* null pointer, bad enum or out-of-range scalar */
+  TTS_E_SHAPE = -2,      /* config or tensor shape the library does not accept */
+  TTS_E_CAPACITY = -3,   /* KV positions or frames would exceed the configured capacity */
+  TTS_E_STATE = -4,      /* call out of order (e.g. a step before weights or prefill) */
+  TTS_E_HIP = -5,        /* a HIP runtime call failed; tts_last_error has its text */
+  TTS_E_UNSUPPORTED = -6 /* valid request outside what this build implements */
+};
+
+enum tts_dtype { TTS_DTYPE_F32 = 0, TTS_DTYPE_BF16 = 1 };
+
+/* One decoder stack (Talker or CodePredictor). vocab is the semantic vocab
+ * for the Talker and the per-codebook acoustic vocab for the CodePredictor. */
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+} tts_stack_cfg;
+
+typedef struct {
+  tts_stack_cfg talker, codepred;
+  int32_t text_vocab;
+  int32_t n_acoustic;      /* must be 15 */
+  float rms_eps;           /* RMSNorm epsilon */
+  float rope_theta;        /* RoPE base */
+  int32_t weight_dtype;    /* enum tts_dtype of every weight tensor */
+  int32_t kv_dtype;        /* enum tts_dtype of the KV caches (fp32 keeps k/v unrounded) */
+  int32_t max_batch;       /* streams per context */
+  int32_t max_cache_steps; /* Talker KV capacity in positions (prefill + frames) */
+  int32_t max_frames;      /* frame capacity of the u / codes arrays of tts_run_frames */
+} tts_config;
+
+/* Sampling controls. do_sample = 0 is greedy argmax (lowest id on ties).
+ * Otherwise: repetition penalty over the history set (positive logits
+ * divided by it, others multiplied), division by temperature, top_k
+ * (<= 0: all ids; ids ordered by logit descending then id ascending), top_p
+ * (>= 1: no-op), then inverse CDF of exp(l - l_max) at the given uniform:
+ * the first kept id whose running sum exceeds u * sum, else the last. */
+typedef struct {
+  int32_t do_sample;
+  int32_t top_k;
+  float top_p;
+  float temperature;
+  float repetition_penalty;
+} tts_sampling;
+
+/* Bytes of device workspace (KV caches, activations, tables, counters) for a
+ * config. Returns TTS_E_SHAPE for configs the kernels do not accept. */
+int tts_workspace_bytes(const tts_config* cfg, size_t* bytes);
+
+/* Create a context on the current HIP device. hip_stream: a hipStream_t (NULL
+ * = the null stream). workspace: device memory of at least
+ * tts_workspace_bytes, 256-byte aligned, borrowed until tts_destroy. */
+int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t workspace_bytes, tts_ctx** out);
+
+/* Bind weights. n tensors named by the canonical names (talker.embed_text,
+ * talker.embed_sem, talker.layers.<i>.{attn_norm,wq,wk,wv,q_norm,k_norm,wo,
+ * mlp_norm,wg,wu,wd}, talker.final_norm, talker.lm_head, cp.proj (only when
+ * the widths differ), cp.embed_ac [15,Va,Ht], cp.layers.<i>.{...},
+ * cp.final_norm, cp.heads [15,Va,Hc]). shapes: n x 4 int64 (row-major, only
+ * the first ranks[i] entries used); dtypes: enum tts_dtype per tensor. Every
+ * tensor must be present with the exact shape, the config's dtype and
+ * 16-byte alignment. Pointers are borrowed until tts_destroy. */
+int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* const* dev_ptrs,
+                     const int64_t* shapes, const int32_t* ranks, const int32_t* dtypes);
+
+/* Reset the streams and run the Talker over text ids [B, n] (positions
+ * 0..n-1). Leaves frame 0's Talker output pending (semantic logits and the
+ * final-normed hidden that conditions the CodePredictor). sem_logits
+ * [B, Vs] receives those logits when non-NULL. */
+int tts_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, float* sem_logits);
+
+/* One Talker step fed with the previous frame's codes [B, 16]: the input is
+ * E_sem[c0] + sum_j E_ac[j][cj]. Advances the Talker position by one and
+ * replaces the pending output; sem_logits [B, Vs] receives it when non-NULL. */
+int tts_talker_step(tts_ctx* ctx, const int32_t* prev_codes, float* sem_logits);
+
+/* The 15 CodePredictor steps of one frame, conditioned on the pending Talker
+ * hidden and on semantic [B]. ac: acoustic sampling; u [B, 15] uniforms
+ * (ignored when greedy; may be NULL then). forced [B, 15] or NULL: when given,
+ * forced[b][j-1] replaces the drawn a_j as the input of step j+1 (teacher
+ * forcing); the drawn tokens are still written to codes [B, 15] and the
+ * logits to logits [B, 15, Va] when non-NULL. */
+int tts_codepred_frame(tts_ctx* ctx, const int32_t* semantic, const tts_sampling* ac, const float* u,
+                       const int32_t* forced, int32_t* codes, float* logits);
+
+/* Standalone sampler over logits [B, V] with uniforms u [B] (may be NULL when
+ * greedy). history [B, V] (uint8, 0/1) or NULL: when given and the penalty is
+ * not 1 it selects the penalised ids, and the drawn id is marked in it.
+ * out [B] receives the ids. V <= 65536. */
+int tts_sample(tts_ctx* ctx, const float* logits, int32_t batch, int32_t vocab, const tts_sampling* s,
+               const float* u, uint8_t* history, int32_t* out);
+
+/* Generate n frames after tts_prefill (or after earlier frames). Frame t
+ * (t counts frames since prefill) draws the semantic token from the pending
+ * Talker logits with u[b][t][0] and the semantic history, runs the
+ * CodePredictor with u[b][t][1..15], writes codes[b][t][0..15], then runs the
+ * Talker step on those codes. u and codes are [B, max_frames, 16]. The frame
+ * loop replays one captured HIP graph per frame, with positions and the frame
+ * index kept on the device. */
+int tts_run_frames(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_sampling* ac, const float* u,
+                   int32_t* codes);
+
+/* Host-side counters: Talker positions written so far and frames generated
+ * since the last prefill. Either pointer may be NULL. */
+int tts_get_progress(const tts_ctx* ctx, int32_t* talker_pos, int32_t* frames);
+
+/* Forget the streams (positions, frames, histories). Weights stay bound. */
+int tts_reset(tts_ctx* ctx);
+
+/* Text of the last error on this context ("" if none). Valid until the next
+ * call on the context. */
+const char* tts_last_error(const tts_ctx* ctx);
+
+/* Release host state and the captured graphs. The workspace and weights are
+ * the caller's. Safe on NULL. */
+void tts_destroy(tts_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTS_H */

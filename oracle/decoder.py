@@ -316,12 +316,12 @@ class OracleModel:
             Q = rms_norm(linear(xn, L["wq"]).reshape(B, S, s.nq, s.d), L["q_norm"], self.eps)
             K = rms_norm(linear(xn, L["wk"]).reshape(B, S, s.nkv, s.d), L["k_norm"], self.eps)
             V = linear(xn, L["wv"]).reshape(B, S, s.nkv, s.d)
-            Q = apply_rope(Q, cos, sin)
-            K = np.repeat(apply_rope(K, cos, sin), rep, axis=2)
-            V = np.repeat(V, rep, axis=2)
-            scores = np.einsum("bihd,bjhd->bhij", Q, K) / self.dtype.type(np.sqrt(s.d))
+            Q = apply_rope(Q, cos, sin).transpose(0, 2, 1, 3)                       # [B, nq, S, d]
+            K = np.repeat(apply_rope(K, cos, sin), rep, axis=2).transpose(0, 2, 3, 1)  # [B, nq, d, S]
+            V = np.repeat(V, rep, axis=2).transpose(0, 2, 1, 3)                       # [B, nq, S, d]
+            scores = np.matmul(Q, K) / self.dtype.type(np.sqrt(s.d))
             scores = np.where(causal[None, None], scores, -np.inf)
-            O = np.einsum("bhij,bjhd->bihd", softmax(scores), V).reshape(B, S, s.nq * s.d)
+            O = np.matmul(softmax(scores), V).transpose(0, 2, 1, 3).reshape(B, S, s.nq * s.d)
             x = x + linear(O, L["wo"])
             xn2 = rms_norm(x, L["mlp_norm"], self.eps)
             x = x + linear(swiglu(linear(xn2, L["wg"]), linear(xn2, L["wu"])), L["wd"])

@@ -1,0 +1,363 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Bars (per step, per stream):
+  * logits: max|dlogit| <= tol * max|logit|, tol = 1e-4 for the fp32 model,
+    1e-2 for the bf16 models;
+  * greedy tokens: the GPU's own argmax equals the oracle's wherever the
+    oracle's top-2 margin exceeds 0.05 (near ties are counted, not compared);
+  * sampled tokens: equal given the same uniforms, except draws whose
+    boundary lies within the model's logit tolerance (counted): the GPU
+    draws from its own logits, which may differ from the oracle's by up to
+    that tolerance.
+End-to-end comparisons are teacher-forced with the oracle's codes: random
+weights leave many greedy steps near a tie, so free-running streams part
+ways within a few frames.
+"""
+import numpy as np
+import pytest
+import torch
+
+from autoregressive_tts_decode_amd import config, synth, tts
+from oracle import OracleModel
+from oracle.decoder import linear
+from oracle.sampler import sample_token
+from parity_util import rowwise_rel_err, greedy_agreement, top2_margin, sample_exempt
+
+pytestmark = pytest.mark.gpu
+GREEDY = config.GREEDY.as_dict()
+SEM = config.SEMANTIC_SAMPLED.as_dict()
+AC = config.ACOUSTIC_SAMPLED.as_dict()
+
+
+def dev():
+    assert torch.cuda.is_available(), "the gpu tests need a HIP device"
+    return torch.device("cuda:0")
+
+
+def make_decoder(model, batch, cap, frames, weights):
+    dw = tts.weights_to_device(weights, model, dev())
+    dec = tts.TTSDecoder(model, batch, cap, frames)
+    dec.load_weights(dw)
+    return dec, dw
+
+
+def teacher_forced(dec, model, ids, ref_codes, frames, logits_out=True):
+    """GPU prefill + per-frame CodePredictor (forced) + Talker step on the oracle's codes."""
+    d = dev()
+    B = ids.shape[0]
+    Vs, Va = model.talker.vocab, model.codepred.vocab
+    sem = torch.zeros((frames, B, Vs), dtype=torch.float32, device=d)
+    acl = torch.zeros((frames, B, 15, Va), dtype=torch.float32, device=d)
+    own = torch.zeros((frames, B, 15), dtype=torch.int32, device=d)
+    codes = torch.from_numpy(np.ascontiguousarray(ref_codes)).to(d)
+    rows = [codes[:, t].contiguous() for t in range(frames)]
+    sems = [codes[:, t, 0].contiguous() for t in range(frames)]
+    forced = [codes[:, t, 1:].contiguous() for t in range(frames)]
+    dec.prefill(torch.from_numpy(ids).to(d), sem[0])
+    for t in range(frames):
+        if t > 0:
+            dec.talker_step(rows[t - 1], sem[t])
+        dec.codepred_frame(sems[t], GREEDY, None, own[t], forced=forced[t], logits=acl[t])
+    torch.cuda.synchronize()
+    return (sem.cpu().numpy().transpose(1, 0, 2), acl.cpu().numpy().transpose(1, 0, 2, 3),
+            own.cpu().numpy().transpose(1, 0, 2))
+
+
+def check_step_parity(model, ref, got_sem, got_ac, got_tok, tol):
+    e_sem = rowwise_rel_err(got_sem, ref["sem_logits"])
+    e_ac = rowwise_rel_err(got_ac, ref["ac_logits"])
+    assert e_sem.max() <= tol, f"semantic logits rel err {e_sem.max():.3e} > {tol}"
+    assert e_ac.max() <= tol, f"acoustic logits rel err {e_ac.max():.3e} > {tol}"
+    n, ex, bad = greedy_agreement(got_tok, ref["ac_logits"])
+    assert not bad, f"{len(bad)} greedy acoustic mismatches on non-exempt steps (of {n}; {ex} exempt): {bad[:5]}"
+    return e_sem.max(), e_ac.max(), n, ex
+
+
+# ----------------------------------------------------------------------------- tiny fp32 model
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl = config.WORKLOADS["tiny"]
+    w = synth.make_weights(wl.model, wl.weight_seed)
+    orc = OracleModel(w, wl.model.as_dict(), np.float64)
+    ids = synth.make_text_ids(wl)
+    u = synth.make_uniforms(wl)
+    ref = orc.generate(ids, wl.frames, GREEDY, GREEDY, u)
+    dec, dw = make_decoder(wl.model, 1, wl.prefill_len + wl.frames + 8, wl.frames + 8, w)
+    return dict(wl=wl, w=w, orc=orc, ids=ids, u=u, ref=ref, dec=dec, dw=dw)
+
+
+def test_tiny_teacher_forced_step_parity(tiny):
+    wl = tiny["wl"]
+    sem, ac, tok = teacher_forced(tiny["dec"], wl.model, tiny["ids"], tiny["ref"]["codes"], wl.frames)
+    es, ea, n, ex = check_step_parity(wl.model, tiny["ref"], sem, ac, tok, 1e-4)
+    print(f"tiny: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}")
+
+
+def test_tiny_run_frames_greedy_matches_oracle_until_a_near_tie(tiny):
+    wl, dec, ref = tiny["wl"], tiny["dec"], tiny["ref"]
+    d = dev()
+    codes = torch.full((1, wl.frames + 8, 16), -1, dtype=torch.int32, device=d)
+    dec.prefill(torch.from_numpy(tiny["ids"]).to(d))
+    dec.run_frames(wl.frames, GREEDY, GREEDY, None, codes)
+    got = codes.cpu().numpy()[:, : wl.frames]
+    want = ref["codes"]
+    flat_g, flat_w = got.reshape(-1), want.reshape(-1)
+    diff = np.nonzero(flat_g != flat_w)[0]
+    if diff.size:
+        i = diff[0]
+        t, j = divmod(i, 16)
+        lg = ref["sem_logits"][0, t] if j == 0 else ref["ac_logits"][0, t, j - 1]
+        assert top2_margin(lg) <= 0.05, f"free-running divergence at frame {t} code {j} with margin {top2_margin(lg):.3f}"
+    assert dec.progress() == (wl.prefill_len + wl.frames, wl.frames)
+    print(f"tiny free-running: identical for {diff[0] if diff.size else flat_g.size} of {flat_g.size} codes")
+
+
+def test_tiny_graph_replay_equals_eager_and_is_deterministic(tiny):
+    wl, dec = tiny["wl"], tiny["dec"]
+    d = dev()
+    F = 6
+    ids = torch.from_numpy(tiny["ids"]).to(d)
+    u = torch.from_numpy(synth.random_uniforms((1, wl.frames + 8, 16), seed=9)).to(d)
+    for sem_cfg, ac_cfg in [(GREEDY, GREEDY), (SEM, AC)]:
+        runs = []
+        for _ in range(2):
+            codes = torch.zeros((1, wl.frames + 8, 16), dtype=torch.int32, device=d)
+            dec.prefill(ids)
+            dec.run_frames(F, sem_cfg, ac_cfg, u, codes)
+            torch.cuda.synchronize()
+            runs.append(codes.cpu().numpy()[:, :F])
+        np.testing.assert_array_equal(runs[0], runs[1])
+        # eager: the same frames through tts_sample / tts_codepred_frame / tts_talker_step
+        logits = torch.zeros((1, wl.model.talker.vocab), dtype=torch.float32, device=d)
+        hist = torch.zeros((1, wl.model.talker.vocab), dtype=torch.uint8, device=d)
+        s = torch.zeros((1,), dtype=torch.int32, device=d)
+        a = torch.zeros((1, 15), dtype=torch.int32, device=d)
+        eager = np.zeros((1, F, 16), np.int32)
+        dec.prefill(ids, logits)
+        for t in range(F):
+            dec.sample(logits, sem_cfg, u[:, t, 0].contiguous(), s, history=hist)
+            dec.codepred_frame(s, ac_cfg, u[:, t, 1:].contiguous(), a)
+            row = torch.cat([s.view(1, 1), a], dim=1).contiguous()
+            dec.talker_step(row, logits)
+            torch.cuda.synchronize()
+            eager[:, t] = row.cpu().numpy()
+        np.testing.assert_array_equal(eager, runs[0])
+
+
+def test_tiny_sampled_frames_teacher_forced(tiny):
+    """Sampling with the pages' controls, draws compared given the same uniforms."""
+    wl, orc, dec = tiny["wl"], tiny["orc"], tiny["dec"]
+    d = dev()
+    F = wl.frames
+    u = synth.random_uniforms((1, F, 16), seed=17)
+    ref = orc.generate(tiny["ids"], F, SEM, AC, u, sampler_dtype=np.float32)
+    codes = ref["codes"]
+    Vs, Va = wl.model.talker.vocab, wl.model.codepred.vocab
+    ud = torch.from_numpy(u).to(d)
+    logits = torch.zeros((1, Vs), dtype=torch.float32, device=d)
+    s = torch.zeros((1,), dtype=torch.int32, device=d)
+    own = torch.zeros((1, 15), dtype=torch.int32, device=d)
+    acl = torch.zeros((1, 15, Va), dtype=torch.float32, device=d)
+    hist_np = np.zeros((1, Vs), bool)
+    dec.prefill(torch.from_numpy(tiny["ids"]).to(d), logits)
+    checked = exempt = 0
+    for t in range(F):
+        if t > 0:
+            dec.talker_step(torch.from_numpy(codes[:, t - 1]).to(d).contiguous(), logits)
+        hist = torch.from_numpy(hist_np.astype(np.uint8)).to(d)
+        dec.sample(logits, SEM, ud[:, t, 0].contiguous(), s, history=hist)
+        dec.codepred_frame(torch.from_numpy(codes[:, t, 0]).to(d).contiguous(), AC, ud[:, t, 1:].contiguous(), own,
+                           forced=torch.from_numpy(codes[:, t, 1:]).to(d).contiguous(), logits=acl)
+        torch.cuda.synchronize()
+        lg = ref["sem_logits"][0, t]
+        if sample_exempt(lg, SEM, float(u[0, t, 0]), hist_np[0], rel=1e-4):
+            exempt += 1
+        else:
+            checked += 1
+            assert int(s.item()) == codes[0, t, 0], f"semantic draw differs at frame {t}"
+        got_ac = own.cpu().numpy()[0]
+        for j in range(15):
+            if sample_exempt(ref["ac_logits"][0, t, j], AC, float(u[0, t, 1 + j]), rel=1e-4):
+                exempt += 1
+            else:
+                checked += 1
+                assert got_ac[j] == codes[0, t, 1 + j], f"acoustic draw {j + 1} differs at frame {t}"
+        hist_np[0, codes[0, t, 0]] = True
+    assert checked > 0.9 * (checked + exempt)
+    print(f"tiny sampled: {checked} draws equal, {exempt} exempt")
+
+
+def test_tiny_split_attention_over_long_context():
+    """Positions past one 64-position attention split (ragged last split)."""
+    model = config.TINY
+    w = synth.make_weights(model, 3)
+    orc = OracleModel(w, model.as_dict(), np.float64)
+    ids = synth.random_ids(150, model.text_vocab, seed=4)
+    F = 5
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((1, F, 16), np.float32))
+    dec, _ = make_decoder(model, 1, 160, 8, w)
+    sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F)
+    check_step_parity(model, ref, sem, ac, tok, 1e-4)
+
+
+def test_tiny_batched_streams_are_independent():
+    """B lockstep streams: each equals its own single-stream run."""
+    model = config.TINY
+    w = synth.make_weights(model, 0)
+    orc = OracleModel(w, model.as_dict(), np.float64)
+    B, F = 3, 4
+    ids = synth.random_ids(20, model.text_vocab, seed=8, batch=B)
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((B, F, 16), np.float32))
+    dec, _ = make_decoder(model, B, 32, 8, w)
+    sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F)
+    check_step_parity(model, ref, sem, ac, tok, 1e-4)
+
+
+# ----------------------------------------------------------------------------- sampler
+
+@pytest.mark.parametrize("V", [3072, 2048, 512, 37])
+def test_sampler_on_uploaded_logits_matches_oracle(tiny, V):
+    dec = tiny["dec"]
+    d = dev()
+    B = 64
+    L = synth.random_logits((B, V), 2.0, seed=V)
+    u = synth.random_uniforms((B,), seed=V + 1)
+    hist = synth.random_uniforms((B, V), seed=V + 2) < 0.05
+    cfgs = [GREEDY, SEM, AC, dict(AC, top_p=0.8), dict(AC, top_k=0), dict(SEM, top_k=7, temperature=0.5)]
+    Ld, ud = torch.from_numpy(L).to(d), torch.from_numpy(u).to(d)
+    for cfg in cfgs:
+        out = torch.zeros((B,), dtype=torch.int32, device=d)
+        hd = torch.from_numpy(hist.astype(np.uint8)).to(d)
+        dec.sample(Ld, cfg, ud, out, history=hd)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        ex = 0
+        for b in range(B):
+            want = sample_token(L[b], cfg, float(u[b]), hist[b], dtype=np.float32)
+            if got[b] != want:
+                assert cfg["do_sample"] and sample_exempt(L[b], cfg, float(u[b]), hist[b], rel=1e-5), (cfg, b, got[b], want)
+                ex += 1
+        assert ex <= 2
+        # the drawn id is marked in the history
+        hn = hd.cpu().numpy()
+        assert all(hn[b, got[b]] == 1 for b in range(B))
+
+
+def test_sampler_greedy_ties_pick_the_lowest_id(tiny):
+    d = dev()
+    L = np.zeros((4, 300), np.float32)
+    L[0, [5, 9, 200]] = 3.0
+    L[1, :] = -1.0
+    L[2, 299] = 1.0
+    L[3, [0, 299]] = 2.0
+    out = torch.zeros((4,), dtype=torch.int32, device=d)
+    tiny["dec"].sample(torch.from_numpy(L).to(d), GREEDY, None, out)
+    torch.cuda.synchronize()
+    assert out.cpu().numpy().tolist() == [5, 0, 299, 0]
+
+
+# ----------------------------------------------------------------------------- error paths on a live context
+
+def test_error_paths_leave_the_context_usable(tiny):
+    wl = tiny["wl"]
+    d = dev()
+    dec = tts.TTSDecoder(wl.model, 1, 40, 4)
+    codes = torch.zeros((1, 16), dtype=torch.int32, device=d)
+    with pytest.raises(tts.TTSError) as e:
+        dec.talker_step(codes)
+    assert e.value.code == tts.TTS_E_STATE
+    with pytest.raises(tts.TTSError) as e:
+        dec.prefill(torch.zeros((1, 4), dtype=torch.int32, device=d))
+    assert e.value.code == tts.TTS_E_STATE  # no weights yet
+    bad = dict(tiny["dw"])
+    bad["talker.lm_head"] = bad["talker.lm_head"][:-1].contiguous()
+    with pytest.raises(tts.TTSError) as e:
+        dec.load_weights(bad)
+    assert e.value.code == tts.TTS_E_SHAPE
+    missing = {k: v for k, v in tiny["dw"].items() if k != "cp.heads"}
+    with pytest.raises(tts.TTSError) as e:
+        dec.load_weights(missing)
+    assert e.value.code == tts.TTS_E_SHAPE
+    dec.load_weights(tiny["dw"])
+    with pytest.raises(tts.TTSError) as e:
+        dec.prefill(torch.zeros((1, 41), dtype=torch.int32, device=d))
+    assert e.value.code == tts.TTS_E_CAPACITY
+    with pytest.raises(tts.TTSError) as e:
+        dec.prefill(torch.zeros((2, 4), dtype=torch.int32, device=d))
+    assert e.value.code == tts.TTS_E_ARG
+    dec.prefill(torch.zeros((1, 30), dtype=torch.int32, device=d))
+    fr = torch.zeros((1, 4, 16), dtype=torch.int32, device=d)
+    with pytest.raises(tts.TTSError) as e:
+        dec.run_frames(5, GREEDY, GREEDY, None, fr)
+    assert e.value.code == tts.TTS_E_CAPACITY
+    with pytest.raises(tts.TTSError) as e:
+        dec.run_frames(1, dict(SEM, temperature=0.0), GREEDY, torch.zeros((1, 4, 16), device=d), fr)
+    assert e.value.code == tts.TTS_E_ARG
+    with pytest.raises(tts.TTSError) as e:
+        dec.run_frames(1, SEM, GREEDY, None, fr)
+    assert e.value.code == tts.TTS_E_ARG
+    dec.run_frames(4, GREEDY, GREEDY, None, fr)
+    assert dec.progress() == (34, 4)
+    with pytest.raises(tts.TTSError) as e:
+        dec.run_frames(1, GREEDY, GREEDY, None, fr)
+    assert e.value.code == tts.TTS_E_CAPACITY
+    torch.cuda.synchronize()
+    assert fr.cpu().numpy().max() < wl.model.codepred.vocab
+    dec.reset()
+    assert dec.progress() == (0, 0)
+    dec.close()
+
+
+# ----------------------------------------------------------------------------- bf16 models
+
+@pytest.fixture(scope="module", params=["0.6b", "1.7b"])
+def bf16_model(request):
+    model = config.MODELS[request.param]
+    w = synth.make_weights(model, 0)
+    return request.param, model, w
+
+
+def test_bf16_teacher_forced_step_parity(bf16_model):
+    name, model, w = bf16_model
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    ids = synth.random_ids(16, model.text_vocab, seed=1)
+    F = 3
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((1, F, 16), np.float32))
+    del orc
+    dec, dw = make_decoder(model, 1, 64 + 240, 240, w)
+    sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F)
+    es, ea, n, ex = check_step_parity(model, ref, sem, ac, tok, 1e-2)
+    print(f"{name}: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}")
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
+def test_1p7b_long_context_logits_at_2255_positions():
+    """Full long-utterance length: 2255 positions through the split attention.
+    The oracle computes the last position by the cache-free whole-sequence pass."""
+    model = config.M17B
+    w = synth.make_weights(model, 0)
+    n = 2255
+    print("long context: weights ready", flush=True)
+    ids = synth.random_ids(n, model.text_vocab, seed=5)
+    dec, dw = make_decoder(model, 1, n + 1, 4, w)
+    d = dev()
+    got = torch.zeros((1, model.talker.vocab), dtype=torch.float32, device=d)
+    dec.prefill(torch.from_numpy(ids).to(d), got)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+    print("long context: GPU prefill done; oracle whole-sequence pass", flush=True)
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    X = orc.embed_text[ids[0]][None]
+    hT = orc.full_forward("talker", X)[:, -1]
+    ref = linear(hT, orc.lm_head)
+    err = rowwise_rel_err(got, ref).max()
+    assert err <= 1e-2, err
+    if top2_margin(ref[0]) > 0.05:
+        assert int(np.argmax(got[0])) == int(np.argmax(ref[0]))
+    print(f"1.7b at 2255 positions: rel err {err:.2e}")

@@ -26,9 +26,9 @@ using namespace tts;
 namespace {
 
 constexpr int kCpPositions = 16;   // CodePredictor positions 0..15 per frame
-constexpr int kAttnChunk = 64;     // Talker positions per attention split
+constexpr int kAttnChunk = 32;     // Talker positions per attention split
 constexpr int kMaxGemvM = 8;       // input rows per GEMV launch
-constexpr size_t kGemvLds = 48 * 1024;
+constexpr int kGemvXRegs = 96;     // per-lane registers a GEMV spends on its input rows (M * U * E)
 
 struct Layer {
   const void *attn_norm = nullptr, *wq = nullptr, *wk = nullptr, *wv = nullptr, *q_norm = nullptr, *k_norm = nullptr;
@@ -56,8 +56,8 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Workspace layout, computed identically by tts_workspace_bytes and tts_create.
 struct Layout {
-  size_t st, tk, tv, ck, cv, tcos, tsin, ccos, csin, x, qkv, attn, h, part, logits, hT, cx, clog, next_tok, sem_tok,
-      ac_codes, history, total;
+  size_t st, tk, tv, ck, cv, tcos, tsin, ccos, csin, x, qkv, attn, h, part, counters, logits, hT, cx, clog, next_tok,
+      sem_tok, ac_codes, history, total;
   int nsplit;
 };
 
@@ -90,6 +90,7 @@ Layout make_layout(const tts_config& c) {
   L.attn = take(rows * std::max((size_t)t.n_q_heads * t.head_dim, (size_t)p.n_q_heads * p.head_dim) * 4);
   L.h = take(rows * std::max(t.ffn, p.ffn) * 4);
   L.part = take(B * t.n_q_heads * (size_t)L.nsplit * (t.head_dim + 2) * 4);
+  L.counters = take(B * t.n_kv_heads * 4);
   L.logits = take(B * t.vocab * 4);
   L.hT = take(B * t.hidden * 4);
   L.cx = take(rows * hmax * 4);
@@ -156,6 +157,7 @@ struct tts_ctx {
   // workspace views
   DevState* st = nullptr;
   float *x = nullptr, *qkv = nullptr, *attn = nullptr, *h = nullptr, *part = nullptr, *logits = nullptr, *hT = nullptr;
+  int32_t* counters = nullptr;
   float *cx = nullptr, *clog = nullptr;
   float *tcos = nullptr, *tsin = nullptr, *ccos = nullptr, *csin = nullptr;
   int32_t *next_tok = nullptr, *sem_tok = nullptr, *ac_codes = nullptr;
@@ -207,56 +209,64 @@ namespace {
 
 // ---------------------------------------------------------------------------- GEMV dispatch
 
-template <typename WT, int U, int M, bool PAIR>
+template <typename WT, int U, int M, bool PAIR, bool NORM>
 int launch_gemv_t(tts_ctx* ctx, const GemvArgs& a) {
-  // only instantiate row counts whose staged input fits the LDS budget
-  if constexpr ((size_t)M * U * 64 * WTraits<WT>::E * 4 > kGemvLds) {
-    return ctx->fail(TTS_E_UNSUPPORTED, "gemv: M=%d with K=%d exceeds the LDS budget", M, a.K);
+  // only instantiate row counts whose input slices fit the register budget
+  if constexpr (M * U * WTraits<WT>::E > kGemvXRegs) {
+    return ctx->fail(TTS_E_UNSUPPORTED, "gemv: M=%d with K=%d exceeds the register budget", M, a.K);
   } else {
-  constexpr int RW = GemvShape<U, PAIR>::RW;
-  const int rows_per_block = 4 * RW;
-  const int blocks = (a.N + rows_per_block - 1) / rows_per_block;
-  const size_t lds = (size_t)M * a.K * 4;
-  hipLaunchKernelGGL((k_gemv<WT, U, M, PAIR>), dim3(blocks), dim3(256), lds, ctx->stream, a);
-  HIP_LAUNCH_CHECK();
-  return TTS_OK;
+    constexpr int RW = GemvShape<U, PAIR>::RW;
+    const int rows_per_block = 4 * RW;
+    const int blocks = (a.N + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL((k_gemv<WT, U, M, PAIR, NORM>), dim3(blocks), dim3(256), 0, ctx->stream, a);
+    HIP_LAUNCH_CHECK();
+    return TTS_OK;
   }
 }
 
-template <typename WT, int U, bool PAIR>
+template <typename WT, int U, bool PAIR, bool NORM>
 int launch_gemv_m(tts_ctx* ctx, const GemvArgs& a) {
   switch (a.M) {
-    case 1: return launch_gemv_t<WT, U, 1, PAIR>(ctx, a);
-    case 2: return launch_gemv_t<WT, U, 2, PAIR>(ctx, a);
-    case 4: return launch_gemv_t<WT, U, 4, PAIR>(ctx, a);
-    case 8: return launch_gemv_t<WT, U, 8, PAIR>(ctx, a);
+    case 1: return launch_gemv_t<WT, U, 1, PAIR, NORM>(ctx, a);
+    case 2: return launch_gemv_t<WT, U, 2, PAIR, NORM>(ctx, a);
+    case 4: return launch_gemv_t<WT, U, 4, PAIR, NORM>(ctx, a);
+    case 8: return launch_gemv_t<WT, U, 8, PAIR, NORM>(ctx, a);
     default: return ctx->fail(TTS_E_UNSUPPORTED, "gemv: M=%d", a.M);
   }
 }
 
-template <typename WT, bool PAIR>
+template <typename WT, bool PAIR, bool NORM>
 int launch_gemv_u(tts_ctx* ctx, const GemvArgs& a) {
   int U = 0;
   if (!units_ok(a.K, WTraits<WT>::E, &U)) return ctx->fail(TTS_E_SHAPE, "gemv: K=%d", a.K);
   switch (U) {
-    case 1: return launch_gemv_m<WT, 1, PAIR>(ctx, a);
-    case 2: return launch_gemv_m<WT, 2, PAIR>(ctx, a);
-    case 3: return launch_gemv_m<WT, 3, PAIR>(ctx, a);
-    case 4: return launch_gemv_m<WT, 4, PAIR>(ctx, a);
-    case 6: return launch_gemv_m<WT, 6, PAIR>(ctx, a);
-    case 8: return launch_gemv_m<WT, 8, PAIR>(ctx, a);
-    case 12: return launch_gemv_m<WT, 12, PAIR>(ctx, a);
-    case 16: return launch_gemv_m<WT, 16, PAIR>(ctx, a);
+    case 1: return launch_gemv_m<WT, 1, PAIR, NORM>(ctx, a);
+    case 2: return launch_gemv_m<WT, 2, PAIR, NORM>(ctx, a);
+    case 3: return launch_gemv_m<WT, 3, PAIR, NORM>(ctx, a);
+    case 4: return launch_gemv_m<WT, 4, PAIR, NORM>(ctx, a);
+    case 6: return launch_gemv_m<WT, 6, PAIR, NORM>(ctx, a);
+    case 8: return launch_gemv_m<WT, 8, PAIR, NORM>(ctx, a);
+    case 12: return launch_gemv_m<WT, 12, PAIR, NORM>(ctx, a);
+    case 16: return launch_gemv_m<WT, 16, PAIR, NORM>(ctx, a);
   }
   return ctx->fail(TTS_E_SHAPE, "gemv: K=%d", a.K);
 }
 
-// Launch a GEMV over M input rows, chunked so that each launch stages at most
-// kMaxGemvM rows and 64 KB of input in LDS. Chunks re-stream the weights.
+template <typename WT>
+int launch_gemv_w(tts_ctx* ctx, const GemvArgs& a) {
+  const bool pair = a.epi == EPI_SWIGLU, norm = a.gain != nullptr;
+  if (pair) return norm ? launch_gemv_u<WT, true, true>(ctx, a) : launch_gemv_u<WT, true, false>(ctx, a);
+  return norm ? launch_gemv_u<WT, false, true>(ctx, a) : launch_gemv_u<WT, false, false>(ctx, a);
+}
+
+// Launch a GEMV over M input rows, chunked so that each launch holds at most
+// kGemvXRegs input elements per lane. Chunks re-stream the weights.
 int gemv(tts_ctx* ctx, GemvArgs a) {
   const int Mtot = a.M;
+  const int E = ctx->bf16() ? 8 : 4;
+  const int U = a.K / (64 * E);
   int chunk = kMaxGemvM;
-  while (chunk > 1 && (size_t)chunk * a.K * 4 > kGemvLds) chunk >>= 1;
+  while (chunk > 1 && chunk * U * E > kGemvXRegs) chunk >>= 1;
   if (a.src == SRC_VEC_THEN_TABLE && chunk < 2) return ctx->fail(TTS_E_SHAPE, "gemv: K=%d too large for paired rows", a.K);
   for (int m0 = 0; m0 < Mtot;) {
     int mc = std::min(chunk, Mtot - m0);
@@ -274,10 +284,8 @@ int gemv(tts_ctx* ctx, GemvArgs a) {
     c.y = a.y + (size_t)m0 * a.y_stride;
     if (a.res) c.res = a.res + (size_t)m0 * a.res_stride;
     if (a.xn_out) c.xn_out = a.xn_out + (size_t)m0 * a.xn_stride;
-    int rc;
-    const bool pair = a.epi == EPI_SWIGLU;
-    if (ctx->bf16()) rc = pair ? launch_gemv_u<uint16_t, true>(ctx, c) : launch_gemv_u<uint16_t, false>(ctx, c);
-    else rc = pair ? launch_gemv_u<float, true>(ctx, c) : launch_gemv_u<float, false>(ctx, c);
+    if (m0 + mc < Mtot) c.bump_pos = c.bump_frame = 0;  // counters advance once, with the last chunk
+    const int rc = ctx->bf16() ? launch_gemv_w<uint16_t>(ctx, c) : launch_gemv_w<float>(ctx, c);
     if (rc) return rc;
     m0 += mc;
   }
@@ -375,16 +383,8 @@ int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_c
     t.pos_const = pos_const; t.pos_from_state = pos_from_state;
     t.kc = (char*)kc + l * layer_cache; t.vc = (char*)vc + l * layer_cache;
     t.cap = cap; t.chunk = nsplit == 1 ? cap : kAttnChunk; t.nsplit = nsplit;
-    t.out = ctx->attn; t.out_stride = qd; t.part = ctx->part; t.st = ctx->st;
+    t.out = ctx->attn; t.out_stride = qd; t.part = ctx->part; t.counters = ctx->counters; t.st = ctx->st;
     if (int rc_ = attention(ctx, t, B)) return rc_;
-    if (nsplit > 1) {
-      MergeArgs mg;
-      mg.part = ctx->part; mg.nq = c.n_q_heads; mg.d = c.head_dim; mg.nsplit = nsplit; mg.chunk = kAttnChunk;
-      mg.M = Mp; mg.pos_const = pos_const; mg.pos_from_state = pos_from_state;
-      mg.out = ctx->attn; mg.out_stride = qd; mg.st = ctx->st;
-      hipLaunchKernelGGL(k_attn_merge, dim3(c.n_q_heads, rows), dim3(c.head_dim), 0, ctx->stream, mg);
-      HIP_LAUNCH_CHECK();
-    }
     // O projection + residual
     a = gemv_args(ctx);
     a.w[0] = W.wo; a.seg_rows[0] = c.hidden; a.N = c.hidden; a.K = qd; a.M = rows;
@@ -410,9 +410,10 @@ int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_c
 
 // Talker final norm + semantic head: logits = W_lm RMSNorm(x); the normed
 // hidden (h_T, which conditions the CodePredictor) is written as well.
-int talker_head(tts_ctx* ctx, int B) {
+int talker_head(tts_ctx* ctx, int B, int bump_pos, int bump_frame) {
   const auto& t = ctx->cfg.talker;
   GemvArgs a = gemv_args(ctx);
+  a.bump_pos = bump_pos; a.bump_frame = bump_frame;
   a.w[0] = ctx->lm_head; a.seg_rows[0] = t.vocab; a.N = t.vocab; a.K = t.hidden; a.M = B;
   a.src = SRC_VEC; a.x = ctx->x; a.x_stride = t.hidden; a.gain = ctx->talker.final_norm;
   a.y = ctx->logits; a.y_stride = t.vocab; a.epi = EPI_STORE;
@@ -580,10 +581,8 @@ int enqueue_frame(tts_ctx* ctx, const tts_sampling& sem, const tts_sampling& ac,
   for (int j = 0; j < 16; ++j) refs[j] = tokref(codes, fs, 16, j, 1);
   if (int rc = embed_sum(ctx, B, refs)) return rc;
   if (int rc = talker_stack(ctx, B, 0, 1)) return rc;
-  if (int rc = talker_head(ctx, B)) return rc;
-  hipLaunchKernelGGL(k_bump, dim3(1), dim3(64), 0, ctx->stream, ctx->st, 1, 1);
-  HIP_LAUNCH_CHECK();
-  return TTS_OK;
+  // the frame's last kernel also advances the device position and frame counters
+  return talker_head(ctx, B, 1, 1);
 }
 
 void drop_graph(tts_ctx* ctx) {
@@ -626,6 +625,7 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
   ctx->st = (DevState*)(w + L.st);
   ctx->x = (float*)(w + L.x); ctx->qkv = (float*)(w + L.qkv); ctx->attn = (float*)(w + L.attn); ctx->h = (float*)(w + L.h);
   ctx->part = (float*)(w + L.part); ctx->logits = (float*)(w + L.logits); ctx->hT = (float*)(w + L.hT);
+  ctx->counters = (int32_t*)(w + L.counters);
   ctx->cx = (float*)(w + L.cx); ctx->clog = (float*)(w + L.clog);
   ctx->tcos = (float*)(w + L.tcos); ctx->tsin = (float*)(w + L.tsin); ctx->ccos = (float*)(w + L.ccos); ctx->csin = (float*)(w + L.csin);
   ctx->next_tok = (int32_t*)(w + L.next_tok); ctx->sem_tok = (int32_t*)(w + L.sem_tok); ctx->ac_codes = (int32_t*)(w + L.ac_codes);
@@ -642,6 +642,8 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
   hipError_t e4 = hipMemcpy(ctx->csin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice);
   if (e1 || e2 || e3 || e4) { delete ctx; return TTS_E_HIP; }
   hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, 0, 0);
+  hipLaunchKernelGGL(k_fill_u8, dim3(1), dim3(256), 0, ctx->stream, (uint8_t*)ctx->counters,
+                     (size_t)cfg->max_batch * cfg->talker.n_kv_heads * 4, (uint8_t)0);
   if (hipGetLastError() != hipSuccess) { delete ctx; return TTS_E_HIP; }
   *out = ctx;
   return TTS_OK;
@@ -738,7 +740,7 @@ int tts_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, floa
       return rc;
     if (int rc = talker_stack(ctx, batch, p, 0)) return rc;
   }
-  if (int rc = talker_head(ctx, batch)) return rc;
+  if (int rc = talker_head(ctx, batch, 0, 0)) return rc;
   hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, n, 0);
   HIP_LAUNCH_CHECK();
   if (sem_logits)
@@ -761,9 +763,7 @@ int tts_talker_step(tts_ctx* ctx, const int32_t* prev_codes, float* sem_logits) 
   for (int j = 0; j < 16; ++j) refs[j] = tokref(prev_codes, 16, 0, j, 0);
   if (int rc = embed_sum(ctx, B, refs)) return rc;
   if (int rc = talker_stack(ctx, B, 0, 1)) return rc;
-  if (int rc = talker_head(ctx, B)) return rc;
-  hipLaunchKernelGGL(k_bump, dim3(1), dim3(64), 0, ctx->stream, ctx->st, 1, 0);
-  HIP_LAUNCH_CHECK();
+  if (int rc = talker_head(ctx, B, 1, 0)) return rc;
   if (sem_logits)
     HIP_TRY(hipMemcpyAsync(sem_logits, ctx->logits, (size_t)B * ctx->cfg.talker.vocab * 4, hipMemcpyDeviceToDevice, ctx->stream));
   ctx->pos += 1;

@@ -140,17 +140,18 @@ struct GemvArgs {
   const void* table;        // embedding table [table_rows, K] (weight dtype) for gathered rows
   int32_t table_rows;
   TokRef tok;               // token of gathered row (indexed by stream)
-  const void* gain;         // RMSNorm gain [K] (weight dtype) or nullptr
+  const void* gain;         // RMSNorm gain [K] (weight dtype); used by the NORM variants
   float eps;
   float* y;
   int32_t y_stride;
   const float* res;         // residual rows (EPI_RESID); may alias y
   int32_t res_stride;
   int32_t epi;              // enum Epi
-  float* xn_out;            // optional: block 0 writes the normalised input rows here
+  float* xn_out;            // optional: wave 0 writes the normalised input rows here
   int32_t xn_stride;
   int32_t nontemporal;      // stream the weights past the caches (read once per frame)
-  const DevState* st;
+  int32_t bump_pos, bump_frame;  // added to the device counters by block 0 (it reads no counter)
+  DevState* st;
 };
 
 // Rows each wave streams, by units per row U (a unit = one 16-byte load per lane).
@@ -159,65 +160,27 @@ template <int U, bool PAIR> struct GemvShape {
   static constexpr int RW = RW0 < 1 ? 1 : (RW0 > 4 ? 4 : RW0);
 };
 
-// Load input row m (fp32 or gathered from a table) element k.. into LDS, with
-// the optional RMSNorm applied. One block stages all M rows.
-template <typename WT, int M>
-__device__ __forceinline__ void gemv_stage_input(const GemvArgs& a, float* xs) {
-  const int tid = threadIdx.x;
-  const int K = a.K;
-  __shared__ float red[M][4];
-  __shared__ float scale[M];
-  float ss[M];
+// E consecutive input elements of row m at element k0, as fp32.
+template <typename WT, int E>
+__device__ __forceinline__ void gemv_load_x(const GemvArgs& a, int m, int k0, float (&f)[E]) {
+  const int stream = (a.src == SRC_VEC_THEN_TABLE) ? (m >> 1) : m;
+  const bool from_table = (a.src == SRC_TABLE) || (a.src == SRC_VEC_THEN_TABLE && (m & 1));
+  if (from_table) {
+    const int t = clamp_tok(tok_at(a.tok, a.st, stream), a.table_rows);
+    const WT* tp = reinterpret_cast<const WT*>(a.table) + (size_t)t * a.K + k0;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(tp);
+    float g[8];
+    unpack(w, g, (WT*)nullptr);
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    ss[m] = 0.f;
-    const int stream = (a.src == SRC_VEC_THEN_TABLE) ? (m >> 1) : m;
-    const bool from_table = (a.src == SRC_TABLE) || (a.src == SRC_VEC_THEN_TABLE && (m & 1));
-    const float* xv = nullptr;
-    const WT* tv = nullptr;
-    if (from_table) {
-      const int t = clamp_tok(tok_at(a.tok, a.st, stream), a.table_rows);
-      tv = reinterpret_cast<const WT*>(a.table) + (size_t)t * K;
-    } else {
-      xv = a.x + (size_t)((a.src == SRC_VEC_THEN_TABLE) ? stream : m) * a.x_stride;
-    }
-    for (int k = tid * 4; k < K; k += 256 * 4) {
-      float v0, v1, v2, v3;
-      if (from_table) {
-        v0 = to_f32(tv[k]); v1 = to_f32(tv[k + 1]); v2 = to_f32(tv[k + 2]); v3 = to_f32(tv[k + 3]);
-      } else {
-        float4 f = *reinterpret_cast<const float4*>(xv + k);
-        v0 = f.x; v1 = f.y; v2 = f.z; v3 = f.w;
-      }
-      ss[m] += v0 * v0 + v1 * v1 + v2 * v2 + v3 * v3;
-      *reinterpret_cast<float4*>(xs + m * K + k) = make_float4(v0, v1, v2, v3);
+    for (int e = 0; e < E; ++e) f[e] = g[e];
+  } else {
+    const float* xp = a.x + (size_t)((a.src == SRC_VEC_THEN_TABLE) ? stream : m) * a.x_stride + k0;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(xp + e);
+      f[e] = v.x; f[e + 1] = v.y; f[e + 2] = v.z; f[e + 3] = v.w;
     }
   }
-  if (a.gain) {
-    const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float s = wave_sum(ss[m]);
-      if (lane == 0) red[m][wave] = s;
-    }
-    __syncthreads();
-    if (tid < M) {
-      float s = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
-      scale[tid] = 1.0f / sqrtf(s / (float)K + a.eps);
-    }
-    __syncthreads();
-    const WT* g = reinterpret_cast<const WT*>(a.gain);
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float sc = scale[m];
-      for (int k = tid; k < K; k += 256) {
-        float v = xs[m * K + k] * sc * to_f32(g[k]);
-        xs[m * K + k] = v;
-        if (a.xn_out && blockIdx.x == 0) a.xn_out[(size_t)m * a.xn_stride + k] = v;
-      }
-    }
-  }
-  __syncthreads();
 }
 
 template <typename WT>
@@ -230,26 +193,46 @@ __device__ __forceinline__ const WT* gemv_row_ptr(const GemvArgs& a, int row) {
   return reinterpret_cast<const WT*>(a.w[s]) + (size_t)(row - off) * a.K;
 }
 
-// One wave streams RW rows (PAIR: RW gate rows + RW up rows) of U units each.
-template <typename WT, int U, int M, bool PAIR>
+// y = W x for M input rows. Every wave is independent: it loads its lanes'
+// slice of each input row (and of the norm gain), then streams RW weight rows
+// (PAIR: RW gate rows and RW up rows) with all loads in flight, reduces each
+// row across the wave with DPP and applies the epilogue. No LDS, no barriers.
+template <typename WT, int U, int M, bool PAIR, bool NORM>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   constexpr int E = WTraits<WT>::E;
   constexpr int CH = 64 * E;
   constexpr int RW = GemvShape<U, PAIR>::RW;
-  constexpr int NR = PAIR ? 2 * RW : RW;  // weight rows per wave
-  extern __shared__ float xs[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r0 = (blockIdx.x * 4 + wave) * RW;
+  constexpr int NR = PAIR ? 2 * RW : RW;
+  const int lane = threadIdx.x & 63;
+  const int wave_id = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int r0 = wave_id * RW;
+  if (r0 >= a.N) return;
 
-  // 1. issue every weight load of this wave
+  // 1. input slices first, so that waiting for them does not queue behind the weights
+  float xv[M][U][E];
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+#pragma unroll
+    for (int c = 0; c < U; ++c) gemv_load_x<WT, E>(a, m, c * CH + lane * E, xv[m][c]);
+  float gv[NORM ? U : 1][E];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int c = 0; c < U; ++c) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const WT*>(a.gain) + c * CH + lane * E);
+      float g[8];
+      unpack(w, g, (WT*)nullptr);
+#pragma unroll
+      for (int e = 0; e < E; ++e) gv[c][e] = g[e];
+    }
+  }
+
+  // 2. every weight load of this wave
   u32x4 wb[NR][U];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     int row = r0 + (PAIR ? (r % RW) : r);
     if (row > a.N - 1) row = a.N - 1;
-    const WT* wp;
-    if (PAIR) wp = reinterpret_cast<const WT*>(a.w[r / RW]) + (size_t)row * a.K;
-    else wp = gemv_row_ptr<WT>(a, row);
+    const WT* wp = PAIR ? reinterpret_cast<const WT*>(a.w[r / RW]) + (size_t)row * a.K : gemv_row_ptr<WT>(a, row);
     const u32x4* p = reinterpret_cast<const u32x4*>(wp) + lane;
     if (a.nontemporal) {
 #pragma unroll
@@ -260,10 +243,31 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
   }
 
-  // 2. stage (and normalise) the input rows in LDS while the weights stream
-  gemv_stage_input<WT, M>(a, xs);
+  // 3. RMSNorm of the input rows (wave-local)
+  if constexpr (NORM) {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float ss = 0.f;
+#pragma unroll
+      for (int c = 0; c < U; ++c)
+#pragma unroll
+        for (int e = 0; e < E; ++e) ss += xv[m][c][e] * xv[m][c][e];
+      ss = wave_sum(ss);
+      const float sc = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+#pragma unroll
+      for (int c = 0; c < U; ++c)
+#pragma unroll
+        for (int e = 0; e < E; ++e) xv[m][c][e] = xv[m][c][e] * sc * gv[c][e];
+      if (a.xn_out && wave_id == 0) {
+#pragma unroll
+        for (int c = 0; c < U; ++c)
+#pragma unroll
+          for (int e = 0; e < E; ++e) a.xn_out[(size_t)m * a.xn_stride + c * CH + lane * E + e] = xv[m][c][e];
+      }
+    }
+  }
 
-  // 3. dot products
+  // 4. dot products
   float acc[NR][M];
 #pragma unroll
   for (int r = 0; r < NR; ++r)
@@ -272,27 +276,20 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
   for (int c = 0; c < U; ++c) {
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float xv[E];
-      const float* xp = xs + m * a.K + c * CH + lane * E;
+    for (int r = 0; r < NR; ++r) {
+      float wf[8];
+      unpack(wb[r][c], wf, (WT*)nullptr);
 #pragma unroll
-      for (int e = 0; e < E; e += 4) {
-        float4 f = *reinterpret_cast<const float4*>(xp + e);
-        xv[e] = f.x; xv[e + 1] = f.y; xv[e + 2] = f.z; xv[e + 3] = f.w;
-      }
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        float wf[8];
-        unpack(wb[r][c], wf, (WT*)nullptr);
+      for (int m = 0; m < M; ++m) {
         float s = acc[r][m];
 #pragma unroll
-        for (int e = 0; e < E; ++e) s = fmaf(wf[e], xv[e], s);
+        for (int e = 0; e < E; ++e) s = fmaf(wf[e], xv[m][c][e], s);
         acc[r][m] = s;
       }
     }
   }
 
-  // 4. reduce and write
+  // 5. reduce and write
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int row = r0 + r;
@@ -300,7 +297,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     for (int m = 0; m < M; ++m) {
       float v = wave_sum(acc[r][m]);
       if (PAIR) {
-        float u = wave_sum(acc[RW + r][m]);
+        const float u = wave_sum(acc[RW + r][m]);
         v = silu(v) * u;
       }
       if (lane == 0 && row < a.N) {
@@ -309,6 +306,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         *yp = v;
       }
     }
+  }
+  if ((a.bump_pos | a.bump_frame) && wave_id == 0 && lane == 0) {
+    a.st->pos += a.bump_pos;
+    a.st->frame += a.bump_frame;
   }
 }
 
@@ -388,6 +389,7 @@ struct AttnArgs {
   float* out;               // nsplit == 1: [rows][nq*d]
   int32_t out_stride;
   float* part;              // nsplit > 1: [rows][nq][nsplit][d + 2] = (o[d], m, l)
+  int32_t* counters;        // nsplit > 1: [B][nkv] arrival counters, zero between uses
   const DevState* st;
 };
 
@@ -417,11 +419,12 @@ __device__ __forceinline__ void load_row(const float* p, float (&f)[EPL]) {
   }
 }
 
-constexpr int kAttnMaxD = 256;
-
 // grid (nsplit, nkv, B), 256 threads. G query heads share a KV head; M new
 // positions per stream; D = head_dim; each 16-lane group holds D/16
-// elements per lane and walks positions s0+grp, s0+grp+16, ...
+// elements per lane and walks positions s0+grp, s0+grp+16, ... of its split.
+// With several splits, every block writes an unnormalised partial
+// (o, max, sum) and the last block to arrive for a (stream, KV head) merges
+// them (device-scope fences around an arrival counter), so no merge kernel.
 template <typename WT, typename KT, int G, int M, int D>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   constexpr int EPL = D / 16;
@@ -431,8 +434,9 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int p0 = a.pos_from_state ? a.st->pos : a.pos_const;
   const int plast = p0 + M - 1;
   const int s0 = split * a.chunk;
-  if (s0 > plast) return;  // nothing to attend in this split (the merge ignores it)
+  if (s0 > plast) return;  // nothing to attend in this split; not counted by the merge
   const int s1 = min(s0 + a.chunk, plast + 1);
+  const int used = min(a.nsplit, plast / a.chunk + 1);
   const int row0 = b * M;
 
   __shared__ float qs[M][G][D];
@@ -531,85 +535,84 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     }
   }
 
-  // 3. combine the 16 groups in fixed order, then write the output or the partial
-  __shared__ float gm[16][M][G], gl[16][M][G];
-  __shared__ float ocomb[M][G][D];
-  __shared__ float mtot[M][G], ltot[M][G];
-  if (gl16 == 0) {
+  // 3. combine: the 4 groups of a wave through lane exchanges (fixed order),
+  //    then the 4 waves through LDS.
+  __shared__ float wo[4][M][G][D];
+  __shared__ float wm[4][M][G], wl[4][M][G];
 #pragma unroll
-    for (int m = 0; m < M; ++m)
+  for (int m = 0; m < M; ++m)
 #pragma unroll
-      for (int h = 0; h < G; ++h) { gm[grp][m][h] = mrun[m][h]; gl[grp][m][h] = lrun[m][h]; }
-  }
-  for (int i = tid; i < M * G * D; i += 256) (&ocomb[0][0][0])[i] = 0.f;
+    for (int h = 0; h < G; ++h) {
+      const float m1 = fmaxf(mrun[m][h], __shfl_xor(mrun[m][h], 16));
+      const float mw = fmaxf(m1, __shfl_xor(m1, 32));
+      const float w = (mrun[m][h] == -INFINITY) ? 0.f : expf(mrun[m][h] - mw);
+      float l = lrun[m][h] * w;
+      l += __shfl_xor(l, 16);
+      l += __shfl_xor(l, 32);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float x = o[m][h][e] * w;
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        if (lane < 16) wo[wave][m][h][gl16 * EPL + e] = x;
+      }
+      if (lane == 0) { wm[wave][m][h] = mw; wl[wave][m][h] = l; }
+    }
   __syncthreads();
-  if (tid < M * G) {
-    const int m = tid / G, h = tid % G;
+  for (int i = tid; i < M * G * D; i += 256) {
+    const int m = i / (G * D), h = (i / D) % G, e = i % D;
     float mx = -INFINITY;
-    for (int q = 0; q < 16; ++q) mx = fmaxf(mx, gm[q][m][h]);
-    float l = 0.f;
-    for (int q = 0; q < 16; ++q) {
-      const float w = (gm[q][m][h] == -INFINITY) ? 0.f : expf(gm[q][m][h] - mx);
-      gm[q][m][h] = w;
-      l += gl[q][m][h] * w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mx = fmaxf(mx, wm[q][m][h]);
+    float l = 0.f, acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float w = (wm[q][m][h] == -INFINITY) ? 0.f : expf(wm[q][m][h] - mx);
+      l += wl[q][m][h] * w;
+      acc += wo[q][m][h][e] * w;
     }
-    mtot[m][h] = mx;
-    ltot[m][h] = l;
+    const int qh = g * G + h;
+    const int row = row0 + m;
+    if (a.nsplit == 1) {
+      a.out[(size_t)row * a.out_stride + (size_t)qh * D + e] = l > 0.f ? acc / l : 0.f;
+    } else {
+      float* pp = a.part + (((size_t)row * a.nq + qh) * a.nsplit + split) * (D + 2);
+      pp[e] = acc;
+      if (e == 0) { pp[D] = mx; pp[D + 1] = l; }
+    }
+  }
+  if (a.nsplit == 1) return;
+
+  // 4. the last split block of this (stream, KV head) merges the partials
+  __shared__ int last;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    int* cnt = a.counters + (size_t)b * a.nkv + g;
+    const int old = atomicAdd(cnt, 1);
+    last = (old == used - 1);
+    if (last) *cnt = 0;  // every arrival has been counted; ready for the next use
   }
   __syncthreads();
-  for (int q = 0; q < 16; ++q) {
-    if (grp == q) {
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float w = gm[q][m][h];
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) ocomb[m][h][gl16 * EPL + e] += w * o[m][h][e];
-        }
-    }
-    __syncthreads();
-  }
+  if (!last) return;
+  __threadfence();
   for (int i = tid; i < M * G * D; i += 256) {
     const int m = i / (G * D), h = (i / D) % G, e = i % D;
     const int qh = g * G + h;
     const int row = row0 + m;
-    if (a.nsplit == 1) {
-      const float l = ltot[m][h];
-      a.out[(size_t)row * a.out_stride + (size_t)qh * D + e] = l > 0.f ? ocomb[m][h][e] / l : 0.f;
-    } else {
-      float* pp = a.part + (((size_t)row * a.nq + qh) * a.nsplit + split) * (D + 2);
-      pp[e] = ocomb[m][h][e];
-      if (e == 0) { pp[D] = mtot[m][h]; pp[D + 1] = ltot[m][h]; }
+    const int usedm = min(a.nsplit, (p0 + m) / a.chunk + 1);
+    const float* pp = a.part + ((size_t)row * a.nq + qh) * a.nsplit * (D + 2);
+    float mx = -INFINITY;
+    for (int sp = 0; sp < usedm; ++sp) mx = fmaxf(mx, pp[sp * (D + 2) + D]);
+    float l = 0.f, acc = 0.f;
+    for (int sp = 0; sp < usedm; ++sp) {
+      const float ms = pp[sp * (D + 2) + D];
+      const float w = (ms == -INFINITY) ? 0.f : expf(ms - mx);
+      l += w * pp[sp * (D + 2) + D + 1];
+      acc += w * pp[sp * (D + 2) + e];
     }
+    a.out[(size_t)row * a.out_stride + (size_t)qh * D + e] = l > 0.f ? acc / l : 0.f;
   }
-}
-
-// Merge split partials: grid (nq, rows), d threads.
-struct MergeArgs {
-  const float* part;
-  int32_t nq, d, nsplit, chunk, M, pos_const, pos_from_state;
-  float* out;
-  int32_t out_stride;
-  const DevState* st;
-};
-
-__global__ __launch_bounds__(256) void k_attn_merge(MergeArgs a) {
-  const int qh = blockIdx.x, row = blockIdx.y, e = threadIdx.x;
-  const int p0 = a.pos_from_state ? a.st->pos : a.pos_const;
-  const int m = row % a.M;
-  const int used = min(a.nsplit, (p0 + m) / a.chunk + 1);
-  const float* pp = a.part + ((size_t)row * a.nq + qh) * a.nsplit * (a.d + 2);
-  float mx = -INFINITY;
-  for (int s = 0; s < used; ++s) mx = fmaxf(mx, pp[s * (a.d + 2) + a.d]);
-  float l = 0.f, acc = 0.f;
-  for (int s = 0; s < used; ++s) {
-    const float ms = pp[s * (a.d + 2) + a.d];
-    const float w = (ms == -INFINITY) ? 0.f : expf(ms - mx);
-    l += w * pp[s * (a.d + 2) + a.d + 1];
-    if (e < a.d) acc += w * pp[s * (a.d + 2) + e];
-  }
-  if (e < a.d) a.out[(size_t)row * a.out_stride + (size_t)qh * a.d + e] = l > 0.f ? acc / l : 0.f;
 }
 
 // ---------------------------------------------------------------------------- sampling
@@ -734,9 +737,6 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
 
 // ---------------------------------------------------------------------------- counters
 
-__global__ void k_bump(DevState* st, int dpos, int dframe) {
-  if (threadIdx.x == 0 && blockIdx.x == 0) { st->pos += dpos; st->frame += dframe; }
-}
 __global__ void k_set_state(DevState* st, int pos, int frame) {
   if (threadIdx.x == 0 && blockIdx.x == 0) { st->pos = pos; st->frame = frame; }
 }

@@ -1,0 +1,47 @@
+"""Summarise a rocprofv3 --kernel-trace --stats run of bench.py as text.
+
+    python -m autoregressive_tts_decode_amd.prof_summary <prefix> [--frames K]
+
+<prefix> is the path prefix rocprofv3 wrote (…/bench): it reads
+<prefix>_kernel_stats.csv and <prefix>_kernel_trace.csv. The frame loop is
+identified in the trace as the last K frames' kernels (every frame ends with
+the semantic-head GEMV that advances the device counters); the per-frame
+kernel-time sum and wall span are reported next to the per-kernel table.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+from collections import defaultdict
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("prefix")
+    ap.add_argument("--frames", type=int, default=0, help="timed frames at the end of the trace")
+    ap.add_argument("--kernels-per-frame", type=int, default=0)
+    ap.add_argument("--top", type=int, default=16)
+    a = ap.parse_args()
+    rows = list(csv.DictReader(open(a.prefix + "_kernel_stats.csv")))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    print(f"total kernel time in the run: {tot / 1e6:.2f} ms over {sum(int(r['Calls']) for r in rows)} launches")
+    print(f"{'kernel':78s} {'calls':>7s} {'avg us':>8s} {'min us':>8s} {'share':>6s}")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))[: a.top]:
+        print(f"{r['Name'][:78]:78s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:8.2f} "
+              f"{float(r['MinNs']) / 1e3:8.2f} {float(r['TotalDurationNs']) / tot * 100:5.1f}%")
+    if a.frames and a.kernels_per_frame:
+        tr = list(csv.DictReader(open(a.prefix + "_kernel_trace.csv")))
+        tr.sort(key=lambda r: int(r["Start_Timestamp"]))
+        n = a.frames * a.kernels_per_frame
+        tail = tr[-n:]
+        busy = sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tail)
+        span = int(tail[-1]["End_Timestamp"]) - int(tail[0]["Start_Timestamp"])
+        per = defaultdict(float)
+        for r in tail:
+            per[r["Kernel_Name"]] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        print(f"\nlast {a.frames} frames ({a.kernels_per_frame} kernels each): kernel time {busy / a.frames / 1e3:.1f} us/frame, "
+              f"wall span {span / a.frames / 1e3:.1f} us/frame")
+
+
+if __name__ == "__main__":
+    main()

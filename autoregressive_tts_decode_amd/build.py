@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libtts.so")
 SOURCES = [os.path.join(PKG, "csrc", "tts.hip")]
-HEADERS = [os.path.join(PKG, "csrc", "tts_device.h"), os.path.join(ROOT, "include", "tts.h")]
+HEADERS = [os.path.join(PKG, "csrc", "tts_device.h"), os.path.join(PKG, "csrc", "tts_xtp.h"),
+           os.path.join(ROOT, "include", "tts.h")]
 ARCH = "gfx950"
 
 

@@ -10,6 +10,7 @@
 // consumes them (which leaves the next frame's Talker output pending).
 #include "tts.h"
 #include "tts_device.h"
+#include "tts_xtp.h"
 
 #include <hip/hip_runtime.h>
 
@@ -57,7 +58,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout, computed identically by tts_workspace_bytes and tts_create.
 struct Layout {
   size_t st, tk, tv, ck, cv, tcos, tsin, ccos, csin, x, qkv, attn, h, part, counters, logits, hT, cx, clog, next_tok,
-      sem_tok, ac_codes, history, total;
+      sem_tok, ac_codes, history, cpdesc, xin, xcr, cand, xerr, xzero_begin, xzero_end, total;
   int nsplit;
 };
 
@@ -99,6 +100,14 @@ Layout make_layout(const tts_config& c) {
   L.sem_tok = take(B * 4);
   L.ac_codes = take(B * c.n_acoustic * 4);
   L.history = take(B * t.vocab);
+  // persistent CodePredictor kernel: descriptor and exchange buffers (its K/V rows stay in LDS)
+  L.cpdesc = take(sizeof(xtp::CpDesc));
+  L.xzero_begin = off;
+  L.xin = take((size_t)xtp::NX * xtp::RING * xtp::ISZ * 8);
+  L.xcr = take((size_t)xtp::NWG * 2 * xtp::CSZ * 8);
+  L.cand = take((size_t)2 * xtp::NWG * xtp::CAND * 8);
+  L.xerr = take(256);
+  L.xzero_end = off;
   L.total = off;
   return L;
 }
@@ -146,6 +155,32 @@ std::string check_config(const tts_config* c) {
   return "";
 }
 
+// Whether the persistent XCD-tensor-parallel CodePredictor kernel handles this config: bf16 weights,
+// 8 KV heads of dimension 128 (one per XCD), and per-workgroup weight slices that fit its two
+// register buffers (rows per wave and 16-byte units per lane).
+bool xtp_capable(const tts_config& c) {
+  const tts_stack_cfg& p = c.codepred;
+  const int E = 8;  // bf16 weights: 8 per 16-byte unit
+  const int Ht = c.talker.hidden;
+  const int ra_rows = xtp::RA_R * xtp::NW, ra_units = 64 * xtp::RA_K;
+  const int rb_rows = xtp::RB_R * xtp::NW, rb_units = 64 * xtp::RB_K;
+  if (c.weight_dtype != TTS_DTYPE_BF16) return false;
+  if (p.n_kv_heads != xtp::NX || p.head_dim != 128) return false;
+  const int G = p.n_q_heads / p.n_kv_heads;
+  if (G < 1 || G > 2 || p.n_q_heads != G * p.n_kv_heads || ((G + 2) * p.head_dim) % xtp::NR) return false;
+  if (p.hidden % xtp::NR || p.hidden > xtp::HMAX || p.hidden % E || p.hidden / E > ra_units) return false;
+  // A rows: q/k/v slice, gate/up slice, head slice
+  if ((G + 2) * p.head_dim / xtp::NR > ra_rows) return false;
+  if (p.ffn % (xtp::NX * xtp::NR) || 2 * (p.ffn / (xtp::NX * xtp::NR)) > ra_rows) return false;
+  if (p.vocab % xtp::NWG || p.vocab / xtp::NWG > ra_rows) return false;
+  // B rows: output projection, down projection, input projection (hidden / 32 rows each)
+  if (p.hidden / xtp::NR > rb_rows || G * p.head_dim / E > rb_units) return false;
+  if (p.ffn / xtp::NX > 768 || (p.ffn / xtp::NX) % E || (p.ffn / xtp::NX) / E > rb_units) return false;
+  if (Ht != p.hidden && (Ht > 2048 || Ht % (xtp::NX * E) || (Ht / xtp::NX) / E > rb_units)) return false;
+  if (p.n_layers > xtp::MAXL || c.n_acoustic != 15) return false;
+  return true;
+}
+
 }  // namespace
 
 struct tts_ctx {
@@ -176,6 +211,11 @@ struct tts_ctx {
   hipGraph_t graph = nullptr;
   hipGraphExec_t gexec = nullptr;
   hipStream_t cap_stream = nullptr;  // private stream used only to record the frame graph
+  // persistent CodePredictor kernel
+  bool xtp_ok = false;   // config supported
+  int exec_mode = TTS_EXEC_PERSISTENT;  // persistent CodePredictor when supported (batch 1, greedy)
+  xtp::CpDesc* cpdesc = nullptr;
+  uint32_t* xerr = nullptr;
   std::string err;
 
   int fail(int code, const char* fmt, ...) {
@@ -484,6 +524,25 @@ int sample(tts_ctx* ctx, const float* logits, int l_stride, int B, int V, const 
 // stream. Acoustic token j of stream b goes to out (refs with offset j-1);
 // logits (optional) to logits_out + b*15*Va + (j-1)*Va. u: uniform refs with
 // offset of acoustic 1 (incremented per step). forced: [B][15] or nullptr.
+// The persistent CodePredictor kernel handles batch 1 with greedy acoustic tokens.
+bool use_xtp(tts_ctx* ctx, int B, const tts_sampling& ac) { return ctx->xtp_ok && ctx->exec_mode == 1 && B == 1 && !ac.do_sample; }
+
+int codepred_frame_xtp(tts_ctx* ctx, const int32_t* semantic, const int32_t* forced, int32_t* codes, int f_stride, int use_frame,
+                       float* logits_out) {
+  xtp::CpCall call;
+  call.desc = ctx->cpdesc;
+  call.semantic = semantic;
+  call.forced = forced;
+  call.codes = codes;
+  call.f_stride = f_stride;
+  call.use_frame = use_frame;
+  call.logits = logits_out;
+  call.next_tok = nullptr;
+  hipLaunchKernelGGL(xtp::k_cp_frame<uint16_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
+  HIP_LAUNCH_CHECK();
+  return TTS_OK;
+}
+
 int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac, URef u, const int32_t* forced,
                    int32_t* out, int ob, int of, int oo, int ouf, float* logits_out) {
   const auto& c = ctx->cfg;
@@ -574,9 +633,12 @@ int enqueue_frame(tts_ctx* ctx, const tts_sampling& sem, const tts_sampling& ac,
   if (int rc = sample(ctx, ctx->logits, c.talker.vocab, B, c.talker.vocab, sem, uref(u, ub, uf, 0, 1), ctx->history,
                       c.talker.vocab, 1, codes, fs, 16, 0, 1, ctx->sem_tok, nullptr, 0, 0))
     return rc;
-  if (int rc = codepred_frame(ctx, B, tokref(ctx->sem_tok, 1, 0, 0, 0), ac, uref(u, ub, uf, u == ctx->hT ? 0 : 1, 1), nullptr, codes,
-                              fs, 16, 1, 1, nullptr))
+  if (use_xtp(ctx, B, ac)) {
+    if (int rc = codepred_frame_xtp(ctx, ctx->sem_tok, nullptr, codes + 1, 16, 1, nullptr)) return rc;
+  } else if (int rc = codepred_frame(ctx, B, tokref(ctx->sem_tok, 1, 0, 0, 0), ac, uref(u, ub, uf, u == ctx->hT ? 0 : 1, 1), nullptr,
+                                     codes, fs, 16, 1, 1, nullptr)) {
     return rc;
+  }
   TokRef refs[16];
   for (int j = 0; j < 16; ++j) refs[j] = tokref(codes, fs, 16, j, 1);
   if (int rc = embed_sum(ctx, B, refs)) return rc;
@@ -630,6 +692,9 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
   ctx->tcos = (float*)(w + L.tcos); ctx->tsin = (float*)(w + L.tsin); ctx->ccos = (float*)(w + L.ccos); ctx->csin = (float*)(w + L.csin);
   ctx->next_tok = (int32_t*)(w + L.next_tok); ctx->sem_tok = (int32_t*)(w + L.sem_tok); ctx->ac_codes = (int32_t*)(w + L.ac_codes);
   ctx->history = (uint8_t*)(w + L.history);
+  ctx->cpdesc = (xtp::CpDesc*)(w + L.cpdesc);
+  ctx->xerr = (uint32_t*)(w + L.xerr);
+  ctx->xtp_ok = xtp_capable(*cfg);
   ctx->talker.c = cfg->talker;
   ctx->cp.c = cfg->codepred;
   // RoPE tables: angles p * theta^(-2i/d) in double, rounded to fp32.
@@ -644,6 +709,9 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
   hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, 0, 0);
   hipLaunchKernelGGL(k_fill_u8, dim3(1), dim3(256), 0, ctx->stream, (uint8_t*)ctx->counters,
                      (size_t)cfg->max_batch * cfg->talker.n_kv_heads * 4, (uint8_t)0);
+  hipLaunchKernelGGL(k_fill_u8, dim3(1), dim3(64), 0, ctx->stream, (uint8_t*)ctx->st, sizeof(DevState), (uint8_t)0);
+  hipLaunchKernelGGL(k_fill_u8, dim3(256), dim3(256), 0, ctx->stream, (uint8_t*)(w + L.xzero_begin),
+                     L.xzero_end - L.xzero_begin, (uint8_t)0);
   if (hipGetLastError() != hipSuccess) { delete ctx; return TTS_E_HIP; }
   *out = ctx;
   return TTS_OK;
@@ -717,6 +785,26 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
   ctx->weights_ok = true;
   ctx->prefilled = false;
   drop_graph(ctx);
+  if (ctx->xtp_ok) {
+    xtp::CpDesc D;
+    std::memset(&D, 0, sizeof D);
+    const tts_stack_cfg& p = c.codepred;
+    for (int l = 0; l < p.n_layers; ++l) {
+      const Layer& L = ctx->cp.layers[l];
+      D.layer[l] = {L.attn_norm, L.wq, L.wk, L.wv, L.q_norm, L.k_norm, L.wo, L.mlp_norm, L.wg, L.wu, L.wd};
+    }
+    D.n_layers = p.n_layers; D.H = p.hidden; D.Ht = c.talker.hidden; D.F = p.ffn; D.V = p.vocab; D.Vs = c.talker.vocab;
+    D.nq = p.n_q_heads; D.nkv = p.n_kv_heads; D.d = p.head_dim; D.n_ac = c.n_acoustic; D.eps = c.rms_eps;
+    D.final_norm = ctx->cp.final_norm; D.heads = ctx->heads; D.proj = ctx->proj; D.embed_ac = ctx->embed_ac;
+    D.embed_sem = ctx->embed_sem;
+    D.rope_cos = ctx->ccos; D.rope_sin = ctx->csin;
+    D.hT = ctx->hT;
+    D.xin = (xtp::u64*)(ctx->ws + ctx->L.xin); D.xcr = (xtp::u64*)(ctx->ws + ctx->L.xcr);
+    D.cand = (xtp::u64*)(ctx->ws + ctx->L.cand);
+    D.st = ctx->st; D.err = ctx->xerr;
+    HIP_TRY(hipMemcpyAsync(ctx->cpdesc, &D, sizeof D, hipMemcpyHostToDevice, ctx->stream));
+    HIP_TRY(hipStreamSynchronize(ctx->stream));
+  }
   ctx->err.clear();
   return TTS_OK;
 }
@@ -780,7 +868,11 @@ int tts_codepred_frame(tts_ctx* ctx, const int32_t* semantic, const tts_sampling
   if (ac->do_sample && !u) return ctx->fail(TTS_E_ARG, "codepred_frame: u is NULL with do_sample");
   const int B = ctx->batch;
   URef ur = uref(u ? u : ctx->hT, u ? 15 : 0, 0, 0, 0);
-  if (int rc = codepred_frame(ctx, B, tokref(semantic, 1, 0, 0, 0), *ac, ur, forced, codes, 15, 0, 0, 0, logits)) return rc;
+  if (use_xtp(ctx, B, *ac)) {
+    if (int rc = codepred_frame_xtp(ctx, semantic, forced, codes, 0, 0, logits)) return rc;
+  } else if (int rc = codepred_frame(ctx, B, tokref(semantic, 1, 0, 0, 0), *ac, ur, forced, codes, 15, 0, 0, 0, logits)) {
+    return rc;
+  }
   ctx->err.clear();
   return TTS_OK;
 }
@@ -850,13 +942,45 @@ int tts_get_progress(const tts_ctx* ctx, int32_t* talker_pos, int32_t* frames) {
 
 int tts_reset(tts_ctx* ctx) {
   if (!ctx) return TTS_E_ARG;
-  hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, 0, 0);
+  // Counters, the exchange tag and every exchange buffer start over, which also clears the
+  // state a failed persistent launch may have left behind.
+  hipLaunchKernelGGL(k_fill_u8, dim3(1), dim3(64), 0, ctx->stream, (uint8_t*)ctx->st, sizeof(DevState), (uint8_t)0);
+  HIP_LAUNCH_CHECK();
+  hipLaunchKernelGGL(k_fill_u8, dim3(256), dim3(256), 0, ctx->stream, (uint8_t*)(ctx->ws + ctx->L.xzero_begin),
+                     ctx->L.xzero_end - ctx->L.xzero_begin, (uint8_t)0);
   HIP_LAUNCH_CHECK();
   ctx->prefilled = false;
   ctx->pos = 0;
   ctx->frames = 0;
   ctx->batch = 0;
   ctx->err.clear();
+  return TTS_OK;
+}
+
+int tts_set_exec_mode(tts_ctx* ctx, int32_t mode) {
+  if (!ctx) return TTS_E_ARG;
+  if (mode != TTS_EXEC_KERNELS && mode != TTS_EXEC_PERSISTENT) return ctx->fail(TTS_E_ARG, "exec mode %d", mode);
+  if (mode == TTS_EXEC_PERSISTENT && !ctx->xtp_ok)
+    return ctx->fail(TTS_E_UNSUPPORTED, "the persistent CodePredictor kernel does not handle this config");
+  if (mode != ctx->exec_mode) drop_graph(ctx);
+  ctx->exec_mode = mode;
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+int tts_get_exec_mode(const tts_ctx* ctx, int32_t* mode, int32_t* persistent_supported) {
+  if (!ctx) return TTS_E_ARG;
+  if (mode) *mode = ctx->exec_mode == 1 && ctx->xtp_ok ? TTS_EXEC_PERSISTENT : TTS_EXEC_KERNELS;
+  if (persistent_supported) *persistent_supported = ctx->xtp_ok ? 1 : 0;
+  return TTS_OK;
+}
+
+int tts_device_status(tts_ctx* ctx, int32_t* status) {
+  if (!ctx || !status) return TTS_E_ARG;
+  HIP_TRY(hipStreamSynchronize(ctx->stream));
+  uint32_t e = 0;
+  HIP_TRY(hipMemcpy(&e, ctx->xerr, 4, hipMemcpyDeviceToHost));
+  *status = (int32_t)e;
   return TTS_OK;
 }
 

@@ -30,7 +30,8 @@ enum Src : int { SRC_VEC = 0, SRC_TABLE = 1, SRC_VEC_THEN_TABLE = 2 };
 struct DevState {
   int32_t pos;
   int32_t frame;
-  int32_t pad[62];
+  uint32_t epoch;   // running exchange tag of the persistent kernels; never reset
+  int32_t pad[61];
 };
 
 // Token / uniform addressing that may depend on the device frame counter:

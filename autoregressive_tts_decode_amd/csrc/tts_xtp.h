@@ -1,0 +1,667 @@
+// Persistent, XCD-tensor-parallel CodePredictor frame kernel (CDNA4, gfx950).
+//
+// The 15 sequential CodePredictor steps of a frame ("Running Qwen3-TTS on an
+// AMD R9700", section "Running Qwen3-TTS") run inside ONE kernel of 256
+// workgroups x 512 threads -- one workgroup per CU, rank r on XCD g where
+// g = blockIdx % 8 and r = blockIdx / 8. Each decoder layer is split across
+// the 8 XCDs tensor-parallel: XCD g owns KV head g (query heads G*g ..
+// G*g+G-1), the matching columns of the output projection and 1/8 of the
+// FFN. Dependencies between phases are exchanges of tagged fp32 values
+// ((tag << 32) | bits, written and read with device-coherent relaxed
+// atomics, so no cache maintenance or fences are needed and correctness does
+// not depend on where a workgroup runs):
+//   intra: the 32 ranks of one XCD gather each other's slices
+//          (q/k/v slice -> attention; reduced residual -> full residual;
+//           SwiGLU slice -> down projection);
+//   cross: rank r of every XCD reduce-scatters the partial sums of the output
+//          and down projections (8 partners, rank-r rows).
+// A consumer polls until every value it needs carries the expected tag; tags
+// are unique per exchange (a running epoch kept on the device), and every
+// exchange buffer is reused only after an exchange that all its readers must
+// have passed, so a value is never overwritten while it may still be read.
+// Each phase issues its weight loads before it waits for its input.
+#pragma once
+
+#include "tts_device.h"
+
+namespace tts {
+namespace xtp {
+
+constexpr int NX = 8;       // XCDs
+constexpr int NR = 32;      // ranks per XCD
+constexpr int NWG = NX * NR;
+constexpr int NT = 512;     // threads per workgroup
+constexpr int NW = NT / 64; // waves per workgroup
+constexpr int MAXL = 6;     // CodePredictor layers supported (K/V rows live in LDS)
+constexpr int kCpPos = 16;  // CodePredictor positions per frame
+constexpr int HMAX = 1024;  // CodePredictor hidden size supported
+constexpr int KVS = 132;    // LDS row stride of the K/V rows (padded against bank conflicts)
+// Weight-row register buffers, per wave: A holds hidden-wide rows (q/k/v, gate/up, head: at most
+// RA_R rows per wave of at most 64 * RA_K 16-byte units), B narrow rows (output and down
+// projections, input projection: RB_R rows of at most 64 * RB_K units).
+constexpr int RA_R = 3, RA_K = 2;
+constexpr int RB_R = 4, RB_K = 1;
+constexpr int RING = 4;     // intra exchange buffers per XCD
+constexpr int ISZ = 2 * HMAX;  // intra buffer entries (2 rows x HMAX)
+constexpr int CSZ = 2 * 64;    // cross slot entries (2 rows x 64)
+constexpr int CAND = 8;        // candidate slot entries (one 64-byte line)
+constexpr long long kSpin = 4000000;
+
+typedef unsigned long long u64;
+
+struct LayerW {
+  const void *attn_norm, *wq, *wk, *wv, *q_norm, *k_norm, *wo, *mlp_norm, *wg, *wu, *wd;
+};
+
+// Everything the kernel reads; built on the host once per weight binding and
+// kept in device memory.
+struct CpDesc {
+  LayerW layer[MAXL];
+  int32_t n_layers, H, Ht, F, V, Vs, nq, nkv, d, n_ac;
+  float eps;
+  const void *final_norm, *heads, *proj, *embed_ac, *embed_sem;
+  const float *rope_cos, *rope_sin;  // [16][d/2]
+  const float* hT;                   // [Ht] pending Talker hidden (final-normed)
+  u64 *xin, *xcr, *cand;
+  DevState* st;
+  uint32_t* err;                     // nonzero after a failed exchange (time-out)
+};
+
+// Per-launch arguments (pointers may differ between calls).
+struct CpCall {
+  const CpDesc* desc;
+  const int32_t* semantic;  // [1]: the frame's semantic id
+  const int32_t* forced;    // [15] or nullptr
+  int32_t* codes;           // acoustic ids land at codes[(use_frame ? frame * f_stride : 0) + j - 1]
+  int32_t f_stride, use_frame;
+  float* logits;            // [15][V] or nullptr
+  int32_t* next_tok;        // optional: last token fed forward (unused by the frame loop)
+};
+
+// Wave index as a wave-uniform (scalar) value, so row addresses derived from it stay scalar.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ u64 pack(float v, uint32_t tag) { return ((u64)tag << 32) | __float_as_uint(v); }
+__device__ __forceinline__ uint32_t tagof(u64 v) { return (uint32_t)(v >> 32); }
+__device__ __forceinline__ float valof(u64 v) { return __uint_as_float((uint32_t)v); }
+__device__ __forceinline__ void st_c(u64* p, u64 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ u64 ld_c(const u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Publish n values of vals (LDS) as tagged entries at dst.
+__device__ __forceinline__ void put(u64* dst, const float* vals, int n, uint32_t tag) {
+  for (int i = threadIdx.x; i < n; i += NT) st_c(dst + i, pack(vals[i], tag));
+}
+
+// Gather nseg segments of len entries into lds[0 .. nseg*len), polling until every entry carries
+// tag. With inner == 1 segment s starts at src + s * sstride; otherwise segment s = (a, b), a = s / inner,
+// b = s % inner, starts at src + a * astride + b * 64. n <= 4 * NT.
+// Returns false (and flags err) on time-out or when another workgroup failed.
+__device__ __forceinline__ bool get(const u64* src, int nseg, int len, int sstride, uint32_t tag, float* lds, uint32_t* err,
+                                    int inner = 1, int astride = 0) {
+  const int n = nseg * len;
+  for (long long s = 0;; ++s) {
+    u64 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < n) {
+        const int seg = i / len, e = i % len;
+        const size_t off = (inner == 1) ? (size_t)seg * sstride : (size_t)(seg / inner) * astride + (size_t)(seg % inner) * 64;
+        v[k] = ld_c(src + off + e);
+      }
+    }
+    int ok = 1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < n) {
+        if (tagof(v[k]) != tag) ok = 0;
+        else lds[i] = valof(v[k]);
+      }
+    }
+    if (__syncthreads_and(ok)) return true;
+    if ((s & 255) == 255) {
+      const uint32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__syncthreads_or(e != 0 || s > kSpin)) {
+        if (threadIdx.x == 0) atomicOr(err, 1u);
+        return false;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- weight rows
+
+// Rows of one phase: wave w streams rows w, w + NW, ... (at most MAXR), each
+// row's 16-byte units spread over the lanes (unit u = lane + 64 k, k < MAXK).
+template <typename WT, int RR, int KK>
+struct Rows {
+  static constexpr int MAXR = RR, MAXK = KK;
+  u32x4 b[RR][KK];
+};
+
+// rowptr(i) -> const WT* of row i (0 <= i < nrows); ncols elements per row.
+template <typename WT, int RR, int KK, typename RowFn>
+__device__ __forceinline__ void rows_issue(Rows<WT, RR, KK>& R, int nrows, int ncols, RowFn rowptr, bool nt) {
+  constexpr int E = WTraits<WT>::E, MAXR = RR, MAXK = KK;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int units = ncols / E;
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const int i = wave + NW * j;
+    if (i < nrows) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(rowptr(i));
+#pragma unroll
+      for (int k = 0; k < MAXK; ++k) {
+        const int u = lane + 64 * k;
+        if (u < units) R.b[j][k] = nt ? __builtin_nontemporal_load(p + u) : p[u];
+      }
+    }
+  }
+}
+
+// out[i * M + m] = dot(row i, x[m * ldx .. + ncols]) for this wave's rows (LDS in/out).
+template <typename WT, int M, int RR, int KK>
+__device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, int ldx, float* out) {
+  constexpr int E = WTraits<WT>::E, MAXR = RR, MAXK = KK;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int units = ncols / E;
+  float acc[MAXR][M];
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[j][m] = 0.f;
+#pragma unroll
+  for (int k = 0; k < MAXK; ++k) {
+    const int u = lane + 64 * k;
+    if (u < units) {
+      float xv[M][8];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float* xp = x + m * ldx + u * E;
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+          const float4 f = *reinterpret_cast<const float4*>(xp + e);
+          xv[m][e] = f.x; xv[m][e + 1] = f.y; xv[m][e + 2] = f.z; xv[m][e + 3] = f.w;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < MAXR; ++j) {
+        if (wave + NW * j < nrows) {
+          float wf[8];
+          unpack(R.b[j][k], wf, (WT*)nullptr);
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            float s = acc[j][m];
+#pragma unroll
+            for (int e = 0; e < E; ++e) s = fmaf(wf[e], xv[m][e], s);
+            acc[j][m] = s;
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < MAXR; ++j) {
+    const int i = wave + NW * j;
+    if (i < nrows) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float v = wave_sum(acc[j][m]);
+        if (lane == 0) out[i * M + m] = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- block helpers
+
+// ---------------------------------------------------------------------------- the kernel
+
+// Shared memory layout (floats). Row m of a residual-width array starts at m * H.
+struct Smem {
+  float xs[2 * HMAX];   // residual rows (full)
+  float xn[2 * HMAX];   // normed / staged input rows; reduce-scatter partials
+  float qkv[2 * 512];   // this XCD's q/k/v slice
+  float ob[2 * 256];    // attention output of this XCD's heads
+  float hb[2 * 768];    // SwiGLU slice
+  float out[2 * 128];   // row results of this workgroup
+  float red[64];
+  float kq[4][128];     // normed + rotated q (G x M vectors) for attention
+  float sc[4][kCpPos];  // attention scores (G x M rows)
+  float cand[2 * NWG];  // argmax candidates of every workgroup
+  float kvc[MAXL][2][kCpPos][KVS];  // this frame's K/V rows of KV head g, per layer
+};
+
+// ---------------------------------------------------------------------------- weight phases
+// A phase's rows are issued into one of two register buffers as soon as the phase two back has
+// consumed it, so their HBM latency overlaps the two exchanges before the phase.
+
+template <typename WT>
+using RowsA = Rows<WT, RA_R, RA_K>;
+template <typename WT>
+using RowsB = Rows<WT, RB_R, RB_K>;
+
+// q/k/v rows [qper*r, +qper) of this XCD's (G q heads | k | v)
+template <typename WT>
+__device__ __forceinline__ void issue_qkv(RowsA<WT>& R, const CpDesc& D, const LayerW& W, int g, int r) {
+  const int H = D.H, d = D.d, G = D.nq / D.nkv, qper = (G + 2) * d / NR;
+  rows_issue(R, qper, H, [&](int i) -> const WT* {
+    const int q = qper * r + i;
+    if (q < G * d) return reinterpret_cast<const WT*>(W.wq) + (size_t)(G * d * g + q) * H;
+    if (q < (G + 1) * d) return reinterpret_cast<const WT*>(W.wk) + (size_t)(d * g + q - G * d) * H;
+    return reinterpret_cast<const WT*>(W.wv) + (size_t)(d * g + q - (G + 1) * d) * H;
+  }, false);
+}
+// output projection rows [hper*r, +hper), columns of this XCD's heads
+template <typename WT>
+__device__ __forceinline__ void issue_o(RowsB<WT>& R, const CpDesc& D, const LayerW& W, int g, int r) {
+  const int hper = D.H / NR, Gd = D.nq / D.nkv * D.d;
+  rows_issue(R, hper, Gd, [&](int i) -> const WT* {
+    return reinterpret_cast<const WT*>(W.wo) + (size_t)(hper * r + i) * (D.nq * D.d) + Gd * g;
+  }, false);
+}
+// gate rows then up rows [fper*r, +fper) of this XCD's FFN slice
+template <typename WT>
+__device__ __forceinline__ void issue_gu(RowsA<WT>& R, const CpDesc& D, const LayerW& W, int g, int r) {
+  const int fx = D.F / NX, fper = fx / NR;
+  rows_issue(R, 2 * fper, D.H, [&](int i) -> const WT* {
+    const int f = fx * g + fper * r + (i % fper);
+    return reinterpret_cast<const WT*>(i < fper ? W.wg : W.wu) + (size_t)f * D.H;
+  }, false);
+}
+// down projection rows [hper*r, +hper), columns of this XCD's FFN slice
+template <typename WT>
+__device__ __forceinline__ void issue_down(RowsB<WT>& R, const CpDesc& D, const LayerW& W, int g, int r) {
+  const int hper = D.H / NR, fx = D.F / NX;
+  rows_issue(R, hper, fx, [&](int i) -> const WT* {
+    return reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r + i) * D.F + fx * g;
+  }, false);
+}
+// head j rows [vper*blockIdx, +vper)
+template <typename WT>
+__device__ __forceinline__ void issue_head(RowsA<WT>& R, const CpDesc& D, int j) {
+  const int vper = D.V / NWG;
+  const WT* head = reinterpret_cast<const WT*>(D.heads) + (size_t)(j - 1) * D.V * D.H;
+  rows_issue(R, vper, D.H, [&](int i) -> const WT* { return head + (size_t)(vper * blockIdx.x + i) * D.H; }, false);
+}
+// input projection rows (K split: XCD g takes columns [Ht/8 * g, +Ht/8), rank r rows [hper*r, +hper))
+template <typename WT>
+__device__ __forceinline__ void issue_proj(RowsB<WT>& R, const CpDesc& D, int g, int r) {
+  const int kx = D.Ht / NX, hper = D.H / NR;
+  rows_issue(R, hper, kx, [&](int i) -> const WT* {
+    return reinterpret_cast<const WT*>(D.proj) + (size_t)(hper * r + i) * D.Ht + kx * g;
+  }, false);
+}
+
+// ---------------------------------------------------------------------------- exchanges
+
+// Cross reduce-scatter of this workgroup's hper x M partial rows (S.out, row-major [row][m]) with
+// rank r of every XCD, plus an optional residual (S.xs), then the intra gather of the full rows into
+// S.xs. cpar alternates the cross slot so a rank one exchange ahead never overwrites unread values.
+__device__ __forceinline__ bool reduce_gather(const CpDesc& D, Smem& S, int M, int H, bool residual, uint32_t& tag, int& iring, int& cpar,
+                              int g, int r) {
+  const int tid = threadIdx.x, hper = H / NR;
+  ++tag;
+  u64* mine = D.xcr + ((size_t)blockIdx.x * 2 + (cpar & 1)) * CSZ;
+  for (int i = tid; i < hper * M; i += NT) st_c(mine + (i % M) * 64 + i / M, pack(S.out[i], tag));
+  // partners: rank r on every XCD = blocks r * NX + x; their slots are 2 * CSZ apart.
+  // Segment (x, m) -> S.xn[(x * M + m) * hper ..]
+  const u64* base = D.xcr + ((size_t)(r * NX) * 2 + (cpar & 1)) * CSZ;
+  if (!get(base, NX * M, hper, 2 * CSZ, tag, S.xn, D.err, M, 2 * CSZ)) return false;
+  ++cpar;
+  ++tag;
+  u64* buf = D.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
+  for (int i = tid; i < hper * M; i += NT) {
+    const int e = i / M, m = i % M;
+    const int row = hper * r + e;
+    float v = residual ? S.xs[m * H + row] : 0.f;
+#pragma unroll
+    for (int x = 0; x < NX; ++x) v += S.xn[(x * M + m) * hper + e];
+    st_c(buf + m * H + row, pack(v, tag));
+  }
+  __syncthreads();  // the gather below overwrites the residual rows read above
+  return get(buf, M, H, H, tag, S.xs, D.err);
+}
+
+// Intra gather of a slice: this workgroup's n values per row (vals(e, m)) land at row offset
+// n * r of every rank's copy; the full rows (width w) of all ranks go to dst.
+template <int M, typename ValFn>
+__device__ __forceinline__ bool slice_gather(const CpDesc& D, int n, int w, ValFn vals, float* dst, uint32_t& tag, int& iring,
+                                             int g, int r) {
+  ++tag;
+  u64* buf = D.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
+  for (int i = threadIdx.x; i < n * M; i += NT) {
+    const int e = i / M, m = i % M;
+    st_c(buf + m * w + n * r + e, pack(vals(e, m), tag));
+  }
+  return get(buf, M, w, w, tag, dst, D.err);
+}
+
+// ---------------------------------------------------------------------------- per-thread constants
+
+// Norm gains and RoPE factors a layer needs, held in registers so no global load sits on the
+// critical path: residual-norm gains of elements tid and tid + NT (H <= 2 NT), and for waves that
+// normalise a q/k vector (one wave per vector of row vm, slot vj) the head-norm gains of lanes
+// lane, lane + 64 and the RoPE cos/sin of position p0 + vm.
+struct LayerConsts {
+  float an[2], mn[2], qk[2], rc, rs;
+};
+
+template <typename WT, int M>
+__device__ __forceinline__ void load_consts(LayerConsts& c, const CpDesc& D, const LayerW& W, int p0) {
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, G = D.nq / D.nkv;
+  const WT* an = reinterpret_cast<const WT*>(W.attn_norm);
+  const WT* mn = reinterpret_cast<const WT*>(W.mlp_norm);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = tid + k * NT;
+    c.an[k] = i < D.H ? to_f32(an[i]) : 0.f;
+    c.mn[k] = i < D.H ? to_f32(mn[i]) : 0.f;
+  }
+  const int vm = wave / (G + 2), vj = wave % (G + 2);
+  c.qk[0] = c.qk[1] = 1.f;
+  c.rc = 1.f;
+  c.rs = 0.f;
+  if (wave < M * (G + 2) && vj <= G) {
+    const WT* gn = reinterpret_cast<const WT*>(vj < G ? W.q_norm : W.k_norm);
+    c.qk[0] = to_f32(gn[lane]);
+    c.qk[1] = to_f32(gn[lane + 64]);
+    c.rc = D.rope_cos[(p0 + vm) * 64 + lane];
+    c.rs = D.rope_sin[(p0 + vm) * 64 + lane];
+  }
+}
+
+// y[m] = x[m] * rsqrt(mean(x[m]^2) + eps) * gain over n <= 2 NT elements (rows n apart in LDS),
+// gain of elements tid, tid + NT in gr.
+template <int M>
+__device__ __forceinline__ void rmsnorm_reg(const float* x, int n, const float* gr, float eps, float* y, float* red) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + k * NT;
+      if (i < n) s += x[m * n + i] * x[m * n + i];
+    }
+    s = wave_sum(s);
+    if (lane == 0) red[m * NW + wave] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += red[m * NW + w];
+    const float sc = 1.0f / sqrtf(s / (float)n + eps);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + k * NT;
+      if (i < n) y[m * n + i] = x[m * n + i] * sc * gr[k];
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------- the layer
+
+// One decoder layer for M rows at positions p0 .. p0 + M - 1. Weight phases alternate between two
+// register buffers and are issued two phases ahead of their use. On entry R1 holds this layer's
+// q/k/v rows, R0 its output-projection rows and c its constants; on exit R1 holds the next layer's
+// q/k/v rows (or head j), R0 the next layer's output-projection rows (or the next step's input
+// projection) and c the next layer's constants.
+template <typename WT, int M>
+__device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int layer, int j, int p0, Smem& S, RowsB<WT>& R0,
+                                         RowsA<WT>& R1, LayerConsts& c, uint32_t& tag, int& iring, int& cpar, int g, int r) {
+  const LayerW& W = D.layer[layer];
+  const int H = D.H, d = D.d, G = D.nq / D.nkv;
+  const int qrows = (G + 2) * d;          // q/k/v rows owned by one XCD
+  const int qper = qrows / NR;            // rows per rank
+  const int hper = H / NR;                // residual rows per rank (reduce-scatter slice)
+  const int fx = D.F / NX, fper = fx / NR;  // FFN slice per XCD / per rank
+  const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const bool last = layer + 1 == D.n_layers;
+
+  // --- q/k/v slice (R1)
+  rmsnorm_reg<M>(S.xs, H, c.an, D.eps, S.xn, S.red);
+  rows_dot<WT, M>(R1, qper, H, S.xn, H, S.out);
+  __syncthreads();
+  issue_gu(R1, D, W, g, r);
+  if (!slice_gather<M>(D, qper, qrows, [&](int e, int m) { return S.out[e * M + m]; }, S.qkv, tag, iring, g, r)) return false;
+
+  // --- attention for this XCD's heads over positions 0 .. p0 + M - 1 (d = 128). Every rank of the
+  // XCD computes it redundantly from the same gathered q/k/v and keeps its own copy of the frame's
+  // K/V rows of KV head g in LDS (positions are written in order, so rows 0 .. p are this frame's).
+  {
+    float (*kc)[KVS] = S.kvc[layer][0];
+    float (*vc)[KVS] = S.kvc[layer][1];
+    const int vm = wave / (G + 2), vj = wave % (G + 2);
+    if (wave < M * (G + 2)) {  // per-head RMSNorm + RoPE (rotate-half pairs i, i + 64)
+      const float* src = S.qkv + vm * qrows + vj * d;
+      float v0 = src[lane], v1 = src[lane + 64];
+      if (vj <= G) {
+        const float ss = wave_sum(v0 * v0 + v1 * v1);
+        const float sc = 1.0f / sqrtf(ss / (float)d + D.eps);
+        v0 = v0 * sc * c.qk[0];
+        v1 = v1 * sc * c.qk[1];
+        const float a = v0 * c.rc - v1 * c.rs, b = v1 * c.rc + v0 * c.rs;
+        v0 = a;
+        v1 = b;
+      }
+      float* dst = (vj < G) ? S.kq[vj * M + vm] : (vj == G ? kc[p0 + vm] : vc[p0 + vm]);
+      dst[lane] = v0;
+      dst[lane + 64] = v1;
+    }
+    __syncthreads();
+    // scores: thread (row hm = (head, m), position t, eighth of the head dimension)
+    {
+      const int di = tid >> 3, part = tid & 7;
+      const int hm = di / kCpPos, t = di % kCpPos;
+      float s = 0.f;
+      if (hm < G * M) {
+        const float4* qa = reinterpret_cast<const float4*>(&S.kq[hm][16 * part]);
+        const float4* ka = reinterpret_cast<const float4*>(&kc[t][16 * part]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 a = qa[i], b = ka[i];
+          s = fmaf(a.x, b.x, s); s = fmaf(a.y, b.y, s); s = fmaf(a.z, b.z, s); s = fmaf(a.w, b.w, s);
+        }
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      if (part == 0 && hm < G * M) {
+        const int p = p0 + hm % M;
+        S.sc[hm][t] = t <= p ? s * (1.0f / sqrtf((float)d)) : -INFINITY;  // rows past p are stale
+      }
+    }
+    __syncthreads();
+    // causal softmax and output: thread (row hm, dimension i)
+    {
+      const int hm = tid >> 7, i = tid & 127;
+      if (hm < G * M) {
+        const int h = hm / M, m = hm % M, p = p0 + m;
+        float mx = S.sc[hm][0];
+#pragma unroll
+        for (int t = 1; t < kCpPos; ++t) mx = fmaxf(mx, S.sc[hm][t]);
+        float l = 0.f, o = 0.f;
+#pragma unroll
+        for (int t = 0; t < kCpPos; ++t) {
+          const float w = t <= p ? expf(S.sc[hm][t] - mx) : 0.f;
+          l += w;
+          o += t <= p ? w * vc[t][i] : 0.f;
+        }
+        S.ob[m * G * d + h * d + i] = o / l;
+      }
+    }
+    __syncthreads();
+  }
+
+  // --- output projection partial (R0: rows [hper*r, +hper), this XCD's head columns), residual
+  rows_dot<WT, M>(R0, hper, G * d, S.ob, G * d, S.out);
+  __syncthreads();
+  issue_down(R0, D, W, g, r);
+  if (!reduce_gather(D, S, M, H, true, tag, iring, cpar, g, r)) return false;
+
+  // --- gate/up slice (R1) + SwiGLU
+  rmsnorm_reg<M>(S.xs, H, c.mn, D.eps, S.xn, S.red);
+  rows_dot<WT, M>(R1, 2 * fper, H, S.xn, H, S.out);
+  __syncthreads();
+  if (!last) {
+    load_consts<WT, M>(c, D, D.layer[layer + 1], p0);
+    issue_qkv(R1, D, D.layer[layer + 1], g, r);
+  } else {
+    issue_head(R1, D, j);
+  }
+  if (!slice_gather<M>(D, fper, fx, [&](int e, int m) { return silu(S.out[e * M + m]) * S.out[(fper + e) * M + m]; }, S.hb, tag,
+                       iring, g, r))
+    return false;
+
+  // --- down projection partial (R0: rows [hper*r, +hper), this XCD's FFN columns), residual
+  rows_dot<WT, M>(R0, hper, fx, S.hb, fx, S.out);
+  __syncthreads();
+  if (!last) issue_o(R0, D, D.layer[layer + 1], g, r);
+  else if (j < D.n_ac && D.proj) issue_proj(R0, D, g, r);
+  return reduce_gather(D, S, M, H, true, tag, iring, cpar, g, r);
+}
+
+// Argmax over the head rows: each workgroup holds nrows logits of rows [row0, row0 + nrows) in
+// S.out (M = 1). Every workgroup publishes its best (value, id) and reads all NWG candidates.
+// Ties go to the lower id. Returns the id (or -1 on failure).
+__device__ __forceinline__ int argmax_exchange(const CpDesc& D, Smem& S, int nrows, int row0, uint32_t& tag, int& apar) {
+  const int tid = threadIdx.x;
+  ++tag;
+  u64* cb = D.cand + (size_t)(apar & 1) * NWG * CAND;
+  if (tid == 0) {
+    float bv = S.out[0];
+    int bi = row0;
+    for (int i = 1; i < nrows; ++i)
+      if (S.out[i] > bv) { bv = S.out[i]; bi = row0 + i; }
+    st_c(cb + blockIdx.x * CAND, pack(bv, tag));
+    st_c(cb + blockIdx.x * CAND + 1, pack(__int_as_float(bi), tag));
+  }
+  if (!get(cb, NWG, 2, CAND, tag, S.cand, D.err)) return -1;
+  ++apar;
+  __shared__ int best;
+  if (tid < NWG) {
+    float v = S.cand[2 * tid];
+    int id = __float_as_int(S.cand[2 * tid + 1]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float v2 = __shfl_xor(v, o);
+      const int id2 = __shfl_xor(id, o);
+      if (v2 > v || (v2 == v && id2 < id)) { v = v2; id = id2; }
+    }
+    if ((tid & 63) == 0) { S.red[tid >> 6] = v; S.red[8 + (tid >> 6)] = __int_as_float(id); }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float bv = S.red[0];
+    int bi = __float_as_int(S.red[8]);
+    for (int w = 1; w < NWG / 64; ++w) {
+      const float v = S.red[w];
+      const int id = __float_as_int(S.red[8 + w]);
+      if (v > bv || (v == bv && id < bi)) { bv = v; bi = id; }
+    }
+    best = bi;
+  }
+  __syncthreads();
+  return best;
+}
+
+// One CodePredictor step j (1..15) with M input rows; tok = its input token. On entry R0 holds the
+// input projection's rows (when the model has one), R1 layer 0's q/k/v rows and c layer 0's
+// constants; on exit they hold the next step's.
+template <typename WT, int M>
+__device__ __forceinline__ bool cp_step(const CpDesc& D, const CpCall& C, int j, int& tok, Smem& S, RowsB<WT>& R0,
+                                        RowsA<WT>& R1, LayerConsts& c, const float* fn, uint32_t& tag, int& iring, int& cpar,
+                                        int& apar, int frame, int g, int r) {
+  const int H = D.H, Ht = D.Ht, V = D.V, tid = threadIdx.x;
+  const WT* tab = (j == 1) ? reinterpret_cast<const WT*>(D.embed_sem)
+                           : reinterpret_cast<const WT*>(D.embed_ac) + (size_t)(j - 2) * V * Ht;
+  const WT* erow = tab + (size_t)tok * Ht;
+  if (D.proj) {
+    const int kx = Ht / NX, hper = H / NR;
+    for (int i = tid; i < kx; i += NT) {
+      if (M == 2) {
+        S.xn[i] = D.hT[kx * g + i];
+        S.xn[kx + i] = to_f32(erow[kx * g + i]);
+      } else {
+        S.xn[i] = to_f32(erow[kx * g + i]);
+      }
+    }
+    __syncthreads();
+    rows_dot<WT, M>(R0, hper, kx, S.xn, kx, S.out);
+    __syncthreads();
+    issue_o(R0, D, D.layer[0], g, r);
+    if (!reduce_gather(D, S, M, H, false, tag, iring, cpar, g, r)) return false;
+  } else {
+    issue_o(R0, D, D.layer[0], g, r);
+    for (int i = tid; i < H; i += NT) {
+      if (M == 2) {
+        S.xs[i] = D.hT[i];
+        S.xs[H + i] = to_f32(erow[i]);
+      } else {
+        S.xs[i] = to_f32(erow[i]);
+      }
+    }
+    __syncthreads();
+  }
+  const int p0 = (j == 1) ? 0 : j;
+  for (int l = 0; l < D.n_layers; ++l)
+    if (!cp_layer<WT, M>(D, C, l, j, p0, S, R0, R1, c, tag, iring, cpar, g, r)) return false;
+  // final norm on the last row, head j (R1), argmax
+  const int vper = V / NWG;
+  rmsnorm_reg<1>(S.xs + (M - 1) * H, H, fn, D.eps, S.xn, S.red);
+  rows_dot<WT, 1>(R1, vper, H, S.xn, H, S.out);
+  __syncthreads();
+  if (j < D.n_ac) {
+    load_consts<WT, 1>(c, D, D.layer[0], j + 1);
+    issue_qkv(R1, D, D.layer[0], g, r);
+  }
+  if (C.logits)
+    for (int i = tid; i < vper; i += NT) C.logits[(size_t)(j - 1) * V + vper * blockIdx.x + i] = S.out[i];
+  const int a = argmax_exchange(D, S, vper, vper * blockIdx.x, tag, apar);
+  if (a < 0) return false;
+  if (blockIdx.x == 0 && tid == 0) C.codes[(C.use_frame ? (long)frame * C.f_stride : 0) + j - 1] = a;
+  tok = C.forced ? C.forced[j - 1] : a;
+  if (tok < 0) tok = 0;
+  if (tok >= V) tok = V - 1;
+  return true;
+}
+
+template <typename WT>
+__global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
+  const CpDesc& D = *C.desc;
+  __shared__ Smem S;
+  const int g = blockIdx.x % NX, r = blockIdx.x / NX;
+  // constants first (they are needed first), then the first two weight phases
+  LayerConsts c;
+  load_consts<WT, 2>(c, D, D.layer[0], 0);
+  float fn[2];
+  {
+    const WT* f = reinterpret_cast<const WT*>(D.final_norm);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) fn[k] = threadIdx.x + k * NT < D.H ? to_f32(f[threadIdx.x + k * NT]) : 0.f;
+  }
+  RowsB<WT> R0;
+  RowsA<WT> R1;
+  if (D.proj) issue_proj(R0, D, g, r);
+  issue_qkv(R1, D, D.layer[0], g, r);
+  uint32_t tag = D.st->epoch;
+  const int frame = D.st->frame;
+  int iring = 0, cpar = 0, apar = 0;
+  int tok = C.semantic[0];
+  if (tok < 0) tok = 0;
+  if (tok >= D.Vs) tok = D.Vs - 1;
+  bool ok = cp_step<WT, 2>(D, C, 1, tok, S, R0, R1, c, fn, tag, iring, cpar, apar, frame, g, r);
+  for (int j = 2; ok && j <= D.n_ac; ++j) ok = cp_step<WT, 1>(D, C, j, tok, S, R0, R1, c, fn, tag, iring, cpar, apar, frame, g, r);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    D.st->epoch = tag + 1;  // every workgroup has read the epoch: all took part in the last exchange
+    if (C.next_tok) C.next_tok[0] = tok;
+  }
+}
+
+}  // namespace xtp
+}  // namespace tts

@@ -144,11 +144,33 @@ int tts_sample(tts_ctx* ctx, const float* logits, int32_t batch, int32_t vocab, 
 int tts_run_frames(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_sampling* ac, const float* u,
                    int32_t* codes);
 
+/* Execution of the CodePredictor frame (same results either way, up to
+ * floating-point summation order):
+ *  TTS_EXEC_PERSISTENT (default where supported): one persistent kernel runs
+ *    all 15 steps, its workgroups split across the 8 XCDs tensor-parallel and
+ *    exchanging tagged values instead of ending kernels. Used for batch 1 with
+ *    greedy acoustic tokens on bf16-weight configs whose CodePredictor has
+ *    8 KV heads of dimension 128; other calls use the per-op kernels.
+ *  TTS_EXEC_KERNELS: one kernel per op.
+ * Switching drops the captured frame graph. TTS_E_UNSUPPORTED if the config
+ * cannot run persistent. */
+enum tts_exec_mode { TTS_EXEC_KERNELS = 0, TTS_EXEC_PERSISTENT = 1 };
+int tts_set_exec_mode(tts_ctx* ctx, int32_t mode);
+int tts_get_exec_mode(const tts_ctx* ctx, int32_t* mode, int32_t* persistent_supported);
+
+/* Synchronise the context's stream and report the persistent kernel's
+ * exchange status: *status = 0 when every exchange completed, nonzero when a
+ * workgroup timed out waiting (e.g. not all workgroups were resident); the
+ * affected outputs are then invalid. */
+int tts_device_status(tts_ctx* ctx, int32_t* status);
+
 /* Host-side counters: Talker positions written so far and frames generated
  * since the last prefill. Either pointer may be NULL. */
 int tts_get_progress(const tts_ctx* ctx, int32_t* talker_pos, int32_t* frames);
 
-/* Forget the streams (positions, frames, histories). Weights stay bound. */
+/* Forget the streams (positions, frames, histories) and clear the persistent
+ * kernel's exchange state, including a failure reported by
+ * tts_device_status. Weights stay bound. */
 int tts_reset(tts_ctx* ctx);
 
 /* Text of the last error on this context ("" if none). Valid until the next

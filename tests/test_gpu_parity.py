@@ -318,7 +318,10 @@ def bf16_model(request):
     return request.param, model, w
 
 
-def test_bf16_teacher_forced_step_parity(bf16_model):
+@pytest.mark.parametrize("mode", ["persistent", "kernels"])
+def test_bf16_teacher_forced_step_parity(bf16_model, mode):
+    """Both CodePredictor executions against the oracle: the persistent XCD-split
+    kernel (the default at batch 1 with greedy acoustic tokens) and the per-op kernels."""
     name, model, w = bf16_model
     orc = OracleModel(w, model.as_dict(), np.float32)
     ids = synth.random_ids(16, model.text_vocab, seed=1)
@@ -326,9 +329,44 @@ def test_bf16_teacher_forced_step_parity(bf16_model):
     ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((1, F, 16), np.float32))
     del orc
     dec, dw = make_decoder(model, 1, 64 + 240, 240, w)
+    _, supported = dec.exec_mode()
+    assert supported, f"{name}: the persistent CodePredictor should support this config"
+    dec.set_exec_mode(tts.EXEC_PERSISTENT if mode == "persistent" else tts.EXEC_KERNELS)
+    assert dec.exec_mode()[0] == (tts.EXEC_PERSISTENT if mode == "persistent" else tts.EXEC_KERNELS)
+    print(f"{name} {mode}: running", flush=True)
     sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F)
+    assert dec.device_status() == 0
     es, ea, n, ex = check_step_parity(model, ref, sem, ac, tok, 1e-2)
-    print(f"{name}: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}")
+    print(f"{name} {mode}: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}")
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
+def test_bf16_run_frames_greedy_both_modes_match_oracle_until_a_near_tie(bf16_model):
+    """The captured frame graph, free-running, with the persistent CodePredictor and with the
+    per-op kernels; codes must equal the oracle's up to the first step the oracle finds near a tie."""
+    name, model, w = bf16_model
+    F = 8
+    ids = synth.random_ids(16, model.text_vocab, seed=3)
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((1, F, 16), np.float32))
+    del orc
+    dec, dw = make_decoder(model, 1, 64, F + 4, w)
+    d = dev()
+    for mode in (tts.EXEC_PERSISTENT, tts.EXEC_KERNELS):
+        dec.set_exec_mode(mode)
+        codes = torch.full((1, F + 4, 16), -1, dtype=torch.int32, device=d)
+        dec.prefill(torch.from_numpy(ids).to(d))
+        dec.run_frames(F, GREEDY, GREEDY, None, codes)
+        assert dec.device_status() == 0
+        got = codes.cpu().numpy()[:, :F].reshape(-1)
+        diff = np.nonzero(got != ref["codes"].reshape(-1))[0]
+        if diff.size:
+            t, j = divmod(int(diff[0]), 16)
+            lg = ref["sem_logits"][0, t] if j == 0 else ref["ac_logits"][0, t, j - 1]
+            assert top2_margin(lg) <= 0.05, f"{name} mode {mode}: divergence at frame {t} code {j}, margin {top2_margin(lg):.3f}"
+        print(f"{name} mode {mode}: identical for {diff[0] if diff.size else got.size} of {got.size} codes", flush=True)
     dec.close()
     del dw
     torch.cuda.empty_cache()

@@ -42,7 +42,7 @@ constexpr int KVS = 132;    // LDS row stride of the K/V rows (padded against ba
 constexpr int RA_R = 3, RA_K = 2;
 constexpr int RB_R = 4, RB_K = 1;
 constexpr int RING = 4;     // intra exchange buffers per XCD
-constexpr int ISZ = 2 * HMAX;  // intra buffer entries (2 rows x HMAX)
+constexpr int ISZ = 2 * HMAX + 128;  // intra buffer entries (2 rows x HMAX, sums of squares)
 constexpr int CSZ = 2 * 64;    // cross slot entries (2 rows x 64)
 constexpr int CAND = 8;        // candidate slot entries (one 64-byte line)
 constexpr long long kSpin = 4000000;
@@ -84,46 +84,54 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 __device__ __forceinline__ u64 pack(float v, uint32_t tag) { return ((u64)tag << 32) | __float_as_uint(v); }
 __device__ __forceinline__ uint32_t tagof(u64 v) { return (uint32_t)(v >> 32); }
 __device__ __forceinline__ float valof(u64 v) { return __uint_as_float((uint32_t)v); }
-__device__ __forceinline__ void st_c(u64* p, u64 v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
-__device__ __forceinline__ u64 ld_c(const u64* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// Every pointer the kernel follows comes out of the descriptor in device memory, so the compiler
+// cannot tell it is global and would emit flat instructions, which also count against the LDS
+// counter: each LDS wait before a barrier would then wait for all weight rows in flight. All
+// global accesses therefore go through explicitly global (address space 1) pointers.
+#define GLB __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ GLB T* glb(T* p) { return (GLB T*)p; }
+template <typename T>
+__device__ __forceinline__ const GLB T* glb(const T* p) { return (const GLB T*)p; }
 
-// Publish n values of vals (LDS) as tagged entries at dst.
-__device__ __forceinline__ void put(u64* dst, const float* vals, int n, uint32_t tag) {
-  for (int i = threadIdx.x; i < n; i += NT) st_c(dst + i, pack(vals[i], tag));
-}
+__device__ __forceinline__ void st_c(u64* p, u64 v) { __hip_atomic_store(glb(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ u64 ld_c(const u64* p) { return __hip_atomic_load(glb(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
 // Gather nseg segments of len entries into lds[0 .. nseg*len), polling until every entry carries
-// tag. With inner == 1 segment s starts at src + s * sstride; otherwise segment s = (a, b), a = s / inner,
-// b = s % inner, starts at src + a * astride + b * 64. n <= 4 * NT.
-// Returns false (and flags err) on time-out or when another workgroup failed.
+// tag; an entry already received is not read again. With inner == 1 segment s starts at
+// src + s * sstride; otherwise segment s = (a, b), a = s / inner, b = s % inner, starts at
+// src + a * astride + b * 64. n <= KMAX * NT. Returns false (and flags err) on time-out or when
+// another workgroup failed.
+template <int KMAX>
 __device__ __forceinline__ bool get(const u64* src, int nseg, int len, int sstride, uint32_t tag, float* lds, uint32_t* err,
                                     int inner = 1, int astride = 0) {
   const int n = nseg * len;
+  // address of this thread's k-th entry
+  auto at = [&](int k) -> const u64* {
+    const int i = threadIdx.x + k * NT, seg = i / len, e = i % len;
+    const size_t off = (inner == 1) ? (size_t)seg * sstride : (size_t)(seg / inner) * astride + (size_t)(seg % inner) * 64;
+    return src + off + e;
+  };
+  unsigned pend = 0;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k)
+    if (threadIdx.x + k * NT < n) pend |= 1u << k;
   for (long long s = 0;; ++s) {
-    u64 v[4];
+    u64 v[KMAX];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = threadIdx.x + k * NT;
-      if (i < n) {
-        const int seg = i / len, e = i % len;
-        const size_t off = (inner == 1) ? (size_t)seg * sstride : (size_t)(seg / inner) * astride + (size_t)(seg % inner) * 64;
-        v[k] = ld_c(src + off + e);
-      }
-    }
-    int ok = 1;
+    for (int k = 0; k < KMAX; ++k)
+      if (pend & (1u << k)) v[k] = ld_c(at(k));
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = threadIdx.x + k * NT;
-      if (i < n) {
-        if (tagof(v[k]) != tag) ok = 0;
-        else lds[i] = valof(v[k]);
+    for (int k = 0; k < KMAX; ++k)
+      if ((pend & (1u << k)) && tagof(v[k]) == tag) {
+        lds[threadIdx.x + k * NT] = valof(v[k]);
+        pend &= ~(1u << k);
       }
-    }
-    if (__syncthreads_and(ok)) return true;
+    if (__syncthreads_and(pend == 0)) return true;
     if ((s & 255) == 255) {
-      const uint32_t e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t e = __hip_atomic_load(glb(err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (__syncthreads_or(e != 0 || s > kSpin)) {
-        if (threadIdx.x == 0) atomicOr(err, 1u);
+        if (threadIdx.x == 0) __hip_atomic_fetch_or(glb(err), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
       }
     }
@@ -150,7 +158,7 @@ __device__ __forceinline__ void rows_issue(Rows<WT, RR, KK>& R, int nrows, int n
   for (int j = 0; j < MAXR; ++j) {
     const int i = wave + NW * j;
     if (i < nrows) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(rowptr(i));
+      const GLB u32x4* p = glb(reinterpret_cast<const u32x4*>(rowptr(i)));
 #pragma unroll
       for (int k = 0; k < MAXK; ++k) {
         const int u = lane + 64 * k;
@@ -220,15 +228,14 @@ __device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, i
 
 // Shared memory layout (floats). Row m of a residual-width array starts at m * H.
 struct Smem {
-  float xs[2 * HMAX];   // residual rows (full)
+  float xs[2 * HMAX + 2 * NR];  // residual rows (full), then per-rank sums of squares per row
   float xn[2 * HMAX];   // normed / staged input rows; reduce-scatter partials
   float qkv[2 * 512];   // this XCD's q/k/v slice
   float ob[2 * 256];    // attention output of this XCD's heads
   float hb[2 * 768];    // SwiGLU slice
   float out[2 * 128];   // row results of this workgroup
   float red[64];
-  float kq[4][128];     // normed + rotated q (G x M vectors) for attention
-  float sc[4][kCpPos];  // attention scores (G x M rows)
+  float kq[4][128];     // normed + rotated q of each attention wave
   float cand[2 * NWG];  // argmax candidates of every workgroup
   float kvc[MAXL][2][kCpPos][KVS];  // this frame's K/V rows of KV head g, per layer
 };
@@ -295,57 +302,74 @@ __device__ __forceinline__ void issue_proj(RowsB<WT>& R, const CpDesc& D, int g,
 }
 
 // ---------------------------------------------------------------------------- exchanges
+// Each exchange publishes this workgroup's values first and only then runs after_put (which
+// issues the next weight rows): issuing loads can stall while the memory pipeline is busy, and
+// other workgroups are waiting for the values, not for this workgroup's weights.
 
 // Cross reduce-scatter of this workgroup's hper x M partial rows (S.out, row-major [row][m]) with
 // rank r of every XCD, plus an optional residual (S.xs), then the intra gather of the full rows into
-// S.xs. cpar alternates the cross slot so a rank one exchange ahead never overwrites unread values.
-__device__ __forceinline__ bool reduce_gather(const CpDesc& D, Smem& S, int M, int H, bool residual, uint32_t& tag, int& iring, int& cpar,
-                              int g, int r) {
+// S.xs[0 .. M*H). With the rows each rank also publishes the sum of squares of its reduced rows,
+// gathered into S.xs[M*H + m*NR + rank], so the next RMSNorm needs no reduction of its own.
+// cpar alternates the cross slot so a rank one exchange ahead never overwrites unread values.
+template <int M, typename AfterPut>
+__device__ __forceinline__ bool reduce_gather(const CpDesc& D, Smem& S, int H, bool residual, uint32_t& tag, int& iring, int& cpar,
+                                              int g, int r, AfterPut after_put) {
   const int tid = threadIdx.x, hper = H / NR;
   ++tag;
   u64* mine = D.xcr + ((size_t)blockIdx.x * 2 + (cpar & 1)) * CSZ;
   for (int i = tid; i < hper * M; i += NT) st_c(mine + (i % M) * 64 + i / M, pack(S.out[i], tag));
+  after_put();
   // partners: rank r on every XCD = blocks r * NX + x; their slots are 2 * CSZ apart.
   // Segment (x, m) -> S.xn[(x * M + m) * hper ..]
   const u64* base = D.xcr + ((size_t)(r * NX) * 2 + (cpar & 1)) * CSZ;
-  if (!get(base, NX * M, hper, 2 * CSZ, tag, S.xn, D.err, M, 2 * CSZ)) return false;
+  if (!get<1>(base, NX * M, hper, 2 * CSZ, tag, S.xn, D.err, M, 2 * CSZ)) return false;
   ++cpar;
   ++tag;
   u64* buf = D.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
-  for (int i = tid; i < hper * M; i += NT) {
-    const int e = i / M, m = i % M;
+  if (tid < 64) {  // hper * M <= 64: wave 0 reduces and publishes this rank's rows
+    const int e = tid / M, m = tid % M;
     const int row = hper * r + e;
-    float v = residual ? S.xs[m * H + row] : 0.f;
+    const bool live = tid < hper * M;
+    float v = 0.f;
+    if (live) {
+      v = residual ? S.xs[m * H + row] : 0.f;
 #pragma unroll
-    for (int x = 0; x < NX; ++x) v += S.xn[(x * M + m) * hper + e];
-    st_c(buf + m * H + row, pack(v, tag));
+      for (int x = 0; x < NX; ++x) v += S.xn[(x * M + m) * hper + e];
+      st_c(buf + m * H + row, pack(v, tag));
+    }
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm) {
+      const float ss = wave_sum(live && m == mm ? v * v : 0.f);
+      if (tid == 0) st_c(buf + M * H + mm * NR + r, pack(ss, tag));
+    }
   }
   __syncthreads();  // the gather below overwrites the residual rows read above
-  return get(buf, M, H, H, tag, S.xs, D.err);
+  return get<(M * (HMAX + NR) + NT - 1) / NT>(buf, 1, M * (H + NR), 0, tag, S.xs, D.err);
 }
 
 // Intra gather of a slice: this workgroup's n values per row (vals(e, m)) land at row offset
 // n * r of every rank's copy; the full rows (width w) of all ranks go to dst.
-template <int M, typename ValFn>
+template <int M, int KMAX, typename ValFn, typename AfterPut>
 __device__ __forceinline__ bool slice_gather(const CpDesc& D, int n, int w, ValFn vals, float* dst, uint32_t& tag, int& iring,
-                                             int g, int r) {
+                                             int g, int r, AfterPut after_put) {
   ++tag;
   u64* buf = D.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
   for (int i = threadIdx.x; i < n * M; i += NT) {
     const int e = i / M, m = i % M;
     st_c(buf + m * w + n * r + e, pack(vals(e, m), tag));
   }
-  return get(buf, M, w, w, tag, dst, D.err);
+  after_put();
+  return get<KMAX>(buf, M, w, w, tag, dst, D.err);
 }
 
 // ---------------------------------------------------------------------------- per-thread constants
 
 // Norm gains and RoPE factors a layer needs, held in registers so no global load sits on the
-// critical path: residual-norm gains of elements tid and tid + NT (H <= 2 NT), and for waves that
-// normalise a q/k vector (one wave per vector of row vm, slot vj) the head-norm gains of lanes
-// lane, lane + 64 and the RoPE cos/sin of position p0 + vm.
+// critical path: residual-norm gains of elements tid and tid + NT (H <= 2 NT), and for the
+// attention waves the q- and k-norm gains of lanes lane, lane + 64 and the RoPE cos/sin of
+// positions p0 .. p0 + M - 1 at lane.
 struct LayerConsts {
-  float an[2], mn[2], qk[2], rc, rs;
+  float an[2], mn[2], qg[2], kg[2], rc[2], rs[2];
 };
 
 template <typename WT, int M>
@@ -356,45 +380,69 @@ __device__ __forceinline__ void load_consts(LayerConsts& c, const CpDesc& D, con
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int i = tid + k * NT;
-    c.an[k] = i < D.H ? to_f32(an[i]) : 0.f;
-    c.mn[k] = i < D.H ? to_f32(mn[i]) : 0.f;
+    c.an[k] = i < D.H ? to_f32(glb(an)[i]) : 0.f;
+    c.mn[k] = i < D.H ? to_f32(glb(mn)[i]) : 0.f;
   }
-  const int vm = wave / (G + 2), vj = wave % (G + 2);
-  c.qk[0] = c.qk[1] = 1.f;
-  c.rc = 1.f;
-  c.rs = 0.f;
-  if (wave < M * (G + 2) && vj <= G) {
-    const WT* gn = reinterpret_cast<const WT*>(vj < G ? W.q_norm : W.k_norm);
-    c.qk[0] = to_f32(gn[lane]);
-    c.qk[1] = to_f32(gn[lane + 64]);
-    c.rc = D.rope_cos[(p0 + vm) * 64 + lane];
-    c.rs = D.rope_sin[(p0 + vm) * 64 + lane];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) { c.qg[k] = c.kg[k] = c.rc[k] = 1.f; c.rs[k] = 0.f; }
+  if (wave < G * M) {
+    const WT* qn = reinterpret_cast<const WT*>(W.q_norm);
+    const WT* kn = reinterpret_cast<const WT*>(W.k_norm);
+    c.qg[0] = to_f32(glb(qn)[lane]);
+    c.qg[1] = to_f32(glb(qn)[lane + 64]);
+    c.kg[0] = to_f32(glb(kn)[lane]);
+    c.kg[1] = to_f32(glb(kn)[lane + 64]);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      c.rc[m] = glb(D.rope_cos)[(p0 + m) * 64 + lane];
+      c.rs[m] = glb(D.rope_sin)[(p0 + m) * 64 + lane];
+    }
   }
 }
 
 // y[m] = x[m] * rsqrt(mean(x[m]^2) + eps) * gain over n <= 2 NT elements (rows n apart in LDS),
-// gain of elements tid, tid + NT in gr.
+// gain of elements tid, tid + NT in gr. ss: the per-rank sums of squares of row m at ss[m * NR ..]
+// (from reduce_gather), or nullptr to reduce here.
 template <int M>
-__device__ __forceinline__ void rmsnorm_reg(const float* x, int n, const float* gr, float eps, float* y, float* red) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+__device__ __forceinline__ void rmsnorm_reg(const float* x, int n, const float* gr, float eps, float* y, float* red,
+                                            const float* ss = nullptr) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float tot[M];
+  if (ss) {
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    float s = 0.f;
+    for (int m = 0; m < M; ++m) {
+      float s = 0.f;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid + k * NT;
-      if (i < n) s += x[m * n + i] * x[m * n + i];
+      for (int q = 0; q < NR; q += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(ss + m * NR + q);
+        s += (f.x + f.y) + (f.z + f.w);
+      }
+      tot[m] = s;
     }
-    s = wave_sum(s);
-    if (lane == 0) red[m * NW + wave] = s;
+  } else {
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float s = 0.f;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int i = tid + k * NT;
+        if (i < n) s += x[m * n + i] * x[m * n + i];
+      }
+      s = wave_sum(s);
+      if (lane == 0) red[m * NW + wave] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) s += red[m * NW + w];
+      tot[m] = s;
+    }
   }
-  __syncthreads();
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    float s = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) s += red[m * NW + w];
-    const float sc = 1.0f / sqrtf(s / (float)n + eps);
+    const float sc = 1.0f / sqrtf(tot[m] / (float)n + eps);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int i = tid + k * NT;
@@ -410,10 +458,12 @@ __device__ __forceinline__ void rmsnorm_reg(const float* x, int n, const float* 
 // register buffers and are issued two phases ahead of their use. On entry R1 holds this layer's
 // q/k/v rows, R0 its output-projection rows and c its constants; on exit R1 holds the next layer's
 // q/k/v rows (or head j), R0 the next layer's output-projection rows (or the next step's input
-// projection) and c the next layer's constants.
+// projection) and c the next layer's constants. have_ss: S.xs carries the per-rank sums of squares
+// of the input rows (it does unless the rows were staged without an exchange).
 template <typename WT, int M>
-__device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int layer, int j, int p0, Smem& S, RowsB<WT>& R0,
-                                         RowsA<WT>& R1, LayerConsts& c, uint32_t& tag, int& iring, int& cpar, int g, int r) {
+__device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int layer, int j, int p0, bool have_ss, Smem& S,
+                                         RowsB<WT>& R0, RowsA<WT>& R1, LayerConsts& c, uint32_t& tag, int& iring, int& cpar,
+                                         int g, int r) {
   const LayerW& W = D.layer[layer];
   const int H = D.H, d = D.d, G = D.nq / D.nkv;
   const int qrows = (G + 2) * d;          // q/k/v rows owned by one XCD
@@ -424,106 +474,106 @@ __device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int l
   const bool last = layer + 1 == D.n_layers;
 
   // --- q/k/v slice (R1)
-  rmsnorm_reg<M>(S.xs, H, c.an, D.eps, S.xn, S.red);
+  rmsnorm_reg<M>(S.xs, H, c.an, D.eps, S.xn, S.red, have_ss ? S.xs + M * H : nullptr);
   rows_dot<WT, M>(R1, qper, H, S.xn, H, S.out);
   __syncthreads();
-  issue_gu(R1, D, W, g, r);
-  if (!slice_gather<M>(D, qper, qrows, [&](int e, int m) { return S.out[e * M + m]; }, S.qkv, tag, iring, g, r)) return false;
+  if (!slice_gather<M, M>(D, qper, qrows, [&](int e, int m) { return S.out[e * M + m]; }, S.qkv, tag, iring, g, r,
+                          [&] { issue_gu(R1, D, W, g, r); }))
+    return false;
 
-  // --- attention for this XCD's heads over positions 0 .. p0 + M - 1 (d = 128). Every rank of the
-  // XCD computes it redundantly from the same gathered q/k/v and keeps its own copy of the frame's
-  // K/V rows of KV head g in LDS (positions are written in order, so rows 0 .. p are this frame's).
-  {
+  // --- attention for this XCD's heads over positions 0 .. p0 + M - 1 (d = 128): one wave per
+  // (head h, row m). Every rank of the XCD computes it redundantly from the same gathered q/k/v
+  // and keeps its own copy of the frame's K/V rows of KV head g in LDS (positions are written in
+  // order, so rows 0 .. p are this frame's). Each attention wave normalises and rotates the step's
+  // k rows itself and appends them (the waves write identical values), so no barrier separates
+  // the append from the scores.
+  if (wave < G * M) {
     float (*kc)[KVS] = S.kvc[layer][0];
     float (*vc)[KVS] = S.kvc[layer][1];
-    const int vm = wave / (G + 2), vj = wave % (G + 2);
-    if (wave < M * (G + 2)) {  // per-head RMSNorm + RoPE (rotate-half pairs i, i + 64)
-      const float* src = S.qkv + vm * qrows + vj * d;
-      float v0 = src[lane], v1 = src[lane + 64];
-      if (vj <= G) {
-        const float ss = wave_sum(v0 * v0 + v1 * v1);
-        const float sc = 1.0f / sqrtf(ss / (float)d + D.eps);
-        v0 = v0 * sc * c.qk[0];
-        v1 = v1 * sc * c.qk[1];
-        const float a = v0 * c.rc - v1 * c.rs, b = v1 * c.rc + v0 * c.rs;
-        v0 = a;
-        v1 = b;
-      }
-      float* dst = (vj < G) ? S.kq[vj * M + vm] : (vj == G ? kc[p0 + vm] : vc[p0 + vm]);
-      dst[lane] = v0;
-      dst[lane + 64] = v1;
+    const int h = wave / M, m = wave % M, p = p0 + m;
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm) {
+      const float* kr = S.qkv + mm * qrows + G * d;
+      float k0 = kr[lane], k1 = kr[lane + 64];
+      const float sc = 1.0f / sqrtf(wave_sum(k0 * k0 + k1 * k1) / (float)d + D.eps);
+      k0 *= sc * c.kg[0];
+      k1 *= sc * c.kg[1];
+      kc[p0 + mm][lane] = k0 * c.rc[mm] - k1 * c.rs[mm];
+      kc[p0 + mm][lane + 64] = k1 * c.rc[mm] + k0 * c.rs[mm];
+      vc[p0 + mm][lane] = kr[d + lane];
+      vc[p0 + mm][lane + 64] = kr[d + lane + 64];
     }
-    __syncthreads();
-    // scores: thread (row hm = (head, m), position t, eighth of the head dimension)
     {
-      const int di = tid >> 3, part = tid & 7;
-      const int hm = di / kCpPos, t = di % kCpPos;
-      float s = 0.f;
-      if (hm < G * M) {
-        const float4* qa = reinterpret_cast<const float4*>(&S.kq[hm][16 * part]);
-        const float4* ka = reinterpret_cast<const float4*>(&kc[t][16 * part]);
+      const float* qr = S.qkv + m * qrows + h * d;
+      float q0 = qr[lane], q1 = qr[lane + 64];
+      const float sc = 1.0f / sqrtf(wave_sum(q0 * q0 + q1 * q1) / (float)d + D.eps);
+      q0 *= sc * c.qg[0];
+      q1 *= sc * c.qg[1];
+      // (select, not index: a dynamic index would move c out of registers)
+      const float rc = (M == 2 && m == 1) ? c.rc[1] : c.rc[0], rs = (M == 2 && m == 1) ? c.rs[1] : c.rs[0];
+      S.kq[wave][lane] = q0 * rc - q1 * rs;
+      S.kq[wave][lane + 64] = q1 * rc + q0 * rs;
+    }
+    // scores: lane = 4 t + e, position t (0..15) and quarter e of the head dimension
+    const int t = lane >> 2, e = lane & 3;
+    float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 a = qa[i], b = ka[i];
-          s = fmaf(a.x, b.x, s); s = fmaf(a.y, b.y, s); s = fmaf(a.z, b.z, s); s = fmaf(a.w, b.w, s);
-        }
-      }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      if (part == 0 && hm < G * M) {
-        const int p = p0 + hm % M;
-        S.sc[hm][t] = t <= p ? s * (1.0f / sqrtf((float)d)) : -INFINITY;  // rows past p are stale
+    for (int i = 0; i < 8; ++i) {
+      const float4 a = *reinterpret_cast<const float4*>(&S.kq[wave][32 * e + 4 * i]);
+      const float4 b = *reinterpret_cast<const float4*>(&kc[t][32 * e + 4 * i]);
+      s = fmaf(a.x, b.x, s); s = fmaf(a.y, b.y, s); s = fmaf(a.z, b.z, s); s = fmaf(a.w, b.w, s);
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s = t <= p ? s * (1.0f / sqrtf((float)d)) : -INFINITY;  // rows past p hold stale values
+    float mx = s;
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float w = t <= p ? expf(s - mx) : 0.f;
+    float l = w;
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1) l += __shfl_xor(l, o);
+    float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < kCpPos; ++tt) {
+      if (tt <= p) {
+        const float wt = __shfl(w, 4 * tt);
+        o0 = fmaf(wt, vc[tt][lane], o0);
+        o1 = fmaf(wt, vc[tt][lane + 64], o1);
       }
     }
-    __syncthreads();
-    // causal softmax and output: thread (row hm, dimension i)
-    {
-      const int hm = tid >> 7, i = tid & 127;
-      if (hm < G * M) {
-        const int h = hm / M, m = hm % M, p = p0 + m;
-        float mx = S.sc[hm][0];
-#pragma unroll
-        for (int t = 1; t < kCpPos; ++t) mx = fmaxf(mx, S.sc[hm][t]);
-        float l = 0.f, o = 0.f;
-#pragma unroll
-        for (int t = 0; t < kCpPos; ++t) {
-          const float w = t <= p ? expf(S.sc[hm][t] - mx) : 0.f;
-          l += w;
-          o += t <= p ? w * vc[t][i] : 0.f;
-        }
-        S.ob[m * G * d + h * d + i] = o / l;
-      }
-    }
-    __syncthreads();
+    S.ob[m * G * d + h * d + lane] = o0 / l;
+    S.ob[m * G * d + h * d + lane + 64] = o1 / l;
   }
+  __syncthreads();
 
   // --- output projection partial (R0: rows [hper*r, +hper), this XCD's head columns), residual
   rows_dot<WT, M>(R0, hper, G * d, S.ob, G * d, S.out);
   __syncthreads();
-  issue_down(R0, D, W, g, r);
-  if (!reduce_gather(D, S, M, H, true, tag, iring, cpar, g, r)) return false;
+  if (!reduce_gather<M>(D, S, H, true, tag, iring, cpar, g, r, [&] { issue_down(R0, D, W, g, r); })) return false;
 
   // --- gate/up slice (R1) + SwiGLU
-  rmsnorm_reg<M>(S.xs, H, c.mn, D.eps, S.xn, S.red);
+  rmsnorm_reg<M>(S.xs, H, c.mn, D.eps, S.xn, S.red, S.xs + M * H);
   rows_dot<WT, M>(R1, 2 * fper, H, S.xn, H, S.out);
   __syncthreads();
-  if (!last) {
-    load_consts<WT, M>(c, D, D.layer[layer + 1], p0);
-    issue_qkv(R1, D, D.layer[layer + 1], g, r);
-  } else {
-    issue_head(R1, D, j);
-  }
-  if (!slice_gather<M>(D, fper, fx, [&](int e, int m) { return silu(S.out[e * M + m]) * S.out[(fper + e) * M + m]; }, S.hb, tag,
-                       iring, g, r))
+  if (!slice_gather<M, M>(D, fper, fx, [&](int e, int m) { return silu(S.out[e * M + m]) * S.out[(fper + e) * M + m]; }, S.hb,
+                          tag, iring, g, r, [&] {
+                            if (!last) {
+                              load_consts<WT, M>(c, D, D.layer[layer + 1], p0);
+                              issue_qkv(R1, D, D.layer[layer + 1], g, r);
+                            } else {
+                              issue_head(R1, D, j);
+                            }
+                          }))
     return false;
 
   // --- down projection partial (R0: rows [hper*r, +hper), this XCD's FFN columns), residual
   rows_dot<WT, M>(R0, hper, fx, S.hb, fx, S.out);
   __syncthreads();
-  if (!last) issue_o(R0, D, D.layer[layer + 1], g, r);
-  else if (j < D.n_ac && D.proj) issue_proj(R0, D, g, r);
-  return reduce_gather(D, S, M, H, true, tag, iring, cpar, g, r);
+  return reduce_gather<M>(D, S, H, true, tag, iring, cpar, g, r, [&] {
+    if (!last) issue_o(R0, D, D.layer[layer + 1], g, r);
+    else if (j < D.n_ac && D.proj) issue_proj(R0, D, g, r);
+  });
 }
 
 // Argmax over the head rows: each workgroup holds nrows logits of rows [row0, row0 + nrows) in
@@ -541,7 +591,7 @@ __device__ __forceinline__ int argmax_exchange(const CpDesc& D, Smem& S, int nro
     st_c(cb + blockIdx.x * CAND, pack(bv, tag));
     st_c(cb + blockIdx.x * CAND + 1, pack(__int_as_float(bi), tag));
   }
-  if (!get(cb, NWG, 2, CAND, tag, S.cand, D.err)) return -1;
+  if (!get<1>(cb, NWG, 2, CAND, tag, S.cand, D.err)) return -1;
   ++apar;
   __shared__ int best;
   if (tid < NWG) {
@@ -585,35 +635,34 @@ __device__ __forceinline__ bool cp_step(const CpDesc& D, const CpCall& C, int j,
     const int kx = Ht / NX, hper = H / NR;
     for (int i = tid; i < kx; i += NT) {
       if (M == 2) {
-        S.xn[i] = D.hT[kx * g + i];
-        S.xn[kx + i] = to_f32(erow[kx * g + i]);
+        S.xn[i] = glb(D.hT)[kx * g + i];
+        S.xn[kx + i] = to_f32(glb(erow)[kx * g + i]);
       } else {
-        S.xn[i] = to_f32(erow[kx * g + i]);
+        S.xn[i] = to_f32(glb(erow)[kx * g + i]);
       }
     }
     __syncthreads();
     rows_dot<WT, M>(R0, hper, kx, S.xn, kx, S.out);
     __syncthreads();
-    issue_o(R0, D, D.layer[0], g, r);
-    if (!reduce_gather(D, S, M, H, false, tag, iring, cpar, g, r)) return false;
+    if (!reduce_gather<M>(D, S, H, false, tag, iring, cpar, g, r, [&] { issue_o(R0, D, D.layer[0], g, r); })) return false;
   } else {
     issue_o(R0, D, D.layer[0], g, r);
     for (int i = tid; i < H; i += NT) {
       if (M == 2) {
-        S.xs[i] = D.hT[i];
-        S.xs[H + i] = to_f32(erow[i]);
+        S.xs[i] = glb(D.hT)[i];
+        S.xs[H + i] = to_f32(glb(erow)[i]);
       } else {
-        S.xs[i] = to_f32(erow[i]);
+        S.xs[i] = to_f32(glb(erow)[i]);
       }
     }
     __syncthreads();
   }
   const int p0 = (j == 1) ? 0 : j;
   for (int l = 0; l < D.n_layers; ++l)
-    if (!cp_layer<WT, M>(D, C, l, j, p0, S, R0, R1, c, tag, iring, cpar, g, r)) return false;
+    if (!cp_layer<WT, M>(D, C, l, j, p0, l > 0 || D.proj, S, R0, R1, c, tag, iring, cpar, g, r)) return false;
   // final norm on the last row, head j (R1), argmax
   const int vper = V / NWG;
-  rmsnorm_reg<1>(S.xs + (M - 1) * H, H, fn, D.eps, S.xn, S.red);
+  rmsnorm_reg<1>(S.xs + (M - 1) * H, H, fn, D.eps, S.xn, S.red, S.xs + M * H + (M - 1) * NR);
   rows_dot<WT, 1>(R1, vper, H, S.xn, H, S.out);
   __syncthreads();
   if (j < D.n_ac) {
@@ -621,11 +670,11 @@ __device__ __forceinline__ bool cp_step(const CpDesc& D, const CpCall& C, int j,
     issue_qkv(R1, D, D.layer[0], g, r);
   }
   if (C.logits)
-    for (int i = tid; i < vper; i += NT) C.logits[(size_t)(j - 1) * V + vper * blockIdx.x + i] = S.out[i];
+    for (int i = tid; i < vper; i += NT) glb(C.logits)[(size_t)(j - 1) * V + vper * blockIdx.x + i] = S.out[i];
   const int a = argmax_exchange(D, S, vper, vper * blockIdx.x, tag, apar);
   if (a < 0) return false;
-  if (blockIdx.x == 0 && tid == 0) C.codes[(C.use_frame ? (long)frame * C.f_stride : 0) + j - 1] = a;
-  tok = C.forced ? C.forced[j - 1] : a;
+  if (blockIdx.x == 0 && tid == 0) glb(C.codes)[(C.use_frame ? (long)frame * C.f_stride : 0) + j - 1] = a;
+  tok = C.forced ? glb(C.forced)[j - 1] : a;
   if (tok < 0) tok = 0;
   if (tok >= V) tok = V - 1;
   return true;
@@ -643,23 +692,23 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   {
     const WT* f = reinterpret_cast<const WT*>(D.final_norm);
 #pragma unroll
-    for (int k = 0; k < 2; ++k) fn[k] = threadIdx.x + k * NT < D.H ? to_f32(f[threadIdx.x + k * NT]) : 0.f;
+    for (int k = 0; k < 2; ++k) fn[k] = threadIdx.x + k * NT < D.H ? to_f32(glb(f)[threadIdx.x + k * NT]) : 0.f;
   }
   RowsB<WT> R0;
   RowsA<WT> R1;
   if (D.proj) issue_proj(R0, D, g, r);
   issue_qkv(R1, D, D.layer[0], g, r);
-  uint32_t tag = D.st->epoch;
-  const int frame = D.st->frame;
+  uint32_t tag = glb(D.st)->epoch;
+  const int frame = glb(D.st)->frame;
   int iring = 0, cpar = 0, apar = 0;
-  int tok = C.semantic[0];
+  int tok = glb(C.semantic)[0];
   if (tok < 0) tok = 0;
   if (tok >= D.Vs) tok = D.Vs - 1;
   bool ok = cp_step<WT, 2>(D, C, 1, tok, S, R0, R1, c, fn, tag, iring, cpar, apar, frame, g, r);
   for (int j = 2; ok && j <= D.n_ac; ++j) ok = cp_step<WT, 1>(D, C, j, tok, S, R0, R1, c, fn, tag, iring, cpar, apar, frame, g, r);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    D.st->epoch = tag + 1;  // every workgroup has read the epoch: all took part in the last exchange
-    if (C.next_tok) C.next_tok[0] = tok;
+    glb(D.st)->epoch = tag + 1;  // every workgroup has read the epoch: all took part in the last exchange
+    if (C.next_tok) glb(C.next_tok)[0] = tok;
   }
 }
 

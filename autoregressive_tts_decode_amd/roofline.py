@@ -72,7 +72,9 @@ def algorithmic_bytes(cfg: ModelCfg, talker_positions_read: float, batch: int = 
     weights = talker_w + cfg.n_acoustic * cp_step_w
     total = weights + emb_rows + cp_rows + kv_t + kv_c
     return {"talker_weights": talker_w, "cp_step_weights": cp_step_w, "weights": weights,
-            "embedding_rows": emb_rows + cp_rows, "kv_talker": kv_t, "kv_cp": kv_c, "total": total}
+            "embedding_rows": emb_rows + cp_rows, "kv_talker": kv_t, "kv_cp": kv_c, "total": total,
+            # the CodePredictor part of the frame alone (its 15 steps)
+            "cp_frame": cfg.n_acoustic * cp_step_w + cp_rows + kv_c}
 
 
 def frame_bytes_for_run(cfg: ModelCfg, prefill_len: int, first_frame: int, n_frames: int, batch: int = 1,

@@ -10,6 +10,7 @@
 // consumes them (which leaves the next frame's Talker output pending).
 #include "tts.h"
 #include "tts_device.h"
+#include "tts_xtk.h"
 #include "tts_xtp.h"
 
 #include <hip/hip_runtime.h>
@@ -58,7 +59,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout, computed identically by tts_workspace_bytes and tts_create.
 struct Layout {
   size_t st, tk, tv, ck, cv, tcos, tsin, ccos, csin, x, qkv, attn, h, part, counters, logits, hT, cx, clog, next_tok,
-      sem_tok, ac_codes, history, cpdesc, xin, xcr, cand, xerr, xzero_begin, xzero_end, total;
+      sem_tok, ac_codes, history, cpdesc, tkdesc, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
   int nsplit;
 };
 
@@ -100,12 +101,14 @@ Layout make_layout(const tts_config& c) {
   L.sem_tok = take(B * 4);
   L.ac_codes = take(B * c.n_acoustic * 4);
   L.history = take(B * t.vocab);
-  // persistent CodePredictor kernel: descriptor and exchange buffers (its K/V rows stay in LDS)
+  // persistent kernels: descriptors and exchange buffers (the CodePredictor's K/V rows stay in LDS)
   L.cpdesc = take(sizeof(xtp::CpDesc));
+  L.tkdesc = take(sizeof(xtp::TkDesc));
   L.xzero_begin = off;
   L.xin = take((size_t)xtp::NX * xtp::RING * xtp::ISZ * 8);
   L.xcr = take((size_t)xtp::NWG * 2 * xtp::CSZ * 8);
   L.cand = take((size_t)2 * xtp::NWG * xtp::CAND * 8);
+  L.att = take((size_t)xtp::NX * 2 * xtp::NR * xtp::ATS * 8);
   L.xerr = take(256);
   L.xzero_end = off;
   L.total = off;
@@ -181,6 +184,21 @@ bool xtp_capable(const tts_config& c) {
   return true;
 }
 
+// Whether the persistent Talker step kernel handles this config: bf16 weights, an fp32 KV cache,
+// 8 KV heads of dimension 128 with 2 query heads each, and weight slices that fit its chunk shapes
+// (see tts_xtk.h).
+bool xtk_capable(const tts_config& c) {
+  const tts_stack_cfg& t = c.talker;
+  if (c.weight_dtype != TTS_DTYPE_BF16 || c.kv_dtype != TTS_DTYPE_F32) return false;
+  if (t.n_kv_heads != xtp::NX || t.head_dim != 128 || t.n_q_heads != 2 * t.n_kv_heads) return false;
+  if (t.hidden % 256 || t.hidden > xtp::THMAX || t.hidden + xtp::NR > xtp::ISZ) return false;
+  if (t.ffn % 256 || t.ffn / xtp::NX > xtp::TFXMAX || (t.ffn / xtp::NX) % 8 || (t.ffn / xtp::NX) / 8 > 128) return false;
+  if (t.ffn / (xtp::NX * xtp::NR) > 3 * xtp::NW) return false;
+  if (t.vocab % xtp::NWG || t.vocab / xtp::NWG > 2 * xtp::NW) return false;
+  if (t.n_layers > xtp::TMAXL) return false;
+  return true;
+}
+
 }  // namespace
 
 struct tts_ctx {
@@ -215,6 +233,8 @@ struct tts_ctx {
   bool xtp_ok = false;   // config supported
   int exec_mode = TTS_EXEC_PERSISTENT;  // persistent CodePredictor when supported (batch 1, greedy)
   xtp::CpDesc* cpdesc = nullptr;
+  bool xtk_ok = false;   // persistent Talker step supported
+  xtp::TkDesc* tkdesc = nullptr;
   uint32_t* xerr = nullptr;
   std::string err;
 
@@ -543,6 +563,20 @@ int codepred_frame_xtp(tts_ctx* ctx, const int32_t* semantic, const int32_t* for
   return TTS_OK;
 }
 
+// The persistent Talker step (batch 1): all layers, final norm and semantic head for the position
+// in the device counters; bumps the position (and the frame) at its end.
+bool use_xtk(tts_ctx* ctx, int B) { return ctx->xtk_ok && ctx->exec_mode == TTS_EXEC_PERSISTENT && B == 1; }
+
+int talker_step_xtk(tts_ctx* ctx, int bump_pos, int bump_frame) {
+  xtp::TkCall call;
+  call.desc = ctx->tkdesc;
+  call.bump_pos = bump_pos;
+  call.bump_frame = bump_frame;
+  hipLaunchKernelGGL(xtp::k_talker_step<uint16_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
+  HIP_LAUNCH_CHECK();
+  return TTS_OK;
+}
+
 int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac, URef u, const int32_t* forced,
                    int32_t* out, int ob, int of, int oo, int ouf, float* logits_out) {
   const auto& c = ctx->cfg;
@@ -642,8 +676,9 @@ int enqueue_frame(tts_ctx* ctx, const tts_sampling& sem, const tts_sampling& ac,
   TokRef refs[16];
   for (int j = 0; j < 16; ++j) refs[j] = tokref(codes, fs, 16, j, 1);
   if (int rc = embed_sum(ctx, B, refs)) return rc;
-  if (int rc = talker_stack(ctx, B, 0, 1)) return rc;
   // the frame's last kernel also advances the device position and frame counters
+  if (use_xtk(ctx, B)) return talker_step_xtk(ctx, 1, 1);
+  if (int rc = talker_stack(ctx, B, 0, 1)) return rc;
   return talker_head(ctx, B, 1, 1);
 }
 
@@ -693,8 +728,10 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
   ctx->next_tok = (int32_t*)(w + L.next_tok); ctx->sem_tok = (int32_t*)(w + L.sem_tok); ctx->ac_codes = (int32_t*)(w + L.ac_codes);
   ctx->history = (uint8_t*)(w + L.history);
   ctx->cpdesc = (xtp::CpDesc*)(w + L.cpdesc);
+  ctx->tkdesc = (xtp::TkDesc*)(w + L.tkdesc);
   ctx->xerr = (uint32_t*)(w + L.xerr);
   ctx->xtp_ok = xtp_capable(*cfg);
+  ctx->xtk_ok = xtk_capable(*cfg);
   ctx->talker.c = cfg->talker;
   ctx->cp.c = cfg->codepred;
   // RoPE tables: angles p * theta^(-2i/d) in double, rounded to fp32.
@@ -805,6 +842,27 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
     HIP_TRY(hipMemcpyAsync(ctx->cpdesc, &D, sizeof D, hipMemcpyHostToDevice, ctx->stream));
     HIP_TRY(hipStreamSynchronize(ctx->stream));
   }
+  if (ctx->xtk_ok) {
+    xtp::TkDesc D;
+    std::memset(&D, 0, sizeof D);
+    const tts_stack_cfg& t = c.talker;
+    for (int l = 0; l < t.n_layers; ++l) {
+      const Layer& L = ctx->talker.layers[l];
+      D.layer[l] = {L.attn_norm, L.wq, L.wk, L.wv, L.q_norm, L.k_norm, L.wo, L.mlp_norm, L.wg, L.wu, L.wd};
+    }
+    D.n_layers = t.n_layers; D.H = t.hidden; D.F = t.ffn; D.V = t.vocab; D.nq = t.n_q_heads; D.nkv = t.n_kv_heads;
+    D.d = t.head_dim; D.cap = c.max_cache_steps; D.eps = c.rms_eps;
+    D.final_norm = ctx->talker.final_norm; D.lm_head = ctx->lm_head;
+    D.rope_cos = ctx->tcos; D.rope_sin = ctx->tsin;
+    D.kc = (float*)(ctx->ws + ctx->L.tk); D.vc = (float*)(ctx->ws + ctx->L.tv);
+    D.ls = (long long)c.max_batch * t.n_kv_heads * c.max_cache_steps;
+    D.x_in = ctx->x; D.logits = ctx->logits; D.hT = ctx->hT;
+    D.xin = (xtp::u64*)(ctx->ws + ctx->L.xin); D.xcr = (xtp::u64*)(ctx->ws + ctx->L.xcr);
+    D.att = (xtp::u64*)(ctx->ws + ctx->L.att);
+    D.st = ctx->st; D.err = ctx->xerr;
+    HIP_TRY(hipMemcpyAsync(ctx->tkdesc, &D, sizeof D, hipMemcpyHostToDevice, ctx->stream));
+    HIP_TRY(hipStreamSynchronize(ctx->stream));
+  }
   ctx->err.clear();
   return TTS_OK;
 }
@@ -850,8 +908,12 @@ int tts_talker_step(tts_ctx* ctx, const int32_t* prev_codes, float* sem_logits) 
   TokRef refs[16];
   for (int j = 0; j < 16; ++j) refs[j] = tokref(prev_codes, 16, 0, j, 0);
   if (int rc = embed_sum(ctx, B, refs)) return rc;
-  if (int rc = talker_stack(ctx, B, 0, 1)) return rc;
-  if (int rc = talker_head(ctx, B, 1, 0)) return rc;
+  if (use_xtk(ctx, B)) {
+    if (int rc = talker_step_xtk(ctx, 1, 0)) return rc;
+  } else {
+    if (int rc = talker_stack(ctx, B, 0, 1)) return rc;
+    if (int rc = talker_head(ctx, B, 1, 0)) return rc;
+  }
   if (sem_logits)
     HIP_TRY(hipMemcpyAsync(sem_logits, ctx->logits, (size_t)B * ctx->cfg.talker.vocab * 4, hipMemcpyDeviceToDevice, ctx->stream));
   ctx->pos += 1;
@@ -960,8 +1022,8 @@ int tts_reset(tts_ctx* ctx) {
 int tts_set_exec_mode(tts_ctx* ctx, int32_t mode) {
   if (!ctx) return TTS_E_ARG;
   if (mode != TTS_EXEC_KERNELS && mode != TTS_EXEC_PERSISTENT) return ctx->fail(TTS_E_ARG, "exec mode %d", mode);
-  if (mode == TTS_EXEC_PERSISTENT && !ctx->xtp_ok)
-    return ctx->fail(TTS_E_UNSUPPORTED, "the persistent CodePredictor kernel does not handle this config");
+  if (mode == TTS_EXEC_PERSISTENT && !ctx->xtp_ok && !ctx->xtk_ok)
+    return ctx->fail(TTS_E_UNSUPPORTED, "no persistent kernel handles this config");
   if (mode != ctx->exec_mode) drop_graph(ctx);
   ctx->exec_mode = mode;
   ctx->err.clear();
@@ -970,8 +1032,8 @@ int tts_set_exec_mode(tts_ctx* ctx, int32_t mode) {
 
 int tts_get_exec_mode(const tts_ctx* ctx, int32_t* mode, int32_t* persistent_supported) {
   if (!ctx) return TTS_E_ARG;
-  if (mode) *mode = ctx->exec_mode == 1 && ctx->xtp_ok ? TTS_EXEC_PERSISTENT : TTS_EXEC_KERNELS;
-  if (persistent_supported) *persistent_supported = ctx->xtp_ok ? 1 : 0;
+  if (mode) *mode = ctx->exec_mode == TTS_EXEC_PERSISTENT && (ctx->xtp_ok || ctx->xtk_ok) ? TTS_EXEC_PERSISTENT : TTS_EXEC_KERNELS;
+  if (persistent_supported) *persistent_supported = (ctx->xtp_ok ? TTS_PERSISTENT_CODEPRED : 0) | (ctx->xtk_ok ? TTS_PERSISTENT_TALKER : 0);
   return TTS_OK;
 }
 

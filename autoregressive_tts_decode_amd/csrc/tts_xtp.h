@@ -53,6 +53,13 @@ struct LayerW {
   const void *attn_norm, *wq, *wk, *wv, *q_norm, *k_norm, *wo, *mlp_norm, *wg, *wu, *wd;
 };
 
+// Exchange buffers (shared by the persistent kernels of a context, which never run concurrently:
+// their tags come from one running counter) and the error word.
+struct Xch {
+  unsigned long long *xin, *xcr;
+  uint32_t* err;
+};
+
 // Everything the kernel reads; built on the host once per weight binding and
 // kept in device memory.
 struct CpDesc {
@@ -97,21 +104,11 @@ __device__ __forceinline__ const GLB T* glb(const T* p) { return (const GLB T*)p
 __device__ __forceinline__ void st_c(u64* p, u64 v) { __hip_atomic_store(glb(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ u64 ld_c(const u64* p) { return __hip_atomic_load(glb(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
-// Gather nseg segments of len entries into lds[0 .. nseg*len), polling until every entry carries
-// tag; an entry already received is not read again. With inner == 1 segment s starts at
-// src + s * sstride; otherwise segment s = (a, b), a = s / inner, b = s % inner, starts at
-// src + a * astride + b * 64. n <= KMAX * NT. Returns false (and flags err) on time-out or when
-// another workgroup failed.
-template <int KMAX>
-__device__ __forceinline__ bool get(const u64* src, int nseg, int len, int sstride, uint32_t tag, float* lds, uint32_t* err,
-                                    int inner = 1, int astride = 0) {
-  const int n = nseg * len;
-  // address of this thread's k-th entry
-  auto at = [&](int k) -> const u64* {
-    const int i = threadIdx.x + k * NT, seg = i / len, e = i % len;
-    const size_t off = (inner == 1) ? (size_t)seg * sstride : (size_t)(seg / inner) * astride + (size_t)(seg % inner) * 64;
-    return src + off + e;
-  };
+// Gather n tagged entries, entry i read from at(i), into lds[0 .. n), polling until every entry
+// carries tag; an entry already received is not read again. n <= KMAX * NT. Returns false (and
+// flags err) on time-out or when another workgroup failed.
+template <int KMAX, typename At>
+__device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t* err, At at) {
   unsigned pend = 0;
 #pragma unroll
   for (int k = 0; k < KMAX; ++k)
@@ -120,7 +117,7 @@ __device__ __forceinline__ bool get(const u64* src, int nseg, int len, int sstri
     u64 v[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-      if (pend & (1u << k)) v[k] = ld_c(at(k));
+      if (pend & (1u << k)) v[k] = ld_c(at(threadIdx.x + k * NT));
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
       if ((pend & (1u << k)) && tagof(v[k]) == tag) {
@@ -136,6 +133,12 @@ __device__ __forceinline__ bool get(const u64* src, int nseg, int len, int sstri
       }
     }
   }
+}
+
+// Gather the n contiguous entries src[0 .. n) (see get_at).
+template <int KMAX>
+__device__ __forceinline__ bool get_flat(const u64* src, int n, uint32_t tag, float* lds, uint32_t* err) {
+  return get_at<KMAX>(n, tag, lds, err, [&](int i) -> const u64* { return src + i; });
 }
 
 // ---------------------------------------------------------------------------- weight rows
@@ -311,30 +314,38 @@ __device__ __forceinline__ void issue_proj(RowsB<WT>& R, const CpDesc& D, int g,
 // S.xs[0 .. M*H). With the rows each rank also publishes the sum of squares of its reduced rows,
 // gathered into S.xs[M*H + m*NR + rank], so the next RMSNorm needs no reduction of its own.
 // cpar alternates the cross slot so a rank one exchange ahead never overwrites unread values.
-template <int M, typename AfterPut>
-__device__ __forceinline__ bool reduce_gather(const CpDesc& D, Smem& S, int H, bool residual, uint32_t& tag, int& iring, int& cpar,
-                                              int g, int r, AfterPut after_put) {
+// HMX: the largest H the caller supports (sizes the cross gather); KMAX: loads per thread of the
+// intra gather (M * (H + NR) entries).
+template <int M, int HMX, int KMAX, typename AfterPut>
+__device__ __forceinline__ bool reduce_gather(const Xch& X, const float* out, float* xs, float* xn, int H, bool residual,
+                                              uint32_t& tag, int& iring, int& cpar, int g, int r, AfterPut after_put) {
   const int tid = threadIdx.x, hper = H / NR;
   ++tag;
-  u64* mine = D.xcr + ((size_t)blockIdx.x * 2 + (cpar & 1)) * CSZ;
-  for (int i = tid; i < hper * M; i += NT) st_c(mine + (i % M) * 64 + i / M, pack(S.out[i], tag));
+  u64* mine = X.xcr + ((size_t)blockIdx.x * 2 + (cpar & 1)) * CSZ;
+  for (int i = tid; i < hper * M; i += NT) st_c(mine + (i % M) * 64 + i / M, pack(out[i], tag));
   after_put();
   // partners: rank r on every XCD = blocks r * NX + x; their slots are 2 * CSZ apart.
-  // Segment (x, m) -> S.xn[(x * M + m) * hper ..]
-  const u64* base = D.xcr + ((size_t)(r * NX) * 2 + (cpar & 1)) * CSZ;
-  if (!get<1>(base, NX * M, hper, 2 * CSZ, tag, S.xn, D.err, M, 2 * CSZ)) return false;
+  // Segment (x, m) -> xn[(x * M + m) * hper ..]
+  // (hper is a power of two: entry i -> element i & (hper - 1) of segment i >> lh)
+  const u64* base = X.xcr + ((size_t)(r * NX) * 2 + (cpar & 1)) * CSZ;
+  const int lh = __builtin_ctz(hper);
+  if (!get_at<(NX * M * (HMX / NR) + NT - 1) / NT>(NX * M * hper, tag, xn, X.err, [&](int i) -> const u64* {
+        const int sg = i >> lh, e = i & (hper - 1);
+        return base + (size_t)(sg / M) * (2 * CSZ) + (sg % M) * 64 + e;
+      }))
+    return false;
   ++cpar;
   ++tag;
-  u64* buf = D.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
+  u64* buf = X.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
   if (tid < 64) {  // hper * M <= 64: wave 0 reduces and publishes this rank's rows
     const int e = tid / M, m = tid % M;
     const int row = hper * r + e;
     const bool live = tid < hper * M;
     float v = 0.f;
     if (live) {
-      v = residual ? S.xs[m * H + row] : 0.f;
+      v = residual ? xs[m * H + row] : 0.f;
 #pragma unroll
-      for (int x = 0; x < NX; ++x) v += S.xn[(x * M + m) * hper + e];
+      for (int x = 0; x < NX; ++x) v += xn[(x * M + m) * hper + e];
       st_c(buf + m * H + row, pack(v, tag));
     }
 #pragma unroll
@@ -344,22 +355,22 @@ __device__ __forceinline__ bool reduce_gather(const CpDesc& D, Smem& S, int H, b
     }
   }
   __syncthreads();  // the gather below overwrites the residual rows read above
-  return get<(M * (HMAX + NR) + NT - 1) / NT>(buf, 1, M * (H + NR), 0, tag, S.xs, D.err);
+  return get_flat<KMAX>(buf, M * (H + NR), tag, xs, X.err);
 }
 
 // Intra gather of a slice: this workgroup's n values per row (vals(e, m)) land at row offset
 // n * r of every rank's copy; the full rows (width w) of all ranks go to dst.
 template <int M, int KMAX, typename ValFn, typename AfterPut>
-__device__ __forceinline__ bool slice_gather(const CpDesc& D, int n, int w, ValFn vals, float* dst, uint32_t& tag, int& iring,
+__device__ __forceinline__ bool slice_gather(const Xch& X, int n, int w, ValFn vals, float* dst, uint32_t& tag, int& iring,
                                              int g, int r, AfterPut after_put) {
   ++tag;
-  u64* buf = D.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
+  u64* buf = X.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
   for (int i = threadIdx.x; i < n * M; i += NT) {
     const int e = i / M, m = i % M;
     st_c(buf + m * w + n * r + e, pack(vals(e, m), tag));
   }
   after_put();
-  return get<KMAX>(buf, M, w, w, tag, dst, D.err);
+  return get_flat<KMAX>(buf, M * w, tag, dst, X.err);
 }
 
 // ---------------------------------------------------------------------------- per-thread constants
@@ -472,12 +483,14 @@ __device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int l
   const int fx = D.F / NX, fper = fx / NR;  // FFN slice per XCD / per rank
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const bool last = layer + 1 == D.n_layers;
+  const Xch X{D.xin, D.xcr, D.err};
+  constexpr int KCP = (M * (HMAX + NR) + NT - 1) / NT;
 
   // --- q/k/v slice (R1)
   rmsnorm_reg<M>(S.xs, H, c.an, D.eps, S.xn, S.red, have_ss ? S.xs + M * H : nullptr);
   rows_dot<WT, M>(R1, qper, H, S.xn, H, S.out);
   __syncthreads();
-  if (!slice_gather<M, M>(D, qper, qrows, [&](int e, int m) { return S.out[e * M + m]; }, S.qkv, tag, iring, g, r,
+  if (!slice_gather<M, M>(X, qper, qrows, [&](int e, int m) { return S.out[e * M + m]; }, S.qkv, tag, iring, g, r,
                           [&] { issue_gu(R1, D, W, g, r); }))
     return false;
 
@@ -550,13 +563,13 @@ __device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int l
   // --- output projection partial (R0: rows [hper*r, +hper), this XCD's head columns), residual
   rows_dot<WT, M>(R0, hper, G * d, S.ob, G * d, S.out);
   __syncthreads();
-  if (!reduce_gather<M>(D, S, H, true, tag, iring, cpar, g, r, [&] { issue_down(R0, D, W, g, r); })) return false;
+  if (!reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] { issue_down(R0, D, W, g, r); })) return false;
 
   // --- gate/up slice (R1) + SwiGLU
   rmsnorm_reg<M>(S.xs, H, c.mn, D.eps, S.xn, S.red, S.xs + M * H);
   rows_dot<WT, M>(R1, 2 * fper, H, S.xn, H, S.out);
   __syncthreads();
-  if (!slice_gather<M, M>(D, fper, fx, [&](int e, int m) { return silu(S.out[e * M + m]) * S.out[(fper + e) * M + m]; }, S.hb,
+  if (!slice_gather<M, M>(X, fper, fx, [&](int e, int m) { return silu(S.out[e * M + m]) * S.out[(fper + e) * M + m]; }, S.hb,
                           tag, iring, g, r, [&] {
                             if (!last) {
                               load_consts<WT, M>(c, D, D.layer[layer + 1], p0);
@@ -570,7 +583,7 @@ __device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int l
   // --- down projection partial (R0: rows [hper*r, +hper), this XCD's FFN columns), residual
   rows_dot<WT, M>(R0, hper, fx, S.hb, fx, S.out);
   __syncthreads();
-  return reduce_gather<M>(D, S, H, true, tag, iring, cpar, g, r, [&] {
+  return reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] {
     if (!last) issue_o(R0, D, D.layer[layer + 1], g, r);
     else if (j < D.n_ac && D.proj) issue_proj(R0, D, g, r);
   });
@@ -591,7 +604,7 @@ __device__ __forceinline__ int argmax_exchange(const CpDesc& D, Smem& S, int nro
     st_c(cb + blockIdx.x * CAND, pack(bv, tag));
     st_c(cb + blockIdx.x * CAND + 1, pack(__int_as_float(bi), tag));
   }
-  if (!get<1>(cb, NWG, 2, CAND, tag, S.cand, D.err)) return -1;
+  if (!get_at<1>(2 * NWG, tag, S.cand, D.err, [&](int i) -> const u64* { return cb + (i >> 1) * CAND + (i & 1); })) return -1;
   ++apar;
   __shared__ int best;
   if (tid < NWG) {
@@ -628,6 +641,8 @@ __device__ __forceinline__ bool cp_step(const CpDesc& D, const CpCall& C, int j,
                                         RowsA<WT>& R1, LayerConsts& c, const float* fn, uint32_t& tag, int& iring, int& cpar,
                                         int& apar, int frame, int g, int r) {
   const int H = D.H, Ht = D.Ht, V = D.V, tid = threadIdx.x;
+  const Xch X{D.xin, D.xcr, D.err};
+  constexpr int KCP = (M * (HMAX + NR) + NT - 1) / NT;
   const WT* tab = (j == 1) ? reinterpret_cast<const WT*>(D.embed_sem)
                            : reinterpret_cast<const WT*>(D.embed_ac) + (size_t)(j - 2) * V * Ht;
   const WT* erow = tab + (size_t)tok * Ht;
@@ -644,7 +659,8 @@ __device__ __forceinline__ bool cp_step(const CpDesc& D, const CpCall& C, int j,
     __syncthreads();
     rows_dot<WT, M>(R0, hper, kx, S.xn, kx, S.out);
     __syncthreads();
-    if (!reduce_gather<M>(D, S, H, false, tag, iring, cpar, g, r, [&] { issue_o(R0, D, D.layer[0], g, r); })) return false;
+    if (!reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, false, tag, iring, cpar, g, r, [&] { issue_o(R0, D, D.layer[0], g, r); }))
+      return false;
   } else {
     issue_o(R0, D, D.layer[0], g, r);
     for (int i = tid; i < H; i += NT) {

@@ -34,6 +34,7 @@ EXPORTED = ["tts_workspace_bytes", "tts_create", "tts_load_weights", "tts_prefil
             "tts_codepred_frame", "tts_sample", "tts_run_frames", "tts_set_exec_mode", "tts_get_exec_mode",
             "tts_device_status", "tts_get_progress", "tts_reset", "tts_last_error", "tts_destroy"]
 EXEC_KERNELS, EXEC_PERSISTENT = 0, 1
+PERSISTENT_CODEPRED, PERSISTENT_TALKER = 1, 2  # bits of exec_mode()[1]
 
 
 class StackCfgC(ctypes.Structure):
@@ -229,10 +230,11 @@ class TTSDecoder:
     def set_exec_mode(self, mode: int):
         self._check(self.lib.tts_set_exec_mode(self.ctx, mode), "tts_set_exec_mode")
 
-    def exec_mode(self) -> tuple[int, bool]:
+    def exec_mode(self) -> tuple[int, int]:
+        """(mode, bits of the persistent kernels this config allows: PERSISTENT_CODEPRED | PERSISTENT_TALKER)."""
         m, sup = ctypes.c_int32(), ctypes.c_int32()
         self._check(self.lib.tts_get_exec_mode(self.ctx, ctypes.byref(m), ctypes.byref(sup)), "tts_get_exec_mode")
-        return m.value, bool(sup.value)
+        return m.value, sup.value
 
     def device_status(self) -> int:
         st = ctypes.c_int32()

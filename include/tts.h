@@ -144,17 +144,23 @@ int tts_sample(tts_ctx* ctx, const float* logits, int32_t batch, int32_t vocab, 
 int tts_run_frames(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_sampling* ac, const float* u,
                    int32_t* codes);
 
-/* Execution of the CodePredictor frame (same results either way, up to
- * floating-point summation order):
- *  TTS_EXEC_PERSISTENT (default where supported): one persistent kernel runs
- *    all 15 steps, its workgroups split across the 8 XCDs tensor-parallel and
- *    exchanging tagged values instead of ending kernels. Used for batch 1 with
- *    greedy acoustic tokens on bf16-weight configs whose CodePredictor has
- *    8 KV heads of dimension 128; other calls use the per-op kernels.
+/* Execution of the CodePredictor frame and of the batch-1 Talker step (same
+ * results either way, up to floating-point summation order):
+ *  TTS_EXEC_PERSISTENT (default where supported): persistent kernels, whose
+ *    workgroups split each layer across the 8 XCDs tensor-parallel and
+ *    exchange tagged values instead of ending kernels. One runs all 15
+ *    CodePredictor steps of a frame (batch 1, greedy acoustic tokens, bf16
+ *    weights, a CodePredictor with 8 KV heads of dimension 128); one runs a
+ *    whole Talker step (batch 1, bf16 weights, fp32 KV cache, 8 KV heads of
+ *    dimension 128 with 2 query heads each). Other calls use the per-op
+ *    kernels. Prefill always uses the per-op kernels.
  *  TTS_EXEC_KERNELS: one kernel per op.
- * Switching drops the captured frame graph. TTS_E_UNSUPPORTED if the config
- * cannot run persistent. */
+ * Switching drops the captured frame graph. TTS_E_UNSUPPORTED if neither
+ * persistent kernel handles the config. tts_get_exec_mode reports the mode
+ * and, in *persistent_supported, which persistent kernels the config allows
+ * (TTS_PERSISTENT_CODEPRED | TTS_PERSISTENT_TALKER). */
 enum tts_exec_mode { TTS_EXEC_KERNELS = 0, TTS_EXEC_PERSISTENT = 1 };
+enum tts_persistent_kernels { TTS_PERSISTENT_CODEPRED = 1, TTS_PERSISTENT_TALKER = 2 };
 int tts_set_exec_mode(tts_ctx* ctx, int32_t mode);
 int tts_get_exec_mode(const tts_ctx* ctx, int32_t* mode, int32_t* persistent_supported);
 

@@ -330,7 +330,7 @@ def test_bf16_teacher_forced_step_parity(bf16_model, mode):
     del orc
     dec, dw = make_decoder(model, 1, 64 + 240, 240, w)
     _, supported = dec.exec_mode()
-    assert supported, f"{name}: the persistent CodePredictor should support this config"
+    assert supported == tts.PERSISTENT_CODEPRED | tts.PERSISTENT_TALKER, f"{name}: both persistent kernels should support this config"
     dec.set_exec_mode(tts.EXEC_PERSISTENT if mode == "persistent" else tts.EXEC_KERNELS)
     assert dec.exec_mode()[0] == (tts.EXEC_PERSISTENT if mode == "persistent" else tts.EXEC_KERNELS)
     print(f"{name} {mode}: running", flush=True)
@@ -399,3 +399,101 @@ def test_1p7b_long_context_logits_at_2255_positions():
     if top2_margin(ref[0]) > 0.05:
         assert int(np.argmax(got[0])) == int(np.argmax(ref[0]))
     print(f"1.7b at 2255 positions: rel err {err:.2e}")
+
+
+def test_1p7b_persistent_talker_step_at_2255_positions():
+    """The persistent Talker step at the full long-utterance length: position 2254 after a 2254-id
+    prefill, fed one frame of codes, so its attention splits 2255 positions over the 32 ranks of
+    each XCD. The oracle runs the whole sequence (text rows, then the frame's code-embedding sum)
+    through its cache-free pass."""
+    model = config.M17B
+    w = synth.make_weights(model, 0)
+    n = 2254
+    ids = synth.random_ids(n, model.text_vocab, seed=6)
+    codes = np.concatenate([synth.random_ids(1, model.talker.vocab, seed=7),
+                            synth.random_ids(15, model.codepred.vocab, seed=8)], axis=1)
+    print("persistent talker long context: weights ready", flush=True)
+    dec, dw = make_decoder(model, 1, n + 2, 4, w)
+    assert dec.exec_mode() == (tts.EXEC_PERSISTENT, tts.PERSISTENT_CODEPRED | tts.PERSISTENT_TALKER)
+    d = dev()
+    got = torch.zeros((1, model.talker.vocab), dtype=torch.float32, device=d)
+    dec.prefill(torch.from_numpy(ids).to(d))
+    dec.talker_step(torch.from_numpy(codes).to(d), got)
+    torch.cuda.synchronize()
+    assert dec.device_status() == 0
+    assert dec.progress() == (n + 1, 0)
+    got = got.cpu().numpy()
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+    print("persistent talker long context: GPU step done; oracle whole-sequence pass", flush=True)
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    X = np.concatenate([orc.embed_text[ids[0]], orc.embed_sum(codes)], axis=0)[None]
+    ref = linear(orc.full_forward("talker", X)[:, -1], orc.lm_head)
+    err = rowwise_rel_err(got, ref).max()
+    assert err <= 1e-2, err
+    if top2_margin(ref[0]) > 0.05:
+        assert int(np.argmax(got[0])) == int(np.argmax(ref[0]))
+    print(f"1.7b persistent talker step at position 2254: rel err {err:.2e}")
+
+
+def test_1p7b_x32_sampled_streams_teacher_forced():
+    """The 32-stream 1.7B configuration with the pages' sampling controls: 32 independent lockstep
+    streams (semantic: top-k 50, T 0.9, repetition penalty 1.05; acoustic: the same without the
+    penalty), each with its own ids, history and uniforms. Logits of every stream and step within
+    the bf16 bar; every non-exempt draw equal to the oracle's given the same uniforms. The prefill is
+    shortened to 8 ids so the fp32 oracle runs 32 streams in seconds."""
+    model = config.M17B
+    w = synth.make_weights(model, 0)
+    B, n, F = 32, 8, 2
+    ids = synth.random_ids(n, model.text_vocab, seed=9, batch=B)
+    u = synth.random_uniforms((B, F, 16), seed=10)
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    print("x32: oracle run", flush=True)
+    ref = orc.generate(ids, F, SEM, AC, u, sampler_dtype=np.float32)
+    del orc
+    codes = ref["codes"]
+    Vs, Va = model.talker.vocab, model.codepred.vocab
+    dec, dw = make_decoder(model, B, n + F + 2, F + 2, w)
+    d = dev()
+    ud = torch.from_numpy(u).to(d)
+    logits = torch.zeros((B, Vs), dtype=torch.float32, device=d)
+    s = torch.zeros((B,), dtype=torch.int32, device=d)
+    own = torch.zeros((B, 15), dtype=torch.int32, device=d)
+    acl = torch.zeros((B, 15, Va), dtype=torch.float32, device=d)
+    hist_np = np.zeros((B, Vs), bool)
+    dec.prefill(torch.from_numpy(ids).to(d), logits)
+    checked = exempt = 0
+    worst = 0.0
+    for t in range(F):
+        if t > 0:
+            dec.talker_step(torch.from_numpy(codes[:, t - 1]).to(d).contiguous(), logits)
+        hist = torch.from_numpy(hist_np.astype(np.uint8)).to(d)
+        dec.sample(logits, SEM, ud[:, t, 0].contiguous(), s, history=hist)
+        dec.codepred_frame(torch.from_numpy(codes[:, t, 0]).to(d).contiguous(), AC, ud[:, t, 1:].contiguous(), own,
+                           forced=torch.from_numpy(codes[:, t, 1:]).to(d).contiguous(), logits=acl)
+        torch.cuda.synchronize()
+        sl, al = logits.cpu().numpy(), acl.cpu().numpy()
+        e_s = rowwise_rel_err(sl, ref["sem_logits"][:, t]).max()
+        e_a = rowwise_rel_err(al, ref["ac_logits"][:, t]).max()
+        assert e_s <= 1e-2 and e_a <= 1e-2, f"frame {t}: logits rel err {e_s:.2e} / {e_a:.2e}"
+        worst = max(worst, e_s, e_a)
+        got_s, got_a = s.cpu().numpy(), own.cpu().numpy()
+        for b in range(B):
+            if sample_exempt(ref["sem_logits"][b, t], SEM, float(u[b, t, 0]), hist_np[b], rel=1e-4):
+                exempt += 1
+            else:
+                checked += 1
+                assert got_s[b] == codes[b, t, 0], f"semantic draw differs: stream {b} frame {t}"
+            for j in range(15):
+                if sample_exempt(ref["ac_logits"][b, t, j], AC, float(u[b, t, 1 + j]), rel=1e-4):
+                    exempt += 1
+                else:
+                    checked += 1
+                    assert got_a[b, j] == codes[b, t, 1 + j], f"acoustic draw {j + 1} differs: stream {b} frame {t}"
+            hist_np[b, codes[b, t, 0]] = True
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+    assert checked > 0.9 * (checked + exempt)
+    print(f"1.7b x32 sampled: logits rel err <= {worst:.2e}; {checked} draws equal, {exempt} exempt")

@@ -10,6 +10,7 @@
 // consumes them (which leaves the next frame's Talker output pending).
 #include "tts.h"
 #include "tts_device.h"
+#include "tts_prefill.h"
 #include "tts_xtk.h"
 #include "tts_xtp.h"
 
@@ -59,7 +60,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout, computed identically by tts_workspace_bytes and tts_create.
 struct Layout {
   size_t st, tk, tv, ck, cv, tcos, tsin, ccos, csin, x, qkv, attn, h, part, counters, logits, hT, cx, clog, next_tok,
-      sem_tok, ac_codes, history, cpdesc, tkdesc, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
+      sem_tok, ac_codes, history, cpdesc, tkdesc, px, pqkv, pq, po, pgu, ph, ps, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
   int nsplit;
 };
 
@@ -101,6 +102,18 @@ Layout make_layout(const tts_config& c) {
   L.sem_tok = take(B * 4);
   L.ac_codes = take(B * c.n_acoustic * 4);
   L.history = take(B * t.vocab);
+  // GEMM prefill: one chunk of up to kPrefillChunk positions per stream
+  {
+    const size_t Mp = B * kPrefillChunk;
+    const size_t qd = (size_t)t.n_q_heads * t.head_dim;
+    L.px = take(Mp * t.hidden * 4);
+    L.pqkv = take(Mp * qkv_t * 4);
+    L.pq = take(Mp * qd * 4);
+    L.po = take(Mp * qd * 4);
+    L.pgu = take(Mp * 2 * t.ffn * 4);
+    L.ph = take(Mp * t.ffn * 4);
+    L.ps = take(Mp * 4);
+  }
   // persistent kernels: descriptors and exchange buffers (the CodePredictor's K/V rows stay in LDS)
   L.cpdesc = take(sizeof(xtp::CpDesc));
   L.tkdesc = take(sizeof(xtp::TkDesc));
@@ -201,6 +214,15 @@ bool xtk_capable(const tts_config& c) {
 
 }  // namespace
 
+// Whether the GEMM prefill handles this config: bf16 weights, head dimension 128 and every GEMM
+// dimension of the Talker a multiple of the 64 x 64 x 64 tile.
+bool prefill_gemm_capable(const tts_config& c) {
+  const tts_stack_cfg& t = c.talker;
+  if (c.weight_dtype != TTS_DTYPE_BF16 || t.head_dim != 128) return false;
+  const int qd = t.n_q_heads * t.head_dim, kd = t.n_kv_heads * t.head_dim;
+  return t.hidden % 64 == 0 && qd % 64 == 0 && kd % 64 == 0 && t.ffn % 64 == 0;
+}
+
 struct tts_ctx {
   tts_config cfg{};
   hipStream_t stream = nullptr;
@@ -234,6 +256,8 @@ struct tts_ctx {
   int exec_mode = TTS_EXEC_PERSISTENT;  // persistent CodePredictor when supported (batch 1, greedy)
   xtp::CpDesc* cpdesc = nullptr;
   bool xtk_ok = false;   // persistent Talker step supported
+  bool pgemm_ok = false;  // GEMM prefill supported
+  int prefill_mode = TTS_PREFILL_GEMM;
   xtp::TkDesc* tkdesc = nullptr;
   uint32_t* xerr = nullptr;
   std::string err;
@@ -479,6 +503,70 @@ int talker_head(tts_ctx* ctx, int B, int bump_pos, int bump_frame) {
   a.y = ctx->logits; a.y_stride = t.vocab; a.epi = EPI_STORE;
   a.xn_out = ctx->hT; a.xn_stride = t.hidden; a.nontemporal = 1;
   return gemv(ctx, a);
+}
+
+// Talker prompt pass as GEMMs: chunks of up to kPrefillChunk positions per stream, M = B x chunk
+// rows per GEMM; the last chunk's last row per stream goes to ctx->x for the head.
+int prefill_gemm(tts_ctx* ctx, const int32_t* ids, int B, int n) {
+  const auto& c = ctx->cfg;
+  const tts_stack_cfg& t = c.talker;
+  const int H = t.hidden, d = t.head_dim, qd = t.n_q_heads * d, kd = t.n_kv_heads * d, nqkv = qd + 2 * kd, F = t.ffn;
+  const size_t layer_cache = (size_t)c.max_batch * t.n_kv_heads * c.max_cache_steps * d * ctx->kvb();
+  char* w = ctx->ws;
+  float *X = (float*)(w + ctx->L.px), *QKV = (float*)(w + ctx->L.pqkv), *Q = (float*)(w + ctx->L.pq),
+        *O = (float*)(w + ctx->L.po), *GU = (float*)(w + ctx->L.pgu), *Hh = (float*)(w + ctx->L.ph),
+        *RS = (float*)(w + ctx->L.ps);
+  auto gemm = [&](const float* A, int lda, const float* rs, const void* gain, std::initializer_list<std::pair<const void*, int>> segs,
+                  float* C, int N, int K, int M, int add) -> int {
+    GemmArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.A = A; a.lda = lda; a.rs = rs; a.gain = gain; a.C = C; a.ldc = N; a.M = M; a.N = N; a.K = K; a.add = add;
+    for (auto& sg : segs) { a.w[a.nseg] = sg.first; a.seg_rows[a.nseg] = sg.second; ++a.nseg; }
+    hipLaunchKernelGGL(k_gemm_bf16, dim3(N / kGBN, (M + kGBM - 1) / kGBM), dim3(256), 0, ctx->stream, a);
+    HIP_LAUNCH_CHECK();
+    return TTS_OK;
+  };
+  for (int p0 = 0; p0 < n; p0 += kPrefillChunk) {
+    const int P = std::min(kPrefillChunk, n - p0), M = B * P;
+    hipLaunchKernelGGL(k_embed_rows<uint16_t>, dim3(M), dim3(256), 0, ctx->stream, ids, n, p0, P, c.text_vocab, ctx->embed_text, H, X);
+    HIP_LAUNCH_CHECK();
+    for (int l = 0; l < t.n_layers; ++l) {
+      const Layer& W = ctx->talker.layers[l];
+      char* kc = w + ctx->L.tk + l * layer_cache;
+      char* vc = w + ctx->L.tv + l * layer_cache;
+      hipLaunchKernelGGL(k_rowscale, dim3((M + 3) / 4), dim3(256), 0, ctx->stream, X, H, M, H, c.rms_eps, RS);
+      HIP_LAUNCH_CHECK();
+      if (int rc = gemm(X, H, RS, W.attn_norm, {{W.wq, qd}, {W.wk, kd}, {W.wv, kd}}, QKV, nqkv, H, M, 0)) return rc;
+      QkArgs q;
+      std::memset(&q, 0, sizeof q);
+      q.qkv = QKV; q.q = Q; q.kc = kc; q.vc = vc; q.q_norm = W.q_norm; q.k_norm = W.k_norm;
+      q.rope_cos = ctx->tcos; q.rope_sin = ctx->tsin;
+      q.M = M; q.P = P; q.p0 = p0; q.nq = t.n_q_heads; q.nkv = t.n_kv_heads; q.cap = c.max_cache_steps; q.eps = c.rms_eps;
+      const int items = M * (t.n_q_heads + 2 * t.n_kv_heads);
+      if (ctx->kv_bf16()) hipLaunchKernelGGL((k_qk_rope_kv<uint16_t, uint16_t>), dim3((items + 3) / 4), dim3(256), 0, ctx->stream, q);
+      else hipLaunchKernelGGL((k_qk_rope_kv<uint16_t, float>), dim3((items + 3) / 4), dim3(256), 0, ctx->stream, q);
+      HIP_LAUNCH_CHECK();
+      PAttnArgs pa;
+      std::memset(&pa, 0, sizeof pa);
+      pa.q = Q; pa.kc = kc; pa.vc = vc; pa.out = O; pa.P = P; pa.p0 = p0; pa.nq = t.n_q_heads; pa.nkv = t.n_kv_heads;
+      pa.cap = c.max_cache_steps;
+      if (ctx->kv_bf16()) hipLaunchKernelGGL(k_prefill_attn<uint16_t>, dim3((P + 3) / 4, t.n_q_heads, B), dim3(256), 0, ctx->stream, pa);
+      else hipLaunchKernelGGL(k_prefill_attn<float>, dim3((P + 3) / 4, t.n_q_heads, B), dim3(256), 0, ctx->stream, pa);
+      HIP_LAUNCH_CHECK();
+      if (int rc = gemm(O, qd, nullptr, nullptr, {{W.wo, H}}, X, H, qd, M, 1)) return rc;
+      hipLaunchKernelGGL(k_rowscale, dim3((M + 3) / 4), dim3(256), 0, ctx->stream, X, H, M, H, c.rms_eps, RS);
+      HIP_LAUNCH_CHECK();
+      if (int rc = gemm(X, H, RS, W.mlp_norm, {{W.wg, F}, {W.wu, F}}, GU, 2 * F, H, M, 0)) return rc;
+      hipLaunchKernelGGL(k_swiglu_rows, dim3(std::min((M * F + 255) / 256, 4096)), dim3(256), 0, ctx->stream, GU, M, F, Hh);
+      HIP_LAUNCH_CHECK();
+      if (int rc = gemm(Hh, F, nullptr, nullptr, {{W.wd, H}}, X, H, F, M, 1)) return rc;
+    }
+    if (p0 + P == n) {
+      hipLaunchKernelGGL(k_last_rows, dim3(B), dim3(256), 0, ctx->stream, X, P, H, ctx->x);
+      HIP_LAUNCH_CHECK();
+    }
+  }
+  return TTS_OK;
 }
 
 int talker_stack(tts_ctx* ctx, int B, int pos_const, int pos_from_state) {
@@ -732,6 +820,7 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
   ctx->xerr = (uint32_t*)(w + L.xerr);
   ctx->xtp_ok = xtp_capable(*cfg);
   ctx->xtk_ok = xtk_capable(*cfg);
+  ctx->pgemm_ok = prefill_gemm_capable(*cfg);
   ctx->talker.c = cfg->talker;
   ctx->cp.c = cfg->codepred;
   // RoPE tables: angles p * theta^(-2i/d) in double, rounded to fp32.
@@ -880,11 +969,15 @@ int tts_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, floa
   HIP_LAUNCH_CHECK();
   hipLaunchKernelGGL(k_fill_u8, dim3(64), dim3(256), 0, ctx->stream, ctx->history, (size_t)batch * c.talker.vocab, (uint8_t)0);
   HIP_LAUNCH_CHECK();
-  for (int p = 0; p < n; ++p) {
-    if (int rc = gather(ctx, SRC_TABLE, batch, c.talker.hidden, nullptr, 0, ctx->embed_text, c.text_vocab, tokref(ids, n, 0, p, 0),
-                        ctx->x, c.talker.hidden))
-      return rc;
-    if (int rc = talker_stack(ctx, batch, p, 0)) return rc;
+  if (ctx->pgemm_ok && ctx->prefill_mode == TTS_PREFILL_GEMM) {
+    if (int rc = prefill_gemm(ctx, ids, batch, n)) return rc;
+  } else {
+    for (int p = 0; p < n; ++p) {
+      if (int rc = gather(ctx, SRC_TABLE, batch, c.talker.hidden, nullptr, 0, ctx->embed_text, c.text_vocab, tokref(ids, n, 0, p, 0),
+                          ctx->x, c.talker.hidden))
+        return rc;
+      if (int rc = talker_stack(ctx, batch, p, 0)) return rc;
+    }
   }
   if (int rc = talker_head(ctx, batch, 0, 0)) return rc;
   hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, n, 0);
@@ -1034,6 +1127,21 @@ int tts_get_exec_mode(const tts_ctx* ctx, int32_t* mode, int32_t* persistent_sup
   if (!ctx) return TTS_E_ARG;
   if (mode) *mode = ctx->exec_mode == TTS_EXEC_PERSISTENT && (ctx->xtp_ok || ctx->xtk_ok) ? TTS_EXEC_PERSISTENT : TTS_EXEC_KERNELS;
   if (persistent_supported) *persistent_supported = (ctx->xtp_ok ? TTS_PERSISTENT_CODEPRED : 0) | (ctx->xtk_ok ? TTS_PERSISTENT_TALKER : 0);
+  return TTS_OK;
+}
+
+int tts_set_prefill_mode(tts_ctx* ctx, int32_t mode) {
+  if (!ctx) return TTS_E_ARG;
+  if (mode != TTS_PREFILL_STEPS && mode != TTS_PREFILL_GEMM) return ctx->fail(TTS_E_ARG, "prefill mode %d", mode);
+  if (mode == TTS_PREFILL_GEMM && !ctx->pgemm_ok) return ctx->fail(TTS_E_UNSUPPORTED, "the GEMM prefill does not handle this config");
+  ctx->prefill_mode = mode;
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+int tts_get_prefill_mode(const tts_ctx* ctx, int32_t* mode) {
+  if (!ctx || !mode) return TTS_E_ARG;
+  *mode = ctx->pgemm_ok && ctx->prefill_mode == TTS_PREFILL_GEMM ? TTS_PREFILL_GEMM : TTS_PREFILL_STEPS;
   return TTS_OK;
 }
 

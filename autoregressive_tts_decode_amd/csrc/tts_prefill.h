@@ -1,0 +1,262 @@
+// Prefill: the Talker over a prompt of n text positions for B lockstep streams as dense GEMMs on
+// the matrix cores ("Running Qwen3-TTS on an AMD R9700", section "Running Qwen3-TTS": the prompt
+// pass before the frame loop). Positions are processed in chunks of at most kPrefillChunk per
+// stream, M = B x chunk rows per GEMM; causal attention of a chunk reads the KV cache, which holds
+// every earlier position. Activations stay fp32: each GEMM splits its fp32 input a into bf16
+// hi = bf16(a) and lo = bf16(a - hi) and accumulates W hi + W lo in fp32 (W is bf16 already), so
+// the product keeps about 16 mantissa bits of a.
+#pragma once
+
+#include "tts_device.h"
+
+namespace tts {
+
+constexpr int kPrefillChunk = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// C[M, N] (+)= (rs[m] * gain[k] * A[m, k]) W^T, W: bf16 [N, K] rows in up to 3 segments (each a
+// multiple of 64 rows), A fp32 [M, lda], C fp32 [M, ldc].
+struct GemmArgs {
+  const float* A;
+  int lda;
+  const float* rs;    // [M] row scale or nullptr
+  const void* gain;   // [K] bf16 or nullptr
+  const void* w[3];
+  int seg_rows[3], nseg;
+  float* C;
+  int ldc;
+  int M, N, K;
+  int add;            // 1: C += result (residual), 0: C = result
+};
+
+constexpr int kGBM = 64, kGBN = 64, kGBK = 64, kGLD = kGBK + 8;  // tile, LDS row stride (bf16)
+
+// One 64 x 64 tile of C per workgroup (4 waves, each 32 x 32 = 2 x 2 MFMA 16x16x32 blocks).
+__global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
+  __shared__ __align__(16) __bf16 Ahi[kGBM][kGLD];
+  __shared__ __align__(16) __bf16 Alo[kGBM][kGLD];
+  __shared__ __align__(16) __bf16 Bs[kGBN][kGLD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.x * kGBN, m0 = blockIdx.y * kGBM;
+  int seg = 0, nrel = n0;
+  while (seg + 1 < a.nseg && nrel >= a.seg_rows[seg]) { nrel -= a.seg_rows[seg]; ++seg; }
+  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w[seg]) + (size_t)nrel * a.K;
+  const int lr = tid >> 2, lk = (tid & 3) * 16;  // loader: row lr of the tile, 16 k from lk
+  const bool arow = m0 + lr < a.M;
+  const float rsc = (a.rs && arow) ? a.rs[m0 + lr] : 1.f;
+  const float* Ap = a.A + (size_t)(m0 + lr) * a.lda + lk;
+  const uint16_t* Wp = W + (size_t)lr * a.K + lk;
+  const uint16_t* gp = reinterpret_cast<const uint16_t*>(a.gain);
+  const int wm = wave >> 1, wn = wave & 1, lq = lane >> 4, lc = lane & 15;
+  f32x4v acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4v){0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.K; k0 += kGBK) {
+    float av[16];
+#pragma unroll
+    for (int e = 0; e < 16; e += 4) {
+      const float4 f = arow ? *reinterpret_cast<const float4*>(Ap + k0 + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      av[e] = f.x; av[e + 1] = f.y; av[e + 2] = f.z; av[e + 3] = f.w;
+    }
+    const u32x4 b0 = *reinterpret_cast<const u32x4*>(Wp + k0);
+    const u32x4 b1 = *reinterpret_cast<const u32x4*>(Wp + k0 + 8);
+    if (gp) {
+      const u32x4 g0 = *reinterpret_cast<const u32x4*>(gp + k0 + lk);
+      const u32x4 g1 = *reinterpret_cast<const u32x4*>(gp + k0 + lk + 8);
+      float gf0[8], gf1[8];
+      unpack(g0, gf0, (uint16_t*)nullptr);
+      unpack(g1, gf1, (uint16_t*)nullptr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        av[e] = av[e] * rsc * gf0[e];
+        av[e + 8] = av[e + 8] * rsc * gf1[e];
+      }
+    } else if (a.rs) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) av[e] *= rsc;
+    }
+    __syncthreads();  // the previous step's operand reads are done
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const __bf16 hi = (__bf16)av[e];
+      Ahi[lr][lk + e] = hi;
+      Alo[lr][lk + e] = (__bf16)(av[e] - (float)hi);
+    }
+    *reinterpret_cast<u32x4*>(&Bs[lr][lk]) = b0;
+    *reinterpret_cast<u32x4*>(&Bs[lr][lk + 8]) = b1;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kGBK; kk += 32) {
+      bf16x8 ah[2], al[2], bw[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        ah[i] = *reinterpret_cast<const bf16x8*>(&Ahi[wm * 32 + i * 16 + lc][kk + 8 * lq]);
+        al[i] = *reinterpret_cast<const bf16x8*>(&Alo[wm * 32 + i * 16 + lc][kk + 8 * lq]);
+        bw[i] = *reinterpret_cast<const bf16x8*>(&Bs[wn * 32 + i * 16 + lc][kk + 8 * lq]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
+        }
+    }
+  }
+  // lane holds C[4 lq + r][lc] of each 16 x 16 block
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 32 + i * 16 + 4 * lq + r, n = n0 + wn * 32 + j * 16 + lc;
+        if (m < a.M) {
+          float* c = a.C + (size_t)m * a.ldc + n;
+          *c = a.add ? *c + acc[i][j][r] : acc[i][j][r];
+        }
+      }
+}
+
+// rs[m] = 1 / sqrt(mean(x[m]^2) + eps) over K; one wave per row.
+__global__ __launch_bounds__(256) void k_rowscale(const float* x, int ldx, int M, int K, float eps, float* rs) {
+  const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (m >= M) return;
+  float s = 0.f;
+  for (int k = lane; k < K; k += 64) s += x[(size_t)m * ldx + k] * x[(size_t)m * ldx + k];
+  s = wave_sum(s);
+  if (lane == 0) rs[m] = 1.0f / sqrtf(s / (float)K + eps);
+}
+
+// Rows b * P + i of X = E_text[ids[b * n + p0 + i]] (i < P), fp32.
+template <typename WT>
+__global__ void k_embed_rows(const int32_t* ids, int n, int p0, int P, int vocab, const void* table, int H, float* X) {
+  const int row = blockIdx.x, b = row / P, i = row % P;
+  int tok = ids[(size_t)b * n + p0 + i];
+  tok = tok < 0 ? 0 : (tok >= vocab ? vocab - 1 : tok);
+  const WT* e = reinterpret_cast<const WT*>(table) + (size_t)tok * H;
+  for (int k = threadIdx.x; k < H; k += blockDim.x) X[(size_t)row * H + k] = to_f32(e[k]);
+}
+
+struct QkArgs {
+  const float* qkv;   // [M, (nq + 2 nkv) d]
+  float* q;           // [M, nq d] normed + rotated q
+  void *kc, *vc;      // cache of this layer: [B][nkv][cap][d]
+  const void *q_norm, *k_norm;
+  const float *rope_cos, *rope_sin;  // [cap][d / 2]
+  int M, P, p0, nq, nkv, cap;
+  float eps;
+};
+
+// One wave per (row, head): q heads -> per-head RMSNorm + RoPE into q; k heads -> the same into the
+// cache at the row's position; v heads -> copied into the cache. d = 128.
+template <typename WT, typename KT>
+__global__ __launch_bounds__(256) void k_qk_rope_kv(QkArgs a) {
+  const int nh = a.nq + 2 * a.nkv;
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (item >= a.M * nh) return;
+  const int row = item / nh, j = item % nh, b = row / a.P, pos = a.p0 + row % a.P;
+  constexpr int d = 128;
+  const float* src = a.qkv + (size_t)row * nh * d + (size_t)j * d;
+  float v0 = src[lane], v1 = src[lane + 64];
+  if (j < a.nq + a.nkv) {
+    const WT* gn = reinterpret_cast<const WT*>(j < a.nq ? a.q_norm : a.k_norm);
+    const float sc = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)d + a.eps);
+    v0 *= sc * to_f32(gn[lane]);
+    v1 *= sc * to_f32(gn[lane + 64]);
+    const float c = a.rope_cos[(size_t)pos * 64 + lane], s = a.rope_sin[(size_t)pos * 64 + lane];
+    const float r0 = v0 * c - v1 * s, r1 = v1 * c + v0 * s;
+    v0 = r0;
+    v1 = r1;
+  }
+  if (j < a.nq) {
+    float* q = a.q + (size_t)row * a.nq * d + (size_t)j * d;
+    q[lane] = v0;
+    q[lane + 64] = v1;
+  } else {
+    const int g = j < a.nq + a.nkv ? j - a.nq : j - a.nq - a.nkv;
+    KT* dst = reinterpret_cast<KT*>(j < a.nq + a.nkv ? a.kc : a.vc) + (((size_t)b * a.nkv + g) * a.cap + pos) * d;
+    store_elem(dst + lane, v0);
+    store_elem(dst + lane + 64, v1);
+  }
+}
+
+struct PAttnArgs {
+  const float* q;     // [M, nq d]
+  const void *kc, *vc;
+  float* out;         // [M, nq d]
+  int P, p0, nq, nkv, cap;
+};
+
+// Causal attention of prefill rows: one wave per (row i of stream b, q head h) over cached
+// positions 0 .. p0 + i; lanes 4 t + e cover 16 positions per pass (quarter e of d = 128).
+template <typename KT>
+__global__ __launch_bounds__(256) void k_prefill_attn(PAttnArgs a) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6), h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63;
+  if (i >= a.P) return;
+  constexpr int d = 128;
+  const int row = b * a.P + i, pos = a.p0 + i, g = h / (a.nq / a.nkv);
+  const KT* kc = reinterpret_cast<const KT*>(a.kc) + ((size_t)b * a.nkv + g) * a.cap * d;
+  const KT* vc = reinterpret_cast<const KT*>(a.vc) + ((size_t)b * a.nkv + g) * a.cap * d;
+  const float* q = a.q + (size_t)row * a.nq * d + (size_t)h * d;
+  const int tq = lane >> 2, e = lane & 3;
+  float qv[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) qv[k] = q[32 * e + k];
+  const float scale = 1.0f / sqrtf((float)d);
+  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int base = 0; base <= pos; base += 16) {
+    const int t = base + tq;
+    const bool valid = t <= pos;
+    const KT* kr = kc + (size_t)(valid ? t : 0) * d + 32 * e;
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) s = fmaf(qv[k], to_f32(kr[k]), s);
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s = valid ? s * scale : -INFINITY;
+    float mx = s;
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float mn = fmaxf(m, mx);
+    const float corr = m == -INFINITY ? 0.f : expf(m - mn);
+    const float w = valid ? expf(s - mn) : 0.f;
+    float ws = w;
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1) ws += __shfl_xor(ws, o);
+    l = l * corr + ws;
+    o0 *= corr;
+    o1 *= corr;
+    m = mn;
+    const int np = min(16, pos + 1 - base);
+    for (int tt = 0; tt < np; ++tt) {
+      const float wt = __shfl(w, 4 * tt);
+      o0 = fmaf(wt, to_f32(vc[(size_t)(base + tt) * d + lane]), o0);
+      o1 = fmaf(wt, to_f32(vc[(size_t)(base + tt) * d + lane + 64]), o1);
+    }
+  }
+  float* o = a.out + (size_t)row * a.nq * d + (size_t)h * d;
+  o[lane] = o0 / l;
+  o[lane + 64] = o1 / l;
+}
+
+// h[m, f] = silu(gu[m, f]) * gu[m, F + f]
+__global__ void k_swiglu_rows(const float* gu, int M, int F, float* h) {
+  const size_t n = (size_t)M * F;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < n; idx += (size_t)gridDim.x * blockDim.x) {
+    const size_t m = idx / F, f = idx % F;
+    h[idx] = silu(gu[m * 2 * F + f]) * gu[m * 2 * F + F + f];
+  }
+}
+
+// x[b] = X[b * P + P - 1] (the last prompt row of each stream)
+__global__ void k_last_rows(const float* X, int P, int H, float* x) {
+  const int b = blockIdx.x;
+  for (int k = threadIdx.x; k < H; k += blockDim.x) x[(size_t)b * H + k] = X[((size_t)b * P + P - 1) * H + k];
+}
+
+}  // namespace tts

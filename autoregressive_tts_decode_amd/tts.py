@@ -31,10 +31,11 @@ STATUS_NAMES = {0: "TTS_OK", -1: "TTS_E_ARG", -2: "TTS_E_SHAPE", -3: "TTS_E_CAPA
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTED = ["tts_workspace_bytes", "tts_create", "tts_load_weights", "tts_prefill", "tts_talker_step",
-            "tts_codepred_frame", "tts_sample", "tts_run_frames", "tts_set_exec_mode", "tts_get_exec_mode",
+            "tts_codepred_frame", "tts_sample", "tts_run_frames", "tts_set_exec_mode", "tts_get_exec_mode", "tts_set_prefill_mode", "tts_get_prefill_mode",
             "tts_device_status", "tts_get_progress", "tts_reset", "tts_last_error", "tts_destroy"]
 EXEC_KERNELS, EXEC_PERSISTENT = 0, 1
 PERSISTENT_CODEPRED, PERSISTENT_TALKER = 1, 2  # bits of exec_mode()[1]
+PREFILL_STEPS, PREFILL_GEMM = 0, 1
 
 
 class StackCfgC(ctypes.Structure):
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tts_run_frames.argtypes = [P, I32, ctypes.POINTER(SamplingC), ctypes.POINTER(SamplingC), P, P]
     lib.tts_get_progress.argtypes = [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     lib.tts_set_exec_mode.argtypes = [P, I32]
+    lib.tts_set_prefill_mode.argtypes = [P, I32]
+    lib.tts_get_prefill_mode.argtypes = [P, ctypes.POINTER(I32)]
     lib.tts_get_exec_mode.argtypes = [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     lib.tts_device_status.argtypes = [P, ctypes.POINTER(I32)]
     lib.tts_reset.argtypes = [P]
@@ -235,6 +238,14 @@ class TTSDecoder:
         m, sup = ctypes.c_int32(), ctypes.c_int32()
         self._check(self.lib.tts_get_exec_mode(self.ctx, ctypes.byref(m), ctypes.byref(sup)), "tts_get_exec_mode")
         return m.value, sup.value
+
+    def set_prefill_mode(self, mode: int):
+        self._check(self.lib.tts_set_prefill_mode(self.ctx, mode), "tts_set_prefill_mode")
+
+    def prefill_mode(self) -> int:
+        m = ctypes.c_int32()
+        self._check(self.lib.tts_get_prefill_mode(self.ctx, ctypes.byref(m)), "tts_get_prefill_mode")
+        return m.value
 
     def device_status(self) -> int:
         st = ctypes.c_int32()

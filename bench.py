@@ -110,6 +110,8 @@ def main():
         times.append(e0.elapsed_time(e1) / 1e3)
     t = statistics.median(times)
     fps = B * K / t
+    tt = model.talker
+    prefill_flops = 2.0 * B * wl.prefill_len * tt.n_layers * roofline.layer_weight_elems(tt)
     # Dominant kernel: the persistent CodePredictor frame kernel (about 60% of a frame), timed
     # alone with HIP events on the decoder's stream over back-to-back launches.
     mode, persistent_ok = dec.exec_mode()
@@ -160,6 +162,9 @@ def main():
                    "kv_cache": dec.kv_dtype},
         "rtf": round(roofline.rtf_from_fps(fps / B), 6),
         "prefill_ms": round(statistics.median(prefill_ms), 2),
+        "prefill": {"mode": "gemm" if dec.prefill_mode() == tts.PREFILL_GEMM else "steps", "positions": wl.prefill_len,
+                    "streams": B, "tflops": round(prefill_flops / (statistics.median(prefill_ms) * 1e-3) / 1e12, 2),
+                    "note": "algorithmic FLOPs (2 per weight per row) of the Talker prompt pass; wall time includes the head"},
         "ms_per_step_all_reps": [round(x / K * 1e3, 4) for x in times],
         "frame_roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
                            "frac": round(achieved / peak, 4),

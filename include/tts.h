@@ -164,6 +164,19 @@ enum tts_persistent_kernels { TTS_PERSISTENT_CODEPRED = 1, TTS_PERSISTENT_TALKER
 int tts_set_exec_mode(tts_ctx* ctx, int32_t mode);
 int tts_get_exec_mode(const tts_ctx* ctx, int32_t* mode, int32_t* persistent_supported);
 
+/* How tts_prefill runs the prompt ("Running Qwen3-TTS on an AMD R9700",
+ * section "Running Qwen3-TTS": the prompt pass before the frame loop):
+ *  TTS_PREFILL_GEMM (default where supported: bf16 weights, head dimension
+ *    128, Talker dimensions multiples of 64): chunks of up to 64 positions
+ *    per stream as MFMA GEMMs over all streams' rows, causal attention over
+ *    the KV cache. fp32 activations enter each GEMM as two bf16 parts
+ *    (hi, lo), so the results match the step path up to summation order.
+ *  TTS_PREFILL_STEPS: one position at a time through the decode kernels.
+ * TTS_E_UNSUPPORTED when GEMM is asked for and the config cannot use it. */
+enum tts_prefill_mode { TTS_PREFILL_STEPS = 0, TTS_PREFILL_GEMM = 1 };
+int tts_set_prefill_mode(tts_ctx* ctx, int32_t mode);
+int tts_get_prefill_mode(const tts_ctx* ctx, int32_t* mode);
+
 /* Synchronise the context's stream and report the persistent kernel's
  * exchange status: *status = 0 when every exchange completed, nonzero when a
  * workgroup timed out waiting (e.g. not all workgroups were resident); the

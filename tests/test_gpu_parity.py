@@ -497,3 +497,44 @@ def test_1p7b_x32_sampled_streams_teacher_forced():
     torch.cuda.empty_cache()
     assert checked > 0.9 * (checked + exempt)
     print(f"1.7b x32 sampled: logits rel err <= {worst:.2e}; {checked} draws equal, {exempt} exempt")
+
+
+@pytest.mark.parametrize("name", ["0.6b", "1.7b"])
+def test_gemm_prefill_matches_step_prefill_and_oracle(name):
+    """The prompt pass as MFMA GEMMs (chunks of 64 positions, 2 streams, a ragged last chunk) against
+    the one-position-at-a-time path and the oracle: logits after the prompt and after one Talker step
+    on the same codes (which reads the KV cache both prefills wrote)."""
+    model = config.MODELS[name]
+    w = synth.make_weights(model, 0)
+    B, n = 2, 100
+    ids = synth.random_ids(n, model.text_vocab, seed=11, batch=B)
+    codes = np.concatenate([synth.random_ids(1, model.talker.vocab, seed=12, batch=B),
+                            synth.random_ids(15, model.codepred.vocab, seed=13, batch=B)], axis=1)
+    dec, dw = make_decoder(model, B, n + 4, 4, w)
+    d = dev()
+    got = {}
+    for mode in (tts.PREFILL_GEMM, tts.PREFILL_STEPS):
+        dec.set_prefill_mode(mode)
+        assert dec.prefill_mode() == mode
+        l0 = torch.zeros((B, model.talker.vocab), dtype=torch.float32, device=d)
+        l1 = torch.zeros_like(l0)
+        dec.prefill(torch.from_numpy(ids).to(d), l0)
+        dec.talker_step(torch.from_numpy(codes).to(d), l1)
+        torch.cuda.synchronize()
+        got[mode] = (l0.cpu().numpy(), l1.cpu().numpy())
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    X = np.concatenate([orc.embed_text[ids], orc.embed_sum(codes)[:, None]], axis=1)  # [B, n + 1, Ht]
+    hs = orc.full_forward("talker", X)
+    ref0, ref1 = linear(hs[:, n - 1], orc.lm_head), linear(hs[:, n], orc.lm_head)
+    for mode, (g0, g1) in got.items():
+        e0, e1 = rowwise_rel_err(g0, ref0).max(), rowwise_rel_err(g1, ref1).max()
+        assert e0 <= 1e-2 and e1 <= 1e-2, (mode, e0, e1)
+        for g, r in ((g0, ref0), (g1, ref1)):
+            n_, ex, bad = greedy_agreement(np.argmax(g, axis=-1), r)
+            assert not bad, (mode, bad)
+        print(f"{name} prefill mode {mode}: rel err after prompt {e0:.2e}, after one step {e1:.2e}")
+    e = rowwise_rel_err(got[tts.PREFILL_GEMM][1], got[tts.PREFILL_STEPS][1]).max()
+    print(f"{name}: GEMM vs step prefill, step logits rel diff {e:.2e}")

@@ -105,14 +105,17 @@ __device__ __forceinline__ void st_c(u64* p, u64 v) { __hip_atomic_store(glb(p),
 __device__ __forceinline__ u64 ld_c(const u64* p) { return __hip_atomic_load(glb(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
 // Gather n tagged entries, entry i read from at(i), into lds[0 .. n), polling until every entry
-// carries tag; an entry already received is not read again. n <= KMAX * NT. Returns false (and
-// flags err) on time-out or when another workgroup failed.
+// carries tag; an entry already received is not read again. Each wave polls its own entries
+// and the workgroup meets once, at the end, so one slow load does not hold back the other waves'
+// next polls. n <= KMAX * NT. Returns false (and flags err) on time-out or when another
+// workgroup failed.
 template <int KMAX, typename At>
 __device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t* err, At at) {
   unsigned pend = 0;
 #pragma unroll
   for (int k = 0; k < KMAX; ++k)
     if (threadIdx.x + k * NT < n) pend |= 1u << k;
+  bool fail = false;
   for (long long s = 0;; ++s) {
     u64 v[KMAX];
 #pragma unroll
@@ -124,15 +127,20 @@ __device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t
         lds[threadIdx.x + k * NT] = valof(v[k]);
         pend &= ~(1u << k);
       }
-    if (__syncthreads_and(pend == 0)) return true;
+    if (!__any(pend != 0)) break;
     if ((s & 255) == 255) {
       const uint32_t e = __hip_atomic_load(glb(err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__syncthreads_or(e != 0 || s > kSpin)) {
-        if (threadIdx.x == 0) __hip_atomic_fetch_or(glb(err), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return false;
+      if (e != 0 || s > kSpin) {
+        fail = true;
+        break;
       }
     }
   }
+  if (__syncthreads_or(fail)) {
+    if (threadIdx.x == 0) __hip_atomic_fetch_or(glb(err), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+  }
+  return true;
 }
 
 // Gather the n contiguous entries src[0 .. n) (see get_at).

@@ -109,22 +109,27 @@ __device__ __forceinline__ u64 ld_c(const u64* p) { return __hip_atomic_load(glb
 // and the workgroup meets once, at the end, so one slow load does not hold back the other waves'
 // next polls. n <= KMAX * NT. Returns false (and flags err) on time-out or when another
 // workgroup failed.
-template <int KMAX, typename At>
+// NPOLL: the first NPOLL threads (whole waves) poll, entry i on thread i % NPOLL; the others only
+// meet the pollers at the final barrier (waves that must not wait behind their own outstanding
+// weight loads). n <= KMAX * NPOLL.
+template <int KMAX, int NPOLL = NT, typename At>
 __device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t* err, At at) {
   unsigned pend = 0;
+  if (NPOLL == NT || threadIdx.x < NPOLL) {
 #pragma unroll
-  for (int k = 0; k < KMAX; ++k)
-    if (threadIdx.x + k * NT < n) pend |= 1u << k;
+    for (int k = 0; k < KMAX; ++k)
+      if (threadIdx.x + k * NPOLL < n) pend |= 1u << k;
+  }
   bool fail = false;
-  for (long long s = 0;; ++s) {
+  for (long long s = 0; NPOLL == NT || threadIdx.x < NPOLL; ++s) {
     u64 v[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-      if (pend & (1u << k)) v[k] = ld_c(at(threadIdx.x + k * NT));
+      if (pend & (1u << k)) v[k] = ld_c(at(threadIdx.x + k * NPOLL));
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
       if ((pend & (1u << k)) && tagof(v[k]) == tag) {
-        lds[threadIdx.x + k * NT] = valof(v[k]);
+        lds[threadIdx.x + k * NPOLL] = valof(v[k]);
         pend &= ~(1u << k);
       }
     if (!__any(pend != 0)) break;
@@ -144,9 +149,9 @@ __device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t
 }
 
 // Gather the n contiguous entries src[0 .. n) (see get_at).
-template <int KMAX>
+template <int KMAX, int NPOLL = NT>
 __device__ __forceinline__ bool get_flat(const u64* src, int n, uint32_t tag, float* lds, uint32_t* err) {
-  return get_at<KMAX>(n, tag, lds, err, [&](int i) -> const u64* { return src + i; });
+  return get_at<KMAX, NPOLL>(n, tag, lds, err, [&](int i) -> const u64* { return src + i; });
 }
 
 // ---------------------------------------------------------------------------- weight rows
@@ -324,7 +329,7 @@ __device__ __forceinline__ void issue_proj(RowsB<WT>& R, const CpDesc& D, int g,
 // cpar alternates the cross slot so a rank one exchange ahead never overwrites unread values.
 // HMX: the largest H the caller supports (sizes the cross gather); KMAX: loads per thread of the
 // intra gather (M * (H + NR) entries).
-template <int M, int HMX, int KMAX, typename AfterPut>
+template <int M, int HMX, int KMAX, int NPOLL = NT, typename AfterPut>
 __device__ __forceinline__ bool reduce_gather(const Xch& X, const float* out, float* xs, float* xn, int H, bool residual,
                                               uint32_t& tag, int& iring, int& cpar, int g, int r, AfterPut after_put) {
   const int tid = threadIdx.x, hper = H / NR;
@@ -337,7 +342,7 @@ __device__ __forceinline__ bool reduce_gather(const Xch& X, const float* out, fl
   // (hper is a power of two: entry i -> element i & (hper - 1) of segment i >> lh)
   const u64* base = X.xcr + ((size_t)(r * NX) * 2 + (cpar & 1)) * CSZ;
   const int lh = __builtin_ctz(hper);
-  if (!get_at<(NX * M * (HMX / NR) + NT - 1) / NT>(NX * M * hper, tag, xn, X.err, [&](int i) -> const u64* {
+  if (!get_at<(NX * M * (HMX / NR) + NPOLL - 1) / NPOLL, NPOLL>(NX * M * hper, tag, xn, X.err, [&](int i) -> const u64* {
         const int sg = i >> lh, e = i & (hper - 1);
         return base + (size_t)(sg / M) * (2 * CSZ) + (sg % M) * 64 + e;
       }))
@@ -363,12 +368,12 @@ __device__ __forceinline__ bool reduce_gather(const Xch& X, const float* out, fl
     }
   }
   __syncthreads();  // the gather below overwrites the residual rows read above
-  return get_flat<KMAX>(buf, M * (H + NR), tag, xs, X.err);
+  return get_flat<KMAX, NPOLL>(buf, M * (H + NR), tag, xs, X.err);
 }
 
 // Intra gather of a slice: this workgroup's n values per row (vals(e, m)) land at row offset
 // n * r of every rank's copy; the full rows (width w) of all ranks go to dst.
-template <int M, int KMAX, typename ValFn, typename AfterPut>
+template <int M, int KMAX, int NPOLL = NT, typename ValFn, typename AfterPut>
 __device__ __forceinline__ bool slice_gather(const Xch& X, int n, int w, ValFn vals, float* dst, uint32_t& tag, int& iring,
                                              int g, int r, AfterPut after_put) {
   ++tag;
@@ -378,7 +383,7 @@ __device__ __forceinline__ bool slice_gather(const Xch& X, int n, int w, ValFn v
     st_c(buf + m * w + n * r + e, pack(vals(e, m), tag));
   }
   after_put();
-  return get_flat<KMAX>(buf, M * w, tag, dst, X.err);
+  return get_flat<KMAX, NPOLL>(buf, M * w, tag, dst, X.err);
 }
 
 // ---------------------------------------------------------------------------- per-thread constants

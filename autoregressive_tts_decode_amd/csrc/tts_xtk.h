@@ -10,9 +10,13 @@
 //   * attention reads the fp32 KV cache in HBM: the positions 0..p are split into 32 contiguous
 //     chunks, one per rank of the XCD; each rank produces a partial softmax state per head, and
 //     two exchanges combine them (rank r combines 8 of the 2 x 128 outputs, then an all-gather);
-//   * the weight slices are large (up to 192 KB per workgroup and phase), so a layer streams as 8
-//     chunks of at most 64 KB per workgroup through two 32-register buffers, alternating, each
-//     chunk issued when the chunk two back has been consumed.
+//   * the waves of a workgroup split by role: four front waves poll the exchanges and run the
+//     attention, four back waves stream the weight rows (the loads of one wave return in order, so
+//     a poll never waits behind weight rows in flight);
+//   * the weight slices are large (up to 192 KB per workgroup and phase): the q/k/v, output and
+//     gate/up rows stream in chunks of at most 32 KB through two 32-register buffers of the back
+//     waves, each chunk issued as soon as the one two back has been consumed, while the down rows
+//     (up to 96 KB) are copied straight into LDS during the attention.
 #pragma once
 
 #include "tts_xtp.h"
@@ -48,8 +52,16 @@ struct TkCall {
   int32_t bump_pos, bump_frame;
 };
 
-// One weight chunk in registers: rows wave + NW * j (j < RR) of the chunk, 16-byte units
-// lane + 64 * k (k < KK) of each row, RR * KK <= WB.
+// Wave roles. The front waves poll every exchange and run the attention; the back waves stream
+// the weight rows and do the row dots. A poll is a load, and the loads of one wave return in
+// order, so a front wave never waits behind weight rows in flight.
+constexpr int NF = 4;                        // front waves
+constexpr int NB = NW - NF;                  // back waves
+constexpr int PF = NF * 64;                  // polling threads
+constexpr int TEW = (THMAX / NR) * TFXMAX;   // down-projection rows of a workgroup (elements)
+
+// One weight chunk in the back waves' registers: rows (wave - NF) + NB * j (j < RR) of the chunk,
+// 16-byte units lane + 64 * k (k < KK) of each row, RR * KK <= WB.
 struct WBuf {
   u32x4 b[WB];
 };
@@ -59,10 +71,11 @@ __device__ __forceinline__ void wb_issue(WBuf& B, int nrows, int ncols, RowFn ro
   static_assert(RR * KK <= WB, "chunk exceeds the weight buffer");
   constexpr int E = WTraits<WT>::E;
   const int lane = threadIdx.x & 63, wave = wave_id();
+  if (wave < NF) return;
   const int units = ncols / E;
 #pragma unroll
   for (int j = 0; j < RR; ++j) {
-    const int i = wave + NW * j;
+    const int i = (wave - NF) + NB * j;
     if (i < nrows) {
       const GLB u32x4* p = glb(reinterpret_cast<const u32x4*>(rowptr(i)));
 #pragma unroll
@@ -74,11 +87,12 @@ __device__ __forceinline__ void wb_issue(WBuf& B, int nrows, int ncols, RowFn ro
   }
 }
 
-// out[i] = dot(row i, x[0 .. ncols)) for this wave's rows of the chunk (x and out in LDS).
+// out[i] = dot(row i, x[0 .. ncols)) for this back wave's rows of the chunk (x and out in LDS).
 template <typename WT, int RR, int KK>
 __device__ __forceinline__ void wb_dot(const WBuf& B, int nrows, int ncols, const float* x, float* out) {
   constexpr int E = WTraits<WT>::E;
   const int lane = threadIdx.x & 63, wave = wave_id();
+  if (wave < NF) return;
   const int units = ncols / E;
   float acc[RR];
 #pragma unroll
@@ -95,7 +109,7 @@ __device__ __forceinline__ void wb_dot(const WBuf& B, int nrows, int ncols, cons
       }
 #pragma unroll
       for (int j = 0; j < RR; ++j) {
-        if (wave + NW * j < nrows) {
+        if ((wave - NF) + NB * j < nrows) {
           float wf[8];
           unpack(B.b[j * KK + k], wf, (WT*)nullptr);
           float s = acc[j];
@@ -108,7 +122,7 @@ __device__ __forceinline__ void wb_dot(const WBuf& B, int nrows, int ncols, cons
   }
 #pragma unroll
   for (int j = 0; j < RR; ++j) {
-    const int i = wave + NW * j;
+    const int i = (wave - NF) + NB * j;
     if (i < nrows) {
       const float v = wave_sum(acc[j]);
       if (lane == 0) out[i] = v;
@@ -116,18 +130,17 @@ __device__ __forceinline__ void wb_dot(const WBuf& B, int nrows, int ncols, cons
   }
 }
 
-// The 8 chunks of a layer (rows per wave RR x 16-byte units per lane KK), for H <= 2048,
+// The chunks of a layer (rows per back wave RR x 16-byte units per lane KK), for H <= 2048,
 // F / 8 <= 768, 8 KV heads of dimension 128 and 2 query heads per KV head:
-//   A0, A1  q/k/v slice rows [0, 8) and [8, 16) x H          -> 1 x 4
-//   C       output projection: H/32 rows x 256                -> 8 x 1
-//   D0..D2  gate rows then up rows (2 F/256 in all) x H,
-//           16 rows per chunk                                  -> 2 x 4
-//   E0, E1  down: first and second half of H/32 rows x F/8     -> 4 x 2
-// and after the last layer F, the semantic head: V/256 rows x H -> 2 x 4.
+//   A0, A1  q/k/v slice rows [0, 8) and [8, 16) x H               -> 2 x 4
+//   C0, C1  output projection: halves of the H/32 rows x 256       -> 8 x 1
+//   D0..D5  gate rows then up rows (2 F/256 in all) x H, 8 a chunk -> 2 x 4
+//   down    H/32 rows x F/8, copied into LDS (not registers) while the attention runs
+// and after the last layer F0, F1, the semantic head: V/256 <= 16 rows x H, 8 a chunk -> 2 x 4.
 template <typename WT>
-__device__ __forceinline__ void tk_issue_a(WBuf& B, const TkDesc& D, const LayerW& W, int half, int g, int r) {
+__device__ __forceinline__ void tk_issue_a(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int half, int g, int r) {
   const int H = D.H, d = D.d, G = D.nq / D.nkv, qper = (G + 2) * d / NR;
-  wb_issue<WT, 1, 4>(B, qper / 2, H, [&](int i) -> const WT* {
+  wb_issue<WT, 2, 4>(B, qper / 2, H, [&](int i) -> const WT* {
     const int q = qper * r + (qper / 2) * half + i;
     if (q < G * d) return reinterpret_cast<const WT*>(W.wq) + (size_t)(G * d * g + q) * H;
     if (q < (G + 1) * d) return reinterpret_cast<const WT*>(W.wk) + (size_t)(d * g + q - G * d) * H;
@@ -135,34 +148,28 @@ __device__ __forceinline__ void tk_issue_a(WBuf& B, const TkDesc& D, const Layer
   });
 }
 template <typename WT>
-__device__ __forceinline__ void tk_issue_c(WBuf& B, const TkDesc& D, const LayerW& W, int g, int r) {
-  const int hper = D.H / NR, Gd = D.nq / D.nkv * D.d;
-  wb_issue<WT, 8, 1>(B, hper, Gd, [&](int i) -> const WT* {
-    return reinterpret_cast<const WT*>(W.wo) + (size_t)(hper * r + i) * (D.nq * D.d) + Gd * g;
+__device__ __forceinline__ void tk_issue_c(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int half, int g, int r) {
+  const int hper = D.H / NR, hh = hper / 2, Gd = D.nq / D.nkv * D.d;
+  wb_issue<WT, 8, 1>(B, hh, Gd, [&](int i) -> const WT* {
+    return reinterpret_cast<const WT*>(W.wo) + (size_t)(hper * r + hh * half + i) * (D.nq * D.d) + Gd * g;
   });
 }
 // rows of chunk c of the rank's gate rows (0 .. fper) followed by its up rows (fper .. 2 fper)
+__device__ __forceinline__ int tk_d_rows(int nd, int c) { return min(8, max(0, nd - 8 * c)); }
 template <typename WT>
-__device__ __forceinline__ void tk_issue_d(WBuf& B, const TkDesc& D, const LayerW& W, int c, int g, int r) {
+__device__ __forceinline__ void tk_issue_d(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int c, int g, int r) {
   const int fx = D.F / NX, fper = fx / NR;
-  wb_issue<WT, 2, 4>(B, min(16, max(0, 2 * fper - 16 * c)), D.H, [&](int i) -> const WT* {
-    const int q = 16 * c + i;
+  wb_issue<WT, 2, 4>(B, tk_d_rows(2 * fper, c), D.H, [&](int i) -> const WT* {
+    const int q = 8 * c + i;
     const int f = fx * g + fper * r + (q < fper ? q : q - fper);
     return reinterpret_cast<const WT*>(q < fper ? W.wg : W.wu) + (size_t)f * D.H;
   });
 }
 template <typename WT>
-__device__ __forceinline__ void tk_issue_e(WBuf& B, const TkDesc& D, const LayerW& W, int half, int g, int r) {
-  const int hper = D.H / NR, hh = hper / 2, fx = D.F / NX;
-  wb_issue<WT, 4, 2>(B, hh, fx, [&](int i) -> const WT* {
-    return reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r + hh * half + i) * D.F + fx * g;
-  });
-}
-template <typename WT>
-__device__ __forceinline__ void tk_issue_f(WBuf& B, const TkDesc& D) {
+__device__ __forceinline__ void tk_issue_f(WBuf& B, const KCONST TkDesc& D, int half) {
   const int vper = D.V / NWG;
-  wb_issue<WT, 2, 4>(B, vper, D.H, [&](int i) -> const WT* {
-    return reinterpret_cast<const WT*>(D.lm_head) + (size_t)(vper * blockIdx.x + i) * D.H;
+  wb_issue<WT, 2, 4>(B, min(8, max(0, vper - 8 * half)), D.H, [&](int i) -> const WT* {
+    return reinterpret_cast<const WT*>(D.lm_head) + (size_t)(vper * blockIdx.x + 8 * half + i) * D.H;
   });
 }
 
@@ -172,22 +179,24 @@ struct TkSmem {
   float qkv[512];             // this XCD's q/k/v slice
   float q[2][128];            // normed + rotated q of the XCD's two heads
   float kp[128], vp[128];     // the step's k (normed + rotated) and v
-  float wm[NW][2], wl[NW][2]; // per-wave softmax max and sum per head
-  float wo[NW][2][128];       // per-wave unnormalised attention output per head
+  float wm[NF][2], wl[NF][2]; // per-wave softmax max and sum per head
+  float wo[NF][2][128];       // per-wave unnormalised attention output per head
   float cmb[NR * 10];         // gathered partials of this rank's 8 outputs
   float ob[256];              // attention output of the XCD's heads
   float hb[TFXMAX];           // SwiGLU slice of the XCD
   float out[128];             // row results of this workgroup
   float red[64];
+  __align__(16) uint16_t ew[TEW];  // down-projection rows [H/32][F/8] of this workgroup
 };
 
-// Per-thread norm gains (elements tid, tid + NT, tid + 2 NT, tid + 3 NT; H <= 4 NT) of one layer.
+// Per-thread constants of one layer: norm gains of elements tid, tid + NT, tid + 2 NT, tid + 3 NT
+// (H <= 4 NT), and for the q/k waves the q- or k-norm gains of lanes lane, lane + 64.
 struct TkConsts {
-  float an[4], mn[4];
+  float an[4], mn[4], qk[2];
 };
 
 template <typename WT>
-__device__ __forceinline__ void tk_load_consts(TkConsts& c, const TkDesc& D, const LayerW& W) {
+__device__ __forceinline__ void tk_load_consts(TkConsts& c, const KCONST TkDesc& D, const KCONST LayerW& W) {
   const WT* an = reinterpret_cast<const WT*>(W.attn_norm);
   const WT* mn = reinterpret_cast<const WT*>(W.mlp_norm);
 #pragma unroll
@@ -195,6 +204,85 @@ __device__ __forceinline__ void tk_load_consts(TkConsts& c, const TkDesc& D, con
     const int i = threadIdx.x + k * NT;
     c.an[k] = i < D.H ? to_f32(glb(an)[i]) : 0.f;
     c.mn[k] = i < D.H ? to_f32(glb(mn)[i]) : 0.f;
+  }
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  c.qk[0] = c.qk[1] = 1.f;
+  if (wave < 3) {
+    const WT* gn = reinterpret_cast<const WT*>(wave < 2 ? W.q_norm : W.k_norm);
+    c.qk[0] = to_f32(glb(gn)[lane]);
+    c.qk[1] = to_f32(glb(gn)[lane + 64]);
+  }
+}
+
+// The back waves copy this workgroup's down-projection rows (H/32 rows of F/8 weights, the XCD's
+// columns) from HBM into S.ew with LDS-direct loads: 16-byte unit u of the block (row u / upr,
+// unit u % upr of the row, upr = F/64 units a row) lands at S.ew[8 u]; one instruction moves 64
+// consecutive units. Completion is awaited (s_waitcnt) by the issuing waves before a barrier.
+template <typename WT>
+__device__ __forceinline__ void tk_dma_e(TkSmem& S, const KCONST TkDesc& D, const KCONST LayerW& W, int g, int r) {
+  constexpr int E = WTraits<WT>::E;
+  static_assert(E == 8, "LDS-direct rows are bf16");
+  const int wave = wave_id();
+  if (wave < NF) return;
+  const int lane = threadIdx.x & 63, hper = D.H / NR, fx = D.F / NX, upr = fx / E, units = hper * upr;
+  const WT* base = reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r) * D.F + fx * g;
+  for (int j = wave - NF; 64 * j < units; j += NB) {
+    const int u = 64 * j + lane;
+    const int row = u / upr, col = u - row * upr;
+    // lanes past the last unit re-read unit 0 and land in the unused tail of S.ew (units is a
+    // multiple of 32 and at most TEW / 8, a multiple of 64)
+    const WT* src = u < units ? base + (size_t)row * D.F + col * E : base;
+    __builtin_amdgcn_global_load_lds((const GLB void*)src, (__attribute__((address_space(3))) void*)&S.ew[64 * E * j], 16, 0, 0);
+  }
+}
+
+// out[i] = dot(down row i, S.hb) for the back waves' rows i = (wave - NF) + NB * j, weights read
+// from S.ew.
+template <typename WT>
+__device__ __forceinline__ void tk_dot_e(const TkSmem& S, int hper, int fx, float* out) {
+  constexpr int E = WTraits<WT>::E;
+  constexpr int RE = THMAX / NR / NB;  // rows per back wave at most
+  const int wave = wave_id();
+  if (wave < NF) return;
+  const int lane = threadIdx.x & 63, upr = fx / E;
+  float xv[2][8];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int u = lane + 64 * k;
+#pragma unroll
+    for (int e = 0; e < 8; e += 4) {
+      const float4 f = u < upr ? *reinterpret_cast<const float4*>(S.hb + u * E + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      xv[k][e] = f.x; xv[k][e + 1] = f.y; xv[k][e + 2] = f.z; xv[k][e + 3] = f.w;
+    }
+  }
+  // groups of 4 rows: the cross-lane sums of a group overlap
+#pragma unroll 1
+  for (int j0 = 0; j0 < RE; j0 += 4) {
+    float acc[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int i = (wave - NF) + NB * (j0 + jj);
+      float s = 0.f;
+      if (i < hper) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int u = lane + 64 * k;
+          if (u < upr) {
+            float wf[8];
+            unpack(*reinterpret_cast<const u32x4*>(&S.ew[(i * upr + u) * E]), wf, (WT*)nullptr);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s = fmaf(wf[e], xv[k][e], s);
+          }
+        }
+      }
+      acc[jj] = s;
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int i = (wave - NF) + NB * (j0 + jj);
+      const float v = wave_sum(acc[jj]);
+      if (i < hper && lane == 0) out[i] = v;
+    }
   }
 }
 
@@ -219,7 +307,7 @@ __device__ __forceinline__ void tk_rmsnorm(const float* x, int n, const float* g
     }
     s = wave_sum(s);
     if (lane == 0) red[wave] = s;
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int w = 0; w < NW; ++w) tot += red[w];
   }
@@ -229,14 +317,17 @@ __device__ __forceinline__ void tk_rmsnorm(const float* x, int n, const float* g
     const int i = tid + k * NT;
     if (i < n) y[i] = x[i] * sc * gr[k];
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Attention of this XCD's two query heads over positions 0..p of KV head g, this rank's chunk of
-// positions, then the two combining exchanges; the XCD's 256 outputs land in S.ob.
+// positions, then the two combining exchanges; the XCD's 256 outputs land in S.ob. Only the front
+// waves compute; the back waves meet them at the barriers. rc, rs: RoPE factors of position p at
+// lane (q/k waves).
 template <typename WT>
-__device__ __forceinline__ bool tk_attention(const TkDesc& D, const Xch& X, const LayerW& W, int layer, int p, TkSmem& S,
-                                             uint32_t& tag, int& iring, int& apar, int g, int r) {
+__device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& X, int layer, int p, const TkConsts& cn,
+                                             float rc, float rs, TkSmem& S, uint32_t& tag, int& iring, int& apar, int g,
+                                             int r) {
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, d = D.d;
   const float* kg = D.kc + ((size_t)layer * D.ls + (size_t)g * D.cap) * d;
   const float* vg = D.vc + ((size_t)layer * D.ls + (size_t)g * D.cap) * d;
@@ -244,13 +335,11 @@ __device__ __forceinline__ bool tk_attention(const TkDesc& D, const Xch& X, cons
   if (wave < 3) {
     const float* src = S.qkv + wave * d;
     float v0 = src[lane], v1 = src[lane + 64];
-    const WT* gn = reinterpret_cast<const WT*>(wave < 2 ? W.q_norm : W.k_norm);
     const float sc = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)d + D.eps);
-    v0 *= sc * to_f32(glb(gn)[lane]);
-    v1 *= sc * to_f32(glb(gn)[lane + 64]);
-    const float c = glb(D.rope_cos)[(size_t)p * 64 + lane], s = glb(D.rope_sin)[(size_t)p * 64 + lane];
+    v0 *= sc * cn.qk[0];
+    v1 *= sc * cn.qk[1];
     float* dst = wave < 2 ? S.q[wave] : S.kp;
-    const float a = v0 * c - v1 * s, b = v1 * c + v0 * s;
+    const float a = v0 * rc - v1 * rs, b = v1 * rc + v0 * rs;
     dst[lane] = a;
     dst[lane + 64] = b;
     if (wave == 2 && r == 0) {  // append k to the cache (read by later steps only)
@@ -268,82 +357,84 @@ __device__ __forceinline__ bool tk_attention(const TkDesc& D, const Xch& X, cons
       glb(vd)[lane + 64] = v1;
     }
   }
-  __syncthreads();
-  // this rank's chunk [t0, t1) of positions 0..p; each wave takes 16 positions per pass
+  lds_barrier();
+  // this rank's chunk [t0, t1) of positions 0..p; each front wave takes 16 positions per pass
   const int n = p + 1, C = (n + NR - 1) / NR;
   const int t0 = r * C, t1 = min(t0 + C, n);
   const int tq = lane >> 2, e = lane & 3;  // lane = 4 * (position in pass) + quarter of the head dimension
   const float scale = 1.0f / sqrtf((float)d);
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, o[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-  for (int base = t0 + wave * 16; base < t1; base += NW * 16) {
-    const int t = base + tq;
-    const bool valid = t < t1;
-    const bool cur = t == p;  // the step's own k is in LDS (the cache write is for later steps)
-    const GLB f32x4* kr = reinterpret_cast<const GLB f32x4*>(glb(kg + (size_t)(valid && !cur ? t : t0) * d + 32 * e));
-    const f32x4* kl = reinterpret_cast<const f32x4*>(S.kp + 32 * e);
-    float s[2] = {0.f, 0.f};
+  if (wave < NF) {
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, o[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    for (int base = t0 + wave * 16; base < t1; base += NF * 16) {
+      const int t = base + tq;
+      const bool valid = t < t1;
+      const bool cur = t == p;  // the step's own k is in LDS (the cache write is for later steps)
+      const GLB f32x4* kr = reinterpret_cast<const GLB f32x4*>(glb(kg + (size_t)(valid && !cur ? t : t0) * d + 32 * e));
+      const f32x4* kl = reinterpret_cast<const f32x4*>(S.kp + 32 * e);
+      float s[2] = {0.f, 0.f};
 #pragma unroll 4
-    for (int i = 0; i < 8; ++i) {
-      f32x4 kv4 = kr[i];
-      if (cur) kv4 = kl[i];
+      for (int i = 0; i < 8; ++i) {
+        f32x4 kv4 = kr[i];
+        if (cur) kv4 = kl[i];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float4 q4 = *reinterpret_cast<const float4*>(&S.q[h][32 * e + 4 * i]);
+          s[h] = fmaf(q4.x, kv4.x, s[h]); s[h] = fmaf(q4.y, kv4.y, s[h]);
+          s[h] = fmaf(q4.z, kv4.z, s[h]); s[h] = fmaf(q4.w, kv4.w, s[h]);
+        }
+      }
+      float w[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const float4 q4 = *reinterpret_cast<const float4*>(&S.q[h][32 * e + 4 * i]);
-        s[h] = fmaf(q4.x, kv4.x, s[h]); s[h] = fmaf(q4.y, kv4.y, s[h]);
-        s[h] = fmaf(q4.z, kv4.z, s[h]); s[h] = fmaf(q4.w, kv4.w, s[h]);
+        s[h] += __shfl_xor(s[h], 1);
+        s[h] += __shfl_xor(s[h], 2);
+        s[h] = valid ? s[h] * scale : -INFINITY;
+        float mx = s[h];
+#pragma unroll
+        for (int q = 4; q < 64; q <<= 1) mx = fmaxf(mx, __shfl_xor(mx, q));
+        const float mn = fmaxf(m[h], mx);  // finite: the pass holds at least one valid position
+        const float corr = m[h] == -INFINITY ? 0.f : expf(m[h] - mn);
+        w[h] = valid ? expf(s[h] - mn) : 0.f;
+        float ws = w[h];
+#pragma unroll
+        for (int q = 4; q < 64; q <<= 1) ws += __shfl_xor(ws, q);
+        l[h] = l[h] * corr + ws;
+        o[h][0] *= corr;
+        o[h][1] *= corr;
+        m[h] = mn;
+      }
+      // outputs: lane owns dimensions lane, lane + 64 of both heads
+      const int npass = min(16, t1 - base);
+      for (int tt = 0; tt < npass; ++tt) {
+        const int tp = base + tt;
+        const float w0 = __shfl(w[0], 4 * tt), w1 = __shfl(w[1], 4 * tt);
+        float v0, v1;
+        if (tp == p) { v0 = S.vp[lane]; v1 = S.vp[lane + 64]; }
+        else { v0 = glb(vg)[(size_t)tp * d + lane]; v1 = glb(vg)[(size_t)tp * d + lane + 64]; }
+        o[0][0] = fmaf(w0, v0, o[0][0]); o[0][1] = fmaf(w0, v1, o[0][1]);
+        o[1][0] = fmaf(w1, v0, o[1][0]); o[1][1] = fmaf(w1, v1, o[1][1]);
       }
     }
-    float w[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      s[h] += __shfl_xor(s[h], 1);
-      s[h] += __shfl_xor(s[h], 2);
-      s[h] = valid ? s[h] * scale : -INFINITY;
-      float mx = s[h];
-#pragma unroll
-      for (int q = 4; q < 64; q <<= 1) mx = fmaxf(mx, __shfl_xor(mx, q));
-      const float mn = fmaxf(m[h], mx);  // finite: the pass holds at least one valid position
-      const float corr = m[h] == -INFINITY ? 0.f : expf(m[h] - mn);
-      w[h] = valid ? expf(s[h] - mn) : 0.f;
-      float ws = w[h];
-#pragma unroll
-      for (int q = 4; q < 64; q <<= 1) ws += __shfl_xor(ws, q);
-      l[h] = l[h] * corr + ws;
-      o[h][0] *= corr;
-      o[h][1] *= corr;
-      m[h] = mn;
-    }
-    // outputs: lane owns dimensions lane, lane + 64 of both heads
-    const int npass = min(16, t1 - base);
-    for (int tt = 0; tt < npass; ++tt) {
-      const int tp = base + tt;
-      const float w0 = __shfl(w[0], 4 * tt), w1 = __shfl(w[1], 4 * tt);
-      float v0, v1;
-      if (tp == p) { v0 = S.vp[lane]; v1 = S.vp[lane + 64]; }
-      else { v0 = glb(vg)[(size_t)tp * d + lane]; v1 = glb(vg)[(size_t)tp * d + lane + 64]; }
-      o[0][0] = fmaf(w0, v0, o[0][0]); o[0][1] = fmaf(w0, v1, o[0][1]);
-      o[1][0] = fmaf(w1, v0, o[1][0]); o[1][1] = fmaf(w1, v1, o[1][1]);
+      if (lane == 0) { S.wm[wave][h] = m[h]; S.wl[wave][h] = l[h]; }
+      S.wo[wave][h][lane] = o[h][0];
+      S.wo[wave][h][lane + 64] = o[h][1];
     }
   }
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (lane == 0) { S.wm[wave][h] = m[h]; S.wl[wave][h] = l[h]; }
-    S.wo[wave][h][lane] = o[h][0];
-    S.wo[wave][h][lane + 64] = o[h][1];
-  }
-  __syncthreads();
-  // this rank's partial: combine the waves; publish (max, sum, 128 outputs) per head
+  lds_barrier();
+  // this rank's partial: combine the front waves; publish (max, sum, 128 outputs) per head
   ++tag;
   u64* slot = D.att + (((size_t)g * 2 + (apar & 1)) * NR + r) * ATS;
   if (tid < 256) {
     const int h = tid >> 7, i = tid & 127;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, S.wm[w][h]);
+    for (int w = 0; w < NF; ++w) mx = fmaxf(mx, S.wm[w][h]);
     float ls = 0.f, os = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
+      for (int w = 0; w < NF; ++w) {
         const float f = S.wm[w][h] == -INFINITY ? 0.f : expf(S.wm[w][h] - mx);
         ls += S.wl[w][h] * f;
         os += S.wo[w][h][i] * f;
@@ -358,13 +449,13 @@ __device__ __forceinline__ bool tk_attention(const TkDesc& D, const Xch& X, cons
   // rank r combines outputs [8 * (r % 16), +8) of head r / 16 from the 32 ranks' partials
   const int hb = r >> 4, db = 8 * (r & 15);
   const u64* base = D.att + ((size_t)g * 2 + (apar & 1)) * NR * ATS;
-  if (!get_at<1>(NR * 10, tag, S.cmb, X.err, [&](int i) -> const u64* {
+  if (!get_at<(NR * 10 + PF - 1) / PF, PF>(NR * 10, tag, S.cmb, X.err, [&](int i) -> const u64* {
         const int s = i / 10, k = i % 10;
         return base + (size_t)s * ATS + hb * 130 + (k < 2 ? k : 2 + db + (k - 2));
       }))
     return false;
   ++apar;
-  if (!slice_gather<1, 1>(X, 8, 256, [&](int k, int) {
+  if (!slice_gather<1, 1, PF>(X, 8, 256, [&](int k, int) {
         float mx = -INFINITY;
         for (int s2 = 0; s2 < NR; ++s2) mx = fmaxf(mx, S.cmb[s2 * 10]);
         float ls = 0.f, os = 0.f;
@@ -380,13 +471,18 @@ __device__ __forceinline__ bool tk_attention(const TkDesc& D, const Xch& X, cons
   return true;
 }
 
+// Wait until every load this wave issued has landed (the LDS-direct rows included).
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
 template <typename WT>
 __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
-  const TkDesc& D = *C.desc;
+  const KCONST TkDesc& D = *(const KCONST TkDesc*)C.desc;
   __shared__ TkSmem S;
   const Xch X{D.xin, D.xcr, D.err};
-  constexpr int KT = (THMAX + NR + NT - 1) / NT;  // intra gather of a residual row + sums of squares
-  const int g = blockIdx.x % NX, r = blockIdx.x / NX, tid = threadIdx.x;
+  constexpr int KT = (THMAX + NR + PF - 1) / PF;  // intra gather of a residual row + sums of squares
+  constexpr int KQ = (512 + PF - 1) / PF;         // intra gather of the q/k/v slices
+  constexpr int KH = (TFXMAX + PF - 1) / PF;      // intra gather of the SwiGLU slices
+  const int g = blockIdx.x % NX, r = blockIdx.x / NX, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int H = D.H, d = D.d, G = D.nq / D.nkv;
   const int qrows = (G + 2) * d, qper = qrows / NR, hper = H / NR, fx = D.F / NX, fper = fx / NR;
   TkConsts c;
@@ -396,62 +492,89 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   tk_issue_a<WT>(X1, D, D.layer[0], 1, g, r);
   uint32_t tag = glb(D.st)->epoch;
   const int p = glb(D.st)->pos;
+  float rc = 1.f, rs = 0.f;  // RoPE factors of position p (the same in every layer)
+  if (wave < 3) {
+    rc = glb(D.rope_cos)[(size_t)p * 64 + lane];
+    rs = glb(D.rope_sin)[(size_t)p * 64 + lane];
+  }
   int iring = 0, cpar = 0, apar = 0;
   for (int i = tid; i < H; i += NT) S.xs[i] = glb(D.x_in)[i];
-  __syncthreads();
+  lds_barrier();
   bool ok = true;
-  const int qh = qper / 2, hh = hper / 2, nd = 2 * fper;  // rows of A0/A1, E0/E1; gate + up rows
+  const int qh = qper / 2, hh = hper / 2, nd = 2 * fper;  // rows of A0/A1, C0/C1; gate + up rows
   for (int l = 0; ok && l < D.n_layers; ++l) {
-    const LayerW& W = D.layer[l];
+    const KCONST LayerW& W = D.layer[l];
     const bool last = l + 1 == D.n_layers;
-    // q/k/v slice (A0: X0, A1: X1)
+    // q/k/v slice (A0: X0, A1: X1); the output projection rows (C0, C1) follow in their place and
+    // the down rows go to LDS
     tk_rmsnorm(S.xs, H, c.an, D.eps, S.xn, S.red, l > 0 ? S.xs + H : nullptr);
-    wb_dot<WT, 1, 4>(X0, qh, H, S.xn, S.out);
-    tk_issue_c<WT>(X0, D, W, g, r);
-    wb_dot<WT, 1, 4>(X1, qh, H, S.xn, S.out + qh);
-    __syncthreads();
-    if (!slice_gather<1, 1>(X, qper, qrows, [&](int e, int) { return S.out[e]; }, S.qkv, tag, iring, g, r,
-                            [&] { tk_issue_d<WT>(X1, D, W, 0, g, r); })) { ok = false; break; }
-    if (!tk_attention<WT>(D, X, W, l, p, S, tag, iring, apar, g, r)) { ok = false; break; }
-    // output projection partial (C: X0), residual
-    wb_dot<WT, 8, 1>(X0, hper, G * d, S.ob, S.out);
-    __syncthreads();
-    if (!reduce_gather<1, THMAX, KT>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r,
-                                     [&] { tk_issue_d<WT>(X0, D, W, 1, g, r); })) { ok = false; break; }
-    // gate and up rows (D0: X1, D1: X0, D2: X1), SwiGLU
+    wb_dot<WT, 2, 4>(X0, qh, H, S.xn, S.out);
+    tk_issue_c<WT>(X0, D, W, 0, g, r);
+    wb_dot<WT, 2, 4>(X1, qh, H, S.xn, S.out + qh);
+    tk_issue_c<WT>(X1, D, W, 1, g, r);
+    tk_dma_e<WT>(S, D, W, g, r);
+    lds_barrier();
+    if (!slice_gather<1, KQ, PF>(X, qper, qrows, [&](int e, int) { return S.out[e]; }, S.qkv, tag, iring, g, r, [] {})) {
+      ok = false;
+      break;
+    }
+    if (!tk_attention<WT>(D, X, l, p, c, rc, rs, S, tag, iring, apar, g, r)) { ok = false; break; }
+    // output projection partial (C0: X0, C1: X1), residual; gate/up chunks 0, 1 follow
+    wb_dot<WT, 8, 1>(X0, hh, G * d, S.ob, S.out);
+    tk_issue_d<WT>(X0, D, W, 0, g, r);
+    wb_dot<WT, 8, 1>(X1, hh, G * d, S.ob, S.out + hh);
+    tk_issue_d<WT>(X1, D, W, 1, g, r);
+    lds_barrier();
+    if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [] {})) {
+      ok = false;
+      break;
+    }
+    // gate and up rows (even chunks in X0, odd in X1), SwiGLU; then the next layer's q/k/v rows
+    // (or the semantic head) follow while the down rows are read from LDS
     tk_rmsnorm(S.xs, H, c.mn, D.eps, S.xn, S.red, S.xs + H);
-    wb_dot<WT, 2, 4>(X1, min(16, nd), H, S.xn, S.out);
-    tk_issue_d<WT>(X1, D, W, 2, g, r);
-    wb_dot<WT, 2, 4>(X0, min(16, max(0, nd - 16)), H, S.xn, S.out + 16);
-    tk_issue_e<WT>(X0, D, W, 0, g, r);
-    wb_dot<WT, 2, 4>(X1, min(16, max(0, nd - 32)), H, S.xn, S.out + 32);
-    __syncthreads();
-    if (!slice_gather<1, 2>(X, fper, fx, [&](int e, int) { return silu(S.out[e]) * S.out[fper + e]; }, S.hb, tag, iring, g, r,
-                            [&] { tk_issue_e<WT>(X1, D, W, 1, g, r); })) { ok = false; break; }
-    // down projection partial (E0: X0, E1: X1), residual
-    wb_dot<WT, 4, 2>(X0, hh, fx, S.hb, S.out);
     if (!last) {
       tk_load_consts<WT>(c, D, D.layer[l + 1]);
-      tk_issue_a<WT>(X0, D, D.layer[l + 1], 0, g, r);
     } else {
-      tk_issue_f<WT>(X0, D);
+      const WT* f = reinterpret_cast<const WT*>(D.final_norm);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) c.an[k] = tid + k * NT < H ? to_f32(glb(f)[tid + k * NT]) : 0.f;
     }
-    wb_dot<WT, 4, 2>(X1, hh, fx, S.hb, S.out + hh);
-    __syncthreads();
-    if (!reduce_gather<1, THMAX, KT>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] {
-          if (!last) tk_issue_a<WT>(X1, D, D.layer[l + 1], 1, g, r);
-        })) { ok = false; break; }
+#pragma unroll 1
+    for (int cc = 0; cc < 6; cc += 2) {
+      wb_dot<WT, 2, 4>(X0, tk_d_rows(nd, cc), H, S.xn, S.out + 8 * cc);
+      if (cc + 2 < 6) tk_issue_d<WT>(X0, D, W, cc + 2, g, r);
+      wb_dot<WT, 2, 4>(X1, tk_d_rows(nd, cc + 1), H, S.xn, S.out + 8 * (cc + 1));
+      if (cc + 3 < 6) tk_issue_d<WT>(X1, D, W, cc + 3, g, r);
+    }
+    if (wave >= NF) wait_loads();  // the down rows are in LDS (seen by all after the barrier)
+    if (!last) {
+      tk_issue_a<WT>(X0, D, D.layer[l + 1], 0, g, r);
+      tk_issue_a<WT>(X1, D, D.layer[l + 1], 1, g, r);
+    } else {
+      tk_issue_f<WT>(X0, D, 0);
+      tk_issue_f<WT>(X1, D, 1);
+    }
+    lds_barrier();
+    if (!slice_gather<1, KH, PF>(X, fper, fx, [&](int e, int) { return silu(S.out[e]) * S.out[fper + e]; }, S.hb, tag,
+                                 iring, g, r, [] {})) {
+      ok = false;
+      break;
+    }
+    // down projection partial from LDS, residual
+    tk_dot_e<WT>(S, hper, fx, S.out);
+    lds_barrier();
+    if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [] {})) {
+      ok = false;
+      break;
+    }
   }
   if (ok) {
-    // final norm, semantic head slice (X0: F)
-    float fg[4];
-    const WT* f = reinterpret_cast<const WT*>(D.final_norm);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) fg[k] = tid + k * NT < H ? to_f32(glb(f)[tid + k * NT]) : 0.f;
-    tk_rmsnorm(S.xs, H, fg, D.eps, S.xn, S.red, S.xs + H);
+    // final norm (gains in c.an), semantic head slice (F0: X0, F1: X1)
+    tk_rmsnorm(S.xs, H, c.an, D.eps, S.xn, S.red, S.xs + H);
     const int vper = D.V / NWG;
-    wb_dot<WT, 2, 4>(X0, vper, H, S.xn, S.out);
-    __syncthreads();
+    wb_dot<WT, 2, 4>(X0, min(8, vper), H, S.xn, S.out);
+    wb_dot<WT, 2, 4>(X1, max(0, vper - 8), H, S.xn, S.out + 8);
+    lds_barrier();
     for (int i = tid; i < vper; i += NT) glb(D.logits)[vper * blockIdx.x + i] = S.out[i];
     if (blockIdx.x == 0)
       for (int i = tid; i < H; i += NT) glb(D.hT)[i] = S.xn[i];

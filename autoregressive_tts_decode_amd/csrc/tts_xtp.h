@@ -87,6 +87,14 @@ struct CpCall {
 
 // Wave index as a wave-uniform (scalar) value, so row addresses derived from it stay scalar.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// threadIdx.x behind an empty asm statement: what is computed from it is recomputed where it is
+// used instead of being hoisted out of the layer loop (hoisted per-thread offsets of every
+// exchange would stay live in registers across the whole loop).
+__device__ __forceinline__ int fresh_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 __device__ __forceinline__ u64 pack(float v, uint32_t tag) { return ((u64)tag << 32) | __float_as_uint(v); }
 __device__ __forceinline__ uint32_t tagof(u64 v) { return (uint32_t)(v >> 32); }
@@ -96,6 +104,12 @@ __device__ __forceinline__ float valof(u64 v) { return __uint_as_float((uint32_t
 // counter: each LDS wait before a barrier would then wait for all weight rows in flight. All
 // global accesses therefore go through explicitly global (address space 1) pointers.
 #define GLB __attribute__((address_space(1)))
+// Descriptors (weight pointers, shapes) sit in device memory that the host fills before a launch
+// and no kernel writes. Read through the constant address space, they load with scalar
+// instructions, which do not count against the vector-load counter: a descriptor read then never
+// waits for the weight rows in flight (a generic read would be a vector load, and its wait would
+// drain every load issued before it).
+#define KCONST __attribute__((address_space(4)))
 template <typename T>
 __device__ __forceinline__ GLB T* glb(T* p) { return (GLB T*)p; }
 template <typename T>
@@ -103,6 +117,27 @@ __device__ __forceinline__ const GLB T* glb(const T* p) { return (const GLB T*)p
 
 __device__ __forceinline__ void st_c(u64* p, u64 v) { __hip_atomic_store(glb(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 __device__ __forceinline__ u64 ld_c(const u64* p) { return __hip_atomic_load(glb(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Workgroup barrier for LDS data: waits for this wave's LDS accesses, then meets the other waves.
+// It is no memory-model fence, so vector loads in flight (weight rows, LDS-direct copies) are not
+// waited for; a __syncthreads fence drains them whenever an LDS-direct copy is pending. The memory
+// clobber keeps the compiler from moving memory accesses across it. Waves that read data another
+// wave copied into LDS with LDS-direct loads need that wave to wait for its loads first.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// lds_barrier that also returns whether any thread passed fail = true. Each wave posts one vote,
+// (tag << 1) | any-fail, in its own slot; a slot holding a later call's tag belongs to a wave that
+// went on, which it does only when it saw no failure, so only this call's failing votes count.
+__device__ __forceinline__ bool barrier_any(bool fail, uint32_t tag) {
+  __shared__ uint32_t votes[NW];
+  const uint32_t mine = (tag << 1) | (__any(fail) ? 1u : 0u);
+  if ((threadIdx.x & 63) == 0) votes[wave_id()] = mine;
+  lds_barrier();
+  bool any = false;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) any |= votes[w] == ((tag << 1) | 1u);
+  return any;
+}
 
 // Gather n tagged entries, entry i read from at(i), into lds[0 .. n), polling until every entry
 // carries tag; an entry already received is not read again. Each wave polls its own entries
@@ -114,22 +149,23 @@ __device__ __forceinline__ u64 ld_c(const u64* p) { return __hip_atomic_load(glb
 // weight loads). n <= KMAX * NPOLL.
 template <int KMAX, int NPOLL = NT, typename At>
 __device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t* err, At at) {
+  const int tid = fresh_tid();
   unsigned pend = 0;
-  if (NPOLL == NT || threadIdx.x < NPOLL) {
+  if (NPOLL == NT || tid < NPOLL) {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-      if (threadIdx.x + k * NPOLL < n) pend |= 1u << k;
+      if (tid + k * NPOLL < n) pend |= 1u << k;
   }
   bool fail = false;
-  for (long long s = 0; NPOLL == NT || threadIdx.x < NPOLL; ++s) {
+  for (long long s = 0; NPOLL == NT || tid < NPOLL; ++s) {
     u64 v[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-      if (pend & (1u << k)) v[k] = ld_c(at(threadIdx.x + k * NPOLL));
+      if (pend & (1u << k)) v[k] = ld_c(at(tid + k * NPOLL));
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
       if ((pend & (1u << k)) && tagof(v[k]) == tag) {
-        lds[threadIdx.x + k * NPOLL] = valof(v[k]);
+        lds[tid + k * NPOLL] = valof(v[k]);
         pend &= ~(1u << k);
       }
     if (!__any(pend != 0)) break;
@@ -141,8 +177,8 @@ __device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t
       }
     }
   }
-  if (__syncthreads_or(fail)) {
-    if (threadIdx.x == 0) __hip_atomic_fetch_or(glb(err), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (barrier_any(fail, tag)) {
+    if (tid == 0) __hip_atomic_fetch_or(glb(err), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return false;
   }
   return true;
@@ -267,7 +303,7 @@ using RowsB = Rows<WT, RB_R, RB_K>;
 
 // q/k/v rows [qper*r, +qper) of this XCD's (G q heads | k | v)
 template <typename WT>
-__device__ __forceinline__ void issue_qkv(RowsA<WT>& R, const CpDesc& D, const LayerW& W, int g, int r) {
+__device__ __forceinline__ void issue_qkv(RowsA<WT>& R, const KCONST CpDesc& D, const KCONST LayerW& W, int g, int r) {
   const int H = D.H, d = D.d, G = D.nq / D.nkv, qper = (G + 2) * d / NR;
   rows_issue(R, qper, H, [&](int i) -> const WT* {
     const int q = qper * r + i;
@@ -278,7 +314,7 @@ __device__ __forceinline__ void issue_qkv(RowsA<WT>& R, const CpDesc& D, const L
 }
 // output projection rows [hper*r, +hper), columns of this XCD's heads
 template <typename WT>
-__device__ __forceinline__ void issue_o(RowsB<WT>& R, const CpDesc& D, const LayerW& W, int g, int r) {
+__device__ __forceinline__ void issue_o(RowsB<WT>& R, const KCONST CpDesc& D, const KCONST LayerW& W, int g, int r) {
   const int hper = D.H / NR, Gd = D.nq / D.nkv * D.d;
   rows_issue(R, hper, Gd, [&](int i) -> const WT* {
     return reinterpret_cast<const WT*>(W.wo) + (size_t)(hper * r + i) * (D.nq * D.d) + Gd * g;
@@ -286,7 +322,7 @@ __device__ __forceinline__ void issue_o(RowsB<WT>& R, const CpDesc& D, const Lay
 }
 // gate rows then up rows [fper*r, +fper) of this XCD's FFN slice
 template <typename WT>
-__device__ __forceinline__ void issue_gu(RowsA<WT>& R, const CpDesc& D, const LayerW& W, int g, int r) {
+__device__ __forceinline__ void issue_gu(RowsA<WT>& R, const KCONST CpDesc& D, const KCONST LayerW& W, int g, int r) {
   const int fx = D.F / NX, fper = fx / NR;
   rows_issue(R, 2 * fper, D.H, [&](int i) -> const WT* {
     const int f = fx * g + fper * r + (i % fper);
@@ -295,7 +331,7 @@ __device__ __forceinline__ void issue_gu(RowsA<WT>& R, const CpDesc& D, const La
 }
 // down projection rows [hper*r, +hper), columns of this XCD's FFN slice
 template <typename WT>
-__device__ __forceinline__ void issue_down(RowsB<WT>& R, const CpDesc& D, const LayerW& W, int g, int r) {
+__device__ __forceinline__ void issue_down(RowsB<WT>& R, const KCONST CpDesc& D, const KCONST LayerW& W, int g, int r) {
   const int hper = D.H / NR, fx = D.F / NX;
   rows_issue(R, hper, fx, [&](int i) -> const WT* {
     return reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r + i) * D.F + fx * g;
@@ -303,14 +339,14 @@ __device__ __forceinline__ void issue_down(RowsB<WT>& R, const CpDesc& D, const 
 }
 // head j rows [vper*blockIdx, +vper)
 template <typename WT>
-__device__ __forceinline__ void issue_head(RowsA<WT>& R, const CpDesc& D, int j) {
+__device__ __forceinline__ void issue_head(RowsA<WT>& R, const KCONST CpDesc& D, int j) {
   const int vper = D.V / NWG;
   const WT* head = reinterpret_cast<const WT*>(D.heads) + (size_t)(j - 1) * D.V * D.H;
   rows_issue(R, vper, D.H, [&](int i) -> const WT* { return head + (size_t)(vper * blockIdx.x + i) * D.H; }, false);
 }
 // input projection rows (K split: XCD g takes columns [Ht/8 * g, +Ht/8), rank r rows [hper*r, +hper))
 template <typename WT>
-__device__ __forceinline__ void issue_proj(RowsB<WT>& R, const CpDesc& D, int g, int r) {
+__device__ __forceinline__ void issue_proj(RowsB<WT>& R, const KCONST CpDesc& D, int g, int r) {
   const int kx = D.Ht / NX, hper = D.H / NR;
   rows_issue(R, hper, kx, [&](int i) -> const WT* {
     return reinterpret_cast<const WT*>(D.proj) + (size_t)(hper * r + i) * D.Ht + kx * g;
@@ -332,7 +368,7 @@ __device__ __forceinline__ void issue_proj(RowsB<WT>& R, const CpDesc& D, int g,
 template <int M, int HMX, int KMAX, int NPOLL = NT, typename AfterPut>
 __device__ __forceinline__ bool reduce_gather(const Xch& X, const float* out, float* xs, float* xn, int H, bool residual,
                                               uint32_t& tag, int& iring, int& cpar, int g, int r, AfterPut after_put) {
-  const int tid = threadIdx.x, hper = H / NR;
+  const int tid = fresh_tid(), hper = H / NR;
   ++tag;
   u64* mine = X.xcr + ((size_t)blockIdx.x * 2 + (cpar & 1)) * CSZ;
   for (int i = tid; i < hper * M; i += NT) st_c(mine + (i % M) * 64 + i / M, pack(out[i], tag));
@@ -367,7 +403,7 @@ __device__ __forceinline__ bool reduce_gather(const Xch& X, const float* out, fl
       if (tid == 0) st_c(buf + M * H + mm * NR + r, pack(ss, tag));
     }
   }
-  __syncthreads();  // the gather below overwrites the residual rows read above
+  lds_barrier();  // the gather below overwrites the residual rows read above
   return get_flat<KMAX, NPOLL>(buf, M * (H + NR), tag, xs, X.err);
 }
 
@@ -378,7 +414,7 @@ __device__ __forceinline__ bool slice_gather(const Xch& X, int n, int w, ValFn v
                                              int g, int r, AfterPut after_put) {
   ++tag;
   u64* buf = X.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
-  for (int i = threadIdx.x; i < n * M; i += NT) {
+  for (int i = fresh_tid(); i < n * M; i += NT) {
     const int e = i / M, m = i % M;
     st_c(buf + m * w + n * r + e, pack(vals(e, m), tag));
   }
@@ -397,7 +433,7 @@ struct LayerConsts {
 };
 
 template <typename WT, int M>
-__device__ __forceinline__ void load_consts(LayerConsts& c, const CpDesc& D, const LayerW& W, int p0) {
+__device__ __forceinline__ void load_consts(LayerConsts& c, const KCONST CpDesc& D, const KCONST LayerW& W, int p0) {
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, G = D.nq / D.nkv;
   const WT* an = reinterpret_cast<const WT*>(W.attn_norm);
   const WT* mn = reinterpret_cast<const WT*>(W.mlp_norm);
@@ -455,7 +491,7 @@ __device__ __forceinline__ void rmsnorm_reg(const float* x, int n, const float* 
       s = wave_sum(s);
       if (lane == 0) red[m * NW + wave] = s;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       float s = 0.f;
@@ -473,7 +509,7 @@ __device__ __forceinline__ void rmsnorm_reg(const float* x, int n, const float* 
       if (i < n) y[m * n + i] = x[m * n + i] * sc * gr[k];
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // ---------------------------------------------------------------------------- the layer
@@ -485,10 +521,10 @@ __device__ __forceinline__ void rmsnorm_reg(const float* x, int n, const float* 
 // projection) and c the next layer's constants. have_ss: S.xs carries the per-rank sums of squares
 // of the input rows (it does unless the rows were staged without an exchange).
 template <typename WT, int M>
-__device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int layer, int j, int p0, bool have_ss, Smem& S,
+__device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C, int layer, int j, int p0, bool have_ss, Smem& S,
                                          RowsB<WT>& R0, RowsA<WT>& R1, LayerConsts& c, uint32_t& tag, int& iring, int& cpar,
                                          int g, int r) {
-  const LayerW& W = D.layer[layer];
+  const KCONST LayerW& W = D.layer[layer];
   const int H = D.H, d = D.d, G = D.nq / D.nkv;
   const int qrows = (G + 2) * d;          // q/k/v rows owned by one XCD
   const int qper = qrows / NR;            // rows per rank
@@ -502,7 +538,7 @@ __device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int l
   // --- q/k/v slice (R1)
   rmsnorm_reg<M>(S.xs, H, c.an, D.eps, S.xn, S.red, have_ss ? S.xs + M * H : nullptr);
   rows_dot<WT, M>(R1, qper, H, S.xn, H, S.out);
-  __syncthreads();
+  lds_barrier();
   if (!slice_gather<M, M>(X, qper, qrows, [&](int e, int m) { return S.out[e * M + m]; }, S.qkv, tag, iring, g, r,
                           [&] { issue_gu(R1, D, W, g, r); }))
     return false;
@@ -571,17 +607,17 @@ __device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int l
     S.ob[m * G * d + h * d + lane] = o0 / l;
     S.ob[m * G * d + h * d + lane + 64] = o1 / l;
   }
-  __syncthreads();
+  lds_barrier();
 
   // --- output projection partial (R0: rows [hper*r, +hper), this XCD's head columns), residual
   rows_dot<WT, M>(R0, hper, G * d, S.ob, G * d, S.out);
-  __syncthreads();
+  lds_barrier();
   if (!reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] { issue_down(R0, D, W, g, r); })) return false;
 
   // --- gate/up slice (R1) + SwiGLU
   rmsnorm_reg<M>(S.xs, H, c.mn, D.eps, S.xn, S.red, S.xs + M * H);
   rows_dot<WT, M>(R1, 2 * fper, H, S.xn, H, S.out);
-  __syncthreads();
+  lds_barrier();
   if (!slice_gather<M, M>(X, fper, fx, [&](int e, int m) { return silu(S.out[e * M + m]) * S.out[(fper + e) * M + m]; }, S.hb,
                           tag, iring, g, r, [&] {
                             if (!last) {
@@ -595,7 +631,7 @@ __device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int l
 
   // --- down projection partial (R0: rows [hper*r, +hper), this XCD's FFN columns), residual
   rows_dot<WT, M>(R0, hper, fx, S.hb, fx, S.out);
-  __syncthreads();
+  lds_barrier();
   return reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] {
     if (!last) issue_o(R0, D, D.layer[layer + 1], g, r);
     else if (j < D.n_ac && D.proj) issue_proj(R0, D, g, r);
@@ -605,7 +641,7 @@ __device__ __forceinline__ bool cp_layer(const CpDesc& D, const CpCall& C, int l
 // Argmax over the head rows: each workgroup holds nrows logits of rows [row0, row0 + nrows) in
 // S.out (M = 1). Every workgroup publishes its best (value, id) and reads all NWG candidates.
 // Ties go to the lower id. Returns the id (or -1 on failure).
-__device__ __forceinline__ int argmax_exchange(const CpDesc& D, Smem& S, int nrows, int row0, uint32_t& tag, int& apar) {
+__device__ __forceinline__ int argmax_exchange(const KCONST CpDesc& D, Smem& S, int nrows, int row0, uint32_t& tag, int& apar) {
   const int tid = threadIdx.x;
   ++tag;
   u64* cb = D.cand + (size_t)(apar & 1) * NWG * CAND;
@@ -631,7 +667,7 @@ __device__ __forceinline__ int argmax_exchange(const CpDesc& D, Smem& S, int nro
     }
     if ((tid & 63) == 0) { S.red[tid >> 6] = v; S.red[8 + (tid >> 6)] = __int_as_float(id); }
   }
-  __syncthreads();
+  lds_barrier();
   if (tid == 0) {
     float bv = S.red[0];
     int bi = __float_as_int(S.red[8]);
@@ -642,7 +678,7 @@ __device__ __forceinline__ int argmax_exchange(const CpDesc& D, Smem& S, int nro
     }
     best = bi;
   }
-  __syncthreads();
+  lds_barrier();
   return best;
 }
 
@@ -650,7 +686,7 @@ __device__ __forceinline__ int argmax_exchange(const CpDesc& D, Smem& S, int nro
 // input projection's rows (when the model has one), R1 layer 0's q/k/v rows and c layer 0's
 // constants; on exit they hold the next step's.
 template <typename WT, int M>
-__device__ __forceinline__ bool cp_step(const CpDesc& D, const CpCall& C, int j, int& tok, Smem& S, RowsB<WT>& R0,
+__device__ __forceinline__ bool cp_step(const KCONST CpDesc& D, const CpCall& C, int j, int& tok, Smem& S, RowsB<WT>& R0,
                                         RowsA<WT>& R1, LayerConsts& c, const float* fn, uint32_t& tag, int& iring, int& cpar,
                                         int& apar, int frame, int g, int r) {
   const int H = D.H, Ht = D.Ht, V = D.V, tid = threadIdx.x;
@@ -669,9 +705,9 @@ __device__ __forceinline__ bool cp_step(const CpDesc& D, const CpCall& C, int j,
         S.xn[i] = to_f32(glb(erow)[kx * g + i]);
       }
     }
-    __syncthreads();
+    lds_barrier();
     rows_dot<WT, M>(R0, hper, kx, S.xn, kx, S.out);
-    __syncthreads();
+    lds_barrier();
     if (!reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, false, tag, iring, cpar, g, r, [&] { issue_o(R0, D, D.layer[0], g, r); }))
       return false;
   } else {
@@ -684,7 +720,7 @@ __device__ __forceinline__ bool cp_step(const CpDesc& D, const CpCall& C, int j,
         S.xs[i] = to_f32(glb(erow)[i]);
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   const int p0 = (j == 1) ? 0 : j;
   for (int l = 0; l < D.n_layers; ++l)
@@ -693,7 +729,7 @@ __device__ __forceinline__ bool cp_step(const CpDesc& D, const CpCall& C, int j,
   const int vper = V / NWG;
   rmsnorm_reg<1>(S.xs + (M - 1) * H, H, fn, D.eps, S.xn, S.red, S.xs + M * H + (M - 1) * NR);
   rows_dot<WT, 1>(R1, vper, H, S.xn, H, S.out);
-  __syncthreads();
+  lds_barrier();
   if (j < D.n_ac) {
     load_consts<WT, 1>(c, D, D.layer[0], j + 1);
     issue_qkv(R1, D, D.layer[0], g, r);
@@ -711,7 +747,7 @@ __device__ __forceinline__ bool cp_step(const CpDesc& D, const CpCall& C, int j,
 
 template <typename WT>
 __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
-  const CpDesc& D = *C.desc;
+  const KCONST CpDesc& D = *(const KCONST CpDesc*)C.desc;
   __shared__ Smem S;
   const int g = blockIdx.x % NX, r = blockIdx.x / NX;
   // constants first (they are needed first), then the first two weight phases

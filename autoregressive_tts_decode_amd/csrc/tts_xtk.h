@@ -58,7 +58,7 @@ struct TkCall {
 constexpr int NF = 4;                        // front waves
 constexpr int NB = NW - NF;                  // back waves
 constexpr int PF = NF * 64;                  // polling threads
-constexpr int TEW = (THMAX / NR) * TFXMAX;   // down-projection rows of a workgroup (elements)
+constexpr int TLW = 65536;                   // LDS weight rows of a workgroup (bf16 elements, 128 KB)
 
 // One weight chunk in the back waves' registers: rows (wave - NF) + NB * j (j < RR) of the chunk,
 // 16-byte units lane + 64 * k (k < KK) of each row, RR * KK <= WB.
@@ -130,13 +130,16 @@ __device__ __forceinline__ void wb_dot(const WBuf& B, int nrows, int ncols, cons
   }
 }
 
-// The chunks of a layer (rows per back wave RR x 16-byte units per lane KK), for H <= 2048,
-// F / 8 <= 768, 8 KV heads of dimension 128 and 2 query heads per KV head:
-//   A0, A1  q/k/v slice rows [0, 8) and [8, 16) x H               -> 2 x 4
-//   C0, C1  output projection: halves of the H/32 rows x 256       -> 8 x 1
-//   D0..D5  gate rows then up rows (2 F/256 in all) x H, 8 a chunk -> 2 x 4
-//   down    H/32 rows x F/8, copied into LDS (not registers) while the attention runs
-// and after the last layer F0, F1, the semantic head: V/256 <= 16 rows x H, 8 a chunk -> 2 x 4.
+// The weight rows of a layer, per workgroup, for H <= 2048, F / 8 <= 768, 8 KV heads of dimension
+// 128 and 2 query heads per KV head. Register chunks (rows per back wave RR x 16-byte units per
+// lane KK) and LDS blocks:
+//   A0, A1   q/k/v slice rows [0, 8) and [8, 16) x H                          regs 2 x 4
+//   C0, C1   output projection: halves of the H/32 rows x 256                  regs 8 x 1
+//   DL       the first nL = min(2 F/256, TLW / H) gate/up rows (gate rows
+//            first, then up rows) x H                                          LDS, during attention
+//   D0, D1   the remaining gate/up rows, 8 a chunk                             regs 2 x 4
+//   E        down projection: H/32 rows x F/8                                  LDS, after DL is read
+// and after the last layer F0, F1, the semantic head: V/256 <= 16 rows x H, 8 a chunk -> regs 2 x 4.
 template <typename WT>
 __device__ __forceinline__ void tk_issue_a(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int half, int g, int r) {
   const int H = D.H, d = D.d, G = D.nq / D.nkv, qper = (G + 2) * d / NR;
@@ -154,16 +157,20 @@ __device__ __forceinline__ void tk_issue_c(WBuf& B, const KCONST TkDesc& D, cons
     return reinterpret_cast<const WT*>(W.wo) + (size_t)(hper * r + hh * half + i) * (D.nq * D.d) + Gd * g;
   });
 }
-// rows of chunk c of the rank's gate rows (0 .. fper) followed by its up rows (fper .. 2 fper)
-__device__ __forceinline__ int tk_d_rows(int nd, int c) { return min(8, max(0, nd - 8 * c)); }
+// gate/up row q of the rank: gate rows 0 .. fper, then up rows fper .. 2 fper
 template <typename WT>
-__device__ __forceinline__ void tk_issue_d(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int c, int g, int r) {
+__device__ __forceinline__ const WT* tk_gu_row(const KCONST TkDesc& D, const KCONST LayerW& W, int q, int g, int r) {
   const int fx = D.F / NX, fper = fx / NR;
-  wb_issue<WT, 2, 4>(B, tk_d_rows(2 * fper, c), D.H, [&](int i) -> const WT* {
-    const int q = 8 * c + i;
-    const int f = fx * g + fper * r + (q < fper ? q : q - fper);
-    return reinterpret_cast<const WT*>(q < fper ? W.wg : W.wu) + (size_t)f * D.H;
-  });
+  const int f = fx * g + fper * r + (q < fper ? q : q - fper);
+  return reinterpret_cast<const WT*>(q < fper ? W.wg : W.wu) + (size_t)f * D.H;
+}
+// register chunk c (8 rows) of the gate/up rows past the nl rows held in LDS
+template <typename WT>
+__device__ __forceinline__ void tk_issue_d(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int nl, int c, int g,
+                                           int r) {
+  const int nd = 2 * (D.F / NX / NR);
+  wb_issue<WT, 2, 4>(B, min(8, max(0, nd - nl - 8 * c)), D.H,
+                     [&](int i) -> const WT* { return tk_gu_row<WT>(D, W, nl + 8 * c + i, g, r); });
 }
 template <typename WT>
 __device__ __forceinline__ void tk_issue_f(WBuf& B, const KCONST TkDesc& D, int half) {
@@ -186,7 +193,7 @@ struct TkSmem {
   float hb[TFXMAX];           // SwiGLU slice of the XCD
   float out[128];             // row results of this workgroup
   float red[64];
-  __align__(16) uint16_t ew[TEW];  // down-projection rows [H/32][F/8] of this workgroup
+  __align__(16) uint16_t lw[TLW];  // weight rows copied by LDS-direct loads (gate/up rows, then down rows)
 };
 
 // Per-thread constants of one layer: norm gains of elements tid, tid + NT, tid + 2 NT, tid + 3 NT
@@ -214,62 +221,61 @@ __device__ __forceinline__ void tk_load_consts(TkConsts& c, const KCONST TkDesc&
   }
 }
 
-// The back waves copy this workgroup's down-projection rows (H/32 rows of F/8 weights, the XCD's
-// columns) from HBM into S.ew with LDS-direct loads: 16-byte unit u of the block (row u / upr,
-// unit u % upr of the row, upr = F/64 units a row) lands at S.ew[8 u]; one instruction moves 64
-// consecutive units. Completion is awaited (s_waitcnt) by the issuing waves before a barrier.
-template <typename WT>
-__device__ __forceinline__ void tk_dma_e(TkSmem& S, const KCONST TkDesc& D, const KCONST LayerW& W, int g, int r) {
+// The front (FRONT) or back waves copy nrows weight rows of upr 16-byte units each (row i from rowptr(i)) into
+// dst with LDS-direct loads: unit u of the block (row u / upr, unit u % upr of the row) lands at
+// dst[8 u], one instruction moving 64 consecutive units. Lanes past the last unit re-read unit 0
+// and land past the block's end, within the 64-unit instruction (the caller keeps that in dst).
+// Completion is awaited (wait_loads) by the issuing waves before a barrier.
+template <typename WT, bool FRONT, typename RowFn>
+__device__ __forceinline__ void tk_dma_rows(uint16_t* dst, int nrows, int upr, RowFn rowptr) {
   constexpr int E = WTraits<WT>::E;
   static_assert(E == 8, "LDS-direct rows are bf16");
+  static_assert(NF == NB, "front and back wave sets of one size");
   const int wave = wave_id();
-  if (wave < NF) return;
-  const int lane = threadIdx.x & 63, hper = D.H / NR, fx = D.F / NX, upr = fx / E, units = hper * upr;
-  const WT* base = reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r) * D.F + fx * g;
-  for (int j = wave - NF; 64 * j < units; j += NB) {
+  if ((wave < NF) != FRONT) return;
+  const int lane = threadIdx.x & 63, units = nrows * upr;
+  for (int j = FRONT ? wave : wave - NF; 64 * j < units; j += NF) {
     const int u = 64 * j + lane;
     const int row = u / upr, col = u - row * upr;
-    // lanes past the last unit re-read unit 0 and land in the unused tail of S.ew (units is a
-    // multiple of 32 and at most TEW / 8, a multiple of 64)
-    const WT* src = u < units ? base + (size_t)row * D.F + col * E : base;
-    __builtin_amdgcn_global_load_lds((const GLB void*)src, (__attribute__((address_space(3))) void*)&S.ew[64 * E * j], 16, 0, 0);
+    const WT* src = u < units ? rowptr(row) + col * E : rowptr(0);
+    __builtin_amdgcn_global_load_lds((const GLB void*)src, (__attribute__((address_space(3))) void*)&dst[64 * E * j], 16, 0, 0);
   }
 }
 
-// out[i] = dot(down row i, S.hb) for the back waves' rows i = (wave - NF) + NB * j, weights read
-// from S.ew.
-template <typename WT>
-__device__ __forceinline__ void tk_dot_e(const TkSmem& S, int hper, int fx, float* out) {
+// Wait until every load this wave issued has landed (the LDS-direct rows included).
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
+// out[i] = dot(row i of w, x[0 .. ncols)) for nrows rows of ncols bf16 weights in LDS (row-major),
+// all waves: wave w takes rows w, w + NW, ... (at most RM), lane the 16-byte units lane + 64 k
+// (k < KK, ncols <= 512 KK). Rows go in groups of 4 so the cross-lane sums of a group overlap.
+template <typename WT, int KK, int RM>
+__device__ __forceinline__ void tk_dot_lds(const uint16_t* w, int nrows, int ncols, const float* x, float* out) {
   constexpr int E = WTraits<WT>::E;
-  constexpr int RE = THMAX / NR / NB;  // rows per back wave at most
-  const int wave = wave_id();
-  if (wave < NF) return;
-  const int lane = threadIdx.x & 63, upr = fx / E;
-  float xv[2][8];
+  const int wave = wave_id(), lane = threadIdx.x & 63, upr = ncols / E;
+  float xv[KK][8];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < KK; ++k) {
     const int u = lane + 64 * k;
 #pragma unroll
     for (int e = 0; e < 8; e += 4) {
-      const float4 f = u < upr ? *reinterpret_cast<const float4*>(S.hb + u * E + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 f = u < upr ? *reinterpret_cast<const float4*>(x + u * E + e) : make_float4(0.f, 0.f, 0.f, 0.f);
       xv[k][e] = f.x; xv[k][e + 1] = f.y; xv[k][e + 2] = f.z; xv[k][e + 3] = f.w;
     }
   }
-  // groups of 4 rows: the cross-lane sums of a group overlap
-#pragma unroll 1
-  for (int j0 = 0; j0 < RE; j0 += 4) {
+#pragma unroll
+  for (int j0 = 0; j0 < RM; j0 += 4) {
     float acc[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int i = (wave - NF) + NB * (j0 + jj);
+      const int i = wave + NW * (j0 + jj);
       float s = 0.f;
-      if (i < hper) {
+      if (j0 + jj < RM && i < nrows) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < KK; ++k) {
           const int u = lane + 64 * k;
           if (u < upr) {
             float wf[8];
-            unpack(*reinterpret_cast<const u32x4*>(&S.ew[(i * upr + u) * E]), wf, (WT*)nullptr);
+            unpack(*reinterpret_cast<const u32x4*>(&w[(i * upr + u) * E]), wf, (WT*)nullptr);
 #pragma unroll
             for (int e = 0; e < 8; ++e) s = fmaf(wf[e], xv[k][e], s);
           }
@@ -279,9 +285,9 @@ __device__ __forceinline__ void tk_dot_e(const TkSmem& S, int hper, int fx, floa
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int i = (wave - NF) + NB * (j0 + jj);
+      const int i = wave + NW * (j0 + jj);
       const float v = wave_sum(acc[jj]);
-      if (i < hper && lane == 0) out[i] = v;
+      if (j0 + jj < RM && i < nrows && lane == 0) out[i] = v;
     }
   }
 }
@@ -471,8 +477,17 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
   return true;
 }
 
-// Wait until every load this wave issued has landed (the LDS-direct rows included).
-__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
+// The constants the layer after l needs (the final-norm gains in c.an after the last layer).
+template <typename WT>
+__device__ __forceinline__ void tk_next_consts(TkConsts& c, const KCONST TkDesc& D, int l, int tid) {
+  if (l + 1 < D.n_layers) {
+    tk_load_consts<WT>(c, D, D.layer[l + 1]);
+  } else {
+    const WT* f = reinterpret_cast<const WT*>(D.final_norm);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c.an[k] = tid + k * NT < D.H ? to_f32(glb(f)[tid + k * NT]) : 0.f;
+  }
+}
 
 template <typename WT>
 __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
@@ -502,57 +517,65 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   lds_barrier();
   bool ok = true;
   const int qh = qper / 2, hh = hper / 2, nd = 2 * fper;  // rows of A0/A1, C0/C1; gate + up rows
+  const int nl = min(min(nd, TLW / H), 4 * NW);            // gate/up rows held in LDS (4 per wave)
   for (int l = 0; ok && l < D.n_layers; ++l) {
     const KCONST LayerW& W = D.layer[l];
     const bool last = l + 1 == D.n_layers;
     // q/k/v slice (A0: X0, A1: X1); the output projection rows (C0, C1) follow in their place and
-    // the down rows go to LDS
+    // the first gate/up rows go to LDS
     tk_rmsnorm(S.xs, H, c.an, D.eps, S.xn, S.red, l > 0 ? S.xs + H : nullptr);
     wb_dot<WT, 2, 4>(X0, qh, H, S.xn, S.out);
     tk_issue_c<WT>(X0, D, W, 0, g, r);
     wb_dot<WT, 2, 4>(X1, qh, H, S.xn, S.out + qh);
     tk_issue_c<WT>(X1, D, W, 1, g, r);
-    tk_dma_e<WT>(S, D, W, g, r);
+    {
+      // the row index differs between lanes: select between the two block bases (no per-lane
+      // descriptor reads, whose wait would also drain the copies in flight)
+      const WT* gb = tk_gu_row<WT>(D, W, 0, g, r);
+      const WT* ub = tk_gu_row<WT>(D, W, fper, g, r);
+      tk_dma_rows<WT, false>(S.lw, nl, H / 8, [&](int i) { return i < fper ? gb + (size_t)i * H : ub + (size_t)(i - fper) * H; });
+    }
     lds_barrier();
     if (!slice_gather<1, KQ, PF>(X, qper, qrows, [&](int e, int) { return S.out[e]; }, S.qkv, tag, iring, g, r, [] {})) {
       ok = false;
       break;
     }
     if (!tk_attention<WT>(D, X, l, p, c, rc, rs, S, tag, iring, apar, g, r)) { ok = false; break; }
-    // output projection partial (C0: X0, C1: X1), residual; gate/up chunks 0, 1 follow
+    // output projection partial (C0: X0, C1: X1), residual; the remaining gate/up rows follow
     wb_dot<WT, 8, 1>(X0, hh, G * d, S.ob, S.out);
-    tk_issue_d<WT>(X0, D, W, 0, g, r);
+    tk_issue_d<WT>(X0, D, W, nl, 0, g, r);
     wb_dot<WT, 8, 1>(X1, hh, G * d, S.ob, S.out + hh);
-    tk_issue_d<WT>(X1, D, W, 1, g, r);
+    tk_issue_d<WT>(X1, D, W, nl, 1, g, r);
     lds_barrier();
     if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [] {})) {
       ok = false;
       break;
     }
-    // gate and up rows (even chunks in X0, odd in X1), SwiGLU; then the next layer's q/k/v rows
-    // (or the semantic head) follow while the down rows are read from LDS
+    // gate and up rows (LDS block, then D0: X0, D1: X1), SwiGLU. Once the LDS block is read the
+    // front waves copy the down rows in its place (their wait then overlaps the SwiGLU exchange)
+    // and the back waves, their registers free, start on the next layer's q/k/v rows (or the
+    // semantic head). Each wave loads its own next-layer constants behind its other loads.
     tk_rmsnorm(S.xs, H, c.mn, D.eps, S.xn, S.red, S.xs + H);
-    if (!last) {
-      tk_load_consts<WT>(c, D, D.layer[l + 1]);
+    if (wave >= NF) wait_loads();
+    lds_barrier();
+    tk_dot_lds<WT, 4, 4>(S.lw, nl, H, S.xn, S.out);
+    lds_barrier();
+    if (wave < NF) {
+      const WT* db = reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r) * D.F + fx * g;
+      const int F = D.F;
+      tk_dma_rows<WT, true>(S.lw, hper, fx / 8, [&](int i) { return db + (size_t)i * F; });
+      tk_next_consts<WT>(c, D, l, tid);
     } else {
-      const WT* f = reinterpret_cast<const WT*>(D.final_norm);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) c.an[k] = tid + k * NT < H ? to_f32(glb(f)[tid + k * NT]) : 0.f;
-    }
-#pragma unroll 1
-    for (int cc = 0; cc < 6; cc += 2) {
-      wb_dot<WT, 2, 4>(X0, tk_d_rows(nd, cc), H, S.xn, S.out + 8 * cc);
-      if (cc + 2 < 6) tk_issue_d<WT>(X0, D, W, cc + 2, g, r);
-      wb_dot<WT, 2, 4>(X1, tk_d_rows(nd, cc + 1), H, S.xn, S.out + 8 * (cc + 1));
-      if (cc + 3 < 6) tk_issue_d<WT>(X1, D, W, cc + 3, g, r);
-    }
-    if (wave >= NF) wait_loads();  // the down rows are in LDS (seen by all after the barrier)
-    if (!last) {
-      tk_issue_a<WT>(X0, D, D.layer[l + 1], 0, g, r);
-      tk_issue_a<WT>(X1, D, D.layer[l + 1], 1, g, r);
-    } else {
-      tk_issue_f<WT>(X0, D, 0);
-      tk_issue_f<WT>(X1, D, 1);
+      wb_dot<WT, 2, 4>(X0, min(8, max(0, nd - nl)), H, S.xn, S.out + nl);
+      wb_dot<WT, 2, 4>(X1, min(8, max(0, nd - nl - 8)), H, S.xn, S.out + nl + 8);
+      tk_next_consts<WT>(c, D, l, tid);
+      if (!last) {
+        tk_issue_a<WT>(X0, D, D.layer[l + 1], 0, g, r);
+        tk_issue_a<WT>(X1, D, D.layer[l + 1], 1, g, r);
+      } else {
+        tk_issue_f<WT>(X0, D, 0);
+        tk_issue_f<WT>(X1, D, 1);
+      }
     }
     lds_barrier();
     if (!slice_gather<1, KH, PF>(X, fper, fx, [&](int e, int) { return silu(S.out[e]) * S.out[fper + e]; }, S.hb, tag,
@@ -561,7 +584,9 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
       break;
     }
     // down projection partial from LDS, residual
-    tk_dot_e<WT>(S, hper, fx, S.out);
+    if (wave < NF) wait_loads();
+    lds_barrier();
+    tk_dot_lds<WT, 2, 8>(S.lw, hper, fx, S.hb, S.out);
     lds_barrier();
     if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [] {})) {
       ok = false;

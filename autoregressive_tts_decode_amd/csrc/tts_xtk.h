@@ -221,26 +221,44 @@ __device__ __forceinline__ void tk_load_consts(TkConsts& c, const KCONST TkDesc&
   }
 }
 
-// The front (FRONT) or back waves copy nrows weight rows of upr 16-byte units each (row i from rowptr(i)) into
-// dst with LDS-direct loads: unit u of the block (row u / upr, unit u % upr of the row) lands at
-// dst[8 u], one instruction moving 64 consecutive units. Lanes past the last unit re-read unit 0
-// and land past the block's end, within the 64-unit instruction (the caller keeps that in dst).
-// Completion is awaited (wait_loads) by the issuing waves before a barrier.
-template <typename WT, bool FRONT, typename RowFn>
-__device__ __forceinline__ void tk_dma_rows(uint16_t* dst, int nrows, int upr, RowFn rowptr) {
-  constexpr int E = WTraits<WT>::E;
-  static_assert(E == 8, "LDS-direct rows are bf16");
-  static_assert(NF == NB, "front and back wave sets of one size");
-  const int wave = wave_id();
-  if ((wave < NF) != FRONT) return;
-  const int lane = threadIdx.x & 63, units = nrows * upr;
-  for (int j = FRONT ? wave : wave - NF; 64 * j < units; j += NF) {
-    const int u = 64 * j + lane;
-    const int row = u / upr, col = u - row * upr;
-    const WT* src = u < units ? rowptr(row) + col * E : rowptr(0);
-    __builtin_amdgcn_global_load_lds((const GLB void*)src, (__attribute__((address_space(3))) void*)&dst[64 * E * j], 16, 0, 0);
+// A block of weight rows copied into LDS in parts, by the front (FRONT) or back waves, with
+// LDS-direct loads: unit u of the block (row u / upr, unit u % upr of the row, upr 16-byte units
+// a row) lands at dst[8 u], one instruction moving 64 consecutive units. Row i starts at
+// b0 + i * stride for i < split, else at b1 + (i - split) * stride. part(n) issues at most n more
+// instructions per wave: a wave that issues more than its share of the CU's memory queue holds
+// stalls until the queue drains, so large copies go in parts spread over the barrier intervals of
+// a layer. A copy has landed once the issuing wave's vector-memory counter has passed it.
+template <typename WT, bool FRONT>
+struct RowCopy {
+  const WT *b0, *b1;
+  long long stride;
+  int split, upr, units, j;
+
+  __device__ __forceinline__ void begin(const WT* b0_, const WT* b1_, int split_, long long stride_, int nrows, int upr_) {
+    b0 = b0_;
+    b1 = b1_;
+    split = split_;
+    stride = stride_;
+    upr = upr_;
+    units = nrows * upr_;
+    j = FRONT ? wave_id() : wave_id() - NF;
   }
-}
+  __device__ __forceinline__ void part(uint16_t* dst, int n) {
+    constexpr int E = WTraits<WT>::E;
+    static_assert(E == 8, "LDS-direct rows are bf16");
+    static_assert(NF == NB, "front and back wave sets of one size");
+    if ((wave_id() < NF) != FRONT) return;
+    const int lane = threadIdx.x & 63;
+    for (int c = 0; c < n && 64 * j < units; ++c, j += NF) {
+      const int u = 64 * j + lane;
+      const int row = u / upr, col = u - row * upr;
+      // lanes past the last unit re-read unit 0 and land in the 64-unit tail of the instruction
+      const int rr = u < units ? row : 0;
+      const WT* src = (rr < split ? b0 + rr * stride : b1 + (rr - split) * stride) + (u < units ? col * E : 0);
+      __builtin_amdgcn_global_load_lds((const GLB void*)src, (__attribute__((address_space(3))) void*)&dst[64 * E * j], 16, 0, 0);
+    }
+  }
+};
 
 // Wait until every load this wave issued has landed (the LDS-direct rows included).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
@@ -328,12 +346,12 @@ __device__ __forceinline__ void tk_rmsnorm(const float* x, int n, const float* g
 
 // Attention of this XCD's two query heads over positions 0..p of KV head g, this rank's chunk of
 // positions, then the two combining exchanges; the XCD's 256 outputs land in S.ob. Only the front
-// waves compute; the back waves meet them at the barriers. rc, rs: RoPE factors of position p at
-// lane (q/k waves).
-template <typename WT>
+// waves compute; the back waves meet them at the barriers, running bg(k) (k = 0 .. 3) in the four
+// intervals before them. rc, rs: RoPE factors of position p at lane (q/k waves).
+template <typename WT, typename Bg>
 __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& X, int layer, int p, const TkConsts& cn,
                                              float rc, float rs, TkSmem& S, uint32_t& tag, int& iring, int& apar, int g,
-                                             int r) {
+                                             int r, Bg bg) {
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, d = D.d;
   const float* kg = D.kc + ((size_t)layer * D.ls + (size_t)g * D.cap) * d;
   const float* vg = D.vc + ((size_t)layer * D.ls + (size_t)g * D.cap) * d;
@@ -362,6 +380,8 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
       glb(vd)[lane] = v0;
       glb(vd)[lane + 64] = v1;
     }
+  } else {
+    bg(0);
   }
   lds_barrier();
   // this rank's chunk [t0, t1) of positions 0..p; each front wave takes 16 positions per pass
@@ -427,6 +447,8 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
       S.wo[wave][h][lane] = o[h][0];
       S.wo[wave][h][lane + 64] = o[h][1];
     }
+  } else {
+    bg(1);
   }
   lds_barrier();
   // this rank's partial: combine the front waves; publish (max, sum, 128 outputs) per head
@@ -451,6 +473,8 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
       st_c(slot + h * 130, pack(mx, tag));
       st_c(slot + h * 130 + 1, pack(ls, tag));
     }
+  } else {
+    bg(2);
   }
   // rank r combines outputs [8 * (r % 16), +8) of head r / 16 from the 32 ranks' partials
   const int hb = r >> 4, db = 8 * (r & 15);
@@ -472,7 +496,7 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
           os += S.cmb[s2 * 10 + 2 + k] * f;
         }
         return os / ls;
-      }, S.ob, tag, iring, g, r, [] {}))
+      }, S.ob, tag, iring, g, r, [&] { if (wave >= NF) bg(3); }))
     return false;
   return true;
 }
@@ -502,9 +526,21 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   const int qrows = (G + 2) * d, qper = qrows / NR, hper = H / NR, fx = D.F / NX, fper = fx / NR;
   TkConsts c;
   tk_load_consts<WT>(c, D, D.layer[0]);
+  const int qh = qper / 2, hh = hper / 2, nd = 2 * fper;  // rows of A0/A1, C0/C1; gate + up rows
+  const int nl = min(min(nd, TLW / H), 4 * NW);            // gate/up rows held in LDS (4 per wave)
+  // The LDS gate/up block of a layer goes in parts (instructions per back wave, 32 for the largest
+  // block): 4 while the previous layer's down exchange runs, 4 after the q/k/v rows, 6 during the
+  // q/k/v exchange, 4 + 6 + 4 in the attention and the rest during its last exchange.
+  RowCopy<WT, false> gu;
+  auto gu_begin = [&](const KCONST LayerW& W) {
+    gu.begin(tk_gu_row<WT>(D, W, 0, g, r), tk_gu_row<WT>(D, W, fper, g, r), fper, H, nl, H / 8);
+  };
+  RowCopy<WT, true> dn;  // the down rows, by the front waves, in two parts
   WBuf X0, X1;
   tk_issue_a<WT>(X0, D, D.layer[0], 0, g, r);
   tk_issue_a<WT>(X1, D, D.layer[0], 1, g, r);
+  gu_begin(D.layer[0]);
+  gu.part(S.lw, 4);
   uint32_t tag = glb(D.st)->epoch;
   const int p = glb(D.st)->pos;
   float rc = 1.f, rs = 0.f;  // RoPE factors of position p (the same in every layer)
@@ -516,43 +552,42 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   for (int i = tid; i < H; i += NT) S.xs[i] = glb(D.x_in)[i];
   lds_barrier();
   bool ok = true;
-  const int qh = qper / 2, hh = hper / 2, nd = 2 * fper;  // rows of A0/A1, C0/C1; gate + up rows
-  const int nl = min(min(nd, TLW / H), 4 * NW);            // gate/up rows held in LDS (4 per wave)
   for (int l = 0; ok && l < D.n_layers; ++l) {
     const KCONST LayerW& W = D.layer[l];
     const bool last = l + 1 == D.n_layers;
-    // q/k/v slice (A0: X0, A1: X1); the output projection rows (C0, C1) follow in their place and
-    // the first gate/up rows go to LDS
+    // q/k/v slice (A0: X0, A1: X1); the output projection rows (C0, C1) follow in their place
     tk_rmsnorm(S.xs, H, c.an, D.eps, S.xn, S.red, l > 0 ? S.xs + H : nullptr);
     wb_dot<WT, 2, 4>(X0, qh, H, S.xn, S.out);
     tk_issue_c<WT>(X0, D, W, 0, g, r);
     wb_dot<WT, 2, 4>(X1, qh, H, S.xn, S.out + qh);
     tk_issue_c<WT>(X1, D, W, 1, g, r);
-    {
-      // the row index differs between lanes: select between the two block bases (no per-lane
-      // descriptor reads, whose wait would also drain the copies in flight)
-      const WT* gb = tk_gu_row<WT>(D, W, 0, g, r);
-      const WT* ub = tk_gu_row<WT>(D, W, fper, g, r);
-      tk_dma_rows<WT, false>(S.lw, nl, H / 8, [&](int i) { return i < fper ? gb + (size_t)i * H : ub + (size_t)(i - fper) * H; });
-    }
+    gu.part(S.lw, 4);
     lds_barrier();
-    if (!slice_gather<1, KQ, PF>(X, qper, qrows, [&](int e, int) { return S.out[e]; }, S.qkv, tag, iring, g, r, [] {})) {
+    if (!slice_gather<1, KQ, PF>(X, qper, qrows, [&](int e, int) { return S.out[e]; }, S.qkv, tag, iring, g, r,
+                                 [&] { gu.part(S.lw, 6); })) {
       ok = false;
       break;
     }
-    if (!tk_attention<WT>(D, X, l, p, c, rc, rs, S, tag, iring, apar, g, r)) { ok = false; break; }
-    // output projection partial (C0: X0, C1: X1), residual; the remaining gate/up rows follow
+    if (!tk_attention<WT>(D, X, l, p, c, rc, rs, S, tag, iring, apar, g, r, [&](int k) {
+          if (k == 3) gu.part(S.lw, 1 << 20);
+          else gu.part(S.lw, k == 1 ? 6 : 4);
+        })) {
+      ok = false;
+      break;
+    }
+    // output projection partial (C0: X0, C1: X1), residual; the register gate/up chunks follow
+    // (D0 now, D1 during the exchange)
     wb_dot<WT, 8, 1>(X0, hh, G * d, S.ob, S.out);
     tk_issue_d<WT>(X0, D, W, nl, 0, g, r);
     wb_dot<WT, 8, 1>(X1, hh, G * d, S.ob, S.out + hh);
-    tk_issue_d<WT>(X1, D, W, nl, 1, g, r);
     lds_barrier();
-    if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [] {})) {
+    if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r,
+                                         [&] { tk_issue_d<WT>(X1, D, W, nl, 1, g, r); })) {
       ok = false;
       break;
     }
     // gate and up rows (LDS block, then D0: X0, D1: X1), SwiGLU. Once the LDS block is read the
-    // front waves copy the down rows in its place (their wait then overlaps the SwiGLU exchange)
+    // front waves copy the down rows in its place (half now, half during the SwiGLU exchange)
     // and the back waves, their registers free, start on the next layer's q/k/v rows (or the
     // semantic head). Each wave loads its own next-layer constants behind its other loads.
     tk_rmsnorm(S.xs, H, c.mn, D.eps, S.xn, S.red, S.xs + H);
@@ -560,35 +595,43 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     lds_barrier();
     tk_dot_lds<WT, 4, 4>(S.lw, nl, H, S.xn, S.out);
     lds_barrier();
+    const int dparts = (hper * (fx / 8) / 64 + 2 * NF - 1) / (2 * NF);  // first half, per front wave
     if (wave < NF) {
-      const WT* db = reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r) * D.F + fx * g;
-      const int F = D.F;
-      tk_dma_rows<WT, true>(S.lw, hper, fx / 8, [&](int i) { return db + (size_t)i * F; });
+      dn.begin(reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r) * D.F + fx * g, nullptr, hper, D.F, hper, fx / 8);
+      dn.part(S.lw, dparts);
       tk_next_consts<WT>(c, D, l, tid);
     } else {
       wb_dot<WT, 2, 4>(X0, min(8, max(0, nd - nl)), H, S.xn, S.out + nl);
+      if (!last) tk_issue_a<WT>(X0, D, D.layer[l + 1], 0, g, r);
+      else tk_issue_f<WT>(X0, D, 0);
       wb_dot<WT, 2, 4>(X1, min(8, max(0, nd - nl - 8)), H, S.xn, S.out + nl + 8);
       tk_next_consts<WT>(c, D, l, tid);
-      if (!last) {
-        tk_issue_a<WT>(X0, D, D.layer[l + 1], 0, g, r);
-        tk_issue_a<WT>(X1, D, D.layer[l + 1], 1, g, r);
-      } else {
-        tk_issue_f<WT>(X0, D, 0);
-        tk_issue_f<WT>(X1, D, 1);
-      }
     }
     lds_barrier();
     if (!slice_gather<1, KH, PF>(X, fper, fx, [&](int e, int) { return silu(S.out[e]) * S.out[fper + e]; }, S.hb, tag,
-                                 iring, g, r, [] {})) {
+                                 iring, g, r, [&] {
+                                   if (wave < NF) {
+                                     dn.part(S.lw, 1 << 20);
+                                   } else {
+                                     if (!last) tk_issue_a<WT>(X1, D, D.layer[l + 1], 1, g, r);
+                                     else tk_issue_f<WT>(X1, D, 1);
+                                   }
+                                 })) {
       ok = false;
       break;
     }
-    // down projection partial from LDS, residual
+    // down projection partial from LDS, residual; the next layer's LDS gate/up block starts
+    // during the exchange
     if (wave < NF) wait_loads();
     lds_barrier();
     tk_dot_lds<WT, 2, 8>(S.lw, hper, fx, S.hb, S.out);
     lds_barrier();
-    if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [] {})) {
+    if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] {
+          if (!last) {
+            gu_begin(D.layer[l + 1]);
+            gu.part(S.lw, 4);
+          }
+        })) {
       ok = false;
       break;
     }

@@ -1,6 +1,11 @@
 """Summarise a rocprofv3 --kernel-trace --stats run of bench.py as text.
 
     python -m autoregressive_tts_decode_amd.prof_summary <prefix> [--frames K]
+    python -m autoregressive_tts_decode_amd.prof_summary <prefix> --pmc COUNTER [--kernel NAME]
+
+With --pmc, <prefix>_counter_collection.csv of a rocprofv3 --pmc run is read instead and the
+per-dispatch average of COUNTER is printed for every kernel (or the kernels whose name contains
+NAME).
 
 <prefix> is the path prefix rocprofv3 wrote (…/bench): it reads
 <prefix>_kernel_stats.csv and <prefix>_kernel_trace.csv. The frame loop is
@@ -21,7 +26,18 @@ def main():
     ap.add_argument("--frames", type=int, default=0, help="timed frames at the end of the trace")
     ap.add_argument("--kernels-per-frame", type=int, default=0)
     ap.add_argument("--top", type=int, default=16)
+    ap.add_argument("--pmc", default="")
+    ap.add_argument("--kernel", default="")
     a = ap.parse_args()
+    if a.pmc:
+        vals = defaultdict(list)
+        for r in csv.DictReader(open(a.prefix + "_counter_collection.csv")):
+            if r["Counter_Name"] == a.pmc and a.kernel in r["Kernel_Name"]:
+                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        print(f"{'kernel':78s} {'dispatches':>10s} {a.pmc + ' avg':>16s} {'min':>14s} {'max':>14s}")
+        for k, v in sorted(vals.items(), key=lambda kv: -sum(kv[1])):
+            print(f"{k[:78]:78s} {len(v):10d} {sum(v) / len(v):16.1f} {min(v):14.1f} {max(v):14.1f}")
+        return
     rows = list(csv.DictReader(open(a.prefix + "_kernel_stats.csv")))
     tot = sum(float(r["TotalDurationNs"]) for r in rows)
     print(f"total kernel time in the run: {tot / 1e6:.2f} ms over {sum(int(r['Calls']) for r in rows)} launches")

@@ -15,6 +15,10 @@ not streamed whole and the 14 idle heads of a step are not read.
 """
 from __future__ import annotations
 
+import hashlib
+import os
+import re
+
 from .config import ModelCfg, StackCfg, FRAME_RATE_HZ
 
 HBM_PEAK_BYTES_PER_S = 8.0e12  # MI355X published HBM3E bandwidth
@@ -90,3 +94,42 @@ def frame_bytes_for_run(cfg: ModelCfg, prefill_len: int, first_frame: int, n_fra
     for t in range(first_frame, first_frame + n_frames):
         tot += algorithmic_bytes(cfg, prefill_len + t + 1, batch, kv_elem_bytes)["total"]
     return tot
+
+
+# ---------------------------------------------------------------------------- measured traffic
+
+_CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+_PROFILES = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles")
+
+
+def kernel_source_sha256(files=("tts_xtp.h", "tts_device.h")) -> str:
+    """SHA-256 over the sources a persistent kernel is built from (in the given order)."""
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(_CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(record: str, files=("tts_xtp.h", "tts_device.h")) -> int | None:
+    """HBM bytes per launch from a committed counter record, or None when there is none or the
+    kernel's sources changed since the counters were taken.
+
+    The record (a text file under profiles/) holds the lines
+    ``kernel_source_sha256: <hex>`` and ``traffic_bytes_per_launch: <int>``.
+    """
+    path = os.path.join(_PROFILES, record)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            m = re.match(r"^\s*(kernel_source_sha256|traffic_bytes_per_launch):\s*(\S+)\s*$", line)
+            if m:
+                fields[m.group(1)] = m.group(2)
+    if fields.get("kernel_source_sha256") != kernel_source_sha256(files):
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None

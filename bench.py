@@ -174,8 +174,10 @@ def main():
     if dom is not None:
         dom_s, dom_bytes = dom
         a_gbs = dom_bytes / dom_s / 1e9
+        # HBM bytes per launch from the committed counter record (null once the kernel changed)
+        traffic = roofline.measured_traffic("k_cp_frame_1.7b_b1_hbm_traffic.md") if args.workload == "1.7b" else None
         out["roofline"] = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": peak, "unit": "GB/s",
-                           "frac": round(a_gbs / peak, 4), "traffic": None,
+                           "frac": round(a_gbs / peak, 4), "traffic": traffic,
                            "kernel": "tts::xtp::k_cp_frame (persistent CodePredictor frame: 15 steps)",
                            "avg_launch_us": round(dom_s * 1e6, 2), "algorithmic_bytes_per_launch": int(dom_bytes)}
     else:

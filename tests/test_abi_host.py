@@ -101,3 +101,17 @@ def test_create_rejects_small_or_misaligned_workspace_before_touching_the_device
     assert lib.tts_create(ctypes.byref(c), None, ctypes.c_void_p(4096 + 8), need, ctypes.byref(out)) == tts.TTS_E_ARG
     assert lib.tts_create(ctypes.byref(c), None, ctypes.c_void_p(4096), need - 1, ctypes.byref(out)) == tts.TTS_E_CAPACITY
     assert out.value is None
+
+
+def test_measured_traffic_record_follows_the_kernel_sources(tmp_path, monkeypatch):
+    """The bench's HBM traffic comes from a committed counter record and is dropped (None) as soon
+    as the kernel's sources no longer hash to the recorded value."""
+    from autoregressive_tts_decode_amd import roofline
+    h = roofline.kernel_source_sha256()
+    assert len(h) == 64 and int(h, 16) >= 0
+    monkeypatch.setattr(roofline, "_PROFILES", str(tmp_path))
+    assert roofline.measured_traffic("absent.md") is None
+    (tmp_path / "ok.md").write_text(f"text\n    kernel_source_sha256: {h}\n    traffic_bytes_per_launch: 12345\n")
+    assert roofline.measured_traffic("ok.md") == 12345
+    (tmp_path / "stale.md").write_text("    kernel_source_sha256: " + "0" * 64 + "\n    traffic_bytes_per_launch: 12345\n")
+    assert roofline.measured_traffic("stale.md") is None

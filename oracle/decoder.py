@@ -20,6 +20,13 @@ Readings where the pages are silent (each is listed in the design notes):
   * GQA grouping: query head h reads KV head h // (n_q_heads / n_kv_heads).
   * Talker input for frame t >= 1 is the sum of the 16 codebook embeddings of
     frame t-1: E_sem[s] + sum_j E_ac[j][a_j], at Talker position n + t - 1.
+  * Streaming text conditioning ("Running Qwen3-TTS on an AMD R9700": the
+    streaming mode feeds the model one text token at a time; "qwen3-tts-hip"
+    README, section "Library Usage": text_lookahead_tokens sets the text of the
+    streaming prefill): with lookahead L the prefill covers ids[:, :L] only,
+    and the Talker step of frame t >= 1 adds the text row E_text[ids[:, L+t-1]]
+    to the frame's embedding sum while L+t-1 < n; once the text is used up
+    nothing is added. With L = n this is the non-streaming decode.
   * CodePredictor conditioning: positions restart at 0 every frame with an
     empty cache; position 0 holds P·h_T (h_T = the Talker's post-final-norm
     hidden of this frame), position 1 holds P·E_sem[s]; acoustic token j is
@@ -222,9 +229,21 @@ class OracleModel:
         st.h_T = h
         return linear(h, self.lm_head)
 
-    def talker_step(self, st: OracleState, prev_codes: np.ndarray) -> np.ndarray:
-        """One Talker step fed with the previous frame's 16 codes; returns semantic logits."""
-        h = self._stack_step(self.talker, self.embed_sum(np.asarray(prev_codes)), st.pos, st.talker_k, st.talker_v)
+    def text_rows(self, text_ids: np.ndarray) -> np.ndarray:
+        """Streaming text term per stream: E_text[id], or zeros where id < 0 (no text left)."""
+        text_ids = np.asarray(text_ids)
+        rows = self.embed_text[np.maximum(text_ids, 0)].copy()
+        rows[text_ids < 0] = 0
+        return rows
+
+    def talker_step(self, st: OracleState, prev_codes: np.ndarray, text_ids: np.ndarray | None = None) -> np.ndarray:
+        """One Talker step fed with the previous frame's 16 codes (plus, when text_ids [B] is
+        given, the streaming text row E_text[id] of each stream with id >= 0); returns semantic
+        logits."""
+        x = self.embed_sum(np.asarray(prev_codes))
+        if text_ids is not None:
+            x = x + self.text_rows(text_ids)
+        h = self._stack_step(self.talker, x, st.pos, st.talker_k, st.talker_v)
         st.pos += 1
         st.h_T = h
         return linear(h, self.lm_head)
@@ -255,18 +274,29 @@ class OracleModel:
             codes[:, j - 1] = sample_rows(lg, sampling, u[:, j - 1], None, dtype=sampler_dtype)
         return codes, logits
 
+    def stream_text_ids(self, ids: np.ndarray, lookahead: int, t: int) -> np.ndarray:
+        """Text ids [B] the Talker step of frame t >= 1 adds in streaming mode (-1: none)."""
+        ids = np.asarray(ids)
+        j = lookahead + t - 1
+        return ids[:, j] if j < ids.shape[1] else np.full(ids.shape[0], -1, dtype=ids.dtype)
+
     def generate(self, ids: np.ndarray, frames: int, sem_sampling: dict, ac_sampling: dict,
                  uniforms: np.ndarray, teacher: np.ndarray | None = None, keep_logits: bool = True,
-                 keep_hidden: bool = False, sampler_dtype=np.float64) -> dict:
+                 keep_hidden: bool = False, sampler_dtype=np.float64, text_lookahead: int | None = None) -> dict:
         """Prefill then ``frames`` frames. uniforms: [B, >=frames, 16].
 
         teacher: [B, frames, 16] codes to feed forward instead of the drawn ones
         (teacher forcing); drawn tokens and logits are still reported.
+        text_lookahead: streaming mode with that many text ids in the prefill, the rest
+        fed one per frame (see the module docstring); None = all ids in the prefill.
         """
         ids = np.asarray(ids)
         B = ids.shape[0]
-        st = self.new_state(B, ids.shape[1] + frames)
-        logits = self.prefill(st, ids)
+        L = ids.shape[1] if text_lookahead is None else int(text_lookahead)
+        if not 1 <= L <= ids.shape[1]:
+            raise ValueError("text_lookahead must lie in [1, n]")
+        st = self.new_state(B, L + frames)
+        logits = self.prefill(st, ids[:, :L])
         history = np.zeros((B, self.talker.vocab), dtype=bool)
         codes = np.zeros((B, frames, 1 + self.n_ac), dtype=np.int32)
         out = {"codes": codes}
@@ -279,7 +309,8 @@ class OracleModel:
         for t in range(frames):
             if t > 0:
                 prev = teacher[:, t - 1] if teacher is not None else codes[:, t - 1]
-                logits = self.talker_step(st, prev)
+                text = self.stream_text_ids(ids, L, t) if L < ids.shape[1] else None
+                logits = self.talker_step(st, prev, text)
             if keep_logits:
                 out["sem_logits"][:, t] = logits
             if keep_hidden:

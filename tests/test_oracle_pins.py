@@ -87,6 +87,64 @@ def test_p1_teacher_forcing_with_own_codes_is_free_running(tiny_weights, tiny_cf
     np.testing.assert_array_equal(free["ac_logits"], forced["ac_logits"])
 
 
+# ----------------------------------------------------------------------------- f1 streaming text
+
+@pytest.mark.parametrize("lookahead,frames", [(3, 5), (1, 4), (4, 9)])
+@pytest.mark.parametrize("dtype,tol", [(np.float64, 1e-12), (np.float32, 1e-5)])
+def test_f1_streaming_decode_equals_full_causal_recompute(lookahead, frames, dtype, tol, tiny_weights, tiny_cfg):
+    """Streaming text conditioning against a cache-free recompute of the sequence the reading
+    defines: [E_text[ids[:L]]; x_t + E_text[ids[L+t-1]] (while the text lasts)] for t >= 1.
+    (4, 9) runs past the end of the text (n = 8): the last frames add no text row."""
+    m = OracleModel(tiny_weights, tiny_cfg, dtype)
+    n = 8
+    ids = synth.random_ids(n, tiny_cfg["text_vocab"], seed=21)
+    u = synth.random_uniforms((1, frames, 16), seed=22)
+    out = m.generate(ids, frames, GREEDY, GREEDY, u, keep_hidden=True, text_lookahead=lookahead)
+    codes = out["codes"]
+    X = [m.embed_text[ids[0, :lookahead]][None]]
+    for t in range(1, frames):
+        x = m.embed_sum(codes[:, t - 1])
+        if lookahead + t - 1 < n:
+            x = x + m.embed_text[ids[:, lookahead + t - 1]]
+        X.append(x[:, None, :])
+    Y = m.full_forward("talker", np.concatenate(X, axis=1))
+    for t in range(frames):
+        assert _rel(out["h_T"][:, t], Y[:, lookahead - 1 + t]) < tol
+        assert _rel(out["sem_logits"][:, t], linear(Y[:, lookahead - 1 + t], m.lm_head)) < tol
+
+
+def test_f1_full_lookahead_is_the_non_streaming_decode(tiny_weights, tiny_cfg):
+    m = OracleModel(tiny_weights, tiny_cfg, np.float64)
+    ids = synth.random_ids(6, tiny_cfg["text_vocab"], seed=23)
+    u = synth.random_uniforms((1, 4, 16), seed=24)
+    a = m.generate(ids, 4, GREEDY, GREEDY, u)
+    b = m.generate(ids, 4, GREEDY, GREEDY, u, text_lookahead=6)
+    np.testing.assert_array_equal(a["codes"], b["codes"])
+    np.testing.assert_array_equal(a["sem_logits"], b["sem_logits"])
+    with pytest.raises(ValueError):
+        m.generate(ids, 2, GREEDY, GREEDY, u, text_lookahead=0)
+
+
+def test_f1_text_row_is_one_hot_matmul_and_absent_past_the_text(tiny_weights, tiny_cfg):
+    """The streaming input is linear in one-hot codes over [E_sem; E_ac...; E_text], and an id of
+    -1 (text used up) contributes nothing."""
+    m = OracleModel(tiny_weights, tiny_cfg, np.float64)
+    g = np.random.default_rng(25)
+    codes = g.integers(0, 512, (3, 16)).astype(np.int32)
+    text = np.array([5, -1, 1023], dtype=np.int32)
+    x = m.embed_sum(codes) + m.text_rows(text)
+    Vt = tiny_cfg["text_vocab"]
+    onehot_text = np.zeros((3, Vt))
+    onehot_text[0, 5] = 1
+    onehot_text[2, 1023] = 1
+    want = np.eye(512)[codes[:, 0]] @ m.embed_sem + onehot_text @ m.embed_text
+    for j in range(1, 16):
+        want = want + np.eye(512)[codes[:, j]] @ m.embed_ac[j - 1]
+    np.testing.assert_allclose(x, want, rtol=1e-13)
+    assert m.stream_text_ids(np.arange(8)[None], 3, 5)[0] == 7
+    assert m.stream_text_ids(np.arange(8)[None], 3, 6)[0] == -1
+
+
 # ----------------------------------------------------------------------------- P2 softmax
 
 @pytest.mark.parametrize("dtype,tol", [(np.float32, 1e-6), (np.float64, 1e-14)])

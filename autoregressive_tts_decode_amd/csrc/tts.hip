@@ -242,6 +242,9 @@ struct tts_ctx {
   const void *embed_text = nullptr, *embed_sem = nullptr, *lm_head = nullptr, *proj = nullptr, *embed_ac = nullptr,
              *heads = nullptr;
   bool weights_ok = false;
+  // streaming text of the frame loop (tts_set_text_stream): ids [B, text_n], borrowed
+  const int32_t* text_ids = nullptr;
+  int text_n = 0, text_next = 0;
   // host mirror of the device counters
   bool prefilled = false;
   int batch = 0, pos = 0, frames = 0;
@@ -576,7 +579,8 @@ int talker_stack(tts_ctx* ctx, int B, int pos_const, int pos_from_state) {
 }
 
 // Talker input from a frame's 16 codes (codebook t of stream b at tok refs).
-int embed_sum(tts_ctx* ctx, int B, const TokRef* refs) {
+// text: the streaming text term (see EmbedArgs), or nullptr for none; text_n: its index bound.
+int embed_sum(tts_ctx* ctx, int B, const TokRef* refs, const TokRef* text = nullptr, int text_n = 0) {
   const auto& c = ctx->cfg;
   EmbedArgs e;
   std::memset(&e, 0, sizeof e);
@@ -592,6 +596,12 @@ int embed_sum(tts_ctx* ctx, int B, const TokRef* refs) {
     e.tok[j] = refs[j];
   }
   e.x = ctx->x; e.x_stride = c.talker.hidden; e.st = ctx->st;
+  if (text) {
+    e.text_table = ctx->embed_text;
+    e.text = *text;
+    e.text_rows = c.text_vocab;
+    e.text_n = text_n;
+  }
   const int gx = (c.talker.hidden + 255) / 256;
   if (ctx->bf16()) hipLaunchKernelGGL(k_embed_sum<uint16_t>, dim3(gx, B), dim3(256), 0, ctx->stream, e);
   else hipLaunchKernelGGL(k_embed_sum<float>, dim3(gx, B), dim3(256), 0, ctx->stream, e);
@@ -763,7 +773,9 @@ int enqueue_frame(tts_ctx* ctx, const tts_sampling& sem, const tts_sampling& ac,
   }
   TokRef refs[16];
   for (int j = 0; j < 16; ++j) refs[j] = tokref(codes, fs, 16, j, 1);
-  if (int rc = embed_sum(ctx, B, refs)) return rc;
+  // streaming text: the step on frame t's codes adds text id [b][next + t] while it exists
+  const TokRef text = tokref(ctx->text_ids, ctx->text_n, 1, ctx->text_next, 1);
+  if (int rc = embed_sum(ctx, B, refs, ctx->text_ids ? &text : nullptr, ctx->text_n)) return rc;
   // the frame's last kernel also advances the device position and frame counters
   if (use_xtk(ctx, B)) return talker_step_xtk(ctx, 1, 1);
   if (int rc = talker_stack(ctx, B, 0, 1)) return rc;
@@ -993,6 +1005,10 @@ int tts_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, floa
 }
 
 int tts_talker_step(tts_ctx* ctx, const int32_t* prev_codes, float* sem_logits) {
+  return tts_talker_step_text(ctx, prev_codes, nullptr, sem_logits);
+}
+
+int tts_talker_step_text(tts_ctx* ctx, const int32_t* prev_codes, const int32_t* text_ids, float* sem_logits) {
   if (!ctx) return TTS_E_ARG;
   if (!ctx->prefilled) return ctx->fail(TTS_E_STATE, "talker_step: call tts_prefill first");
   if (!prev_codes) return ctx->fail(TTS_E_ARG, "talker_step: prev_codes is NULL");
@@ -1000,7 +1016,8 @@ int tts_talker_step(tts_ctx* ctx, const int32_t* prev_codes, float* sem_logits) 
   const int B = ctx->batch;
   TokRef refs[16];
   for (int j = 0; j < 16; ++j) refs[j] = tokref(prev_codes, 16, 0, j, 0);
-  if (int rc = embed_sum(ctx, B, refs)) return rc;
+  const TokRef text = tokref(text_ids, 1, 0, 0, 0);
+  if (int rc = embed_sum(ctx, B, refs, text_ids ? &text : nullptr, 1)) return rc;
   if (use_xtk(ctx, B)) {
     if (int rc = talker_step_xtk(ctx, 1, 0)) return rc;
   } else {
@@ -1108,6 +1125,21 @@ int tts_reset(tts_ctx* ctx) {
   ctx->pos = 0;
   ctx->frames = 0;
   ctx->batch = 0;
+  if (ctx->text_ids) drop_graph(ctx);
+  ctx->text_ids = nullptr;
+  ctx->text_n = ctx->text_next = 0;
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+int tts_set_text_stream(tts_ctx* ctx, const int32_t* text_ids, int32_t n_text, int32_t next) {
+  if (!ctx) return TTS_E_ARG;
+  if (text_ids && (n_text < 1 || next < 0))
+    return ctx->fail(TTS_E_ARG, "set_text_stream: n_text %d must be >= 1 and next %d >= 0", n_text, next);
+  drop_graph(ctx);  // the frame graph holds the text term's addresses
+  ctx->text_ids = text_ids;
+  ctx->text_n = text_ids ? n_text : 0;
+  ctx->text_next = text_ids ? next : 0;
   ctx->err.clear();
   return TTS_OK;
 }

@@ -326,17 +326,34 @@ struct EmbedArgs {
   float* x;
   int32_t x_stride;
   const DevState* st;
+  // Streaming text term ("Running Qwen3-TTS on an AMD R9700": the streaming mode feeds the text
+  // one token per frame): when text.base is set, stream b adds the row E_text[id] of
+  // id = text.base[b * text.b_stride + j], j = text.offset (+ frame * text.f_stride with
+  // use_frame), provided j < text_n and id >= 0; otherwise nothing.
+  const void* text_table;
+  TokRef text;
+  int32_t text_rows, text_n;
 };
 
 template <typename WT>
 __global__ __launch_bounds__(256) void k_embed_sum(EmbedArgs a) {
   const int b = blockIdx.y;
-  __shared__ int toks[16];
+  __shared__ int toks[17];
   if (threadIdx.x < a.ntab) toks[threadIdx.x] = clamp_tok(tok_at(a.tok[threadIdx.x], a.st, b), a.rows[threadIdx.x]);
+  if (threadIdx.x == 16) {
+    int id = -1;
+    if (a.text.base) {
+      const long j = a.text.offset + (a.text.use_frame ? (long)a.st->frame * a.text.f_stride : 0);
+      if (j < a.text_n) id = a.text.base[(long)b * a.text.b_stride + j];
+    }
+    toks[16] = id < 0 ? -1 : clamp_tok(id, a.text_rows);
+  }
   __syncthreads();
+  const int ttok = toks[16];
   for (int k = blockIdx.x * 256 + threadIdx.x; k < a.H; k += gridDim.x * 256) {
     float s = to_f32(reinterpret_cast<const WT*>(a.table[0])[(size_t)toks[0] * a.H + k]);
     for (int t = 1; t < a.ntab; ++t) s += to_f32(reinterpret_cast<const WT*>(a.table[t])[(size_t)toks[t] * a.H + k]);
+    if (ttok >= 0) s += to_f32(reinterpret_cast<const WT*>(a.text_table)[(size_t)ttok * a.H + k]);
     a.x[(size_t)b * a.x_stride + k] = s;
   }
 }

@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "TTS_OK", -1: "TTS_E_ARG", -2: "TTS_E_SHAPE", -3: "TTS_E_CAPA
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTED = ["tts_workspace_bytes", "tts_create", "tts_load_weights", "tts_prefill", "tts_talker_step",
-            "tts_codepred_frame", "tts_sample", "tts_run_frames", "tts_set_exec_mode", "tts_get_exec_mode", "tts_set_prefill_mode", "tts_get_prefill_mode",
+            "tts_talker_step_text", "tts_set_text_stream", "tts_codepred_frame", "tts_sample", "tts_run_frames", "tts_set_exec_mode", "tts_get_exec_mode", "tts_set_prefill_mode", "tts_get_prefill_mode",
             "tts_device_status", "tts_get_progress", "tts_reset", "tts_last_error", "tts_destroy"]
 EXEC_KERNELS, EXEC_PERSISTENT = 0, 1
 PERSISTENT_CODEPRED, PERSISTENT_TALKER = 1, 2  # bits of exec_mode()[1]
@@ -80,6 +80,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(I32), ctypes.POINTER(I32)]
     lib.tts_prefill.argtypes = [P, P, I32, I32, P]
     lib.tts_talker_step.argtypes = [P, P, P]
+    lib.tts_talker_step_text.argtypes = [P, P, P, P]
+    lib.tts_set_text_stream.argtypes = [P, P, I32, I32]
     lib.tts_codepred_frame.argtypes = [P, P, ctypes.POINTER(SamplingC), P, P, P, P]
     lib.tts_sample.argtypes = [P, P, I32, I32, ctypes.POINTER(SamplingC), P, P, P]
     lib.tts_run_frames.argtypes = [P, I32, ctypes.POINTER(SamplingC), ctypes.POINTER(SamplingC), P, P]
@@ -203,8 +205,23 @@ class TTSDecoder:
         B, n = ids.shape
         self._check(self.lib.tts_prefill(self.ctx, _ptr(ids), B, n, _ptr(sem_logits)), "tts_prefill")
 
-    def talker_step(self, prev_codes, sem_logits=None):
-        self._check(self.lib.tts_talker_step(self.ctx, _ptr(prev_codes), _ptr(sem_logits)), "tts_talker_step")
+    def talker_step(self, prev_codes, sem_logits=None, text_ids=None):
+        """One Talker step on the previous frame's codes [B, 16]; text_ids [B] (int32, -1 = none)
+        adds the streaming text row of each stream."""
+        if text_ids is None:
+            self._check(self.lib.tts_talker_step(self.ctx, _ptr(prev_codes), _ptr(sem_logits)), "tts_talker_step")
+        else:
+            self._check(self.lib.tts_talker_step_text(self.ctx, _ptr(prev_codes), _ptr(text_ids), _ptr(sem_logits)),
+                        "tts_talker_step_text")
+
+    def set_text_stream(self, text_ids, next_index: int = 0):
+        """Streaming text for run_frames: text_ids [B, n_text] (int32 device tensor, kept alive by
+        the caller) or None; the step on frame t's codes adds id [b][next_index + t]."""
+        if text_ids is None:
+            self._check(self.lib.tts_set_text_stream(self.ctx, None, 0, 0), "tts_set_text_stream")
+        else:
+            self._check(self.lib.tts_set_text_stream(self.ctx, _ptr(text_ids), int(text_ids.shape[1]), int(next_index)),
+                        "tts_set_text_stream")
 
     def codepred_frame(self, semantic, sampling, u, codes, forced=None, logits=None):
         s = sampling_struct(sampling)

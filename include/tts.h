@@ -118,6 +118,15 @@ int tts_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, floa
  * replaces the pending output; sem_logits [B, Vs] receives it when non-NULL. */
 int tts_talker_step(tts_ctx* ctx, const int32_t* prev_codes, float* sem_logits);
 
+/* tts_talker_step with the streaming text term ("Running Qwen3-TTS on an AMD
+ * R9700": the streaming mode feeds the text one token per frame; "qwen3-tts-hip"
+ * README, section "Library Usage": text_lookahead_tokens text ids go into the
+ * streaming prefill). text_ids [B] (device, or NULL for none): stream b's input
+ * also gets the text embedding row E_text[text_ids[b]] added after the 16 codebook
+ * rows; an id < 0 adds nothing (the text is used up). Ids past the text table are
+ * clamped to its last row. Same errors as tts_talker_step. */
+int tts_talker_step_text(tts_ctx* ctx, const int32_t* prev_codes, const int32_t* text_ids, float* sem_logits);
+
 /* The 15 CodePredictor steps of one frame, conditioned on the pending Talker
  * hidden and on semantic [B]. ac: acoustic sampling; u [B, 15] uniforms
  * (ignored when greedy; may be NULL then). forced [B, 15] or NULL: when given,
@@ -143,6 +152,16 @@ int tts_sample(tts_ctx* ctx, const float* logits, int32_t batch, int32_t vocab, 
  * index kept on the device. */
 int tts_run_frames(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_sampling* ac, const float* u,
                    int32_t* codes);
+
+/* Streaming text for tts_run_frames (see tts_talker_step_text). text_ids
+ * [B, n_text] (device, int32, borrowed until replaced, cleared by tts_reset or
+ * NULL): the Talker step run on frame t's codes (t counts frames since the
+ * prefill) adds E_text[text_ids[b][next + t]] while next + t < n_text, nothing
+ * after that (ids < 0 add nothing either). For a prefill of the first L ids of
+ * an utterance, next = L. NULL switches the text term off. Replacing it drops
+ * the captured frame graph. TTS_E_ARG when ids are given with n_text < 1 or
+ * next < 0. */
+int tts_set_text_stream(tts_ctx* ctx, const int32_t* text_ids, int32_t n_text, int32_t next);
 
 /* Execution of the CodePredictor frame and of the batch-1 Talker step (same
  * results either way, up to floating-point summation order):

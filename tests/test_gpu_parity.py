@@ -63,6 +63,28 @@ def teacher_forced(dec, model, ids, ref_codes, frames, logits_out=True):
             own.cpu().numpy().transpose(1, 0, 2))
 
 
+def stream_teacher_forced(dec, model, ids, lookahead, ref_codes, frames):
+    """Streaming decode on the GPU with the oracle's codes fed forward: prefill of the first
+    `lookahead` ids, then every Talker step adds the next text id (-1 once the text is used up)."""
+    d = dev()
+    B, n = ids.shape
+    Vs, Va = model.talker.vocab, model.codepred.vocab
+    sem = torch.zeros((frames, B, Vs), dtype=torch.float32, device=d)
+    acl = torch.zeros((frames, B, 15, Va), dtype=torch.float32, device=d)
+    own = torch.zeros((frames, B, 15), dtype=torch.int32, device=d)
+    codes = torch.from_numpy(np.ascontiguousarray(ref_codes)).to(d)
+    text = [None] + [torch.from_numpy(ids[:, lookahead + t - 1].astype(np.int32) if lookahead + t - 1 < n
+                                      else np.full(B, -1, np.int32)).to(d) for t in range(1, frames)]
+    dec.prefill(torch.from_numpy(np.ascontiguousarray(ids[:, :lookahead])).to(d), sem[0])
+    for t in range(frames):
+        if t > 0:
+            dec.talker_step(codes[:, t - 1].contiguous(), sem[t], text_ids=text[t])
+        dec.codepred_frame(codes[:, t, 0].contiguous(), GREEDY, None, own[t], forced=codes[:, t, 1:].contiguous(), logits=acl[t])
+    torch.cuda.synchronize()
+    return (sem.cpu().numpy().transpose(1, 0, 2), acl.cpu().numpy().transpose(1, 0, 2, 3),
+            own.cpu().numpy().transpose(1, 0, 2))
+
+
 def check_step_parity(model, ref, got_sem, got_ac, got_tok, tol):
     e_sem = rowwise_rel_err(got_sem, ref["sem_logits"])
     e_ac = rowwise_rel_err(got_ac, ref["ac_logits"])
@@ -367,6 +389,73 @@ def test_bf16_run_frames_greedy_both_modes_match_oracle_until_a_near_tie(bf16_mo
             lg = ref["sem_logits"][0, t] if j == 0 else ref["ac_logits"][0, t, j - 1]
             assert top2_margin(lg) <= 0.05, f"{name} mode {mode}: divergence at frame {t} code {j}, margin {top2_margin(lg):.3f}"
         print(f"{name} mode {mode}: identical for {diff[0] if diff.size else got.size} of {got.size} codes", flush=True)
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- streaming text
+
+def test_tiny_streaming_text_teacher_forced_and_frame_graph(tiny):
+    """Streaming text conditioning: prefill of 4 of 12 ids, one text row per Talker step, none
+    once the text is used up (frames 9..15), eager steps and the captured frame graph."""
+    wl, dec = tiny["wl"], tiny["dec"]
+    ids = synth.random_ids(12, wl.model.text_vocab, seed=31)
+    L, F = 4, wl.frames
+    ref = tiny["orc"].generate(ids, F, GREEDY, GREEDY, tiny["u"], text_lookahead=L)
+    sem, ac, tok = stream_teacher_forced(dec, wl.model, ids, L, ref["codes"], F)
+    es, ea, n, ex = check_step_parity(wl.model, ref, sem, ac, tok, 1e-4)
+    print(f"tiny streaming: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}", flush=True)
+    d = dev()
+    text = torch.from_numpy(ids.astype(np.int32)).to(d)
+    codes = torch.full((1, F + 8, 16), -1, dtype=torch.int32, device=d)
+    dec.set_text_stream(text, L)
+    try:
+        dec.prefill(torch.from_numpy(np.ascontiguousarray(ids[:, :L])).to(d))
+        dec.run_frames(F, GREEDY, GREEDY, None, codes)
+        torch.cuda.synchronize()
+    finally:
+        dec.set_text_stream(None)
+    got = codes.cpu().numpy()[:, :F].reshape(-1)
+    diff = np.nonzero(got != ref["codes"].reshape(-1))[0]
+    if diff.size:
+        t, j = divmod(int(diff[0]), 16)
+        lg = ref["sem_logits"][0, t] if j == 0 else ref["ac_logits"][0, t, j - 1]
+        assert top2_margin(lg) <= 0.05, f"streaming frame graph diverges at frame {t} code {j}"
+    print(f"tiny streaming frame graph: identical for {diff[0] if diff.size else got.size} of {got.size} codes")
+
+
+def test_bf16_streaming_text_teacher_forced_and_frame_graph(bf16_model):
+    """Streaming text on the bf16 models with the persistent kernels (the default path): 4 of 6 ids
+    in the prefill, text rows on frames 1 and 2, none after; then the frame graph free-running."""
+    name, model, w = bf16_model
+    ids = synth.random_ids(6, model.text_vocab, seed=32)
+    L, F = 4, 4
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((1, F, 16), np.float32), text_lookahead=L)
+    ref_free = orc.generate(ids, 8, GREEDY, GREEDY, np.zeros((1, 8, 16), np.float32), text_lookahead=L)
+    del orc
+    dec, dw = make_decoder(model, 1, 64, 16, w)
+    assert dec.exec_mode()[0] == tts.EXEC_PERSISTENT
+    print(f"{name} streaming: running", flush=True)
+    sem, ac, tok = stream_teacher_forced(dec, model, ids, L, ref["codes"], F)
+    assert dec.device_status() == 0
+    es, ea, n, ex = check_step_parity(model, ref, sem, ac, tok, 1e-2)
+    print(f"{name} streaming: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}", flush=True)
+    d = dev()
+    text = torch.from_numpy(ids.astype(np.int32)).to(d)
+    codes = torch.full((1, 16, 16), -1, dtype=torch.int32, device=d)
+    dec.set_text_stream(text, L)
+    dec.prefill(torch.from_numpy(np.ascontiguousarray(ids[:, :L])).to(d))
+    dec.run_frames(8, GREEDY, GREEDY, None, codes)
+    assert dec.device_status() == 0
+    got = codes.cpu().numpy()[:, :8].reshape(-1)
+    diff = np.nonzero(got != ref_free["codes"].reshape(-1))[0]
+    if diff.size:
+        t, j = divmod(int(diff[0]), 16)
+        lg = ref_free["sem_logits"][0, t] if j == 0 else ref_free["ac_logits"][0, t, j - 1]
+        assert top2_margin(lg) <= 0.05, f"{name}: streaming frame graph diverges at frame {t} code {j}"
+    print(f"{name} streaming frame graph: identical for {diff[0] if diff.size else got.size} of {got.size} codes")
     dec.close()
     del dw
     torch.cuda.empty_cache()

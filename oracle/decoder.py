@@ -27,6 +27,14 @@ Readings where the pages are silent (each is listed in the design notes):
     and the Talker step of frame t >= 1 adds the text row E_text[ids[:, L+t-1]]
     to the frame's embedding sum while L+t-1 < n; once the text is used up
     nothing is added. With L = n this is the non-streaming decode.
+  * Ragged batches and the per-stream stop (the method's next steps; the pages
+    name no scheme, and leave the stop unfinished): streams with prompts of
+    different lengths decode exactly as if each ran alone, from position 0;
+    with a designated semantic id eos, a stream whose drawn semantic token of
+    frame t is eos stops there: stop[b] = t, the frame's 15 acoustic codes are
+    reported as -1 and every later frame as 16 x -1. The drawn codes are what
+    the stream's own next steps consume either way (a stopped stream's later
+    output is discarded, so what it computes does not matter).
   * CodePredictor conditioning: positions restart at 0 every frame with an
     empty cache; position 0 holds P·h_T (h_T = the Talker's post-final-norm
     hidden of this frame), position 1 holds P·E_sem[s]; acoustic token j is
@@ -282,23 +290,35 @@ class OracleModel:
 
     def generate(self, ids: np.ndarray, frames: int, sem_sampling: dict, ac_sampling: dict,
                  uniforms: np.ndarray, teacher: np.ndarray | None = None, keep_logits: bool = True,
-                 keep_hidden: bool = False, sampler_dtype=np.float64, text_lookahead: int | None = None) -> dict:
+                 keep_hidden: bool = False, sampler_dtype=np.float64, text_lookahead: int | None = None,
+                 lengths=None, eos_id: int | None = None) -> dict:
         """Prefill then ``frames`` frames. uniforms: [B, >=frames, 16].
 
         teacher: [B, frames, 16] codes to feed forward instead of the drawn ones
         (teacher forcing); drawn tokens and logits are still reported.
         text_lookahead: streaming mode with that many text ids in the prefill, the rest
         fed one per frame (see the module docstring); None = all ids in the prefill.
+        lengths: per-stream prompt lengths (stream b's prompt is ids[b, :lengths[b]]); each
+        stream then runs on its own. eos_id: the per-stream stop (see the module docstring);
+        out["stop"] [B] holds each stream's stop frame or -1.
         """
         ids = np.asarray(ids)
         B = ids.shape[0]
+        if lengths is not None:
+            if text_lookahead is not None:
+                raise ValueError("lengths and text_lookahead do not combine")
+            parts = [self.generate(ids[b:b + 1, :int(lengths[b])], frames, sem_sampling, ac_sampling, uniforms[b:b + 1],
+                                   None if teacher is None else teacher[b:b + 1], keep_logits, keep_hidden, sampler_dtype,
+                                   eos_id=eos_id) for b in range(B)]
+            return {k: np.concatenate([q[k] for q in parts], axis=0) for k in parts[0]}
         L = ids.shape[1] if text_lookahead is None else int(text_lookahead)
         if not 1 <= L <= ids.shape[1]:
             raise ValueError("text_lookahead must lie in [1, n]")
         st = self.new_state(B, L + frames)
         logits = self.prefill(st, ids[:, :L])
         history = np.zeros((B, self.talker.vocab), dtype=bool)
-        codes = np.zeros((B, frames, 1 + self.n_ac), dtype=np.int32)
+        codes = np.zeros((B, frames, 1 + self.n_ac), dtype=np.int32)  # as drawn
+        stop = np.full(B, -1, dtype=np.int64)
         out = {"codes": codes}
         if keep_logits:
             out["sem_logits"] = np.zeros((B, frames, self.talker.vocab), dtype=self.dtype)
@@ -324,6 +344,18 @@ class OracleModel:
             codes[:, t, 1:] = a
             if keep_logits:
                 out["ac_logits"][:, t] = lg
+            if eos_id is not None:
+                for b in range(B):
+                    if stop[b] < 0 and codes[b, t, 0] == eos_id:
+                        stop[b] = t
+        if eos_id is not None:
+            shown = codes.copy()
+            for b in range(B):
+                if stop[b] >= 0:
+                    shown[b, stop[b], 1:] = -1
+                    shown[b, stop[b] + 1:] = -1
+            out["codes"] = shown
+            out["stop"] = stop
         return out
 
     # ------------------------------------------------------------------ brute force (no cache)

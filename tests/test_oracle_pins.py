@@ -145,6 +145,50 @@ def test_f1_text_row_is_one_hot_matmul_and_absent_past_the_text(tiny_weights, ti
     assert m.stream_text_ids(np.arange(8)[None], 3, 6)[0] == -1
 
 
+# ----------------------------------------------------------------------------- f2 stop + ragged
+
+def test_f2_stop_masks_only_the_reported_codes(tiny_weights, tiny_cfg):
+    """The stop id changes nothing the streams compute: drawn codes and logits equal the run
+    without it; the reported codes are masked from the first frame whose semantic token is the
+    stop id (its 15 acoustic codes, then whole frames)."""
+    m = OracleModel(tiny_weights, tiny_cfg, np.float64)
+    ids = np.concatenate([synth.random_ids(8, 1024, seed=s) for s in (41, 42, 43)])
+    u = np.zeros((3, 8, 16), np.float32)
+    free = m.generate(ids, 8, GREEDY, GREEDY, u)
+    eos = int(free["codes"][1, 3, 0])
+    out = m.generate(ids, 8, GREEDY, GREEDY, u, eos_id=eos)
+    np.testing.assert_array_equal(out["sem_logits"], free["sem_logits"])
+    np.testing.assert_array_equal(out["ac_logits"], free["ac_logits"])
+    for b in range(3):
+        hits = np.nonzero(free["codes"][b, :, 0] == eos)[0]
+        t = int(hits[0]) if hits.size else -1
+        assert out["stop"][b] == t
+        if t < 0:
+            np.testing.assert_array_equal(out["codes"][b], free["codes"][b])
+        else:
+            np.testing.assert_array_equal(out["codes"][b, :t], free["codes"][b, :t])
+            assert out["codes"][b, t, 0] == eos and (out["codes"][b, t, 1:] == -1).all()
+            assert (out["codes"][b, t + 1:] == -1).all()
+    assert out["stop"][1] <= 3
+
+
+def test_f2_ragged_streams_equal_the_lockstep_batch_when_lengths_agree(tiny_weights, tiny_cfg):
+    """Per-stream (ragged) decoding with equal lengths reproduces the lockstep batched decode, and
+    a shorter stream equals its own single-stream run on the truncated prompt."""
+    m = OracleModel(tiny_weights, tiny_cfg, np.float64)
+    ids = np.concatenate([synth.random_ids(9, 1024, seed=s) for s in (44, 45)])
+    u = synth.random_uniforms((2, 4, 16), seed=46)
+    batch = m.generate(ids, 4, GREEDY, GREEDY, u)
+    ragged = m.generate(ids, 4, GREEDY, GREEDY, u, lengths=[9, 9])
+    np.testing.assert_allclose(ragged["sem_logits"], batch["sem_logits"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(ragged["codes"], batch["codes"])
+    short = m.generate(ids, 4, GREEDY, GREEDY, u, lengths=[9, 5])
+    alone = m.generate(ids[1:, :5], 4, GREEDY, GREEDY, u[1:])
+    np.testing.assert_array_equal(short["sem_logits"][1], alone["sem_logits"][0])
+    with pytest.raises(ValueError):
+        m.generate(ids, 2, GREEDY, GREEDY, u, lengths=[9, 5], text_lookahead=3)
+
+
 # ----------------------------------------------------------------------------- P2 softmax
 
 @pytest.mark.parametrize("dtype,tol", [(np.float32, 1e-6), (np.float64, 1e-14)])

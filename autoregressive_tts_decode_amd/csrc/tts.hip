@@ -60,7 +60,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout, computed identically by tts_workspace_bytes and tts_create.
 struct Layout {
   size_t st, tk, tv, ck, cv, tcos, tsin, ccos, csin, x, qkv, attn, h, part, counters, logits, hT, cx, clog, next_tok,
-      sem_tok, ac_codes, history, cpdesc, tkdesc, px, pqkv, pq, po, pgu, ph, ps, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
+      sem_tok, ac_codes, history, kvstart, aids, cpdesc, tkdesc, px, pqkv, pq, po, pgu, ph, ps, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
   int nsplit;
 };
 
@@ -102,6 +102,8 @@ Layout make_layout(const tts_config& c) {
   L.sem_tok = take(B * 4);
   L.ac_codes = take(B * c.n_acoustic * 4);
   L.history = take(B * t.vocab);
+  L.kvstart = take(B * 4);
+  L.aids = take((size_t)B * cap * 4);
   // GEMM prefill: one chunk of up to kPrefillChunk positions per stream
   {
     const size_t Mp = B * kPrefillChunk;
@@ -245,6 +247,12 @@ struct tts_ctx {
   // streaming text of the frame loop (tts_set_text_stream): ids [B, text_n], borrowed
   const int32_t* text_ids = nullptr;
   int text_n = 0, text_next = 0;
+  // ragged prompts: per-stream first visible Talker position, right-aligned ids
+  int32_t *kvstart = nullptr, *aids = nullptr;
+  std::vector<int32_t> starts_host;  // source of the last start upload (kept alive for the copy)
+  // per-stream stop (tts_set_stop): eos id (-1: none) and the caller's stop-frame array
+  int eos_id = -1;
+  int32_t* stop = nullptr;
   // host mirror of the device counters
   bool prefilled = false;
   int batch = 0, pos = 0, frames = 0;
@@ -441,8 +449,10 @@ GemvArgs gemv_args(tts_ctx* ctx) {
 // One pass of a decoder stack over Mp new positions per stream (rows b*Mp+m
 // of x, hidden H). Position of row m: pos_const + m, or the device Talker
 // position when pos_from_state. KV caches [layers][B][nkv][cap][d].
+// kvstart: per-stream first visible cache position (ragged Talker prompts), or nullptr.
 int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_const, int pos_from_state, void* kc,
-               void* vc, int cap, int nsplit, const float* rc, const float* rs, bool nontemporal) {
+               void* vc, int cap, int nsplit, const float* rc, const float* rs, bool nontemporal,
+               const int32_t* kvstart = nullptr) {
   const tts_stack_cfg& c = S.c;
   const int rows = B * Mp;
   const int qd = c.n_q_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
@@ -471,6 +481,7 @@ int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_c
     t.kc = (char*)kc + l * layer_cache; t.vc = (char*)vc + l * layer_cache;
     t.cap = cap; t.chunk = nsplit == 1 ? cap : kAttnChunk; t.nsplit = nsplit;
     t.out = ctx->attn; t.out_stride = qd; t.part = ctx->part; t.counters = ctx->counters; t.st = ctx->st;
+    t.kvstart = kvstart;
     if (int rc_ = attention(ctx, t, B)) return rc_;
     // O projection + residual
     a = gemv_args(ctx);
@@ -553,6 +564,7 @@ int prefill_gemm(tts_ctx* ctx, const int32_t* ids, int B, int n) {
       std::memset(&pa, 0, sizeof pa);
       pa.q = Q; pa.kc = kc; pa.vc = vc; pa.out = O; pa.P = P; pa.p0 = p0; pa.nq = t.n_q_heads; pa.nkv = t.n_kv_heads;
       pa.cap = c.max_cache_steps;
+      pa.kvstart = ctx->kvstart;
       if (ctx->kv_bf16()) hipLaunchKernelGGL(k_prefill_attn<uint16_t>, dim3((P + 3) / 4, t.n_q_heads, B), dim3(256), 0, ctx->stream, pa);
       else hipLaunchKernelGGL(k_prefill_attn<float>, dim3((P + 3) / 4, t.n_q_heads, B), dim3(256), 0, ctx->stream, pa);
       HIP_LAUNCH_CHECK();
@@ -575,7 +587,7 @@ int prefill_gemm(tts_ctx* ctx, const int32_t* ids, int B, int n) {
 int talker_stack(tts_ctx* ctx, int B, int pos_const, int pos_from_state) {
   const auto& c = ctx->cfg;
   return stack_step(ctx, ctx->talker, ctx->x, B, 1, pos_const, pos_from_state, ctx->ws + ctx->L.tk, ctx->ws + ctx->L.tv,
-                    c.max_cache_steps, ctx->L.nsplit, ctx->tcos, ctx->tsin, true);
+                    c.max_cache_steps, ctx->L.nsplit, ctx->tcos, ctx->tsin, true, ctx->kvstart);
 }
 
 // Talker input from a frame's 16 codes (codebook t of stream b at tok refs).
@@ -776,6 +788,11 @@ int enqueue_frame(tts_ctx* ctx, const tts_sampling& sem, const tts_sampling& ac,
   // streaming text: the step on frame t's codes adds text id [b][next + t] while it exists
   const TokRef text = tokref(ctx->text_ids, ctx->text_n, 1, ctx->text_next, 1);
   if (int rc = embed_sum(ctx, B, refs, ctx->text_ids ? &text : nullptr, ctx->text_n)) return rc;
+  // per-stream stop: the next Talker input holds the codes as drawn; the reported codes are masked
+  if (ctx->eos_id >= 0) {
+    hipLaunchKernelGGL(k_eos_mask, dim3((B + 63) / 64), dim3(64), 0, ctx->stream, codes, fs, ctx->st, ctx->eos_id, ctx->stop, B);
+    HIP_LAUNCH_CHECK();
+  }
   // the frame's last kernel also advances the device position and frame counters
   if (use_xtk(ctx, B)) return talker_step_xtk(ctx, 1, 1);
   if (int rc = talker_stack(ctx, B, 0, 1)) return rc;
@@ -827,6 +844,8 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
   ctx->tcos = (float*)(w + L.tcos); ctx->tsin = (float*)(w + L.tsin); ctx->ccos = (float*)(w + L.ccos); ctx->csin = (float*)(w + L.csin);
   ctx->next_tok = (int32_t*)(w + L.next_tok); ctx->sem_tok = (int32_t*)(w + L.sem_tok); ctx->ac_codes = (int32_t*)(w + L.ac_codes);
   ctx->history = (uint8_t*)(w + L.history);
+  ctx->kvstart = (int32_t*)(w + L.kvstart);
+  ctx->aids = (int32_t*)(w + L.aids);
   ctx->cpdesc = (xtp::CpDesc*)(w + L.cpdesc);
   ctx->tkdesc = (xtp::TkDesc*)(w + L.tkdesc);
   ctx->xerr = (uint32_t*)(w + L.xerr);
@@ -968,17 +987,33 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
   return TTS_OK;
 }
 
-int tts_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, float* sem_logits) {
-  if (!ctx) return TTS_E_ARG;
-  if (!ctx->weights_ok) return ctx->fail(TTS_E_STATE, "prefill: weights not loaded");
-  if (!ids) return ctx->fail(TTS_E_ARG, "prefill: ids is NULL");
-  if (batch < 1 || batch > ctx->cfg.max_batch) return ctx->fail(TTS_E_ARG, "prefill: batch %d outside [1, %d]", batch, ctx->cfg.max_batch);
-  if (n < 1) return ctx->fail(TTS_E_ARG, "prefill: n must be >= 1");
-  if (n > ctx->cfg.max_cache_steps) return ctx->fail(TTS_E_CAPACITY, "prefill: %d positions exceed max_cache_steps %d", n, ctx->cfg.max_cache_steps);
+}  // extern "C"
+
+namespace {
+
+// The prompt pass of tts_prefill / tts_prefill_ragged after validation. starts: per-stream first
+// prompt position (host, B entries) or nullptr for all 0; with starts, ids are the caller's
+// left-aligned rows and are right-aligned into the workspace first.
+int prefill_body(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, const int32_t* starts, float* sem_logits) {
   const auto& c = ctx->cfg;
   drop_graph(ctx);
   hipLaunchKernelGGL(k_set_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, 0, 0);
   HIP_LAUNCH_CHECK();
+  if (starts) {
+    ctx->starts_host.assign(starts, starts + batch);
+    HIP_TRY(hipMemcpyAsync(ctx->kvstart, ctx->starts_host.data(), (size_t)batch * 4, hipMemcpyHostToDevice, ctx->stream));
+    hipLaunchKernelGGL(k_align_ids, dim3(std::min((batch * n + 255) / 256, 1024)), dim3(256), 0, ctx->stream, ids, n, ctx->kvstart,
+                       batch, ctx->aids);
+    HIP_LAUNCH_CHECK();
+    ids = ctx->aids;
+  } else {
+    hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, ctx->stream, ctx->kvstart, batch, 0);
+    HIP_LAUNCH_CHECK();
+  }
+  if (ctx->stop) {
+    hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, ctx->stream, ctx->stop, c.max_batch, -1);
+    HIP_LAUNCH_CHECK();
+  }
   hipLaunchKernelGGL(k_fill_u8, dim3(64), dim3(256), 0, ctx->stream, ctx->history, (size_t)batch * c.talker.vocab, (uint8_t)0);
   HIP_LAUNCH_CHECK();
   if (ctx->pgemm_ok && ctx->prefill_mode == TTS_PREFILL_GEMM) {
@@ -1000,6 +1035,54 @@ int tts_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, floa
   ctx->pos = n;
   ctx->frames = 0;
   ctx->prefilled = true;
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+int check_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n) {
+  if (!ctx->weights_ok) return ctx->fail(TTS_E_STATE, "prefill: weights not loaded");
+  if (!ids) return ctx->fail(TTS_E_ARG, "prefill: ids is NULL");
+  if (batch < 1 || batch > ctx->cfg.max_batch) return ctx->fail(TTS_E_ARG, "prefill: batch %d outside [1, %d]", batch, ctx->cfg.max_batch);
+  if (n < 1) return ctx->fail(TTS_E_ARG, "prefill: n must be >= 1");
+  if (n > ctx->cfg.max_cache_steps) return ctx->fail(TTS_E_CAPACITY, "prefill: %d positions exceed max_cache_steps %d", n, ctx->cfg.max_cache_steps);
+  return TTS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tts_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, float* sem_logits) {
+  if (!ctx) return TTS_E_ARG;
+  if (int rc = check_prefill(ctx, ids, batch, n)) return rc;
+  return prefill_body(ctx, ids, batch, n, nullptr, sem_logits);
+}
+
+int tts_prefill_ragged(tts_ctx* ctx, const int32_t* ids, const int32_t* lengths, int32_t batch, int32_t n, float* sem_logits) {
+  if (!ctx) return TTS_E_ARG;
+  if (!lengths) return ctx->fail(TTS_E_ARG, "prefill_ragged: lengths is NULL");
+  if (int rc = check_prefill(ctx, ids, batch, n)) return rc;
+  std::vector<int32_t> starts(batch);
+  for (int b = 0; b < batch; ++b) {
+    if (lengths[b] < 1 || lengths[b] > n) return ctx->fail(TTS_E_SHAPE, "prefill_ragged: lengths[%d] = %d outside [1, %d]", b, lengths[b], n);
+    starts[b] = n - lengths[b];
+  }
+  // one stream needs no padding: its prompt is simply shorter
+  if (batch == 1) return prefill_body(ctx, ids, 1, lengths[0], nullptr, sem_logits);
+  return prefill_body(ctx, ids, batch, n, starts.data(), sem_logits);
+}
+
+int tts_set_stop(tts_ctx* ctx, int32_t eos_id, int32_t* stop_frames) {
+  if (!ctx) return TTS_E_ARG;
+  if (eos_id >= ctx->cfg.talker.vocab) return ctx->fail(TTS_E_ARG, "set_stop: eos_id %d outside the semantic vocabulary", eos_id);
+  if (eos_id >= 0 && !stop_frames) return ctx->fail(TTS_E_ARG, "set_stop: stop_frames is NULL");
+  drop_graph(ctx);  // the frame graph holds the stop kernel (or its absence)
+  ctx->eos_id = eos_id < 0 ? -1 : eos_id;
+  ctx->stop = eos_id < 0 ? nullptr : stop_frames;
+  if (ctx->stop) {
+    hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, ctx->stream, ctx->stop, ctx->cfg.max_batch, -1);
+    HIP_LAUNCH_CHECK();
+  }
   ctx->err.clear();
   return TTS_OK;
 }

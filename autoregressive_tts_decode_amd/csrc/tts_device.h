@@ -409,6 +409,7 @@ struct AttnArgs {
   float* part;              // nsplit > 1: [rows][nq][nsplit][d + 2] = (o[d], m, l)
   int32_t* counters;        // nsplit > 1: [B][nkv] arrival counters, zero between uses
   const DevState* st;
+  const int32_t* kvstart;   // [B] first visible cache position of each stream (ragged prompts), or nullptr (0)
 };
 
 // Cache element loads of EPL contiguous elements into floats.
@@ -456,6 +457,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int s1 = min(s0 + a.chunk, plast + 1);
   const int used = min(a.nsplit, plast / a.chunk + 1);
   const int row0 = b * M;
+  const int st0 = a.kvstart ? a.kvstart[b] : 0;  // positions before it are another stream's padding
 
   __shared__ float qs[M][G][D];
   KT* kcache = reinterpret_cast<KT*>(a.kc) + ((size_t)b * a.nkv + g) * a.cap * D;
@@ -533,7 +535,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     load_row<EPL>(vcache + (size_t)t * D + gl16 * EPL, vf);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const bool visible = t <= p0 + m;
+      const bool visible = t <= p0 + m && t >= st0;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float s = 0.f;
@@ -760,6 +762,39 @@ __global__ void k_set_state(DevState* st, int pos, int frame) {
 }
 __global__ void k_fill_u8(uint8_t* p, size_t n, uint8_t v) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// Per-stream stop on a designated semantic id (row f2 of the method's next steps; the pages leave
+// the stop unfinished). Frame t of stream b, after its codes are written and consumed by the next
+// Talker input: if the stream is running and its semantic token is eos, the stream stops at frame
+// t (stop[b] = t) and the frame's 15 acoustic codes are masked to -1; a stream stopped at an
+// earlier frame gets all 16 codes of frame t masked. The decode itself runs on in lockstep.
+__global__ void k_eos_mask(int32_t* codes, int b_stride, const DevState* st, int eos, int32_t* stop, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int t = st->frame;
+  int32_t* c = codes + (size_t)b * b_stride + (size_t)t * 16;
+  if (stop[b] < 0) {
+    if (c[0] == eos) {
+      stop[b] = t;
+      for (int j = 1; j < 16; ++j) c[j] = -1;
+    }
+  } else if (t > stop[b]) {
+    for (int j = 0; j < 16; ++j) c[j] = -1;
+  }
+}
+
+__global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
+}
+
+// Ragged prompts, right-aligned: out[b][p] = ids[b][p - start[b]] for p >= start[b], else 0 (a
+// padding id whose positions every attention masks).
+__global__ void k_align_ids(const int32_t* ids, int n, const int32_t* start, int B, int32_t* out) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < B * n; i += gridDim.x * blockDim.x) {
+    const int b = i / n, p = i % n, s = start[b];
+    out[i] = p >= s ? ids[(size_t)b * n + p - s] : 0;
+  }
 }
 
 }  // namespace tts

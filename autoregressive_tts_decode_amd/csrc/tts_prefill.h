@@ -190,6 +190,7 @@ struct PAttnArgs {
   const void *kc, *vc;
   float* out;         // [M, nq d]
   int P, p0, nq, nkv, cap;
+  const int32_t* kvstart;  // [B] first visible position of each stream (ragged prompts), or nullptr (0)
 };
 
 // Causal attention of prefill rows: one wave per (row i of stream b, q head h) over cached
@@ -209,7 +210,9 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PAttnArgs a) {
   for (int k = 0; k < 32; ++k) qv[k] = q[32 * e + k];
   const float scale = 1.0f / sqrtf((float)d);
   float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int base = 0; base <= pos; base += 16) {
+  // positions before the stream's start are padding (a row of the padding itself attends to
+  // nothing and gives 0)
+  for (int base = a.kvstart ? a.kvstart[b] : 0; base <= pos; base += 16) {
     const int t = base + tq;
     const bool valid = t <= pos;
     const KT* kr = kc + (size_t)(valid ? t : 0) * d + 32 * e;
@@ -240,8 +243,8 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PAttnArgs a) {
     }
   }
   float* o = a.out + (size_t)row * a.nq * d + (size_t)h * d;
-  o[lane] = o0 / l;
-  o[lane + 64] = o1 / l;
+  o[lane] = l > 0.f ? o0 / l : 0.f;
+  o[lane + 64] = l > 0.f ? o1 / l : 0.f;
 }
 
 // h[m, f] = silu(gu[m, f]) * gu[m, F + f]

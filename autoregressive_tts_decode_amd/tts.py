@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "TTS_OK", -1: "TTS_E_ARG", -2: "TTS_E_SHAPE", -3: "TTS_E_CAPA
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 EXPORTED = ["tts_workspace_bytes", "tts_create", "tts_load_weights", "tts_prefill", "tts_talker_step",
-            "tts_talker_step_text", "tts_set_text_stream", "tts_codepred_frame", "tts_sample", "tts_run_frames", "tts_set_exec_mode", "tts_get_exec_mode", "tts_set_prefill_mode", "tts_get_prefill_mode",
+            "tts_talker_step_text", "tts_set_text_stream", "tts_prefill_ragged", "tts_set_stop", "tts_codepred_frame", "tts_sample", "tts_run_frames", "tts_set_exec_mode", "tts_get_exec_mode", "tts_set_prefill_mode", "tts_get_prefill_mode",
             "tts_device_status", "tts_get_progress", "tts_reset", "tts_last_error", "tts_destroy"]
 EXEC_KERNELS, EXEC_PERSISTENT = 0, 1
 PERSISTENT_CODEPRED, PERSISTENT_TALKER = 1, 2  # bits of exec_mode()[1]
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tts_talker_step.argtypes = [P, P, P]
     lib.tts_talker_step_text.argtypes = [P, P, P, P]
     lib.tts_set_text_stream.argtypes = [P, P, I32, I32]
+    lib.tts_prefill_ragged.argtypes = [P, P, ctypes.POINTER(I32), I32, I32, P]
+    lib.tts_set_stop.argtypes = [P, I32, P]
     lib.tts_codepred_frame.argtypes = [P, P, ctypes.POINTER(SamplingC), P, P, P, P]
     lib.tts_sample.argtypes = [P, P, I32, I32, ctypes.POINTER(SamplingC), P, P, P]
     lib.tts_run_frames.argtypes = [P, I32, ctypes.POINTER(SamplingC), ctypes.POINTER(SamplingC), P, P]
@@ -204,6 +206,18 @@ class TTSDecoder:
     def prefill(self, ids, sem_logits=None):
         B, n = ids.shape
         self._check(self.lib.tts_prefill(self.ctx, _ptr(ids), B, n, _ptr(sem_logits)), "tts_prefill")
+
+    def prefill_ragged(self, ids, lengths, sem_logits=None):
+        """Prefill of prompts of different lengths: ids [B, n] (stream b's prompt is its first
+        lengths[b] ids), lengths a host sequence of B ints in [1, n]."""
+        B, n = ids.shape
+        arr = (ctypes.c_int32 * B)(*[int(x) for x in lengths])
+        self._check(self.lib.tts_prefill_ragged(self.ctx, _ptr(ids), arr, B, n, _ptr(sem_logits)), "tts_prefill_ragged")
+
+    def set_stop(self, eos_id: int, stop_frames=None):
+        """Per-stream stop on semantic id eos_id (-1: off); stop_frames: int32 device tensor of
+        max_batch entries receiving each stream's stop frame (-1 while it runs)."""
+        self._check(self.lib.tts_set_stop(self.ctx, int(eos_id), _ptr(stop_frames)), "tts_set_stop")
 
     def talker_step(self, prev_codes, sem_logits=None, text_ids=None):
         """One Talker step on the previous frame's codes [B, 16]; text_ids [B] (int32, -1 = none)

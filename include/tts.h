@@ -113,6 +113,33 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
  * [B, Vs] receives those logits when non-NULL. */
 int tts_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, float* sem_logits);
 
+/* tts_prefill for prompts of different lengths (ragged batch; row f2 of the
+ * method's next steps: per-stream lengths in batched attention). ids [B, n]
+ * (device): stream b's prompt is ids[b][0 .. lengths[b]), the rest of the row
+ * is ignored. lengths: HOST array of B entries in [1, n]. With B > 1 the
+ * prompts are right-aligned at positions n - lengths[b] .. n - 1 and every
+ * Talker attention masks the positions before a stream's start; queries and
+ * keys then differ from a prompt placed at position 0 only by a common
+ * rotation, which leaves their products unchanged ("Running Qwen3-TTS on an
+ * AMD R9700" fixes no positional scheme; rotate-half RoPE depends on position
+ * differences only), so each stream decodes as if alone up to rounding. One
+ * stream is simply a prompt of lengths[0] ids. TTS_E_SHAPE for a length
+ * outside [1, n]; otherwise as tts_prefill. */
+int tts_prefill_ragged(tts_ctx* ctx, const int32_t* ids, const int32_t* lengths, int32_t batch, int32_t n,
+                       float* sem_logits);
+
+/* Per-stream stop on a designated semantic id for tts_run_frames (row f2 of
+ * the method's next steps; the pages leave the stop unfinished). eos_id in
+ * [0, Vs), or -1 to switch it off. stop_frames: device int32 array of
+ * max_batch entries, borrowed: set to -1 here and by every prefill; when
+ * stream b draws eos_id as the semantic token of frame t, stop_frames[b] = t,
+ * the frame's 15 acoustic codes are written as -1, and every later frame of
+ * the stream is written as 16 x -1. The batch keeps decoding in lockstep (a
+ * stopped stream's work continues and is discarded), so the caller may stop
+ * calling tts_run_frames once every stream has stopped. Changing the setting
+ * drops the captured frame graph. */
+int tts_set_stop(tts_ctx* ctx, int32_t eos_id, int32_t* stop_frames);
+
 /* One Talker step fed with the previous frame's codes [B, 16]: the input is
  * E_sem[c0] + sum_j E_ac[j][cj]. Advances the Talker position by one and
  * replaces the pending output; sem_logits [B, Vs] receives it when non-NULL. */

@@ -41,8 +41,9 @@ def make_decoder(model, batch, cap, frames, weights):
     return dec, dw
 
 
-def teacher_forced(dec, model, ids, ref_codes, frames, logits_out=True):
-    """GPU prefill + per-frame CodePredictor (forced) + Talker step on the oracle's codes."""
+def teacher_forced(dec, model, ids, ref_codes, frames, logits_out=True, lengths=None):
+    """GPU prefill (ragged when lengths is given) + per-frame CodePredictor (forced) + Talker step
+    on the oracle's codes."""
     d = dev()
     B = ids.shape[0]
     Vs, Va = model.talker.vocab, model.codepred.vocab
@@ -53,7 +54,10 @@ def teacher_forced(dec, model, ids, ref_codes, frames, logits_out=True):
     rows = [codes[:, t].contiguous() for t in range(frames)]
     sems = [codes[:, t, 0].contiguous() for t in range(frames)]
     forced = [codes[:, t, 1:].contiguous() for t in range(frames)]
-    dec.prefill(torch.from_numpy(ids).to(d), sem[0])
+    if lengths is None:
+        dec.prefill(torch.from_numpy(ids).to(d), sem[0])
+    else:
+        dec.prefill_ragged(torch.from_numpy(np.ascontiguousarray(ids)).to(d), lengths, sem[0])
     for t in range(frames):
         if t > 0:
             dec.talker_step(rows[t - 1], sem[t])
@@ -459,6 +463,118 @@ def test_bf16_streaming_text_teacher_forced_and_frame_graph(bf16_model):
     dec.close()
     del dw
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- ragged prompts, stop id
+
+def _first_divergence_is_a_near_tie(got, ref, tag):
+    diff = np.nonzero(got.reshape(-1) != ref["codes"].reshape(-1))[0]
+    if diff.size:
+        b, rest = divmod(int(diff[0]), ref["codes"].shape[1] * 16)
+        t, j = divmod(rest, 16)
+        lg = ref["sem_logits"][b, t] if j == 0 else ref["ac_logits"][b, t, j - 1]
+        assert top2_margin(lg) <= 0.05, f"{tag}: divergence at stream {b} frame {t} code {j}, margin {top2_margin(lg):.3f}"
+    return diff[0] if diff.size else got.size
+
+
+def test_tiny_ragged_prompts_teacher_forced():
+    """Three streams with prompts of 12, 7 and 1 ids in one lockstep batch: each must decode as the
+    oracle's stream decoding alone from position 0."""
+    model = config.TINY
+    w = synth.make_weights(model, 0)
+    orc = OracleModel(w, model.as_dict(), np.float64)
+    ids = np.concatenate([synth.random_ids(12, model.text_vocab, seed=s) for s in (51, 52, 53)])
+    lengths, F = [12, 7, 1], 6
+    u = synth.random_uniforms((3, F, 16), seed=54)
+    ref = orc.generate(ids, F, GREEDY, GREEDY, u, lengths=lengths)
+    dec, dw = make_decoder(model, 3, 12 + F + 4, F + 4, w)
+    sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F, lengths=lengths)
+    es, ea, n, ex = check_step_parity(model, ref, sem, ac, tok, 1e-4)
+    print(f"tiny ragged: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}")
+    dec.close()
+
+
+@pytest.mark.parametrize("prefill", ["gemm", "steps"])
+def test_0p6b_ragged_prompts_teacher_forced(prefill):
+    model = config.MODELS["0.6b"]
+    w = synth.make_weights(model, 0)
+    ids = np.concatenate([synth.random_ids(16, model.text_vocab, seed=s) for s in (55, 56, 57)])
+    lengths, F = [16, 9, 4], 3
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((3, F, 16), np.float32), lengths=lengths)
+    del orc
+    dec, dw = make_decoder(model, 3, 64, 8, w)
+    dec.set_prefill_mode(tts.PREFILL_GEMM if prefill == "gemm" else tts.PREFILL_STEPS)
+    print(f"0.6b ragged {prefill}: running", flush=True)
+    sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F, lengths=lengths)
+    es, ea, n, ex = check_step_parity(model, ref, sem, ac, tok, 1e-2)
+    print(f"0.6b ragged {prefill}: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}")
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
+def test_tiny_stop_id_in_the_frame_graph():
+    """Greedy frame graph with a stop id that stream 1 draws at frame 3: stop frames and masked
+    codes equal the oracle's, the other streams run on."""
+    model = config.TINY
+    w = synth.make_weights(model, 0)
+    orc = OracleModel(w, model.as_dict(), np.float64)
+    ids = np.concatenate([synth.random_ids(10, model.text_vocab, seed=s) for s in (61, 62, 63)])
+    F = 10
+    u = np.zeros((3, F, 16), np.float32)
+    free = orc.generate(ids, F, GREEDY, GREEDY, u)
+    eos = int(free["codes"][1, 3, 0])
+    ref = orc.generate(ids, F, GREEDY, GREEDY, u, eos_id=eos)
+    assert ref["stop"][1] >= 0
+    d = dev()
+    dec, dw = make_decoder(model, 3, 10 + F + 4, F + 4, w)
+    stop = torch.full((dec_max_batch(dec),), 7, dtype=torch.int32, device=d)
+    dec.set_stop(eos, stop)
+    codes = torch.full((3, F + 4, 16), -7, dtype=torch.int32, device=d)
+    dec.prefill(torch.from_numpy(ids).to(d))
+    dec.run_frames(F, GREEDY, GREEDY, None, codes)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy()[:, :F]
+    k = _first_divergence_is_a_near_tie(got, ref, "tiny stop")
+    if k == got.size:
+        np.testing.assert_array_equal(stop.cpu().numpy()[:3], ref["stop"])
+    print(f"tiny stop id {eos}: stop frames {stop.cpu().numpy()[:3]} (oracle {ref['stop']}), identical for {k} of {got.size} codes")
+    dec.set_stop(-1)
+    dec.close()
+
+
+def test_0p6b_stop_id_with_the_persistent_kernels():
+    model = config.MODELS["0.6b"]
+    w = synth.make_weights(model, 0)
+    ids = synth.random_ids(12, model.text_vocab, seed=64)
+    F = 8
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    free = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((1, F, 16), np.float32))
+    eos = int(free["codes"][0, 4, 0])
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((1, F, 16), np.float32), eos_id=eos)
+    del orc
+    d = dev()
+    dec, dw = make_decoder(model, 1, 64, 16, w)
+    assert dec.exec_mode()[0] == tts.EXEC_PERSISTENT
+    stop = torch.full((dec_max_batch(dec),), 7, dtype=torch.int32, device=d)
+    dec.set_stop(eos, stop)
+    codes = torch.full((1, 16, 16), -7, dtype=torch.int32, device=d)
+    dec.prefill(torch.from_numpy(ids).to(d))
+    dec.run_frames(F, GREEDY, GREEDY, None, codes)
+    assert dec.device_status() == 0
+    got = codes.cpu().numpy()[:, :F]
+    k = _first_divergence_is_a_near_tie(got, ref, "0.6b stop")
+    if k == got.size:
+        assert int(stop.cpu().numpy()[0]) == int(ref["stop"][0])
+    print(f"0.6b stop id {eos}: stop frame {int(stop.cpu().numpy()[0])} (oracle {int(ref['stop'][0])}), identical for {k} of {got.size} codes")
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
+def dec_max_batch(dec):
+    return dec.max_batch
 
 
 def test_1p7b_long_context_logits_at_2255_positions():

@@ -31,6 +31,7 @@ namespace {
 constexpr int kCpPositions = 16;   // CodePredictor positions 0..15 per frame
 constexpr int kAttnChunk = 32;     // Talker positions per attention split
 constexpr int kMaxGemvM = 8;       // input rows per GEMV launch
+constexpr int kGemmMinRows = 16;   // batched projections with at least this many rows run as MFMA GEMMs
 constexpr int kGemvXRegs = 96;     // per-lane registers a GEMV spends on its input rows (M * U * E)
 
 struct Layer {
@@ -387,6 +388,65 @@ int gemv(tts_ctx* ctx, GemvArgs a) {
   return TTS_OK;
 }
 
+// A projection of M >= kGemmMinRows rows (batched decode) as one MFMA GEMM instead of GEMV
+// launches of at most kMaxGemvM rows: the GEMV keeps its input rows in registers, so at large K it
+// takes 2 rows per launch and re-streams the weights for every pair, while the GEMM reads each
+// weight tile once per 64 rows. Same operands and epilogues as the GEMV (RMSNorm via a row scale
+// and the gain applied while A is loaded; the residual as C += result; SwiGLU through a staging
+// buffer; gathered input rows staged first). Needs bf16 weights and 64-multiple row segments.
+int gather(tts_ctx* ctx, int src, int M, int H, const float* vec, int vec_stride, const void* table, int table_rows, TokRef tok,
+           float* out, int out_stride);
+
+bool gemm_routes(const tts_ctx* ctx, const GemvArgs& a) {
+  if (!ctx->pgemm_ok || !ctx->bf16() || a.M < kGemmMinRows || a.K % kGBK) return false;
+  for (int s = 0; s < a.nseg; ++s)
+    if (a.seg_rows[s] % kGBN) return false;
+  if (a.epi == EPI_RESID && (a.res != a.y || a.res_stride != a.y_stride)) return false;
+  if (a.epi == EPI_SWIGLU && (a.nseg != 2 || a.y_stride != a.N)) return false;
+  return a.M <= ctx->cfg.max_batch * kPrefillChunk;  // the staging buffers' rows
+}
+
+int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
+  char* w = ctx->ws;
+  float *X = (float*)(w + ctx->L.px), *GU = (float*)(w + ctx->L.pgu), *RS = (float*)(w + ctx->L.ps);
+  const float* A = a.x;
+  int lda = a.x_stride;
+  if (a.src != SRC_VEC) {
+    if (int rc = gather(ctx, a.src, a.M, a.K, a.x, a.x_stride, a.table, a.table_rows, a.tok, X, a.K)) return rc;
+    A = X;
+    lda = a.K;
+  }
+  if (a.gain) {
+    hipLaunchKernelGGL(k_rowscale, dim3((a.M + 3) / 4), dim3(256), 0, ctx->stream, A, lda, a.M, a.K, ctx->cfg.rms_eps, RS);
+    HIP_LAUNCH_CHECK();
+    if (a.xn_out) {
+      hipLaunchKernelGGL(k_norm_rows<uint16_t>, dim3(a.M), dim3(256), 0, ctx->stream, A, lda, RS, a.gain, a.K, a.xn_out, a.xn_stride);
+      HIP_LAUNCH_CHECK();
+    }
+  }
+  GemmArgs g;
+  std::memset(&g, 0, sizeof g);
+  g.A = A; g.lda = lda; g.rs = a.gain ? RS : nullptr; g.gain = a.gain; g.M = a.M; g.K = a.K;
+  int N = 0;
+  for (int s = 0; s < a.nseg; ++s) { g.w[s] = a.w[s]; g.seg_rows[s] = a.seg_rows[s]; N += a.seg_rows[s]; }
+  g.nseg = a.nseg; g.N = N;
+  if (a.epi == EPI_SWIGLU) { g.C = GU; g.ldc = N; g.add = 0; }
+  else { g.C = a.y; g.ldc = a.y_stride; g.add = a.epi == EPI_RESID ? 1 : 0; }
+  hipLaunchKernelGGL(k_gemm_bf16, dim3(N / kGBN, (a.M + kGBM - 1) / kGBM), dim3(256), 0, ctx->stream, g);
+  HIP_LAUNCH_CHECK();
+  if (a.epi == EPI_SWIGLU) {
+    hipLaunchKernelGGL(k_swiglu_rows, dim3(std::min((a.M * a.N + 255) / 256, 4096)), dim3(256), 0, ctx->stream, GU, a.M, a.N, a.y);
+    HIP_LAUNCH_CHECK();
+  }
+  if (a.bump_pos || a.bump_frame) {
+    hipLaunchKernelGGL(k_bump_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, a.bump_pos, a.bump_frame);
+    HIP_LAUNCH_CHECK();
+  }
+  return TTS_OK;
+}
+
+int proj(tts_ctx* ctx, GemvArgs a) { return gemm_routes(ctx, a) ? proj_gemm(ctx, a) : gemv(ctx, a); }
+
 // ---------------------------------------------------------------------------- attention dispatch
 
 template <typename WT, typename KT, int G, int M, int D>
@@ -469,7 +529,7 @@ int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_c
     a.src = SRC_VEC; a.x = x; a.x_stride = c.hidden;
     a.gain = W.attn_norm;
     a.y = ctx->qkv; a.y_stride = qkv_n; a.epi = EPI_STORE; a.nontemporal = nontemporal;
-    if (int rc_ = gemv(ctx, a)) return rc_;
+    if (int rc_ = proj(ctx, a)) return rc_;
     // q/k norm + RoPE + KV append + attention
     AttnArgs t;
     std::memset(&t, 0, sizeof t);
@@ -488,20 +548,20 @@ int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_c
     a.w[0] = W.wo; a.seg_rows[0] = c.hidden; a.N = c.hidden; a.K = qd; a.M = rows;
     a.src = SRC_VEC; a.x = ctx->attn; a.x_stride = qd;
     a.y = x; a.y_stride = c.hidden; a.res = x; a.res_stride = c.hidden; a.epi = EPI_RESID; a.nontemporal = nontemporal;
-    if (int rc_ = gemv(ctx, a)) return rc_;
+    if (int rc_ = proj(ctx, a)) return rc_;
     // RMSNorm + gate/up + SwiGLU
     a = gemv_args(ctx);
     a.w[0] = W.wg; a.w[1] = W.wu; a.seg_rows[0] = c.ffn; a.seg_rows[1] = c.ffn; a.nseg = 2;
     a.N = c.ffn; a.K = c.hidden; a.M = rows;
     a.src = SRC_VEC; a.x = x; a.x_stride = c.hidden; a.gain = W.mlp_norm;
     a.y = ctx->h; a.y_stride = c.ffn; a.epi = EPI_SWIGLU; a.nontemporal = nontemporal;
-    if (int rc_ = gemv(ctx, a)) return rc_;
+    if (int rc_ = proj(ctx, a)) return rc_;
     // down projection + residual
     a = gemv_args(ctx);
     a.w[0] = W.wd; a.seg_rows[0] = c.hidden; a.N = c.hidden; a.K = c.ffn; a.M = rows;
     a.src = SRC_VEC; a.x = ctx->h; a.x_stride = c.ffn;
     a.y = x; a.y_stride = c.hidden; a.res = x; a.res_stride = c.hidden; a.epi = EPI_RESID; a.nontemporal = nontemporal;
-    if (int rc_ = gemv(ctx, a)) return rc_;
+    if (int rc_ = proj(ctx, a)) return rc_;
   }
   return TTS_OK;
 }
@@ -516,7 +576,7 @@ int talker_head(tts_ctx* ctx, int B, int bump_pos, int bump_frame) {
   a.src = SRC_VEC; a.x = ctx->x; a.x_stride = t.hidden; a.gain = ctx->talker.final_norm;
   a.y = ctx->logits; a.y_stride = t.vocab; a.epi = EPI_STORE;
   a.xn_out = ctx->hT; a.xn_stride = t.hidden; a.nontemporal = 1;
-  return gemv(ctx, a);
+  return proj(ctx, a);
 }
 
 // Talker prompt pass as GEMMs: chunks of up to kPrefillChunk positions per stream, M = B x chunk
@@ -705,7 +765,7 @@ int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac,
         a.src = SRC_VEC_THEN_TABLE; a.x = ctx->hT; a.x_stride = Ht; a.table = ctx->embed_sem; a.table_rows = c.talker.vocab;
         a.tok = semantic;
         a.y = ctx->cx; a.y_stride = Hc; a.epi = EPI_STORE;
-        if (int rc = gemv(ctx, a)) return rc;
+        if (int rc = proj(ctx, a)) return rc;
       } else if (int rc = gather(ctx, SRC_VEC_THEN_TABLE, 2 * B, Hc, ctx->hT, Ht, ctx->embed_sem, c.talker.vocab, semantic, ctx->cx,
                                  Hc)) {
         return rc;
@@ -718,7 +778,7 @@ int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac,
         a.w[0] = ctx->proj; a.seg_rows[0] = Hc; a.N = Hc; a.K = Ht; a.M = B;
         a.src = SRC_TABLE; a.table = table; a.table_rows = Va; a.tok = prev;
         a.y = ctx->cx; a.y_stride = Hc; a.epi = EPI_STORE;
-        if (int rc = gemv(ctx, a)) return rc;
+        if (int rc = proj(ctx, a)) return rc;
       } else if (int rc = gather(ctx, SRC_TABLE, B, Hc, nullptr, 0, table, Va, prev, ctx->cx, Hc)) {
         return rc;
       }
@@ -732,7 +792,7 @@ int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac,
     a.src = SRC_VEC; a.x = ctx->cx + (size_t)(Mp - 1) * Hc; a.x_stride = Mp * Hc; a.gain = ctx->cp.final_norm;
     float* lg = logits_out ? logits_out + (size_t)(j - 1) * Va : ctx->clog;
     a.y = lg; a.y_stride = logits_out ? c.n_acoustic * Va : Va; a.epi = EPI_STORE;
-    if (int rc = gemv(ctx, a)) return rc;
+    if (int rc = proj(ctx, a)) return rc;
     URef uj = u;
     uj.offset += j - 1;
     if (int rc = sample(ctx, lg, a.y_stride, B, Va, ac, uj, nullptr, 0, 0, out, ob, of, oo + j - 1, ouf, ctx->next_tok, forced,

@@ -2,9 +2,11 @@
 // the matrix cores ("Running Qwen3-TTS on an AMD R9700", section "Running Qwen3-TTS": the prompt
 // pass before the frame loop). Positions are processed in chunks of at most kPrefillChunk per
 // stream, M = B x chunk rows per GEMM; causal attention of a chunk reads the KV cache, which holds
-// every earlier position. Activations stay fp32: each GEMM splits its fp32 input a into bf16
-// hi = bf16(a) and lo = bf16(a - hi) and accumulates W hi + W lo in fp32 (W is bf16 already), so
-// the product keeps about 16 mantissa bits of a.
+// every earlier position. The same GEMM serves batched decode steps (many streams' rows).
+// Activations stay fp32: each GEMM splits its fp32 input a into three bf16 parts, hi = bf16(a),
+// mid = bf16(a - hi), lo = bf16(a - hi - mid), whose sum is a exactly for normal values (each
+// remainder is exact in fp32 and the last fits 8 mantissa bits), and accumulates W hi + W mid +
+// W lo in fp32 (W is bf16 already): the product is the fp32 one up to accumulation order.
 #pragma once
 
 #include "tts_device.h"
@@ -36,6 +38,7 @@ constexpr int kGBM = 64, kGBN = 64, kGBK = 64, kGLD = kGBK + 8;  // tile, LDS ro
 // One 64 x 64 tile of C per workgroup (4 waves, each 32 x 32 = 2 x 2 MFMA 16x16x32 blocks).
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
   __shared__ __align__(16) __bf16 Ahi[kGBM][kGLD];
+  __shared__ __align__(16) __bf16 Amid[kGBM][kGLD];
   __shared__ __align__(16) __bf16 Alo[kGBM][kGLD];
   __shared__ __align__(16) __bf16 Bs[kGBN][kGLD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -83,18 +86,22 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const __bf16 hi = (__bf16)av[e];
+      const float r1 = av[e] - (float)hi;
+      const __bf16 mid = (__bf16)r1;
       Ahi[lr][lk + e] = hi;
-      Alo[lr][lk + e] = (__bf16)(av[e] - (float)hi);
+      Amid[lr][lk + e] = mid;
+      Alo[lr][lk + e] = (__bf16)(r1 - (float)mid);
     }
     *reinterpret_cast<u32x4*>(&Bs[lr][lk]) = b0;
     *reinterpret_cast<u32x4*>(&Bs[lr][lk + 8]) = b1;
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < kGBK; kk += 32) {
-      bf16x8 ah[2], al[2], bw[2];
+      bf16x8 ah[2], am[2], al[2], bw[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         ah[i] = *reinterpret_cast<const bf16x8*>(&Ahi[wm * 32 + i * 16 + lc][kk + 8 * lq]);
+        am[i] = *reinterpret_cast<const bf16x8*>(&Amid[wm * 32 + i * 16 + lc][kk + 8 * lq]);
         al[i] = *reinterpret_cast<const bf16x8*>(&Alo[wm * 32 + i * 16 + lc][kk + 8 * lq]);
         bw[i] = *reinterpret_cast<const bf16x8*>(&Bs[wn * 32 + i * 16 + lc][kk + 8 * lq]);
       }
@@ -102,8 +109,10 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
+          // smallest part first, so the large products are added to the small ones' sum
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[i], bw[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(am[i], bw[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[i], bw[j], acc[i][j], 0, 0, 0);
         }
     }
   }
@@ -130,6 +139,23 @@ __global__ __launch_bounds__(256) void k_rowscale(const float* x, int ldx, int M
   for (int k = lane; k < K; k += 64) s += x[(size_t)m * ldx + k] * x[(size_t)m * ldx + k];
   s = wave_sum(s);
   if (lane == 0) rs[m] = 1.0f / sqrtf(s / (float)K + eps);
+}
+
+// out[m] = x[m] * rs[m] * gain (the normalised rows a GEMM with a row scale consumed), one
+// block per row.
+template <typename WT>
+__global__ void k_norm_rows(const float* x, int ldx, const float* rs, const void* gain, int K, float* out, int ldo) {
+  const int m = blockIdx.x;
+  const WT* g = reinterpret_cast<const WT*>(gain);
+  for (int k = threadIdx.x; k < K; k += blockDim.x) out[(size_t)m * ldo + k] = x[(size_t)m * ldx + k] * rs[m] * to_f32(g[k]);
+}
+
+// The device counters' advance that a GEMV epilogue does when a GEMM replaces it.
+__global__ void k_bump_state(DevState* st, int dpos, int dframe) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    st->pos += dpos;
+    st->frame += dframe;
+  }
 }
 
 // Rows b * P + i of X = E_text[ids[b * n + p0 + i]] (i < P), fp32.

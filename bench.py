@@ -38,6 +38,8 @@ def parse():
     p.add_argument("--cpu-frames", type=int, default=200, help="frames of the oracle CPU baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kv-dtype", default="fp32", choices=["fp32", "bf16"])
+    p.add_argument("--ragged", action="store_true",
+                   help="prompt lengths drawn per stream (seed 7) from [prefill/4, prefill], prefilled ragged")
     p.add_argument("--kernel-iters", type=int, default=40,
                    help="back-to-back launches of the dominant kernel timed for the roofline")
     return p.parse_args()
@@ -92,11 +94,17 @@ def main():
     codes = torch.zeros((B, W + K, 16), dtype=torch.int32, device=d)
     stream = dec.stream
 
+    lengths = None
+    if args.ragged:
+        lengths = np.random.default_rng(7).integers(max(1, wl.prefill_len // 4), wl.prefill_len + 1, B).tolist()
     times, prefill_ms = [], []
     for _ in range(args.reps):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        dec.prefill(ids)
+        if lengths is None:
+            dec.prefill(ids)
+        else:
+            dec.prefill_ragged(ids, lengths)
         torch.cuda.synchronize()
         prefill_ms.append((time.perf_counter() - t0) * 1e3)
         if W:
@@ -182,6 +190,9 @@ def main():
                            "avg_launch_us": round(dom_s * 1e6, 2), "algorithmic_bytes_per_launch": int(dom_bytes)}
     else:
         out["roofline"] = dict(out["frame_roofline"], traffic=None)
+    if lengths is not None:
+        out["config"]["prompt_lengths"] = {"ragged": True, "min": min(lengths), "max": max(lengths),
+                                           "mean": round(sum(lengths) / len(lengths), 1)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, weights, args.cpu_frames)
     dec.close()

@@ -215,8 +215,9 @@ int tts_get_exec_mode(const tts_ctx* ctx, int32_t* mode, int32_t* persistent_sup
  *  TTS_PREFILL_GEMM (default where supported: bf16 weights, head dimension
  *    128, Talker dimensions multiples of 64): chunks of up to 64 positions
  *    per stream as MFMA GEMMs over all streams' rows, causal attention over
- *    the KV cache. fp32 activations enter each GEMM as two bf16 parts
- *    (hi, lo), so the results match the step path up to summation order.
+ *    the KV cache. fp32 activations enter each GEMM as three bf16 parts
+ *    (hi, mid, lo) whose sum is the fp32 value, so the results match the
+ *    step path up to summation order.
  *  TTS_PREFILL_STEPS: one position at a time through the decode kernels.
  * TTS_E_UNSUPPORTED when GEMM is asked for and the config cannot use it. */
 enum tts_prefill_mode { TTS_PREFILL_STEPS = 0, TTS_PREFILL_GEMM = 1 };

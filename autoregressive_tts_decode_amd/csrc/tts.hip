@@ -32,6 +32,7 @@ constexpr int kCpPositions = 16;   // CodePredictor positions 0..15 per frame
 constexpr int kAttnChunk = 32;     // Talker positions per attention split
 constexpr int kMaxGemvM = 8;       // input rows per GEMV launch
 constexpr int kGemmMinRows = 16;   // batched projections with at least this many rows run as MFMA GEMMs
+constexpr int kGemmWgs = 512;      // workgroups a split-K decode GEMM aims for
 constexpr int kGemvXRegs = 96;     // per-lane registers a GEMV spends on its input rows (M * U * E)
 
 struct Layer {
@@ -432,7 +433,19 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
   g.nseg = a.nseg; g.N = N;
   if (a.epi == EPI_SWIGLU) { g.C = GU; g.ldc = N; g.add = 0; }
   else { g.C = a.y; g.ldc = a.y_stride; g.add = a.epi == EPI_RESID ? 1 : 0; }
-  hipLaunchKernelGGL(k_gemm_bf16, dim3(N / kGBN, (a.M + kGBM - 1) / kGBM), dim3(256), 0, ctx->stream, g);
+  // Split K so that about kGemmWgs workgroups stream the weights (a decode GEMM has few row tiles:
+  // unsplit, N/64 workgroups would each walk all of K with one load in flight). The slices add
+  // into C with atomics, so C starts as the residual or as zeros.
+  const int tiles = (N / kGBN) * ((a.M + kGBM - 1) / kGBM);
+  int ks = std::max(1, std::min(a.K / kGBK, kGemmWgs / tiles));
+  const int kslice = ((a.K / kGBK + ks - 1) / ks) * kGBK;
+  ks = (a.K + kslice - 1) / kslice;
+  g.kslice = kslice;
+  if (ks > 1 && !g.add) {
+    hipLaunchKernelGGL(k_zero_rows, dim3(a.M), dim3(256), 0, ctx->stream, g.C, g.ldc, N);
+    HIP_LAUNCH_CHECK();
+  }
+  hipLaunchKernelGGL(k_gemm_bf16, dim3(N / kGBN, (a.M + kGBM - 1) / kGBM, ks), dim3(256), 0, ctx->stream, g);
   HIP_LAUNCH_CHECK();
   if (a.epi == EPI_SWIGLU) {
     hipLaunchKernelGGL(k_swiglu_rows, dim3(std::min((a.M * a.N + 255) / 256, 4096)), dim3(256), 0, ctx->stream, GU, a.M, a.N, a.y);
@@ -594,7 +607,7 @@ int prefill_gemm(tts_ctx* ctx, const int32_t* ids, int B, int n) {
                   float* C, int N, int K, int M, int add) -> int {
     GemmArgs a;
     std::memset(&a, 0, sizeof a);
-    a.A = A; a.lda = lda; a.rs = rs; a.gain = gain; a.C = C; a.ldc = N; a.M = M; a.N = N; a.K = K; a.add = add;
+    a.A = A; a.lda = lda; a.rs = rs; a.gain = gain; a.C = C; a.ldc = N; a.M = M; a.N = N; a.K = K; a.add = add; a.kslice = K;
     for (auto& sg : segs) { a.w[a.nseg] = sg.first; a.seg_rows[a.nseg] = sg.second; ++a.nseg; }
     hipLaunchKernelGGL(k_gemm_bf16, dim3(N / kGBN, (M + kGBM - 1) / kGBM), dim3(256), 0, ctx->stream, a);
     HIP_LAUNCH_CHECK();

@@ -31,6 +31,9 @@ struct GemmArgs {
   int ldc;
   int M, N, K;
   int add;            // 1: C += result (residual), 0: C = result
+  int kslice;         // K columns per workgroup (blockIdx.z selects the slice); kslice < K: every
+                      // workgroup adds its partial into C with float atomics, C holding the
+                      // residual (add = 1) or zeros
 };
 
 constexpr int kGBM = 64, kGBN = 64, kGBK = 64, kGLD = kGBK + 8;  // tile, LDS row stride (bf16)
@@ -46,6 +49,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
   int seg = 0, nrel = n0;
   while (seg + 1 < a.nseg && nrel >= a.seg_rows[seg]) { nrel -= a.seg_rows[seg]; ++seg; }
   const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w[seg]) + (size_t)nrel * a.K;
+  const int kbeg = blockIdx.z * a.kslice, kend = min(kbeg + a.kslice, a.K);
+  const bool split = a.kslice < a.K;
   const int lr = tid >> 2, lk = (tid & 3) * 16;  // loader: row lr of the tile, 16 k from lk
   const bool arow = m0 + lr < a.M;
   const float rsc = (a.rs && arow) ? a.rs[m0 + lr] : 1.f;
@@ -58,7 +63,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4v){0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < a.K; k0 += kGBK) {
+  for (int k0 = kbeg; k0 < kend; k0 += kGBK) {
     float av[16];
 #pragma unroll
     for (int e = 0; e < 16; e += 4) {
@@ -126,7 +131,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
         const int m = m0 + wm * 32 + i * 16 + 4 * lq + r, n = n0 + wn * 32 + j * 16 + lc;
         if (m < a.M) {
           float* c = a.C + (size_t)m * a.ldc + n;
-          *c = a.add ? *c + acc[i][j][r] : acc[i][j][r];
+          if (split) atomicAdd(c, acc[i][j][r]);
+          else *c = a.add ? *c + acc[i][j][r] : acc[i][j][r];
         }
       }
 }
@@ -148,6 +154,11 @@ __global__ void k_norm_rows(const float* x, int ldx, const float* rs, const void
   const int m = blockIdx.x;
   const WT* g = reinterpret_cast<const WT*>(gain);
   for (int k = threadIdx.x; k < K; k += blockDim.x) out[(size_t)m * ldo + k] = x[(size_t)m * ldx + k] * rs[m] * to_f32(g[k]);
+}
+
+// rows[m][0 .. n) = 0 (a split-K GEMM's output before its slices add into it); one block per row.
+__global__ void k_zero_rows(float* rows, int ld, int n) {
+  for (int k = threadIdx.x; k < n; k += blockDim.x) rows[(size_t)blockIdx.x * ld + k] = 0.f;
 }
 
 // The device counters' advance that a GEMV epilogue does when a GEMM replaces it.

@@ -96,6 +96,11 @@ __device__ __forceinline__ int fresh_tid() {
   return t;
 }
 
+// Lane i's value, read into a scalar register (wave-uniform).
+__device__ __forceinline__ float readlane_f(float v, int i) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), i));
+}
+
 __device__ __forceinline__ u64 pack(float v, uint32_t tag) { return ((u64)tag << 32) | __float_as_uint(v); }
 __device__ __forceinline__ uint32_t tagof(u64 v) { return (uint32_t)(v >> 32); }
 __device__ __forceinline__ float valof(u64 v) { return __uint_as_float((uint32_t)v); }
@@ -585,21 +590,22 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
       const float4 b = *reinterpret_cast<const float4*>(&kc[t][32 * e + 4 * i]);
       s = fmaf(a.x, b.x, s); s = fmaf(a.y, b.y, s); s = fmaf(a.z, b.z, s); s = fmaf(a.w, b.w, s);
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
+    // the quarters' sums within each group of 4 lanes (DPP quad permutes), then the max, the
+    // weights' sum and the output over the 16 positions from the lanes 4 t read as scalars: no
+    // cross-lane step goes through LDS
+    s += TTS_DPP(s, 0xB1);  // quad_perm [1,0,3,2]
+    s += TTS_DPP(s, 0x4E);  // quad_perm [2,3,0,1]
     s = t <= p ? s * (1.0f / sqrtf((float)d)) : -INFINITY;  // rows past p hold stale values
-    float mx = s;
+    float mx = -INFINITY;
 #pragma unroll
-    for (int o = 4; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int tt = 0; tt < kCpPos; ++tt) mx = fmaxf(mx, readlane_f(s, 4 * tt));
     const float w = t <= p ? expf(s - mx) : 0.f;
-    float l = w;
-#pragma unroll
-    for (int o = 4; o < 64; o <<= 1) l += __shfl_xor(l, o);
-    float o0 = 0.f, o1 = 0.f;
+    float l = 0.f, o0 = 0.f, o1 = 0.f;
 #pragma unroll
     for (int tt = 0; tt < kCpPos; ++tt) {
       if (tt <= p) {
-        const float wt = __shfl(w, 4 * tt);
+        const float wt = readlane_f(w, 4 * tt);
+        l += wt;
         o0 = fmaf(wt, vc[tt][lane], o0);
         o1 = fmaf(wt, vc[tt][lane + 64], o1);
       }

@@ -409,31 +409,33 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
           s[h] = fmaf(q4.z, kv4.z, s[h]); s[h] = fmaf(q4.w, kv4.w, s[h]);
         }
       }
+      // quarter sums within each group of 4 lanes (DPP), then the pass's max and weight sum over
+      // the positions from the lanes 4 t read as scalars: no cross-lane step goes through LDS
+      const int npass = min(16, t1 - base);
       float w[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        s[h] += __shfl_xor(s[h], 1);
-        s[h] += __shfl_xor(s[h], 2);
+        s[h] += TTS_DPP(s[h], 0xB1);  // quad_perm [1,0,3,2]
+        s[h] += TTS_DPP(s[h], 0x4E);  // quad_perm [2,3,0,1]
         s[h] = valid ? s[h] * scale : -INFINITY;
-        float mx = s[h];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int q = 4; q < 64; q <<= 1) mx = fmaxf(mx, __shfl_xor(mx, q));
+        for (int tt = 0; tt < 16; ++tt) mx = fmaxf(mx, readlane_f(s[h], 4 * tt));
         const float mn = fmaxf(m[h], mx);  // finite: the pass holds at least one valid position
         const float corr = m[h] == -INFINITY ? 0.f : expf(m[h] - mn);
         w[h] = valid ? expf(s[h] - mn) : 0.f;
-        float ws = w[h];
+        float ws = 0.f;
 #pragma unroll
-        for (int q = 4; q < 64; q <<= 1) ws += __shfl_xor(ws, q);
+        for (int tt = 0; tt < 16; ++tt) ws += readlane_f(w[h], 4 * tt);
         l[h] = l[h] * corr + ws;
         o[h][0] *= corr;
         o[h][1] *= corr;
         m[h] = mn;
       }
       // outputs: lane owns dimensions lane, lane + 64 of both heads
-      const int npass = min(16, t1 - base);
       for (int tt = 0; tt < npass; ++tt) {
         const int tp = base + tt;
-        const float w0 = __shfl(w[0], 4 * tt), w1 = __shfl(w[1], 4 * tt);
+        const float w0 = readlane_f(w[0], 4 * tt), w1 = readlane_f(w[1], 4 * tt);
         float v0, v1;
         if (tp == p) { v0 = S.vp[lane]; v1 = S.vp[lane + 64]; }
         else { v0 = glb(vg)[(size_t)tp * d + lane]; v1 = glb(vg)[(size_t)tp * d + lane + 64]; }

@@ -335,6 +335,42 @@ def test_error_paths_leave_the_context_usable(tiny):
     dec.close()
 
 
+def test_error_paths_of_stop_ragged_and_text_stream(tiny):
+    """The stop id, ragged prefill and text stream validate their arguments before anything is
+    enqueued, and a rejected call leaves the context usable."""
+    wl = tiny["wl"]
+    d = dev()
+    dec = tts.TTSDecoder(wl.model, 2, 40, 4)
+    dec.load_weights(tiny["dw"])
+    stop = torch.zeros((2,), dtype=torch.int32, device=d)
+    with pytest.raises(tts.TTSError) as e:
+        dec.set_stop(wl.model.talker.vocab, stop)
+    assert e.value.code == tts.TTS_E_ARG
+    with pytest.raises(tts.TTSError) as e:
+        dec.set_stop(3, None)
+    assert e.value.code == tts.TTS_E_ARG
+    ids = torch.zeros((2, 8), dtype=torch.int32, device=d)
+    for bad in ([0, 8], [9, 8]):
+        with pytest.raises(tts.TTSError) as e:
+            dec.prefill_ragged(ids, bad)
+        assert e.value.code == tts.TTS_E_SHAPE
+    text = torch.zeros((2, 4), dtype=torch.int32, device=d)
+    assert dec.lib.tts_set_text_stream(dec.ctx, text.data_ptr(), 0, 0) == tts.TTS_E_ARG  # ids with n_text < 1
+    with pytest.raises(tts.TTSError) as e:
+        dec.set_text_stream(text, -1)
+    assert e.value.code == tts.TTS_E_ARG
+    dec.set_stop(3, stop)
+    torch.cuda.synchronize()
+    assert (stop.cpu().numpy() == -1).all()
+    dec.prefill_ragged(ids, [8, 3])
+    fr = torch.zeros((2, 4, 16), dtype=torch.int32, device=d)
+    dec.run_frames(2, GREEDY, GREEDY, None, fr)
+    torch.cuda.synchronize()
+    assert dec.progress() == (10, 2)
+    dec.set_stop(-1)
+    dec.close()
+
+
 # ----------------------------------------------------------------------------- bf16 models
 
 @pytest.fixture(scope="module", params=["0.6b", "1.7b"])

@@ -63,18 +63,30 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = (f32x4v){0.f, 0.f, 0.f, 0.f};
+  // A, W and gain operands of a K step go to registers one step ahead: the next step's loads are
+  // in flight while this step's tile is staged and multiplied.
+  float4 an[4];
+  u32x4 bn0, bn1, gn0, gn1;
+  auto load_step = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) an[q] = arow ? *reinterpret_cast<const float4*>(Ap + k0 + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+    bn0 = *reinterpret_cast<const u32x4*>(Wp + k0);
+    bn1 = *reinterpret_cast<const u32x4*>(Wp + k0 + 8);
+    if (gp) {
+      gn0 = *reinterpret_cast<const u32x4*>(gp + k0 + lk);
+      gn1 = *reinterpret_cast<const u32x4*>(gp + k0 + lk + 8);
+    }
+  };
+  if (kbeg < kend) load_step(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += kGBK) {
     float av[16];
 #pragma unroll
-    for (int e = 0; e < 16; e += 4) {
-      const float4 f = arow ? *reinterpret_cast<const float4*>(Ap + k0 + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-      av[e] = f.x; av[e + 1] = f.y; av[e + 2] = f.z; av[e + 3] = f.w;
+    for (int q = 0; q < 4; ++q) {
+      av[4 * q] = an[q].x; av[4 * q + 1] = an[q].y; av[4 * q + 2] = an[q].z; av[4 * q + 3] = an[q].w;
     }
-    const u32x4 b0 = *reinterpret_cast<const u32x4*>(Wp + k0);
-    const u32x4 b1 = *reinterpret_cast<const u32x4*>(Wp + k0 + 8);
+    const u32x4 b0 = bn0, b1 = bn1, g0 = gn0, g1 = gn1;
+    if (k0 + kGBK < kend) load_step(k0 + kGBK);
     if (gp) {
-      const u32x4 g0 = *reinterpret_cast<const u32x4*>(gp + k0 + lk);
-      const u32x4 g1 = *reinterpret_cast<const u32x4*>(gp + k0 + lk + 8);
       float gf0[8], gf1[8];
       unpack(g0, gf0, (uint16_t*)nullptr);
       unpack(g1, gf1, (uint16_t*)nullptr);

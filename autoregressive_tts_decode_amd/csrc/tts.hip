@@ -417,14 +417,6 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
     A = X;
     lda = a.K;
   }
-  if (a.gain) {
-    hipLaunchKernelGGL(k_rowscale, dim3((a.M + 3) / 4), dim3(256), 0, ctx->stream, A, lda, a.M, a.K, ctx->cfg.rms_eps, RS);
-    HIP_LAUNCH_CHECK();
-    if (a.xn_out) {
-      hipLaunchKernelGGL(k_norm_rows<uint16_t>, dim3(a.M), dim3(256), 0, ctx->stream, A, lda, RS, a.gain, a.K, a.xn_out, a.xn_stride);
-      HIP_LAUNCH_CHECK();
-    }
-  }
   GemmArgs g;
   std::memset(&g, 0, sizeof g);
   g.A = A; g.lda = lda; g.rs = a.gain ? RS : nullptr; g.gain = a.gain; g.M = a.M; g.K = a.K;
@@ -435,13 +427,23 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
   else { g.C = a.y; g.ldc = a.y_stride; g.add = a.epi == EPI_RESID ? 1 : 0; }
   // Split K so that about kGemmWgs workgroups stream the weights (a decode GEMM has few row tiles:
   // unsplit, N/64 workgroups would each walk all of K with one load in flight). The slices add
-  // into C with atomics, so C starts as the residual or as zeros.
+  // into C with atomics, so C starts as the residual or as zeros (cleared by the row-scale
+  // kernel when there is one).
   const int tiles = (N / kGBN) * ((a.M + kGBM - 1) / kGBM);
   int ks = std::max(1, std::min(a.K / kGBK, kGemmWgs / tiles));
   const int kslice = ((a.K / kGBK + ks - 1) / ks) * kGBK;
   ks = (a.K + kslice - 1) / kslice;
   g.kslice = kslice;
-  if (ks > 1 && !g.add) {
+  const bool zero = ks > 1 && !g.add;
+  if (a.gain) {
+    hipLaunchKernelGGL(k_rowscale, dim3((a.M + 3) / 4), dim3(256), 0, ctx->stream, A, lda, a.M, a.K, ctx->cfg.rms_eps, RS,
+                       zero ? g.C : nullptr, g.ldc, N);
+    HIP_LAUNCH_CHECK();
+    if (a.xn_out) {
+      hipLaunchKernelGGL(k_norm_rows<uint16_t>, dim3(a.M), dim3(256), 0, ctx->stream, A, lda, RS, a.gain, a.K, a.xn_out, a.xn_stride);
+      HIP_LAUNCH_CHECK();
+    }
+  } else if (zero) {
     hipLaunchKernelGGL(k_zero_rows, dim3(a.M), dim3(256), 0, ctx->stream, g.C, g.ldc, N);
     HIP_LAUNCH_CHECK();
   }

@@ -149,14 +149,18 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
       }
 }
 
-// rs[m] = 1 / sqrt(mean(x[m]^2) + eps) over K; one wave per row.
-__global__ __launch_bounds__(256) void k_rowscale(const float* x, int ldx, int M, int K, float eps, float* rs) {
+// rs[m] = 1 / sqrt(mean(x[m]^2) + eps) over K; one wave per row. With zc, the wave also clears
+// row m of zc[.., 0 .. zn) (the output a split-K GEMM adds its slices into).
+__global__ __launch_bounds__(256) void k_rowscale(const float* x, int ldx, int M, int K, float eps, float* rs,
+                                                  float* zc = nullptr, int zld = 0, int zn = 0) {
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (m >= M) return;
   float s = 0.f;
   for (int k = lane; k < K; k += 64) s += x[(size_t)m * ldx + k] * x[(size_t)m * ldx + k];
   s = wave_sum(s);
   if (lane == 0) rs[m] = 1.0f / sqrtf(s / (float)K + eps);
+  if (zc)
+    for (int k = lane; k < zn; k += 64) zc[(size_t)m * zld + k] = 0.f;
 }
 
 // out[m] = x[m] * rs[m] * gain (the normalised rows a GEMM with a row scale consumed), one

@@ -38,7 +38,7 @@ class ModelCfg:
     talker: StackCfg
     codepred: StackCfg
     text_vocab: int
-    weight_dtype: str  # "fp32" or "bf16"
+    weight_dtype: str  # "fp32", "bf16" or "fp8" (E4M3 projection matrices, bf16 gains/embeddings)
     n_acoustic: int = N_ACOUSTIC
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
@@ -105,6 +105,13 @@ M17B = ModelCfg(
     weight_dtype="bf16",
 )
 
+# Weight-only FP8 variants: the same drawn (bf16-rounded) weights, with every projection matrix
+# stored as E4M3 codes and one fp32 scale per output row.
+M06B_FP8 = ModelCfg(name="0.6b-class-fp8", talker=M06B.talker, codepred=M06B.codepred, text_vocab=M06B.text_vocab,
+                    weight_dtype="fp8")
+M17B_FP8 = ModelCfg(name="1.7b-class-fp8", talker=M17B.talker, codepred=M17B.codepred, text_vocab=M17B.text_vocab,
+                    weight_dtype="fp8")
+
 WORKLOADS = {
     "tiny": Workload("tiny", TINY, batch=1, prefill_len=32, frames=16),
     "0.6b": Workload("0.6b", M06B, batch=1, prefill_len=64, frames=240),
@@ -114,7 +121,21 @@ WORKLOADS = {
                          semantic=SEMANTIC_SAMPLED, acoustic=ACOUSTIC_SAMPLED),
 }
 
-MODELS = {"tiny": TINY, "0.6b": M06B, "1.7b": M17B}
+MODELS = {"tiny": TINY, "0.6b": M06B, "1.7b": M17B, "0.6b-fp8": M06B_FP8, "1.7b-fp8": M17B_FP8}
+
+# Projection matrices (stored as E4M3 codes plus per-row scales in fp8 models).
+QUANT_SUFFIXES = (".wq", ".wk", ".wv", ".wo", ".wg", ".wu", ".wd")
+QUANT_NAMES = ("talker.lm_head", "cp.proj", "cp.heads")
+
+
+def is_quantized(cfg: ModelCfg, name: str) -> bool:
+    """True for the tensors an fp8 model stores as E4M3 codes with a '<name>.scale' companion."""
+    return cfg.weight_dtype == "fp8" and (name in QUANT_NAMES or name.endswith(QUANT_SUFFIXES))
+
+
+def scale_specs(cfg: ModelCfg) -> list[tuple[str, tuple[int, ...]]]:
+    """The fp32 per-row scale tensors of an fp8 model (none for other dtypes)."""
+    return [(name + ".scale", shape[:-1]) for name, shape, _ in tensor_specs(cfg) if is_quantized(cfg, name)]
 
 
 def tensor_specs(cfg: ModelCfg) -> list[tuple[str, tuple[int, ...], str]]:

@@ -11,6 +11,12 @@ not available, so seeded random tensors of the same shapes stand in):
     0.02 * standard_normal(float32), norm gains 1 + 0.01 * standard_normal;
   * bf16 configs store round-to-nearest-even bf16 of those fp32 draws
     (returned as uint16 bit patterns);
+  * fp8 configs start from the same bf16 values; each projection matrix
+    (config.is_quantized) is then stored per output row as scale = max|w| / 448
+    (fp32; 1 for an all-zero row) and E4M3 codes of w / scale, rounded to
+    nearest even by torch's float8_e4m3fn cast (uint8 codes; the scale goes
+    under '<name>.scale'). This is weight preparation, done once offline;
+    the decode then reads only codes and scales.
   * text ids are uniform integers in [0, text_vocab) from PCG64([ids_seed]);
   * uniforms are fp32 in [0, 1) from PCG64([uniform_seed]), laid out
     [batch, frame, 16]: index 0 drives the semantic draw, j the acoustic j.
@@ -22,7 +28,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from .config import ModelCfg, Workload, tensor_specs, CODES_PER_FRAME
+from .config import ModelCfg, Workload, tensor_specs, is_quantized, CODES_PER_FRAME
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -43,19 +49,43 @@ def _draw(seed: int, k: int, shape: tuple[int, ...], kind: str, bf16: bool) -> n
     return f32_to_bf16_bits(a) if bf16 else a
 
 
+E4M3_MAX = 448.0  # largest finite E4M3 magnitude
+
+
+def quantize_rows_e4m3(bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 bit patterns [..., K] -> (uint8 E4M3 codes [..., K], fp32 row scales [...])."""
+    import torch
+    w = (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    amax = np.abs(w).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = np.clip(w / scale[..., None], -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    codes = torch.from_numpy(np.ascontiguousarray(q)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale
+
+
+def _draw_stored(cfg: ModelCfg, seed: int, k: int, name: str, shape: tuple[int, ...], kind: str) -> dict:
+    if cfg.weight_dtype != "fp8":
+        return {name: _draw(seed, k, shape, kind, cfg.weight_dtype == "bf16")}
+    a = _draw(seed, k, shape, kind, True)
+    if not is_quantized(cfg, name):
+        return {name: a}
+    codes, scale = quantize_rows_e4m3(a)
+    return {name: codes, name + ".scale": scale}
+
+
 def make_weights(cfg: ModelCfg, seed: int = 0, threads: int | None = None,
                  only: set[str] | None = None) -> dict[str, np.ndarray]:
-    """All model tensors. fp32 configs: float32 arrays; bf16 configs: uint16 bf16 bits."""
-    bf16 = cfg.weight_dtype == "bf16"
+    """All model tensors. fp32 configs: float32 arrays; bf16 configs: uint16 bf16 bits;
+    fp8 configs: uint8 E4M3 codes + float32 '<name>.scale' for the matrices, bf16 bits otherwise."""
     specs = tensor_specs(cfg)
     jobs = [(k, name, shape, kind) for k, (name, shape, kind) in enumerate(specs)
             if only is None or name in only]
     threads = threads or min(8, len(os.sched_getaffinity(0)))
     out: dict[str, np.ndarray] = {}
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        futs = {name: ex.submit(_draw, seed, k, shape, kind, bf16) for k, name, shape, kind in jobs}
-        for name, f in futs.items():
-            out[name] = f.result()
+        futs = [ex.submit(_draw_stored, cfg, seed, k, name, shape, kind) for k, name, shape, kind in jobs]
+        for f in futs:
+            out.update(f.result())
     return out
 
 

@@ -25,7 +25,8 @@
  *    return nothing was enqueued and the device state is unchanged. The text
  *    of the last error is available from tts_last_error.
  *  - Tokens are int32. Logits are fp32. Weights are row-major [out, in],
- *    all fp32 (TTS_DTYPE_F32) or all bf16 (TTS_DTYPE_BF16).
+ *    all fp32 (TTS_DTYPE_F32), all bf16 (TTS_DTYPE_BF16), or FP8 projection
+ *    matrices with bf16 gains and embeddings (TTS_DTYPE_FP8_E4M3, below).
  *  - B (batch) streams run in lockstep: same prefill length, same positions.
  */
 #ifndef TTS_H
@@ -52,7 +53,17 @@ enum tts_status {
   TTS_E_UNSUPPORTED = -6 /* valid request outside what this build implements */
 };
 
-enum tts_dtype { TTS_DTYPE_F32 = 0, TTS_DTYPE_BF16 = 1 };
+/* TTS_DTYPE_FP8_E4M3 (weight_dtype only): weight-only 8-bit quantisation
+ * ("Benchmarking a TTS Model on Your Own GPU": an eight-bit copy of the
+ * weights, widened on the fly, with FP8 done natively by newer hardware).
+ * The projection matrices (wq wk wv wo wg wu wd, talker.lm_head, cp.proj,
+ * cp.heads) are OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3
+ * mantissa bits; subnormals; 0x7f/0xff NaN, never produced), one byte per
+ * element, and each comes with "<name>.scale": fp32, shape = the matrix's
+ * shape without its last dimension. Element [.., r, k] stands for
+ * scale[.., r] * decode(code[.., r, k]); products and sums are fp32.
+ * Norm gains and the three embedding tables stay bf16. */
+enum tts_dtype { TTS_DTYPE_F32 = 0, TTS_DTYPE_BF16 = 1, TTS_DTYPE_FP8_E4M3 = 2 };
 
 /* One decoder stack (Talker or CodePredictor). vocab is the semantic vocab
  * for the Talker and the per-codebook acoustic vocab for the CodePredictor. */
@@ -66,7 +77,7 @@ typedef struct {
   int32_t n_acoustic;      /* must be 15 */
   float rms_eps;           /* RMSNorm epsilon */
   float rope_theta;        /* RoPE base */
-  int32_t weight_dtype;    /* enum tts_dtype of every weight tensor */
+  int32_t weight_dtype;    /* enum tts_dtype of the weights (FP8: matrices only, see above) */
   int32_t kv_dtype;        /* enum tts_dtype of the KV caches (fp32 keeps k/v unrounded) */
   int32_t max_batch;       /* streams per context */
   int32_t max_cache_steps; /* Talker KV capacity in positions (prefill + frames) */
@@ -103,7 +114,10 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
  * cp.final_norm, cp.heads [15,Va,Hc]). shapes: n x 4 int64 (row-major, only
  * the first ranks[i] entries used); dtypes: enum tts_dtype per tensor. Every
  * tensor must be present with the exact shape, the config's dtype and
- * 16-byte alignment. Pointers are borrowed until tts_destroy. */
+ * 16-byte alignment; FP8 configs add one "<matrix>.scale" per matrix (fp32)
+ * and give gains and embeddings as bf16. Pointers are borrowed until
+ * tts_destroy. FP8 configs decode with the per-op kernels only (the
+ * persistent step kernels and the MFMA GEMM routes need bf16 weights). */
 int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* const* dev_ptrs,
                      const int64_t* shapes, const int32_t* ranks, const int32_t* dtypes);
 

@@ -58,6 +58,27 @@ def bf16_bits_to_float(bits: np.ndarray, dtype=np.float64) -> np.ndarray:
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(dtype)
 
 
+def e4m3_to_float(codes: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """Decode OCP E4M3 bytes by the format's definition: bit 7 sign, bits 6..3
+    exponent e (bias 7), bits 2..0 mantissa m. e = 0 is subnormal, (m / 8) * 2^-6;
+    otherwise (1 + m / 8) * 2^(e - 7); e = 15 with m = 7 is NaN (the format has no
+    infinities). Every finite code is exact in float32 and float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return (sign * mag).astype(dtype)
+
+
+def dequant_rows(codes: np.ndarray, scale: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """The matrix an FP8 weight stands for: element [.., r, k] = scale[.., r] * decode(code[.., r, k])
+    ("Benchmarking a TTS Model on Your Own GPU": eight-bit weights are widened on the fly; the
+    per-row scale is the reading of how the 8-bit range is fitted to each row)."""
+    return (e4m3_to_float(codes, np.float64) * np.asarray(scale, dtype=np.float64)[..., None]).astype(dtype)
+
+
 def rms_norm(v: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm over the last axis: v * g / sqrt(mean(v^2) + eps)."""
     ms = np.mean(v * v, axis=-1, keepdims=True)
@@ -147,7 +168,10 @@ class OracleModel:
     """Talker + CodePredictor in a working dtype (np.float64 or np.float32).
 
     ``weights`` maps the canonical tensor names to arrays: float32 for fp32
-    models, uint16 bf16 bit patterns for bf16 models. ``cfg`` is a plain dict
+    models, uint16 bf16 bit patterns for bf16 models; fp8 models give the
+    projection matrices as uint8 E4M3 codes with a float32 '<name>.scale' per
+    output row (everything else bf16), and the oracle runs on the matrices
+    they stand for (``dequant_rows``). ``cfg`` is a plain dict
     with keys talker / codepred (n_layers, hidden, n_q_heads, n_kv_heads,
     head_dim, ffn, vocab), text_vocab, n_acoustic, rms_eps, rope_theta,
     weight_dtype.
@@ -158,11 +182,15 @@ class OracleModel:
         self.eps = float(cfg["rms_eps"])
         self.theta = float(cfg["rope_theta"])
         self.n_ac = int(cfg["n_acoustic"])
-        bf16 = cfg["weight_dtype"] == "bf16"
+        wd = cfg["weight_dtype"]
 
         def cvt(name):
             a = weights[name]
-            return bf16_bits_to_float(a, self.dtype) if bf16 else np.asarray(a, dtype=self.dtype)
+            if wd == "fp8" and name + ".scale" in weights:
+                return dequant_rows(a, weights[name + ".scale"], self.dtype)
+            if np.asarray(a).dtype == np.uint8:
+                raise KeyError(f"{name}: E4M3 codes without '{name}.scale'")
+            return bf16_bits_to_float(a, self.dtype) if wd in ("bf16", "fp8") else np.asarray(a, dtype=self.dtype)
 
         def stack(prefix, s):
             st = _Stack(s["n_layers"], s["hidden"], s["n_q_heads"], s["n_kv_heads"], s["head_dim"], s["ffn"], s["vocab"])

@@ -189,6 +189,88 @@ def test_f2_ragged_streams_equal_the_lockstep_batch_when_lengths_agree(tiny_weig
         m.generate(ids, 2, GREEDY, GREEDY, u, lengths=[9, 5], text_lookahead=3)
 
 
+# ----------------------------------------------------------------------------- f3 FP8 weights
+
+def test_f3_e4m3_decode_matches_torch_float8_e4m3fn():
+    """All 256 codes decode as torch's float8_e4m3fn (an independent implementation of the OCP
+    E4M3 format) does: same finite values, same NaN codes, same signed zeros."""
+    import torch
+    from oracle.decoder import e4m3_to_float
+    codes = np.arange(256, dtype=np.uint8)
+    ours = e4m3_to_float(codes, np.float64)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[fin], ref[fin])
+    np.testing.assert_array_equal(np.signbit(ours[fin]), np.signbit(ref[fin]))
+    assert int(np.isnan(ours).sum()) == 2
+
+
+def test_f3_e4m3_closed_forms():
+    """Values the format's definition fixes: largest finite 448, smallest subnormal 2^-9, smallest
+    normal 2^-6, largest subnormal 7 * 2^-9, one, minus one; positive codes increase strictly."""
+    from oracle.decoder import e4m3_to_float
+    v = {c: float(e4m3_to_float(np.array([c], np.uint8))[0]) for c in (0x7E, 0x01, 0x08, 0x07, 0x38, 0xB8, 0x00)}
+    assert v[0x7E] == 448.0 and v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    assert v[0x07] == 7 * 2.0 ** -9 and v[0x38] == 1.0 and v[0xB8] == -1.0 and v[0x00] == 0.0
+    pos = e4m3_to_float(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    np.testing.assert_array_equal(e4m3_to_float(np.arange(0x80, 0xFF, dtype=np.uint8)), -pos)
+
+
+def test_f3_quantizer_rounds_each_row_to_the_nearest_code():
+    """The stored codes are the nearest E4M3 value of w / scale (relative error <= 2^-4 in the
+    normal range, absolute <= 2^-10 below it) and each row's largest magnitude maps to 448."""
+    from oracle.decoder import e4m3_to_float
+    bits = synth.f32_to_bf16_bits(np.random.default_rng(3).standard_normal((64, 512)).astype(np.float32) * 0.02)
+    codes, scale = synth.quantize_rows_e4m3(bits)
+    w = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    t = w / scale.astype(np.float64)[:, None]
+    q = e4m3_to_float(codes)
+    err = np.abs(q - t)
+    normal = np.abs(t) >= 2.0 ** -6
+    assert np.all(err[normal] <= 2.0 ** -4 * np.abs(t[normal]) * (1 + 1e-6))
+    assert np.all(err[~normal] <= 2.0 ** -10 * (1 + 1e-6))
+    np.testing.assert_array_equal(np.abs(q).max(axis=1), 448.0)
+    # nearest: no other finite code is closer
+    grid = e4m3_to_float(np.arange(256, dtype=np.uint8))
+    grid = grid[~np.isnan(grid)]
+    best = np.min(np.abs(t[..., None] - grid), axis=-1)
+    assert np.all(err <= best + 2.0 ** -22 * np.abs(t))  # w / scale is formed in fp32
+
+
+TINY_FP8 = config.ModelCfg(name="tiny-fp8", talker=config.TINY.talker, codepred=config.TINY.codepred,
+                           text_vocab=config.TINY.text_vocab, weight_dtype="fp8")
+
+
+def test_f3_fp8_model_tracks_the_bf16_model():
+    """The fp8 model is the bf16 model with each matrix moved to its nearest scaled E4M3 grid: its
+    logits stay within a few percent of the bf16 model's (an 8-bit weight error of at most 2^-4
+    relative per element, random in sign), while the same codes under a per-column instead of
+    per-row scale -- a transposed scale -- are far off."""
+    from oracle.decoder import dequant_rows
+    bf = config.ModelCfg(name="tiny-bf16", talker=TINY_FP8.talker, codepred=TINY_FP8.codepred,
+                         text_vocab=TINY_FP8.text_vocab, weight_dtype="bf16")
+    w8 = synth.make_weights(TINY_FP8, 5)
+    w16 = synth.make_weights(bf, 5)
+    assert all(w8[n[:-6]].dtype == np.uint8 and w8[n].shape == s for n, s in config.scale_specs(TINY_FP8))
+    ids = synth.random_ids(6, TINY_FP8.text_vocab, seed=47)
+    u = np.zeros((1, 3, 16), np.float32)
+    a = OracleModel(w8, TINY_FP8.as_dict(), np.float64).generate(ids, 3, GREEDY, GREEDY, u)
+    b = OracleModel(w16, bf.as_dict(), np.float64).generate(ids, 3, GREEDY, GREEDY, u, teacher=a["codes"])
+    rel_sem = np.linalg.norm(a["sem_logits"] - b["sem_logits"]) / np.linalg.norm(b["sem_logits"])
+    rel_ac = np.linalg.norm(a["ac_logits"] - b["ac_logits"]) / np.linalg.norm(b["ac_logits"])
+    assert rel_sem < 0.1 and rel_ac < 0.1, (rel_sem, rel_ac)
+    # planted mistake, on the CPU: the scale applied along the wrong axis of the head matrices
+    bad = dict(w8)
+    hs = bad["cp.heads.scale"]
+    bad["cp.heads.scale"] = np.ascontiguousarray(np.broadcast_to(hs.mean(axis=1, keepdims=True), hs.shape)
+                                                 * np.random.default_rng(0).uniform(0.2, 5, hs.shape)).astype(np.float32)
+    c = OracleModel(bad, TINY_FP8.as_dict(), np.float64).generate(ids, 3, GREEDY, GREEDY, u, teacher=a["codes"])
+    rel_bad = np.linalg.norm(c["ac_logits"] - b["ac_logits"]) / np.linalg.norm(b["ac_logits"])
+    assert rel_bad > 0.3, rel_bad
+
+
 # ----------------------------------------------------------------------------- P2 softmax
 
 @pytest.mark.parametrize("dtype,tol", [(np.float32, 1e-6), (np.float64, 1e-14)])

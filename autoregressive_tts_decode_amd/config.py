@@ -119,6 +119,8 @@ WORKLOADS = {
     "1.7b-long": Workload("1.7b-long", M17B, batch=1, prefill_len=256, frames=2000),
     "1.7b-x32": Workload("1.7b-x32", M17B, batch=32, prefill_len=64, frames=240,
                          semantic=SEMANTIC_SAMPLED, acoustic=ACOUSTIC_SAMPLED),
+    "0.6b-fp8": Workload("0.6b-fp8", M06B_FP8, batch=1, prefill_len=64, frames=240),
+    "1.7b-fp8": Workload("1.7b-fp8", M17B_FP8, batch=1, prefill_len=64, frames=240),
 }
 
 MODELS = {"tiny": TINY, "0.6b": M06B, "1.7b": M17B, "0.6b-fp8": M06B_FP8, "1.7b-fp8": M17B_FP8}

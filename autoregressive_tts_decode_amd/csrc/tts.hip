@@ -66,7 +66,11 @@ struct Layout {
   int nsplit;
 };
 
-size_t elem_bytes(const tts_config& c) { return c.weight_dtype == TTS_DTYPE_BF16 ? 2 : 4; }
+// Bytes per element of the projection matrices and of the gains / embedding tables.
+size_t mat_bytes(const tts_config& c) { return c.weight_dtype == TTS_DTYPE_F32 ? 4 : (c.weight_dtype == TTS_DTYPE_BF16 ? 2 : 1); }
+size_t tab_bytes(const tts_config& c) { return c.weight_dtype == TTS_DTYPE_F32 ? 4 : 2; }
+// Elements per 16-byte lane load of the matrices.
+int mat_per_unit(const tts_config& c) { return (int)(16 / mat_bytes(c)); }
 size_t kv_bytes(const tts_config& c) { return c.kv_dtype == TTS_DTYPE_BF16 ? 2 : 4; }
 
 Layout make_layout(const tts_config& c) {
@@ -143,7 +147,8 @@ bool units_ok(int K, int E, int* U) {
 // Returns an error text or "" when the config is one the kernels accept.
 std::string check_config(const tts_config* c) {
   if (!c) return "config is NULL";
-  if (c->weight_dtype != TTS_DTYPE_F32 && c->weight_dtype != TTS_DTYPE_BF16) return "weight_dtype must be TTS_DTYPE_F32 or TTS_DTYPE_BF16";
+  if (c->weight_dtype != TTS_DTYPE_F32 && c->weight_dtype != TTS_DTYPE_BF16 && c->weight_dtype != TTS_DTYPE_FP8_E4M3)
+    return "weight_dtype must be TTS_DTYPE_F32, TTS_DTYPE_BF16 or TTS_DTYPE_FP8_E4M3";
   if (c->kv_dtype != TTS_DTYPE_F32 && c->kv_dtype != TTS_DTYPE_BF16) return "kv_dtype must be TTS_DTYPE_F32 or TTS_DTYPE_BF16";
   if (c->n_acoustic != 15) return "n_acoustic must be 15";
   if (c->max_batch < 1 || c->max_batch > 64) return "max_batch must be in [1, 64]";
@@ -151,7 +156,7 @@ std::string check_config(const tts_config* c) {
   if (c->max_frames < 1) return "max_frames must be >= 1";
   if (!(c->rms_eps > 0.f) || !(c->rope_theta > 1.f)) return "rms_eps must be > 0 and rope_theta > 1";
   if (c->text_vocab < 1) return "text_vocab must be >= 1";
-  const int E = c->weight_dtype == TTS_DTYPE_BF16 ? 8 : 4;
+  const int E = mat_per_unit(*c);
   const tts_stack_cfg* ss[2] = {&c->talker, &c->codepred};
   for (int i = 0; i < 2; ++i) {
     const tts_stack_cfg& s = *ss[i];
@@ -285,8 +290,20 @@ struct tts_ctx {
     return code;
   }
   bool bf16() const { return cfg.weight_dtype == TTS_DTYPE_BF16; }
+  bool fp8() const { return cfg.weight_dtype == TTS_DTYPE_FP8_E4M3; }
+  bool tab16() const { return cfg.weight_dtype != TTS_DTYPE_F32; }  // gains and embedding tables are bf16
   bool kv_bf16() const { return cfg.kv_dtype == TTS_DTYPE_BF16; }
-  size_t eb() const { return elem_bytes(cfg); }
+  size_t meb() const { return mat_bytes(cfg); }
+  size_t teb() const { return tab_bytes(cfg); }
+  // E4M3 matrices and their per-row scales, for the scale of a row pointer into any of them
+  struct QTensor { uintptr_t base; size_t bytes; int K; const float* scale; };
+  std::vector<QTensor> qtensors;
+  const float* scale_of(const void* w, int K) const {
+    const uintptr_t p = (uintptr_t)w;
+    for (const QTensor& q : qtensors)
+      if (p >= q.base && p < q.base + q.bytes && q.K == K && (p - q.base) % (size_t)K == 0) return q.scale + (p - q.base) / K;
+    return nullptr;
+  }
   size_t kvb() const { return kv_bytes(cfg); }
 };
 
@@ -360,8 +377,15 @@ int launch_gemv_w(tts_ctx* ctx, const GemvArgs& a) {
 // kGemvXRegs input elements per lane. Chunks re-stream the weights.
 int gemv(tts_ctx* ctx, GemvArgs a) {
   const int Mtot = a.M;
-  const int E = ctx->bf16() ? 8 : 4;
+  const int E = mat_per_unit(ctx->cfg);
   const int U = a.K / (64 * E);
+  if (ctx->fp8()) {
+    for (int s = 0; s < kMaxSeg; ++s) {
+      if (!a.w[s]) continue;
+      a.wscale[s] = ctx->scale_of(a.w[s], a.K);
+      if (!a.wscale[s]) return ctx->fail(TTS_E_STATE, "gemv: no E4M3 scale for a weight segment");
+    }
+  }
   int chunk = kMaxGemvM;
   while (chunk > 1 && chunk * U * E > kGemvXRegs) chunk >>= 1;
   if (a.src == SRC_VEC_THEN_TABLE && chunk < 2) return ctx->fail(TTS_E_SHAPE, "gemv: K=%d too large for paired rows", a.K);
@@ -382,7 +406,8 @@ int gemv(tts_ctx* ctx, GemvArgs a) {
     if (a.res) c.res = a.res + (size_t)m0 * a.res_stride;
     if (a.xn_out) c.xn_out = a.xn_out + (size_t)m0 * a.xn_stride;
     if (m0 + mc < Mtot) c.bump_pos = c.bump_frame = 0;  // counters advance once, with the last chunk
-    const int rc = ctx->bf16() ? launch_gemv_w<uint16_t>(ctx, c) : launch_gemv_w<float>(ctx, c);
+    const int rc = ctx->fp8() ? launch_gemv_w<uint8_t>(ctx, c)
+                   : (ctx->bf16() ? launch_gemv_w<uint16_t>(ctx, c) : launch_gemv_w<float>(ctx, c));
     if (rc) return rc;
     m0 += mc;
   }
@@ -495,7 +520,7 @@ int launch_attn_g(tts_ctx* ctx, const AttnArgs& a, int B) {
 }
 
 int attention(tts_ctx* ctx, const AttnArgs& a, int B) {
-  if (ctx->bf16()) return ctx->kv_bf16() ? launch_attn_g<uint16_t, uint16_t>(ctx, a, B) : launch_attn_g<uint16_t, float>(ctx, a, B);
+  if (ctx->tab16()) return ctx->kv_bf16() ? launch_attn_g<uint16_t, uint16_t>(ctx, a, B) : launch_attn_g<uint16_t, float>(ctx, a, B);
   return ctx->kv_bf16() ? launch_attn_g<float, uint16_t>(ctx, a, B) : launch_attn_g<float, float>(ctx, a, B);
 }
 
@@ -673,7 +698,7 @@ int embed_sum(tts_ctx* ctx, int B, const TokRef* refs, const TokRef* text = null
   std::memset(&e, 0, sizeof e);
   e.ntab = 1 + c.n_acoustic;
   e.H = c.talker.hidden;
-  const size_t ac_table = (size_t)c.codepred.vocab * c.talker.hidden * ctx->eb();
+  const size_t ac_table = (size_t)c.codepred.vocab * c.talker.hidden * ctx->teb();
   e.table[0] = ctx->embed_sem;
   e.rows[0] = c.talker.vocab;
   e.tok[0] = refs[0];
@@ -690,7 +715,7 @@ int embed_sum(tts_ctx* ctx, int B, const TokRef* refs, const TokRef* text = null
     e.text_n = text_n;
   }
   const int gx = (c.talker.hidden + 255) / 256;
-  if (ctx->bf16()) hipLaunchKernelGGL(k_embed_sum<uint16_t>, dim3(gx, B), dim3(256), 0, ctx->stream, e);
+  if (ctx->tab16()) hipLaunchKernelGGL(k_embed_sum<uint16_t>, dim3(gx, B), dim3(256), 0, ctx->stream, e);
   else hipLaunchKernelGGL(k_embed_sum<float>, dim3(gx, B), dim3(256), 0, ctx->stream, e);
   HIP_LAUNCH_CHECK();
   return TTS_OK;
@@ -703,7 +728,7 @@ int gather(tts_ctx* ctx, int src, int M, int H, const float* vec, int vec_stride
   g.src = src; g.M = M; g.H = H; g.vec = vec; g.vec_stride = vec_stride; g.table = table; g.table_rows = table_rows; g.tok = tok;
   g.x = out; g.x_stride = out_stride; g.st = ctx->st;
   const int gx = (H + 255) / 256;
-  if (ctx->bf16()) hipLaunchKernelGGL(k_gather<uint16_t>, dim3(gx, M), dim3(256), 0, ctx->stream, g);
+  if (ctx->tab16()) hipLaunchKernelGGL(k_gather<uint16_t>, dim3(gx, M), dim3(256), 0, ctx->stream, g);
   else hipLaunchKernelGGL(k_gather<float>, dim3(gx, M), dim3(256), 0, ctx->stream, g);
   HIP_LAUNCH_CHECK();
   return TTS_OK;
@@ -766,8 +791,8 @@ int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac,
                    int32_t* out, int ob, int of, int oo, int ouf, float* logits_out) {
   const auto& c = ctx->cfg;
   const int Hc = c.codepred.hidden, Ht = c.talker.hidden, Va = c.codepred.vocab;
-  const size_t ac_table = (size_t)Va * Ht * ctx->eb();
-  const size_t head_sz = (size_t)Va * Hc * ctx->eb();
+  const size_t ac_table = (size_t)Va * Ht * ctx->teb();
+  const size_t head_sz = (size_t)Va * Hc * ctx->meb();
   void* kc = ctx->ws + ctx->L.ck;
   void* vc = ctx->ws + ctx->L.cv;
   for (int j = 1; j <= c.n_acoustic; ++j) {
@@ -954,7 +979,8 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
   if (!ctx) return TTS_E_ARG;
   if (n < 0 || !names || !dev_ptrs || !shapes || !ranks || !dtypes) return ctx->fail(TTS_E_ARG, "load_weights: NULL argument");
   const tts_config& c = ctx->cfg;
-  struct Want { std::vector<int64_t> shape; const void** slot; };
+  // dtype -1: the config's weight dtype for matrices; -2: its gain / table dtype (bf16 for FP8)
+  struct Want { std::vector<int64_t> shape; const void** slot; int dtype = -1; };
   std::unordered_map<std::string, Want> want;
   StackW talker, cp;
   talker.c = c.talker; cp.c = c.codepred;
@@ -967,29 +993,42 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
     for (int i = 0; i < s.n_layers; ++i) {
       std::string p = std::string(prefix) + ".layers." + std::to_string(i) + ".";
       Layer& L = S.layers[i];
-      want[p + "attn_norm"] = {{H}, &L.attn_norm};
+      want[p + "attn_norm"] = {{H}, &L.attn_norm, -2};
       want[p + "wq"] = {{qd, H}, &L.wq};
       want[p + "wk"] = {{kd, H}, &L.wk};
       want[p + "wv"] = {{kd, H}, &L.wv};
-      want[p + "q_norm"] = {{s.head_dim}, &L.q_norm};
-      want[p + "k_norm"] = {{s.head_dim}, &L.k_norm};
+      want[p + "q_norm"] = {{s.head_dim}, &L.q_norm, -2};
+      want[p + "k_norm"] = {{s.head_dim}, &L.k_norm, -2};
       want[p + "wo"] = {{H, qd}, &L.wo};
-      want[p + "mlp_norm"] = {{H}, &L.mlp_norm};
+      want[p + "mlp_norm"] = {{H}, &L.mlp_norm, -2};
       want[p + "wg"] = {{s.ffn, H}, &L.wg};
       want[p + "wu"] = {{s.ffn, H}, &L.wu};
       want[p + "wd"] = {{H, s.ffn}, &L.wd};
     }
-    want[std::string(prefix) + ".final_norm"] = {{H}, &S.final_norm};
+    want[std::string(prefix) + ".final_norm"] = {{H}, &S.final_norm, -2};
   };
   add_stack("talker", talker);
   add_stack("cp", cp);
   const int64_t Ht = c.talker.hidden, Hc = c.codepred.hidden;
-  want["talker.embed_text"] = {{c.text_vocab, Ht}, &embed_text};
-  want["talker.embed_sem"] = {{c.talker.vocab, Ht}, &embed_sem};
+  want["talker.embed_text"] = {{c.text_vocab, Ht}, &embed_text, -2};
+  want["talker.embed_sem"] = {{c.talker.vocab, Ht}, &embed_sem, -2};
   want["talker.lm_head"] = {{c.talker.vocab, Ht}, &lm_head};
   if (Ht != Hc) want["cp.proj"] = {{Hc, Ht}, &proj};
-  want["cp.embed_ac"] = {{c.n_acoustic, c.codepred.vocab, Ht}, &embed_ac};
+  want["cp.embed_ac"] = {{c.n_acoustic, c.codepred.vocab, Ht}, &embed_ac, -2};
   want["cp.heads"] = {{c.n_acoustic, c.codepred.vocab, Hc}, &heads};
+  // E4M3 matrices: one fp32 scale per row ("<name>.scale", the matrix shape without its last dim)
+  std::vector<std::string> mats;
+  std::unordered_map<std::string, const void*> scale_ptr;
+  if (c.weight_dtype == TTS_DTYPE_FP8_E4M3) {
+    for (auto& kv : want)
+      if (kv.second.dtype == -1) mats.push_back(kv.first);
+    for (const std::string& m : mats) {
+      std::vector<int64_t> sh = want[m].shape;
+      sh.pop_back();
+      scale_ptr[m] = nullptr;
+      want[m + ".scale"] = {sh, &scale_ptr[m], TTS_DTYPE_F32};
+    }
+  }
   std::unordered_map<std::string, bool> seen;
   for (int i = 0; i < n; ++i) {
     if (!names[i]) return ctx->fail(TTS_E_ARG, "load_weights: name %d is NULL", i);
@@ -1003,7 +1042,9 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
       if (shapes[i * 4 + k] != shp[k])
         return ctx->fail(TTS_E_SHAPE, "load_weights: '%s' dim %zu is %lld, expected %lld", names[i], k, (long long)shapes[i * 4 + k],
                          (long long)shp[k]);
-    if (dtypes[i] != c.weight_dtype) return ctx->fail(TTS_E_SHAPE, "load_weights: '%s' dtype %d, expected %d", names[i], dtypes[i], c.weight_dtype);
+    const int wdt = it->second.dtype == -1 ? c.weight_dtype
+                    : (it->second.dtype == -2 ? (c.weight_dtype == TTS_DTYPE_F32 ? TTS_DTYPE_F32 : TTS_DTYPE_BF16) : it->second.dtype);
+    if (dtypes[i] != wdt) return ctx->fail(TTS_E_SHAPE, "load_weights: '%s' dtype %d, expected %d", names[i], dtypes[i], wdt);
     if (!dev_ptrs[i]) return ctx->fail(TTS_E_ARG, "load_weights: '%s' pointer is NULL", names[i]);
     if (((uintptr_t)dev_ptrs[i]) & 15) return ctx->fail(TTS_E_ARG, "load_weights: '%s' is not 16-byte aligned", names[i]);
     *it->second.slot = dev_ptrs[i];
@@ -1014,6 +1055,13 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
   ctx->cp = cp;
   ctx->embed_text = embed_text; ctx->embed_sem = embed_sem; ctx->lm_head = lm_head; ctx->proj = proj;
   ctx->embed_ac = embed_ac; ctx->heads = heads;
+  ctx->qtensors.clear();
+  for (const std::string& m : mats) {
+    const auto& sh = want[m].shape;
+    size_t bytes = 1;
+    for (int64_t d : sh) bytes *= (size_t)d;
+    ctx->qtensors.push_back({(uintptr_t)*want[m].slot, bytes, (int)sh.back(), (const float*)scale_ptr[m]});
+  }
   ctx->weights_ok = true;
   ctx->prefilled = false;
   drop_graph(ctx);

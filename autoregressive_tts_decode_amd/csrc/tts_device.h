@@ -76,9 +76,13 @@ __device__ __forceinline__ void store_elem(float* p, float v) { *p = v; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Matrix element types: float (fp32), uint16_t (bf16 bit patterns), uint8_t (E4M3 codes with a
+// per-row fp32 scale). GT is the type of the gains and embedding tables next to them: E4M3
+// matrices come with bf16 gains and tables.
 template <typename WT> struct WTraits;
-template <> struct WTraits<float> { static constexpr int E = 4; };     // elements per 16-byte lane load
-template <> struct WTraits<uint16_t> { static constexpr int E = 8; };
+template <> struct WTraits<float> { static constexpr int E = 4; using GT = float; };     // elements per 16-byte lane load
+template <> struct WTraits<uint16_t> { static constexpr int E = 8; using GT = uint16_t; };
+template <> struct WTraits<uint8_t> { static constexpr int E = 16; using GT = uint16_t; };
 
 // Unpack one 16-byte weight chunk into E floats.
 __device__ __forceinline__ void unpack(const u32x4& w, float (&f)[8], uint16_t*) {
@@ -87,6 +91,33 @@ __device__ __forceinline__ void unpack(const u32x4& w, float (&f)[8], uint16_t*)
 }
 __device__ __forceinline__ void unpack(const u32x4& w, float (&f)[8], float*) {
   f[0] = __uint_as_float(w.x); f[1] = __uint_as_float(w.y); f[2] = __uint_as_float(w.z); f[3] = __uint_as_float(w.w);
+}
+// E4M3 (OCP) codes, byte i of the chunk -> f[i]: the CDNA4 conversion widens two bytes per
+// instruction (the low or the high half of a dword), exactly.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void unpack(const u32x4& w, float (&f)[16], uint8_t*) {
+  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)d[i], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)d[i], true);
+    f[4 * i] = lo.x; f[4 * i + 1] = lo.y; f[4 * i + 2] = hi.x; f[4 * i + 3] = hi.y;
+  }
+}
+
+// E consecutive elements of type T (fp32 or bf16) at p, as fp32, in 16-byte loads.
+template <typename T, int E>
+__device__ __forceinline__ void load_vals(const T* p, float (&f)[E]) {
+  constexpr int PER = 16 / (int)sizeof(T);
+  static_assert(E % PER == 0, "whole 16-byte loads");
+#pragma unroll
+  for (int i = 0; i < E / PER; ++i) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p + i * PER);
+    float g[8];
+    unpack(w, g, (T*)nullptr);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) f[i * PER + e] = g[e];
+  }
 }
 
 // ---------------------------------------------------------------------------- wave reductions (DPP)
@@ -130,6 +161,7 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
 struct GemvArgs {
   const void* w[kMaxSeg];   // segments share K; their rows are concatenated
+  const float* wscale[kMaxSeg];  // E4M3 weights: per-row scales of each segment (else unused)
   int32_t seg_rows[kMaxSeg];
   int32_t nseg;
   int32_t N;                // total output rows (SwiGLU: rows per branch)
@@ -138,10 +170,10 @@ struct GemvArgs {
   int32_t src;              // enum Src
   const float* x;           // fp32 input rows
   int32_t x_stride;
-  const void* table;        // embedding table [table_rows, K] (weight dtype) for gathered rows
+  const void* table;        // embedding table [table_rows, K] (WTraits<WT>::GT) for gathered rows
   int32_t table_rows;
   TokRef tok;               // token of gathered row (indexed by stream)
-  const void* gain;         // RMSNorm gain [K] (weight dtype); used by the NORM variants
+  const void* gain;         // RMSNorm gain [K] (WTraits<WT>::GT); used by the NORM variants
   float eps;
   float* y;
   int32_t y_stride;
@@ -167,13 +199,9 @@ __device__ __forceinline__ void gemv_load_x(const GemvArgs& a, int m, int k0, fl
   const int stream = (a.src == SRC_VEC_THEN_TABLE) ? (m >> 1) : m;
   const bool from_table = (a.src == SRC_TABLE) || (a.src == SRC_VEC_THEN_TABLE && (m & 1));
   if (from_table) {
+    using GT = typename WTraits<WT>::GT;
     const int t = clamp_tok(tok_at(a.tok, a.st, stream), a.table_rows);
-    const WT* tp = reinterpret_cast<const WT*>(a.table) + (size_t)t * a.K + k0;
-    const u32x4 w = *reinterpret_cast<const u32x4*>(tp);
-    float g[8];
-    unpack(w, g, (WT*)nullptr);
-#pragma unroll
-    for (int e = 0; e < E; ++e) f[e] = g[e];
+    load_vals<GT, E>(reinterpret_cast<const GT*>(a.table) + (size_t)t * a.K + k0, f);
   } else {
     const float* xp = a.x + (size_t)((a.src == SRC_VEC_THEN_TABLE) ? stream : m) * a.x_stride + k0;
 #pragma unroll
@@ -185,12 +213,13 @@ __device__ __forceinline__ void gemv_load_x(const GemvArgs& a, int m, int k0, fl
 }
 
 template <typename WT>
-__device__ __forceinline__ const WT* gemv_row_ptr(const GemvArgs& a, int row) {
+__device__ __forceinline__ const WT* gemv_row_ptr(const GemvArgs& a, int row, const float** scale = nullptr) {
   int s = 0, off = 0;
 #pragma unroll
   for (int i = 0; i < kMaxSeg - 1; ++i) {
     if (s < a.nseg - 1 && row >= off + a.seg_rows[s]) { off += a.seg_rows[s]; ++s; }
   }
+  if (scale) *scale = a.wscale[s] + (row - off);
   return reinterpret_cast<const WT*>(a.w[s]) + (size_t)(row - off) * a.K;
 }
 
@@ -198,9 +227,14 @@ __device__ __forceinline__ const WT* gemv_row_ptr(const GemvArgs& a, int row) {
 // slice of each input row (and of the norm gain), then streams RW weight rows
 // (PAIR: RW gate rows and RW up rows) with all loads in flight, reduces each
 // row across the wave with DPP and applies the epilogue. No LDS, no barriers.
+// E4M3 weights (WT = uint8_t) are widened in registers and each row's sum is
+// multiplied by its scale before the epilogue.
 template <typename WT, int U, int M, bool PAIR, bool NORM>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+  using GT = typename WTraits<WT>::GT;
+  constexpr bool Q8 = sizeof(WT) == 1;
   constexpr int E = WTraits<WT>::E;
+  constexpr int EU = E < 8 ? 8 : E;  // unpack buffer (fp32 fills 4 of 8)
   constexpr int CH = 64 * E;
   constexpr int RW = GemvShape<U, PAIR>::RW;
   constexpr int NR = PAIR ? 2 * RW : RW;
@@ -218,22 +252,19 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   float gv[NORM ? U : 1][E];
   if constexpr (NORM) {
 #pragma unroll
-    for (int c = 0; c < U; ++c) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const WT*>(a.gain) + c * CH + lane * E);
-      float g[8];
-      unpack(w, g, (WT*)nullptr);
-#pragma unroll
-      for (int e = 0; e < E; ++e) gv[c][e] = g[e];
-    }
+    for (int c = 0; c < U; ++c) load_vals<GT, E>(reinterpret_cast<const GT*>(a.gain) + c * CH + lane * E, gv[c]);
   }
 
-  // 2. every weight load of this wave
+  // 2. every weight load of this wave (and the rows' scales)
   u32x4 wb[NR][U];
+  float wsc[Q8 ? NR : 1];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     int row = r0 + (PAIR ? (r % RW) : r);
     if (row > a.N - 1) row = a.N - 1;
-    const WT* wp = PAIR ? reinterpret_cast<const WT*>(a.w[r / RW]) + (size_t)row * a.K : gemv_row_ptr<WT>(a, row);
+    const float* sp = nullptr;
+    const WT* wp = PAIR ? reinterpret_cast<const WT*>(a.w[r / RW]) + (size_t)row * a.K : gemv_row_ptr<WT>(a, row, &sp);
+    if constexpr (Q8) wsc[r] = PAIR ? a.wscale[r / RW][row] : *sp;
     const u32x4* p = reinterpret_cast<const u32x4*>(wp) + lane;
     if (a.nontemporal) {
 #pragma unroll
@@ -278,7 +309,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
   for (int c = 0; c < U; ++c) {
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
-      float wf[8];
+      float wf[EU];
       unpack(wb[r][c], wf, (WT*)nullptr);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
@@ -297,8 +328,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       float v = wave_sum(acc[r][m]);
+      if constexpr (Q8) v *= wsc[r];
       if (PAIR) {
-        const float u = wave_sum(acc[RW + r][m]);
+        float u = wave_sum(acc[RW + r][m]);
+        if constexpr (Q8) u *= wsc[RW + r];
         v = silu(v) * u;
       }
       if (lane == 0 && row < a.N) {

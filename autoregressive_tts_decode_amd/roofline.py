@@ -37,8 +37,19 @@ def rtf_from_fps(fps: float) -> float:
     return FRAME_RATE_HZ / fps
 
 
-def _wbytes(cfg: ModelCfg) -> int:
-    return 2 if cfg.weight_dtype == "bf16" else 4
+def _mbytes(cfg: ModelCfg) -> int:
+    """Bytes per projection-matrix element (E4M3 codes: 1)."""
+    return {"fp32": 4, "bf16": 2, "fp8": 1}[cfg.weight_dtype]
+
+
+def _tbytes(cfg: ModelCfg) -> int:
+    """Bytes per gain / embedding element (bf16 next to E4M3 matrices)."""
+    return 4 if cfg.weight_dtype == "fp32" else 2
+
+
+def _matrix_bytes(cfg: ModelCfg, rows: int, cols: int) -> int:
+    """A projection matrix as stored: its elements, plus one fp32 scale per row for E4M3."""
+    return rows * cols * _mbytes(cfg) + (4 * rows if cfg.weight_dtype == "fp8" else 0)
 
 
 def layer_weight_elems(s: StackCfg) -> int:
@@ -46,6 +57,14 @@ def layer_weight_elems(s: StackCfg) -> int:
     proj = s.hidden * (qd + 2 * kd) + qd * s.hidden + 3 * s.hidden * s.ffn
     norms = 2 * s.hidden + 2 * s.head_dim
     return proj + norms
+
+
+def layer_weight_bytes(cfg: ModelCfg, s: StackCfg) -> int:
+    """Stored bytes of one decoder layer: the seven projections and the four gains."""
+    qd, kd = s.n_q_heads * s.head_dim, s.n_kv_heads * s.head_dim
+    mats = (_matrix_bytes(cfg, qd + 2 * kd, s.hidden) + _matrix_bytes(cfg, s.hidden, qd)
+            + _matrix_bytes(cfg, 2 * s.ffn, s.hidden) + _matrix_bytes(cfg, s.hidden, s.ffn))
+    return mats + (2 * s.hidden + 2 * s.head_dim) * _tbytes(cfg)
 
 
 def kv_bytes_per_position(s: StackCfg, kv_elem_bytes: int) -> int:
@@ -61,14 +80,14 @@ def algorithmic_bytes(cfg: ModelCfg, talker_positions_read: float, batch: int = 
     the batch; embeddings, KV reads scale with it.
     """
     t, c = cfg.talker, cfg.codepred
-    b = _wbytes(cfg)
-    kvb = b if kv_elem_bytes is None else kv_elem_bytes
-    talker_w = (t.n_layers * layer_weight_elems(t) + t.hidden + t.vocab * t.hidden) * b
-    emb_rows = batch * (1 + cfg.n_acoustic) * t.hidden * b
-    cp_step_w = (c.n_layers * layer_weight_elems(c) + c.hidden + c.vocab * c.hidden) * b
+    tb = _tbytes(cfg)
+    kvb = tb if kv_elem_bytes is None else kv_elem_bytes
+    talker_w = t.n_layers * layer_weight_bytes(cfg, t) + t.hidden * tb + _matrix_bytes(cfg, t.vocab, t.hidden)
+    emb_rows = batch * (1 + cfg.n_acoustic) * t.hidden * tb
+    cp_step_w = c.n_layers * layer_weight_bytes(cfg, c) + c.hidden * tb + _matrix_bytes(cfg, c.vocab, c.hidden)
     if t.hidden != c.hidden:
-        cp_step_w += c.hidden * t.hidden * b
-    cp_rows = batch * (1 + cfg.n_acoustic) * t.hidden * b  # E_sem row + 14 acoustic rows (+h_T) fed to the CodePredictor
+        cp_step_w += _matrix_bytes(cfg, c.hidden, t.hidden)
+    cp_rows = batch * (1 + cfg.n_acoustic) * t.hidden * tb  # E_sem row + 14 acoustic rows (+h_T) fed to the CodePredictor
     kv_t = batch * t.n_layers * kv_bytes_per_position(t, kvb) * talker_positions_read
     # CodePredictor attention over positions 0..j for its 16 positions (0..15).
     cp_positions = sum(j + 1 for j in range(cfg.n_acoustic + 1))

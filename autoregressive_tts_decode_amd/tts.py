@@ -15,7 +15,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .config import ModelCfg, SamplingCfg, StackCfg, N_ACOUSTIC, tensor_specs
+from .config import ModelCfg, SamplingCfg, StackCfg, N_ACOUSTIC, tensor_specs, scale_specs
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtts.so")
 
@@ -28,7 +28,8 @@ TTS_E_HIP = -5
 TTS_E_UNSUPPORTED = -6
 STATUS_NAMES = {0: "TTS_OK", -1: "TTS_E_ARG", -2: "TTS_E_SHAPE", -3: "TTS_E_CAPACITY", -4: "TTS_E_STATE",
                 -5: "TTS_E_HIP", -6: "TTS_E_UNSUPPORTED"}
-DTYPE_F32, DTYPE_BF16 = 0, 1
+DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
+_WEIGHT_DTYPE = {"fp32": DTYPE_F32, "bf16": DTYPE_BF16, "fp8": DTYPE_FP8_E4M3}
 
 EXPORTED = ["tts_workspace_bytes", "tts_create", "tts_load_weights", "tts_prefill", "tts_talker_step",
             "tts_talker_step_text", "tts_set_text_stream", "tts_prefill_ragged", "tts_set_stop", "tts_codepred_frame", "tts_sample", "tts_run_frames", "tts_set_exec_mode", "tts_get_exec_mode", "tts_set_prefill_mode", "tts_get_prefill_mode",
@@ -111,7 +112,7 @@ def config_struct(model: ModelCfg, max_batch: int, max_cache_steps: int, max_fra
         return StackCfgC(s.n_layers, s.hidden, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn, s.vocab)
 
     return ConfigC(sc(model.talker), sc(model.codepred), model.text_vocab, model.n_acoustic, model.rms_eps,
-                   model.rope_theta, DTYPE_BF16 if model.weight_dtype == "bf16" else DTYPE_F32,
+                   model.rope_theta, _WEIGHT_DTYPE[model.weight_dtype],
                    DTYPE_BF16 if kv_dtype == "bf16" else DTYPE_F32, max_batch, max_cache_steps, max_frames)
 
 
@@ -199,7 +200,7 @@ class TTSDecoder:
             ranks[i] = t.dim()
             for j, s in enumerate(t.shape):
                 shapes[4 * i + j] = s
-            dtypes[i] = DTYPE_BF16 if t.dtype == torch.bfloat16 else (DTYPE_F32 if t.dtype == torch.float32 else 99)
+            dtypes[i] = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_F32, torch.uint8: DTYPE_FP8_E4M3}.get(t.dtype, 99)
         self._check(self.lib.tts_load_weights(self.ctx, n, c_names, ptrs, shapes, ranks, dtypes), "tts_load_weights")
         self._weights = weights
 
@@ -285,13 +286,17 @@ class TTSDecoder:
 
 
 def weights_to_device(weights: dict, model: ModelCfg, device="cuda") -> dict:
-    """Upload generator arrays (fp32, or uint16 bf16 bit patterns) as torch tensors."""
+    """Upload generator arrays as torch tensors: fp32 arrays as float32, uint16 bf16 bit patterns
+    as bfloat16, uint8 E4M3 codes as uint8 (fp8 models; their '<name>.scale' arrays as float32)."""
     import torch
     out = {}
-    for name, _, _ in tensor_specs(model):
-        a = weights[name]
-        if model.weight_dtype == "bf16":
-            t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    names = [n for n, _, _ in tensor_specs(model)] + [n for n, _ in scale_specs(model)]
+    for name in names:
+        a = np.ascontiguousarray(weights[name])
+        if a.dtype == np.uint16:
+            t = torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+        elif a.dtype == np.uint8:
+            t = torch.from_numpy(a).to(device)
         else:
             t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
         out[name] = t

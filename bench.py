@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--kv-dtype", default="fp32", choices=["fp32", "bf16"])
     p.add_argument("--ragged", action="store_true",
                    help="prompt lengths drawn per stream (seed 7) from [prefill/4, prefill], prefilled ragged")
+    p.add_argument("--exec", default="auto", choices=["auto", "kernels"],
+                   help="auto: the persistent step kernels where the config allows them; kernels: per-op kernels only")
     p.add_argument("--kernel-iters", type=int, default=40,
                    help="back-to-back launches of the dominant kernel timed for the roofline")
     return p.parse_args()
@@ -89,6 +91,8 @@ def main():
     dw = tts.weights_to_device(weights, model, d)
     dec = tts.TTSDecoder(model, B, cap, W + K, kv_dtype=args.kv_dtype)
     dec.load_weights(dw)
+    if args.exec == "kernels":
+        dec.set_exec_mode(tts.EXEC_KERNELS)
     ids = torch.from_numpy(synth.make_text_ids(wl)).to(d)
     u = torch.from_numpy(synth.make_uniforms(wl, frames=W + K)).to(d)
     codes = torch.zeros((B, W + K, 16), dtype=torch.int32, device=d)
@@ -160,13 +164,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if model.weight_dtype == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3 weights, f32 arithmetic", "fp32": "f32"}[model.weight_dtype],
         "data": "synthetic",
         "config": {"workload": f"{model.name}: Talker 28x2048 (16q/8kv heads, d128, FFN 6144, Vs 3072) + "
                                f"CodePredictor 5x1024 (FFN 3072, 15 heads x 2048); batch {B}, prefill "
                                f"{wl.prefill_len} ids, {W + K} frames ({'sampled' if wl.semantic.do_sample else 'greedy'})"
                    if args.workload.startswith("1.7b") else f"{model.name}; batch {B}, prefill {wl.prefill_len}, {W + K} frames",
                    "batch": B, "prefill_len": wl.prefill_len, "frames": W + K, "timed_frames": K,
+                   "exec": "persistent" if mode == tts.EXEC_PERSISTENT else "per-op kernels",
                    "kv_cache": dec.kv_dtype},
         "rtf": round(roofline.rtf_from_fps(fps / B), 6),
         "prefill_ms": round(statistics.median(prefill_ms), 2),

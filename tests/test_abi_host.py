@@ -62,6 +62,19 @@ def test_workspace_bytes_rejects_bad_configs(field, value):
     assert lib.tts_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == tts.TTS_E_SHAPE
 
 
+def test_workspace_bytes_fp8_needs_1024_multiples():
+    """E4M3 matrices are read 16 per 16-byte lane load, so every contraction width must be a
+    multiple of 1024 (64 lanes x 16): the 1.7B shapes pass, the tiny model's 256 does not."""
+    lib = tts.load_library()
+    n = ctypes.c_size_t(0)
+    ok = tts.config_struct(config.MODELS["1.7b-fp8"], 1, 512, 64)
+    assert lib.tts_workspace_bytes(ctypes.byref(ok), ctypes.byref(n)) == tts.TTS_OK and n.value > 0
+    tiny = config.ModelCfg(name="tiny-fp8", talker=config.TINY.talker, codepred=config.TINY.codepred,
+                           text_vocab=config.TINY.text_vocab, weight_dtype="fp8")
+    bad = tts.config_struct(tiny, 1, 64, 8)
+    assert lib.tts_workspace_bytes(ctypes.byref(bad), ctypes.byref(n)) == tts.TTS_E_SHAPE
+
+
 def test_workspace_bytes_rejects_unsupported_stack_shapes():
     lib = tts.load_library()
     n = ctypes.c_size_t(0)

@@ -434,6 +434,83 @@ def test_bf16_run_frames_greedy_both_modes_match_oracle_until_a_near_tie(bf16_mo
     torch.cuda.empty_cache()
 
 
+# ----------------------------------------------------------------------------- FP8 (E4M3) weights
+
+@pytest.fixture(scope="module", params=["0.6b-fp8", "1.7b-fp8"])
+def fp8_model(request):
+    model = config.MODELS[request.param]
+    w = synth.make_weights(model, 0)
+    return request.param, model, w
+
+
+def test_fp8_teacher_forced_step_parity(fp8_model):
+    """Weight-only E4M3 decode (per-op kernels, GEMV prefill) against the oracle run on the
+    matrices the codes and row scales stand for. Both sides compute in fp32 from the same
+    weights, so the bf16 models' bar applies."""
+    name, model, w = fp8_model
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    ids = synth.random_ids(16, model.text_vocab, seed=1)
+    F = 3
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((1, F, 16), np.float32))
+    del orc
+    dec, dw = make_decoder(model, 1, 64 + 240, 240, w)
+    mode, supported = dec.exec_mode()
+    assert supported == 0 and mode == tts.EXEC_KERNELS, "E4M3 weights run on the per-op kernels"
+    assert dec.prefill_mode() == tts.PREFILL_STEPS
+    print(f"{name}: running", flush=True)
+    sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F)
+    es, ea, n, ex = check_step_parity(model, ref, sem, ac, tok, 1e-2)
+    print(f"{name}: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}")
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
+def test_fp8_frame_graph_greedy_matches_oracle_until_a_near_tie():
+    """The captured frame graph on E4M3 weights, free-running: codes equal the oracle's up to the
+    first step the oracle finds near a tie."""
+    model = config.MODELS["0.6b-fp8"]
+    w = synth.make_weights(model, 0)
+    F = 8
+    ids = synth.random_ids(16, model.text_vocab, seed=3)
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((1, F, 16), np.float32))
+    del orc
+    dec, dw = make_decoder(model, 1, 64, F + 4, w)
+    d = dev()
+    codes = torch.full((1, F + 4, 16), -1, dtype=torch.int32, device=d)
+    dec.prefill(torch.from_numpy(ids).to(d))
+    dec.run_frames(F, GREEDY, GREEDY, None, codes)
+    got = codes.cpu().numpy()[:, :F].reshape(-1)
+    diff = np.nonzero(got != ref["codes"].reshape(-1))[0]
+    if diff.size:
+        t, j = divmod(int(diff[0]), 16)
+        lg = ref["sem_logits"][0, t] if j == 0 else ref["ac_logits"][0, t, j - 1]
+        assert top2_margin(lg) <= 0.05, f"divergence at frame {t} code {j}, margin {top2_margin(lg):.3f}"
+    print(f"0.6b-fp8 frame graph: identical for {diff[0] if diff.size else got.size} of {got.size} codes", flush=True)
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
+def test_fp8_load_weights_checks_scales_and_dtypes():
+    """An E4M3 context wants every matrix as uint8 with its fp32 '.scale', gains and tables as bf16."""
+    model = config.MODELS["0.6b-fp8"]
+    w = synth.make_weights(model, 0)
+    dw = tts.weights_to_device(w, model, dev())
+    dec = tts.TTSDecoder(model, 1, 64, 8)
+    missing = dict(dw)
+    del missing["talker.layers.3.wo.scale"]
+    with pytest.raises(RuntimeError, match="wo.scale"):
+        dec.load_weights(missing)
+    wrong = dict(dw)
+    wrong["talker.layers.0.attn_norm"] = dw["talker.layers.0.attn_norm"].float()
+    with pytest.raises(RuntimeError, match="dtype"):
+        dec.load_weights(wrong)
+    dec.load_weights(dw)
+    dec.close()
+
+
 # ----------------------------------------------------------------------------- streaming text
 
 def test_tiny_streaming_text_teacher_forced_and_frame_graph(tiny):

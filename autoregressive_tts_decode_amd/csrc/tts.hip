@@ -227,7 +227,7 @@ bool xtk_capable(const tts_config& c) {
 // dimension of the Talker a multiple of the 64 x 64 x 64 tile.
 bool prefill_gemm_capable(const tts_config& c) {
   const tts_stack_cfg& t = c.talker;
-  if (c.weight_dtype != TTS_DTYPE_BF16 || t.head_dim != 128) return false;
+  if ((c.weight_dtype != TTS_DTYPE_BF16 && c.weight_dtype != TTS_DTYPE_FP8_E4M3) || t.head_dim != 128) return false;
   const int qd = t.n_q_heads * t.head_dim, kd = t.n_kv_heads * t.head_dim;
   return t.hidden % 64 == 0 && qd % 64 == 0 && kd % 64 == 0 && t.ffn % 64 == 0;
 }
@@ -424,12 +424,27 @@ int gather(tts_ctx* ctx, int src, int M, int H, const float* vec, int vec_stride
            float* out, int out_stride);
 
 bool gemm_routes(const tts_ctx* ctx, const GemvArgs& a) {
-  if (!ctx->pgemm_ok || !ctx->bf16() || a.M < kGemmMinRows || a.K % kGBK) return false;
+  if (!ctx->pgemm_ok || !(ctx->bf16() || ctx->fp8()) || a.M < kGemmMinRows || a.K % kGBK) return false;
   for (int s = 0; s < a.nseg; ++s)
     if (a.seg_rows[s] % kGBN) return false;
   if (a.epi == EPI_RESID && (a.res != a.y || a.res_stride != a.y_stride)) return false;
   if (a.epi == EPI_SWIGLU && (a.nseg != 2 || a.y_stride != a.N)) return false;
   return a.M <= ctx->cfg.max_batch * kPrefillChunk;  // the staging buffers' rows
+}
+
+// The MFMA GEMM on the context's weight type (E4M3: the segments' row scales looked up here).
+int launch_gemm(tts_ctx* ctx, GemmArgs g, dim3 grid) {
+  if (ctx->fp8()) {
+    for (int s = 0; s < g.nseg; ++s) {
+      g.wscale[s] = ctx->scale_of(g.w[s], g.K);
+      if (!g.wscale[s]) return ctx->fail(TTS_E_STATE, "gemm: no E4M3 scale for a weight segment");
+    }
+    hipLaunchKernelGGL(k_gemm_bf16<true>, grid, dim3(256), 0, ctx->stream, g);
+  } else {
+    hipLaunchKernelGGL(k_gemm_bf16<false>, grid, dim3(256), 0, ctx->stream, g);
+  }
+  HIP_LAUNCH_CHECK();
+  return TTS_OK;
 }
 
 int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
@@ -472,7 +487,7 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
     hipLaunchKernelGGL(k_zero_rows, dim3(a.M), dim3(256), 0, ctx->stream, g.C, g.ldc, N);
     HIP_LAUNCH_CHECK();
   }
-  hipLaunchKernelGGL(k_gemm_bf16, dim3(N / kGBN, (a.M + kGBM - 1) / kGBM, ks), dim3(256), 0, ctx->stream, g);
+  if (int rc = launch_gemm(ctx, g, dim3(N / kGBN, (a.M + kGBM - 1) / kGBM, ks))) return rc;
   HIP_LAUNCH_CHECK();
   if (a.epi == EPI_SWIGLU) {
     hipLaunchKernelGGL(k_swiglu_rows, dim3(std::min((a.M * a.N + 255) / 256, 4096)), dim3(256), 0, ctx->stream, GU, a.M, a.N, a.y);
@@ -636,9 +651,7 @@ int prefill_gemm(tts_ctx* ctx, const int32_t* ids, int B, int n) {
     std::memset(&a, 0, sizeof a);
     a.A = A; a.lda = lda; a.rs = rs; a.gain = gain; a.C = C; a.ldc = N; a.M = M; a.N = N; a.K = K; a.add = add; a.kslice = K;
     for (auto& sg : segs) { a.w[a.nseg] = sg.first; a.seg_rows[a.nseg] = sg.second; ++a.nseg; }
-    hipLaunchKernelGGL(k_gemm_bf16, dim3(N / kGBN, (M + kGBM - 1) / kGBM), dim3(256), 0, ctx->stream, a);
-    HIP_LAUNCH_CHECK();
-    return TTS_OK;
+    return launch_gemm(ctx, a, dim3(N / kGBN, (M + kGBM - 1) / kGBM));
   };
   for (int p0 = 0; p0 < n; p0 += kPrefillChunk) {
     const int P = std::min(kPrefillChunk, n - p0), M = B * P;

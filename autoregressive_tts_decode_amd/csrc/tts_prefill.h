@@ -25,7 +25,8 @@ struct GemmArgs {
   int lda;
   const float* rs;    // [M] row scale or nullptr
   const void* gain;   // [K] bf16 or nullptr
-  const void* w[3];
+  const void* w[3];   // bf16 rows, or E4M3 codes (Q8) with per-row fp32 scales in wscale
+  const float* wscale[3];
   int seg_rows[3], nseg;
   float* C;
   int ldc;
@@ -39,6 +40,9 @@ struct GemmArgs {
 constexpr int kGBM = 64, kGBN = 64, kGBK = 64, kGLD = kGBK + 8;  // tile, LDS row stride (bf16)
 
 // One 64 x 64 tile of C per workgroup (4 waves, each 32 x 32 = 2 x 2 MFMA 16x16x32 blocks).
+// Q8: the weights are E4M3 codes; every code is a bf16 value exactly, so the B tile is widened to
+// bf16 as it is staged and each output column (weight row) is multiplied by its scale at the end.
+template <bool Q8>
 __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
   __shared__ __align__(16) __bf16 Ahi[kGBM][kGLD];
   __shared__ __align__(16) __bf16 Amid[kGBM][kGLD];
@@ -48,14 +52,15 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
   const int n0 = blockIdx.x * kGBN, m0 = blockIdx.y * kGBM;
   int seg = 0, nrel = n0;
   while (seg + 1 < a.nseg && nrel >= a.seg_rows[seg]) { nrel -= a.seg_rows[seg]; ++seg; }
-  const uint16_t* W = reinterpret_cast<const uint16_t*>(a.w[seg]) + (size_t)nrel * a.K;
+  constexpr int WB = Q8 ? 1 : 2;  // bytes per weight element
+  const char* W = reinterpret_cast<const char*>(a.w[seg]) + (size_t)nrel * a.K * WB;
   const int kbeg = blockIdx.z * a.kslice, kend = min(kbeg + a.kslice, a.K);
   const bool split = a.kslice < a.K;
   const int lr = tid >> 2, lk = (tid & 3) * 16;  // loader: row lr of the tile, 16 k from lk
   const bool arow = m0 + lr < a.M;
   const float rsc = (a.rs && arow) ? a.rs[m0 + lr] : 1.f;
   const float* Ap = a.A + (size_t)(m0 + lr) * a.lda + lk;
-  const uint16_t* Wp = W + (size_t)lr * a.K + lk;
+  const char* Wp = W + ((size_t)lr * a.K + lk) * WB;
   const uint16_t* gp = reinterpret_cast<const uint16_t*>(a.gain);
   const int wm = wave >> 1, wn = wave & 1, lq = lane >> 4, lc = lane & 15;
   f32x4v acc[2][2];
@@ -70,8 +75,8 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
   auto load_step = [&](int k0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) an[q] = arow ? *reinterpret_cast<const float4*>(Ap + k0 + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
-    bn0 = *reinterpret_cast<const u32x4*>(Wp + k0);
-    bn1 = *reinterpret_cast<const u32x4*>(Wp + k0 + 8);
+    bn0 = *reinterpret_cast<const u32x4*>(Wp + (size_t)k0 * WB);
+    if constexpr (!Q8) bn1 = *reinterpret_cast<const u32x4*>(Wp + (size_t)k0 * WB + 16);
     if (gp) {
       gn0 = *reinterpret_cast<const u32x4*>(gp + k0 + lk);
       gn1 = *reinterpret_cast<const u32x4*>(gp + k0 + lk + 8);
@@ -109,8 +114,18 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
       Amid[lr][lk + e] = mid;
       Alo[lr][lk + e] = (__bf16)(r1 - (float)mid);
     }
-    *reinterpret_cast<u32x4*>(&Bs[lr][lk]) = b0;
-    *reinterpret_cast<u32x4*>(&Bs[lr][lk + 8]) = b1;
+    if constexpr (Q8) {
+      float wf[16];
+      unpack(b0, wf, (uint8_t*)nullptr);
+      uint32_t pk[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pk[e] = (__float_as_uint(wf[2 * e]) >> 16) | (__float_as_uint(wf[2 * e + 1]) & 0xffff0000u);
+      *reinterpret_cast<u32x4*>(&Bs[lr][lk]) = (u32x4){pk[0], pk[1], pk[2], pk[3]};
+      *reinterpret_cast<u32x4*>(&Bs[lr][lk + 8]) = (u32x4){pk[4], pk[5], pk[6], pk[7]};
+    } else {
+      *reinterpret_cast<u32x4*>(&Bs[lr][lk]) = b0;
+      *reinterpret_cast<u32x4*>(&Bs[lr][lk + 8]) = b1;
+    }
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < kGBK; kk += 32) {
@@ -134,6 +149,11 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
     }
   }
   // lane holds C[4 lq + r][lc] of each 16 x 16 block
+  float csc[2] = {1.f, 1.f};
+  if constexpr (Q8) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) csc[j] = a.wscale[seg][nrel + wn * 32 + j * 16 + lc];
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -143,8 +163,9 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
         const int m = m0 + wm * 32 + i * 16 + 4 * lq + r, n = n0 + wn * 32 + j * 16 + lc;
         if (m < a.M) {
           float* c = a.C + (size_t)m * a.ldc + n;
-          if (split) atomicAdd(c, acc[i][j][r]);
-          else *c = a.add ? *c + acc[i][j][r] : acc[i][j][r];
+          const float v = Q8 ? acc[i][j][r] * csc[j] : acc[i][j][r];
+          if (split) atomicAdd(c, v);
+          else *c = a.add ? *c + v : v;
         }
       }
 }

@@ -444,7 +444,7 @@ def fp8_model(request):
 
 
 def test_fp8_teacher_forced_step_parity(fp8_model):
-    """Weight-only E4M3 decode (per-op kernels, GEMV prefill) against the oracle run on the
+    """Weight-only E4M3 decode (per-op kernels, MFMA GEMM prefill) against the oracle run on the
     matrices the codes and row scales stand for. Both sides compute in fp32 from the same
     weights, so the bf16 models' bar applies."""
     name, model, w = fp8_model
@@ -456,7 +456,7 @@ def test_fp8_teacher_forced_step_parity(fp8_model):
     dec, dw = make_decoder(model, 1, 64 + 240, 240, w)
     mode, supported = dec.exec_mode()
     assert supported == 0 and mode == tts.EXEC_KERNELS, "E4M3 weights run on the per-op kernels"
-    assert dec.prefill_mode() == tts.PREFILL_STEPS
+    assert dec.prefill_mode() == tts.PREFILL_GEMM
     print(f"{name}: running", flush=True)
     sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F)
     es, ea, n, ex = check_step_parity(model, ref, sem, ac, tok, 1e-2)
@@ -488,6 +488,27 @@ def test_fp8_frame_graph_greedy_matches_oracle_until_a_near_tie():
         lg = ref["sem_logits"][0, t] if j == 0 else ref["ac_logits"][0, t, j - 1]
         assert top2_margin(lg) <= 0.05, f"divergence at frame {t} code {j}, margin {top2_margin(lg):.3f}"
     print(f"0.6b-fp8 frame graph: identical for {diff[0] if diff.size else got.size} of {got.size} codes", flush=True)
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
+def test_fp8_batched_streams_take_the_gemm_route():
+    """16 lockstep streams of the 0.6B E4M3 model: every projection has 16 or more rows, so the
+    decode runs its projections as MFMA GEMMs on the widened codes (split K, row scales at the
+    output). Teacher-forced logits of every stream within the bar, greedy tokens equal."""
+    model = config.MODELS["0.6b-fp8"]
+    w = synth.make_weights(model, 0)
+    B, n, F = 16, 8, 2
+    ids = synth.random_ids(n, model.text_vocab, seed=21, batch=B)
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((B, F, 16), np.float32))
+    del orc
+    dec, dw = make_decoder(model, B, n + F + 2, F + 2, w)
+    print("0.6b-fp8 x16: running", flush=True)
+    sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F)
+    es, ea, n_, ex = check_step_parity(model, ref, sem, ac, tok, 1e-2)
+    print(f"0.6b-fp8 x16: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n_}, exempt {ex}")
     dec.close()
     del dw
     torch.cuda.empty_cache()
@@ -817,7 +838,7 @@ def test_1p7b_x32_sampled_streams_teacher_forced():
     print(f"1.7b x32 sampled: logits rel err <= {worst:.2e}; {checked} draws equal, {exempt} exempt")
 
 
-@pytest.mark.parametrize("name", ["0.6b", "1.7b"])
+@pytest.mark.parametrize("name", ["0.6b", "1.7b", "0.6b-fp8"])
 def test_gemm_prefill_matches_step_prefill_and_oracle(name):
     """The prompt pass as MFMA GEMMs (chunks of 64 positions, 2 streams, a ragged last chunk) against
     the one-position-at-a-time path and the oracle: logits after the prompt and after one Talker step

@@ -4,8 +4,8 @@
 // Qwen3-TTS": the per-frame Talker pass that emits the semantic token) runs as ONE kernel of 256
 // workgroups x 512 threads: all decoder layers, the final norm and the semantic head for the
 // position held in the device counters. The layer split is the one of the CodePredictor kernel:
-// XCD g = blockIdx % 8 owns KV head g (its query heads, their output-projection columns) and
-// FFN rows [F/8 * g, +F/8); rank r = blockIdx / 8 owns 1/32 of each of those row sets. The
+// XCD g (the one the workgroup runs on) owns KV head g (its query heads, their output-projection
+// columns) and FFN rows [F/8 * g, +F/8); rank r = blockIdx / 8 owns 1/32 of each of those row sets. The
 // exchanges are the same tagged-value hand-offs. What differs:
 //   * attention reads the fp32 KV cache in HBM: the positions 0..p are split into 32 contiguous
 //     chunks, one per rank of the XCD; each rank produces a partial softmax state per head, and
@@ -470,10 +470,10 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
         os += S.wo[w][h][i] * f;
       }
     }
-    st_c(slot + h * 130 + 2 + i, pack(os, tag));
+    st_l(slot + h * 130 + 2 + i, pack(os, tag));
     if (i == 0) {
-      st_c(slot + h * 130, pack(mx, tag));
-      st_c(slot + h * 130 + 1, pack(ls, tag));
+      st_l(slot + h * 130, pack(mx, tag));
+      st_l(slot + h * 130 + 1, pack(ls, tag));
     }
   } else {
     bg(2);
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   constexpr int KT = (THMAX + NR + PF - 1) / PF;  // intra gather of a residual row + sums of squares
   constexpr int KQ = (512 + PF - 1) / PF;         // intra gather of the q/k/v slices
   constexpr int KH = (TFXMAX + PF - 1) / PF;      // intra gather of the SwiGLU slices
-  const int g = blockIdx.x % NX, r = blockIdx.x / NX, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
+  const int g = xcd_id(), r = blockIdx.x / NX, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int H = D.H, d = D.d, G = D.nq / D.nkv;
   const int qrows = (G + 2) * d, qper = qrows / NR, hper = H / NR, fx = D.F / NX, fper = fx / NR;
   TkConsts c;

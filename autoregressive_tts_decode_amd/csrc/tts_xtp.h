@@ -3,18 +3,30 @@
 // The 15 sequential CodePredictor steps of a frame ("Running Qwen3-TTS on an
 // AMD R9700", section "Running Qwen3-TTS") run inside ONE kernel of 256
 // workgroups x 512 threads -- one workgroup per CU, rank r on XCD g where
-// g = blockIdx % 8 and r = blockIdx / 8. Each decoder layer is split across
+// g is the XCD the workgroup runs on (its XCC_ID) and r = blockIdx / 8. Each
+// decoder layer is split across
 // the 8 XCDs tensor-parallel: XCD g owns KV head g (query heads G*g ..
 // G*g+G-1), the matching columns of the output projection and 1/8 of the
 // FFN. Dependencies between phases are exchanges of tagged fp32 values
-// ((tag << 32) | bits, written and read with device-coherent relaxed
-// atomics, so no cache maintenance or fences are needed and correctness does
-// not depend on where a workgroup runs):
+// ((tag << 32) | bits, read with device-scope relaxed atomic loads, so no
+// cache maintenance or fences are needed):
 //   intra: the 32 ranks of one XCD gather each other's slices
 //          (q/k/v slice -> attention; reduced residual -> full residual;
 //           SwiGLU slice -> down projection);
 //   cross: rank r of every XCD reduce-scatters the partial sums of the output
 //          and down projections (8 partners, rank-r rows).
+// Cross values are written with device-scope stores, which write through to
+// memory. Intra values are written with plain stores, which stay in the XCD's
+// L2 as dirty lines; a device-scope load from a CU of the same XCD is served
+// by that line (measured: an all-gather hop among the 32 ranks of an XCD takes
+// ~0.35 us this way against ~0.95 us through memory). The group of a
+// workgroup is therefore the XCD it runs on, read from the hardware, not a
+// function of blockIdx: the dispatcher deals workgroups to the XCDs round
+// robin, but from an XCD that depends on earlier launches. Round robin puts
+// the 32 workgroups blockIdx = 8 k + c (k < 32) on one XCD, so r = blockIdx / 8
+// numbers them 0..31. Were the deal ever uneven, a (g, r) slot would go
+// unwritten and its readers time out; a tag never matches a stale value, so
+// the failure is a time-out reported in the error word, never a wrong value.
 // A consumer polls until every value it needs carries the expected tag; tags
 // are unique per exchange (a running epoch kept on the device), and every
 // exchange buffer is reused only after an exchange that all its readers must
@@ -120,8 +132,24 @@ __device__ __forceinline__ GLB T* glb(T* p) { return (GLB T*)p; }
 template <typename T>
 __device__ __forceinline__ const GLB T* glb(const T* p) { return (const GLB T*)p; }
 
+// Cross-XCD value: device-scope store (written through to memory).
 __device__ __forceinline__ void st_c(u64* p, u64 v) { __hip_atomic_store(glb(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+// Intra-XCD value: plain 64-bit store, kept in this XCD's L2 where its readers' loads find it.
+__device__ __forceinline__ void st_l(u64* p, u64 v) { __hip_atomic_store(glb(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT); }
+// Every exchange read: device-scope load (misses the CU's L1; served by a dirty line of this
+// XCD's L2, else by memory).
 __device__ __forceinline__ u64 ld_c(const u64* p) { return __hip_atomic_load(glb(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Error-word bit: an exchange timed out, or another workgroup failed.
+constexpr uint32_t kErrTimeout = 1u;
+
+// The XCD (0..7) this workgroup runs on, from the hardware register XCC_ID: the group that shares
+// an L2 and so the intra-XCD exchange buffers.
+__device__ __forceinline__ int xcd_id() {
+  uint32_t xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  return (int)(xcc & (NX - 1));
+}
 
 // Workgroup barrier for LDS data: waits for this wave's LDS accesses, then meets the other waves.
 // It is no memory-model fence, so vector loads in flight (weight rows, LDS-direct copies) are not
@@ -183,7 +211,7 @@ __device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t
     }
   }
   if (barrier_any(fail, tag)) {
-    if (tid == 0) __hip_atomic_fetch_or(glb(err), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_fetch_or(glb(err), kErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return false;
   }
   return true;
@@ -375,10 +403,10 @@ __device__ __forceinline__ bool reduce_gather(const Xch& X, const float* out, fl
                                               uint32_t& tag, int& iring, int& cpar, int g, int r, AfterPut after_put) {
   const int tid = fresh_tid(), hper = H / NR;
   ++tag;
-  u64* mine = X.xcr + ((size_t)blockIdx.x * 2 + (cpar & 1)) * CSZ;
+  u64* mine = X.xcr + ((size_t)(r * NX + g) * 2 + (cpar & 1)) * CSZ;
   for (int i = tid; i < hper * M; i += NT) st_c(mine + (i % M) * 64 + i / M, pack(out[i], tag));
   after_put();
-  // partners: rank r on every XCD = blocks r * NX + x; their slots are 2 * CSZ apart.
+  // partners: rank r on every XCD x, slot r * NX + x; their slots are 2 * CSZ apart.
   // Segment (x, m) -> xn[(x * M + m) * hper ..]
   // (hper is a power of two: entry i -> element i & (hper - 1) of segment i >> lh)
   const u64* base = X.xcr + ((size_t)(r * NX) * 2 + (cpar & 1)) * CSZ;
@@ -400,12 +428,12 @@ __device__ __forceinline__ bool reduce_gather(const Xch& X, const float* out, fl
       v = residual ? xs[m * H + row] : 0.f;
 #pragma unroll
       for (int x = 0; x < NX; ++x) v += xn[(x * M + m) * hper + e];
-      st_c(buf + m * H + row, pack(v, tag));
+      st_l(buf + m * H + row, pack(v, tag));
     }
 #pragma unroll
     for (int mm = 0; mm < M; ++mm) {
       const float ss = wave_sum(live && m == mm ? v * v : 0.f);
-      if (tid == 0) st_c(buf + M * H + mm * NR + r, pack(ss, tag));
+      if (tid == 0) st_l(buf + M * H + mm * NR + r, pack(ss, tag));
     }
   }
   lds_barrier();  // the gather below overwrites the residual rows read above
@@ -421,7 +449,7 @@ __device__ __forceinline__ bool slice_gather(const Xch& X, int n, int w, ValFn v
   u64* buf = X.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
   for (int i = fresh_tid(); i < n * M; i += NT) {
     const int e = i / M, m = i % M;
-    st_c(buf + m * w + n * r + e, pack(vals(e, m), tag));
+    st_l(buf + m * w + n * r + e, pack(vals(e, m), tag));
   }
   after_put();
   return get_flat<KMAX, NPOLL>(buf, M * w, tag, dst, X.err);
@@ -755,7 +783,7 @@ template <typename WT>
 __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   const KCONST CpDesc& D = *(const KCONST CpDesc*)C.desc;
   __shared__ Smem S;
-  const int g = blockIdx.x % NX, r = blockIdx.x / NX;
+  const int g = xcd_id(), r = blockIdx.x / NX;
   // constants first (they are needed first), then the first two weight phases
   LayerConsts c;
   load_consts<WT, 2>(c, D, D.layer[0], 0);

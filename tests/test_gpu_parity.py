@@ -227,6 +227,45 @@ def test_tiny_split_attention_over_long_context():
     check_step_parity(model, ref, sem, ac, tok, 1e-4)
 
 
+def test_tiny_64_streams_take_64_position_attention_splits():
+    """64 streams of 2 KV heads make 128 (stream, head) pairs, so the decode attention runs
+    64-position splits; a 150-id prompt spans three of them with a ragged last one, merged by the
+    last block to arrive. Every stream must still equal its own oracle run."""
+    model = config.TINY
+    w = synth.make_weights(model, 5)
+    orc = OracleModel(w, model.as_dict(), np.float64)
+    B, F = 64, 2
+    ids = synth.random_ids(150, model.text_vocab, seed=9, batch=B)
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((B, F, 16), np.float32))
+    dec, _ = make_decoder(model, B, 160, 4, w)
+    sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F)
+    es, ea, n, ex = check_step_parity(model, ref, sem, ac, tok, 1e-4)
+    print(f"tiny 64 streams: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}")
+    dec.close()
+
+
+def test_0p6b_32_streams_take_128_position_attention_splits():
+    """32 streams of 8 KV heads (256 pairs) run 128-position decode attention splits; after a
+    132-id prompt the first decode step attends over two of them. Logits of both frames of every
+    stream within the bf16 bar of the oracle."""
+    model = config.MODELS["0.6b"]
+    w = synth.make_weights(model, 0)
+    B, F = 32, 2
+    ids = synth.random_ids(132, model.text_vocab, seed=19, batch=B)
+    print("0.6b 32 streams: oracle", flush=True)
+    orc = OracleModel(w, model.as_dict(), np.float32)
+    ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((B, F, 16), np.float32))
+    del orc
+    print("0.6b 32 streams: decoder", flush=True)
+    dec, dw = make_decoder(model, B, 136, 4, w)
+    sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F)
+    es, ea, n, ex = check_step_parity(model, ref, sem, ac, tok, 1e-2)
+    print(f"0.6b 32 streams: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}")
+    dec.close()
+    del dw
+    torch.cuda.empty_cache()
+
+
 def test_tiny_batched_streams_are_independent():
     """B lockstep streams: each equals its own single-stream run."""
     model = config.TINY

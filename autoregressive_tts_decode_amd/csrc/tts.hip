@@ -487,8 +487,11 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
   g.kslice = kslice;
   const bool zero = ks > 1 && !g.add;
   if (a.gain) {
-    hipLaunchKernelGGL(k_rowscale, dim3((a.M + 3) / 4), dim3(256), 0, ctx->stream, A, lda, a.M, a.K, ctx->cfg.rms_eps, RS,
-                       zero ? g.C : nullptr, g.ldc, N);
+    // 4 rows' scales per block; with an output to clear, enough blocks for one 16-byte store per
+    // thread (at most 1024)
+    const int zb = zero ? std::min(1024, (int)(((size_t)a.M * N / 4 + 255) / 256)) : 0;
+    hipLaunchKernelGGL(k_rowscale, dim3(std::max((a.M + 3) / 4, zb)), dim3(256), 0, ctx->stream, A, lda, a.M, a.K,
+                       ctx->cfg.rms_eps, RS, zero ? g.C : nullptr, g.ldc, N);
     HIP_LAUNCH_CHECK();
     if (a.xn_out) {
       hipLaunchKernelGGL(k_norm_rows<uint16_t>, dim3(a.M), dim3(256), 0, ctx->stream, A, lda, RS, a.gain, a.K, a.xn_out, a.xn_stride);

@@ -170,18 +170,40 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
       }
 }
 
-// rs[m] = 1 / sqrt(mean(x[m]^2) + eps) over K; one wave per row. With zc, the wave also clears
-// row m of zc[.., 0 .. zn) (the output a split-K GEMM adds its slices into).
+// rs[m] = 1 / sqrt(mean(x[m]^2) + eps) over K; one wave per row (blocks past the rows have no
+// scale to compute). With zc, the grid also clears rows 0 .. M-1 of zc[.., 0 .. zn) (the output a
+// split-K GEMM adds its slices into), whatever block and thread count it has.
 __global__ __launch_bounds__(256) void k_rowscale(const float* x, int ldx, int M, int K, float eps, float* rs,
                                                   float* zc = nullptr, int zld = 0, int zn = 0) {
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (m >= M) return;
-  float s = 0.f;
-  for (int k = lane; k < K; k += 64) s += x[(size_t)m * ldx + k] * x[(size_t)m * ldx + k];
-  s = wave_sum(s);
-  if (lane == 0) rs[m] = 1.0f / sqrtf(s / (float)K + eps);
-  if (zc)
-    for (int k = lane; k < zn; k += 64) zc[(size_t)m * zld + k] = 0.f;
+  if (m < M) {
+    const float* row = x + (size_t)m * ldx;
+    float s = 0.f;
+    if ((K & 3) == 0 && (ldx & 3) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+      for (int k = 4 * lane; k < K; k += 256) {
+        const float4 v = *reinterpret_cast<const float4*>(row + k);
+        s += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+      }
+    } else {
+      for (int k = lane; k < K; k += 64) s += row[k] * row[k];
+    }
+    s = wave_sum(s);
+    if (lane == 0) rs[m] = 1.0f / sqrtf(s / (float)K + eps);
+  }
+  // the output rows to clear, spread over every block of the grid in 16-byte stores
+  if (zc) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    if ((zn & 3) == 0 && (zld & 3) == 0 && (reinterpret_cast<uintptr_t>(zc) & 15) == 0) {
+      const int q4 = zn / 4;
+      for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < (size_t)M * q4; q += stride) {
+        const size_t r = q / q4, c = q % q4;
+        *reinterpret_cast<float4*>(zc + r * zld + 4 * c) = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    } else {
+      for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < (size_t)M * zn; q += stride)
+        zc[(q / zn) * zld + q % zn] = 0.f;
+    }
+  }
 }
 
 // out[m] = x[m] * rs[m] * gain (the normalised rows a GEMM with a row scale consumed), one

@@ -695,6 +695,25 @@ __device__ __forceinline__ uint32_t orderable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int kTopKMax = 256;  // top_k up to this selects its candidates instead of sorting all V
+
+// Inclusive prefix sum of v over the 256 threads of a block (ws: 4 ints of LDS). Every thread must
+// call it.
+__device__ __forceinline__ int block_incl_scan256(int v, int* ws) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) ws[w] = v;
+  __syncthreads();
+  int add = 0;
+  for (int i = 0; i < w; ++i) add += ws[i];
+  __syncthreads();  // ws is free again
+  return v + add;
+}
+
 // One block (256 threads) per stream.
 __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -723,9 +742,81 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   } else {
     __shared__ unsigned long long keys[kSortMax];
     __shared__ float vals[kSortMax];
+    const uint8_t* hist = a.history ? a.history + (size_t)b * a.h_stride : nullptr;
+    if (a.top_k >= 1 && a.top_k <= kTopKMax && a.top_k <= a.V) {
+      // Top-k without sorting all V: the order wanted is (logit desc, id asc), i.e. ascending
+      // keys (~orderable(v) << 32 | id). A radix select over the 32-bit orderable values finds
+      // the k-th largest value T; the candidates are every id above T and the lowest ids equal to
+      // T up to k; only those k are sorted. Thread t handles the contiguous ids [t C, t C + C).
+      __shared__ uint32_t okey[kSortMax];
+      __shared__ unsigned long long cand[kTopKMax];
+      __shared__ int bins[256], ws[4], sel_d, sel_need, ncand;
+      const int k = a.top_k, C = (a.V + 255) / 256, i0 = tid * C, i1 = min(i0 + C, a.V);
+      for (int i = i0; i < i1; ++i) {
+        float v = l[i];
+        if (hist && a.penalty != 1.0f && hist[i]) v = (v > 0.f) ? v / a.penalty : v * a.penalty;
+        v = v / a.temperature;
+        vals[i] = v;
+        okey[i] = orderable(v);
+      }
+      uint32_t prefix = 0, pmask = 0;
+      int need = k;  // how many of the values matching prefix are still to be taken
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        bins[tid] = 0;
+        __syncthreads();
+        for (int i = i0; i < i1; ++i) {
+          const uint32_t o = okey[i];
+          if ((o & pmask) == prefix) atomicAdd(&bins[(o >> shift) & 255], 1);
+        }
+        __syncthreads();
+        // digits from the top: thread t holds digit 255 - t; the digit whose running count first
+        // reaches need holds the k-th largest value
+        const int h = bins[255 - tid];
+        const int incl = block_incl_scan256(h, ws);
+        if (incl - h < need && need <= incl) {
+          sel_d = 255 - tid;
+          sel_need = need - (incl - h);
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sel_d << shift;
+        pmask |= 0xffu << shift;
+        need = sel_need;
+        __syncthreads();
+      }
+      const uint32_t T = prefix;
+      int eq = 0;
+      for (int i = i0; i < i1; ++i) eq += okey[i] == T;
+      if (tid == 0) ncand = 0;
+      int rank = block_incl_scan256(eq, ws) - eq;  // ids equal to T before this thread's range
+      for (int i = i0; i < i1; ++i) {
+        const uint32_t o = okey[i];
+        bool take = o > T;
+        if (o == T) take = rank++ < need;
+        if (take) cand[atomicAdd(&ncand, 1)] = ((unsigned long long)(~o) << 32) | (uint32_t)i;
+      }
+      int n2k = 1;
+      while (n2k < k) n2k <<= 1;
+      __syncthreads();
+      for (int i = k + tid; i < n2k; i += 256) cand[i] = ~0ull;
+      __syncthreads();
+      for (int kk = 2; kk <= n2k; kk <<= 1) {
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+          for (int i = tid; i < n2k; i += 256) {
+            const int ixj = i ^ j;
+            if (ixj > i) {
+              const unsigned long long x = cand[i], y = cand[ixj];
+              const bool up = (i & kk) == 0;
+              if ((x > y) == up) { cand[i] = y; cand[ixj] = x; }
+            }
+          }
+          __syncthreads();
+        }
+      }
+      for (int i = tid; i < k; i += 256) keys[i] = cand[i];
+      __syncthreads();
+    } else {
     int n2 = 1;
     while (n2 < a.V) n2 <<= 1;
-    const uint8_t* hist = a.history ? a.history + (size_t)b * a.h_stride : nullptr;
     for (int i = tid; i < n2; i += 256) {
       if (i < a.V) {
         float v = l[i];
@@ -751,6 +842,7 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
         }
         __syncthreads();
       }
+    }
     }
     if (tid == 0) {
       int kk = (a.top_k <= 0 || a.top_k > a.V) ? a.V : a.top_k;

@@ -309,6 +309,26 @@ def test_sampler_on_uploaded_logits_matches_oracle(tiny, V):
         assert all(hn[b, got[b]] == 1 for b in range(B))
 
 
+def test_sampler_top_k_ties_keep_the_lowest_ids(tiny):
+    """Five equal largest logits at ids 40, 2, 90, 11, 7 with top_k = 3: the kept set is the
+    lowest ids {2, 7, 11} (order logit desc, id asc), equally weighted, so uniforms 0.1, 0.5 and
+    0.9 draw 2, 7 and 11; with top_k = 1 every draw is id 2. Both equal the oracle's sampler."""
+    d = dev()
+    V = 300
+    row = -5.0 + 0.1 * synth.random_logits((1, V), 1.0, seed=77)[0]
+    row[[40, 2, 90, 11, 7]] = 4.0
+    L = np.repeat(row[None, :].astype(np.float32), 3, axis=0)
+    u = np.array([0.1, 0.5, 0.9], np.float32)
+    for k, want in ((3, [2, 7, 11]), (1, [2, 2, 2])):
+        cfg = dict(do_sample=True, top_k=k, top_p=1.0, temperature=1.0, repetition_penalty=1.0)
+        out = torch.zeros((3,), dtype=torch.int32, device=d)
+        tiny["dec"].sample(torch.from_numpy(L).to(d), cfg, torch.from_numpy(u).to(d), out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().tolist()
+        assert got == want, (k, got)
+        assert got == [sample_token(L[b], cfg, float(u[b]), None, dtype=np.float32) for b in range(3)]
+
+
 def test_sampler_greedy_ties_pick_the_lowest_id(tiny):
     d = dev()
     L = np.zeros((4, 300), np.float32)

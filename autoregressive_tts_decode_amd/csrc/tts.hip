@@ -207,7 +207,8 @@ bool xtp_capable(const tts_config& c) {
   if (p.hidden % xtp::NR || p.hidden > xtp::HMAX || p.hidden % E || p.hidden / E > ra_units) return false;
   // A rows: q/k/v slice, gate/up slice, head slice
   if ((G + 2) * p.head_dim / xtp::NR > ra_rows) return false;
-  if (p.ffn % (xtp::NX * xtp::NR) || 2 * (p.ffn / (xtp::NX * xtp::NR)) > ra_rows) return false;
+  // gate/up rows: the A buffer's rows, then the C buffer's
+  if (p.ffn % (xtp::NX * xtp::NR) || 2 * (p.ffn / (xtp::NX * xtp::NR)) > ra_rows + xtp::RC_R * xtp::NW) return false;
   if (p.vocab % xtp::NWG || p.vocab / xtp::NWG > ra_rows) return false;
   // B rows: output projection, down projection, input projection (hidden / 32 rows each)
   if (p.hidden / xtp::NR > rb_rows || G * p.head_dim / E > rb_units) return false;

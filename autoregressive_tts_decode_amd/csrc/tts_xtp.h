@@ -48,10 +48,15 @@ constexpr int MAXL = 6;     // CodePredictor layers supported (K/V rows live in 
 constexpr int kCpPos = 16;  // CodePredictor positions per frame
 constexpr int HMAX = 1024;  // CodePredictor hidden size supported
 constexpr int KVS = 132;    // LDS row stride of the K/V rows (padded against bank conflicts)
-// Weight-row register buffers, per wave: A holds hidden-wide rows (q/k/v, gate/up, head: at most
-// RA_R rows per wave of at most 64 * RA_K 16-byte units), B narrow rows (output and down
-// projections, input projection: RB_R rows of at most 64 * RB_K units).
-constexpr int RA_R = 3, RA_K = 2;
+// Weight-row register buffers, per wave: A holds hidden-wide rows (q/k/v, the first RA_R * NW
+// gate/up rows, head: at most RA_R rows per wave of at most 64 * RA_K 16-byte units), C the
+// gate/up rows past those (RC_R rows per wave), B narrow rows (output and down projections, input
+// projection: RB_R rows of at most 64 * RB_K units). A wave holds its loads' issue once it has
+// more than about 4 KB in flight (measured), so no exchange issues more than 4 KB per wave: the
+// gate/up rows are split between A (issued in the q/k/v exchange) and C (issued during the
+// attention, when most waves are idle and the next poll is an attention and a dot away).
+constexpr int RA_R = 2, RA_K = 2;
+constexpr int RC_R = 1;
 constexpr int RB_R = 4, RB_K = 1;
 constexpr int RING = 4;     // intra exchange buffers per XCD
 constexpr int ISZ = 2 * HMAX + 128;  // intra buffer entries (2 rows x HMAX, sums of squares)
@@ -225,8 +230,8 @@ __device__ __forceinline__ bool get_flat(const u64* src, int n, uint32_t tag, fl
 
 // ---------------------------------------------------------------------------- weight rows
 
-// Rows of one phase: wave w streams rows w, w + NW, ... (at most MAXR), each
-// row's 16-byte units spread over the lanes (unit u = lane + 64 k, k < MAXK).
+// Rows of one phase: wave w streams rows row0 + w + NW j (j < MAXR), each row's 16-byte units
+// spread over the lanes (unit u = lane + 64 k, k < MAXK).
 template <typename WT, int RR, int KK>
 struct Rows {
   static constexpr int MAXR = RR, MAXK = KK;
@@ -235,13 +240,13 @@ struct Rows {
 
 // rowptr(i) -> const WT* of row i (0 <= i < nrows); ncols elements per row.
 template <typename WT, int RR, int KK, typename RowFn>
-__device__ __forceinline__ void rows_issue(Rows<WT, RR, KK>& R, int nrows, int ncols, RowFn rowptr, bool nt) {
+__device__ __forceinline__ void rows_issue(Rows<WT, RR, KK>& R, int nrows, int ncols, RowFn rowptr, bool nt, int row0 = 0) {
   constexpr int E = WTraits<WT>::E, MAXR = RR, MAXK = KK;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int units = ncols / E;
 #pragma unroll
   for (int j = 0; j < MAXR; ++j) {
-    const int i = wave + NW * j;
+    const int i = row0 + wave + NW * j;
     if (i < nrows) {
       const GLB u32x4* p = glb(reinterpret_cast<const u32x4*>(rowptr(i)));
 #pragma unroll
@@ -255,9 +260,10 @@ __device__ __forceinline__ void rows_issue(Rows<WT, RR, KK>& R, int nrows, int n
 
 // out[i * M + m] = dot(row i, x[m * ldx .. + ncols]) for this wave's rows (LDS in/out).
 template <typename WT, int M, int RR, int KK>
-__device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, int ldx, float* out) {
+__device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, int ldx, float* out,
+                                         int row0 = 0) {
   constexpr int E = WTraits<WT>::E, MAXR = RR, MAXK = KK;
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = threadIdx.x & 63, wave = row0 + wave_id();
   const int units = ncols / E;
   float acc[MAXR][M];
 #pragma unroll
@@ -332,6 +338,8 @@ struct Smem {
 template <typename WT>
 using RowsA = Rows<WT, RA_R, RA_K>;
 template <typename WT>
+using RowsC = Rows<WT, RC_R, RA_K>;
+template <typename WT>
 using RowsB = Rows<WT, RB_R, RB_K>;
 
 // q/k/v rows [qper*r, +qper) of this XCD's (G q heads | k | v)
@@ -353,14 +361,15 @@ __device__ __forceinline__ void issue_o(RowsB<WT>& R, const KCONST CpDesc& D, co
     return reinterpret_cast<const WT*>(W.wo) + (size_t)(hper * r + i) * (D.nq * D.d) + Gd * g;
   }, false);
 }
-// gate rows then up rows [fper*r, +fper) of this XCD's FFN slice
-template <typename WT>
-__device__ __forceinline__ void issue_gu(RowsA<WT>& R, const KCONST CpDesc& D, const KCONST LayerW& W, int g, int r) {
+// gate rows then up rows [fper*r, +fper) of this XCD's FFN slice: rows [row0, row0 + RR NW)
+template <typename WT, int RR>
+__device__ __forceinline__ void issue_gu(Rows<WT, RR, RA_K>& R, int row0, const KCONST CpDesc& D, const KCONST LayerW& W, int g,
+                                         int r) {
   const int fx = D.F / NX, fper = fx / NR;
   rows_issue(R, 2 * fper, D.H, [&](int i) -> const WT* {
     const int f = fx * g + fper * r + (i % fper);
     return reinterpret_cast<const WT*>(i < fper ? W.wg : W.wu) + (size_t)f * D.H;
-  }, false);
+  }, false, row0);
 }
 // down projection rows [hper*r, +hper), columns of this XCD's FFN slice
 template <typename WT>
@@ -555,8 +564,8 @@ __device__ __forceinline__ void rmsnorm_reg(const float* x, int n, const float* 
 // of the input rows (it does unless the rows were staged without an exchange).
 template <typename WT, int M>
 __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C, int layer, int j, int p0, bool have_ss, Smem& S,
-                                         RowsB<WT>& R0, RowsA<WT>& R1, LayerConsts& c, uint32_t& tag, int& iring, int& cpar,
-                                         int g, int r) {
+                                         RowsB<WT>& R0, RowsA<WT>& R1, RowsC<WT>& R2, LayerConsts& c, uint32_t& tag, int& iring,
+                                         int& cpar, int g, int r) {
   const KCONST LayerW& W = D.layer[layer];
   const int H = D.H, d = D.d, G = D.nq / D.nkv;
   const int qrows = (G + 2) * d;          // q/k/v rows owned by one XCD
@@ -573,7 +582,7 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
   rows_dot<WT, M>(R1, qper, H, S.xn, H, S.out);
   lds_barrier();
   if (!slice_gather<M, M>(X, qper, qrows, [&](int e, int m) { return S.out[e * M + m]; }, S.qkv, tag, iring, g, r,
-                          [&] { issue_gu(R1, D, W, g, r); }))
+                          [&] { issue_gu(R1, 0, D, W, g, r); }))
     return false;
 
   // --- attention for this XCD's heads over positions 0 .. p0 + M - 1 (d = 128): one wave per
@@ -641,6 +650,7 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
     S.ob[m * G * d + h * d + lane] = o0 / l;
     S.ob[m * G * d + h * d + lane + 64] = o1 / l;
   }
+  issue_gu(R2, RA_R * NW, D, W, g, r);  // the gate/up rows past R1's
   lds_barrier();
 
   // --- output projection partial (R0: rows [hper*r, +hper), this XCD's head columns), residual
@@ -651,6 +661,7 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
   // --- gate/up slice (R1) + SwiGLU
   rmsnorm_reg<M>(S.xs, H, c.mn, D.eps, S.xn, S.red, S.xs + M * H);
   rows_dot<WT, M>(R1, 2 * fper, H, S.xn, H, S.out);
+  rows_dot<WT, M>(R2, 2 * fper, H, S.xn, H, S.out, RA_R * NW);
   lds_barrier();
   if (!slice_gather<M, M>(X, fper, fx, [&](int e, int m) { return silu(S.out[e * M + m]) * S.out[(fper + e) * M + m]; }, S.hb,
                           tag, iring, g, r, [&] {
@@ -721,8 +732,8 @@ __device__ __forceinline__ int argmax_exchange(const KCONST CpDesc& D, Smem& S, 
 // constants; on exit they hold the next step's.
 template <typename WT, int M>
 __device__ __forceinline__ bool cp_step(const KCONST CpDesc& D, const CpCall& C, int j, int& tok, Smem& S, RowsB<WT>& R0,
-                                        RowsA<WT>& R1, LayerConsts& c, const float* fn, uint32_t& tag, int& iring, int& cpar,
-                                        int& apar, int frame, int g, int r) {
+                                        RowsA<WT>& R1, RowsC<WT>& R2, LayerConsts& c, const float* fn, uint32_t& tag, int& iring,
+                                        int& cpar, int& apar, int frame, int g, int r) {
   const int H = D.H, Ht = D.Ht, V = D.V, tid = threadIdx.x;
   const Xch X{D.xin, D.xcr, D.err};
   constexpr int KCP = (M * (HMAX + NR) + NT - 1) / NT;
@@ -758,7 +769,7 @@ __device__ __forceinline__ bool cp_step(const KCONST CpDesc& D, const CpCall& C,
   }
   const int p0 = (j == 1) ? 0 : j;
   for (int l = 0; l < D.n_layers; ++l)
-    if (!cp_layer<WT, M>(D, C, l, j, p0, l > 0 || D.proj, S, R0, R1, c, tag, iring, cpar, g, r)) return false;
+    if (!cp_layer<WT, M>(D, C, l, j, p0, l > 0 || D.proj, S, R0, R1, R2, c, tag, iring, cpar, g, r)) return false;
   // final norm on the last row, head j (R1), argmax
   const int vper = V / NWG;
   rmsnorm_reg<1>(S.xs + (M - 1) * H, H, fn, D.eps, S.xn, S.red, S.xs + M * H + (M - 1) * NR);
@@ -795,6 +806,7 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   }
   RowsB<WT> R0;
   RowsA<WT> R1;
+  RowsC<WT> R2;
   if (D.proj) issue_proj(R0, D, g, r);
   issue_qkv(R1, D, D.layer[0], g, r);
   uint32_t tag = glb(D.st)->epoch;
@@ -803,8 +815,9 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   int tok = glb(C.semantic)[0];
   if (tok < 0) tok = 0;
   if (tok >= D.Vs) tok = D.Vs - 1;
-  bool ok = cp_step<WT, 2>(D, C, 1, tok, S, R0, R1, c, fn, tag, iring, cpar, apar, frame, g, r);
-  for (int j = 2; ok && j <= D.n_ac; ++j) ok = cp_step<WT, 1>(D, C, j, tok, S, R0, R1, c, fn, tag, iring, cpar, apar, frame, g, r);
+  bool ok = cp_step<WT, 2>(D, C, 1, tok, S, R0, R1, R2, c, fn, tag, iring, cpar, apar, frame, g, r);
+  for (int j = 2; ok && j <= D.n_ac; ++j)
+    ok = cp_step<WT, 1>(D, C, j, tok, S, R0, R1, R2, c, fn, tag, iring, cpar, apar, frame, g, r);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     glb(D.st)->epoch = tag + 1;  // every workgroup has read the epoch: all took part in the last exchange
     if (C.next_tok) glb(C.next_tok)[0] = tok;

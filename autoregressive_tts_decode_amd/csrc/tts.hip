@@ -196,11 +196,12 @@ std::string check_config(const tts_config* c) {
 // register buffers (rows per wave and 16-byte units per lane).
 bool xtp_capable(const tts_config& c) {
   const tts_stack_cfg& p = c.codepred;
-  const int E = 8;  // bf16 weights: 8 per 16-byte unit
+  // bf16 weights: 8 per 16-byte unit; E4M3 codes: 16 (with one fp32 scale per row)
+  const int E = c.weight_dtype == TTS_DTYPE_FP8_E4M3 ? 16 : 8;
   const int Ht = c.talker.hidden;
   const int ra_rows = xtp::RA_R * xtp::NW, ra_units = 64 * xtp::RA_K;
   const int rb_rows = xtp::RB_R * xtp::NW, rb_units = 64 * xtp::RB_K;
-  if (c.weight_dtype != TTS_DTYPE_BF16) return false;
+  if (c.weight_dtype != TTS_DTYPE_BF16 && c.weight_dtype != TTS_DTYPE_FP8_E4M3) return false;
   if (p.n_kv_heads != xtp::NX || p.head_dim != 128) return false;
   const int G = p.n_q_heads / p.n_kv_heads;
   if (G < 1 || G > 2 || p.n_q_heads != G * p.n_kv_heads || ((G + 2) * p.head_dim) % xtp::NR) return false;
@@ -796,7 +797,8 @@ int codepred_frame_xtp(tts_ctx* ctx, const int32_t* semantic, const int32_t* for
   call.use_frame = use_frame;
   call.logits = logits_out;
   call.next_tok = nullptr;
-  hipLaunchKernelGGL(xtp::k_cp_frame<uint16_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
+  if (ctx->fp8()) hipLaunchKernelGGL(xtp::k_cp_frame<uint8_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
+  else hipLaunchKernelGGL(xtp::k_cp_frame<uint16_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
   HIP_LAUNCH_CHECK();
   return TTS_OK;
 }
@@ -1100,6 +1102,20 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
     for (int l = 0; l < p.n_layers; ++l) {
       const Layer& L = ctx->cp.layers[l];
       D.layer[l] = {L.attn_norm, L.wq, L.wk, L.wv, L.q_norm, L.k_norm, L.wo, L.mlp_norm, L.wg, L.wu, L.wd};
+      if (ctx->fp8()) {
+        const int H = p.hidden, qd = p.n_q_heads * p.head_dim;
+        D.scale[l] = {ctx->scale_of(L.wq, H), ctx->scale_of(L.wk, H), ctx->scale_of(L.wv, H), ctx->scale_of(L.wo, qd),
+                      ctx->scale_of(L.wg, H), ctx->scale_of(L.wu, H), ctx->scale_of(L.wd, p.ffn)};
+        const xtp::LayerS& q = D.scale[l];
+        if (!q.wq || !q.wk || !q.wv || !q.wo || !q.wg || !q.wu || !q.wd)
+          return ctx->fail(TTS_E_STATE, "load_weights: no E4M3 scale for a CodePredictor layer %d matrix", l);
+      }
+    }
+    if (ctx->fp8()) {
+      D.head_scale = ctx->scale_of(ctx->heads, p.hidden);
+      D.proj_scale = ctx->proj ? ctx->scale_of(ctx->proj, c.talker.hidden) : nullptr;
+      if (!D.head_scale || (ctx->proj && !D.proj_scale))
+        return ctx->fail(TTS_E_STATE, "load_weights: no E4M3 scale for the CodePredictor heads or input projection");
     }
     D.n_layers = p.n_layers; D.H = p.hidden; D.Ht = c.talker.hidden; D.F = p.ffn; D.V = p.vocab; D.Vs = c.talker.vocab;
     D.nq = p.n_q_heads; D.nkv = p.n_kv_heads; D.d = p.head_dim; D.n_ac = c.n_acoustic; D.eps = c.rms_eps;

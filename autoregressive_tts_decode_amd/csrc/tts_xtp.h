@@ -79,8 +79,16 @@ struct Xch {
 
 // Everything the kernel reads; built on the host once per weight binding and
 // kept in device memory.
+// Per-row fp32 scales of E4M3 matrices (null for bf16 weights): row i of a matrix is
+// scale[i] * codes[i].
+struct LayerS {
+  const float *wq, *wk, *wv, *wo, *wg, *wu, *wd;
+};
+
 struct CpDesc {
   LayerW layer[MAXL];
+  LayerS scale[MAXL];
+  const float *head_scale, *proj_scale;  // [15 * V], [H]
   int32_t n_layers, H, Ht, F, V, Vs, nq, nkv, d, n_ac;
   float eps;
   const void *final_norm, *heads, *proj, *embed_ac, *embed_sem;
@@ -236,17 +244,21 @@ template <typename WT, int RR, int KK>
 struct Rows {
   static constexpr int MAXR = RR, MAXK = KK;
   u32x4 b[RR][KK];
+  float s[RR];  // row scales (E4M3 weights; 1 for bf16)
 };
 
 // rowptr(i) -> const WT* of row i (0 <= i < nrows); ncols elements per row.
-template <typename WT, int RR, int KK, typename RowFn>
-__device__ __forceinline__ void rows_issue(Rows<WT, RR, KK>& R, int nrows, int ncols, RowFn rowptr, bool nt, int row0 = 0) {
+// rowscale(i) -> const float* of row i's scale (E4M3 weights only; read with the row).
+template <typename WT, int RR, int KK, typename RowFn, typename ScaleFn>
+__device__ __forceinline__ void rows_issue(Rows<WT, RR, KK>& R, int nrows, int ncols, RowFn rowptr, ScaleFn rowscale, bool nt,
+                                           int row0 = 0) {
   constexpr int E = WTraits<WT>::E, MAXR = RR, MAXK = KK;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int units = ncols / E;
 #pragma unroll
   for (int j = 0; j < MAXR; ++j) {
     const int i = row0 + wave + NW * j;
+    if constexpr (E == 16) R.s[j] = i < nrows ? *glb(rowscale(i)) : 0.f;
     if (i < nrows) {
       const GLB u32x4* p = glb(reinterpret_cast<const u32x4*>(rowptr(i)));
 #pragma unroll
@@ -274,7 +286,7 @@ __device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, i
   for (int k = 0; k < MAXK; ++k) {
     const int u = lane + 64 * k;
     if (u < units) {
-      float xv[M][8];
+      float xv[M][E];
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const float* xp = x + m * ldx + u * E;
@@ -287,7 +299,7 @@ __device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, i
 #pragma unroll
       for (int j = 0; j < MAXR; ++j) {
         if (wave + NW * j < nrows) {
-          float wf[8];
+          float wf[E];
           unpack(R.b[j][k], wf, (WT*)nullptr);
 #pragma unroll
           for (int m = 0; m < M; ++m) {
@@ -306,7 +318,8 @@ __device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, i
     if (i < nrows) {
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const float v = wave_sum(acc[j][m]);
+        float v = wave_sum(acc[j][m]);
+        if constexpr (E == 16) v *= R.s[j];
         if (lane == 0) out[i * M + m] = v;
       }
     }
@@ -342,57 +355,76 @@ using RowsC = Rows<WT, RC_R, RA_K>;
 template <typename WT>
 using RowsB = Rows<WT, RB_R, RB_K>;
 
+// The issue functions take the layer index: its weight pointers and, for E4M3 matrices, its row
+// scales (an E4M3 matrix row carries one fp32 scale; sc(ptr, i) is row i's, or null for bf16).
+__device__ __forceinline__ const float* sc(const float* p, size_t i) { return p ? p + i : nullptr; }
+
 // q/k/v rows [qper*r, +qper) of this XCD's (G q heads | k | v)
 template <typename WT>
-__device__ __forceinline__ void issue_qkv(RowsA<WT>& R, const KCONST CpDesc& D, const KCONST LayerW& W, int g, int r) {
+__device__ __forceinline__ void issue_qkv(RowsA<WT>& R, const KCONST CpDesc& D, int l, int g, int r) {
+  const KCONST LayerW& W = D.layer[l];
+  const KCONST LayerS& Sc = D.scale[l];
   const int H = D.H, d = D.d, G = D.nq / D.nkv, qper = (G + 2) * d / NR;
   rows_issue(R, qper, H, [&](int i) -> const WT* {
     const int q = qper * r + i;
     if (q < G * d) return reinterpret_cast<const WT*>(W.wq) + (size_t)(G * d * g + q) * H;
     if (q < (G + 1) * d) return reinterpret_cast<const WT*>(W.wk) + (size_t)(d * g + q - G * d) * H;
     return reinterpret_cast<const WT*>(W.wv) + (size_t)(d * g + q - (G + 1) * d) * H;
+  }, [&](int i) -> const float* {
+    const int q = qper * r + i;
+    if (q < G * d) return sc(Sc.wq, G * d * g + q);
+    if (q < (G + 1) * d) return sc(Sc.wk, d * g + q - G * d);
+    return sc(Sc.wv, d * g + q - (G + 1) * d);
   }, false);
 }
 // output projection rows [hper*r, +hper), columns of this XCD's heads
 template <typename WT>
-__device__ __forceinline__ void issue_o(RowsB<WT>& R, const KCONST CpDesc& D, const KCONST LayerW& W, int g, int r) {
+__device__ __forceinline__ void issue_o(RowsB<WT>& R, const KCONST CpDesc& D, int l, int g, int r) {
+  const KCONST LayerW& W = D.layer[l];
+  const float* so = D.scale[l].wo;
   const int hper = D.H / NR, Gd = D.nq / D.nkv * D.d;
   rows_issue(R, hper, Gd, [&](int i) -> const WT* {
     return reinterpret_cast<const WT*>(W.wo) + (size_t)(hper * r + i) * (D.nq * D.d) + Gd * g;
-  }, false);
+  }, [&](int i) { return sc(so, hper * r + i); }, false);
 }
 // gate rows then up rows [fper*r, +fper) of this XCD's FFN slice: rows [row0, row0 + RR NW)
 template <typename WT, int RR>
-__device__ __forceinline__ void issue_gu(Rows<WT, RR, RA_K>& R, int row0, const KCONST CpDesc& D, const KCONST LayerW& W, int g,
-                                         int r) {
+__device__ __forceinline__ void issue_gu(Rows<WT, RR, RA_K>& R, int row0, const KCONST CpDesc& D, int l, int g, int r) {
+  const KCONST LayerW& W = D.layer[l];
+  const KCONST LayerS& Sc = D.scale[l];
   const int fx = D.F / NX, fper = fx / NR;
   rows_issue(R, 2 * fper, D.H, [&](int i) -> const WT* {
     const int f = fx * g + fper * r + (i % fper);
     return reinterpret_cast<const WT*>(i < fper ? W.wg : W.wu) + (size_t)f * D.H;
-  }, false, row0);
+  }, [&](int i) { return sc(i < fper ? Sc.wg : Sc.wu, fx * g + fper * r + (i % fper)); }, false, row0);
 }
 // down projection rows [hper*r, +hper), columns of this XCD's FFN slice
 template <typename WT>
-__device__ __forceinline__ void issue_down(RowsB<WT>& R, const KCONST CpDesc& D, const KCONST LayerW& W, int g, int r) {
+__device__ __forceinline__ void issue_down(RowsB<WT>& R, const KCONST CpDesc& D, int l, int g, int r) {
+  const KCONST LayerW& W = D.layer[l];
+  const float* sd = D.scale[l].wd;
   const int hper = D.H / NR, fx = D.F / NX;
   rows_issue(R, hper, fx, [&](int i) -> const WT* {
     return reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r + i) * D.F + fx * g;
-  }, false);
+  }, [&](int i) { return sc(sd, hper * r + i); }, false);
 }
 // head j rows [vper*blockIdx, +vper)
 template <typename WT>
 __device__ __forceinline__ void issue_head(RowsA<WT>& R, const KCONST CpDesc& D, int j) {
   const int vper = D.V / NWG;
   const WT* head = reinterpret_cast<const WT*>(D.heads) + (size_t)(j - 1) * D.V * D.H;
-  rows_issue(R, vper, D.H, [&](int i) -> const WT* { return head + (size_t)(vper * blockIdx.x + i) * D.H; }, false);
+  const float* sh = D.head_scale;
+  rows_issue(R, vper, D.H, [&](int i) -> const WT* { return head + (size_t)(vper * blockIdx.x + i) * D.H; },
+             [&](int i) { return sc(sh, (size_t)(j - 1) * D.V + vper * blockIdx.x + i); }, false);
 }
 // input projection rows (K split: XCD g takes columns [Ht/8 * g, +Ht/8), rank r rows [hper*r, +hper))
 template <typename WT>
 __device__ __forceinline__ void issue_proj(RowsB<WT>& R, const KCONST CpDesc& D, int g, int r) {
   const int kx = D.Ht / NX, hper = D.H / NR;
+  const float* sp = D.proj_scale;
   rows_issue(R, hper, kx, [&](int i) -> const WT* {
     return reinterpret_cast<const WT*>(D.proj) + (size_t)(hper * r + i) * D.Ht + kx * g;
-  }, false);
+  }, [&](int i) { return sc(sp, hper * r + i); }, false);
 }
 
 // ---------------------------------------------------------------------------- exchanges
@@ -477,8 +509,9 @@ struct LayerConsts {
 template <typename WT, int M>
 __device__ __forceinline__ void load_consts(LayerConsts& c, const KCONST CpDesc& D, const KCONST LayerW& W, int p0) {
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, G = D.nq / D.nkv;
-  const WT* an = reinterpret_cast<const WT*>(W.attn_norm);
-  const WT* mn = reinterpret_cast<const WT*>(W.mlp_norm);
+  using GT = typename WTraits<WT>::GT;  // gains stay bf16 next to E4M3 matrices
+  const GT* an = reinterpret_cast<const GT*>(W.attn_norm);
+  const GT* mn = reinterpret_cast<const GT*>(W.mlp_norm);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int i = tid + k * NT;
@@ -488,8 +521,8 @@ __device__ __forceinline__ void load_consts(LayerConsts& c, const KCONST CpDesc&
 #pragma unroll
   for (int k = 0; k < 2; ++k) { c.qg[k] = c.kg[k] = c.rc[k] = 1.f; c.rs[k] = 0.f; }
   if (wave < G * M) {
-    const WT* qn = reinterpret_cast<const WT*>(W.q_norm);
-    const WT* kn = reinterpret_cast<const WT*>(W.k_norm);
+    const GT* qn = reinterpret_cast<const GT*>(W.q_norm);
+    const GT* kn = reinterpret_cast<const GT*>(W.k_norm);
     c.qg[0] = to_f32(glb(qn)[lane]);
     c.qg[1] = to_f32(glb(qn)[lane + 64]);
     c.kg[0] = to_f32(glb(kn)[lane]);
@@ -582,7 +615,7 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
   rows_dot<WT, M>(R1, qper, H, S.xn, H, S.out);
   lds_barrier();
   if (!slice_gather<M, M>(X, qper, qrows, [&](int e, int m) { return S.out[e * M + m]; }, S.qkv, tag, iring, g, r,
-                          [&] { issue_gu(R1, 0, D, W, g, r); }))
+                          [&] { issue_gu(R1, 0, D, layer, g, r); }))
     return false;
 
   // --- attention for this XCD's heads over positions 0 .. p0 + M - 1 (d = 128): one wave per
@@ -650,13 +683,13 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
     S.ob[m * G * d + h * d + lane] = o0 / l;
     S.ob[m * G * d + h * d + lane + 64] = o1 / l;
   }
-  issue_gu(R2, RA_R * NW, D, W, g, r);  // the gate/up rows past R1's
+  issue_gu(R2, RA_R * NW, D, layer, g, r);  // the gate/up rows past R1's
   lds_barrier();
 
   // --- output projection partial (R0: rows [hper*r, +hper), this XCD's head columns), residual
   rows_dot<WT, M>(R0, hper, G * d, S.ob, G * d, S.out);
   lds_barrier();
-  if (!reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] { issue_down(R0, D, W, g, r); })) return false;
+  if (!reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] { issue_down(R0, D, layer, g, r); })) return false;
 
   // --- gate/up slice (R1) + SwiGLU
   rmsnorm_reg<M>(S.xs, H, c.mn, D.eps, S.xn, S.red, S.xs + M * H);
@@ -667,7 +700,7 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
                           tag, iring, g, r, [&] {
                             if (!last) {
                               load_consts<WT, M>(c, D, D.layer[layer + 1], p0);
-                              issue_qkv(R1, D, D.layer[layer + 1], g, r);
+                              issue_qkv(R1, D, layer + 1, g, r);
                             } else {
                               issue_head(R1, D, j);
                             }
@@ -678,7 +711,7 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
   rows_dot<WT, M>(R0, hper, fx, S.hb, fx, S.out);
   lds_barrier();
   return reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] {
-    if (!last) issue_o(R0, D, D.layer[layer + 1], g, r);
+    if (!last) issue_o(R0, D, layer + 1, g, r);
     else if (j < D.n_ac && D.proj) issue_proj(R0, D, g, r);
   });
 }
@@ -737,9 +770,10 @@ __device__ __forceinline__ bool cp_step(const KCONST CpDesc& D, const CpCall& C,
   const int H = D.H, Ht = D.Ht, V = D.V, tid = threadIdx.x;
   const Xch X{D.xin, D.xcr, D.err};
   constexpr int KCP = (M * (HMAX + NR) + NT - 1) / NT;
-  const WT* tab = (j == 1) ? reinterpret_cast<const WT*>(D.embed_sem)
-                           : reinterpret_cast<const WT*>(D.embed_ac) + (size_t)(j - 2) * V * Ht;
-  const WT* erow = tab + (size_t)tok * Ht;
+  using GT = typename WTraits<WT>::GT;  // embedding tables stay bf16 next to E4M3 matrices
+  const GT* tab = (j == 1) ? reinterpret_cast<const GT*>(D.embed_sem)
+                           : reinterpret_cast<const GT*>(D.embed_ac) + (size_t)(j - 2) * V * Ht;
+  const GT* erow = tab + (size_t)tok * Ht;
   if (D.proj) {
     const int kx = Ht / NX, hper = H / NR;
     for (int i = tid; i < kx; i += NT) {
@@ -753,10 +787,10 @@ __device__ __forceinline__ bool cp_step(const KCONST CpDesc& D, const CpCall& C,
     lds_barrier();
     rows_dot<WT, M>(R0, hper, kx, S.xn, kx, S.out);
     lds_barrier();
-    if (!reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, false, tag, iring, cpar, g, r, [&] { issue_o(R0, D, D.layer[0], g, r); }))
+    if (!reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, false, tag, iring, cpar, g, r, [&] { issue_o(R0, D, 0, g, r); }))
       return false;
   } else {
-    issue_o(R0, D, D.layer[0], g, r);
+    issue_o(R0, D, 0, g, r);
     for (int i = tid; i < H; i += NT) {
       if (M == 2) {
         S.xs[i] = glb(D.hT)[i];
@@ -777,7 +811,7 @@ __device__ __forceinline__ bool cp_step(const KCONST CpDesc& D, const CpCall& C,
   lds_barrier();
   if (j < D.n_ac) {
     load_consts<WT, 1>(c, D, D.layer[0], j + 1);
-    issue_qkv(R1, D, D.layer[0], g, r);
+    issue_qkv(R1, D, 0, g, r);
   }
   if (C.logits)
     for (int i = tid; i < vper; i += NT) glb(C.logits)[(size_t)(j - 1) * V + vper * blockIdx.x + i] = S.out[i];
@@ -800,7 +834,7 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   load_consts<WT, 2>(c, D, D.layer[0], 0);
   float fn[2];
   {
-    const WT* f = reinterpret_cast<const WT*>(D.final_norm);
+    const typename WTraits<WT>::GT* f = reinterpret_cast<const typename WTraits<WT>::GT*>(D.final_norm);
 #pragma unroll
     for (int k = 0; k < 2; ++k) fn[k] = threadIdx.x + k * NT < D.H ? to_f32(glb(f)[threadIdx.x + k * NT]) : 0.f;
   }
@@ -808,7 +842,7 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   RowsA<WT> R1;
   RowsC<WT> R2;
   if (D.proj) issue_proj(R0, D, g, r);
-  issue_qkv(R1, D, D.layer[0], g, r);
+  issue_qkv(R1, D, 0, g, r);
   uint32_t tag = glb(D.st)->epoch;
   const int frame = glb(D.st)->frame;
   int iring = 0, cpar = 0, apar = 0;

@@ -502,10 +502,13 @@ def fp8_model(request):
     return request.param, model, w
 
 
-def test_fp8_teacher_forced_step_parity(fp8_model):
-    """Weight-only E4M3 decode (per-op kernels, MFMA GEMM prefill) against the oracle run on the
-    matrices the codes and row scales stand for. Both sides compute in fp32 from the same
-    weights, so the bf16 models' bar applies."""
+@pytest.mark.parametrize("mode", ["persistent", "kernels"])
+def test_fp8_teacher_forced_step_parity(fp8_model, mode):
+    """Weight-only E4M3 decode against the oracle run on the matrices the codes and row scales
+    stand for, with the CodePredictor frame on the persistent kernel (E4M3 rows and row scales in
+    its register buffers; the default) and on the per-op kernels. The Talker runs per-op kernels,
+    the prompt the MFMA GEMMs. Both sides compute in fp32 from the same weights, so the bf16
+    models' bar applies."""
     name, model, w = fp8_model
     orc = OracleModel(w, model.as_dict(), np.float32)
     ids = synth.random_ids(16, model.text_vocab, seed=1)
@@ -513,13 +516,16 @@ def test_fp8_teacher_forced_step_parity(fp8_model):
     ref = orc.generate(ids, F, GREEDY, GREEDY, np.zeros((1, F, 16), np.float32))
     del orc
     dec, dw = make_decoder(model, 1, 64 + 240, 240, w)
-    mode, supported = dec.exec_mode()
-    assert supported == 0 and mode == tts.EXEC_KERNELS, "E4M3 weights run on the per-op kernels"
+    default, supported = dec.exec_mode()
+    assert supported == tts.PERSISTENT_CODEPRED and default == tts.EXEC_PERSISTENT, \
+        "E4M3 weights: the persistent CodePredictor kernel, per-op Talker kernels"
+    dec.set_exec_mode(tts.EXEC_PERSISTENT if mode == "persistent" else tts.EXEC_KERNELS)
     assert dec.prefill_mode() == tts.PREFILL_GEMM
-    print(f"{name}: running", flush=True)
+    print(f"{name} {mode}: running", flush=True)
     sem, ac, tok = teacher_forced(dec, model, ids, ref["codes"], F)
+    assert dec.device_status() == 0
     es, ea, n, ex = check_step_parity(model, ref, sem, ac, tok, 1e-2)
-    print(f"{name}: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}")
+    print(f"{name} {mode}: sem rel err {es:.2e}, ac rel err {ea:.2e}, greedy checked {n}, exempt {ex}")
     dec.close()
     del dw
     torch.cuda.empty_cache()

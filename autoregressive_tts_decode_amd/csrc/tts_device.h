@@ -477,6 +477,10 @@ __device__ __forceinline__ void load_row(const float* p, float (&f)[EPL]) {
 // With several splits, every block writes an unnormalised partial
 // (o, max, sum) and the last block to arrive for a (stream, KV head) merges
 // them (device-scope fences around an arrival counter), so no merge kernel.
+// While the context fits kAttnOneSplit positions, one block per (stream, KV
+// head) attends over all of it and writes the output itself: at short
+// contexts the partial and merge pass cost more than the longer walk.
+constexpr int kAttnOneSplit = 128;
 template <typename WT, typename KT, int G, int M, int D>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   constexpr int EPL = D / 16;
@@ -485,10 +489,12 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int p0 = a.pos_from_state ? a.st->pos : a.pos_const;
   const int plast = p0 + M - 1;
-  const int s0 = split * a.chunk;
+  // positions per split for this launch's context (the same in every block of the grid)
+  const int chunk = (a.nsplit > 1 && plast < kAttnOneSplit) ? kAttnOneSplit : a.chunk;
+  const int s0 = split * chunk;
   if (s0 > plast) return;  // nothing to attend in this split; not counted by the merge
-  const int s1 = min(s0 + a.chunk, plast + 1);
-  const int used = min(a.nsplit, plast / a.chunk + 1);
+  const int s1 = min(s0 + chunk, plast + 1);
+  const int used = min(a.nsplit, plast / chunk + 1);
   const int row0 = b * M;
   const int st0 = a.kvstart ? a.kvstart[b] : 0;  // positions before it are another stream's padding
 
@@ -541,7 +547,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     if (j < G) {
 #pragma unroll
       for (int i = 0; i < PL; ++i) qs[m][j][lane + 64 * i] = v[i];
-    } else if (p >= s0 && p < s0 + a.chunk) {
+    } else if (p >= s0 && p < s0 + chunk) {
       KT* dst = (j == G ? kcache : vcache) + (size_t)p * D;
 #pragma unroll
       for (int i = 0; i < PL; ++i) store_elem(dst + lane + 64 * i, v[i]);
@@ -626,7 +632,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     }
     const int qh = g * G + h;
     const int row = row0 + m;
-    if (a.nsplit == 1) {
+    if (used == 1) {
       a.out[(size_t)row * a.out_stride + (size_t)qh * D + e] = l > 0.f ? acc / l : 0.f;
     } else {
       float* pp = a.part + (((size_t)row * a.nq + qh) * a.nsplit + split) * (D + 2);
@@ -634,7 +640,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
       if (e == 0) { pp[D] = mx; pp[D + 1] = l; }
     }
   }
-  if (a.nsplit == 1) return;
+  if (used == 1) return;
 
   // 4. the last split block of this (stream, KV head) merges the partials
   __shared__ int last;
@@ -653,7 +659,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     const int m = i / (G * D), h = (i / D) % G, e = i % D;
     const int qh = g * G + h;
     const int row = row0 + m;
-    const int usedm = min(a.nsplit, (p0 + m) / a.chunk + 1);
+    const int usedm = min(a.nsplit, (p0 + m) / chunk + 1);
     const float* pp = a.part + ((size_t)row * a.nq + qh) * a.nsplit * (D + 2);
     float mx = -INFINITY;
     for (int sp = 0; sp < usedm; ++sp) mx = fmaxf(mx, pp[sp * (D + 2) + D]);

@@ -271,9 +271,13 @@ __device__ __forceinline__ void rows_issue(Rows<WT, RR, KK>& R, int nrows, int n
 }
 
 // out[i * M + m] = dot(row i, x[m * ldx .. + ncols]) for this wave's rows (LDS in/out).
-template <typename WT, int M, int RR, int KK>
-__device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, int ldx, float* out,
-                                         int row0 = 0) {
+// NG: the dot is taken with RMSNorm(x row m) instead: every element times its bf16 gain gn[k]
+// (LDS), the row sum times 1 / sqrt(mean(x^2) + eps), with sum(x^2) the sum of the NR per-rank
+// sums of squares at ss[m * NR ..]. The norm is then one scale per row sum and needs no pass
+// (and no barrier) of its own.
+template <typename WT, int M, int RR, int KK, bool NG>
+__device__ __forceinline__ void rows_dot_impl(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, int ldx, float* out,
+                                              int row0, const uint16_t* gn, const float* ss, float eps) {
   constexpr int E = WTraits<WT>::E, MAXR = RR, MAXK = KK;
   const int lane = threadIdx.x & 63, wave = row0 + wave_id();
   const int units = ncols / E;
@@ -296,6 +300,17 @@ __device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, i
           xv[m][e] = f.x; xv[m][e + 1] = f.y; xv[m][e + 2] = f.z; xv[m][e + 3] = f.w;
         }
       }
+      if constexpr (NG) {
+#pragma unroll
+        for (int h = 0; h < E; h += 8) {
+          float gf[8];
+          unpack(*reinterpret_cast<const u32x4*>(gn + u * E + h), gf, (uint16_t*)nullptr);
+#pragma unroll
+          for (int m = 0; m < M; ++m)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[m][h + e] *= gf[e];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < MAXR; ++j) {
         if (wave + NW * j < nrows) {
@@ -312,6 +327,21 @@ __device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, i
       }
     }
   }
+  // the norm scales after the dots (their LDS reads would otherwise hold registers through them)
+  float sc[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    sc[m] = 1.f;
+    if constexpr (NG) {
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < NR; q += 4) {
+        const float4 f = *reinterpret_cast<const float4*>(ss + m * NR + q);
+        t += (f.x + f.y) + (f.z + f.w);
+      }
+      sc[m] = 1.0f / sqrtf(t / (float)ncols + eps);
+    }
+  }
 #pragma unroll
   for (int j = 0; j < MAXR; ++j) {
     const int i = wave + NW * j;
@@ -320,10 +350,24 @@ __device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, i
       for (int m = 0; m < M; ++m) {
         float v = wave_sum(acc[j][m]);
         if constexpr (E == 16) v *= R.s[j];
+        if constexpr (NG) v *= sc[m];
         if (lane == 0) out[i * M + m] = v;
       }
     }
   }
+}
+
+template <typename WT, int M, int RR, int KK>
+__device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, int ldx, float* out,
+                                         int row0 = 0) {
+  rows_dot_impl<WT, M, RR, KK, false>(R, nrows, ncols, x, ldx, out, row0, nullptr, nullptr, 0.f);
+}
+
+// The same with RMSNorm(x) as the input (x: the residual rows, row stride ncols).
+template <typename WT, int M, int RR, int KK>
+__device__ __forceinline__ void rows_dot_norm(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, const uint16_t* gn,
+                                              const float* ss, float eps, float* out, int row0 = 0) {
+  rows_dot_impl<WT, M, RR, KK, true>(R, nrows, ncols, x, ncols, out, row0, gn, ss, eps);
 }
 
 // ---------------------------------------------------------------------------- block helpers
@@ -342,6 +386,7 @@ struct Smem {
   float kq[4][128];     // normed + rotated q of each attention wave
   float cand[2 * NWG];  // argmax candidates of every workgroup
   float kvc[MAXL][2][kCpPos][KVS];  // this frame's K/V rows of KV head g, per layer
+  __align__(16) uint16_t gn[2 * MAXL + 1][HMAX];  // bf16 norm gains: layer l attention 2 l, MLP 2 l + 1; final 2 MAXL
 };
 
 // ---------------------------------------------------------------------------- weight phases
@@ -498,26 +543,17 @@ __device__ __forceinline__ bool slice_gather(const Xch& X, int n, int w, ValFn v
 
 // ---------------------------------------------------------------------------- per-thread constants
 
-// Norm gains and RoPE factors a layer needs, held in registers so no global load sits on the
-// critical path: residual-norm gains of elements tid and tid + NT (H <= 2 NT), and for the
-// attention waves the q- and k-norm gains of lanes lane, lane + 64 and the RoPE cos/sin of
-// positions p0 .. p0 + M - 1 at lane.
+// Per-head norm gains and RoPE factors a layer needs, held in registers so no global load sits on
+// the critical path: for the attention waves the q- and k-norm gains of lanes lane, lane + 64 and
+// the RoPE cos/sin of positions p0 .. p0 + M - 1 at lane. (The residual-norm gains sit in LDS.)
 struct LayerConsts {
-  float an[2], mn[2], qg[2], kg[2], rc[2], rs[2];
+  float qg[2], kg[2], rc[2], rs[2];
 };
 
 template <typename WT, int M>
 __device__ __forceinline__ void load_consts(LayerConsts& c, const KCONST CpDesc& D, const KCONST LayerW& W, int p0) {
   const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63, G = D.nq / D.nkv;
   using GT = typename WTraits<WT>::GT;  // gains stay bf16 next to E4M3 matrices
-  const GT* an = reinterpret_cast<const GT*>(W.attn_norm);
-  const GT* mn = reinterpret_cast<const GT*>(W.mlp_norm);
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = tid + k * NT;
-    c.an[k] = i < D.H ? to_f32(glb(an)[i]) : 0.f;
-    c.mn[k] = i < D.H ? to_f32(glb(mn)[i]) : 0.f;
-  }
 #pragma unroll
   for (int k = 0; k < 2; ++k) { c.qg[k] = c.kg[k] = c.rc[k] = 1.f; c.rs[k] = 0.f; }
   if (wave < G * M) {
@@ -535,68 +571,16 @@ __device__ __forceinline__ void load_consts(LayerConsts& c, const KCONST CpDesc&
   }
 }
 
-// y[m] = x[m] * rsqrt(mean(x[m]^2) + eps) * gain over n <= 2 NT elements (rows n apart in LDS),
-// gain of elements tid, tid + NT in gr. ss: the per-rank sums of squares of row m at ss[m * NR ..]
-// (from reduce_gather), or nullptr to reduce here.
-template <int M>
-__device__ __forceinline__ void rmsnorm_reg(const float* x, int n, const float* gr, float eps, float* y, float* red,
-                                            const float* ss = nullptr) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float tot[M];
-  if (ss) {
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float s = 0.f;
-#pragma unroll
-      for (int q = 0; q < NR; q += 4) {
-        const float4 f = *reinterpret_cast<const float4*>(ss + m * NR + q);
-        s += (f.x + f.y) + (f.z + f.w);
-      }
-      tot[m] = s;
-    }
-  } else {
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float s = 0.f;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int i = tid + k * NT;
-        if (i < n) s += x[m * n + i] * x[m * n + i];
-      }
-      s = wave_sum(s);
-      if (lane == 0) red[m * NW + wave] = s;
-    }
-    lds_barrier();
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      float s = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) s += red[m * NW + w];
-      tot[m] = s;
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const float sc = 1.0f / sqrtf(tot[m] / (float)n + eps);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = tid + k * NT;
-      if (i < n) y[m * n + i] = x[m * n + i] * sc * gr[k];
-    }
-  }
-  lds_barrier();
-}
-
 // ---------------------------------------------------------------------------- the layer
 
 // One decoder layer for M rows at positions p0 .. p0 + M - 1. Weight phases alternate between two
 // register buffers and are issued two phases ahead of their use. On entry R1 holds this layer's
 // q/k/v rows, R0 its output-projection rows and c its constants; on exit R1 holds the next layer's
 // q/k/v rows (or head j), R0 the next layer's output-projection rows (or the next step's input
-// projection) and c the next layer's constants. have_ss: S.xs carries the per-rank sums of squares
-// of the input rows (it does unless the rows were staged without an exchange).
+// projection) and c the next layer's constants. S.xs holds the input rows and, after them, their
+// NR sums of squares per row (the RMSNorms take those; gains in S.gn).
 template <typename WT, int M>
-__device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C, int layer, int j, int p0, bool have_ss, Smem& S,
+__device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C, int layer, int j, int p0, Smem& S,
                                          RowsB<WT>& R0, RowsA<WT>& R1, RowsC<WT>& R2, LayerConsts& c, uint32_t& tag, int& iring,
                                          int& cpar, int g, int r) {
   const KCONST LayerW& W = D.layer[layer];
@@ -611,8 +595,7 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
   constexpr int KCP = (M * (HMAX + NR) + NT - 1) / NT;
 
   // --- q/k/v slice (R1)
-  rmsnorm_reg<M>(S.xs, H, c.an, D.eps, S.xn, S.red, have_ss ? S.xs + M * H : nullptr);
-  rows_dot<WT, M>(R1, qper, H, S.xn, H, S.out);
+  rows_dot_norm<WT, M>(R1, qper, H, S.xs, S.gn[2 * layer], S.xs + M * H, D.eps, S.out);
   lds_barrier();
   if (!slice_gather<M, M>(X, qper, qrows, [&](int e, int m) { return S.out[e * M + m]; }, S.qkv, tag, iring, g, r,
                           [&] { issue_gu(R1, 0, D, layer, g, r); }))
@@ -692,9 +675,8 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
   if (!reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] { issue_down(R0, D, layer, g, r); })) return false;
 
   // --- gate/up slice (R1) + SwiGLU
-  rmsnorm_reg<M>(S.xs, H, c.mn, D.eps, S.xn, S.red, S.xs + M * H);
-  rows_dot<WT, M>(R1, 2 * fper, H, S.xn, H, S.out);
-  rows_dot<WT, M>(R2, 2 * fper, H, S.xn, H, S.out, RA_R * NW);
+  rows_dot_norm<WT, M>(R1, 2 * fper, H, S.xs, S.gn[2 * layer + 1], S.xs + M * H, D.eps, S.out);
+  rows_dot_norm<WT, M>(R2, 2 * fper, H, S.xs, S.gn[2 * layer + 1], S.xs + M * H, D.eps, S.out, RA_R * NW);
   lds_barrier();
   if (!slice_gather<M, M>(X, fper, fx, [&](int e, int m) { return silu(S.out[e * M + m]) * S.out[(fper + e) * M + m]; }, S.hb,
                           tag, iring, g, r, [&] {
@@ -765,7 +747,7 @@ __device__ __forceinline__ int argmax_exchange(const KCONST CpDesc& D, Smem& S, 
 // constants; on exit they hold the next step's.
 template <typename WT, int M>
 __device__ __forceinline__ bool cp_step(const KCONST CpDesc& D, const CpCall& C, int j, int& tok, Smem& S, RowsB<WT>& R0,
-                                        RowsA<WT>& R1, RowsC<WT>& R2, LayerConsts& c, const float* fn, uint32_t& tag, int& iring,
+                                        RowsA<WT>& R1, RowsC<WT>& R2, LayerConsts& c, uint32_t& tag, int& iring,
                                         int& cpar, int& apar, int frame, int g, int r) {
   const int H = D.H, Ht = D.Ht, V = D.V, tid = threadIdx.x;
   const Xch X{D.xin, D.xcr, D.err};
@@ -800,14 +782,26 @@ __device__ __forceinline__ bool cp_step(const KCONST CpDesc& D, const CpCall& C,
       }
     }
     lds_barrier();
+    // the rows' sums of squares in the layout an exchange leaves them: NR per row (one per wave
+    // here, the rest zero)
+    {
+      const int wave = wave_id(), lane = tid & 63;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float q = 0.f;
+        for (int i = wave * 64 + lane; i < H; i += NT) q += S.xs[m * H + i] * S.xs[m * H + i];
+        q = wave_sum(q);
+        if (lane < NR / NW) S.xs[M * H + m * NR + wave + NW * lane] = lane == 0 ? q : 0.f;
+      }
+    }
+    lds_barrier();
   }
   const int p0 = (j == 1) ? 0 : j;
   for (int l = 0; l < D.n_layers; ++l)
-    if (!cp_layer<WT, M>(D, C, l, j, p0, l > 0 || D.proj, S, R0, R1, R2, c, tag, iring, cpar, g, r)) return false;
+    if (!cp_layer<WT, M>(D, C, l, j, p0, S, R0, R1, R2, c, tag, iring, cpar, g, r)) return false;
   // final norm on the last row, head j (R1), argmax
   const int vper = V / NWG;
-  rmsnorm_reg<1>(S.xs + (M - 1) * H, H, fn, D.eps, S.xn, S.red, S.xs + M * H + (M - 1) * NR);
-  rows_dot<WT, 1>(R1, vper, H, S.xn, H, S.out);
+  rows_dot_norm<WT, 1>(R1, vper, H, S.xs + (M - 1) * H, S.gn[2 * MAXL], S.xs + M * H + (M - 1) * NR, D.eps, S.out);
   lds_barrier();
   if (j < D.n_ac) {
     load_consts<WT, 1>(c, D, D.layer[0], j + 1);
@@ -832,11 +826,16 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   // constants first (they are needed first), then the first two weight phases
   LayerConsts c;
   load_consts<WT, 2>(c, D, D.layer[0], 0);
-  float fn[2];
+  // every RMSNorm gain of the frame into LDS (bf16, as stored; the first barrier of the frame
+  // comes before their first use)
   {
-    const typename WTraits<WT>::GT* f = reinterpret_cast<const typename WTraits<WT>::GT*>(D.final_norm);
-#pragma unroll
-    for (int k = 0; k < 2; ++k) fn[k] = threadIdx.x + k * NT < D.H ? to_f32(glb(f)[threadIdx.x + k * NT]) : 0.f;
+    static_assert(sizeof(typename WTraits<WT>::GT) == 2, "norm gains are bf16");
+    const int nv = D.H / 8;  // 16-byte units per gain vector
+    for (int i = threadIdx.x; i < (2 * D.n_layers + 1) * nv; i += NT) {
+      const int v = i / nv, u = i % nv;
+      const void* src = v == 2 * D.n_layers ? D.final_norm : (v & 1) ? D.layer[v >> 1].mlp_norm : D.layer[v >> 1].attn_norm;
+      *reinterpret_cast<u32x4*>(&S.gn[v == 2 * D.n_layers ? 2 * MAXL : v][8 * u]) = glb(reinterpret_cast<const u32x4*>(src))[u];
+    }
   }
   RowsB<WT> R0;
   RowsA<WT> R1;
@@ -849,9 +848,9 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   int tok = glb(C.semantic)[0];
   if (tok < 0) tok = 0;
   if (tok >= D.Vs) tok = D.Vs - 1;
-  bool ok = cp_step<WT, 2>(D, C, 1, tok, S, R0, R1, R2, c, fn, tag, iring, cpar, apar, frame, g, r);
+  bool ok = cp_step<WT, 2>(D, C, 1, tok, S, R0, R1, R2, c, tag, iring, cpar, apar, frame, g, r);
   for (int j = 2; ok && j <= D.n_ac; ++j)
-    ok = cp_step<WT, 1>(D, C, j, tok, S, R0, R1, R2, c, fn, tag, iring, cpar, apar, frame, g, r);
+    ok = cp_step<WT, 1>(D, C, j, tok, S, R0, R1, R2, c, tag, iring, cpar, apar, frame, g, r);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     glb(D.st)->epoch = tag + 1;  // every workgroup has read the epoch: all took part in the last exchange
     if (C.next_tok) glb(C.next_tok)[0] = tok;

@@ -275,8 +275,9 @@ __device__ __forceinline__ void rows_issue(Rows<WT, RR, KK>& R, int nrows, int n
 // (LDS), the row sum times 1 / sqrt(mean(x^2) + eps), with sum(x^2) the sum of the NR per-rank
 // sums of squares at ss[m * NR ..]. The norm is then one scale per row sum and needs no pass
 // (and no barrier) of its own.
-template <typename WT, int M, int RR, int KK, bool NG>
-__device__ __forceinline__ void rows_dot_impl(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, int ldx, float* out,
+// emit(i, m, v) takes each row sum (lane 0 of the row's wave).
+template <typename WT, int M, int RR, int KK, bool NG, typename Emit>
+__device__ __forceinline__ void rows_dot_impl(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, int ldx, Emit emit,
                                               int row0, const uint16_t* gn, const float* ss, float eps) {
   constexpr int E = WTraits<WT>::E, MAXR = RR, MAXK = KK;
   const int lane = threadIdx.x & 63, wave = row0 + wave_id();
@@ -351,7 +352,7 @@ __device__ __forceinline__ void rows_dot_impl(const Rows<WT, RR, KK>& R, int nro
         float v = wave_sum(acc[j][m]);
         if constexpr (E == 16) v *= R.s[j];
         if constexpr (NG) v *= sc[m];
-        if (lane == 0) out[i * M + m] = v;
+        if (lane == 0) emit(i, m, v);
       }
     }
   }
@@ -360,14 +361,28 @@ __device__ __forceinline__ void rows_dot_impl(const Rows<WT, RR, KK>& R, int nro
 template <typename WT, int M, int RR, int KK>
 __device__ __forceinline__ void rows_dot(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, int ldx, float* out,
                                          int row0 = 0) {
-  rows_dot_impl<WT, M, RR, KK, false>(R, nrows, ncols, x, ldx, out, row0, nullptr, nullptr, 0.f);
+  rows_dot_impl<WT, M, RR, KK, false>(R, nrows, ncols, x, ldx, [&](int i, int m, float v) { out[i * M + m] = v; }, row0, nullptr,
+                                      nullptr, 0.f);
+}
+
+// The row sums to emit(i, m, v) instead of LDS.
+template <typename WT, int M, int RR, int KK, typename Emit>
+__device__ __forceinline__ void rows_dot_to(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, int ldx, Emit emit) {
+  rows_dot_impl<WT, M, RR, KK, false>(R, nrows, ncols, x, ldx, emit, 0, nullptr, nullptr, 0.f);
 }
 
 // The same with RMSNorm(x) as the input (x: the residual rows, row stride ncols).
 template <typename WT, int M, int RR, int KK>
 __device__ __forceinline__ void rows_dot_norm(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, const uint16_t* gn,
                                               const float* ss, float eps, float* out, int row0 = 0) {
-  rows_dot_impl<WT, M, RR, KK, true>(R, nrows, ncols, x, ncols, out, row0, gn, ss, eps);
+  rows_dot_impl<WT, M, RR, KK, true>(R, nrows, ncols, x, ncols, [&](int i, int m, float v) { out[i * M + m] = v; }, row0, gn, ss,
+                                     eps);
+}
+
+template <typename WT, int M, int RR, int KK, typename Emit>
+__device__ __forceinline__ void rows_dot_norm_to(const Rows<WT, RR, KK>& R, int nrows, int ncols, const float* x, const uint16_t* gn,
+                                                 const float* ss, float eps, Emit emit) {
+  rows_dot_impl<WT, M, RR, KK, true>(R, nrows, ncols, x, ncols, emit, 0, gn, ss, eps);
 }
 
 // ---------------------------------------------------------------------------- block helpers
@@ -484,13 +499,16 @@ __device__ __forceinline__ void issue_proj(RowsB<WT>& R, const KCONST CpDesc& D,
 // cpar alternates the cross slot so a rank one exchange ahead never overwrites unread values.
 // HMX: the largest H the caller supports (sizes the cross gather); KMAX: loads per thread of the
 // intra gather (M * (H + NR) entries).
-template <int M, int HMX, int KMAX, int NPOLL = NT, typename AfterPut>
-__device__ __forceinline__ bool reduce_gather(const Xch& X, const float* out, float* xs, float* xn, int H, bool residual,
-                                              uint32_t& tag, int& iring, int& cpar, int g, int r, AfterPut after_put) {
+// produce(emit): makes the partial rows, calling emit(row, m, value) once for every row < hper and
+// m < M (from any thread; reduce_gather: all threads from S.out).
+template <int M, int HMX, int KMAX, int NPOLL = NT, typename Produce, typename AfterPut>
+__device__ __forceinline__ bool reduce_gather_p(const Xch& X, Produce produce, float* xs, float* xn, int H, bool residual,
+                                                uint32_t& tag, int& iring, int& cpar, int g, int r, AfterPut after_put) {
   const int tid = fresh_tid(), hper = H / NR;
   ++tag;
   u64* mine = X.xcr + ((size_t)(r * NX + g) * 2 + (cpar & 1)) * CSZ;
-  for (int i = tid; i < hper * M; i += NT) st_c(mine + (i % M) * 64 + i / M, pack(out[i], tag));
+  const uint32_t t = tag;
+  produce([&](int e, int m, float v) { st_c(mine + m * 64 + e, pack(v, t)); });
   after_put();
   // partners: rank r on every XCD x, slot r * NX + x; their slots are 2 * CSZ apart.
   // Segment (x, m) -> xn[(x * M + m) * hper ..]
@@ -526,19 +544,41 @@ __device__ __forceinline__ bool reduce_gather(const Xch& X, const float* out, fl
   return get_flat<KMAX, NPOLL>(buf, M * (H + NR), tag, xs, X.err);
 }
 
+template <int M, int HMX, int KMAX, int NPOLL = NT, typename AfterPut>
+__device__ __forceinline__ bool reduce_gather(const Xch& X, const float* out, float* xs, float* xn, int H, bool residual,
+                                              uint32_t& tag, int& iring, int& cpar, int g, int r, AfterPut after_put) {
+  const int hper = H / NR;
+  return reduce_gather_p<M, HMX, KMAX, NPOLL>(
+      X,
+      [&](auto emit) {
+        for (int i = fresh_tid(); i < hper * M; i += NT) emit(i / M, i % M, out[i]);
+      },
+      xs, xn, H, residual, tag, iring, cpar, g, r, after_put);
+}
+
 // Intra gather of a slice: this workgroup's n values per row (vals(e, m)) land at row offset
 // n * r of every rank's copy; the full rows (width w) of all ranks go to dst.
+// produce(emit): calls emit(e, m, value) once for every e < n and m < M (from any thread).
+template <int M, int KMAX, int NPOLL = NT, typename Produce, typename AfterPut>
+__device__ __forceinline__ bool slice_gather_p(const Xch& X, int n, int w, Produce produce, float* dst, uint32_t& tag, int& iring,
+                                               int g, int r, AfterPut after_put) {
+  ++tag;
+  u64* buf = X.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
+  const uint32_t t = tag;
+  produce([&](int e, int m, float v) { st_l(buf + m * w + n * r + e, pack(v, t)); });
+  after_put();
+  return get_flat<KMAX, NPOLL>(buf, M * w, tag, dst, X.err);
+}
+
 template <int M, int KMAX, int NPOLL = NT, typename ValFn, typename AfterPut>
 __device__ __forceinline__ bool slice_gather(const Xch& X, int n, int w, ValFn vals, float* dst, uint32_t& tag, int& iring,
                                              int g, int r, AfterPut after_put) {
-  ++tag;
-  u64* buf = X.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
-  for (int i = fresh_tid(); i < n * M; i += NT) {
-    const int e = i / M, m = i % M;
-    st_l(buf + m * w + n * r + e, pack(vals(e, m), tag));
-  }
-  after_put();
-  return get_flat<KMAX, NPOLL>(buf, M * w, tag, dst, X.err);
+  return slice_gather_p<M, KMAX, NPOLL>(
+      X, n, w,
+      [&](auto emit) {
+        for (int i = fresh_tid(); i < n * M; i += NT) emit(i / M, i % M, vals(i / M, i % M));
+      },
+      dst, tag, iring, g, r, after_put);
 }
 
 // ---------------------------------------------------------------------------- per-thread constants
@@ -594,11 +634,12 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
   const Xch X{D.xin, D.xcr, D.err};
   constexpr int KCP = (M * (HMAX + NR) + NT - 1) / NT;
 
-  // --- q/k/v slice (R1)
-  rows_dot_norm<WT, M>(R1, qper, H, S.xs, S.gn[2 * layer], S.xs + M * H, D.eps, S.out);
-  lds_barrier();
-  if (!slice_gather<M, M>(X, qper, qrows, [&](int e, int m) { return S.out[e * M + m]; }, S.qkv, tag, iring, g, r,
-                          [&] { issue_gu(R1, 0, D, layer, g, r); }))
+  // --- q/k/v slice (R1). Here and in the output and down projections every wave publishes its row
+  // sums as it makes them (no LDS staging, no barrier before the exchange).
+  if (!slice_gather_p<M, M>(
+          X, qper, qrows,
+          [&](auto emit) { rows_dot_norm_to<WT, M>(R1, qper, H, S.xs, S.gn[2 * layer], S.xs + M * H, D.eps, emit); }, S.qkv,
+          tag, iring, g, r, [&] { issue_gu(R1, 0, D, layer, g, r); }))
     return false;
 
   // --- attention for this XCD's heads over positions 0 .. p0 + M - 1 (d = 128): one wave per
@@ -670,9 +711,10 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
   lds_barrier();
 
   // --- output projection partial (R0: rows [hper*r, +hper), this XCD's head columns), residual
-  rows_dot<WT, M>(R0, hper, G * d, S.ob, G * d, S.out);
-  lds_barrier();
-  if (!reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] { issue_down(R0, D, layer, g, r); })) return false;
+  if (!reduce_gather_p<M, HMAX, KCP>(
+          X, [&](auto emit) { rows_dot_to<WT, M>(R0, hper, G * d, S.ob, G * d, emit); }, S.xs, S.xn, H, true, tag, iring, cpar, g,
+          r, [&] { issue_down(R0, D, layer, g, r); }))
+    return false;
 
   // --- gate/up slice (R1) + SwiGLU
   rows_dot_norm<WT, M>(R1, 2 * fper, H, S.xs, S.gn[2 * layer + 1], S.xs + M * H, D.eps, S.out);
@@ -690,12 +732,11 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
     return false;
 
   // --- down projection partial (R0: rows [hper*r, +hper), this XCD's FFN columns), residual
-  rows_dot<WT, M>(R0, hper, fx, S.hb, fx, S.out);
-  lds_barrier();
-  return reduce_gather<M, HMAX, KCP>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] {
-    if (!last) issue_o(R0, D, layer + 1, g, r);
-    else if (j < D.n_ac && D.proj) issue_proj(R0, D, g, r);
-  });
+  return reduce_gather_p<M, HMAX, KCP>(
+      X, [&](auto emit) { rows_dot_to<WT, M>(R0, hper, fx, S.hb, fx, emit); }, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] {
+        if (!last) issue_o(R0, D, layer + 1, g, r);
+        else if (j < D.n_ac && D.proj) issue_proj(R0, D, g, r);
+      });
 }
 
 // Argmax over the head rows: each workgroup holds nrows logits of rows [row0, row0 + nrows) in

@@ -639,8 +639,14 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
   if (!slice_gather_p<M, M>(
           X, qper, qrows,
           [&](auto emit) { rows_dot_norm_to<WT, M>(R1, qper, H, S.xs, S.gn[2 * layer], S.xs + M * H, D.eps, emit); }, S.qkv,
-          tag, iring, g, r, [&] { issue_gu(R1, 0, D, layer, g, r); }))
+          tag, iring, g, r, [&] {
+            if constexpr (WTraits<WT>::E == 16) issue_gu(R1, 0, D, layer, g, r);
+          }))
     return false;
+  // bf16: the first gate/up rows go out after this exchange, not before its poll. The poll would
+  // wait behind them (a wave's loads return in order), and the attention leaves most waves idle.
+  // (E4M3 rows are half the bytes; for them issuing before the poll measured faster.)
+  if constexpr (WTraits<WT>::E != 16) issue_gu(R1, 0, D, layer, g, r);
 
   // --- attention for this XCD's heads over positions 0 .. p0 + M - 1 (d = 128): one wave per
   // (head h, row m). Every rank of the XCD computes it redundantly from the same gathered q/k/v

@@ -724,17 +724,18 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
 
   // --- gate/up slice (R1) + SwiGLU
   rows_dot_norm<WT, M>(R1, 2 * fper, H, S.xs, S.gn[2 * layer + 1], S.xs + M * H, D.eps, S.out);
+  // R1 is free: the next phase's rows go out before the second part's dot, so they are further
+  // along when the SwiGLU exchange polls behind them
+  if (!last) {
+    load_consts<WT, M>(c, D, D.layer[layer + 1], p0);
+    issue_qkv(R1, D, layer + 1, g, r);
+  } else {
+    issue_head(R1, D, j);
+  }
   rows_dot_norm<WT, M>(R2, 2 * fper, H, S.xs, S.gn[2 * layer + 1], S.xs + M * H, D.eps, S.out, RA_R * NW);
   lds_barrier();
   if (!slice_gather<M, M>(X, fper, fx, [&](int e, int m) { return silu(S.out[e * M + m]) * S.out[(fper + e) * M + m]; }, S.hb,
-                          tag, iring, g, r, [&] {
-                            if (!last) {
-                              load_consts<WT, M>(c, D, D.layer[layer + 1], p0);
-                              issue_qkv(R1, D, layer + 1, g, r);
-                            } else {
-                              issue_head(R1, D, j);
-                            }
-                          }))
+                          tag, iring, g, r, [] {}))
     return false;
 
   // --- down projection partial (R0: rows [hper*r, +hper), this XCD's FFN columns), residual

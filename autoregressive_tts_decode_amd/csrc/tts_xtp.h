@@ -31,7 +31,8 @@
 // are unique per exchange (a running epoch kept on the device), and every
 // exchange buffer is reused only after an exchange that all its readers must
 // have passed, so a value is never overwritten while it may still be read.
-// Each phase issues its weight loads before it waits for its input.
+// Each phase's weight loads are issued before it waits for its input, at a point where no poll
+// follows within about a microsecond (a poll waits behind the loads its wave issued before it).
 #pragma once
 
 #include "tts_device.h"
@@ -53,8 +54,10 @@ constexpr int KVS = 132;    // LDS row stride of the K/V rows (padded against ba
 // gate/up rows past those (RC_R rows per wave), B narrow rows (output and down projections, input
 // projection: RB_R rows of at most 64 * RB_K units). A wave holds its loads' issue once it has
 // more than about 4 KB in flight (measured), so no exchange issues more than 4 KB per wave: the
-// gate/up rows are split between A (issued in the q/k/v exchange) and C (issued during the
-// attention, when most waves are idle and the next poll is an attention and a dot away).
+// gate/up rows are split between A (issued right after the q/k/v exchange for bf16 rows, between
+// its publish and its poll for E4M3 rows) and C (issued with the attention, when most waves are
+// idle and the next poll is an attention and a dot away). The next layer's q/k/v rows go into A
+// between the two gate/up dots.
 constexpr int RA_R = 2, RA_K = 2;
 constexpr int RC_R = 1;
 constexpr int RB_R = 4, RB_K = 1;

@@ -54,9 +54,8 @@ constexpr int KVS = 132;    // LDS row stride of the K/V rows (padded against ba
 // gate/up rows past those (RC_R rows per wave), B narrow rows (output and down projections, input
 // projection: RB_R rows of at most 64 * RB_K units). A wave holds its loads' issue once it has
 // more than about 4 KB in flight (measured), so no exchange issues more than 4 KB per wave: the
-// gate/up rows are split between A (issued right after the q/k/v exchange for bf16 rows, between
-// its publish and its poll for E4M3 rows) and C (issued with the attention, when most waves are
-// idle and the next poll is an attention and a dot away). The next layer's q/k/v rows go into A
+// gate/up rows are split between A (issued right after the q/k/v exchange) and C (issued with the
+// attention, when most waves are idle and the next poll is an attention and a dot away). The next layer's q/k/v rows go into A
 // between the two gate/up dots.
 constexpr int RA_R = 2, RA_K = 2;
 constexpr int RC_R = 1;
@@ -642,14 +641,11 @@ __device__ __forceinline__ bool cp_layer(const KCONST CpDesc& D, const CpCall& C
   if (!slice_gather_p<M, M>(
           X, qper, qrows,
           [&](auto emit) { rows_dot_norm_to<WT, M>(R1, qper, H, S.xs, S.gn[2 * layer], S.xs + M * H, D.eps, emit); }, S.qkv,
-          tag, iring, g, r, [&] {
-            if constexpr (WTraits<WT>::E == 16) issue_gu(R1, 0, D, layer, g, r);
-          }))
+          tag, iring, g, r, [] {}))
     return false;
-  // bf16: the first gate/up rows go out after this exchange, not before its poll. The poll would
-  // wait behind them (a wave's loads return in order), and the attention leaves most waves idle.
-  // (E4M3 rows are half the bytes; for them issuing before the poll measured faster.)
-  if constexpr (WTraits<WT>::E != 16) issue_gu(R1, 0, D, layer, g, r);
+  // The first gate/up rows go out after this exchange, not before its poll: the poll would wait
+  // behind them (a wave's loads return in order), while the attention leaves most waves idle.
+  issue_gu(R1, 0, D, layer, g, r);
 
   // --- attention for this XCD's heads over positions 0 .. p0 + M - 1 (d = 128): one wave per
   // (head h, row m). Every rank of the XCD computes it redundantly from the same gathered q/k/v

@@ -11,6 +11,7 @@
 #include "tts.h"
 #include "tts_device.h"
 #include "tts_prefill.h"
+#include "tts_xcp.h"
 #include "tts_xtk.h"
 #include "tts_xtp.h"
 
@@ -219,6 +220,20 @@ bool xtp_capable(const tts_config& c) {
   return true;
 }
 
+// Whether the lean persistent CodePredictor kernel (tts_xcp.h) handles this config: bf16 weights
+// and the CodePredictor shape it is specialised to (hidden 1024, FFN 3072, 16 query and 8 KV heads
+// of 128, vocabulary 2048, at most 5 layers, 15 codebooks), with no input projection or one from a
+// Talker hidden of 2048.
+bool xcp_capable(const tts_config& c) {
+  const tts_stack_cfg& p = c.codepred;
+  if (c.weight_dtype != TTS_DTYPE_BF16) return false;
+  if (p.hidden != xcp::H || p.ffn != xcp::F || p.n_q_heads != xcp::G * xcp::NX || p.n_kv_heads != xcp::NX ||
+      p.head_dim != xcp::D || p.vocab != xcp::V)
+    return false;
+  if (p.n_layers < 1 || p.n_layers > xcp::MAXL || c.n_acoustic != 15) return false;
+  return c.talker.hidden == xcp::H || c.talker.hidden == xcp::NX * xcp::KX;
+}
+
 // Whether the persistent Talker step kernel handles this config: bf16 weights, an fp32 KV cache,
 // 8 KV heads of dimension 128 with 2 query heads each, and weight slices that fit its chunk shapes
 // (see tts_xtk.h).
@@ -287,6 +302,7 @@ struct tts_ctx {
   int exec_mode = TTS_EXEC_PERSISTENT;  // persistent CodePredictor when supported (batch 1, greedy)
   xtp::CpDesc* cpdesc = nullptr;
   bool xtk_ok = false;   // persistent Talker step supported
+  bool xcp_ok = false;   // the lean CodePredictor kernel supports the config (bf16)
   bool pgemm_ok = false;  // GEMM prefill supported
   int prefill_mode = TTS_PREFILL_GEMM;
   xtp::TkDesc* tkdesc = nullptr;
@@ -797,7 +813,8 @@ int codepred_frame_xtp(tts_ctx* ctx, const int32_t* semantic, const int32_t* for
   call.use_frame = use_frame;
   call.logits = logits_out;
   call.next_tok = nullptr;
-  if (ctx->fp8()) hipLaunchKernelGGL(xtp::k_cp_frame<uint8_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
+  if (ctx->xcp_ok) hipLaunchKernelGGL(xcp::k_cp_frame, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
+  else if (ctx->fp8()) hipLaunchKernelGGL(xtp::k_cp_frame<uint8_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
   else hipLaunchKernelGGL(xtp::k_cp_frame<uint16_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
   HIP_LAUNCH_CHECK();
   return TTS_OK;
@@ -981,6 +998,7 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
   ctx->xerr = (uint32_t*)(w + L.xerr);
   ctx->xtp_ok = xtp_capable(*cfg);
   ctx->xtk_ok = xtk_capable(*cfg);
+  ctx->xcp_ok = ctx->xtp_ok && xcp_capable(*cfg);
   ctx->pgemm_ok = prefill_gemm_capable(*cfg);
   ctx->talker.c = cfg->talker;
   ctx->cp.c = cfg->codepred;
@@ -1446,3 +1464,18 @@ void tts_destroy(tts_ctx* ctx) {
 }
 
 }  // extern "C"
+
+#ifdef TTS_PHASE_TRACE
+// Phase-timeline build only: switch stamping on (on = 1, clears the record first) or off, and
+// copy the record (kTraceWg x kTracePer stamps, 0 = none) to the host buffer out when given.
+extern "C" int tts_trace_ctl(int on, long long* out) {
+  if (out && hipMemcpyFromSymbol(out, HIP_SYMBOL(tts::g_trace), sizeof(long long) * tts::kTraceWg * tts::kTracePer) != hipSuccess)
+    return TTS_E_HIP;
+  if (on) {
+    std::vector<long long> z((size_t)tts::kTraceWg * tts::kTracePer, 0);
+    if (hipMemcpyToSymbol(HIP_SYMBOL(tts::g_trace), z.data(), z.size() * sizeof(long long)) != hipSuccess) return TTS_E_HIP;
+  }
+  if (hipMemcpyToSymbol(HIP_SYMBOL(tts::g_trace_on), &on, sizeof(int)) != hipSuccess) return TTS_E_HIP;
+  return hipDeviceSynchronize() == hipSuccess ? TTS_OK : TTS_E_HIP;
+}
+#endif

@@ -74,7 +74,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout, computed identically by tts_workspace_bytes and tts_create.
 struct Layout {
   size_t st, tk, tv, ck, cv, tcos, tsin, ccos, csin, x, qkv, attn, h, part, counters, logits, hT, cx, clog, next_tok,
-      sem_tok, ac_codes, history, kvstart, aids, cpdesc, tkdesc, px, pqkv, pq, po, pgu, ph, ps, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
+      sem_tok, ac_codes, history, kvstart, aids, cpdesc, tkdesc, px, pqkv, pq, po, pgu, ph, ps, pks, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
   int nsplit;
 };
 
@@ -83,7 +83,7 @@ size_t mat_bytes(const tts_config& c) { return c.weight_dtype == TTS_DTYPE_F32 ?
 size_t tab_bytes(const tts_config& c) { return c.weight_dtype == TTS_DTYPE_F32 ? 4 : 2; }
 // Elements per 16-byte lane load of the matrices.
 int mat_per_unit(const tts_config& c) { return (int)(16 / mat_bytes(c)); }
-size_t kv_bytes(const tts_config& c) { return c.kv_dtype == TTS_DTYPE_BF16 ? 2 : 4; }
+size_t kv_bytes(const tts_config&) { return 4; }
 
 Layout make_layout(const tts_config& c) {
   Layout L{};
@@ -133,6 +133,9 @@ Layout make_layout(const tts_config& c) {
     L.pgu = take(Mp * 2 * t.ffn * 4);
     L.ph = take(Mp * t.ffn * 4);
     L.ps = take(Mp * 4);
+    // split-K partial tiles: a split GEMM has at most kGemmWgs (row tile, column tile, K slice)
+    // workgroups, each writing one 64 x 64 fp32 tile
+    L.pks = take((size_t)kGemmWgs * kGBM * kGBN * 4);
   }
   // persistent kernels: descriptors and exchange buffers (the CodePredictor's K/V rows stay in LDS)
   L.cpdesc = take(sizeof(xtp::CpDesc));
@@ -161,7 +164,8 @@ std::string check_config(const tts_config* c) {
   if (!c) return "config is NULL";
   if (c->weight_dtype != TTS_DTYPE_F32 && c->weight_dtype != TTS_DTYPE_BF16 && c->weight_dtype != TTS_DTYPE_FP8_E4M3)
     return "weight_dtype must be TTS_DTYPE_F32, TTS_DTYPE_BF16 or TTS_DTYPE_FP8_E4M3";
-  if (c->kv_dtype != TTS_DTYPE_F32 && c->kv_dtype != TTS_DTYPE_BF16) return "kv_dtype must be TTS_DTYPE_F32 or TTS_DTYPE_BF16";
+  // a bf16 cache alone puts the 1.7B acoustic logits just over the 1e-2 parity bar, so the caches stay fp32
+  if (c->kv_dtype != TTS_DTYPE_F32) return "kv_dtype must be TTS_DTYPE_F32";
   if (c->n_acoustic != 15) return "n_acoustic must be 15";
   if (c->max_batch < 1 || c->max_batch > 64) return "max_batch must be in [1, 64]";
   if (c->max_cache_steps < 2 || c->max_cache_steps > 65536) return "max_cache_steps must be in [2, 65536]";
@@ -303,6 +307,11 @@ struct tts_ctx {
   xtp::CpDesc* cpdesc = nullptr;
   bool xtk_ok = false;   // persistent Talker step supported
   bool xcp_ok = false;   // the lean CodePredictor kernel supports the config (bf16)
+  int32_t dev_mask = 0;  // persistent kernels the device allows (tts_persistent_allowed)
+  // exchange error word seen from the host without blocking (device_err_check)
+  uint32_t* errh = nullptr;  // pinned host copy
+  hipEvent_t err_ev = nullptr;
+  bool err_pending = false;
   bool pgemm_ok = false;  // GEMM prefill supported
   int prefill_mode = TTS_PREFILL_GEMM;
   xtp::TkDesc* tkdesc = nullptr;
@@ -321,7 +330,6 @@ struct tts_ctx {
   bool bf16() const { return cfg.weight_dtype == TTS_DTYPE_BF16; }
   bool fp8() const { return cfg.weight_dtype == TTS_DTYPE_FP8_E4M3; }
   bool tab16() const { return cfg.weight_dtype != TTS_DTYPE_F32; }  // gains and embedding tables are bf16
-  bool kv_bf16() const { return cfg.kv_dtype == TTS_DTYPE_BF16; }
   size_t meb() const { return mat_bytes(cfg); }
   size_t teb() const { return tab_bytes(cfg); }
   // E4M3 matrices and their per-row scales, for the scale of a row pointer into any of them
@@ -349,6 +357,32 @@ struct tts_ctx {
   } while (0)
 
 namespace {
+
+// The persistent kernels' exchange error word, seen from the host without blocking: every call
+// that may launch them queues a copy of the word into pinned host memory and an event behind its
+// work (device_err_probe); the next such call reads that copy once the event has completed and
+// fails with TTS_E_DEVICE, enqueueing nothing, when the word was set. The word stays set until
+// tts_reset, so every later call reports it again.
+int device_err_check(tts_ctx* ctx) {
+  if (!ctx->err_pending) return TTS_OK;
+  const hipError_t q = hipEventQuery(ctx->err_ev);
+  if (q == hipErrorNotReady) return TTS_OK;
+  ctx->err_pending = false;
+  if (q != hipSuccess) return ctx->fail(TTS_E_HIP, "hipEventQuery: %s", hipGetErrorString(q));
+  if (*ctx->errh)
+    return ctx->fail(TTS_E_DEVICE,
+                     "a persistent kernel timed out in an exchange (error word %u): outputs since the last clean call are "
+                     "invalid; tts_reset clears the state",
+                     *ctx->errh);
+  return TTS_OK;
+}
+int device_err_probe(tts_ctx* ctx) {
+  if (!(ctx->xtp_ok || ctx->xtk_ok) || ctx->exec_mode != TTS_EXEC_PERSISTENT) return TTS_OK;
+  HIP_TRY(hipMemcpyAsync(ctx->errh, ctx->xerr, 4, hipMemcpyDeviceToHost, ctx->stream));
+  HIP_TRY(hipEventRecord(ctx->err_ev, ctx->stream));
+  ctx->err_pending = true;
+  return TTS_OK;
+}
 
 // ---------------------------------------------------------------------------- GEMV dispatch
 
@@ -495,32 +529,33 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
   if (a.epi == EPI_SWIGLU) { g.C = GU; g.ldc = N; g.add = 0; }
   else { g.C = a.y; g.ldc = a.y_stride; g.add = a.epi == EPI_RESID ? 1 : 0; }
   // Split K so that about kGemmWgs workgroups stream the weights (a decode GEMM has few row tiles:
-  // unsplit, N/64 workgroups would each walk all of K with one load in flight). The slices add
-  // into C with atomics, so C starts as the residual or as zeros (cleared by the row-scale
-  // kernel when there is one).
+  // unsplit, N/64 workgroups would each walk all of K with one load in flight). Each slice writes
+  // its partial tile; k_splitk_reduce then adds them into C in slice order (with the residual
+  // first for a residual epilogue), so results do not depend on workgroup timing.
   const int tiles = (N / kGBN) * ((a.M + kGBM - 1) / kGBM);
   int ks = std::max(1, std::min(a.K / kGBK, kGemmWgs / tiles));
   const int kslice = ((a.K / kGBK + ks - 1) / ks) * kGBK;
   ks = (a.K + kslice - 1) / kslice;
   g.kslice = kslice;
-  const bool zero = ks > 1 && !g.add;
+  g.part = (float*)(w + ctx->L.pks);
+  if (ks > 1 && (size_t)ks * tiles > (size_t)kGemmWgs)
+    return ctx->fail(TTS_E_STATE, "gemm: %d K slices of %d tiles exceed the partial-tile buffer", ks, tiles);
   if (a.gain) {
-    // 4 rows' scales per block; with an output to clear, enough blocks for one 16-byte store per
-    // thread (at most 1024)
-    const int zb = zero ? std::min(1024, (int)(((size_t)a.M * N / 4 + 255) / 256)) : 0;
-    hipLaunchKernelGGL(k_rowscale, dim3(std::max((a.M + 3) / 4, zb)), dim3(256), 0, ctx->stream, A, lda, a.M, a.K,
-                       ctx->cfg.rms_eps, RS, zero ? g.C : nullptr, g.ldc, N);
+    hipLaunchKernelGGL(k_rowscale, dim3((a.M + 3) / 4), dim3(256), 0, ctx->stream, A, lda, a.M, a.K, ctx->cfg.rms_eps, RS);
     HIP_LAUNCH_CHECK();
     if (a.xn_out) {
       hipLaunchKernelGGL(k_norm_rows<uint16_t>, dim3(a.M), dim3(256), 0, ctx->stream, A, lda, RS, a.gain, a.K, a.xn_out, a.xn_stride);
       HIP_LAUNCH_CHECK();
     }
-  } else if (zero) {
-    hipLaunchKernelGGL(k_zero_rows, dim3(a.M), dim3(256), 0, ctx->stream, g.C, g.ldc, N);
-    HIP_LAUNCH_CHECK();
   }
   if (int rc = launch_gemm(ctx, g, dim3(N / kGBN, (a.M + kGBM - 1) / kGBM, ks))) return rc;
   HIP_LAUNCH_CHECK();
+  if (ks > 1) {
+    const size_t q = (size_t)a.M * N / 4;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)std::min<size_t>((q + 255) / 256, 2048)), dim3(256), 0, ctx->stream, g.C,
+                       g.ldc, g.part, a.M, N, ks, g.add);
+    HIP_LAUNCH_CHECK();
+  }
   if (a.epi == EPI_SWIGLU) {
     hipLaunchKernelGGL(k_swiglu_rows, dim3(std::min((a.M * a.N + 255) / 256, 4096)), dim3(256), 0, ctx->stream, GU, a.M, a.N, a.y);
     HIP_LAUNCH_CHECK();
@@ -567,8 +602,8 @@ int launch_attn_g(tts_ctx* ctx, const AttnArgs& a, int B) {
 }
 
 int attention(tts_ctx* ctx, const AttnArgs& a, int B) {
-  if (ctx->tab16()) return ctx->kv_bf16() ? launch_attn_g<uint16_t, uint16_t>(ctx, a, B) : launch_attn_g<uint16_t, float>(ctx, a, B);
-  return ctx->kv_bf16() ? launch_attn_g<float, uint16_t>(ctx, a, B) : launch_attn_g<float, float>(ctx, a, B);
+  if (ctx->tab16()) return launch_attn_g<uint16_t, float>(ctx, a, B);
+  return launch_attn_g<float, float>(ctx, a, B);
 }
 
 // ---------------------------------------------------------------------------- building blocks
@@ -702,16 +737,14 @@ int prefill_gemm(tts_ctx* ctx, const int32_t* ids, int B, int n) {
       q.rope_cos = ctx->tcos; q.rope_sin = ctx->tsin;
       q.M = M; q.P = P; q.p0 = p0; q.nq = t.n_q_heads; q.nkv = t.n_kv_heads; q.cap = c.max_cache_steps; q.eps = c.rms_eps;
       const int items = M * (t.n_q_heads + 2 * t.n_kv_heads);
-      if (ctx->kv_bf16()) hipLaunchKernelGGL((k_qk_rope_kv<uint16_t, uint16_t>), dim3((items + 3) / 4), dim3(256), 0, ctx->stream, q);
-      else hipLaunchKernelGGL((k_qk_rope_kv<uint16_t, float>), dim3((items + 3) / 4), dim3(256), 0, ctx->stream, q);
+      hipLaunchKernelGGL((k_qk_rope_kv<uint16_t, float>), dim3((items + 3) / 4), dim3(256), 0, ctx->stream, q);
       HIP_LAUNCH_CHECK();
       PAttnArgs pa;
       std::memset(&pa, 0, sizeof pa);
       pa.q = Q; pa.kc = kc; pa.vc = vc; pa.out = O; pa.P = P; pa.p0 = p0; pa.nq = t.n_q_heads; pa.nkv = t.n_kv_heads;
       pa.cap = c.max_cache_steps;
       pa.kvstart = ctx->kvstart;
-      if (ctx->kv_bf16()) hipLaunchKernelGGL(k_prefill_attn<uint16_t>, dim3((P + 3) / 4, t.n_q_heads, B), dim3(256), 0, ctx->stream, pa);
-      else hipLaunchKernelGGL(k_prefill_attn<float>, dim3((P + 3) / 4, t.n_q_heads, B), dim3(256), 0, ctx->stream, pa);
+      hipLaunchKernelGGL(k_prefill_attn<float>, dim3((P + 3) / 4, t.n_q_heads, B), dim3(256), 0, ctx->stream, pa);
       HIP_LAUNCH_CHECK();
       if (int rc = gemm(O, qd, nullptr, nullptr, {{W.wo, H}}, X, H, qd, M, 1)) return rc;
       hipLaunchKernelGGL(k_rowscale, dim3((M + 3) / 4), dim3(256), 0, ctx->stream, X, H, M, H, c.rms_eps, RS);
@@ -960,6 +993,17 @@ void drop_graph(tts_ctx* ctx) {
 
 extern "C" {
 
+int32_t tts_persistent_allowed(const tts_device_desc* d) {
+  if (!d) return 0;
+  // gfx950 itself, with or without feature suffixes ("gfx950:sramecc+:xnack-")
+  if (std::strncmp(d->arch, "gfx950", 6) != 0 || (d->arch[6] != '\0' && d->arch[6] != ':')) return 0;
+  if (d->compute_units != xtp::NWG || d->xccs != xtp::NX) return 0;
+  int32_t m = 0;
+  if (d->codepred_wg_per_cu >= 1) m |= TTS_PERSISTENT_CODEPRED;
+  if (d->talker_wg_per_cu >= 1) m |= TTS_PERSISTENT_TALKER;
+  return m;
+}
+
 int tts_workspace_bytes(const tts_config* cfg, size_t* bytes) {
   if (!bytes) return TTS_E_ARG;
   std::string e = check_config(cfg);
@@ -999,6 +1043,42 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
   ctx->xtp_ok = xtp_capable(*cfg);
   ctx->xtk_ok = xtk_capable(*cfg);
   ctx->xcp_ok = ctx->xtp_ok && xcp_capable(*cfg);
+  // The persistent kernels need every one of their 256 workgroups resident at once, 32 on each of
+  // the 8 XCDs: gate them on the device (elsewhere the per-op kernels run).
+  {
+    tts_device_desc dd;
+    std::memset(&dd, 0, sizeof dd);
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, ctx->device) != hipSuccess) { delete ctx; return TTS_E_HIP; }
+    std::snprintf(dd.arch, sizeof dd.arch, "%s", prop.gcnArchName);
+    dd.compute_units = prop.multiProcessorCount;
+    int xccs = 0;
+    if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, ctx->device) != hipSuccess) xccs = 0;
+    dd.xccs = xccs;
+    int occ = 0;
+    const void* cpk = ctx->xcp_ok ? reinterpret_cast<const void*>(xcp::k_cp_frame)
+                    : cfg->weight_dtype == TTS_DTYPE_FP8_E4M3 ? reinterpret_cast<const void*>(xtp::k_cp_frame<uint8_t>)
+                                                              : reinterpret_cast<const void*>(xtp::k_cp_frame<uint16_t>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, cpk, xtp::NT, 0) != hipSuccess) occ = 0;
+    dd.codepred_wg_per_cu = occ;
+    occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(xtp::k_talker_step<uint16_t>), xtp::NT,
+                                                     0) != hipSuccess)
+      occ = 0;
+    dd.talker_wg_per_cu = occ;
+    (void)hipGetLastError();
+    ctx->dev_mask = tts_persistent_allowed(&dd);
+    ctx->xtp_ok = ctx->xtp_ok && (ctx->dev_mask & TTS_PERSISTENT_CODEPRED);
+    ctx->xcp_ok = ctx->xcp_ok && ctx->xtp_ok;
+    ctx->xtk_ok = ctx->xtk_ok && (ctx->dev_mask & TTS_PERSISTENT_TALKER);
+  }
+  if (hipHostMalloc((void**)&ctx->errh, sizeof(uint32_t), hipHostMallocDefault) != hipSuccess) { delete ctx; return TTS_E_HIP; }
+  *ctx->errh = 0;
+  if (hipEventCreateWithFlags(&ctx->err_ev, hipEventDisableTiming) != hipSuccess) {
+    (void)hipHostFree(ctx->errh);
+    delete ctx;
+    return TTS_E_HIP;
+  }
   ctx->pgemm_ok = prefill_gemm_capable(*cfg);
   ctx->talker.c = cfg->talker;
   ctx->cp.c = cfg->codepred;
@@ -1281,6 +1361,7 @@ int tts_talker_step_text(tts_ctx* ctx, const int32_t* prev_codes, const int32_t*
   if (!ctx->prefilled) return ctx->fail(TTS_E_STATE, "talker_step: call tts_prefill first");
   if (!prev_codes) return ctx->fail(TTS_E_ARG, "talker_step: prev_codes is NULL");
   if (ctx->pos + 1 > ctx->cfg.max_cache_steps) return ctx->fail(TTS_E_CAPACITY, "talker_step: KV cache full (%d positions)", ctx->pos);
+  if (int rc = device_err_check(ctx)) return rc;
   const int B = ctx->batch;
   TokRef refs[16];
   for (int j = 0; j < 16; ++j) refs[j] = tokref(prev_codes, 16, 0, j, 0);
@@ -1295,6 +1376,7 @@ int tts_talker_step_text(tts_ctx* ctx, const int32_t* prev_codes, const int32_t*
   if (sem_logits)
     HIP_TRY(hipMemcpyAsync(sem_logits, ctx->logits, (size_t)B * ctx->cfg.talker.vocab * 4, hipMemcpyDeviceToDevice, ctx->stream));
   ctx->pos += 1;
+  if (int rc = device_err_probe(ctx)) return rc;
   ctx->err.clear();
   return TTS_OK;
 }
@@ -1306,6 +1388,7 @@ int tts_codepred_frame(tts_ctx* ctx, const int32_t* semantic, const tts_sampling
   if (!semantic || !codes) return ctx->fail(TTS_E_ARG, "codepred_frame: semantic and codes must not be NULL");
   if (int rc = check_sampling(ctx, ac, ctx->cfg.codepred.vocab, "acoustic")) return rc;
   if (ac->do_sample && !u) return ctx->fail(TTS_E_ARG, "codepred_frame: u is NULL with do_sample");
+  if (int rc = device_err_check(ctx)) return rc;
   const int B = ctx->batch;
   URef ur = uref(u ? u : ctx->hT, u ? 15 : 0, 0, 0, 0);
   if (use_xtp(ctx, B, *ac)) {
@@ -1313,6 +1396,7 @@ int tts_codepred_frame(tts_ctx* ctx, const int32_t* semantic, const tts_sampling
   } else if (int rc = codepred_frame(ctx, B, tokref(semantic, 1, 0, 0, 0), *ac, ur, forced, codes, 15, 0, 0, 0, logits)) {
     return rc;
   }
+  if (int rc = device_err_probe(ctx)) return rc;
   ctx->err.clear();
   return TTS_OK;
 }
@@ -1345,6 +1429,7 @@ int tts_run_frames(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_s
   if (ctx->pos + n > ctx->cfg.max_cache_steps)
     return ctx->fail(TTS_E_CAPACITY, "run_frames: %d + %d positions exceed max_cache_steps %d", ctx->pos, n, ctx->cfg.max_cache_steps);
   if (n == 0) return TTS_OK;
+  if (int rc = device_err_check(ctx)) return rc;
   GraphKey key{*sem, *ac, u, codes, ctx->batch};
   if (!ctx->have_graph || !(ctx->gkey == key)) {
     drop_graph(ctx);
@@ -1369,6 +1454,7 @@ int tts_run_frames(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_s
   for (int i = 0; i < n; ++i) HIP_TRY(hipGraphLaunch(ctx->gexec, ctx->stream));
   ctx->frames += n;
   ctx->pos += n;
+  if (int rc = device_err_probe(ctx)) return rc;
   ctx->err.clear();
   return TTS_OK;
 }
@@ -1396,6 +1482,9 @@ int tts_reset(tts_ctx* ctx) {
   if (ctx->text_ids) drop_graph(ctx);
   ctx->text_ids = nullptr;
   ctx->text_n = ctx->text_next = 0;
+  // the error word is cleared above (it is part of the exchange state); the pending host copy is
+  // of the old word
+  ctx->err_pending = false;
   ctx->err.clear();
   return TTS_OK;
 }
@@ -1460,6 +1549,8 @@ void tts_destroy(tts_ctx* ctx) {
   if (!ctx) return;
   drop_graph(ctx);
   if (ctx->cap_stream) (void)hipStreamDestroy(ctx->cap_stream);
+  if (ctx->err_ev) (void)hipEventDestroy(ctx->err_ev);
+  if (ctx->errh) (void)hipHostFree(ctx->errh);
   delete ctx;
 }
 

@@ -33,8 +33,10 @@ struct GemmArgs {
   int M, N, K;
   int add;            // 1: C += result (residual), 0: C = result
   int kslice;         // K columns per workgroup (blockIdx.z selects the slice); kslice < K: every
-                      // workgroup adds its partial into C with float atomics, C holding the
-                      // residual (add = 1) or zeros
+                      // workgroup writes its partial tile to part (slice z at part + z M N, row
+                      // stride N) and k_splitk_reduce adds the slices into C in slice order, so the
+                      // sum is the same on every run
+  float* part;
 };
 
 constexpr int kGBM = 64, kGBN = 64, kGBK = 64, kGLD = kGBK + 8;  // tile, LDS row stride (bf16)
@@ -164,46 +166,44 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
         if (m < a.M) {
           float* c = a.C + (size_t)m * a.ldc + n;
           const float v = Q8 ? acc[i][j][r] * csc[j] : acc[i][j][r];
-          if (split) atomicAdd(c, v);
+          if (split) a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = v;
           else *c = a.add ? *c + v : v;
         }
       }
 }
 
-// rs[m] = 1 / sqrt(mean(x[m]^2) + eps) over K; one wave per row (blocks past the rows have no
-// scale to compute). With zc, the grid also clears rows 0 .. M-1 of zc[.., 0 .. zn) (the output a
-// split-K GEMM adds its slices into), whatever block and thread count it has.
-__global__ __launch_bounds__(256) void k_rowscale(const float* x, int ldx, int M, int K, float eps, float* rs,
-                                                  float* zc = nullptr, int zld = 0, int zn = 0) {
+// C[m][n] = (add ? C[m][n] : 0) + part[0][m][n] + part[1][m][n] + ... + part[ks - 1][m][n], the
+// slices added in that order (N a multiple of 4; four columns per thread).
+__global__ __launch_bounds__(256) void k_splitk_reduce(float* C, int ldc, const float* part, int M, int N, int ks, int add) {
+  const int q4 = N / 4;
+  const size_t n = (size_t)M * q4;
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < n; q += (size_t)gridDim.x * blockDim.x) {
+    const size_t m = q / q4, c = 4 * (q % q4);
+    float4 v = add ? *reinterpret_cast<const float4*>(C + m * ldc + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z = 0; z < ks; ++z) {
+      const float4 p = *reinterpret_cast<const float4*>(part + ((size_t)z * M + m) * N + c);
+      v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+    }
+    *reinterpret_cast<float4*>(C + m * ldc + c) = v;
+  }
+}
+
+// rs[m] = 1 / sqrt(mean(x[m]^2) + eps) over K; one wave per row.
+__global__ __launch_bounds__(256) void k_rowscale(const float* x, int ldx, int M, int K, float eps, float* rs) {
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (m < M) {
-    const float* row = x + (size_t)m * ldx;
-    float s = 0.f;
-    if ((K & 3) == 0 && (ldx & 3) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
-      for (int k = 4 * lane; k < K; k += 256) {
-        const float4 v = *reinterpret_cast<const float4*>(row + k);
-        s += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
-      }
-    } else {
-      for (int k = lane; k < K; k += 64) s += row[k] * row[k];
+  if (m >= M) return;
+  const float* row = x + (size_t)m * ldx;
+  float s = 0.f;
+  if ((K & 3) == 0 && (ldx & 3) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0) {
+    for (int k = 4 * lane; k < K; k += 256) {
+      const float4 v = *reinterpret_cast<const float4*>(row + k);
+      s += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
     }
-    s = wave_sum(s);
-    if (lane == 0) rs[m] = 1.0f / sqrtf(s / (float)K + eps);
+  } else {
+    for (int k = lane; k < K; k += 64) s += row[k] * row[k];
   }
-  // the output rows to clear, spread over every block of the grid in 16-byte stores
-  if (zc) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    if ((zn & 3) == 0 && (zld & 3) == 0 && (reinterpret_cast<uintptr_t>(zc) & 15) == 0) {
-      const int q4 = zn / 4;
-      for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < (size_t)M * q4; q += stride) {
-        const size_t r = q / q4, c = q % q4;
-        *reinterpret_cast<float4*>(zc + r * zld + 4 * c) = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    } else {
-      for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < (size_t)M * zn; q += stride)
-        zc[(q / zn) * zld + q % zn] = 0.f;
-    }
-  }
+  s = wave_sum(s);
+  if (lane == 0) rs[m] = 1.0f / sqrtf(s / (float)K + eps);
 }
 
 // out[m] = x[m] * rs[m] * gain (the normalised rows a GEMM with a row scale consumed), one
@@ -213,11 +213,6 @@ __global__ void k_norm_rows(const float* x, int ldx, const float* rs, const void
   const int m = blockIdx.x;
   const WT* g = reinterpret_cast<const WT*>(gain);
   for (int k = threadIdx.x; k < K; k += blockDim.x) out[(size_t)m * ldo + k] = x[(size_t)m * ldx + k] * rs[m] * to_f32(g[k]);
-}
-
-// rows[m][0 .. n) = 0 (a split-K GEMM's output before its slices add into it); one block per row.
-__global__ void k_zero_rows(float* rows, int ld, int n) {
-  for (int k = threadIdx.x; k < n; k += blockDim.x) rows[(size_t)blockIdx.x * ld + k] = 0.f;
 }
 
 // The device counters' advance that a GEMV epilogue does when a GEMM replaces it.

@@ -26,14 +26,16 @@ TTS_E_CAPACITY = -3
 TTS_E_STATE = -4
 TTS_E_HIP = -5
 TTS_E_UNSUPPORTED = -6
+TTS_E_DEVICE = -7
 STATUS_NAMES = {0: "TTS_OK", -1: "TTS_E_ARG", -2: "TTS_E_SHAPE", -3: "TTS_E_CAPACITY", -4: "TTS_E_STATE",
-                -5: "TTS_E_HIP", -6: "TTS_E_UNSUPPORTED"}
+                -5: "TTS_E_HIP", -6: "TTS_E_UNSUPPORTED", -7: "TTS_E_DEVICE"}
 DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
 _WEIGHT_DTYPE = {"fp32": DTYPE_F32, "bf16": DTYPE_BF16, "fp8": DTYPE_FP8_E4M3}
 
 EXPORTED = ["tts_workspace_bytes", "tts_create", "tts_load_weights", "tts_prefill", "tts_talker_step",
             "tts_talker_step_text", "tts_set_text_stream", "tts_prefill_ragged", "tts_set_stop", "tts_codepred_frame", "tts_sample", "tts_run_frames", "tts_set_exec_mode", "tts_get_exec_mode", "tts_set_prefill_mode", "tts_get_prefill_mode",
-            "tts_device_status", "tts_get_progress", "tts_reset", "tts_last_error", "tts_destroy"]
+            "tts_device_status", "tts_persistent_allowed", "tts_get_progress", "tts_reset", "tts_last_error",
+            "tts_destroy"]
 EXEC_KERNELS, EXEC_PERSISTENT = 0, 1
 PERSISTENT_CODEPRED, PERSISTENT_TALKER = 1, 2  # bits of exec_mode()[1]
 PREFILL_STEPS, PREFILL_GEMM = 0, 1
@@ -49,6 +51,11 @@ class ConfigC(ctypes.Structure):
                 ("n_acoustic", ctypes.c_int32), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
                 ("weight_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32), ("max_batch", ctypes.c_int32),
                 ("max_cache_steps", ctypes.c_int32), ("max_frames", ctypes.c_int32)]
+
+
+class DeviceDescC(ctypes.Structure):
+    _fields_ = [("arch", ctypes.c_char * 64), ("compute_units", ctypes.c_int32), ("xccs", ctypes.c_int32),
+                ("codepred_wg_per_cu", ctypes.c_int32), ("talker_wg_per_cu", ctypes.c_int32)]
 
 
 class SamplingC(ctypes.Structure):
@@ -94,6 +101,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tts_get_prefill_mode.argtypes = [P, ctypes.POINTER(I32)]
     lib.tts_get_exec_mode.argtypes = [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     lib.tts_device_status.argtypes = [P, ctypes.POINTER(I32)]
+    lib.tts_persistent_allowed.argtypes = [ctypes.POINTER(DeviceDescC)]
     lib.tts_reset.argtypes = [P]
     lib.tts_last_error.argtypes = [P]
     lib.tts_last_error.restype = ctypes.c_char_p
@@ -104,6 +112,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def persistent_allowed(arch: str, compute_units: int, xccs: int, codepred_wg_per_cu: int, talker_wg_per_cu: int) -> int:
+    """tts_persistent_allowed on a device description: the PERSISTENT_* bits of the kernels allowed."""
+    d = DeviceDescC(arch.encode(), compute_units, xccs, codepred_wg_per_cu, talker_wg_per_cu)
+    return int(load_library().tts_persistent_allowed(ctypes.byref(d)))
 
 
 def config_struct(model: ModelCfg, max_batch: int, max_cache_steps: int, max_frames: int,

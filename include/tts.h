@@ -50,7 +50,10 @@ enum tts_status {
   TTS_E_CAPACITY = -3,   /* KV positions or frames would exceed the configured capacity */
   TTS_E_STATE = -4,      /* call out of order (e.g. a step before weights or prefill) */
   TTS_E_HIP = -5,        /* a HIP runtime call failed; tts_last_error has its text */
-  TTS_E_UNSUPPORTED = -6 /* valid request outside what this build implements */
+  TTS_E_UNSUPPORTED = -6, /* valid request outside what this build implements */
+  TTS_E_DEVICE = -7      /* a persistent kernel launched by an earlier call timed out in an exchange:
+                            outputs since the last clean call are invalid; nothing was enqueued;
+                            reported by every call that may launch them until tts_reset */
 };
 
 /* TTS_DTYPE_FP8_E4M3 (weight_dtype only): weight-only 8-bit quantisation
@@ -78,7 +81,8 @@ typedef struct {
   float rms_eps;           /* RMSNorm epsilon */
   float rope_theta;        /* RoPE base */
   int32_t weight_dtype;    /* enum tts_dtype of the weights (FP8: matrices only, see above) */
-  int32_t kv_dtype;        /* enum tts_dtype of the KV caches (fp32 keeps k/v unrounded) */
+  int32_t kv_dtype;        /* must be TTS_DTYPE_F32: the KV caches hold k/v unrounded (a bf16 cache
+                              alone puts the 1.7B-class acoustic logits over the 1e-2 parity bar) */
   int32_t max_batch;       /* streams per context */
   int32_t max_cache_steps; /* Talker KV capacity in positions (prefill + frames) */
   int32_t max_frames;      /* frame capacity of the u / codes arrays of tts_run_frames */
@@ -107,7 +111,10 @@ int tts_workspace_bytes(const tts_config* cfg, size_t* bytes);
  * tts_workspace_bytes, 256-byte aligned, borrowed until tts_destroy. */
 int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t workspace_bytes, tts_ctx** out);
 
-/* Bind weights. n tensors named by the canonical names (talker.embed_text,
+/* Bind weights ("qwen3-tts-hip" README, section "Library Usage": an engine is
+ * loaded once from a model directory and then serves requests; section "Module
+ * Layout": the Talker and CodePredictor decoder stacks, their weights and
+ * config). n tensors named by the canonical names (talker.embed_text,
  * talker.embed_sem, talker.layers.<i>.{attn_norm,wq,wk,wv,q_norm,k_norm,wo,
  * mlp_norm,wg,wu,wd}, talker.final_norm, talker.lm_head, cp.proj (only when
  * the widths differ), cp.embed_ac [15,Va,Ht], cp.layers.<i>.{...},
@@ -116,13 +123,17 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
  * tensor must be present with the exact shape, the config's dtype and
  * 16-byte alignment; FP8 configs add one "<matrix>.scale" per matrix (fp32)
  * and give gains and embeddings as bf16. Pointers are borrowed until
- * tts_destroy. FP8 configs decode with the per-op kernels only (the
- * persistent step kernels and the MFMA GEMM routes need bf16 weights). */
+ * tts_destroy. FP8 configs run the persistent CodePredictor frame kernel, the
+ * MFMA GEMM routes and the per-op kernels; the persistent Talker step kernel
+ * needs bf16 weights (FP8 Talker steps use the per-op kernels). */
 int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* const* dev_ptrs,
                      const int64_t* shapes, const int32_t* ranks, const int32_t* dtypes);
 
-/* Reset the streams and run the Talker over text ids [B, n] (positions
- * 0..n-1). Leaves frame 0's Talker output pending (semantic logits and the
+/* The prompt pass ("Running Qwen3-TTS on an AMD R9700", section "Running
+ * Qwen3-TTS": the Talker reads the text conditioning before the frame loop;
+ * "qwen3-tts-hip" README, section "Library Usage": a request's text, or its
+ * first text_lookahead_tokens ids in streaming mode). Reset the streams and run
+ * the Talker over text ids [B, n] (positions 0..n-1). Leaves frame 0's Talker output pending (semantic logits and the
  * final-normed hidden that conditions the CodePredictor). sem_logits
  * [B, Vs] receives those logits when non-NULL. */
 int tts_prefill(tts_ctx* ctx, const int32_t* ids, int32_t batch, int32_t n, float* sem_logits);
@@ -154,8 +165,11 @@ int tts_prefill_ragged(tts_ctx* ctx, const int32_t* ids, const int32_t* lengths,
  * drops the captured frame graph. */
 int tts_set_stop(tts_ctx* ctx, int32_t eos_id, int32_t* stop_frames);
 
-/* One Talker step fed with the previous frame's codes [B, 16]: the input is
- * E_sem[c0] + sum_j E_ac[j][cj]. Advances the Talker position by one and
+/* One Talker step ("Running Qwen3-TTS on an AMD R9700", section "Running
+ * Qwen3-TTS": per frame the Talker generates the first, semantic codebook
+ * token; "qwen3-tts-hip" README, section "Python Parity Fixtures": the
+ * embedding sum is a checked stage) fed with the previous frame's codes
+ * [B, 16]: the input is E_sem[c0] + sum_j E_ac[j][cj]. Advances the Talker position by one and
  * replaces the pending output; sem_logits [B, Vs] receives it when non-NULL. */
 int tts_talker_step(tts_ctx* ctx, const int32_t* prev_codes, float* sem_logits);
 
@@ -168,7 +182,11 @@ int tts_talker_step(tts_ctx* ctx, const int32_t* prev_codes, float* sem_logits);
  * clamped to its last row. Same errors as tts_talker_step. */
 int tts_talker_step_text(tts_ctx* ctx, const int32_t* prev_codes, const int32_t* text_ids, float* sem_logits);
 
-/* The 15 CodePredictor steps of one frame, conditioned on the pending Talker
+/* The 15 CodePredictor steps of one frame ("Running Qwen3-TTS on an AMD
+ * R9700", section "Running Qwen3-TTS": the smaller transformer fills in the
+ * remaining 15 acoustic tokens of the frame, one after the other, and the
+ * per-frame cost counts it 15 times; "qwen3-tts-hip" README, section "Library
+ * Usage": the subtalker sampling controls), conditioned on the pending Talker
  * hidden and on semantic [B]. ac: acoustic sampling; u [B, 15] uniforms
  * (ignored when greedy; may be NULL then). forced [B, 15] or NULL: when given,
  * forced[b][j-1] replaces the drawn a_j as the input of step j+1 (teacher
@@ -177,10 +195,13 @@ int tts_talker_step_text(tts_ctx* ctx, const int32_t* prev_codes, const int32_t*
 int tts_codepred_frame(tts_ctx* ctx, const int32_t* semantic, const tts_sampling* ac, const float* u,
                        const int32_t* forced, int32_t* codes, float* logits);
 
-/* Standalone sampler over logits [B, V] with uniforms u [B] (may be NULL when
- * greedy). history [B, V] (uint8, 0/1) or NULL: when given and the penalty is
- * not 1 it selects the penalised ids, and the drawn id is marked in it.
- * out [B] receives the ids. V <= 65536. */
+/* Standalone sampler ("qwen3-tts-hip" README, section "Library Usage":
+ * do_sample, top_k, top_p, temperature and repetition_penalty for the semantic
+ * token, the subtalker_* set for the acoustic tokens) over logits [B, V] with
+ * uniforms u [B] (may be NULL when greedy). history [B, V] (uint8, 0/1) or
+ * NULL: when given and the penalty is not 1 it selects the penalised ids, and
+ * the drawn id is marked in it. out [B] receives the ids. Greedy: V <= 65536;
+ * sampled: V <= 4096 (TTS_E_UNSUPPORTED above). */
 int tts_sample(tts_ctx* ctx, const float* logits, int32_t batch, int32_t vocab, const tts_sampling* s,
                const float* u, uint8_t* history, int32_t* out);
 
@@ -209,11 +230,12 @@ int tts_set_text_stream(tts_ctx* ctx, const int32_t* text_ids, int32_t n_text, i
  *  TTS_EXEC_PERSISTENT (default where supported): persistent kernels, whose
  *    workgroups split each layer across the 8 XCDs tensor-parallel and
  *    exchange tagged values instead of ending kernels. One runs all 15
- *    CodePredictor steps of a frame (batch 1, greedy acoustic tokens, bf16
- *    weights, a CodePredictor with 8 KV heads of dimension 128); one runs a
- *    whole Talker step (batch 1, bf16 weights, fp32 KV cache, 8 KV heads of
- *    dimension 128 with 2 query heads each). Other calls use the per-op
- *    kernels. Prefill always uses the per-op kernels.
+ *    CodePredictor steps of a frame (batch 1, greedy acoustic tokens, bf16 or
+ *    E4M3 weights, a CodePredictor with 8 KV heads of dimension 128); one runs
+ *    a whole Talker step (batch 1, bf16 weights, 8 KV heads of dimension 128
+ *    with 2 query heads each). Both need a device that keeps all their 256
+ *    workgroups resident at once (tts_persistent_allowed). Other calls use the
+ *    per-op kernels. The prompt pass never uses them (see tts_set_prefill_mode).
  *  TTS_EXEC_KERNELS: one kernel per op.
  * Switching drops the captured frame graph. TTS_E_UNSUPPORTED if neither
  * persistent kernel handles the config. tts_get_exec_mode reports the mode
@@ -241,8 +263,29 @@ int tts_get_prefill_mode(const tts_ctx* ctx, int32_t* mode);
 /* Synchronise the context's stream and report the persistent kernel's
  * exchange status: *status = 0 when every exchange completed, nonzero when a
  * workgroup timed out waiting (e.g. not all workgroups were resident); the
- * affected outputs are then invalid. */
+ * affected outputs are then invalid. Without this call the same state is
+ * reported, one call late and without blocking, as TTS_E_DEVICE by the next
+ * call that may launch a persistent kernel. */
 int tts_device_status(tts_ctx* ctx, int32_t* status);
+
+/* What the persistent kernels need from a device: gfx950 with 256 compute
+ * units on 8 XCDs (each kernel deals its 256 workgroups to the XCDs round
+ * robin, 32 to an XCD, and exchanges values through that XCD's L2), and room
+ * for at least one of its workgroups (512 threads and its LDS) on a CU.
+ * tts_create fills this from the current device and runs the persistent kernels
+ * only where tts_persistent_allowed returns their bit; elsewhere the per-op
+ * kernels run. arch: the device's gcnArchName ("gfx950:sramecc+:xnack-").
+ * codepred_wg_per_cu / talker_wg_per_cu: resident workgroups per CU of the
+ * CodePredictor and Talker kernels (hipOccupancyMaxActiveBlocksPerMultiprocessor).
+ * Returns TTS_PERSISTENT_CODEPRED | TTS_PERSISTENT_TALKER bits; 0 for NULL. */
+typedef struct {
+  char arch[64];
+  int32_t compute_units;
+  int32_t xccs;
+  int32_t codepred_wg_per_cu;
+  int32_t talker_wg_per_cu;
+} tts_device_desc;
+int32_t tts_persistent_allowed(const tts_device_desc* d);
 
 /* Host-side counters: Talker positions written so far and frames generated
  * since the last prefill. Either pointer may be NULL. */

@@ -128,3 +128,35 @@ def test_measured_traffic_record_follows_the_kernel_sources(tmp_path, monkeypatc
     assert roofline.measured_traffic("ok.md") == 12345
     (tmp_path / "stale.md").write_text("    kernel_source_sha256: " + "0" * 64 + "\n    traffic_bytes_per_launch: 12345\n")
     assert roofline.measured_traffic("stale.md") is None
+
+
+@pytest.mark.parametrize("arch,cus,xccs,cp,tk,want", [
+    ("gfx950:sramecc+:xnack-", 256, 8, 1, 1, tts.PERSISTENT_CODEPRED | tts.PERSISTENT_TALKER),
+    ("gfx950", 256, 8, 1, 0, tts.PERSISTENT_CODEPRED),
+    ("gfx950", 256, 8, 0, 2, tts.PERSISTENT_TALKER),
+    ("gfx950", 256, 8, 0, 0, 0),
+    ("gfx950:sramecc+", 128, 4, 1, 1, 0),      # a partition of the device: fewer CUs and XCDs
+    ("gfx950", 256, 1, 1, 1, 0),               # one XCD reported
+    ("gfx950", 304, 8, 1, 1, 0),               # another CU count
+    ("gfx942:sramecc+:xnack-", 256, 8, 1, 1, 0),
+    ("gfx9500", 256, 8, 1, 1, 0),
+    ("", 256, 8, 1, 1, 0),
+])
+def test_persistent_kernels_are_gated_on_the_device(arch, cus, xccs, cp, tk, want):
+    """The persistent kernels run only where all 256 of their workgroups can be resident at once,
+    32 on each of 8 XCDs of a gfx950, with room for one of their workgroups per CU."""
+    assert tts.persistent_allowed(arch, cus, xccs, cp, tk) == want
+
+
+def test_persistent_gate_rejects_null():
+    assert tts.load_library().tts_persistent_allowed(None) == 0
+
+
+def test_bf16_kv_cache_is_refused():
+    """The KV caches stay fp32 (a bf16 cache alone puts the 1.7B acoustic logits over the 1e-2 bar)."""
+    lib = tts.load_library()
+    n = ctypes.c_size_t(0)
+    c = _cfg(kv_dtype=tts.DTYPE_BF16)
+    assert lib.tts_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == tts.TTS_E_SHAPE
+    c = _cfg(kv_dtype=tts.DTYPE_F32)
+    assert lib.tts_workspace_bytes(ctypes.byref(c), ctypes.byref(n)) == tts.TTS_OK

@@ -21,6 +21,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -74,7 +75,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout, computed identically by tts_workspace_bytes and tts_create.
 struct Layout {
   size_t st, tk, tv, ck, cv, tcos, tsin, ccos, csin, x, qkv, attn, h, part, counters, logits, hT, cx, clog, next_tok,
-      sem_tok, ac_codes, history, kvstart, aids, cpdesc, tkdesc, px, pqkv, pq, po, pgu, ph, ps, pks, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
+      sem_tok, ac_codes, history, kvstart, aids, cpdesc, tkdesc, cpdesc_s, tkdesc_s, px, pqkv, pq, po, pgu, ph, ps, pks, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
   int nsplit;
 };
 
@@ -140,6 +141,10 @@ Layout make_layout(const tts_config& c) {
   // persistent kernels: descriptors and exchange buffers (the CodePredictor's K/V rows stay in LDS)
   L.cpdesc = take(sizeof(xtp::CpDesc));
   L.tkdesc = take(sizeof(xtp::TkDesc));
+  // the same descriptors with the exchange buffers in the device's static scratch array
+  // (tts_run_frames_noalloc)
+  L.cpdesc_s = take(sizeof(xtp::CpDesc));
+  L.tkdesc_s = take(sizeof(xtp::TkDesc));
   L.xzero_begin = off;
   L.xin = take((size_t)xtp::NX * xtp::RING * xtp::ISZ * 8);
   L.xcr = take((size_t)xtp::NWG * 2 * xtp::CSZ * 8);
@@ -305,6 +310,10 @@ struct tts_ctx {
   bool xtp_ok = false;   // config supported
   int exec_mode = TTS_EXEC_PERSISTENT;  // persistent CodePredictor when supported (batch 1, greedy)
   xtp::CpDesc* cpdesc = nullptr;
+  xtp::CpDesc* cpdesc_s = nullptr;  // exchange buffers in the static scratch array
+  xtp::TkDesc* tkdesc_s = nullptr;
+  char* scratch = nullptr;          // this device's static scratch array (device address)
+  bool use_scratch = false;         // persistent launches take the *_s descriptors
   bool xtk_ok = false;   // persistent Talker step supported
   bool xcp_ok = false;   // the lean CodePredictor kernel supports the config (bf16)
   int32_t dev_mask = 0;  // persistent kernels the device allows (tts_persistent_allowed)
@@ -355,6 +364,41 @@ struct tts_ctx {
     hipError_t e_ = hipGetLastError();                                                              \
     if (e_ != hipSuccess) return ctx->fail(TTS_E_HIP, "kernel launch: %s", hipGetErrorString(e_)); \
   } while (0)
+
+// Static scratch of tts_run_frames_noalloc: the persistent kernels' exchange buffers (intra-XCD
+// rings, cross-XCD slots, argmax candidates, the Talker's attention partials) for callers that
+// cannot allocate. Each GPU the library runs on holds one copy for the life of the process; every
+// call on that GPU shares it.
+constexpr size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+struct ScratchLayout {
+  static constexpr size_t xin = 0;
+  static constexpr size_t xcr = align256(xin + (size_t)xtp::NX * xtp::RING * xtp::ISZ * 8);
+  static constexpr size_t cand = align256(xcr + (size_t)xtp::NWG * 2 * xtp::CSZ * 8);
+  static constexpr size_t att = align256(cand + (size_t)2 * xtp::NWG * xtp::CAND * 8);
+  static constexpr size_t total = align256(att + (size_t)xtp::NX * 2 * xtp::NR * xtp::ATS * 8);
+};
+constexpr size_t kScratchBytes = ScratchLayout::total;  // 2.1 MiB
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The device address of this device's scratch array, looked up once per device (the array's
+// name is a host-side stand-in in host code, not a device address). Call with the device current.
+char* scratch_device_ptr(int device, hipError_t* err) {
+  static std::mutex mu;
+  static std::vector<char*> table;
+  std::lock_guard<std::mutex> lock(mu);
+  if (device < 0) return nullptr;
+  if ((int)table.size() <= device) table.resize(device + 1, nullptr);
+  if (!table[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *err = e;
+      return nullptr;
+    }
+    table[device] = (char*)p;
+  }
+  return table[device];
+}
 
 namespace {
 
@@ -838,7 +882,7 @@ bool use_xtp(tts_ctx* ctx, int B, const tts_sampling& ac) { return ctx->xtp_ok &
 int codepred_frame_xtp(tts_ctx* ctx, const int32_t* semantic, const int32_t* forced, int32_t* codes, int f_stride, int use_frame,
                        float* logits_out) {
   xtp::CpCall call;
-  call.desc = ctx->cpdesc;
+  call.desc = ctx->use_scratch ? ctx->cpdesc_s : ctx->cpdesc;
   call.semantic = semantic;
   call.forced = forced;
   call.codes = codes;
@@ -859,7 +903,7 @@ bool use_xtk(tts_ctx* ctx, int B) { return ctx->xtk_ok && ctx->exec_mode == TTS_
 
 int talker_step_xtk(tts_ctx* ctx, int bump_pos, int bump_frame) {
   xtp::TkCall call;
-  call.desc = ctx->tkdesc;
+  call.desc = ctx->use_scratch ? ctx->tkdesc_s : ctx->tkdesc;
   call.bump_pos = bump_pos;
   call.bump_frame = bump_frame;
   hipLaunchKernelGGL(xtp::k_talker_step<uint16_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
@@ -1039,6 +1083,14 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
   ctx->aids = (int32_t*)(w + L.aids);
   ctx->cpdesc = (xtp::CpDesc*)(w + L.cpdesc);
   ctx->tkdesc = (xtp::TkDesc*)(w + L.tkdesc);
+  ctx->cpdesc_s = (xtp::CpDesc*)(w + L.cpdesc_s);
+  ctx->tkdesc_s = (xtp::TkDesc*)(w + L.tkdesc_s);
+  // this device's static scratch array (tts_run_frames_noalloc), looked up once per device here
+  {
+    hipError_t se = hipSuccess;
+    ctx->scratch = scratch_device_ptr(ctx->device, &se);
+    if (!ctx->scratch) { delete ctx; return TTS_E_HIP; }
+  }
   ctx->xerr = (uint32_t*)(w + L.xerr);
   ctx->xtp_ok = xtp_capable(*cfg);
   ctx->xtk_ok = xtk_capable(*cfg);
@@ -1225,6 +1277,10 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
     D.cand = (xtp::u64*)(ctx->ws + ctx->L.cand);
     D.st = ctx->st; D.err = ctx->xerr;
     HIP_TRY(hipMemcpyAsync(ctx->cpdesc, &D, sizeof D, hipMemcpyHostToDevice, ctx->stream));
+    ScratchLayout SL;
+    D.xin = (xtp::u64*)(ctx->scratch + SL.xin); D.xcr = (xtp::u64*)(ctx->scratch + SL.xcr);
+    D.cand = (xtp::u64*)(ctx->scratch + SL.cand);
+    HIP_TRY(hipMemcpyAsync(ctx->cpdesc_s, &D, sizeof D, hipMemcpyHostToDevice, ctx->stream));
     HIP_TRY(hipStreamSynchronize(ctx->stream));
   }
   if (ctx->xtk_ok) {
@@ -1246,6 +1302,10 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
     D.att = (xtp::u64*)(ctx->ws + ctx->L.att);
     D.st = ctx->st; D.err = ctx->xerr;
     HIP_TRY(hipMemcpyAsync(ctx->tkdesc, &D, sizeof D, hipMemcpyHostToDevice, ctx->stream));
+    ScratchLayout SL;
+    D.xin = (xtp::u64*)(ctx->scratch + SL.xin); D.xcr = (xtp::u64*)(ctx->scratch + SL.xcr);
+    D.att = (xtp::u64*)(ctx->scratch + SL.att);
+    HIP_TRY(hipMemcpyAsync(ctx->tkdesc_s, &D, sizeof D, hipMemcpyHostToDevice, ctx->stream));
     HIP_TRY(hipStreamSynchronize(ctx->stream));
   }
   ctx->err.clear();
@@ -1452,6 +1512,52 @@ int tts_run_frames(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_s
     ctx->gkey = key;
   }
   for (int i = 0; i < n; ++i) HIP_TRY(hipGraphLaunch(ctx->gexec, ctx->stream));
+  ctx->frames += n;
+  ctx->pos += n;
+  if (int rc = device_err_probe(ctx)) return rc;
+  ctx->err.clear();
+  return TTS_OK;
+}
+
+int tts_run_frames_noalloc(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_sampling* ac, const float* u,
+                           int32_t* codes) {
+  if (!ctx) return TTS_E_ARG;
+  if (!ctx->prefilled) return ctx->fail(TTS_E_STATE, "run_frames_noalloc: call tts_prefill first");
+  if (n < 0) return ctx->fail(TTS_E_ARG, "run_frames_noalloc: n must be >= 0");
+  if (!codes) return ctx->fail(TTS_E_ARG, "run_frames_noalloc: codes is NULL");
+  if (int rc = check_sampling(ctx, sem, ctx->cfg.talker.vocab, "semantic")) return rc;
+  if (int rc = check_sampling(ctx, ac, ctx->cfg.codepred.vocab, "acoustic")) return rc;
+  if ((sem->do_sample || ac->do_sample) && !u) return ctx->fail(TTS_E_ARG, "run_frames_noalloc: u is NULL with sampling");
+  if (ctx->frames + n > ctx->cfg.max_frames)
+    return ctx->fail(TTS_E_CAPACITY, "run_frames_noalloc: %d + %d frames exceed max_frames %d", ctx->frames, n, ctx->cfg.max_frames);
+  if (ctx->pos + n > ctx->cfg.max_cache_steps)
+    return ctx->fail(TTS_E_CAPACITY, "run_frames_noalloc: %d + %d positions exceed max_cache_steps %d", ctx->pos, n,
+                     ctx->cfg.max_cache_steps);
+  const int B = ctx->batch;
+  if (!use_xtp(ctx, B, *ac) || !use_xtk(ctx, B))
+    return ctx->fail(TTS_E_UNSUPPORTED,
+                     "run_frames_noalloc: runs both persistent kernels only (batch 1, greedy acoustic tokens, bf16 weights, "
+                     "persistent exec mode)");
+  // the exchange buffers this call needs, against the array's fixed size
+  if (ScratchLayout::total > kScratchBytes)
+    return ctx->fail(TTS_E_CAPACITY, "run_frames_noalloc: %zu bytes of exchange buffers exceed the %zu-byte scratch array",
+                     (size_t)ScratchLayout::total, kScratchBytes);
+  if (n == 0) return TTS_OK;
+  if (int rc = device_err_check(ctx)) return rc;
+  // The array keeps the last call's values, possibly another context's, whose exchange tags may be
+  // the ones this context expects next: clear it first (a fill kernel, so a caller's graph capture
+  // holds no memset node).
+  hipLaunchKernelGGL(k_fill_u8, dim3(256), dim3(256), 0, ctx->stream, (uint8_t*)ctx->scratch, kScratchBytes, (uint8_t)0);
+  HIP_LAUNCH_CHECK();
+  // the frames launched one by one (no graph to instantiate)
+  ctx->use_scratch = true;
+  for (int i = 0; i < n; ++i) {
+    if (int rc = enqueue_frame(ctx, *sem, *ac, u, codes)) {
+      ctx->use_scratch = false;
+      return rc;
+    }
+  }
+  ctx->use_scratch = false;
   ctx->frames += n;
   ctx->pos += n;
   if (int rc = device_err_probe(ctx)) return rc;

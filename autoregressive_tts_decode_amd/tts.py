@@ -33,7 +33,7 @@ DTYPE_F32, DTYPE_BF16, DTYPE_FP8_E4M3 = 0, 1, 2
 _WEIGHT_DTYPE = {"fp32": DTYPE_F32, "bf16": DTYPE_BF16, "fp8": DTYPE_FP8_E4M3}
 
 EXPORTED = ["tts_workspace_bytes", "tts_create", "tts_load_weights", "tts_prefill", "tts_talker_step",
-            "tts_talker_step_text", "tts_set_text_stream", "tts_prefill_ragged", "tts_set_stop", "tts_codepred_frame", "tts_sample", "tts_run_frames", "tts_set_exec_mode", "tts_get_exec_mode", "tts_set_prefill_mode", "tts_get_prefill_mode",
+            "tts_talker_step_text", "tts_set_text_stream", "tts_prefill_ragged", "tts_set_stop", "tts_codepred_frame", "tts_sample", "tts_run_frames", "tts_run_frames_noalloc", "tts_set_exec_mode", "tts_get_exec_mode", "tts_set_prefill_mode", "tts_get_prefill_mode",
             "tts_device_status", "tts_persistent_allowed", "tts_get_progress", "tts_reset", "tts_last_error",
             "tts_destroy"]
 EXEC_KERNELS, EXEC_PERSISTENT = 0, 1
@@ -95,6 +95,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tts_codepred_frame.argtypes = [P, P, ctypes.POINTER(SamplingC), P, P, P, P]
     lib.tts_sample.argtypes = [P, P, I32, I32, ctypes.POINTER(SamplingC), P, P, P]
     lib.tts_run_frames.argtypes = [P, I32, ctypes.POINTER(SamplingC), ctypes.POINTER(SamplingC), P, P]
+    lib.tts_run_frames_noalloc.argtypes = [P, I32, ctypes.POINTER(SamplingC), ctypes.POINTER(SamplingC), P, P]
     lib.tts_get_progress.argtypes = [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]
     lib.tts_set_exec_mode.argtypes = [P, I32]
     lib.tts_set_prefill_mode.argtypes = [P, I32]
@@ -267,6 +268,11 @@ class TTSDecoder:
         s1, s2 = sampling_struct(sem), sampling_struct(ac)
         self._check(self.lib.tts_run_frames(self.ctx, n, ctypes.byref(s1), ctypes.byref(s2), _ptr(u), _ptr(codes)),
                     "tts_run_frames")
+
+    def run_frames_noalloc(self, n, sem, ac, u, codes):
+        s1, s2 = sampling_struct(sem), sampling_struct(ac)
+        self._check(self.lib.tts_run_frames_noalloc(self.ctx, n, ctypes.byref(s1), ctypes.byref(s2), _ptr(u), _ptr(codes)),
+                    "tts_run_frames_noalloc")
 
     def progress(self) -> tuple[int, int]:
         p, f = ctypes.c_int32(), ctypes.c_int32()

@@ -215,6 +215,22 @@ int tts_sample(tts_ctx* ctx, const float* logits, int32_t batch, int32_t vocab, 
 int tts_run_frames(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_sampling* ac, const float* u,
                    int32_t* codes);
 
+/* tts_run_frames for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * frames, launched one by one with no graph to instantiate, and the persistent
+ * kernels' exchange buffers (2.1 MiB: intra-XCD rings, cross-XCD slots, argmax
+ * candidates, Talker attention partials) taken from a static array of this
+ * size that each GPU the library runs on holds until the process ends, instead
+ * of from the context's workspace. Same arguments, results and errors as
+ * tts_run_frames, plus TTS_E_UNSUPPORTED unless both persistent kernels run
+ * (batch 1, greedy acoustic tokens, bf16 weights, persistent exec mode) and
+ * TTS_E_CAPACITY if their exchange buffers would not fit the array. Calls no
+ * allocating routine. The array keeps the last call's contents and is cleared
+ * (by a kernel) at the start of every call; calls that overlap on one GPU,
+ * from any contexts or threads, race on it. */
+int tts_run_frames_noalloc(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_sampling* ac, const float* u,
+                           int32_t* codes);
+
 /* Streaming text for tts_run_frames (see tts_talker_step_text). text_ids
  * [B, n_text] (device, int32, borrowed until replaced, cleared by tts_reset or
  * NULL): the Talker step run on frame t's codes (t counts frames since the

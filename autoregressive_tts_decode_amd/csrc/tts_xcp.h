@@ -14,13 +14,25 @@
 // layers; an input projection from a Talker hidden of 2048, or none), so every loop is static.
 // A frame is bound by the exchange chain, and what sits between two exchanges is issued by eight
 // waves sharing four SIMDs: every instruction on that path counts. Hence:
-//   * row sums of two to four weight rows are reduced together (two cross-half lane swaps and one
-//     16-lane DPP reduction instead of one full wave reduction per row);
-//   * the residual rows are double buffered, so the all-gather of the new residual needs no
-//     barrier behind the reduce that reads the old one;
-//   * the input projection's rows (the same every step) stay in registers for the whole frame;
-//   * a phase's weight rows for the next layer are issued after the first poll that follows the
-//     phase (a poll waits behind the loads issued before it), a full layer ahead of their use.
+//   * the projections run on the matrix cores. A 16 x 32 weight tile (16 rows of the workgroup's
+//     slice, 32 columns) is the B operand of one v_mfma_f32_16x16x32_bf16, one weight row per
+//     column of B; the A operand holds the input row cut into three bf16 parts: hi is x with the
+//     low 16 bits of its fp32 pattern cleared, mid the same of x - hi, lo = x - hi - mid. Each
+//     remainder is exact in fp32 and lo has at most 8 significant bits, so the parts sum to x
+//     exactly; products of bf16 values are exact in fp32, so a row dot is an fp32 dot up to the
+//     order of its sums. The parts are rows 0..2 of A (4..6 for a second input row): the lane
+//     holding a weight row's C column gets its dot as the sum of three C values, with no
+//     cross-lane reduction. The K range is split across the eight waves, whose partial sums are
+//     added in wave order (a fixed order: the result does not depend on timing);
+//   * inputs are cut into their parts where they arrive: by the exchange polls (residual rows,
+//     times the next RMSNorm gain; the SwiGLU slice) and by the attention waves;
+//   * a workgroup keeps only its own 32 elements of each residual row (the reduce that makes them
+//     runs there) and the per-rank sums of squares, double buffered, so the all-gather of the new
+//     residual needs no barrier behind the reduce that reads the old one;
+//   * the input projection's tiles (the same every step) stay in registers for the whole frame;
+//   * a phase's weight tiles for the next layer are issued a layer ahead of their use, in pieces of
+//     at most 32 KB per CU spread over the layer's six polls: a CU holds its waves at the issue once about
+//     16 KB are in flight, and a poll waits behind the loads issued before it.
 #pragma once
 
 #include "tts_trace.h"
@@ -45,242 +57,164 @@ constexpr int G = 2;             // query heads per KV head
 constexpr int F = 3072;          // FFN size
 constexpr int V = 2048;          // codebook vocabulary (rows of one head)
 constexpr int QR = (G + 2) * D;  // q/k/v rows of one XCD: 512
-constexpr int QPER = QR / NR;    // 16 per rank
-constexpr int HPER = H / NR;     // 32 residual rows per rank
+constexpr int QPER = QR / NR;    // 16 per rank: one tile
+constexpr int HPER = H / NR;     // 32 residual rows per rank: two tiles
 constexpr int FX = F / NX;       // 384 FFN units per XCD
-constexpr int FPER = FX / NR;    // 12 per rank
-constexpr int VPER = V / NWG;    // 8 head rows per workgroup, one per wave
+constexpr int FPER = FX / NR;    // 12 per rank: 24 gate/up rows, a tile and a half
+constexpr int VPER = V / NWG;    // 8 head rows per workgroup: half a tile
 constexpr int KX = 256;          // input-projection columns per XCD (Talker hidden 2048 / 8)
 constexpr int MAXL = 5;          // CodePredictor layers supported
 constexpr int P = 16;            // CodePredictor positions per frame
 constexpr int KVS = 132;         // LDS row stride of the K/V rows (padded against bank conflicts)
-constexpr int E = 8;             // bf16 elements per 16-byte unit
-constexpr int KQ = H / E / 64;   // units per lane of a hidden-wide row: 2
-constexpr int UO = G * D / E;    // units of an output-projection (or input-projection) row: 32
-constexpr int UD = FX / E;       // units of a down-projection row: 48
-constexpr int XW = H + NR;       // residual row plus the per-rank sums of squares
+// LDS row strides (bf16 elements) of the split inputs: 64 bytes past the row, so the parts of one
+// input row fall on different banks
+constexpr int SH = H + 32;
+constexpr int SO = G * D + 32;
+constexpr int SF = FX + 32;
 
-static_assert(QPER == 2 * NW && HPER == 4 * NW && 2 * FPER == 3 * NW && VPER == NW, "row split");
-static_assert(UO == 32 && UD <= 64 && KX / E == UO, "unit split");
+static_assert(QPER == 16 && HPER == 32 && 2 * FPER == 24 && VPER == 8, "row tiles");
+static_assert(H / 32 == 4 * NW && G * D / 32 == NW && KX == G * D && 2 * (FX / 32) == 3 * NW, "K split");
 
-// Weight rows of one layer in registers (this workgroup's slices, bf16):
-//   q   q/k/v rows 2 w, 2 w + 1 of the rank's 16; units lane, lane + 64
-//   o   output projection: unit lane & 31 of rows 4 w + (lane >> 5) (o[0]) and 4 w + 2 + (lane >> 5) (o[1])
-//   gu  gate/up rows 3 w .. 3 w + 2 of the rank's 24 (gate rows 0..11, then up rows 0..11)
-//   dn  down projection rows 4 w .. 4 w + 3, unit lane (lanes < 48)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Weight tiles of one layer in registers. A tile's B fragment: lane l holds its row l % 16 at
+// columns 32 s + 8 (l / 16) .. + 8 of K step s.
+//   q    the rank's 16 q/k/v rows, K steps 4 w .. 4 w + 3 (of 32)
+//   o    output-projection rows 0..15 (o[0]) and 16..31 (o[1]) of the rank, K step w (of 8)
+//   ga   gate/up rows 0..15, K steps 4 w, 4 w + 1; gb the same at K steps 4 w + 2, 4 w + 3
+//   gc   gate/up rows 16..23 (lanes l % 16 < 8), K steps 4 w .. 4 w + 3; in a step's last layer
+//        lanes l % 16 >= 8 take the step's head rows, used after that layer
+//   dn   down rows 16 (w / 4) .. + 15 of the rank, K steps 3 (w % 4) .. + 2 (of 12)
+// (Each piece that is issued on its own is a variable of its own: a partial update of one array
+// would make the compiler copy the whole array.)
 struct Wl {
-  u32x4 q[2][KQ];
+  u32x4 q[4];
   u32x4 o[2];
-  u32x4 gu[3][KQ];
-  u32x4 dn[4];
+  u32x4 ga[2], gb[2];
+  u32x4 gc[4];
+  u32x4 dn[3];
 };
 
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// The lane index from a fresh thread index: what is computed from it is recomputed where it is
+// used instead of being kept live across the layer loop (registers are the scarce resource here:
+// the weight tiles of a whole layer stay in them).
+__device__ __forceinline__ int lane_id() { return xtp::fresh_tid() & 63; }
 // bf16 gains of elements lane and lane + 64 of a head-dimension vector in LDS
 __device__ __forceinline__ void unpack_pair(const uint16_t* gv, int lane, float (&o)[2]) {
   o[0] = to_f32(gv[lane]);
   o[1] = to_f32(gv[lane + 64]);
 }
-
-// ---------------------------------------------------------------------------- lane reductions
-
-typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-// a + b with the upper half of a exchanged for the lower half of b: lanes 0..31 hold
-// a[l] + a[l + 32], lanes 32..63 hold b[l - 32] + b[l].
-__device__ __forceinline__ float fold32(float a, float b) {
-  const u32x2v s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return __uint_as_float(s.x) + __uint_as_float(s.y);
-}
-// The same on 16-lane rows: row 0 <- a r0 + a r1, row 1 <- b r0 + b r1, row 2 <- a r2 + a r3,
-// row 3 <- b r2 + b r3.
-__device__ __forceinline__ float fold16(float a, float b) {
-  const u32x2v s = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return __uint_as_float(s.x) + __uint_as_float(s.y);
-}
 __device__ __forceinline__ float rl(float v, int i) { return xtp::readlane_f(v, i); }
 
-// N (<= 4) values, each to be summed over the whole wave: on return v[i] is that sum (uniform).
-template <int N>
-__device__ __forceinline__ void sum_rows(float (&v)[N]) {
-  static_assert(N >= 1 && N <= 4, "one to four rows");
-  if constexpr (N == 1) {
-    v[0] = wave_sum(v[0]);
-  } else if constexpr (N == 2) {
-    const float s = row16_sum(fold32(v[0], v[1]));
-    v[0] = rl(s, 0) + rl(s, 16);
-    v[1] = rl(s, 32) + rl(s, 48);
-  } else {
-    const float s = row16_sum(fold16(fold32(v[0], v[1]), fold32(v[2], N == 4 ? v[3] : 0.f)));
-    v[0] = rl(s, 0);
-    v[1] = rl(s, 32);
-    v[2] = rl(s, 16);
-    if constexpr (N == 4) v[3] = rl(s, 48);
-  }
+// x into its parts at element k of input row m of a split buffer sp [M][3][stride]
+__device__ __forceinline__ void put_split(uint16_t* sp, int stride, int m, int k, float x) {
+  const uint32_t u = __float_as_uint(x);
+  const float r1 = x - __uint_as_float(u & 0xffff0000u);
+  const uint32_t u1 = __float_as_uint(r1);
+  const float r2 = r1 - __uint_as_float(u1 & 0xffff0000u);
+  uint16_t* d = sp + 3 * m * stride + k;
+  d[0] = (uint16_t)(u >> 16);
+  d[stride] = (uint16_t)(u1 >> 16);
+  d[2 * stride] = (uint16_t)(__float_as_uint(r2) >> 16);
 }
 
-// ---------------------------------------------------------------------------- weight rows
+// ---------------------------------------------------------------------------- weight tiles
 
 template <typename T>
 __device__ __forceinline__ const GLB u32x4* units(const T* p) {
   return xtp::glb(reinterpret_cast<const u32x4*>(p));
 }
+// 16 bytes of a tile fragment: element row0 (a uniform row base) + (l % 16) ld + 8 (l / 16) + c of a
+// bf16 matrix with ld columns. The lane offset comes from a fresh thread index, so it is
+// recomputed at each issue instead of being kept live across the layer loop for every site.
+__device__ __forceinline__ u32x4 ld_frag(const void* m, int ld, int row0, int c) {
+  const int l = xtp::fresh_tid() & 63;
+  const uint16_t* base = reinterpret_cast<const uint16_t*>(m) + (size_t)row0 * ld + c;
+  return *units(base + ((l & 15) * ld + 8 * (l >> 4)));
+}
 
-// q/k/v rows 2 w + i of rank r's slice of XCD g's (query heads | key | value) rows
+// the rank's q/k/v rows QPER r + l % 16 of XCD g's (query heads | key | value) rows; the 16 rows
+// lie in one of the three matrices (QPER divides D)
 __device__ __forceinline__ void issue_q(Wl& R, const KCONST CpDesc& Dd, int l, int g, int r) {
   const KCONST LayerW& W = Dd.layer[l];
-  const int lane = lane_id(), w = xtp::wave_id();
+  const int w = xtp::wave_id(), q0 = QPER * r;
+  const void* m = q0 < G * D ? W.wq : q0 < (G + 1) * D ? W.wk : W.wv;
+  const int row0 = q0 < G * D ? G * D * g + q0 : q0 < (G + 1) * D ? D * g + q0 - G * D : D * g + q0 - (G + 1) * D;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int q = QPER * r + 2 * w + i;
-    const uint16_t* row = q < G * D ? reinterpret_cast<const uint16_t*>(W.wq) + (size_t)(G * D * g + q) * H
-                        : q < (G + 1) * D ? reinterpret_cast<const uint16_t*>(W.wk) + (size_t)(D * g + q - G * D) * H
-                                          : reinterpret_cast<const uint16_t*>(W.wv) + (size_t)(D * g + q - (G + 1) * D) * H;
-    const GLB u32x4* p = units(row);
-#pragma unroll
-    for (int k = 0; k < KQ; ++k) R.q[i][k] = p[lane + 64 * k];
-  }
+  for (int s = 0; s < 4; ++s) R.q[s] = ld_frag(m, H, row0, 32 * (4 * w + s));
 }
-// rows [HPER r, +HPER) x columns [c0, c0 + 256) of a matrix with ld columns, in the o layout
+// rows HPER r + 16 t + l % 16 (t = 0, 1), K step w of the 256 columns from c0, of a matrix with
+// ld columns (output projection; input projection)
 __device__ __forceinline__ void issue_narrow(u32x4 (&o)[2], const void* m, int ld, int c0, int r) {
-  const int lane = lane_id(), w = xtp::wave_id();
+  const int w = xtp::wave_id();
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int row = HPER * r + 4 * w + 2 * k + (lane >> 5);
-    o[k] = units(reinterpret_cast<const uint16_t*>(m) + (size_t)row * ld + c0)[lane & 31];
-  }
+  for (int t = 0; t < 2; ++t) o[t] = ld_frag(m, ld, HPER * r + 16 * t, c0 + 32 * w);
 }
 __device__ __forceinline__ void issue_o(Wl& R, const KCONST CpDesc& Dd, int l, int g, int r) {
   issue_narrow(R.o, Dd.layer[l].wo, Dd.nq * D, G * D * g, r);
 }
-// gate/up row 3 w + i: gate rows 0..FPER-1, then up rows, of FFN units [FX g + FPER r, +FPER)
-__device__ __forceinline__ void issue_gu(Wl& R, const KCONST CpDesc& Dd, int l, int g, int r) {
+// A descriptor pointer as a wave-uniform value. Selecting per lane between two pointers read from
+// the descriptor would otherwise become a per-lane read of the descriptor (a vector load whose wait
+// drains every weight load in flight); read each with a scalar load first.
+__device__ __forceinline__ const uint16_t* uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// gate/up rows q = l % 16 of the rank's gate rows 0..FPER-1, then up rows, of FFN units
+// [FX g + FPER r, +FPER) (lanes 12..15: up rows 0..3), K steps 4 w + s0, 4 w + s0 + 1
+__device__ __forceinline__ void issue_gu0(u32x4 (&t)[2], const KCONST CpDesc& Dd, int l, int g, int r, int s0) {
   const KCONST LayerW& W = Dd.layer[l];
-  const int lane = lane_id(), w = xtp::wave_id();
+  const uint16_t *wg = uniform_ptr(W.wg), *wu = uniform_ptr(W.wu);
+  const int w = xtp::wave_id(), f0 = FX * g + FPER * r;
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int q = 3 * w + i;
-    const int f = FX * g + FPER * r + (q < FPER ? q : q - FPER);
-    const GLB u32x4* p = units(reinterpret_cast<const uint16_t*>(q < FPER ? W.wg : W.wu) + (size_t)f * H);
-#pragma unroll
-    for (int k = 0; k < KQ; ++k) R.gu[i][k] = p[lane + 64 * k];
+  for (int s = 0; s < 2; ++s) {
+    const bool gate = (xtp::fresh_tid() & 15) < FPER;
+    t[s] = ld_frag(gate ? wg : wu, H, gate ? f0 : f0 - FPER, 32 * (4 * w + s0 + s));
   }
 }
-// down rows HPER r + 4 w + i, columns of XCD g's FFN units, unit lane
+// Lanes l % 16 < 8: gate/up rows 16..23 (up rows 4..11). Lanes l % 16 >= 8: with head j >= 1,
+// that head's rows VPER blockIdx + l % 16 - 8 (the head tile of the step's last layer, used after
+// it); else the up rows again (columns of C that are never used). K steps 4 w .. 4 w + 3.
+__device__ __forceinline__ void issue_gu1(Wl& R, const KCONST CpDesc& Dd, int l, int g, int r, int j) {
+  const int w = xtp::wave_id(), f0 = FX * g + FPER * r;
+  const uint16_t *wu = uniform_ptr(Dd.layer[l].wu), *hd = uniform_ptr(Dd.heads);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const bool head = j > 0 && (xtp::fresh_tid() & 8);
+    R.gc[s] = ld_frag(head ? hd : wu, H, head ? (j - 1) * V + VPER * (int)blockIdx.x - 8 : f0 + (16 - FPER) - 8 * ((xtp::fresh_tid() >> 3) & 1),
+                      32 * (4 * w + s));
+  }
+}
+// down rows HPER r + 16 (w / 4) + l % 16, K steps 3 (w % 4) .. + 2 of XCD g's FFN columns
 __device__ __forceinline__ void issue_dn(Wl& R, const KCONST CpDesc& Dd, int l, int g, int r) {
-  const int lane = lane_id(), w = xtp::wave_id();
+  const int w = xtp::wave_id();
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = HPER * r + 4 * w + i;
-    if (lane < UD) R.dn[i] = units(reinterpret_cast<const uint16_t*>(Dd.layer[l].wd) + (size_t)row * F + FX * g)[lane];
-  }
+  for (int s = 0; s < 3; ++s) R.dn[s] = ld_frag(Dd.layer[l].wd, F, HPER * r + 16 * (w >> 2), FX * g + 32 * (3 * (w & 3) + s));
 }
-// head j row VPER blockIdx + w
-__device__ __forceinline__ void issue_hd(u32x4 (&hd)[1][KQ], const KCONST CpDesc& Dd, int j) {
-  const int lane = lane_id(), w = xtp::wave_id();
-  const GLB u32x4* p = units(reinterpret_cast<const uint16_t*>(Dd.heads) + ((size_t)(j - 1) * V + VPER * blockIdx.x + w) * H);
-#pragma unroll
-  for (int k = 0; k < KQ; ++k) hd[0][k] = p[lane + 64 * k];
-}
+// ---------------------------------------------------------------------------- matrix-core dots
 
-// ---------------------------------------------------------------------------- row dots
+// NS K steps from ks0 of one weight tile against the split input sp (row stride st): lane l
+// supplies A row l % 16 = 4 m + p, part p of input row m (rows past the parts: zeros).
+template <int M, int NS>
+__device__ __forceinline__ f32x4 mfma_steps(const u32x4* wt, const uint16_t* sp, int st, int ks0, const uint16_t* zero,
+                                            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}) {
+  const int row = lane_id() & 15, m = row >> 2, p = row & 3;
+  const bool live = p < 3 && m < M;
+  const uint16_t* base = sp + (3 * m + p) * st;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(live ? base + 32 * (ks0 + s) + 8 * (lane_id() >> 4) : zero);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, wt[s]), acc, 0, 0, 0);
+  }
+  return acc;
+}
+// Lane 16 m + i (m < M) gets the dot of weight row i with input row m: C rows 4 m .. 4 m + 2.
+__device__ __forceinline__ float parts_sum(const f32x4& acc) { return (acc[0] + acc[1]) + acc[2]; }
 
-// x[m][8 u .. 8 u + 8) from LDS, times the bf16 gains gn[8 u ..] when given
-template <int M>
-__device__ __forceinline__ void load_x(const float* x, int ldx, int u, const uint16_t* gn, float (&xv)[M][8]) {
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const float4 a = *reinterpret_cast<const float4*>(x + m * ldx + 8 * u);
-    const float4 b = *reinterpret_cast<const float4*>(x + m * ldx + 8 * u + 4);
-    xv[m][0] = a.x; xv[m][1] = a.y; xv[m][2] = a.z; xv[m][3] = a.w;
-    xv[m][4] = b.x; xv[m][5] = b.y; xv[m][6] = b.z; xv[m][7] = b.w;
-  }
-  if (gn) {
-    float gf[8];
-    unpack(*reinterpret_cast<const u32x4*>(gn + 8 * u), gf, (uint16_t*)nullptr);
-#pragma unroll
-    for (int m = 0; m < M; ++m)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xv[m][e] *= gf[e];
-  }
-}
-template <int M>
-__device__ __forceinline__ void fma_unit(const u32x4& w, const float (&xv)[M][8], float (&acc)[M]) {
-  float wf[8];
-  unpack(w, wf, (uint16_t*)nullptr);
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    float s = acc[m];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s = fmaf(wf[e], xv[m][e], s);
-    acc[m] = s;
-  }
-}
-// R hidden-wide rows (units lane + 64 k) against M rows of x (stride ldx), gains gn (or null):
-// per-lane partial sums acc[i][m].
-template <int R, int M>
-__device__ __forceinline__ void dot_wide(const u32x4 (&w)[R][KQ], const float* x, int ldx, const uint16_t* gn,
-                                         float (&acc)[R][M]) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int i = 0; i < R; ++i)
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[i][m] = 0.f;
-#pragma unroll
-  for (int k = 0; k < KQ; ++k) {
-    float xv[M][8];
-    load_x<M>(x, ldx, lane + 64 * k, gn, xv);
-#pragma unroll
-    for (int i = 0; i < R; ++i) fma_unit<M>(w[i][k], xv, acc[i]);
-  }
-}
-// The four narrow rows of the o layout against M rows of x (256 wide, stride ldx): out[i][m] is the
-// sum of row 4 w + i (uniform).
-template <int M>
-__device__ __forceinline__ void dot_narrow(const u32x4 (&o)[2], const float* x, int ldx, float (&out)[4][M]) {
-  const int lane = lane_id();
-  float xv[M][8];
-  load_x<M>(x, ldx, lane & 31, nullptr, xv);
-  float a[2][M];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-#pragma unroll
-    for (int m = 0; m < M; ++m) a[k][m] = 0.f;
-    fma_unit<M>(o[k], xv, a[k]);
-  }
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    // rows: lanes 0-15 row 0, 16-31 row 2, 32-47 row 1, 48-63 row 3
-    const float s = row16_sum(fold16(a[0][m], a[1][m]));
-    out[0][m] = rl(s, 0);
-    out[2][m] = rl(s, 16);
-    out[1][m] = rl(s, 32);
-    out[3][m] = rl(s, 48);
-  }
-}
-// The four down rows against M rows of the SwiGLU slice (384 wide, stride FX).
-template <int M>
-__device__ __forceinline__ void dot_down(const u32x4 (&dn)[4], const float* x, float (&out)[4][M]) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int m = 0; m < M; ++m) out[i][m] = 0.f;
-  if (lane < UD) {
-    float xv[M][8];
-    load_x<M>(x, FX, lane, nullptr, xv);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fma_unit<M>(dn[i], xv, out[i]);
-  }
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    float v[4] = {out[0][m], out[1][m], out[2][m], out[3][m]};
-    sum_rows<4>(v);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i][m] = v[i];
-  }
-}
-
-// 1 / sqrt(mean(x^2) + eps) of a residual row from its NR per-rank sums of squares
+// 1 / sqrt(mean(x^2) + eps) of a residual row from its NR per-rank sums of squares (whole wave)
 __device__ __forceinline__ float norm_scale(const float* ss, float eps) {
   const int lane = lane_id();
   float v = lane < NR ? ss[lane] : 0.f;
@@ -288,30 +222,22 @@ __device__ __forceinline__ float norm_scale(const float* ss, float eps) {
   return 1.0f / sqrtf((rl(v, 0) + rl(v, 16)) / (float)H + eps);
 }
 
-// Lane 0 stores entry idx(t) = vals[t] for t < N (wave-uniform values).
-template <int N, typename Idx, typename St>
-__device__ __forceinline__ void put_lanes(const float (&vals)[N], Idx idx, St store) {
-  if (lane_id() == 0) {
-#pragma unroll
-    for (int t = 0; t < N; ++t) store(idx(t), vals[t]);
-  }
-}
-
 // ---------------------------------------------------------------------------- shared memory
 
 struct Smem {
-  float xs[2][2 * XW];           // residual rows (double buffered): row m at m H, sums of squares at M H + m NR
+  float xo[2][2][HPER];          // this rank's elements of the residual rows [buffer][row]
+  float ss[2][2 * NR];           // per-rank sums of squares of the residual rows [buffer][row NR + rank]
   float xn[NX * 2 * HPER];       // reduce-scatter partials: partner x, row m at (x M + m) HPER
-  float xp[2 * KX];              // input-projection input slice (row m at m KX)
   float qkv[2 * QR];             // this XCD's q/k/v rows (row m at m QR)
   float kq[4][D];                // normed, rotated q of each attention wave
-  float ob[2 * G * D];           // attention output of this XCD's heads (row m at m G D)
-  float gus[2 * FPER * 2];       // gate/up row sums: row q, input row m at q M + m
-  float hb[2 * FX];              // SwiGLU slice of the XCD (row m at m FX)
+  float part[NW][2][32];         // per-wave partial dots [wave][tile][16 m + row]
   float cand[2 * NWG];           // argmax candidates (value, id bits)
-  float red[2 * NW];
   float rope[P][2][D / 2];       // cos, sin of positions 0..15
   float kvc[MAXL][2][P][KVS];    // this frame's K/V rows of KV head g, per layer
+  __align__(16) uint16_t xsp[2 * 3 * SH];  // residual rows times the next RMSNorm gain, in parts
+  __align__(16) uint16_t osp[2 * 3 * SO];  // attention output (or input-projection slice), in parts
+  __align__(16) uint16_t hsp[2 * 3 * SF];  // SwiGLU slice of the XCD, in parts
+  __align__(16) uint16_t zero[8];
   __align__(16) uint16_t gn[2 * MAXL + 1][H];  // RMSNorm gains: layer l attention 2 l, MLP 2 l + 1, final 2 MAXL
   __align__(16) uint16_t gqk[MAXL][2][D];      // q-norm, k-norm gains per layer
 };
@@ -329,11 +255,14 @@ struct Ctx {
 };
 
 // Cross reduce-scatter of the partial rows published by produce() (rows [HPER r, +HPER) of this
-// rank for M input rows), plus the residual xs[cur] when given, then the intra all-gather of the
-// full new rows into xs[cur ^ 1] (the other buffer). after_put runs between publish and poll.
+// rank for M input rows), plus the residual when given, then the intra all-gather of the full new
+// rows: this rank's elements into xo and the sums of squares into ss of the other buffer, and
+// every element, times the gain gn (the next RMSNorm's), in parts into xsp. after_put runs between
+// publish and poll.
 template <int M, typename Produce, typename AfterPut>
-__device__ __forceinline__ bool reduce_gather(Ctx& c, bool residual, Produce produce, AfterPut after_put) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ bool reduce_gather(Ctx& c, bool residual, const uint16_t* gn, Produce produce, AfterPut after_put) {
+  const int tid = xtp::fresh_tid();
+  Smem& S = *c.S;
   ++c.tag;
   const uint32_t t = c.tag;
   u64* mine = c.X.xcr + ((size_t)(c.r * NX + c.g) * 2 + (c.cpar & 1)) * xtp::CSZ;
@@ -342,7 +271,7 @@ __device__ __forceinline__ bool reduce_gather(Ctx& c, bool residual, Produce pro
   after_put();
   TTS_STAMP(21);
   const u64* base = c.X.xcr + ((size_t)(c.r * NX) * 2 + (c.cpar & 1)) * xtp::CSZ;
-  if (!xtp::get_at<(NX * M * HPER + NT - 1) / NT>(NX * M * HPER, t, c.S->xn, c.X.err, [&](int i) -> const u64* {
+  if (!xtp::get_at<(NX * M * HPER + NT - 1) / NT>(NX * M * HPER, t, S.xn, c.X.err, [&](int i) -> const u64* {
         const int sg = i >> 5, e = i & 31;  // segment (partner x, row m) = sg -> x = sg / M, m = sg % M
         return base + (size_t)(sg / M) * (2 * xtp::CSZ) + (sg % M) * 64 + e;
       }))
@@ -351,79 +280,79 @@ __device__ __forceinline__ bool reduce_gather(Ctx& c, bool residual, Produce pro
   ++c.cpar;
   ++c.tag;
   u64* buf = c.intra_buf();
-  const float* xs = c.S->xs[c.xb];
-  if (tid < 64) {  // wave 0: lane m * 32 + e reduces row HPER r + e of input row m
+  const int nb = c.xb ^ 1;
+  if (tid < 64) {  // wave 0: lane 32 m + e reduces element HPER r + e of input row m
     const int m = tid >> 5, e = tid & 31;
     float v = 0.f;
     if (m < M) {
-      if (residual) v = xs[m * H + HPER * c.r + e];
+      if (residual) v = S.xo[c.xb][m][e];
 #pragma unroll
-      for (int x = 0; x < NX; ++x) v += c.S->xn[(x * M + m) * HPER + e];
+      for (int x = 0; x < NX; ++x) v += S.xn[(x * M + m) * HPER + e];
+      S.xo[nb][m][e] = v;
       xtp::st_l(buf + m * H + HPER * c.r + e, xtp::pack(v, c.tag));
     }
     const float s = row16_sum(v * v);
-    const float ss[2] = {rl(s, 0) + rl(s, 16), rl(s, 32) + rl(s, 48)};
-    if (tid < M) xtp::st_l(buf + M * H + tid * NR + c.r, xtp::pack(tid == 0 ? ss[0] : ss[1], c.tag));
+    const float sq[2] = {rl(s, 0) + rl(s, 16), rl(s, 32) + rl(s, 48)};
+    if (tid < M) xtp::st_l(buf + M * H + tid * NR + c.r, xtp::pack(tid == 0 ? sq[0] : sq[1], c.tag));
   }
-  c.xb ^= 1;
+  c.xb = nb;
   TTS_STAMP(23);
-  const bool ok = xtp::get_flat<(2 * XW + NT - 1) / NT>(buf, M * XW, c.tag, c.S->xs[c.xb], c.X.err);
+  const bool ok = xtp::get_each<(M * (H + NR) + NT - 1) / NT>(
+      M * (H + NR), c.tag, c.X.err, [&](int i) -> const u64* { return buf + i; },
+      [&](int i, float v) {
+        if (i < M * H)
+          put_split(S.xsp, SH, i / H, i % H, v * to_f32(gn[i % H]));
+        else
+          S.ss[nb][i - M * H] = v;
+      });
   TTS_STAMP(24);
-  return ok;
-}
-
-// Intra gather of a slice: this rank's n values per input row (published by produce at row
-// offset n r of a w-wide row) into dst (row m at m w) for every rank of the XCD.
-template <int M, int KMAX, typename Produce>
-__device__ __forceinline__ bool slice_gather(Ctx& c, int n, int w, Produce produce, float* dst) {
-  ++c.tag;
-  const uint32_t t = c.tag;
-  u64* buf = c.intra_buf();
-  produce([&](int e, int m, float v) { xtp::st_l(buf + m * w + n * c.r + e, xtp::pack(v, t)); });
-  TTS_STAMP(11);
-  const bool ok = xtp::get_flat<KMAX>(buf, M * w, t, dst, c.X.err);
-  TTS_STAMP(13);
   return ok;
 }
 
 // ---------------------------------------------------------------------------- the layer
 
-// next layer (or the next step's first layer) whose rows a phase issues after consuming its own
+// next layer (or the next step's first layer) whose tiles a phase issues after consuming its own
 struct Next {
   int l;      // -1: none
-  bool head;  // issue head j with the output-projection rows (last layer of a step)
+  bool head;  // load head j's rows with the gc tiles (last layer of a step)
 };
 
 template <int M>
-__device__ __forceinline__ bool cp_layer(Ctx& c, Wl& R, u32x4 (&hd)[1][KQ], int l, int j, int p0, Next nx) {
+__device__ __forceinline__ bool cp_layer(Ctx& c, Wl& R, int l, int j, int p0, Next nx) {
   const KCONST CpDesc& Dd = *c.Dd;
   Smem& S = *c.S;
   const int lane = lane_id(), w = xtp::wave_id(), g = c.g, r = c.r;
   const float eps = Dd.eps;
+  const uint16_t* gn_mlp = S.gn[2 * l + 1];
+  const uint16_t* gn_next = l + 1 < Dd.n_layers ? S.gn[2 * (l + 1)] : S.gn[2 * MAXL];
 
-  // --- q/k/v slice: rows 2 w, 2 w + 1 against RMSNorm(x), published straight from the dot
+  // --- q/k/v tile against RMSNorm(x): the parts in xsp carry the gain, the reducer the scale
   TTS_STAMP(10);
   {
-    const float* xs = S.xs[c.xb];
-    float sc[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) sc[m] = norm_scale(xs + M * H + m * NR, eps);
-    float a[2][M];
-    dot_wide<2, M>(R.q, xs, H, S.gn[2 * l], a);
-    float v[2 * M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) { v[2 * m] = a[0][m]; v[2 * m + 1] = a[1][m]; }
-    sum_rows<2 * M>(v);
-#pragma unroll
-    for (int m = 0; m < M; ++m) { v[2 * m] *= sc[m]; v[2 * m + 1] *= sc[m]; }
-    if (!slice_gather<M, (2 * QR + NT - 1) / NT>(
-            c, QPER, QR,
-            [&](auto emit) { put_lanes<2 * M>(v, [](int t) { return t; }, [&](int t, float x) { emit(2 * w + (t & 1), t >> 1, x); }); },
-            S.qkv))
-      return false;
+    const f32x4 a = mfma_steps<M, 4>(R.q, S.xsp, SH, 4 * w, S.zero);
+    if (lane < 16 * M) S.part[w][0][lane] = parts_sum(a);
   }
-  if (nx.l >= 0) issue_q(R, Dd, nx.l, g, r);
-  TTS_STAMP(12);
+  xtp::lds_barrier();
+  {
+    ++c.tag;
+    const uint32_t t = c.tag;
+    u64* buf = c.intra_buf();
+    if (w == 0) {
+      const float sc0 = norm_scale(S.ss[c.xb], eps);
+      const float sc1 = M == 2 ? norm_scale(S.ss[c.xb] + NR, eps) : 0.f;
+      if (lane < 16 * M) {  // row lane % 16 of input row lane / 16, the waves' partials in wave order
+        float v = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) v += S.part[ww][0][lane];
+        xtp::st_l(buf + (lane >> 4) * QR + QPER * r + (lane & 15), xtp::pack(v * (lane < 16 ? sc0 : sc1), t));
+      }
+    }
+    TTS_STAMP(11);
+    if (!xtp::get_flat<(M * QR + NT - 1) / NT>(buf, M * QR, t, S.qkv, c.X.err)) return false;
+    TTS_STAMP(13);
+  }
+  // the next q/k/v tiles: the waves that run no attention now, the attention waves after it
+  if (nx.l >= 0 && w >= G * M) issue_q(R, Dd, nx.l, g, r);
 
   // --- attention of this XCD's heads over positions 0 .. p0 + M - 1: one wave per (head, row)
   if (w < G * M) {
@@ -482,202 +411,217 @@ __device__ __forceinline__ bool cp_layer(Ctx& c, Wl& R, u32x4 (&hd)[1][KQ], int 
       o0 = fmaf(wv, vc[tt][lane], o0);
       o1 = fmaf(wv, vc[tt][lane + 64], o1);
     }
-    S.ob[m * G * D + h * D + lane] = o0 / ls;
-    S.ob[m * G * D + h * D + lane + 64] = o1 / ls;
+    put_split(S.osp, SO, m, h * D + lane, o0 / ls);
+    put_split(S.osp, SO, m, h * D + lane + 64, o1 / ls);
+    if (nx.l >= 0) issue_q(R, Dd, nx.l, g, r);
   }
   xtp::lds_barrier();
   TTS_STAMP(14);
 
-  // --- output projection partial of rows HPER r + 4 w + i (this XCD's head columns), residual
+  // --- output-projection partials of the rank's 32 rows (this XCD's head columns), residual
   {
-    float o[4][M];
-    dot_narrow<M>(R.o, S.ob, G * D, o);
-    if (!reduce_gather<M>(
-            c, true,
-            [&](auto emit) {
-              float v[4 * M];
-#pragma unroll
-              for (int m = 0; m < M; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[4 * m + i] = o[i][m];
-              put_lanes<4 * M>(v, [](int t) { return t; }, [&](int t, float x) { emit(4 * w + (t & 3), t >> 2, x); });
-            },
-            [&] {
-              if (nx.l >= 0) issue_o(R, Dd, nx.l, g, r);
-              if (nx.head) issue_hd(hd, Dd, j);
-            }))
-      return false;
-  }
-
-  // --- gate/up rows 3 w + i against RMSNorm(x), SwiGLU of the rank's FFN units
-  {
-    const float* xs = S.xs[c.xb];
-    float sc[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) sc[m] = norm_scale(xs + M * H + m * NR, eps);
-    float a[3][M];
-    dot_wide<3, M>(R.gu, xs, H, S.gn[2 * l + 1], a);
-    if constexpr (M == 1) {
-      float v[3] = {a[0][0], a[1][0], a[2][0]};
-      sum_rows<3>(v);
-      const float vs[3] = {v[0] * sc[0], v[1] * sc[0], v[2] * sc[0]};
-      put_lanes<3>(vs, [](int t) { return t; }, [&](int t, float x) { S.gus[3 * w + t] = x; });
-    } else {
-      float v0[4] = {a[0][0], a[0][1], a[1][0], a[1][1]};
-      float v1[2] = {a[2][0], a[2][1]};
-      sum_rows<4>(v0);
-      sum_rows<2>(v1);
-      const float vs[6] = {v0[0] * sc[0], v0[1] * sc[1], v0[2] * sc[0], v0[3] * sc[1], v1[0] * sc[0], v1[1] * sc[1]};
-      put_lanes<6>(vs, [](int t) { return t; }, [&](int t, float x) { S.gus[6 * w + t] = x; });
+    const f32x4 a0 = mfma_steps<M, 1>(&R.o[0], S.osp, SO, w, S.zero);
+    const f32x4 a1 = mfma_steps<M, 1>(&R.o[1], S.osp, SO, w, S.zero);
+    if (lane < 16 * M) {
+      S.part[w][0][lane] = parts_sum(a0);
+      S.part[w][1][lane] = parts_sum(a1);
     }
-    xtp::lds_barrier();
+  }
+  xtp::lds_barrier();
+  if (!reduce_gather<M>(
+          c, true, gn_mlp,
+          [&](auto emit) {
+            const int tid = xtp::fresh_tid();
+            if (tid < 32 * M) {  // element e = 16 tile + i of input row m: tid = 32 m + e
+              const int m = tid >> 5, e = tid & 31;
+              float v = 0.f;
+#pragma unroll
+              for (int ww = 0; ww < NW; ++ww) v += S.part[ww][e >> 4][16 * m + (e & 15)];
+              emit(e, m, v);
+            }
+          },
+          [&] {
+            if (nx.l >= 0) issue_o(R, Dd, nx.l, g, r);
+          }))
+    return false;
+
+  // --- gate/up tiles against RMSNorm(x), SwiGLU of the rank's FFN units
+  {
+    const f32x4 a0 = mfma_steps<M, 2>(R.gb, S.xsp, SH, 4 * w + 2, S.zero, mfma_steps<M, 2>(R.ga, S.xsp, SH, 4 * w, S.zero));
+    const f32x4 a1 = mfma_steps<M, 4>(R.gc, S.xsp, SH, 4 * w, S.zero);
+    if (lane < 16 * M) {
+      S.part[w][0][lane] = parts_sum(a0);
+      S.part[w][1][lane] = parts_sum(a1);
+    }
+  }
+  // the gate/up registers are free: the next layer's tiles go out in two pieces, here and after
+  // the SwiGLU gather
+  if (nx.l >= 0 || nx.head) issue_gu1(R, Dd, nx.l >= 0 ? nx.l : l, g, r, nx.head ? j : 0);
+  xtp::lds_barrier();
+  {
+    ++c.tag;
+    const uint32_t t = c.tag;
+    u64* buf = c.intra_buf();
+    if (w == 0) {
+      const float sc0 = norm_scale(S.ss[c.xb], eps);
+      const float sc1 = M == 2 ? norm_scale(S.ss[c.xb] + NR, eps) : 0.f;
+      if (lane < FPER * M) {  // FFN unit f of input row m: lane = FPER m + f
+        const int m = lane / FPER, f = lane % FPER, qu = FPER + f;  // qu: its up row
+        float gs = 0.f, us = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          gs += S.part[ww][0][16 * m + f];
+          us += S.part[ww][qu >> 4][16 * m + (qu & 15)];
+        }
+        const float sc = m == 0 ? sc0 : sc1;
+        xtp::st_l(buf + m * FX + FPER * r + f, xtp::pack(silu(gs * sc) * (us * sc), t));
+      }
+    }
     TTS_STAMP(15);
-    if (!slice_gather<M, (2 * FX + NT - 1) / NT>(
-            c, FPER, FX,
-            [&](auto emit) {
-              const int tid = threadIdx.x;
-              if (tid < FPER * M) {
-                const int f = tid % FPER, m = tid / FPER;
-                emit(f, m, silu(S.gus[f * M + m]) * S.gus[(FPER + f) * M + m]);
-              }
-            },
-            S.hb))
+    if (!xtp::get_each<(M * FX + NT - 1) / NT>(M * FX, t, c.X.err, [&](int i) -> const u64* { return buf + i; },
+                                               [&](int i, float v) { put_split(S.hsp, SF, i / FX, i % FX, v); }))
       return false;
   }
-  if (nx.l >= 0) issue_gu(R, Dd, nx.l, g, r);
+  if (nx.l >= 0) issue_gu0(R.ga, Dd, nx.l, g, r, 0);
+  if (nx.l >= 0) issue_gu0(R.gb, Dd, nx.l, g, r, 2);
   TTS_STAMP(16);
 
-  // --- down projection partial of rows HPER r + 4 w + i (this XCD's FFN columns), residual
-  float dv[4][M];
-  dot_down<M>(R.dn, S.hb, dv);
-  return reduce_gather<M>(
-      c, true,
-      [&](auto emit) {
-        float v[4 * M];
+  // --- down-projection partials of the rank's 32 rows (this XCD's FFN columns), residual
+  {
+    const f32x4 a = mfma_steps<M, 3>(R.dn, S.hsp, SF, 3 * (w & 3), S.zero);
+    if (lane < 16 * M) S.part[w][0][lane] = parts_sum(a);
+  }
+  xtp::lds_barrier();
+  if (!reduce_gather<M>(
+          c, true, gn_next,
+          [&](auto emit) {
+            const int tid = xtp::fresh_tid();
+            if (tid < 32 * M) {  // tile e / 16 is the sum of waves 4 (e / 16) .. + 3
+              const int m = tid >> 5, e = tid & 31, w0 = 4 * (e >> 4);
+              float v = 0.f;
 #pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[4 * m + i] = dv[i][m];
-        put_lanes<4 * M>(v, [](int t) { return t; }, [&](int t, float x) { emit(4 * w + (t & 3), t >> 2, x); });
-      },
-      [&] {
-        if (nx.l >= 0) issue_dn(R, Dd, nx.l, g, r);
-      });
+              for (int ww = 0; ww < 4; ++ww) v += S.part[w0 + ww][0][16 * m + (e & 15)];
+              emit(e, m, v);
+            }
+          },
+          [&] {
+            if (nx.l >= 0) issue_dn(R, Dd, nx.l, g, r);
+          }))
+    return false;
+  return true;
 }
 
 // ---------------------------------------------------------------------------- the step
 
-// The best (value, id) of this workgroup's VPER logits (one per wave, in S.red), published to
-// every workgroup; every wave then takes the argmax of all NWG candidates (ties: the lower id).
+// Minimum of an int over the wave (DPP within 16-lane rows, then the four row results).
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true));  // row_ror:4
+  v = min(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true));  // row_ror:8
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// The best (value, id) of this workgroup's VPER logits (lanes 0..VPER-1 of wave 0 hold them),
+// published to every workgroup; every wave then takes the argmax of all NWG candidates. Ties go to
+// the lowest id: the maximum value first, then the lowest id among the lanes that hold it.
 // Returns the id, or -1 on failure.
 __device__ __forceinline__ int argmax_exchange(Ctx& c, float logit) {
-  const int lane = lane_id(), w = xtp::wave_id(), tid = threadIdx.x;
+  const int lane = lane_id(), w = xtp::wave_id();
   Smem& S = *c.S;
-  if (lane == 0) S.red[w] = logit;
-  xtp::lds_barrier();
   ++c.tag;
   u64* cb = c.Dd->cand + (size_t)(c.apar & 1) * NWG * xtp::CAND;
   if (w == 0) {
-    // lanes 0..7: the wave logits; the lowest index wins ties
-    float v = lane < NW ? S.red[lane] : -INFINITY;
-    int id = lane;
-#pragma unroll
-    for (int o = 1; o < NW; o <<= 1) {
-      const float v2 = __shfl_xor(v, o);
-      const int id2 = __shfl_xor(id, o);
-      if (v2 > v || (v2 == v && id2 < id)) { v = v2; id = id2; }
-    }
-    const float vals[2] = {v, __int_as_float(VPER * (int)blockIdx.x + id)};
-    put_lanes<2>(vals, [](int t) { return t; },
-                 [&](int t, float x) { xtp::st_c(cb + blockIdx.x * xtp::CAND + t, xtp::pack(x, c.tag)); });
+    const float v = lane < VPER ? logit : -INFINITY;
+    const float mx = wave_max(v);
+    const int id = wave_min_i(lane < VPER && v == mx ? lane : 0x7fffffff);
+    const int best = VPER * (int)blockIdx.x + (id < VPER ? id : 0);  // no lane equal: NaN logits
+    if (lane < 2) xtp::st_c(cb + blockIdx.x * xtp::CAND + lane, xtp::pack(lane == 0 ? mx : __int_as_float(best), c.tag));
   }
   if (!xtp::get_at<1>(2 * NWG, c.tag, S.cand, c.X.err,
                       [&](int i) -> const u64* { return cb + (i >> 1) * xtp::CAND + (i & 1); }))
     return -1;
   ++c.apar;
-  (void)tid;
-  // every wave: lane l takes candidates l, l + 64, l + 128, l + 192 (lower ids first), then the wave
+  // every wave: lane l takes candidates l, l + 64, l + 128, l + 192 (ids increase with the index,
+  // so a later candidate replaces an earlier one only when strictly larger)
   float v = S.cand[2 * lane];
   int id = __float_as_int(S.cand[2 * lane + 1]);
 #pragma unroll
   for (int k = 1; k < NWG / 64; ++k) {
     const float v2 = S.cand[2 * (lane + 64 * k)];
     const int id2 = __float_as_int(S.cand[2 * (lane + 64 * k) + 1]);
-    if (v2 > v) { v = v2; id = id2; }  // ids of later candidates are higher
+    if (v2 > v) { v = v2; id = id2; }
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float v2 = __shfl_xor(v, o);
-    const int id2 = __shfl_xor(id, o);
-    if (v2 > v || (v2 == v && id2 < id)) { v = v2; id = id2; }
-  }
-  return __builtin_amdgcn_readfirstlane(id);
+  const float mx = wave_max(v);
+  const int best = wave_min_i(v == mx ? id : 0x7fffffff);
+  return best < V ? best : 0;
 }
 
-// Step j's input rows into xs[xb] (rows and per-rank sums of squares): with an input projection
-// its K split across the XCDs (rows of the resident pj) and a reduce-scatter + all-gather;
-// without one the rows themselves. M = 2 at step 1 (h_T and E_sem[tok]), else E_ac[j - 1][tok].
+// Step j's input rows: this rank's elements into xo[xb], the sums of squares into ss[xb], and the
+// rows times the first layer's attention gain, in parts, into xsp. With an input projection its K
+// is split across the XCDs (the resident tiles pj), then a reduce-scatter + all-gather; without
+// one the rows are read as they are. M = 2 at step 1 (h_T and E_sem[tok]), else E_ac[j - 1][tok].
 template <int M>
 __device__ __forceinline__ bool step_input(Ctx& c, const u32x4 (&pj)[2], int j, int tok) {
   const KCONST CpDesc& Dd = *c.Dd;
   Smem& S = *c.S;
-  const int tid = threadIdx.x, lane = lane_id(), w = xtp::wave_id();
+  const int tid = xtp::fresh_tid(), lane = lane_id(), w = xtp::wave_id();
   const int Ht = Dd.Ht;
   const uint16_t* tab = j == 1 ? reinterpret_cast<const uint16_t*>(Dd.embed_sem)
                                : reinterpret_cast<const uint16_t*>(Dd.embed_ac) + (size_t)(j - 2) * V * Ht;
   const uint16_t* erow = tab + (size_t)tok * Ht;
+  const uint16_t* gn0 = S.gn[0];
   if (Dd.proj) {
-    // this XCD's 256 columns of each input row
-    if (tid < KX / 4) {
-      const int c0 = KX * c.g + 4 * tid;
-      if (M == 2) {
-        const u32x4 hv = *reinterpret_cast<const GLB u32x4*>(xtp::glb(Dd.hT) + c0);
-        *reinterpret_cast<u32x4*>(&S.xp[4 * tid]) = hv;
-      }
-      const u32x2v ev = *reinterpret_cast<const GLB u32x2v*>(xtp::glb(erow) + c0);
-      float* dst = &S.xp[(M - 1) * KX + 4 * tid];
-      dst[0] = bf16_lo(ev.x); dst[1] = bf16_hi(ev.x); dst[2] = bf16_lo(ev.y); dst[3] = bf16_hi(ev.y);
+    // this XCD's 256 columns of each input row, in parts
+    if (tid < KX) {
+      const int c0 = KX * c.g + tid;
+      if (M == 2) put_split(S.osp, SO, 0, tid, xtp::glb(Dd.hT)[c0]);
+      put_split(S.osp, SO, M - 1, tid, to_f32(xtp::glb(erow)[c0]));
     }
     xtp::lds_barrier();
-    float o[4][M];
-    dot_narrow<M>(pj, S.xp, KX, o);
+    const f32x4 a0 = mfma_steps<M, 1>(&pj[0], S.osp, SO, w, S.zero);
+    const f32x4 a1 = mfma_steps<M, 1>(&pj[1], S.osp, SO, w, S.zero);
+    if (lane < 16 * M) {
+      S.part[w][0][lane] = parts_sum(a0);
+      S.part[w][1][lane] = parts_sum(a1);
+    }
+    xtp::lds_barrier();
     return reduce_gather<M>(
-        c, false,
+        c, false, gn0,
         [&](auto emit) {
-          float v[4 * M];
+          if (tid < 32 * M) {
+            const int m = tid >> 5, e = tid & 31;
+            float v = 0.f;
 #pragma unroll
-          for (int m = 0; m < M; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[4 * m + i] = o[i][m];
-          put_lanes<4 * M>(v, [](int t) { return t; }, [&](int t, float x) { emit(4 * w + (t & 3), t >> 2, x); });
+            for (int ww = 0; ww < NW; ++ww) v += S.part[ww][e >> 4][16 * m + (e & 15)];
+            emit(e, m, v);
+          }
         },
         [] {});
   }
   // no projection (Talker hidden = CodePredictor hidden): the rows as they are; the sums of
   // squares in the layout an all-gather leaves them (one per wave here, the other slots zero)
-  float* xs = S.xs[c.xb];
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    float x0, x1;
-    const int i0 = 128 * w + lane, i1 = i0 + 64;
-    if (M == 2 && m == 0) {
-      x0 = xtp::glb(Dd.hT)[i0];
-      x1 = xtp::glb(Dd.hT)[i1];
-    } else {
-      x0 = to_f32(xtp::glb(erow)[i0]);
-      x1 = to_f32(xtp::glb(erow)[i1]);
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = 128 * w + 64 * k + lane;
+      const float x = (M == 2 && m == 0) ? xtp::glb(Dd.hT)[i] : to_f32(xtp::glb(erow)[i]);
+      put_split(S.xsp, SH, m, i, x * to_f32(gn0[i]));
+      if ((unsigned)(i - HPER * c.r) < (unsigned)HPER) S.xo[c.xb][m][i - HPER * c.r] = x;
+      q = fmaf(x, x, q);
     }
-    xs[m * H + i0] = x0;
-    xs[m * H + i1] = x1;
-    const float q = wave_sum(x0 * x0 + x1 * x1);
-    if (lane < NR / NW) xs[M * H + m * NR + w + NW * lane] = lane == 0 ? q : 0.f;
+    q = wave_sum(q);
+    if (lane < NR / NW) S.ss[c.xb][m * NR + w + NW * lane] = lane == 0 ? q : 0.f;
   }
   xtp::lds_barrier();
   return true;
 }
 
 template <int M>
-__device__ __forceinline__ bool cp_step(Ctx& c, const CpCall& C, Wl& R, u32x4 (&hd)[1][KQ], const u32x4 (&pj)[2], int j, int& tok,
+__device__ __forceinline__ bool cp_step(Ctx& c, const CpCall& C, Wl& R, const u32x4 (&pj)[2], int j, int& tok,
                                         int frame) {
   const KCONST CpDesc& Dd = *c.Dd;
   Smem& S = *c.S;
@@ -691,15 +635,23 @@ __device__ __forceinline__ bool cp_step(Ctx& c, const CpCall& C, Wl& R, u32x4 (&
     Next nx;
     nx.l = l + 1 < nl ? l + 1 : (j < Dd.n_ac ? 0 : -1);
     nx.head = l + 1 == nl;
-    if (!cp_layer<M>(c, R, hd, l, j, p0, nx)) return false;
+    if (!cp_layer<M>(c, R, l, j, p0, nx)) return false;
   }
-  // final RMSNorm of the last row, head j row VPER blockIdx + w, argmax
-  const float* xs = S.xs[c.xb];
-  const float sc = norm_scale(xs + M * H + (M - 1) * NR, Dd.eps);
-  float a[1][1];
-  dot_wide<1, 1>(hd, xs + (M - 1) * H, H, S.gn[2 * MAXL], a);
-  const float logit = wave_sum(a[0][0]) * sc;
-  if (C.logits && lane == 0) xtp::glb(C.logits)[(size_t)(j - 1) * V + VPER * blockIdx.x + w] = logit;
+  // final RMSNorm of the last row (its parts times the final gain are in xsp), head j rows
+  // VPER blockIdx + i (columns 8..15 of the gc tiles), argmax
+  {
+    const f32x4 a = mfma_steps<M, 4>(R.gc, S.xsp, SH, 4 * w, S.zero);
+    if (lane < 16 * M) S.part[w][0][lane] = parts_sum(a);
+  }
+  xtp::lds_barrier();
+  float logit = 0.f;
+  if (w == 0) {  // lane i < VPER: head row VPER blockIdx + i (C column VPER + i) on the last input row
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) v += S.part[ww][0][16 * (M - 1) + VPER + (lane & (VPER - 1))];
+    logit = v * norm_scale(S.ss[c.xb] + (M - 1) * NR, Dd.eps);
+    if (C.logits && lane < VPER) xtp::glb(C.logits)[(size_t)(j - 1) * V + VPER * blockIdx.x + lane] = logit;
+  }
   TTS_STAMP(42);
   const int best = argmax_exchange(c, logit);
   TTS_STAMP(43);
@@ -718,7 +670,6 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   TTS_STAMP(1);
   const int g = xtp::xcd_id(), r = blockIdx.x / NX, tid = threadIdx.x;
   Wl R;
-  u32x4 hd[1][KQ];
   u32x4 pj[2];
   // RMSNorm gains, q/k-norm gains and the RoPE factors into LDS
   {
@@ -737,13 +688,16 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
       S.rope[i / (D / 2)][0][i % (D / 2)] = xtp::glb(Dd.rope_cos)[i];
       S.rope[i / (D / 2)][1][i % (D / 2)] = xtp::glb(Dd.rope_sin)[i];
     }
+    if (tid < 8) S.zero[tid] = 0;
   }
-  // the first layer's weight rows (and the resident input-projection rows) after the small
+  // the first layer's weight tiles (and the resident input-projection tiles) after the small
   // loads above, which would otherwise wait behind them
   if (Dd.proj) issue_narrow(pj, Dd.proj, Dd.Ht, KX * g, r);
   issue_q(R, Dd, 0, g, r);
   issue_o(R, Dd, 0, g, r);
-  issue_gu(R, Dd, 0, g, r);
+  issue_gu0(R.ga, Dd, 0, g, r, 0);
+  issue_gu0(R.gb, Dd, 0, g, r, 2);
+  issue_gu1(R, Dd, 0, g, r, 0);
   issue_dn(R, Dd, 0, g, r);
   Ctx c{&Dd, &S, g, r, xtp::glb(Dd.st)->epoch, 0, 0, 0, 0, xtp::Xch{Dd.xin, Dd.xcr, Dd.err}};
   const int frame = xtp::glb(Dd.st)->frame;
@@ -752,8 +706,8 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   if (tok >= Dd.Vs) tok = Dd.Vs - 1;
   xtp::lds_barrier();
   TTS_STAMP(2);
-  bool ok = cp_step<2>(c, C, R, hd, pj, 1, tok, frame);
-  for (int j = 2; ok && j <= Dd.n_ac; ++j) ok = cp_step<1>(c, C, R, hd, pj, j, tok, frame);
+  bool ok = cp_step<2>(c, C, R, pj, 1, tok, frame);
+  for (int j = 2; ok && j <= Dd.n_ac; ++j) ok = cp_step<1>(c, C, R, pj, j, tok, frame);
   TTS_STAMP(3);
   if (blockIdx.x == 0 && tid == 0) {
     xtp::glb(Dd.st)->epoch = c.tag + 1;  // every workgroup has read the epoch: all took part in the last exchange

@@ -195,8 +195,9 @@ __device__ __forceinline__ bool barrier_any(bool fail, uint32_t tag) {
 // NPOLL: the first NPOLL threads (whole waves) poll, entry i on thread i % NPOLL; the others only
 // meet the pollers at the final barrier (waves that must not wait behind their own outstanding
 // weight loads). n <= KMAX * NPOLL.
-template <int KMAX, int NPOLL = NT, typename At>
-__device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t* err, At at) {
+// get_each hands each value to store(i, value) as it arrives instead.
+template <int KMAX, int NPOLL = NT, typename At, typename Store>
+__device__ __forceinline__ bool get_each(int n, uint32_t tag, uint32_t* err, At at, Store store) {
   const int tid = fresh_tid();
   unsigned pend = 0;
   if (NPOLL == NT || tid < NPOLL) {
@@ -213,7 +214,7 @@ __device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
       if ((pend & (1u << k)) && tagof(v[k]) == tag) {
-        lds[tid + k * NPOLL] = valof(v[k]);
+        store(tid + k * NPOLL, valof(v[k]));
         pend &= ~(1u << k);
       }
     if (!__any(pend != 0)) break;
@@ -230,6 +231,11 @@ __device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t
     return false;
   }
   return true;
+}
+
+template <int KMAX, int NPOLL = NT, typename At>
+__device__ __forceinline__ bool get_at(int n, uint32_t tag, float* lds, uint32_t* err, At at) {
+  return get_each<KMAX, NPOLL>(n, tag, err, at, [&](int i, float v) { lds[i] = v; });
 }
 
 // Gather the n contiguous entries src[0 .. n) (see get_at).

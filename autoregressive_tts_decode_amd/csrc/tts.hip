@@ -75,7 +75,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout, computed identically by tts_workspace_bytes and tts_create.
 struct Layout {
   size_t st, tk, tv, ck, cv, tcos, tsin, ccos, csin, x, qkv, attn, h, part, counters, logits, hT, cx, clog, next_tok,
-      sem_tok, ac_codes, history, kvstart, aids, cpdesc, tkdesc, cpdesc_s, tkdesc_s, px, pqkv, pq, po, pgu, ph, ps, pks, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
+      sem_tok, ac_codes, history, kvstart, aids, ptab, cpdesc, tkdesc, cpdesc_s, tkdesc_s, px, pqkv, pq, po, pgu, ph, ps, pks, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
   int nsplit;
 };
 
@@ -85,6 +85,11 @@ size_t tab_bytes(const tts_config& c) { return c.weight_dtype == TTS_DTYPE_F32 ?
 // Elements per 16-byte lane load of the matrices.
 int mat_per_unit(const tts_config& c) { return (int)(16 / mat_bytes(c)); }
 size_t kv_bytes(const tts_config&) { return 4; }
+
+bool xcp_capable(const tts_config& c);
+// The lean CodePredictor kernel with an input projection P reads step j >= 2's input row from the
+// table of projected codebook rows P E_ac[j - 2][a] (fp32), formed once per weight binding.
+bool wants_proj_table(const tts_config& c) { return xcp_capable(c) && c.talker.hidden != c.codepred.hidden; }
 
 Layout make_layout(const tts_config& c) {
   Layout L{};
@@ -123,6 +128,7 @@ Layout make_layout(const tts_config& c) {
   L.history = take(B * t.vocab);
   L.kvstart = take(B * 4);
   L.aids = take((size_t)B * cap * 4);
+  L.ptab = take(wants_proj_table(c) ? (size_t)c.n_acoustic * p.vocab * p.hidden * 4 : 0);
   // GEMM prefill: one chunk of up to kPrefillChunk positions per stream
   {
     const size_t Mp = B * kPrefillChunk;
@@ -1271,6 +1277,16 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
     D.nq = p.n_q_heads; D.nkv = p.n_kv_heads; D.d = p.head_dim; D.n_ac = c.n_acoustic; D.eps = c.rms_eps;
     D.final_norm = ctx->cp.final_norm; D.heads = ctx->heads; D.proj = ctx->proj; D.embed_ac = ctx->embed_ac;
     D.embed_sem = ctx->embed_sem;
+    D.ptab = nullptr;
+    if (ctx->xcp_ok && ctx->proj && wants_proj_table(c)) {
+      // projected codebook rows P E_ac[j][a] for steps 2..15 of the lean CodePredictor kernel
+      float* T = (float*)(ctx->ws + ctx->L.ptab);
+      const int R = c.n_acoustic * p.vocab, N = p.hidden, K = c.talker.hidden;
+      hipLaunchKernelGGL(k_proj_table, dim3(N / 64, (R + 63) / 64), dim3(256), 0, ctx->stream, (const uint16_t*)ctx->embed_ac,
+                         (const uint16_t*)ctx->proj, T, R, N, K);
+      HIP_LAUNCH_CHECK();
+      D.ptab = T;
+    }
     D.rope_cos = ctx->ccos; D.rope_sin = ctx->csin;
     D.hT = ctx->hT;
     D.xin = (xtp::u64*)(ctx->ws + ctx->L.xin); D.xcr = (xtp::u64*)(ctx->ws + ctx->L.xcr);

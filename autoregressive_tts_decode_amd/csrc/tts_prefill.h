@@ -172,6 +172,44 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
       }
 }
 
+// Rows of a bf16 table E [R][K] through a bias-free bf16 projection P [N][K]: T[a][i] =
+// sum_k E[a][k] P[i][k] in fp32 (T [R][N]). A product of two bf16 values is exact in fp32 and k
+// runs in order, so T holds P E[a] up to the order of its sums, the same on every run. One 64 x 64
+// tile of T per workgroup (16 x 16 threads, 4 x 4 outputs each); K % 32 == 0. Weight preparation,
+// run once per weight binding.
+__global__ __launch_bounds__(256) void k_proj_table(const uint16_t* E, const uint16_t* P, float* T, int R, int N, int K) {
+  __shared__ float Es[32][65];  // [k][row of the tile]
+  __shared__ float Ps[32][65];  // [k][column of the tile]
+  const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  float acc[4][4];
+  for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 4; ++q) acc[i][q] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += 32) {
+    for (int e = tid; e < 64 * 32; e += 256) {
+      const int rr = e / 32, kk = e % 32;
+      Es[kk][rr] = r0 + rr < R ? to_f32(E[(size_t)(r0 + rr) * K + k0 + kk]) : 0.f;
+      Ps[kk][rr] = c0 + rr < N ? to_f32(P[(size_t)(c0 + rr) * K + k0 + kk]) : 0.f;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < 32; ++kk) {
+      float a[4], b[4];
+      for (int i = 0; i < 4; ++i) {
+        a[i] = Es[kk][tr + 16 * i];
+        b[i] = Ps[kk][tc + 16 * i];
+      }
+      for (int i = 0; i < 4; ++i)
+        for (int q = 0; q < 4; ++q) acc[i][q] = fmaf(a[i], b[q], acc[i][q]);
+    }
+    __syncthreads();
+  }
+  for (int i = 0; i < 4; ++i)
+    for (int q = 0; q < 4; ++q) {
+      const int row = r0 + tr + 16 * i, col = c0 + tc + 16 * q;
+      if (row < R && col < N) T[(size_t)row * N + col] = acc[i][q];
+    }
+}
+
 // C[m][n] = (add ? C[m][n] : 0) + part[0][m][n] + part[1][m][n] + ... + part[ks - 1][m][n], the
 // slices added in that order (N a multiple of 4; four columns per thread).
 __global__ __launch_bounds__(256) void k_splitk_reduce(float* C, int ldc, const float* part, int M, int N, int ks, int add) {

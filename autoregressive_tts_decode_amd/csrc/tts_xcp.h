@@ -559,9 +559,11 @@ __device__ __forceinline__ int argmax_exchange(Ctx& c, float logit) {
 }
 
 // Step j's input rows: this rank's elements into xo[xb], the sums of squares into ss[xb], and the
-// rows times the first layer's attention gain, in parts, into xsp. With an input projection its K
-// is split across the XCDs (the resident tiles pj), then a reduce-scatter + all-gather; without
-// one the rows are read as they are. M = 2 at step 1 (h_T and E_sem[tok]), else E_ac[j - 1][tok].
+// rows times the first layer's attention gain, in parts, into xsp. M = 2 at step 1 (h_T and
+// E_sem[tok]), else E_ac[j - 1][tok]. With an input projection P, step 1 splits its K across the
+// XCDs (the resident tiles pj), then a reduce-scatter + all-gather; steps 2..15 read the row
+// P E_ac[j - 1][tok] of the projected table (a linear map of a table row is that row of the mapped
+// table), which saves that exchange. Without a projection the rows are read as they are.
 template <int M>
 __device__ __forceinline__ bool step_input(Ctx& c, const u32x4 (&pj)[2], int j, int tok) {
   const KCONST CpDesc& Dd = *c.Dd;
@@ -572,7 +574,9 @@ __device__ __forceinline__ bool step_input(Ctx& c, const u32x4 (&pj)[2], int j, 
                                : reinterpret_cast<const uint16_t*>(Dd.embed_ac) + (size_t)(j - 2) * V * Ht;
   const uint16_t* erow = tab + (size_t)tok * Ht;
   const uint16_t* gn0 = S.gn[0];
-  if (Dd.proj) {
+  // steps 2..15 with a projection: the projected codebook row P E_ac[j - 2][tok] from the table
+  const float* trow = M == 1 && Dd.ptab ? Dd.ptab + ((size_t)(j - 2) * V + tok) * H : nullptr;
+  if (Dd.proj && !trow) {
     // this XCD's 256 columns of each input row, in parts
     if (tid < KX) {
       const int c0 = KX * c.g + tid;
@@ -600,15 +604,16 @@ __device__ __forceinline__ bool step_input(Ctx& c, const u32x4 (&pj)[2], int j, 
         },
         [] {});
   }
-  // no projection (Talker hidden = CodePredictor hidden): the rows as they are; the sums of
-  // squares in the layout an all-gather leaves them (one per wave here, the other slots zero)
+  // no projection (Talker hidden = CodePredictor hidden), or a projected table row: the rows as
+  // they are; the sums of squares in the layout an all-gather leaves them (one per wave here, the
+  // other slots zero)
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     float q = 0.f;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int i = 128 * w + 64 * k + lane;
-      const float x = (M == 2 && m == 0) ? xtp::glb(Dd.hT)[i] : to_f32(xtp::glb(erow)[i]);
+      const float x = (M == 2 && m == 0) ? xtp::glb(Dd.hT)[i] : trow ? xtp::glb(trow)[i] : to_f32(xtp::glb(erow)[i]);
       put_split(S.xsp, SH, m, i, x * to_f32(gn0[i]));
       if ((unsigned)(i - HPER * c.r) < (unsigned)HPER) S.xo[c.xb][m][i - HPER * c.r] = x;
       q = fmaf(x, x, q);

@@ -94,6 +94,7 @@ struct CpDesc {
   int32_t n_layers, H, Ht, F, V, Vs, nq, nkv, d, n_ac;
   float eps;
   const void *final_norm, *heads, *proj, *embed_ac, *embed_sem;
+  const float* ptab;                 // [n_ac][V][H] projected codebook rows P E_ac[j][a], or null
   const float *rope_cos, *rope_sin;  // [16][d/2]
   const float* hT;                   // [Ht] pending Talker hidden (final-normed)
   u64 *xin, *xcr, *cand;

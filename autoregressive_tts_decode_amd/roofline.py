@@ -121,7 +121,7 @@ _CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 _PROFILES = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles")
 
 
-def kernel_source_sha256(files=("tts_xtp.h", "tts_device.h")) -> str:
+def kernel_source_sha256(files=("tts_xcp.h", "tts_xtp.h", "tts_device.h")) -> str:
     """SHA-256 over the sources a persistent kernel is built from (in the given order)."""
     h = hashlib.sha256()
     for f in files:
@@ -130,7 +130,7 @@ def kernel_source_sha256(files=("tts_xtp.h", "tts_device.h")) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(record: str, files=("tts_xtp.h", "tts_device.h")) -> int | None:
+def measured_traffic(record: str, files=("tts_xcp.h", "tts_xtp.h", "tts_device.h")) -> int | None:
     """HBM bytes per launch from a committed counter record, or None when there is none or the
     kernel's sources changed since the counters were taken.
 

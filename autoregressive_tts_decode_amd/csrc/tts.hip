@@ -75,7 +75,7 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout, computed identically by tts_workspace_bytes and tts_create.
 struct Layout {
   size_t st, tk, tv, ck, cv, tcos, tsin, ccos, csin, x, qkv, attn, h, part, counters, logits, hT, cx, clog, next_tok,
-      sem_tok, ac_codes, history, kvstart, aids, ptab, cpdesc, tkdesc, cpdesc_s, tkdesc_s, px, pqkv, pq, po, pgu, ph, ps, pks, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
+      sem_tok, ac_codes, history, kvstart, aids, ptab, cpdesc, tkdesc, cpdesc_s, tkdesc_s, px, pqkv, pq, po, pgu, ph, ps, pks, ssq, xin, xcr, cand, att, xerr, xzero_begin, xzero_end, total;
   int nsplit;
 };
 
@@ -143,6 +143,8 @@ Layout make_layout(const tts_config& c) {
     // split-K partial tiles: a split GEMM has at most kGemmWgs (row tile, column tile, K slice)
     // workgroups, each writing one 64 x 64 fp32 tile
     L.pks = take((size_t)kGemmWgs * kGBM * kGBN * 4);
+    // per-row, per-256-column chunk sums of squares a residual GEMM leaves for the next RMSNorm
+    L.ssq = take(Mp * ((hmax + 255) / 256) * 4);
   }
   // persistent kernels: descriptors and exchange buffers (the CodePredictor's K/V rows stay in LDS)
   L.cpdesc = take(sizeof(xtp::CpDesc));
@@ -294,6 +296,10 @@ struct tts_ctx {
   const void *embed_text = nullptr, *embed_sem = nullptr, *lm_head = nullptr, *proj = nullptr, *embed_ac = nullptr,
              *heads = nullptr;
   bool weights_ok = false;
+  const float* ptab = nullptr;  // projected codebook rows P E_ac[j][a] (fp32), when formed
+  // rows whose chunk sums of squares sit in the ssq buffer (the last ssq_out GEMM's output), or null
+  const float* ssq_x = nullptr;
+  int ssq_stride = 0, ssq_rows = 0, ssq_K = 0;
   // streaming text of the frame loop (tts_set_text_stream): ids [B, text_n], borrowed
   const int32_t* text_ids = nullptr;
   int text_n = 0, text_next = 0;
@@ -534,7 +540,7 @@ int gemv(tts_ctx* ctx, GemvArgs a) {
 // and the gain applied while A is loaded; the residual as C += result; SwiGLU through a staging
 // buffer; gathered input rows staged first). Needs bf16 weights and 64-multiple row segments.
 int gather(tts_ctx* ctx, int src, int M, int H, const float* vec, int vec_stride, const void* table, int table_rows, TokRef tok,
-           float* out, int out_stride);
+           float* out, int out_stride, bool f32_table = false);
 
 bool gemm_routes(const tts_ctx* ctx, const GemvArgs& a) {
   if (!ctx->pgemm_ok || !(ctx->bf16() || ctx->fp8()) || a.M < kGemmMinRows || a.K % kGBK) return false;
@@ -562,7 +568,11 @@ int launch_gemm(tts_ctx* ctx, GemmArgs g, dim3 grid) {
 
 int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
   char* w = ctx->ws;
-  float *X = (float*)(w + ctx->L.px), *GU = (float*)(w + ctx->L.pgu), *RS = (float*)(w + ctx->L.ps);
+  float *X = (float*)(w + ctx->L.px), *GU = (float*)(w + ctx->L.pgu), *RS = (float*)(w + ctx->L.ps),
+        *SSQ = (float*)(w + ctx->L.ssq);
+  // RMSNorm scales from the sums of squares the residual GEMM that wrote these rows left behind
+  const bool use_ssq = a.gain && a.ssq_in && a.src == SRC_VEC && !a.xn_out && ctx->ssq_x == a.x &&
+                       ctx->ssq_stride == a.x_stride && ctx->ssq_rows == a.M && ctx->ssq_K == a.K;
   const float* A = a.x;
   int lda = a.x_stride;
   if (a.src != SRC_VEC) {
@@ -590,7 +600,9 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
   g.part = (float*)(w + ctx->L.pks);
   if (ks > 1 && (size_t)ks * tiles > (size_t)kGemmWgs)
     return ctx->fail(TTS_E_STATE, "gemm: %d K slices of %d tiles exceed the partial-tile buffer", ks, tiles);
-  if (a.gain) {
+  if (use_ssq) {
+    g.rs = nullptr; g.ssq = SSQ; g.nchunk = (a.K + 255) / 256; g.eps = ctx->cfg.rms_eps;
+  } else if (a.gain) {
     hipLaunchKernelGGL(k_rowscale, dim3((a.M + 3) / 4), dim3(256), 0, ctx->stream, A, lda, a.M, a.K, ctx->cfg.rms_eps, RS);
     HIP_LAUNCH_CHECK();
     if (a.xn_out) {
@@ -600,15 +612,26 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
   }
   if (int rc = launch_gemm(ctx, g, dim3(N / kGBN, (a.M + kGBM - 1) / kGBM, ks))) return rc;
   HIP_LAUNCH_CHECK();
-  if (ks > 1) {
-    const size_t q = (size_t)a.M * N / 4;
-    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)std::min<size_t>((q + 255) / 256, 2048)), dim3(256), 0, ctx->stream, g.C,
-                       g.ldc, g.part, a.M, N, ks, g.add);
+  const bool ssq_out = a.ssq_out && a.epi == EPI_RESID;
+  if (a.epi == EPI_SWIGLU) {
+    // the slices' gate and up sums meet in the SwiGLU pass (no separate reduction)
+    if (ks > 1)
+      hipLaunchKernelGGL(k_splitk_swiglu, dim3(std::min((a.M * a.N + 255) / 256, 4096)), dim3(256), 0, ctx->stream, g.part, a.M,
+                         a.N, ks, a.y, a.y_stride);
+    else
+      hipLaunchKernelGGL(k_swiglu_rows, dim3(std::min((a.M * a.N + 255) / 256, 4096)), dim3(256), 0, ctx->stream, GU, a.M, a.N, a.y);
+    HIP_LAUNCH_CHECK();
+  } else if (ks > 1 || ssq_out) {
+    // slices added in order (with the residual first); a residual GEMM also leaves the new rows'
+    // sums of squares for the RMSNorm of the GEMM that reads them next
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((N + 255) / 256, a.M), dim3(256), 0, ctx->stream, g.C, g.ldc, g.part, a.M, N,
+                       ks > 1 ? ks : 0, ks > 1 ? g.add : 1, ssq_out ? SSQ : nullptr);
     HIP_LAUNCH_CHECK();
   }
-  if (a.epi == EPI_SWIGLU) {
-    hipLaunchKernelGGL(k_swiglu_rows, dim3(std::min((a.M * a.N + 255) / 256, 4096)), dim3(256), 0, ctx->stream, GU, a.M, a.N, a.y);
-    HIP_LAUNCH_CHECK();
+  if (ssq_out) {
+    ctx->ssq_x = a.y; ctx->ssq_stride = a.y_stride; ctx->ssq_rows = a.M; ctx->ssq_K = N;
+  } else if (a.y == ctx->ssq_x) {
+    ctx->ssq_x = nullptr;
   }
   if (a.bump_pos || a.bump_frame) {
     hipLaunchKernelGGL(k_bump_state, dim3(1), dim3(64), 0, ctx->stream, ctx->st, a.bump_pos, a.bump_frame);
@@ -617,7 +640,11 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
   return TTS_OK;
 }
 
-int proj(tts_ctx* ctx, GemvArgs a) { return gemm_routes(ctx, a) ? proj_gemm(ctx, a) : gemv(ctx, a); }
+int proj(tts_ctx* ctx, GemvArgs a) {
+  if (gemm_routes(ctx, a)) return proj_gemm(ctx, a);
+  ctx->ssq_x = nullptr;  // the GEMV leaves no sums of squares
+  return gemv(ctx, a);
+}
 
 // ---------------------------------------------------------------------------- attention dispatch
 
@@ -691,10 +718,12 @@ int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_c
   const int qkv_n = qd + 2 * kd;
   // per-layer cache stride uses the allocated stream capacity, not the live batch
   const size_t layer_cache = (size_t)ctx->cfg.max_batch * c.n_kv_heads * cap * c.head_dim * ctx->kvb();
+  ctx->ssq_x = nullptr;  // x was written outside this stack
   for (int l = 0; l < c.n_layers; ++l) {
     const Layer& W = S.layers[l];
-    // RMSNorm + QKV
+    // RMSNorm + QKV (after layer 0 the previous down projection left x's sums of squares)
     GemvArgs a = gemv_args(ctx);
+    a.ssq_in = l > 0;
     a.w[0] = W.wq; a.w[1] = W.wk; a.w[2] = W.wv;
     a.seg_rows[0] = qd; a.seg_rows[1] = kd; a.seg_rows[2] = kd;
     a.nseg = 3; a.N = qkv_n; a.K = c.hidden; a.M = rows;
@@ -720,9 +749,11 @@ int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_c
     a.w[0] = W.wo; a.seg_rows[0] = c.hidden; a.N = c.hidden; a.K = qd; a.M = rows;
     a.src = SRC_VEC; a.x = ctx->attn; a.x_stride = qd;
     a.y = x; a.y_stride = c.hidden; a.res = x; a.res_stride = c.hidden; a.epi = EPI_RESID; a.nontemporal = nontemporal;
+    a.ssq_out = 1;
     if (int rc_ = proj(ctx, a)) return rc_;
     // RMSNorm + gate/up + SwiGLU
     a = gemv_args(ctx);
+    a.ssq_in = 1;
     a.w[0] = W.wg; a.w[1] = W.wu; a.seg_rows[0] = c.ffn; a.seg_rows[1] = c.ffn; a.nseg = 2;
     a.N = c.ffn; a.K = c.hidden; a.M = rows;
     a.src = SRC_VEC; a.x = x; a.x_stride = c.hidden; a.gain = W.mlp_norm;
@@ -733,6 +764,7 @@ int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_c
     a.w[0] = W.wd; a.seg_rows[0] = c.hidden; a.N = c.hidden; a.K = c.ffn; a.M = rows;
     a.src = SRC_VEC; a.x = ctx->h; a.x_stride = c.ffn;
     a.y = x; a.y_stride = c.hidden; a.res = x; a.res_stride = c.hidden; a.epi = EPI_RESID; a.nontemporal = nontemporal;
+    a.ssq_out = 1;
     if (int rc_ = proj(ctx, a)) return rc_;
   }
   return TTS_OK;
@@ -850,13 +882,14 @@ int embed_sum(tts_ctx* ctx, int B, const TokRef* refs, const TokRef* text = null
 }
 
 int gather(tts_ctx* ctx, int src, int M, int H, const float* vec, int vec_stride, const void* table, int table_rows, TokRef tok,
-           float* out, int out_stride) {
+           float* out, int out_stride, bool f32_table) {
   GatherArgs g;
   std::memset(&g, 0, sizeof g);
   g.src = src; g.M = M; g.H = H; g.vec = vec; g.vec_stride = vec_stride; g.table = table; g.table_rows = table_rows; g.tok = tok;
   g.x = out; g.x_stride = out_stride; g.st = ctx->st;
+  if (out == ctx->ssq_x) ctx->ssq_x = nullptr;
   const int gx = (H + 255) / 256;
-  if (ctx->tab16()) hipLaunchKernelGGL(k_gather<uint16_t>, dim3(gx, M), dim3(256), 0, ctx->stream, g);
+  if (ctx->tab16() && !f32_table) hipLaunchKernelGGL(k_gather<uint16_t>, dim3(gx, M), dim3(256), 0, ctx->stream, g);
   else hipLaunchKernelGGL(k_gather<float>, dim3(gx, M), dim3(256), 0, ctx->stream, g);
   HIP_LAUNCH_CHECK();
   return TTS_OK;
@@ -943,7 +976,12 @@ int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac,
     } else {
       const void* table = (const char*)ctx->embed_ac + (size_t)(j - 2) * ac_table;
       TokRef prev = tokref(ctx->next_tok, 1, 0, 0, 0);
-      if (ctx->proj) {
+      if (ctx->ptab) {
+        // the projected row P E_ac[j - 2][a] from the table (a linear map of a row is that row of
+        // the mapped table)
+        if (int rc = gather(ctx, SRC_TABLE, B, Hc, nullptr, 0, ctx->ptab + (size_t)(j - 2) * Va * Hc, Va, prev, ctx->cx, Hc, true))
+          return rc;
+      } else if (ctx->proj) {
         GemvArgs a = gemv_args(ctx);
         a.w[0] = ctx->proj; a.seg_rows[0] = Hc; a.N = Hc; a.K = Ht; a.M = B;
         a.src = SRC_TABLE; a.table = table; a.table_rows = Va; a.tok = prev;
@@ -960,6 +998,7 @@ int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac,
     GemvArgs a = gemv_args(ctx);
     a.w[0] = (const char*)ctx->heads + (size_t)(j - 1) * head_sz; a.seg_rows[0] = Va; a.N = Va; a.K = Hc; a.M = B;
     a.src = SRC_VEC; a.x = ctx->cx + (size_t)(Mp - 1) * Hc; a.x_stride = Mp * Hc; a.gain = ctx->cp.final_norm;
+    a.ssq_in = 1;  // used when these are the rows the last down projection wrote (Mp = 1)
     float* lg = logits_out ? logits_out + (size_t)(j - 1) * Va : ctx->clog;
     a.y = lg; a.y_stride = logits_out ? c.n_acoustic * Va : Va; a.epi = EPI_STORE;
     if (int rc = proj(ctx, a)) return rc;
@@ -1250,6 +1289,7 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
   }
   ctx->weights_ok = true;
   ctx->prefilled = false;
+  ctx->ptab = nullptr;
   drop_graph(ctx);
   if (ctx->xtp_ok) {
     xtp::CpDesc D;
@@ -1287,6 +1327,7 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
       HIP_LAUNCH_CHECK();
       D.ptab = T;
     }
+    ctx->ptab = D.ptab;
     D.rope_cos = ctx->ccos; D.rope_sin = ctx->csin;
     D.hT = ctx->hT;
     D.xin = (xtp::u64*)(ctx->ws + ctx->L.xin); D.xcr = (xtp::u64*)(ctx->ws + ctx->L.xcr);

@@ -183,6 +183,8 @@ struct GemvArgs {
   float* xn_out;            // optional: wave 0 writes the normalised input rows here
   int32_t xn_stride;
   int32_t nontemporal;      // stream the weights past the caches (read once per frame)
+  int32_t ssq_out;          // EPI_RESID GEMM: also leave the new rows' chunk sums of squares
+  int32_t ssq_in;           // RMSNorm GEMM whose input rows are the last ssq_out rows, unchanged
   int32_t bump_pos, bump_frame;  // added to the device counters by block 0 (it reads no counter)
   DevState* st;
 };

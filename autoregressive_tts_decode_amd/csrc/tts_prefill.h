@@ -37,6 +37,9 @@ struct GemmArgs {
                       // stride N) and k_splitk_reduce adds the slices into C in slice order, so the
                       // sum is the same on every run
   float* part;
+  const float* ssq;   // or: the row scales come from per-chunk sums of squares of A's rows,
+  int nchunk;         // ssq[m * nchunk + c] for 256-column chunks c (added in chunk order)
+  float eps;
 };
 
 constexpr int kGBM = 64, kGBN = 64, kGBK = 64, kGLD = kGBK + 8;  // tile, LDS row stride (bf16)
@@ -60,7 +63,12 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
   const bool split = a.kslice < a.K;
   const int lr = tid >> 2, lk = (tid & 3) * 16;  // loader: row lr of the tile, 16 k from lk
   const bool arow = m0 + lr < a.M;
-  const float rsc = (a.rs && arow) ? a.rs[m0 + lr] : 1.f;
+  float rsc = (a.rs && arow) ? a.rs[m0 + lr] : 1.f;
+  if (a.ssq && arow) {
+    float q = 0.f;
+    for (int c = 0; c < a.nchunk; ++c) q += a.ssq[(size_t)(m0 + lr) * a.nchunk + c];
+    rsc = 1.0f / sqrtf(q / (float)a.K + a.eps);
+  }
   const float* Ap = a.A + (size_t)(m0 + lr) * a.lda + lk;
   const char* Wp = W + ((size_t)lr * a.K + lk) * WB;
   const uint16_t* gp = reinterpret_cast<const uint16_t*>(a.gain);
@@ -211,18 +219,40 @@ __global__ __launch_bounds__(256) void k_proj_table(const uint16_t* E, const uin
 }
 
 // C[m][n] = (add ? C[m][n] : 0) + part[0][m][n] + part[1][m][n] + ... + part[ks - 1][m][n], the
-// slices added in that order (N a multiple of 4; four columns per thread).
-__global__ __launch_bounds__(256) void k_splitk_reduce(float* C, int ldc, const float* part, int M, int N, int ks, int add) {
-  const int q4 = N / 4;
-  const size_t n = (size_t)M * q4;
-  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < n; q += (size_t)gridDim.x * blockDim.x) {
-    const size_t m = q / q4, c = 4 * (q % q4);
-    float4 v = add ? *reinterpret_cast<const float4*>(C + m * ldc + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+// slices added in that order; one row chunk of 256 columns per workgroup (grid: chunks x M). With
+// ssq, also the chunk's sum of squares of the new row, ssq[m * gridDim.x + chunk] (a fixed-order
+// reduction), which the next RMSNorm reads instead of a pass of its own over the row.
+__global__ __launch_bounds__(256) void k_splitk_reduce(float* C, int ldc, const float* part, int M, int N, int ks, int add,
+                                                       float* ssq) {
+  __shared__ float wsum[4];
+  const int m = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
+  float v = 0.f;
+  if (n < N) {
+    v = add ? C[(size_t)m * ldc + n] : 0.f;
+    for (int z = 0; z < ks; ++z) v += part[((size_t)z * M + m) * N + n];
+    C[(size_t)m * ldc + n] = v;
+  }
+  if (ssq) {
+    const float q = wave_sum(v * v);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = q;
+    __syncthreads();
+    if (threadIdx.x == 0) ssq[(size_t)m * gridDim.x + blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  }
+}
+
+// h[m][f] = silu(sum_z part[z][m][f]) * sum_z part[z][m][F + f] (slices in order; part rows hold
+// the F gate columns, then the F up columns).
+__global__ __launch_bounds__(256) void k_splitk_swiglu(const float* part, int M, int F, int ks, float* h, int ldh) {
+  const size_t n = (size_t)M * F;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < n; idx += (size_t)gridDim.x * blockDim.x) {
+    const size_t m = idx / F, f = idx % F;
+    float g = 0.f, u = 0.f;
     for (int z = 0; z < ks; ++z) {
-      const float4 p = *reinterpret_cast<const float4*>(part + ((size_t)z * M + m) * N + c);
-      v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
+      const float* row = part + ((size_t)z * M + m) * 2 * F;
+      g += row[f];
+      u += row[F + f];
     }
-    *reinterpret_cast<float4*>(C + m * ldc + c) = v;
+    h[m * ldh + f] = silu(g) * u;
   }
 }
 

@@ -19,6 +19,7 @@
 //     (up to 96 KB) are copied straight into LDS during the attention.
 #pragma once
 
+#include "tts_trace.h"
 #include "tts_xtp.h"
 
 namespace tts {
@@ -384,6 +385,7 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
     bg(0);
   }
   lds_barrier();
+  TTS_STAMP(53);
   // this rank's chunk [t0, t1) of positions 0..p; each front wave takes 16 positions per pass
   const int n = p + 1, C = (n + NR - 1) / NR;
   const int t0 = r * C, t1 = min(t0 + C, n);
@@ -453,6 +455,7 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
     bg(1);
   }
   lds_barrier();
+  TTS_STAMP(54);
   // this rank's partial: combine the front waves; publish (max, sum, 128 outputs) per head
   ++tag;
   u64* slot = D.att + (((size_t)g * 2 + (apar & 1)) * NR + r) * ATS;
@@ -478,6 +481,7 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
   } else {
     bg(2);
   }
+  TTS_STAMP(55);
   // rank r combines outputs [8 * (r % 16), +8) of head r / 16 from the 32 ranks' partials
   const int hb = r >> 4, db = 8 * (r & 15);
   const u64* base = D.att + ((size_t)g * 2 + (apar & 1)) * NR * ATS;
@@ -486,6 +490,7 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
         return base + (size_t)s * ATS + hb * 130 + (k < 2 ? k : 2 + db + (k - 2));
       }))
     return false;
+  TTS_STAMP(56);
   ++apar;
   if (!slice_gather<1, 1, PF>(X, 8, 256, [&](int k, int) {
         float mx = -INFINITY;
@@ -519,6 +524,8 @@ template <typename WT>
 __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   const KCONST TkDesc& D = *(const KCONST TkDesc*)C.desc;
   __shared__ TkSmem S;
+  TTS_TRACE_BEGIN(2048);
+  TTS_STAMP(49);
   const Xch X{D.xin, D.xcr, D.err};
   constexpr int KT = (THMAX + NR + PF - 1) / PF;  // intra gather of a residual row + sums of squares
   constexpr int KQ = (512 + PF - 1) / PF;         // intra gather of the q/k/v slices
@@ -557,6 +564,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   for (int l = 0; ok && l < D.n_layers; ++l) {
     const KCONST LayerW& W = D.layer[l];
     const bool last = l + 1 == D.n_layers;
+    TTS_STAMP(50);
     // q/k/v slice (A0: X0, A1: X1); the output projection rows (C0, C1) follow in their place
     tk_rmsnorm(S.xs, H, c.an, D.eps, S.xn, S.red, l > 0 ? S.xs + H : nullptr);
     wb_dot<WT, 2, 4>(X0, qh, H, S.xn, S.out);
@@ -565,11 +573,13 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     tk_issue_c<WT>(X1, D, W, 1, g, r);
     gu.part(S.lw, 4);
     lds_barrier();
+    TTS_STAMP(51);
     if (!slice_gather<1, KQ, PF>(X, qper, qrows, [&](int e, int) { return S.out[e]; }, S.qkv, tag, iring, g, r,
                                  [&] { gu.part(S.lw, 6); })) {
       ok = false;
       break;
     }
+    TTS_STAMP(52);
     if (!tk_attention<WT>(D, X, l, p, c, rc, rs, S, tag, iring, apar, g, r, [&](int k) {
           if (k == 3) gu.part(S.lw, 1 << 20);
           else gu.part(S.lw, k == 1 ? 6 : 4);
@@ -577,17 +587,20 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
       ok = false;
       break;
     }
+    TTS_STAMP(57);
     // output projection partial (C0: X0, C1: X1), residual; the register gate/up chunks follow
     // (D0 now, D1 during the exchange)
     wb_dot<WT, 8, 1>(X0, hh, G * d, S.ob, S.out);
     tk_issue_d<WT>(X0, D, W, nl, 0, g, r);
     wb_dot<WT, 8, 1>(X1, hh, G * d, S.ob, S.out + hh);
     lds_barrier();
+    TTS_STAMP(58);
     if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r,
                                          [&] { tk_issue_d<WT>(X1, D, W, nl, 1, g, r); })) {
       ok = false;
       break;
     }
+    TTS_STAMP(59);
     // gate and up rows (LDS block, then D0: X0, D1: X1), SwiGLU. Once the LDS block is read the
     // front waves copy the down rows in its place (half now, half during the SwiGLU exchange)
     // and the back waves, their registers free, start on the next layer's q/k/v rows (or the
@@ -597,6 +610,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     lds_barrier();
     tk_dot_lds<WT, 4, 4>(S.lw, nl, H, S.xn, S.out);
     lds_barrier();
+    TTS_STAMP(60);
     const int dparts = (hper * (fx / 8) / 64 + 2 * NF - 1) / (2 * NF);  // first half, per front wave
     if (wave < NF) {
       dn.begin(reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r) * D.F + fx * g, nullptr, hper, D.F, hper, fx / 8);
@@ -610,6 +624,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
       tk_next_consts<WT>(c, D, l, tid);
     }
     lds_barrier();
+    TTS_STAMP(61);
     if (!slice_gather<1, KH, PF>(X, fper, fx, [&](int e, int) { return silu(S.out[e]) * S.out[fper + e]; }, S.hb, tag,
                                  iring, g, r, [&] {
                                    if (wave < NF) {
@@ -624,10 +639,12 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     }
     // down projection partial from LDS, residual; the next layer's LDS gate/up block starts
     // during the exchange
+    TTS_STAMP(62);
     if (wave < NF) wait_loads();
     lds_barrier();
     tk_dot_lds<WT, 2, 8>(S.lw, hper, fx, S.hb, S.out);
     lds_barrier();
+    TTS_STAMP(63);
     if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] {
           if (!last) {
             gu_begin(D.layer[l + 1]);
@@ -638,6 +655,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
       break;
     }
   }
+  TTS_STAMP(64);
   if (ok) {
     // final norm (gains in c.an), semantic head slice (F0: X0, F1: X1)
     tk_rmsnorm(S.xs, H, c.an, D.eps, S.xn, S.red, S.xs + H);
@@ -649,6 +667,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     if (blockIdx.x == 0)
       for (int i = tid; i < H; i += NT) glb(D.hT)[i] = S.xn[i];
   }
+  TTS_STAMP(65);
   if (blockIdx.x == 0 && tid == 0) {
     // every workgroup has read the counters: all took part in the last exchange
     GLB DevState* st = glb(D.st);

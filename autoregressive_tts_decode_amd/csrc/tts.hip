@@ -87,6 +87,19 @@ int mat_per_unit(const tts_config& c) { return (int)(16 / mat_bytes(c)); }
 size_t kv_bytes(const tts_config&) { return 4; }
 
 bool xcp_capable(const tts_config& c);
+
+// K split of the decode GEMM (k_gemm_dec) for N output rows, K columns and M input rows: slices of
+// at most 256 columns (128 past 32 rows: the LDS holds the slice's A rows in three parts), more
+// of them while the grid has fewer than 256 workgroups; returns the slice count.
+int dec_split(int N, int K, int M, int* kslice) {
+  const int kmax = M <= 32 ? 256 : 128, tiles = N / 64;
+  const int ks_min = (K + kmax - 1) / kmax;
+  const int want = std::max(1, (256 + tiles - 1) / tiles);
+  int ks = std::max(ks_min, std::min(want, K / 64));
+  const int ksl = ((K / 64 + ks - 1) / ks) * 64;
+  *kslice = ksl;
+  return (K + ksl - 1) / ksl;
+}
 // The lean CodePredictor kernel with an input projection P reads step j >= 2's input row from the
 // table of projected codebook rows P E_ac[j - 2][a] (fp32), formed once per weight binding.
 bool wants_proj_table(const tts_config& c) { return xcp_capable(c) && c.talker.hidden != c.codepred.hidden; }
@@ -141,8 +154,23 @@ Layout make_layout(const tts_config& c) {
     L.ph = take(Mp * t.ffn * 4);
     L.ps = take(Mp * 4);
     // split-K partial tiles: a split GEMM has at most kGemmWgs (row tile, column tile, K slice)
-    // workgroups, each writing one 64 x 64 fp32 tile
-    L.pks = take((size_t)kGemmWgs * kGBM * kGBN * 4);
+    // workgroups, each writing one 64 x 64 fp32 tile; the decode GEMM (rows <= 64) writes
+    // slices x rows x N
+    size_t pks = (size_t)kGemmWgs * kGBM * kGBN * 4;
+    const int mdec = (int)std::min<size_t>(rows, 64);
+    const size_t qkvt = (size_t)(t.n_q_heads + 2 * t.n_kv_heads) * t.head_dim, qkvc = (size_t)(p.n_q_heads + 2 * p.n_kv_heads) * p.head_dim;
+    const size_t shapes[][2] = {{qkvt, (size_t)t.hidden}, {(size_t)t.hidden, (size_t)t.n_q_heads * t.head_dim},
+                                {2 * (size_t)t.ffn, (size_t)t.hidden}, {(size_t)t.hidden, (size_t)t.ffn}, {(size_t)t.vocab, (size_t)t.hidden},
+                                {qkvc, (size_t)p.hidden}, {(size_t)p.hidden, (size_t)p.n_q_heads * p.head_dim},
+                                {2 * (size_t)p.ffn, (size_t)p.hidden}, {(size_t)p.hidden, (size_t)p.ffn}, {(size_t)p.vocab, (size_t)p.hidden},
+                                {(size_t)p.hidden, (size_t)t.hidden}};
+    for (const auto& sh : shapes) {
+      if (sh[0] % 64 || sh[1] % 64) continue;
+      int ksl = 0;
+      const int ks = dec_split((int)sh[0], (int)sh[1], mdec, &ksl);
+      pks = std::max(pks, (size_t)ks * mdec * sh[0] * 4);
+    }
+    L.pks = take(pks);
     // per-row, per-256-column chunk sums of squares a residual GEMM leaves for the next RMSNorm
     L.ssq = take(Mp * ((hmax + 255) / 256) * 4);
   }
@@ -592,14 +620,23 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
   // unsplit, N/64 workgroups would each walk all of K with one load in flight). Each slice writes
   // its partial tile; k_splitk_reduce then adds them into C in slice order (with the residual
   // first for a residual epilogue), so results do not depend on workgroup timing.
+  // Few rows (decode): k_gemm_dec, each workgroup's weight fragments loaded straight to registers.
+  const bool dec = ctx->bf16() && a.M <= 64;
   const int tiles = (N / kGBN) * ((a.M + kGBM - 1) / kGBM);
-  int ks = std::max(1, std::min(a.K / kGBK, kGemmWgs / tiles));
-  const int kslice = ((a.K / kGBK + ks - 1) / ks) * kGBK;
-  ks = (a.K + kslice - 1) / kslice;
+  int ks = 1, kslice = a.K;
+  if (dec) {
+    ks = dec_split(N, a.K, a.M, &kslice);
+  } else {
+    ks = std::max(1, std::min(a.K / kGBK, kGemmWgs / tiles));
+    kslice = ((a.K / kGBK + ks - 1) / ks) * kGBK;
+    ks = (a.K + kslice - 1) / kslice;
+    if (ks > 1 && (size_t)ks * tiles > (size_t)kGemmWgs)
+      return ctx->fail(TTS_E_STATE, "gemm: %d K slices of %d tiles exceed the partial-tile buffer", ks, tiles);
+  }
   g.kslice = kslice;
   g.part = (float*)(w + ctx->L.pks);
-  if (ks > 1 && (size_t)ks * tiles > (size_t)kGemmWgs)
-    return ctx->fail(TTS_E_STATE, "gemm: %d K slices of %d tiles exceed the partial-tile buffer", ks, tiles);
+  if (dec && ks > 1 && (size_t)ks * a.M * N * 4 > ctx->L.ssq - ctx->L.pks)
+    return ctx->fail(TTS_E_STATE, "gemm: %d K slices of %d x %d rows exceed the partial buffer", ks, a.M, N);
   if (use_ssq) {
     g.rs = nullptr; g.ssq = SSQ; g.nchunk = (a.K + 255) / 256; g.eps = ctx->cfg.rms_eps;
   } else if (a.gain) {
@@ -610,7 +647,13 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
       HIP_LAUNCH_CHECK();
     }
   }
-  if (int rc = launch_gemm(ctx, g, dim3(N / kGBN, (a.M + kGBM - 1) / kGBM, ks))) return rc;
+  if (dec) {
+    if (a.M <= 16) hipLaunchKernelGGL((k_gemm_dec<1, 256>), dim3(N / 64, 1, ks), dim3(256), 0, ctx->stream, g);
+    else if (a.M <= 32) hipLaunchKernelGGL((k_gemm_dec<2, 256>), dim3(N / 64, 1, ks), dim3(256), 0, ctx->stream, g);
+    else hipLaunchKernelGGL((k_gemm_dec<4, 128>), dim3(N / 64, 1, ks), dim3(256), 0, ctx->stream, g);
+  } else if (int rc = launch_gemm(ctx, g, dim3(N / kGBN, (a.M + kGBM - 1) / kGBM, ks))) {
+    return rc;
+  }
   HIP_LAUNCH_CHECK();
   const bool ssq_out = a.ssq_out && a.epi == EPI_RESID;
   if (a.epi == EPI_SWIGLU) {

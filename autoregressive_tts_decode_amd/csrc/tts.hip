@@ -286,10 +286,14 @@ bool xtk_capable(const tts_config& c) {
   const tts_stack_cfg& t = c.talker;
   if (c.weight_dtype != TTS_DTYPE_BF16 || c.kv_dtype != TTS_DTYPE_F32) return false;
   if (t.n_kv_heads != xtp::NX || t.head_dim != 128 || t.n_q_heads != 2 * t.n_kv_heads) return false;
-  if (t.hidden % 256 || t.hidden > xtp::THMAX || t.hidden + xtp::NR > xtp::ISZ) return false;
-  if (t.ffn % 256 || t.ffn / xtp::NX > xtp::TFXMAX || (t.ffn / xtp::NX) % 8 || (t.ffn / xtp::NX) / 8 > 128) return false;
-  if (t.ffn / (xtp::NX * xtp::NR) > 3 * xtp::NW) return false;
-  if (t.vocab % xtp::NWG || t.vocab / xtp::NWG > 2 * xtp::NW) return false;
+  // MFMA tiles of 16 rows: H / 32 output rows per rank in 1, 2 or 4 tiles (H in {512, 1024, 2048});
+  // F / 256 gate + up rows per rank, at most 32 in LDS and one more tile in registers; the down
+  // tiles' K steps (F / 256) split evenly over the waves that share a tile
+  if (t.hidden != 512 && t.hidden != 1024 && t.hidden != 2048) return false;
+  if (t.hidden > xtp::THMAX || t.hidden + xtp::NR > xtp::ISZ) return false;
+  if (t.ffn % 256 || t.ffn / xtp::NX > xtp::TFXMAX || 2 * (t.ffn / 256) > 48) return false;
+  if ((t.ffn / 256) % (xtp::NW / (t.hidden / 512))) return false;
+  if (t.vocab % xtp::NWG || t.vocab / xtp::NWG > 16) return false;
   if (t.n_layers > xtp::TMAXL) return false;
   return true;
 }

@@ -16,7 +16,14 @@
 //   * the weight slices are large (up to 192 KB per workgroup and phase): the q/k/v, output and
 //     gate/up rows stream in chunks of at most 32 KB through two 32-register buffers of the back
 //     waves, each chunk issued as soon as the one two back has been consumed, while the down rows
-//     (up to 96 KB) are copied straight into LDS during the attention.
+//     (up to 96 KB) are copied straight into LDS during the attention;
+//   * the row dots run on the matrix cores: a 16-row tile of weight rows is the B operand of
+//     v_mfma_f32_16x16x32_bf16 (registers hold B fragments: lane l row l % 16, columns 32 s +
+//     8 (l / 16) of K step s; LDS rows are padded by 16 bytes so a fragment's 16 rows fall on
+//     different banks), the A operand the input row cut into two bf16 parts, hi (the fp32
+//     pattern with its low 16 bits cleared) and mid (x - hi rounded to bf16): hi + mid is x to
+//     within 2^-17 |x|, and the products are exact in fp32. The K range of a tile is split over
+//     waves, whose partial sums are added in wave order.
 #pragma once
 
 #include "tts_trace.h"
@@ -59,13 +66,71 @@ struct TkCall {
 constexpr int NF = 4;                        // front waves
 constexpr int NB = NW - NF;                  // back waves
 constexpr int PF = NF * 64;                  // polling threads
-constexpr int TLW = 65536;                   // LDS weight rows of a workgroup (bf16 elements, 128 KB)
+constexpr int TLW = 65536 + 256;             // LDS weight rows of a workgroup (bf16 elements): 32 padded rows of 2048
+constexpr int LPAD = 8;                      // LDS row padding of the weight rows (bf16 elements)
+constexpr int XST = THMAX + 16;              // row stride of the split normed residual row (bf16 elements)
+constexpr int OST = 256 + 16;                // ... of the split attention output of the XCD
+constexpr int HST = TFXMAX + 16;             // ... of the split SwiGLU slice
 
 // One weight chunk in the back waves' registers: rows (wave - NF) + NB * j (j < RR) of the chunk,
 // 16-byte units lane + 64 * k (k < KK) of each row, RR * KK <= WB.
 struct WBuf {
   u32x4 b[WB];
 };
+
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+// x at element k of a two-part split buffer (parts at sp[k], sp[st + k])
+__device__ __forceinline__ void put2(uint16_t* sp, int st, int k, float x) {
+  const uint32_t u = __float_as_uint(x);
+  const __bf16 mid = (__bf16)(x - __uint_as_float(u & 0xffff0000u));
+  sp[k] = (uint16_t)(u >> 16);
+  sp[st + k] = __builtin_bit_cast(uint16_t, mid);
+}
+// A fragment of K step ks: lane l supplies row l % 16 = part (rows 0, 1) or zeros, columns
+// 32 ks + 8 (l / 16) .. + 8.
+__device__ __forceinline__ bf16x8v a_frag2(const uint16_t* sp, int st, int ks, const uint16_t* zero) {
+  const int lane = fresh_tid() & 63, row = lane & 15;
+  const uint16_t* p = row < 2 ? sp + row * st + 32 * ks + 8 * (lane >> 4) : zero;
+  return *reinterpret_cast<const bf16x8v*>(p);
+}
+// The tile's dot for the lane's C column (lanes < 16): the two parts' rows of C.
+__device__ __forceinline__ float parts2(const f32x4& acc) { return acc[0] + acc[1]; }
+
+// B fragments of one 16-row weight tile into a back wave's buffer: K steps s0 .. s0 + n - 1
+// (n <= WB) of tile row l % 16, rowptr(i) (rows i >= nrows read as zeros).
+template <typename RowFn>
+__device__ __forceinline__ void wb_issue_tile(WBuf& B, int nrows, int s0, int n, RowFn rowptr) {
+  if (wave_id() < NF) return;
+  const int lane = fresh_tid() & 63, i = lane & 15;
+  const bool live = i < nrows;
+  const uint16_t* row = rowptr(live ? i : 0) + 32 * s0 + 8 * (lane >> 4);
+#pragma unroll
+  for (int s = 0; s < WB; ++s)
+    if (s < n) B.b[s] = live ? *glb(reinterpret_cast<const u32x4*>(row + 32 * s)) : (u32x4){0u, 0u, 0u, 0u};
+}
+// acc += the tile in B (K steps s0 .. s0 + n - 1) against the split input sp
+__device__ __forceinline__ f32x4 mfma_regs(const WBuf& B, int n, const uint16_t* sp, int st, int s0, const uint16_t* zero,
+                                           f32x4 acc) {
+#pragma unroll
+  for (int s = 0; s < WB; ++s)
+    if (s < n)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_frag2(sp, st, s0 + s, zero), __builtin_bit_cast(bf16x8v, B.b[s]), acc, 0, 0, 0);
+  return acc;
+}
+// The 16-row tile at rows t0 .. t0 + 15 of the LDS rows w (row stride ws; rows >= nrows read row
+// t0), K steps s0 .. s0 + n - 1, against the split input sp.
+__device__ __forceinline__ f32x4 mfma_lds(const uint16_t* w, int ws, int t0, int nrows, int s0, int n, const uint16_t* sp,
+                                          int st, const uint16_t* zero) {
+  const int lane = fresh_tid() & 63;
+  const int row = t0 + (lane & 15) < nrows ? t0 + (lane & 15) : t0;
+  const uint16_t* wr = w + row * ws + 8 * (lane >> 4);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = s0; s < s0 + n; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_frag2(sp, st, s, zero), *reinterpret_cast<const bf16x8v*>(wr + 32 * s), acc,
+                                                  0, 0, 0);
+  return acc;
+}
 
 template <typename WT, int RR, int KK, typename RowFn>
 __device__ __forceinline__ void wb_issue(WBuf& B, int nrows, int ncols, RowFn rowptr) {
@@ -88,74 +153,35 @@ __device__ __forceinline__ void wb_issue(WBuf& B, int nrows, int ncols, RowFn ro
   }
 }
 
-// out[i] = dot(row i, x[0 .. ncols)) for this back wave's rows of the chunk (x and out in LDS).
-template <typename WT, int RR, int KK>
-__device__ __forceinline__ void wb_dot(const WBuf& B, int nrows, int ncols, const float* x, float* out) {
-  constexpr int E = WTraits<WT>::E;
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  if (wave < NF) return;
-  const int units = ncols / E;
-  float acc[RR];
-#pragma unroll
-  for (int j = 0; j < RR; ++j) acc[j] = 0.f;
-#pragma unroll
-  for (int k = 0; k < KK; ++k) {
-    const int u = lane + 64 * k;
-    if (u < units) {
-      float xv[8];
-#pragma unroll
-      for (int e = 0; e < E; e += 4) {
-        const float4 f = *reinterpret_cast<const float4*>(x + u * E + e);
-        xv[e] = f.x; xv[e + 1] = f.y; xv[e + 2] = f.z; xv[e + 3] = f.w;
-      }
-#pragma unroll
-      for (int j = 0; j < RR; ++j) {
-        if ((wave - NF) + NB * j < nrows) {
-          float wf[8];
-          unpack(B.b[j * KK + k], wf, (WT*)nullptr);
-          float s = acc[j];
-#pragma unroll
-          for (int e = 0; e < E; ++e) s = fmaf(wf[e], xv[e], s);
-          acc[j] = s;
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < RR; ++j) {
-    const int i = (wave - NF) + NB * j;
-    if (i < nrows) {
-      const float v = wave_sum(acc[j]);
-      if (lane == 0) out[i] = v;
-    }
-  }
-}
-
-// The weight rows of a layer, per workgroup, for H <= 2048, F / 8 <= 768, 8 KV heads of dimension
-// 128 and 2 query heads per KV head. Register chunks (rows per back wave RR x 16-byte units per
-// lane KK) and LDS blocks:
-//   A0, A1   q/k/v slice rows [0, 8) and [8, 16) x H                          regs 2 x 4
-//   C0, C1   output projection: halves of the H/32 rows x 256                  regs 8 x 1
-//   DL       the first nL = min(2 F/256, TLW / H) gate/up rows (gate rows
-//            first, then up rows) x H                                          LDS, during attention
-//   D0, D1   the remaining gate/up rows, 8 a chunk                             regs 2 x 4
-//   E        down projection: H/32 rows x F/8                                  LDS, after DL is read
-// and after the last layer F0, F1, the semantic head: V/256 <= 16 rows x H, 8 a chunk -> regs 2 x 4.
+// The weight rows of a layer, per workgroup (H in {1024, 2048}, 8 KV heads of dimension 128 and
+// 2 query heads per KV head), as 16-row MFMA tiles. Register tiles live in the back waves' two
+// buffers; back wave b = wave - NF takes a share of each tile's K steps:
+//   A0, A1   the 16 q/k/v rows x H: K steps [H/128 b, + H/128), the first 8 in A0      regs
+//   C        output projection: the H/32 rows x 256 of the XCD's heads, H/512 tiles
+//            split over the 4 back waves, 8 K steps each tile                        regs (buffer 0)
+//   DL       the first nl gate/up rows (gate rows first, then up rows) x H               LDS
+//   D0, D1   the remaining gate/up rows (at most one tile) x H, as A0, A1                regs
+//   E        down projection: H/32 rows x F/8                                             LDS
+// and after the last layer F0, F1, the semantic head's V/256 <= 16 rows x H, as A0, A1.
 template <typename WT>
 __device__ __forceinline__ void tk_issue_a(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int half, int g, int r) {
-  const int H = D.H, d = D.d, G = D.nq / D.nkv, qper = (G + 2) * d / NR;
-  wb_issue<WT, 2, 4>(B, qper / 2, H, [&](int i) -> const WT* {
-    const int q = qper * r + (qper / 2) * half + i;
-    if (q < G * d) return reinterpret_cast<const WT*>(W.wq) + (size_t)(G * d * g + q) * H;
-    if (q < (G + 1) * d) return reinterpret_cast<const WT*>(W.wk) + (size_t)(d * g + q - G * d) * H;
-    return reinterpret_cast<const WT*>(W.wv) + (size_t)(d * g + q - (G + 1) * d) * H;
+  const int H = D.H, d = D.d, G = D.nq / D.nkv, qper = (G + 2) * d / NR, spw = H / 128;
+  const int b = wave_id() - NF;
+  if (8 * half >= spw) return;
+  wb_issue_tile(B, qper, spw * b + 8 * half, min(8, spw - 8 * half), [&](int i) -> const uint16_t* {
+    const int q = qper * r + i;
+    if (q < G * d) return reinterpret_cast<const uint16_t*>(W.wq) + (size_t)(G * d * g + q) * H;
+    if (q < (G + 1) * d) return reinterpret_cast<const uint16_t*>(W.wk) + (size_t)(d * g + q - G * d) * H;
+    return reinterpret_cast<const uint16_t*>(W.wv) + (size_t)(d * g + q - (G + 1) * d) * H;
   });
 }
 template <typename WT>
 __device__ __forceinline__ void tk_issue_c(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int half, int g, int r) {
-  const int hper = D.H / NR, hh = hper / 2, Gd = D.nq / D.nkv * D.d;
-  wb_issue<WT, 8, 1>(B, hh, Gd, [&](int i) -> const WT* {
-    return reinterpret_cast<const WT*>(W.wo) + (size_t)(hper * r + hh * half + i) * (D.nq * D.d) + Gd * g;
+  if (half) return;  // one buffer holds the whole output projection
+  const int hper = D.H / NR, Gd = D.nq / D.nkv * D.d, T = hper / 16, wpt = NB / T, spw = (Gd / 32) / wpt;
+  const int b = wave_id() - NF, t = b / wpt;
+  wb_issue_tile(B, 16, spw * (b % wpt), spw, [&](int i) -> const uint16_t* {
+    return reinterpret_cast<const uint16_t*>(W.wo) + (size_t)(hper * r + 16 * t + i) * (D.nq * D.d) + Gd * g;
   });
 }
 // gate/up row q of the rank: gate rows 0 .. fper, then up rows fper .. 2 fper
@@ -165,37 +191,60 @@ __device__ __forceinline__ const WT* tk_gu_row(const KCONST TkDesc& D, const KCO
   const int f = fx * g + fper * r + (q < fper ? q : q - fper);
   return reinterpret_cast<const WT*>(q < fper ? W.wg : W.wu) + (size_t)f * D.H;
 }
-// register chunk c (8 rows) of the gate/up rows past the nl rows held in LDS
+// A descriptor pointer as a wave-uniform value (each 32-bit half through readfirstlane, kept
+// unsigned so the low half never sign-extends into the high one).
+__device__ __forceinline__ const uint16_t* tk_uniform_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+}
+
+// half c of the register tile of gate/up rows nl .. nd - 1 (past the nl rows held in LDS)
 template <typename WT>
 __device__ __forceinline__ void tk_issue_d(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int nl, int c, int g,
                                            int r) {
-  const int nd = 2 * (D.F / NX / NR);
-  wb_issue<WT, 2, 4>(B, min(8, max(0, nd - nl - 8 * c)), D.H,
-                     [&](int i) -> const WT* { return tk_gu_row<WT>(D, W, nl + 8 * c + i, g, r); });
+  const int nd = 2 * (D.F / NX / NR), spw = D.H / 128;
+  const int b = wave_id() - NF;
+  if (nd <= nl || 8 * c >= spw) return;
+  // the gate and up matrices are read through scalar loads first (a per-lane choice between two
+  // descriptor pointers would otherwise become a per-lane descriptor read)
+  const uint16_t *wg = tk_uniform_ptr(W.wg), *wu = tk_uniform_ptr(W.wu);
+  const int fx = D.F / NX, fper = fx / NR;
+  wb_issue_tile(B, nd - nl, spw * b + 8 * c, min(8, spw - 8 * c), [&](int i) -> const uint16_t* {
+    const int q = nl + i;
+    const int f = fx * g + fper * r + (q < fper ? q : q - fper);
+    return (q < fper ? wg : wu) + (size_t)f * D.H;
+  });
 }
 template <typename WT>
 __device__ __forceinline__ void tk_issue_f(WBuf& B, const KCONST TkDesc& D, int half) {
-  const int vper = D.V / NWG;
-  wb_issue<WT, 2, 4>(B, min(8, max(0, vper - 8 * half)), D.H, [&](int i) -> const WT* {
-    return reinterpret_cast<const WT*>(D.lm_head) + (size_t)(vper * blockIdx.x + 8 * half + i) * D.H;
+  const int vper = D.V / NWG, spw = D.H / 128;
+  const int b = wave_id() - NF;
+  if (8 * half >= spw) return;
+  wb_issue_tile(B, vper, spw * b + 8 * half, min(8, spw - 8 * half), [&](int i) -> const uint16_t* {
+    return reinterpret_cast<const uint16_t*>(D.lm_head) + (size_t)(vper * blockIdx.x + i) * D.H;
   });
 }
 
 struct TkSmem {
   float xs[THMAX + 64];       // residual row, then the per-rank sums of squares
-  float xn[THMAX];            // normed row; cross-reduce partials
+  __align__(16) uint16_t xnp[2 * XST];  // normed row in two parts; (as floats) cross-reduce partials
   float qkv[512];             // this XCD's q/k/v slice
   float q[2][128];            // normed + rotated q of the XCD's two heads
   float kp[128], vp[128];     // the step's k (normed + rotated) and v
   float wm[NF][2], wl[NF][2]; // per-wave softmax max and sum per head
   float wo[NF][2][128];       // per-wave unnormalised attention output per head
-  float cmb[NR * 10];         // gathered partials of this rank's 8 outputs
-  float ob[256];              // attention output of the XCD's heads
-  float hb[TFXMAX];           // SwiGLU slice of the XCD
-  float out[128];             // row results of this workgroup
+  float cmb[NR * 10];         // gathered partials of this rank's 8 outputs; per-wave dot partials
+  __align__(16) uint16_t obp[2 * OST];  // attention output of the XCD's heads, in two parts
+  __align__(16) uint16_t hbp[2 * HST];  // SwiGLU slice of the XCD, in two parts
+  __align__(16) uint16_t zero[8];
   float red[64];
-  __align__(16) uint16_t lw[TLW];  // weight rows copied by LDS-direct loads (gate/up rows, then down rows)
+  __align__(16) uint16_t lw[TLW];  // weight rows copied by LDS-direct loads (gate/up rows, then down rows), padded
 };
+static_assert(NR * 10 >= NW * 2 * 16, "per-wave dot partials fit the combine buffer");
+// per-wave dot partials: [wave][set][row of the tile]
+__device__ __forceinline__ float* tk_pt(TkSmem& S, int wave, int set) { return S.cmb + (wave * 2 + set) * 16; }
 
 // Per-thread constants of one layer: norm gains of elements tid, tid + NT, tid + 2 NT, tid + 3 NT
 // (H <= 4 NT), and for the q/k waves the q- or k-norm gains of lanes lane, lane + 64.
@@ -223,9 +272,10 @@ __device__ __forceinline__ void tk_load_consts(TkConsts& c, const KCONST TkDesc&
 }
 
 // A block of weight rows copied into LDS in parts, by the front (FRONT) or back waves, with
-// LDS-direct loads: unit u of the block (row u / upr, unit u % upr of the row, upr 16-byte units
-// a row) lands at dst[8 u], one instruction moving 64 consecutive units. Row i starts at
-// b0 + i * stride for i < split, else at b1 + (i - split) * stride. part(n) issues at most n more
+// LDS-direct loads: row i (at b0 + i * stride for i < split, else b1 + (i - split) * stride, upr
+// 16-byte units) lands at dst[i * ldst ..], ldst = 8 upr + LPAD elements, so the rows of an MFMA
+// fragment fall on different LDS banks. One instruction moves up to 64 consecutive units of one
+// row (cpr instructions a row; lanes past the row's end are off). part(n) issues at most n more
 // instructions per wave: a wave that issues more than its share of the CU's memory queue holds
 // stalls until the queue drains, so large copies go in parts spread over the barrier intervals of
 // a layer. A copy has landed once the issuing wave's vector-memory counter has passed it.
@@ -233,7 +283,7 @@ template <typename WT, bool FRONT>
 struct RowCopy {
   const WT *b0, *b1;
   long long stride;
-  int split, upr, units, j;
+  int split, upr, cpr, ninst, ldst, j;
 
   __device__ __forceinline__ void begin(const WT* b0_, const WT* b1_, int split_, long long stride_, int nrows, int upr_) {
     b0 = b0_;
@@ -241,7 +291,9 @@ struct RowCopy {
     split = split_;
     stride = stride_;
     upr = upr_;
-    units = nrows * upr_;
+    cpr = (upr_ + 63) / 64;
+    ninst = nrows * cpr;
+    ldst = 8 * upr_ + LPAD;
     j = FRONT ? wave_id() : wave_id() - NF;
   }
   __device__ __forceinline__ void part(uint16_t* dst, int n) {
@@ -250,13 +302,13 @@ struct RowCopy {
     static_assert(NF == NB, "front and back wave sets of one size");
     if ((wave_id() < NF) != FRONT) return;
     const int lane = threadIdx.x & 63;
-    for (int c = 0; c < n && 64 * j < units; ++c, j += NF) {
-      const int u = 64 * j + lane;
-      const int row = u / upr, col = u - row * upr;
-      // lanes past the last unit re-read unit 0 and land in the 64-unit tail of the instruction
-      const int rr = u < units ? row : 0;
-      const WT* src = (rr < split ? b0 + rr * stride : b1 + (rr - split) * stride) + (u < units ? col * E : 0);
-      __builtin_amdgcn_global_load_lds((const GLB void*)src, (__attribute__((address_space(3))) void*)&dst[64 * E * j], 16, 0, 0);
+    for (int c = 0; c < n && j < ninst; ++c, j += NF) {
+      const int row = j / cpr, ch = j - row * cpr;
+      const int u = 64 * ch + lane;
+      const WT* src = (row < split ? b0 + row * stride : b1 + (row - split) * stride) + (u < upr ? u : 0) * E;
+      if (u < upr)
+        __builtin_amdgcn_global_load_lds((const GLB void*)src, (__attribute__((address_space(3))) void*)&dst[row * ldst + 64 * E * ch],
+                                         16, 0, 0);
     }
   }
 };
@@ -264,57 +316,11 @@ struct RowCopy {
 // Wait until every load this wave issued has landed (the LDS-direct rows included).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
-// out[i] = dot(row i of w, x[0 .. ncols)) for nrows rows of ncols bf16 weights in LDS (row-major),
-// all waves: wave w takes rows w, w + NW, ... (at most RM), lane the 16-byte units lane + 64 k
-// (k < KK, ncols <= 512 KK). Rows go in groups of 4 so the cross-lane sums of a group overlap.
-template <typename WT, int KK, int RM>
-__device__ __forceinline__ void tk_dot_lds(const uint16_t* w, int nrows, int ncols, const float* x, float* out) {
-  constexpr int E = WTraits<WT>::E;
-  const int wave = wave_id(), lane = threadIdx.x & 63, upr = ncols / E;
-  float xv[KK][8];
-#pragma unroll
-  for (int k = 0; k < KK; ++k) {
-    const int u = lane + 64 * k;
-#pragma unroll
-    for (int e = 0; e < 8; e += 4) {
-      const float4 f = u < upr ? *reinterpret_cast<const float4*>(x + u * E + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-      xv[k][e] = f.x; xv[k][e + 1] = f.y; xv[k][e + 2] = f.z; xv[k][e + 3] = f.w;
-    }
-  }
-#pragma unroll
-  for (int j0 = 0; j0 < RM; j0 += 4) {
-    float acc[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int i = wave + NW * (j0 + jj);
-      float s = 0.f;
-      if (j0 + jj < RM && i < nrows) {
-#pragma unroll
-        for (int k = 0; k < KK; ++k) {
-          const int u = lane + 64 * k;
-          if (u < upr) {
-            float wf[8];
-            unpack(*reinterpret_cast<const u32x4*>(&w[(i * upr + u) * E]), wf, (WT*)nullptr);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s = fmaf(wf[e], xv[k][e], s);
-          }
-        }
-      }
-      acc[jj] = s;
-    }
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int i = wave + NW * (j0 + jj);
-      const float v = wave_sum(acc[jj]);
-      if (j0 + jj < RM && i < nrows && lane == 0) out[i] = v;
-    }
-  }
-}
-
-// y = x * rsqrt(mean(x^2) + eps) * gain over n <= 4 NT elements; ss: NR per-rank partial sums
-// of squares (from reduce_gather) or nullptr to reduce here.
-__device__ __forceinline__ void tk_rmsnorm(const float* x, int n, const float* gr, float eps, float* y, float* red,
-                                           const float* ss) {
+// x * rsqrt(mean(x^2) + eps) * gain over n <= 4 NT elements, in two parts into sp (row stride
+// XST); with out, also as fp32 (to global memory). ss: NR per-rank partial sums of squares (from
+// reduce_gather) or nullptr to reduce here.
+__device__ __forceinline__ void tk_rmsnorm(const float* x, int n, const float* gr, float eps, uint16_t* sp, float* red,
+                                           const float* ss, float* out = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float tot = 0.f;
   if (ss) {
@@ -340,13 +346,17 @@ __device__ __forceinline__ void tk_rmsnorm(const float* x, int n, const float* g
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = tid + k * NT;
-    if (i < n) y[i] = x[i] * sc * gr[k];
+    if (i < n) {
+      const float y = x[i] * sc * gr[k];
+      put2(sp, XST, i, y);
+      if (out) glb(out)[i] = y;
+    }
   }
   lds_barrier();
 }
 
 // Attention of this XCD's two query heads over positions 0..p of KV head g, this rank's chunk of
-// positions, then the two combining exchanges; the XCD's 256 outputs land in S.ob. Only the front
+// positions, then the two combining exchanges; the XCD's 256 outputs land in S.obp, in two parts. Only the front
 // waves compute; the back waves meet them at the barriers, running bg(k) (k = 0 .. 3) in the four
 // intervals before them. rc, rs: RoPE factors of position p at lane (q/k waves).
 template <typename WT, typename Bg>
@@ -492,7 +502,9 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
     return false;
   TTS_STAMP(56);
   ++apar;
-  if (!slice_gather<1, 1, PF>(X, 8, 256, [&](int k, int) {
+  if (!slice_gather_pe<1, 1, PF>(X, 8, 256, [&](auto emit) {
+        if (threadIdx.x >= 8) return;
+        const int k = threadIdx.x;
         float mx = -INFINITY;
         for (int s2 = 0; s2 < NR; ++s2) mx = fmaxf(mx, S.cmb[s2 * 10]);
         float ls = 0.f, os = 0.f;
@@ -502,8 +514,8 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
           ls += S.cmb[s2 * 10 + 1] * f;
           os += S.cmb[s2 * 10 + 2 + k] * f;
         }
-        return os / ls;
-      }, S.ob, tag, iring, g, r, [&] { if (wave >= NF) bg(3); }))
+        emit(k, 0, os / ls);
+      }, [&](int i, float v) { put2(S.obp, OST, i, v); }, tag, iring, g, r, [&] { if (wave >= NF) bg(3); }))
     return false;
   return true;
 }
@@ -535,8 +547,16 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   const int qrows = (G + 2) * d, qper = qrows / NR, hper = H / NR, fx = D.F / NX, fper = fx / NR;
   TkConsts c;
   tk_load_consts<WT>(c, D, D.layer[0]);
-  const int qh = qper / 2, hh = hper / 2, nd = 2 * fper;  // rows of A0/A1, C0/C1; gate + up rows
-  const int nl = min(min(nd, TLW / H), 4 * NW);            // gate/up rows held in LDS (4 per wave)
+  const int nd = 2 * fper;                                // gate + up rows of the rank
+  const int nl = min(min(nd, TLW / (H + LPAD)), 32);      // gate/up rows held in LDS (at most 2 tiles)
+  const int b = wave - NF;                                // back wave index (register tiles)
+  // K split of the tiles: register tiles over the 4 back waves, LDS tiles over all 8 waves
+  const int ksh = H / 32;                                 // K steps of a hidden-wide row
+  const int spq = ksh / NB;                               // per back wave, hidden-wide register tiles
+  const int tc = hper / 16, wpc = NB / tc, spc = (G * d / 32) / wpc;  // output projection tiles
+  const int tgl = (nl + 15) / 16, wpg = NW / tgl, spg = ksh / wpg;    // LDS gate/up tiles
+  const int tdn = hper / 16, wpd = NW / tdn, spd = (fx / 32) / wpd;   // down tiles
+  const int gld = H + LPAD, dld = fx + LPAD;              // LDS row strides of the gate/up and down rows
   // The LDS gate/up block of a layer goes in parts (instructions per back wave, 32 for the largest
   // block): 4 while the previous layer's down exchange runs, 4 after the q/k/v rows, 6 during the
   // q/k/v exchange, 4 + 6 + 4 in the attention and the rest during its last exchange.
@@ -559,22 +579,33 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   }
   int iring = 0, cpar = 0, apar = 0;
   for (int i = tid; i < H; i += NT) S.xs[i] = glb(D.x_in)[i];
+  if (tid < 8) S.zero[tid] = 0;
   lds_barrier();
+  float* xn = reinterpret_cast<float*>(S.xnp);  // cross-reduce partials (the split row is dead by then)
+  // the sum over a tile's waves (tile t of wpt waves from wave w0) of row i of their partials
+  auto tile_sum = [&](int w0, int wpt, int set, int t, int i) {
+    float v = 0.f;
+    for (int k = 0; k < wpt; ++k) v += tk_pt(S, w0 + t * wpt + k, set)[i];
+    return v;
+  };
   bool ok = true;
   for (int l = 0; ok && l < D.n_layers; ++l) {
     const KCONST LayerW& W = D.layer[l];
     const bool last = l + 1 == D.n_layers;
     TTS_STAMP(50);
-    // q/k/v slice (A0: X0, A1: X1); the output projection rows (C0, C1) follow in their place
-    tk_rmsnorm(S.xs, H, c.an, D.eps, S.xn, S.red, l > 0 ? S.xs + H : nullptr);
-    wb_dot<WT, 2, 4>(X0, qh, H, S.xn, S.out);
+    // q/k/v tile (A0: X0, A1: X1); the output projection tiles (C) follow in buffer 0
+    tk_rmsnorm(S.xs, H, c.an, D.eps, S.xnp, S.red, l > 0 ? S.xs + H : nullptr);
+    if (wave >= NF) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma_regs(X0, min(8, spq), S.xnp, XST, spq * b, S.zero, acc);
+      acc = mfma_regs(X1, spq - 8, S.xnp, XST, spq * b + 8, S.zero, acc);
+      if (lane < 16) tk_pt(S, wave, 0)[lane] = parts2(acc);
+    }
     tk_issue_c<WT>(X0, D, W, 0, g, r);
-    wb_dot<WT, 2, 4>(X1, qh, H, S.xn, S.out + qh);
-    tk_issue_c<WT>(X1, D, W, 1, g, r);
     gu.part(S.lw, 4);
     lds_barrier();
     TTS_STAMP(51);
-    if (!slice_gather<1, KQ, PF>(X, qper, qrows, [&](int e, int) { return S.out[e]; }, S.qkv, tag, iring, g, r,
+    if (!slice_gather<1, KQ, PF>(X, qper, qrows, [&](int e, int) { return tile_sum(NF, NB, 0, 0, e); }, S.qkv, tag, iring, g, r,
                                  [&] { gu.part(S.lw, 6); })) {
       ok = false;
       break;
@@ -588,84 +619,116 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
       break;
     }
     TTS_STAMP(57);
-    // output projection partial (C0: X0, C1: X1), residual; the register gate/up chunks follow
-    // (D0 now, D1 during the exchange)
-    wb_dot<WT, 8, 1>(X0, hh, G * d, S.ob, S.out);
+    // output projection tiles (C: X0), residual; the register gate/up tile follows (D0 now, D1
+    // during the exchange)
+    if (wave >= NF) {
+      const f32x4 acc = mfma_regs(X0, spc, S.obp, OST, spc * (b % wpc), S.zero, (f32x4){0.f, 0.f, 0.f, 0.f});
+      if (lane < 16) tk_pt(S, wave, 0)[lane] = parts2(acc);
+    }
     tk_issue_d<WT>(X0, D, W, nl, 0, g, r);
-    wb_dot<WT, 8, 1>(X1, hh, G * d, S.ob, S.out + hh);
     lds_barrier();
     TTS_STAMP(58);
-    if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r,
-                                         [&] { tk_issue_d<WT>(X1, D, W, nl, 1, g, r); })) {
+    if (!reduce_gather_p<1, THMAX, KT, PF>(
+            X,
+            [&](auto emit) {
+              for (int i = fresh_tid(); i < hper; i += NT) emit(i, 0, tile_sum(NF, wpc, 0, i / 16, i % 16));
+            },
+            S.xs, xn, H, true, tag, iring, cpar, g, r, [&] { tk_issue_d<WT>(X1, D, W, nl, 1, g, r); })) {
       ok = false;
       break;
     }
     TTS_STAMP(59);
-    // gate and up rows (LDS block, then D0: X0, D1: X1), SwiGLU. Once the LDS block is read the
-    // front waves copy the down rows in its place (half now, half during the SwiGLU exchange)
-    // and the back waves, their registers free, start on the next layer's q/k/v rows (or the
-    // semantic head). Each wave loads its own next-layer constants behind its other loads.
-    tk_rmsnorm(S.xs, H, c.mn, D.eps, S.xn, S.red, S.xs + H);
+    // gate and up rows (LDS tiles, then the register tile D0: X0, D1: X1), SwiGLU. Once the LDS
+    // block is read the front waves copy the down rows in its place (half now, half during the
+    // SwiGLU exchange) and the back waves, their registers free, start on the next layer's q/k/v
+    // rows (or the semantic head). Each wave loads its own next-layer constants behind its other
+    // loads.
+    tk_rmsnorm(S.xs, H, c.mn, D.eps, S.xnp, S.red, S.xs + H);
     if (wave >= NF) wait_loads();
     lds_barrier();
-    tk_dot_lds<WT, 4, 4>(S.lw, nl, H, S.xn, S.out);
+    {
+      const int t = wave / wpg;
+      const f32x4 acc = mfma_lds(S.lw, gld, 16 * t, nl, spg * (wave % wpg), spg, S.xnp, XST, S.zero);
+      if (lane < 16) tk_pt(S, wave, 0)[lane] = parts2(acc);
+    }
     lds_barrier();
-    TTS_STAMP(60);
-    const int dparts = (hper * (fx / 8) / 64 + 2 * NF - 1) / (2 * NF);  // first half, per front wave
+    const int dparts = (hper * ((fx / 8 + 63) / 64) + 2 * NF - 1) / (2 * NF);  // first half, per front wave
     if (wave < NF) {
       dn.begin(reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r) * D.F + fx * g, nullptr, hper, D.F, hper, fx / 8);
       dn.part(S.lw, dparts);
       tk_next_consts<WT>(c, D, l, tid);
     } else {
-      wb_dot<WT, 2, 4>(X0, min(8, max(0, nd - nl)), H, S.xn, S.out + nl);
+      if (nd > nl) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma_regs(X0, min(8, spq), S.xnp, XST, spq * b, S.zero, acc);
+        acc = mfma_regs(X1, spq - 8, S.xnp, XST, spq * b + 8, S.zero, acc);
+        if (lane < 16) tk_pt(S, wave, 1)[lane] = parts2(acc);
+      }
       if (!last) tk_issue_a<WT>(X0, D, D.layer[l + 1], 0, g, r);
       else tk_issue_f<WT>(X0, D, 0);
-      wb_dot<WT, 2, 4>(X1, min(8, max(0, nd - nl - 8)), H, S.xn, S.out + nl + 8);
       tk_next_consts<WT>(c, D, l, tid);
     }
     lds_barrier();
     TTS_STAMP(61);
-    if (!slice_gather<1, KH, PF>(X, fper, fx, [&](int e, int) { return silu(S.out[e]) * S.out[fper + e]; }, S.hb, tag,
-                                 iring, g, r, [&] {
-                                   if (wave < NF) {
-                                     dn.part(S.lw, 1 << 20);
-                                   } else {
-                                     if (!last) tk_issue_a<WT>(X1, D, D.layer[l + 1], 1, g, r);
-                                     else tk_issue_f<WT>(X1, D, 1);
-                                   }
-                                 })) {
+    // gate/up row q: an LDS tile row below nl, else a row of the register tile
+    auto gu_val = [&](int q) { return q < nl ? tile_sum(0, wpg, 0, q / 16, q % 16) : tile_sum(NF, NB, 1, 0, q - nl); };
+    if (!slice_gather_pe<1, KH, PF>(
+            X, fper, fx,
+            [&](auto emit) {
+              for (int i = fresh_tid(); i < fper; i += NT) emit(i, 0, silu(gu_val(i)) * gu_val(fper + i));
+            },
+            [&](int i, float v) { put2(S.hbp, HST, i, v); }, tag, iring, g, r, [&] {
+              if (wave < NF) {
+                dn.part(S.lw, 1 << 20);
+              } else {
+                if (!last) tk_issue_a<WT>(X1, D, D.layer[l + 1], 1, g, r);
+                else tk_issue_f<WT>(X1, D, 1);
+              }
+            })) {
       ok = false;
       break;
     }
-    // down projection partial from LDS, residual; the next layer's LDS gate/up block starts
-    // during the exchange
+    // down projection tiles from LDS, residual; the next layer's LDS gate/up block starts during
+    // the exchange
     TTS_STAMP(62);
     if (wave < NF) wait_loads();
     lds_barrier();
-    tk_dot_lds<WT, 2, 8>(S.lw, hper, fx, S.hb, S.out);
+    {
+      const int t = wave / wpd;
+      const f32x4 acc = mfma_lds(S.lw, dld, 16 * t, hper, spd * (wave % wpd), spd, S.hbp, HST, S.zero);
+      if (lane < 16) tk_pt(S, wave, 0)[lane] = parts2(acc);
+    }
     lds_barrier();
     TTS_STAMP(63);
-    if (!reduce_gather<1, THMAX, KT, PF>(X, S.out, S.xs, S.xn, H, true, tag, iring, cpar, g, r, [&] {
-          if (!last) {
-            gu_begin(D.layer[l + 1]);
-            gu.part(S.lw, 4);
-          }
-        })) {
+    if (!reduce_gather_p<1, THMAX, KT, PF>(
+            X,
+            [&](auto emit) {
+              for (int i = fresh_tid(); i < hper; i += NT) emit(i, 0, tile_sum(0, wpd, 0, i / 16, i % 16));
+            },
+            S.xs, xn, H, true, tag, iring, cpar, g, r, [&] {
+              if (!last) {
+                gu_begin(D.layer[l + 1]);
+                gu.part(S.lw, 4);
+              }
+            })) {
       ok = false;
       break;
     }
   }
   TTS_STAMP(64);
   if (ok) {
-    // final norm (gains in c.an), semantic head slice (F0: X0, F1: X1)
-    tk_rmsnorm(S.xs, H, c.an, D.eps, S.xn, S.red, S.xs + H);
+    // final norm (gains in c.an; workgroup 0 also writes the normed row, h_T), semantic head tile
+    // (F0: X0, F1: X1)
+    tk_rmsnorm(S.xs, H, c.an, D.eps, S.xnp, S.red, S.xs + H, blockIdx.x == 0 ? D.hT : nullptr);
     const int vper = D.V / NWG;
-    wb_dot<WT, 2, 4>(X0, min(8, vper), H, S.xn, S.out);
-    wb_dot<WT, 2, 4>(X1, max(0, vper - 8), H, S.xn, S.out + 8);
+    if (wave >= NF) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma_regs(X0, min(8, spq), S.xnp, XST, spq * b, S.zero, acc);
+      acc = mfma_regs(X1, spq - 8, S.xnp, XST, spq * b + 8, S.zero, acc);
+      if (lane < 16) tk_pt(S, wave, 0)[lane] = parts2(acc);
+    }
     lds_barrier();
-    for (int i = tid; i < vper; i += NT) glb(D.logits)[vper * blockIdx.x + i] = S.out[i];
-    if (blockIdx.x == 0)
-      for (int i = tid; i < H; i += NT) glb(D.hT)[i] = S.xn[i];
+    for (int i = tid; i < vper; i += NT) glb(D.logits)[vper * blockIdx.x + i] = tile_sum(NF, NB, 0, 0, i);
   }
   TTS_STAMP(65);
   if (blockIdx.x == 0 && tid == 0) {

@@ -579,6 +579,18 @@ __device__ __forceinline__ bool slice_gather_p(const Xch& X, int n, int w, Produ
   return get_flat<KMAX, NPOLL>(buf, M * w, tag, dst, X.err);
 }
 
+// slice_gather_p handing each gathered value to store(i, value) instead of an fp32 row.
+template <int M, int KMAX, int NPOLL = NT, typename Produce, typename Store, typename AfterPut>
+__device__ __forceinline__ bool slice_gather_pe(const Xch& X, int n, int w, Produce produce, Store store, uint32_t& tag, int& iring,
+                                                int g, int r, AfterPut after_put) {
+  ++tag;
+  u64* buf = X.xin + ((size_t)g * RING + (iring++ & (RING - 1))) * ISZ;
+  const uint32_t t = tag;
+  produce([&](int e, int m, float v) { st_l(buf + m * w + n * r + e, pack(v, t)); });
+  after_put();
+  return get_each<KMAX, NPOLL>(M * w, tag, X.err, [&](int i) -> const u64* { return buf + i; }, store);
+}
+
 template <int M, int KMAX, int NPOLL = NT, typename ValFn, typename AfterPut>
 __device__ __forceinline__ bool slice_gather(const Xch& X, int n, int w, ValFn vals, float* dst, uint32_t& tag, int& iring,
                                              int g, int r, AfterPut after_put) {

@@ -76,10 +76,11 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="1.7b")
     ap.add_argument("--frames-before", type=int, default=4)
     ap.add_argument("--save", default="")
+    ap.add_argument("--lib", default=TRACE_LIB, help="a library built with TTS_PHASE_TRACE")
     args = ap.parse_args(argv)
-    if not os.path.exists(TRACE_LIB):
-        raise RuntimeError(f"{TRACE_LIB} not built: python -m autoregressive_tts_decode_amd.build")
-    lib = tts.load_library(TRACE_LIB)
+    if not os.path.exists(args.lib):
+        raise RuntimeError(f"{args.lib} not built: python -m autoregressive_tts_decode_amd.build")
+    lib = tts.load_library(args.lib)
     lib.tts_trace_ctl.argtypes = [ctypes.c_int, ctypes.c_void_p]
     wl = config.WORKLOADS[args.workload]
     d = torch.device("cuda:0")

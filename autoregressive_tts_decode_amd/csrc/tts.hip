@@ -284,7 +284,7 @@ bool xcp_capable(const tts_config& c) {
 // (see tts_xtk.h).
 bool xtk_capable(const tts_config& c) {
   const tts_stack_cfg& t = c.talker;
-  if (c.weight_dtype != TTS_DTYPE_BF16 || c.kv_dtype != TTS_DTYPE_F32) return false;
+  if ((c.weight_dtype != TTS_DTYPE_BF16 && c.weight_dtype != TTS_DTYPE_FP8_E4M3) || c.kv_dtype != TTS_DTYPE_F32) return false;
   if (t.n_kv_heads != xtp::NX || t.head_dim != 128 || t.n_q_heads != 2 * t.n_kv_heads) return false;
   // MFMA tiles of 16 rows: H / 32 output rows per rank in 1, 2 or 4 tiles (H in {512, 1024, 2048});
   // F / 256 gate + up rows per rank, at most 32 in LDS and one more tile in registers; the down
@@ -992,7 +992,8 @@ int talker_step_xtk(tts_ctx* ctx, int bump_pos, int bump_frame) {
   call.desc = ctx->use_scratch ? ctx->tkdesc_s : ctx->tkdesc;
   call.bump_pos = bump_pos;
   call.bump_frame = bump_frame;
-  hipLaunchKernelGGL(xtp::k_talker_step<uint16_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
+  if (ctx->fp8()) hipLaunchKernelGGL(xtp::k_talker_step<uint8_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
+  else hipLaunchKernelGGL(xtp::k_talker_step<uint16_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
   HIP_LAUNCH_CHECK();
   return TTS_OK;
 }
@@ -1206,9 +1207,9 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, cpk, xtp::NT, 0) != hipSuccess) occ = 0;
     dd.codepred_wg_per_cu = occ;
     occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(xtp::k_talker_step<uint16_t>), xtp::NT,
-                                                     0) != hipSuccess)
-      occ = 0;
+    const void* tkk = cfg->weight_dtype == TTS_DTYPE_FP8_E4M3 ? reinterpret_cast<const void*>(xtp::k_talker_step<uint8_t>)
+                                                              : reinterpret_cast<const void*>(xtp::k_talker_step<uint16_t>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, tkk, xtp::NT, 0) != hipSuccess) occ = 0;
     dd.talker_wg_per_cu = occ;
     (void)hipGetLastError();
     ctx->dev_mask = tts_persistent_allowed(&dd);
@@ -1394,6 +1395,18 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
     for (int l = 0; l < t.n_layers; ++l) {
       const Layer& L = ctx->talker.layers[l];
       D.layer[l] = {L.attn_norm, L.wq, L.wk, L.wv, L.q_norm, L.k_norm, L.wo, L.mlp_norm, L.wg, L.wu, L.wd};
+      if (ctx->fp8()) {
+        const int H = t.hidden, qd = t.n_q_heads * t.head_dim;
+        D.scale[l] = {ctx->scale_of(L.wq, H), ctx->scale_of(L.wk, H), ctx->scale_of(L.wv, H), ctx->scale_of(L.wo, qd),
+                      ctx->scale_of(L.wg, H), ctx->scale_of(L.wu, H), ctx->scale_of(L.wd, t.ffn)};
+        const xtp::LayerS& q = D.scale[l];
+        if (!q.wq || !q.wk || !q.wv || !q.wo || !q.wg || !q.wu || !q.wd)
+          return ctx->fail(TTS_E_STATE, "load_weights: no E4M3 scale for a Talker layer %d matrix", l);
+      }
+    }
+    if (ctx->fp8()) {
+      D.head_scale = ctx->scale_of(ctx->lm_head, t.hidden);
+      if (!D.head_scale) return ctx->fail(TTS_E_STATE, "load_weights: no E4M3 scale for the semantic head");
     }
     D.n_layers = t.n_layers; D.H = t.hidden; D.F = t.ffn; D.V = t.vocab; D.nq = t.n_q_heads; D.nkv = t.n_kv_heads;
     D.d = t.head_dim; D.cap = c.max_cache_steps; D.eps = c.rms_eps;

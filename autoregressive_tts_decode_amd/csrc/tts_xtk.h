@@ -42,6 +42,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct TkDesc {
   LayerW layer[TMAXL];
+  LayerS scale[TMAXL];               // per-row fp32 scales of E4M3 matrices (unused for bf16 rows)
+  const float* head_scale;           // [V] of the E4M3 semantic head
   int32_t n_layers, H, F, V, nq, nkv, d, cap;
   float eps;
   const void *final_norm, *lm_head;
@@ -66,8 +68,8 @@ struct TkCall {
 constexpr int NF = 4;                        // front waves
 constexpr int NB = NW - NF;                  // back waves
 constexpr int PF = NF * 64;                  // polling threads
-constexpr int TLW = 65536 + 256;             // LDS weight rows of a workgroup (bf16 elements): 32 padded rows of 2048
-constexpr int LPAD = 8;                      // LDS row padding of the weight rows (bf16 elements)
+constexpr int TLWB = 2 * (65536 + 256);      // LDS weight rows of a workgroup (bytes): 32 padded bf16 rows of 2048
+constexpr int LPADB = 16;                    // LDS row padding of the weight rows (bytes)
 constexpr int XST = THMAX + 16;              // row stride of the split normed residual row (bf16 elements)
 constexpr int OST = 256 + 16;                // ... of the split attention output of the XCD
 constexpr int HST = TFXMAX + 16;             // ... of the split SwiGLU slice
@@ -80,6 +82,22 @@ struct WBuf {
 
 typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
 
+// Bytes per weight element (bf16 rows or E4M3 codes) and K steps per 16-byte unit of a lane.
+template <typename WT>
+struct TkW {
+  static constexpr int ES = (int)sizeof(WT);
+  static constexpr int KE = 2 / ES;
+  static constexpr int KPB = KE * WB;  // K steps in one weight buffer
+};
+// Column (element) of K step ks that lane group q = lane / 16 starts at. For bf16 rows a lane's
+// 8 columns of a step are 32 ks + 8 q; for E4M3 rows two steps share a 16-byte unit, so the pair
+// (2 m, 2 m + 1) takes columns 64 m + 16 q (+ 8 for the odd step). The input fragments use the
+// same columns, so every MFMA still pairs each weight with its own input element.
+template <int KE>
+__device__ __forceinline__ int kcol(int ks, int q) {
+  return 32 * KE * (ks / KE) + 8 * KE * q + 8 * (ks % KE);
+}
+
 // x at element k of a two-part split buffer (parts at sp[k], sp[st + k])
 __device__ __forceinline__ void put2(uint16_t* sp, int st, int k, float x) {
   const uint32_t u = __float_as_uint(x);
@@ -87,143 +105,170 @@ __device__ __forceinline__ void put2(uint16_t* sp, int st, int k, float x) {
   sp[k] = (uint16_t)(u >> 16);
   sp[st + k] = __builtin_bit_cast(uint16_t, mid);
 }
-// A fragment of K step ks: lane l supplies row l % 16 = part (rows 0, 1) or zeros, columns
-// 32 ks + 8 (l / 16) .. + 8.
+// A fragment of K step ks: lane l supplies row l % 16 = part (rows 0, 1) or zeros, the 8 columns
+// of kcol(ks, l / 16).
+template <int KE>
 __device__ __forceinline__ bf16x8v a_frag2(const uint16_t* sp, int st, int ks, const uint16_t* zero) {
   const int lane = fresh_tid() & 63, row = lane & 15;
-  const uint16_t* p = row < 2 ? sp + row * st + 32 * ks + 8 * (lane >> 4) : zero;
+  const uint16_t* p = row < 2 ? sp + row * st + kcol<KE>(ks, lane >> 4) : zero;
   return *reinterpret_cast<const bf16x8v*>(p);
 }
 // The tile's dot for the lane's C column (lanes < 16): the two parts' rows of C.
 __device__ __forceinline__ float parts2(const f32x4& acc) { return acc[0] + acc[1]; }
 
-// B fragments of one 16-row weight tile into a back wave's buffer: K steps s0 .. s0 + n - 1
-// (n <= WB) of tile row l % 16, rowptr(i) (rows i >= nrows read as zeros).
-template <typename RowFn>
-__device__ __forceinline__ void wb_issue_tile(WBuf& B, int nrows, int s0, int n, RowFn rowptr) {
-  if (wave_id() < NF) return;
-  const int lane = fresh_tid() & 63, i = lane & 15;
-  const bool live = i < nrows;
-  const uint16_t* row = rowptr(live ? i : 0) + 32 * s0 + 8 * (lane >> 4);
+// 8 E4M3 codes (two dwords) as a bf16 B fragment: the conversion widens two codes to fp32
+// exactly, and every E4M3 value is a bf16 value, so the upper half of each fp32 is the code's
+// bf16 pattern.
+__device__ __forceinline__ bf16x8v e4m3x8_bf16(uint32_t w0, uint32_t w1) {
+  const uint32_t w[2] = {w0, w1};
+  uint32_t o[4];
 #pragma unroll
-  for (int s = 0; s < WB; ++s)
-    if (s < n) B.b[s] = live ? *glb(reinterpret_cast<const u32x4*>(row + 32 * s)) : (u32x4){0u, 0u, 0u, 0u};
+  for (int i = 0; i < 2; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    o[2 * i] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
+    o[2 * i + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
+  }
+  const u32x4 v = {o[0], o[1], o[2], o[3]};
+  return __builtin_bit_cast(bf16x8v, v);
 }
-// acc += the tile in B (K steps s0 .. s0 + n - 1) against the split input sp
-__device__ __forceinline__ f32x4 mfma_regs(const WBuf& B, int n, const uint16_t* sp, int st, int s0, const uint16_t* zero,
-                                           f32x4 acc) {
-#pragma unroll
-  for (int s = 0; s < WB; ++s)
-    if (s < n)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_frag2(sp, st, s0 + s, zero), __builtin_bit_cast(bf16x8v, B.b[s]), acc, 0, 0, 0);
-  return acc;
-}
-// The 16-row tile at rows t0 .. t0 + 15 of the LDS rows w (row stride ws; rows >= nrows read row
-// t0), K steps s0 .. s0 + n - 1, against the split input sp.
-__device__ __forceinline__ f32x4 mfma_lds(const uint16_t* w, int ws, int t0, int nrows, int s0, int n, const uint16_t* sp,
-                                          int st, const uint16_t* zero) {
-  const int lane = fresh_tid() & 63;
-  const int row = t0 + (lane & 15) < nrows ? t0 + (lane & 15) : t0;
-  const uint16_t* wr = w + row * ws + 8 * (lane >> 4);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = s0; s < s0 + n; ++s)
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_frag2(sp, st, s, zero), *reinterpret_cast<const bf16x8v*>(wr + 32 * s), acc,
-                                                  0, 0, 0);
-  return acc;
-}
-
-template <typename WT, int RR, int KK, typename RowFn>
-__device__ __forceinline__ void wb_issue(WBuf& B, int nrows, int ncols, RowFn rowptr) {
-  static_assert(RR * KK <= WB, "chunk exceeds the weight buffer");
-  constexpr int E = WTraits<WT>::E;
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  if (wave < NF) return;
-  const int units = ncols / E;
-#pragma unroll
-  for (int j = 0; j < RR; ++j) {
-    const int i = (wave - NF) + NB * j;
-    if (i < nrows) {
-      const GLB u32x4* p = glb(reinterpret_cast<const u32x4*>(rowptr(i)));
-#pragma unroll
-      for (int k = 0; k < KK; ++k) {
-        const int u = lane + 64 * k;
-        if (u < units) B.b[j * KK + k] = p[u];
-      }
-    }
+// The B fragment of step s of a buffer (bf16: entry s; E4M3: half s % 2 of entry s / 2)
+template <int KE>
+__device__ __forceinline__ bf16x8v b_frag(const WBuf& B, int s) {
+  if constexpr (KE == 1) {
+    return __builtin_bit_cast(bf16x8v, B.b[s]);
+  } else {
+    const u32x4 v = B.b[s / 2];
+    return s % 2 ? e4m3x8_bf16(v[2], v[3]) : e4m3x8_bf16(v[0], v[1]);
   }
 }
 
-// The weight rows of a layer, per workgroup (H in {1024, 2048}, 8 KV heads of dimension 128 and
-// 2 query heads per KV head), as 16-row MFMA tiles. Register tiles live in the back waves' two
+// B fragments of one 16-row weight tile into a back wave's buffer: K steps s0 .. s0 + n - 1
+// (n <= KPB, s0 a multiple of KE) of tile row l % 16; rowptr(i) is the byte address of row i's
+// first column (rows i >= nrows read as zeros). An odd E4M3 count also loads the step after the
+// last, which lies in the same row.
+template <typename WT, typename RowFn>
+__device__ __forceinline__ void wb_issue_tile(WBuf& B, int nrows, int s0, int n, RowFn rowptr) {
+  constexpr int ES = TkW<WT>::ES, KE = TkW<WT>::KE;
+  if (wave_id() < NF) return;
+  const int lane = fresh_tid() & 63, i = lane & 15;
+  const bool live = i < nrows;
+  const uint8_t* row = rowptr(live ? i : 0) + ES * kcol<KE>(s0, lane >> 4);
+  const int ne = (n + KE - 1) / KE;
+#pragma unroll
+  for (int s = 0; s < WB; ++s)
+    if (s < ne) B.b[s] = live ? *glb(reinterpret_cast<const u32x4*>(row + 64 * s)) : (u32x4){0u, 0u, 0u, 0u};
+}
+// acc += the tile in B (K steps s0 .. s0 + n - 1) against the split input sp
+template <typename WT>
+__device__ __forceinline__ f32x4 mfma_regs(const WBuf& B, int n, const uint16_t* sp, int st, int s0, const uint16_t* zero,
+                                           f32x4 acc) {
+  constexpr int KE = TkW<WT>::KE;
+#pragma unroll
+  for (int s = 0; s < KE * WB; ++s)
+    if (s < n)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_frag2<KE>(sp, st, s0 + s, zero), b_frag<KE>(B, s), acc, 0, 0, 0);
+  return acc;
+}
+// The 16-row tile at rows t0 .. t0 + 15 of the LDS rows w (row stride ws bytes; rows >= nrows
+// read row t0), K steps s0 .. s0 + n - 1, against the split input sp.
+template <typename WT>
+__device__ __forceinline__ f32x4 mfma_lds(const uint8_t* w, int ws, int t0, int nrows, int s0, int n, const uint16_t* sp,
+                                          int st, const uint16_t* zero) {
+  constexpr int ES = TkW<WT>::ES, KE = TkW<WT>::KE;
+  const int lane = fresh_tid() & 63, q = lane >> 4;
+  const int row = t0 + (lane & 15) < nrows ? t0 + (lane & 15) : t0;
+  const uint8_t* wr = w + row * ws;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = s0; s < s0 + n; ++s) {
+    bf16x8v bf;
+    if constexpr (KE == 1) {
+      bf = *reinterpret_cast<const bf16x8v*>(wr + ES * kcol<KE>(s, q));
+    } else {
+      const uint2 c = *reinterpret_cast<const uint2*>(wr + kcol<KE>(s, q));
+      bf = e4m3x8_bf16(c.x, c.y);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_frag2<KE>(sp, st, s, zero), bf, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// The weight rows of a layer, per workgroup (H in {512, 1024, 2048}, 8 KV heads of dimension 128
+// and 2 query heads per KV head), as 16-row MFMA tiles. Register tiles live in the back waves' two
 // buffers; back wave b = wave - NF takes a share of each tile's K steps:
-//   A0, A1   the 16 q/k/v rows x H: K steps [H/128 b, + H/128), the first 8 in A0      regs
+//   A0, A1   the 16 q/k/v rows x H: K steps [H/128 b, + H/128), the first KPB in A0     regs
 //   C        output projection: the H/32 rows x 256 of the XCD's heads, H/512 tiles
 //            split over the 4 back waves, 8 K steps each tile                        regs (buffer 0)
 //   DL       the first nl gate/up rows (gate rows first, then up rows) x H               LDS
 //   D0, D1   the remaining gate/up rows (at most one tile) x H, as A0, A1                regs
 //   E        down projection: H/32 rows x F/8                                             LDS
 // and after the last layer F0, F1, the semantic head's V/256 <= 16 rows x H, as A0, A1.
+// Row addresses are in bytes (ES per element).
 template <typename WT>
 __device__ __forceinline__ void tk_issue_a(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int half, int g, int r) {
+  constexpr int ES = TkW<WT>::ES, KPB = TkW<WT>::KPB;
   const int H = D.H, d = D.d, G = D.nq / D.nkv, qper = (G + 2) * d / NR, spw = H / 128;
   const int b = wave_id() - NF;
-  if (8 * half >= spw) return;
-  wb_issue_tile(B, qper, spw * b + 8 * half, min(8, spw - 8 * half), [&](int i) -> const uint16_t* {
+  if (KPB * half >= spw) return;
+  wb_issue_tile<WT>(B, qper, spw * b + KPB * half, min(KPB, spw - KPB * half), [&](int i) -> const uint8_t* {
     const int q = qper * r + i;
-    if (q < G * d) return reinterpret_cast<const uint16_t*>(W.wq) + (size_t)(G * d * g + q) * H;
-    if (q < (G + 1) * d) return reinterpret_cast<const uint16_t*>(W.wk) + (size_t)(d * g + q - G * d) * H;
-    return reinterpret_cast<const uint16_t*>(W.wv) + (size_t)(d * g + q - (G + 1) * d) * H;
+    if (q < G * d) return reinterpret_cast<const uint8_t*>(W.wq) + (size_t)ES * (G * d * g + q) * H;
+    if (q < (G + 1) * d) return reinterpret_cast<const uint8_t*>(W.wk) + (size_t)ES * (d * g + q - G * d) * H;
+    return reinterpret_cast<const uint8_t*>(W.wv) + (size_t)ES * (d * g + q - (G + 1) * d) * H;
   });
 }
 template <typename WT>
 __device__ __forceinline__ void tk_issue_c(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int half, int g, int r) {
+  constexpr int ES = TkW<WT>::ES;
   if (half) return;  // one buffer holds the whole output projection
   const int hper = D.H / NR, Gd = D.nq / D.nkv * D.d, T = hper / 16, wpt = NB / T, spw = (Gd / 32) / wpt;
   const int b = wave_id() - NF, t = b / wpt;
-  wb_issue_tile(B, 16, spw * (b % wpt), spw, [&](int i) -> const uint16_t* {
-    return reinterpret_cast<const uint16_t*>(W.wo) + (size_t)(hper * r + 16 * t + i) * (D.nq * D.d) + Gd * g;
+  wb_issue_tile<WT>(B, 16, spw * (b % wpt), spw, [&](int i) -> const uint8_t* {
+    return reinterpret_cast<const uint8_t*>(W.wo) + (size_t)ES * ((size_t)(hper * r + 16 * t + i) * (D.nq * D.d) + Gd * g);
   });
 }
-// gate/up row q of the rank: gate rows 0 .. fper, then up rows fper .. 2 fper
+// gate/up row q of the rank (gate rows 0 .. fper, then up rows fper .. 2 fper), as a byte address
 template <typename WT>
-__device__ __forceinline__ const WT* tk_gu_row(const KCONST TkDesc& D, const KCONST LayerW& W, int q, int g, int r) {
+__device__ __forceinline__ const uint8_t* tk_gu_row(const KCONST TkDesc& D, const KCONST LayerW& W, int q, int g, int r) {
   const int fx = D.F / NX, fper = fx / NR;
   const int f = fx * g + fper * r + (q < fper ? q : q - fper);
-  return reinterpret_cast<const WT*>(q < fper ? W.wg : W.wu) + (size_t)f * D.H;
+  return reinterpret_cast<const uint8_t*>(q < fper ? W.wg : W.wu) + (size_t)TkW<WT>::ES * f * D.H;
 }
 // A descriptor pointer as a wave-uniform value (each 32-bit half through readfirstlane, kept
 // unsigned so the low half never sign-extends into the high one).
-__device__ __forceinline__ const uint16_t* tk_uniform_ptr(const void* p) {
+__device__ __forceinline__ const uint8_t* tk_uniform_ptr(const void* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 
 // half c of the register tile of gate/up rows nl .. nd - 1 (past the nl rows held in LDS)
 template <typename WT>
 __device__ __forceinline__ void tk_issue_d(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int nl, int c, int g,
                                            int r) {
+  constexpr int ES = TkW<WT>::ES, KPB = TkW<WT>::KPB;
   const int nd = 2 * (D.F / NX / NR), spw = D.H / 128;
   const int b = wave_id() - NF;
-  if (nd <= nl || 8 * c >= spw) return;
+  if (nd <= nl || KPB * c >= spw) return;
   // the gate and up matrices are read through scalar loads first (a per-lane choice between two
   // descriptor pointers would otherwise become a per-lane descriptor read)
-  const uint16_t *wg = tk_uniform_ptr(W.wg), *wu = tk_uniform_ptr(W.wu);
+  const uint8_t *wg = tk_uniform_ptr(W.wg), *wu = tk_uniform_ptr(W.wu);
   const int fx = D.F / NX, fper = fx / NR;
-  wb_issue_tile(B, nd - nl, spw * b + 8 * c, min(8, spw - 8 * c), [&](int i) -> const uint16_t* {
+  wb_issue_tile<WT>(B, nd - nl, spw * b + KPB * c, min(KPB, spw - KPB * c), [&](int i) -> const uint8_t* {
     const int q = nl + i;
     const int f = fx * g + fper * r + (q < fper ? q : q - fper);
-    return (q < fper ? wg : wu) + (size_t)f * D.H;
+    return (q < fper ? wg : wu) + (size_t)ES * f * D.H;
   });
 }
 template <typename WT>
 __device__ __forceinline__ void tk_issue_f(WBuf& B, const KCONST TkDesc& D, int half) {
+  constexpr int ES = TkW<WT>::ES, KPB = TkW<WT>::KPB;
   const int vper = D.V / NWG, spw = D.H / 128;
   const int b = wave_id() - NF;
-  if (8 * half >= spw) return;
-  wb_issue_tile(B, vper, spw * b + 8 * half, min(8, spw - 8 * half), [&](int i) -> const uint16_t* {
-    return reinterpret_cast<const uint16_t*>(D.lm_head) + (size_t)(vper * blockIdx.x + i) * D.H;
+  if (KPB * half >= spw) return;
+  wb_issue_tile<WT>(B, vper, spw * b + KPB * half, min(KPB, spw - KPB * half), [&](int i) -> const uint8_t* {
+    return reinterpret_cast<const uint8_t*>(D.lm_head) + (size_t)ES * (vper * blockIdx.x + i) * D.H;
   });
 }
 
@@ -240,22 +285,28 @@ struct TkSmem {
   __align__(16) uint16_t hbp[2 * HST];  // SwiGLU slice of the XCD, in two parts
   __align__(16) uint16_t zero[8];
   float red[64];
-  __align__(16) uint16_t lw[TLW];  // weight rows copied by LDS-direct loads (gate/up rows, then down rows), padded
+  __align__(16) uint8_t lw[TLWB];  // weight rows copied by LDS-direct loads (gate/up rows, then down rows), padded
 };
 static_assert(NR * 10 >= NW * 2 * 16, "per-wave dot partials fit the combine buffer");
 // per-wave dot partials: [wave][set][row of the tile]
 __device__ __forceinline__ float* tk_pt(TkSmem& S, int wave, int set) { return S.cmb + (wave * 2 + set) * 16; }
 
 // Per-thread constants of one layer: norm gains of elements tid, tid + NT, tid + 2 NT, tid + 3 NT
-// (H <= 4 NT), and for the q/k waves the q- or k-norm gains of lanes lane, lane + 64.
+// (H <= 4 NT), and for the q/k waves the q- or k-norm gains of lanes lane, lane + 64. With E4M3
+// rows also the row scales of the rank's rows that thread tid emits: q/k/v row tid (sq), output
+// row tid (so), gate and up row tid (sg, su), down row tid (sd), and after the last layer the
+// semantic head row tid (sh); sg, su, sd are loaded one layer ahead into sgn, sun, sdn (the
+// current ones are still needed when the next layer's constants arrive).
 struct TkConsts {
   float an[4], mn[4], qk[2];
+  float sq, so, sg, su, sd, sh, sgn, sun, sdn;
 };
 
 template <typename WT>
-__device__ __forceinline__ void tk_load_consts(TkConsts& c, const KCONST TkDesc& D, const KCONST LayerW& W) {
-  const WT* an = reinterpret_cast<const WT*>(W.attn_norm);
-  const WT* mn = reinterpret_cast<const WT*>(W.mlp_norm);
+__device__ __forceinline__ void tk_load_consts(TkConsts& c, const KCONST TkDesc& D, int l, int g, int r) {
+  const KCONST LayerW& W = D.layer[l];
+  const uint16_t* an = reinterpret_cast<const uint16_t*>(W.attn_norm);  // gains are bf16 for every weight type
+  const uint16_t* mn = reinterpret_cast<const uint16_t*>(W.mlp_norm);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = threadIdx.x + k * NT;
@@ -265,49 +316,66 @@ __device__ __forceinline__ void tk_load_consts(TkConsts& c, const KCONST TkDesc&
   const int wave = wave_id(), lane = threadIdx.x & 63;
   c.qk[0] = c.qk[1] = 1.f;
   if (wave < 3) {
-    const WT* gn = reinterpret_cast<const WT*>(wave < 2 ? W.q_norm : W.k_norm);
+    const uint16_t* gn = reinterpret_cast<const uint16_t*>(wave < 2 ? W.q_norm : W.k_norm);
     c.qk[0] = to_f32(glb(gn)[lane]);
     c.qk[1] = to_f32(glb(gn)[lane + 64]);
+  }
+  c.sq = c.so = c.sgn = c.sun = c.sdn = c.sh = 1.f;
+  if constexpr (TkW<WT>::ES == 1) {
+    const KCONST LayerS& Sc = D.scale[l];
+    const int tid = threadIdx.x, d = D.d, G = D.nq / D.nkv, qper = (G + 2) * d / NR, hper = D.H / NR;
+    const int fx = D.F / NX, fper = fx / NR;
+    if (tid < qper) {
+      const int q = qper * r + tid;
+      c.sq = q < G * d ? glb(Sc.wq)[G * d * g + q] : q < (G + 1) * d ? glb(Sc.wk)[d * g + q - G * d] : glb(Sc.wv)[d * g + q - (G + 1) * d];
+    }
+    if (tid < hper) {
+      c.so = glb(Sc.wo)[hper * r + tid];
+      c.sdn = glb(Sc.wd)[hper * r + tid];
+    }
+    if (tid < fper) {
+      c.sgn = glb(Sc.wg)[fx * g + fper * r + tid];
+      c.sun = glb(Sc.wu)[fx * g + fper * r + tid];
+    }
   }
 }
 
 // A block of weight rows copied into LDS in parts, by the front (FRONT) or back waves, with
 // LDS-direct loads: row i (at b0 + i * stride for i < split, else b1 + (i - split) * stride, upr
-// 16-byte units) lands at dst[i * ldst ..], ldst = 8 upr + LPAD elements, so the rows of an MFMA
+// 16-byte units) lands at dst[i * ldst ..], ldst = 16 upr + LPADB bytes, so the rows of an MFMA
 // fragment fall on different LDS banks. One instruction moves up to 64 consecutive units of one
 // row (cpr instructions a row; lanes past the row's end are off). part(n) issues at most n more
 // instructions per wave: a wave that issues more than its share of the CU's memory queue holds
 // stalls until the queue drains, so large copies go in parts spread over the barrier intervals of
 // a layer. A copy has landed once the issuing wave's vector-memory counter has passed it.
-template <typename WT, bool FRONT>
+template <bool FRONT>
 struct RowCopy {
-  const WT *b0, *b1;
+  const uint8_t *b0, *b1;
   long long stride;
   int split, upr, cpr, ninst, ldst, j;
 
-  __device__ __forceinline__ void begin(const WT* b0_, const WT* b1_, int split_, long long stride_, int nrows, int upr_) {
-    b0 = b0_;
-    b1 = b1_;
+  // b0, b1: byte addresses of rows 0 and split; stride: bytes between rows; upr: 16-byte units a row
+  __device__ __forceinline__ void begin(const void* b0_, const void* b1_, int split_, long long stride_, int nrows, int upr_) {
+    b0 = reinterpret_cast<const uint8_t*>(b0_);
+    b1 = reinterpret_cast<const uint8_t*>(b1_);
     split = split_;
     stride = stride_;
     upr = upr_;
     cpr = (upr_ + 63) / 64;
     ninst = nrows * cpr;
-    ldst = 8 * upr_ + LPAD;
+    ldst = 16 * upr_ + LPADB;
     j = FRONT ? wave_id() : wave_id() - NF;
   }
-  __device__ __forceinline__ void part(uint16_t* dst, int n) {
-    constexpr int E = WTraits<WT>::E;
-    static_assert(E == 8, "LDS-direct rows are bf16");
+  __device__ __forceinline__ void part(uint8_t* dst, int n) {
     static_assert(NF == NB, "front and back wave sets of one size");
     if ((wave_id() < NF) != FRONT) return;
     const int lane = threadIdx.x & 63;
     for (int c = 0; c < n && j < ninst; ++c, j += NF) {
       const int row = j / cpr, ch = j - row * cpr;
       const int u = 64 * ch + lane;
-      const WT* src = (row < split ? b0 + row * stride : b1 + (row - split) * stride) + (u < upr ? u : 0) * E;
+      const uint8_t* src = (row < split ? b0 + row * stride : b1 + (row - split) * stride) + 16 * (u < upr ? u : 0);
       if (u < upr)
-        __builtin_amdgcn_global_load_lds((const GLB void*)src, (__attribute__((address_space(3))) void*)&dst[row * ldst + 64 * E * ch],
+        __builtin_amdgcn_global_load_lds((const GLB void*)src, (__attribute__((address_space(3))) void*)&dst[row * ldst + 1024 * ch],
                                          16, 0, 0);
     }
   }
@@ -522,13 +590,17 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
 
 // The constants the layer after l needs (the final-norm gains in c.an after the last layer).
 template <typename WT>
-__device__ __forceinline__ void tk_next_consts(TkConsts& c, const KCONST TkDesc& D, int l, int tid) {
+__device__ __forceinline__ void tk_next_consts(TkConsts& c, const KCONST TkDesc& D, int l, int tid, int g, int r) {
   if (l + 1 < D.n_layers) {
-    tk_load_consts<WT>(c, D, D.layer[l + 1]);
+    tk_load_consts<WT>(c, D, l + 1, g, r);
   } else {
-    const WT* f = reinterpret_cast<const WT*>(D.final_norm);
+    const uint16_t* f = reinterpret_cast<const uint16_t*>(D.final_norm);
 #pragma unroll
     for (int k = 0; k < 4; ++k) c.an[k] = tid + k * NT < D.H ? to_f32(glb(f)[tid + k * NT]) : 0.f;
+    if constexpr (TkW<WT>::ES == 1) {
+      const int vper = D.V / NWG;
+      c.sh = tid < vper ? glb(D.head_scale)[vper * blockIdx.x + tid] : 1.f;
+    }
   }
 }
 
@@ -545,10 +617,13 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   const int g = xcd_id(), r = blockIdx.x / NX, tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
   const int H = D.H, d = D.d, G = D.nq / D.nkv;
   const int qrows = (G + 2) * d, qper = qrows / NR, hper = H / NR, fx = D.F / NX, fper = fx / NR;
+  constexpr int ES = TkW<WT>::ES, KPB = TkW<WT>::KPB;
+  // an E4M3 row's sum times its scale (bf16 rows have none)
+  auto scl = [](float v, float s) { return ES == 1 ? v * s : v; };
   TkConsts c;
-  tk_load_consts<WT>(c, D, D.layer[0]);
+  tk_load_consts<WT>(c, D, 0, g, r);
   const int nd = 2 * fper;                                // gate + up rows of the rank
-  const int nl = min(min(nd, TLW / (H + LPAD)), 32);      // gate/up rows held in LDS (at most 2 tiles)
+  const int nl = min(min(nd, TLWB / (ES * H + LPADB)), 32);  // gate/up rows held in LDS (at most 2 tiles)
   const int b = wave - NF;                                // back wave index (register tiles)
   // K split of the tiles: register tiles over the 4 back waves, LDS tiles over all 8 waves
   const int ksh = H / 32;                                 // K steps of a hidden-wide row
@@ -556,15 +631,15 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   const int tc = hper / 16, wpc = NB / tc, spc = (G * d / 32) / wpc;  // output projection tiles
   const int tgl = (nl + 15) / 16, wpg = NW / tgl, spg = ksh / wpg;    // LDS gate/up tiles
   const int tdn = hper / 16, wpd = NW / tdn, spd = (fx / 32) / wpd;   // down tiles
-  const int gld = H + LPAD, dld = fx + LPAD;              // LDS row strides of the gate/up and down rows
+  const int gld = ES * H + LPADB, dld = ES * fx + LPADB;  // LDS row strides (bytes) of the gate/up and down rows
   // The LDS gate/up block of a layer goes in parts (instructions per back wave, 32 for the largest
   // block): 4 while the previous layer's down exchange runs, 4 after the q/k/v rows, 6 during the
   // q/k/v exchange, 4 + 6 + 4 in the attention and the rest during its last exchange.
-  RowCopy<WT, false> gu;
+  RowCopy<false> gu;
   auto gu_begin = [&](const KCONST LayerW& W) {
-    gu.begin(tk_gu_row<WT>(D, W, 0, g, r), tk_gu_row<WT>(D, W, fper, g, r), fper, H, nl, H / 8);
+    gu.begin(tk_gu_row<WT>(D, W, 0, g, r), tk_gu_row<WT>(D, W, fper, g, r), fper, (long long)ES * H, nl, ES * H / 16);
   };
-  RowCopy<WT, true> dn;  // the down rows, by the front waves, in two parts
+  RowCopy<true> dn;  // the down rows, by the front waves, in two parts
   WBuf X0, X1;
   tk_issue_a<WT>(X0, D, D.layer[0], 0, g, r);
   tk_issue_a<WT>(X1, D, D.layer[0], 1, g, r);
@@ -593,19 +668,22 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     const KCONST LayerW& W = D.layer[l];
     const bool last = l + 1 == D.n_layers;
     TTS_STAMP(50);
+    c.sg = c.sgn;  // this layer's gate/up/down row scales (E4M3)
+    c.su = c.sun;
+    c.sd = c.sdn;
     // q/k/v tile (A0: X0, A1: X1); the output projection tiles (C) follow in buffer 0
     tk_rmsnorm(S.xs, H, c.an, D.eps, S.xnp, S.red, l > 0 ? S.xs + H : nullptr);
     if (wave >= NF) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma_regs(X0, min(8, spq), S.xnp, XST, spq * b, S.zero, acc);
-      acc = mfma_regs(X1, spq - 8, S.xnp, XST, spq * b + 8, S.zero, acc);
+      acc = mfma_regs<WT>(X0, min(KPB, spq), S.xnp, XST, spq * b, S.zero, acc);
+      acc = mfma_regs<WT>(X1, spq - KPB, S.xnp, XST, spq * b + KPB, S.zero, acc);
       if (lane < 16) tk_pt(S, wave, 0)[lane] = parts2(acc);
     }
     tk_issue_c<WT>(X0, D, W, 0, g, r);
     gu.part(S.lw, 4);
     lds_barrier();
     TTS_STAMP(51);
-    if (!slice_gather<1, KQ, PF>(X, qper, qrows, [&](int e, int) { return tile_sum(NF, NB, 0, 0, e); }, S.qkv, tag, iring, g, r,
+    if (!slice_gather<1, KQ, PF>(X, qper, qrows, [&](int e, int) { return scl(tile_sum(NF, NB, 0, 0, e), c.sq); }, S.qkv, tag, iring, g, r,
                                  [&] { gu.part(S.lw, 6); })) {
       ok = false;
       break;
@@ -622,7 +700,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     // output projection tiles (C: X0), residual; the register gate/up tile follows (D0 now, D1
     // during the exchange)
     if (wave >= NF) {
-      const f32x4 acc = mfma_regs(X0, spc, S.obp, OST, spc * (b % wpc), S.zero, (f32x4){0.f, 0.f, 0.f, 0.f});
+      const f32x4 acc = mfma_regs<WT>(X0, spc, S.obp, OST, spc * (b % wpc), S.zero, (f32x4){0.f, 0.f, 0.f, 0.f});
       if (lane < 16) tk_pt(S, wave, 0)[lane] = parts2(acc);
     }
     tk_issue_d<WT>(X0, D, W, nl, 0, g, r);
@@ -631,7 +709,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     if (!reduce_gather_p<1, THMAX, KT, PF>(
             X,
             [&](auto emit) {
-              for (int i = fresh_tid(); i < hper; i += NT) emit(i, 0, tile_sum(NF, wpc, 0, i / 16, i % 16));
+              for (int i = fresh_tid(); i < hper; i += NT) emit(i, 0, scl(tile_sum(NF, wpc, 0, i / 16, i % 16), c.so));
             },
             S.xs, xn, H, true, tag, iring, cpar, g, r, [&] { tk_issue_d<WT>(X1, D, W, nl, 1, g, r); })) {
       ok = false;
@@ -648,25 +726,26 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     lds_barrier();
     {
       const int t = wave / wpg;
-      const f32x4 acc = mfma_lds(S.lw, gld, 16 * t, nl, spg * (wave % wpg), spg, S.xnp, XST, S.zero);
+      const f32x4 acc = mfma_lds<WT>(S.lw, gld, 16 * t, nl, spg * (wave % wpg), spg, S.xnp, XST, S.zero);
       if (lane < 16) tk_pt(S, wave, 0)[lane] = parts2(acc);
     }
     lds_barrier();
-    const int dparts = (hper * ((fx / 8 + 63) / 64) + 2 * NF - 1) / (2 * NF);  // first half, per front wave
+    const int dparts = (hper * ((ES * fx / 16 + 63) / 64) + 2 * NF - 1) / (2 * NF);  // first half, per front wave
     if (wave < NF) {
-      dn.begin(reinterpret_cast<const WT*>(W.wd) + (size_t)(hper * r) * D.F + fx * g, nullptr, hper, D.F, hper, fx / 8);
+      dn.begin(reinterpret_cast<const uint8_t*>(W.wd) + (size_t)ES * ((size_t)(hper * r) * D.F + fx * g), nullptr, hper,
+               (long long)ES * D.F, hper, ES * fx / 16);
       dn.part(S.lw, dparts);
-      tk_next_consts<WT>(c, D, l, tid);
+      tk_next_consts<WT>(c, D, l, tid, g, r);
     } else {
       if (nd > nl) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma_regs(X0, min(8, spq), S.xnp, XST, spq * b, S.zero, acc);
-        acc = mfma_regs(X1, spq - 8, S.xnp, XST, spq * b + 8, S.zero, acc);
+        acc = mfma_regs<WT>(X0, min(KPB, spq), S.xnp, XST, spq * b, S.zero, acc);
+        acc = mfma_regs<WT>(X1, spq - KPB, S.xnp, XST, spq * b + KPB, S.zero, acc);
         if (lane < 16) tk_pt(S, wave, 1)[lane] = parts2(acc);
       }
       if (!last) tk_issue_a<WT>(X0, D, D.layer[l + 1], 0, g, r);
       else tk_issue_f<WT>(X0, D, 0);
-      tk_next_consts<WT>(c, D, l, tid);
+      tk_next_consts<WT>(c, D, l, tid, g, r);
     }
     lds_barrier();
     TTS_STAMP(61);
@@ -675,7 +754,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     if (!slice_gather_pe<1, KH, PF>(
             X, fper, fx,
             [&](auto emit) {
-              for (int i = fresh_tid(); i < fper; i += NT) emit(i, 0, silu(gu_val(i)) * gu_val(fper + i));
+              for (int i = fresh_tid(); i < fper; i += NT) emit(i, 0, silu(scl(gu_val(i), c.sg)) * scl(gu_val(fper + i), c.su));
             },
             [&](int i, float v) { put2(S.hbp, HST, i, v); }, tag, iring, g, r, [&] {
               if (wave < NF) {
@@ -695,7 +774,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     lds_barrier();
     {
       const int t = wave / wpd;
-      const f32x4 acc = mfma_lds(S.lw, dld, 16 * t, hper, spd * (wave % wpd), spd, S.hbp, HST, S.zero);
+      const f32x4 acc = mfma_lds<WT>(S.lw, dld, 16 * t, hper, spd * (wave % wpd), spd, S.hbp, HST, S.zero);
       if (lane < 16) tk_pt(S, wave, 0)[lane] = parts2(acc);
     }
     lds_barrier();
@@ -703,7 +782,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     if (!reduce_gather_p<1, THMAX, KT, PF>(
             X,
             [&](auto emit) {
-              for (int i = fresh_tid(); i < hper; i += NT) emit(i, 0, tile_sum(0, wpd, 0, i / 16, i % 16));
+              for (int i = fresh_tid(); i < hper; i += NT) emit(i, 0, scl(tile_sum(0, wpd, 0, i / 16, i % 16), c.sd));
             },
             S.xs, xn, H, true, tag, iring, cpar, g, r, [&] {
               if (!last) {
@@ -723,12 +802,12 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     const int vper = D.V / NWG;
     if (wave >= NF) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mfma_regs(X0, min(8, spq), S.xnp, XST, spq * b, S.zero, acc);
-      acc = mfma_regs(X1, spq - 8, S.xnp, XST, spq * b + 8, S.zero, acc);
+      acc = mfma_regs<WT>(X0, min(KPB, spq), S.xnp, XST, spq * b, S.zero, acc);
+      acc = mfma_regs<WT>(X1, spq - KPB, S.xnp, XST, spq * b + KPB, S.zero, acc);
       if (lane < 16) tk_pt(S, wave, 0)[lane] = parts2(acc);
     }
     lds_barrier();
-    for (int i = tid; i < vper; i += NT) glb(D.logits)[vper * blockIdx.x + i] = tile_sum(NF, NB, 0, 0, i);
+    for (int i = tid; i < vper; i += NT) glb(D.logits)[vper * blockIdx.x + i] = scl(tile_sum(NF, NB, 0, 0, i), c.sh);
   }
   TTS_STAMP(65);
   if (blockIdx.x == 0 && tid == 0) {

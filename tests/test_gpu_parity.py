@@ -499,10 +499,10 @@ def fp8_model(request):
 @pytest.mark.parametrize("mode", ["persistent", "kernels"])
 def test_fp8_teacher_forced_step_parity(fp8_model, mode):
     """Weight-only E4M3 decode against the oracle run on the matrices the codes and row scales
-    stand for, with the CodePredictor frame on the persistent kernel (E4M3 rows and row scales in
-    its register buffers; the default) and on the per-op kernels. The Talker runs per-op kernels,
-    the prompt the MFMA GEMMs. Both sides compute in fp32 from the same weights, so the bf16
-    models' bar applies."""
+    stand for, on the persistent kernels (the default: the Talker step with E4M3 tiles widened to
+    bf16 for the MFMAs, the CodePredictor frame with E4M3 rows in its register buffers, row scales
+    applied to each row's sum) and on the per-op kernels; the prompt runs on the MFMA GEMMs. Both
+    sides compute in fp32 from the same weights, so the bf16 models' bar applies."""
     name, model, w = fp8_model
     orc = OracleModel(w, model.as_dict(), np.float32)
     ids = synth.random_ids(16, model.text_vocab, seed=1)
@@ -511,8 +511,8 @@ def test_fp8_teacher_forced_step_parity(fp8_model, mode):
     del orc
     dec, dw = make_decoder(model, 1, 64 + 240, 240, w)
     default, supported = dec.exec_mode()
-    assert supported == tts.PERSISTENT_CODEPRED and default == tts.EXEC_PERSISTENT, \
-        "E4M3 weights: the persistent CodePredictor kernel, per-op Talker kernels"
+    assert supported == tts.PERSISTENT_CODEPRED | tts.PERSISTENT_TALKER and default == tts.EXEC_PERSISTENT, \
+        "E4M3 weights: both persistent kernels"
     dec.set_exec_mode(tts.EXEC_PERSISTENT if mode == "persistent" else tts.EXEC_KERNELS)
     assert dec.prefill_mode() == tts.PREFILL_GEMM
     print(f"{name} {mode}: running", flush=True)

@@ -405,11 +405,15 @@ __device__ __forceinline__ bool cp_layer(Ctx& c, Wl& R, int l, int j, int p0, Ne
     const float wt = t <= p ? expf(sc - mx) : 0.f;
     const float ws = row16_sum(e == 0 ? wt : 0.f);
     const float ls = (rl(ws, 0) + rl(ws, 16)) + (rl(ws, 32) + rl(ws, 48));
+    // all P rows in one unrolled pass, so their LDS reads go out together; rows past p (stale,
+    // possibly never written) are replaced by row p, whose weight there is 0
     float o0 = 0.f, o1 = 0.f;
-    for (int tt = 0; tt <= p; ++tt) {
+#pragma unroll
+    for (int tt = 0; tt < P; ++tt) {
+      const int tr = min(tt, p);
       const float wv = rl(wt, 4 * tt);
-      o0 = fmaf(wv, vc[tt][lane], o0);
-      o1 = fmaf(wv, vc[tt][lane + 64], o1);
+      o0 = fmaf(wv, vc[tr][lane], o0);
+      o1 = fmaf(wv, vc[tr][lane + 64], o1);
     }
     put_split(S.osp, SO, m, h * D + lane, o0 / ls);
     put_split(S.osp, SO, m, h * D + lane + 64, o1 / ls);

@@ -147,17 +147,28 @@ __device__ __forceinline__ bf16x8v b_frag(const WBuf& B, int s) {
 // (n <= KPB, s0 a multiple of KE) of tile row l % 16; rowptr(i) is the byte address of row i's
 // first column (rows i >= nrows read as zeros). An odd E4M3 count also loads the step after the
 // last, which lies in the same row.
+// Zeros in every entry of a buffer. Paths that issue no tile (the front waves, a buffer a shape
+// leaves unused) clear it instead, so every path writes the whole buffer: the earlier contents are
+// dead at each issue point and the compiler keeps no copy of them (a copy would wait for the
+// loads in flight).
+__device__ __forceinline__ void wb_clear(WBuf& B) {
+#pragma unroll
+  for (int s = 0; s < WB; ++s) B.b[s] = (u32x4){0u, 0u, 0u, 0u};
+}
 template <typename WT, typename RowFn>
 __device__ __forceinline__ void wb_issue_tile(WBuf& B, int nrows, int s0, int n, RowFn rowptr) {
   constexpr int ES = TkW<WT>::ES, KE = TkW<WT>::KE;
-  if (wave_id() < NF) return;
+  if (wave_id() < NF) return wb_clear(B);
   const int lane = fresh_tid() & 63, i = lane & 15;
   const bool live = i < nrows;
   const uint8_t* row = rowptr(live ? i : 0) + ES * kcol<KE>(s0, lane >> 4);
   const int ne = (n + KE - 1) / KE;
 #pragma unroll
-  for (int s = 0; s < WB; ++s)
-    if (s < ne) B.b[s] = live ? *glb(reinterpret_cast<const u32x4*>(row + 64 * s)) : (u32x4){0u, 0u, 0u, 0u};
+  for (int s = 0; s < WB; ++s) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (s < ne && live) v = *glb(reinterpret_cast<const u32x4*>(row + 64 * s));
+    B.b[s] = v;
+  }
 }
 // acc += the tile in B (K steps s0 .. s0 + n - 1) against the split input sp
 template <typename WT>
@@ -209,7 +220,7 @@ __device__ __forceinline__ void tk_issue_a(WBuf& B, const KCONST TkDesc& D, cons
   constexpr int ES = TkW<WT>::ES, KPB = TkW<WT>::KPB;
   const int H = D.H, d = D.d, G = D.nq / D.nkv, qper = (G + 2) * d / NR, spw = H / 128;
   const int b = wave_id() - NF;
-  if (KPB * half >= spw) return;
+  if (KPB * half >= spw) return wb_clear(B);
   wb_issue_tile<WT>(B, qper, spw * b + KPB * half, min(KPB, spw - KPB * half), [&](int i) -> const uint8_t* {
     const int q = qper * r + i;
     if (q < G * d) return reinterpret_cast<const uint8_t*>(W.wq) + (size_t)ES * (G * d * g + q) * H;
@@ -220,7 +231,7 @@ __device__ __forceinline__ void tk_issue_a(WBuf& B, const KCONST TkDesc& D, cons
 template <typename WT>
 __device__ __forceinline__ void tk_issue_c(WBuf& B, const KCONST TkDesc& D, const KCONST LayerW& W, int half, int g, int r) {
   constexpr int ES = TkW<WT>::ES;
-  if (half) return;  // one buffer holds the whole output projection
+  if (half) return wb_clear(B);  // one buffer holds the whole output projection
   const int hper = D.H / NR, Gd = D.nq / D.nkv * D.d, T = hper / 16, wpt = NB / T, spw = (Gd / 32) / wpt;
   const int b = wave_id() - NF, t = b / wpt;
   wb_issue_tile<WT>(B, 16, spw * (b % wpt), spw, [&](int i) -> const uint8_t* {
@@ -250,7 +261,7 @@ __device__ __forceinline__ void tk_issue_d(WBuf& B, const KCONST TkDesc& D, cons
   constexpr int ES = TkW<WT>::ES, KPB = TkW<WT>::KPB;
   const int nd = 2 * (D.F / NX / NR), spw = D.H / 128;
   const int b = wave_id() - NF;
-  if (nd <= nl || KPB * c >= spw) return;
+  if (nd <= nl || KPB * c >= spw) return wb_clear(B);
   // the gate and up matrices are read through scalar loads first (a per-lane choice between two
   // descriptor pointers would otherwise become a per-lane descriptor read)
   const uint8_t *wg = tk_uniform_ptr(W.wg), *wu = tk_uniform_ptr(W.wu);
@@ -266,7 +277,7 @@ __device__ __forceinline__ void tk_issue_f(WBuf& B, const KCONST TkDesc& D, int 
   constexpr int ES = TkW<WT>::ES, KPB = TkW<WT>::KPB;
   const int vper = D.V / NWG, spw = D.H / 128;
   const int b = wave_id() - NF;
-  if (KPB * half >= spw) return;
+  if (KPB * half >= spw) return wb_clear(B);
   wb_issue_tile<WT>(B, vper, spw * b + KPB * half, min(KPB, spw - KPB * half), [&](int i) -> const uint8_t* {
     return reinterpret_cast<const uint8_t*>(D.lm_head) + (size_t)ES * (vper * blockIdx.x + i) * D.H;
   });

@@ -271,7 +271,7 @@ bool xtp_capable(const tts_config& c) {
 // Talker hidden of 2048.
 bool xcp_capable(const tts_config& c) {
   const tts_stack_cfg& p = c.codepred;
-  if (c.weight_dtype != TTS_DTYPE_BF16) return false;
+  if (c.weight_dtype != TTS_DTYPE_BF16 && c.weight_dtype != TTS_DTYPE_FP8_E4M3) return false;
   if (p.hidden != xcp::H || p.ffn != xcp::F || p.n_q_heads != xcp::G * xcp::NX || p.n_kv_heads != xcp::NX ||
       p.head_dim != xcp::D || p.vocab != xcp::V)
     return false;
@@ -359,7 +359,7 @@ struct tts_ctx {
   char* scratch = nullptr;          // this device's static scratch array (device address)
   bool use_scratch = false;         // persistent launches take the *_s descriptors
   bool xtk_ok = false;   // persistent Talker step supported
-  bool xcp_ok = false;   // the lean CodePredictor kernel supports the config (bf16)
+  bool xcp_ok = false;   // the lean CodePredictor kernel supports the config (bf16 or E4M3)
   int32_t dev_mask = 0;  // persistent kernels the device allows (tts_persistent_allowed)
   // exchange error word seen from the host without blocking (device_err_check)
   uint32_t* errh = nullptr;  // pinned host copy
@@ -976,7 +976,8 @@ int codepred_frame_xtp(tts_ctx* ctx, const int32_t* semantic, const int32_t* for
   call.use_frame = use_frame;
   call.logits = logits_out;
   call.next_tok = nullptr;
-  if (ctx->xcp_ok) hipLaunchKernelGGL(xcp::k_cp_frame, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
+  if (ctx->xcp_ok && ctx->fp8()) hipLaunchKernelGGL(xcp::k_cp_frame<uint8_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
+  else if (ctx->xcp_ok) hipLaunchKernelGGL(xcp::k_cp_frame<uint16_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
   else if (ctx->fp8()) hipLaunchKernelGGL(xtp::k_cp_frame<uint8_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
   else hipLaunchKernelGGL(xtp::k_cp_frame<uint16_t>, dim3(xtp::NWG), dim3(xtp::NT), 0, ctx->stream, call);
   HIP_LAUNCH_CHECK();
@@ -1201,9 +1202,11 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
     if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, ctx->device) != hipSuccess) xccs = 0;
     dd.xccs = xccs;
     int occ = 0;
-    const void* cpk = ctx->xcp_ok ? reinterpret_cast<const void*>(xcp::k_cp_frame)
-                    : cfg->weight_dtype == TTS_DTYPE_FP8_E4M3 ? reinterpret_cast<const void*>(xtp::k_cp_frame<uint8_t>)
-                                                              : reinterpret_cast<const void*>(xtp::k_cp_frame<uint16_t>);
+    const bool e8 = cfg->weight_dtype == TTS_DTYPE_FP8_E4M3;
+    const void* cpk = ctx->xcp_ok ? (e8 ? reinterpret_cast<const void*>(xcp::k_cp_frame<uint8_t>)
+                                        : reinterpret_cast<const void*>(xcp::k_cp_frame<uint16_t>))
+                                  : (e8 ? reinterpret_cast<const void*>(xtp::k_cp_frame<uint8_t>)
+                                        : reinterpret_cast<const void*>(xtp::k_cp_frame<uint16_t>));
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, cpk, xtp::NT, 0) != hipSuccess) occ = 0;
     dd.codepred_wg_per_cu = occ;
     occ = 0;
@@ -1370,8 +1373,12 @@ int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* co
       // projected codebook rows P E_ac[j][a] for steps 2..15 of the lean CodePredictor kernel
       float* T = (float*)(ctx->ws + ctx->L.ptab);
       const int R = c.n_acoustic * p.vocab, N = p.hidden, K = c.talker.hidden;
-      hipLaunchKernelGGL(k_proj_table, dim3(N / 64, (R + 63) / 64), dim3(256), 0, ctx->stream, (const uint16_t*)ctx->embed_ac,
-                         (const uint16_t*)ctx->proj, T, R, N, K);
+      if (ctx->fp8())
+        hipLaunchKernelGGL(k_proj_table<uint8_t>, dim3(N / 64, (R + 63) / 64), dim3(256), 0, ctx->stream,
+                           (const uint16_t*)ctx->embed_ac, (const uint8_t*)ctx->proj, D.proj_scale, T, R, N, K);
+      else
+        hipLaunchKernelGGL(k_proj_table<uint16_t>, dim3(N / 64, (R + 63) / 64), dim3(256), 0, ctx->stream,
+                           (const uint16_t*)ctx->embed_ac, (const uint16_t*)ctx->proj, (const float*)nullptr, T, R, N, K);
       HIP_LAUNCH_CHECK();
       D.ptab = T;
     }

@@ -281,8 +281,13 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
 // sum_k E[a][k] P[i][k] in fp32 (T [R][N]). A product of two bf16 values is exact in fp32 and k
 // runs in order, so T holds P E[a] up to the order of its sums, the same on every run. One 64 x 64
 // tile of T per workgroup (16 x 16 threads, 4 x 4 outputs each); K % 32 == 0. Weight preparation,
-// run once per weight binding.
-__global__ __launch_bounds__(256) void k_proj_table(const uint16_t* E, const uint16_t* P, float* T, int R, int N, int K) {
+// run once per weight binding. With E4M3 codes for P (PT = uint8_t), row i of P is pscale[i] times
+// its codes: the codes are widened exactly and T[a][i] is the code sum times pscale[i].
+__device__ __forceinline__ float proj_val(uint16_t v) { return to_f32(v); }
+__device__ __forceinline__ float proj_val(uint8_t v) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)v, false)[0]; }
+template <typename PT>
+__global__ __launch_bounds__(256) void k_proj_table(const uint16_t* E, const PT* P, const float* pscale, float* T, int R, int N,
+                                                    int K) {
   __shared__ float Es[32][65];  // [k][row of the tile]
   __shared__ float Ps[32][65];  // [k][column of the tile]
   const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
@@ -294,7 +299,7 @@ __global__ __launch_bounds__(256) void k_proj_table(const uint16_t* E, const uin
     for (int e = tid; e < 64 * 32; e += 256) {
       const int rr = e / 32, kk = e % 32;
       Es[kk][rr] = r0 + rr < R ? to_f32(E[(size_t)(r0 + rr) * K + k0 + kk]) : 0.f;
-      Ps[kk][rr] = c0 + rr < N ? to_f32(P[(size_t)(c0 + rr) * K + k0 + kk]) : 0.f;
+      Ps[kk][rr] = c0 + rr < N ? proj_val(P[(size_t)(c0 + rr) * K + k0 + kk]) : 0.f;
     }
     __syncthreads();
     for (int kk = 0; kk < 32; ++kk) {
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(256) void k_proj_table(const uint16_t* E, const uin
   for (int i = 0; i < 4; ++i)
     for (int q = 0; q < 4; ++q) {
       const int row = r0 + tr + 16 * i, col = c0 + tc + 16 * q;
-      if (row < R && col < N) T[(size_t)row * N + col] = acc[i][q];
+      if (row < R && col < N) T[(size_t)row * N + col] = pscale ? acc[i][q] * pscale[col] : acc[i][q];
     }
 }
 

@@ -66,6 +66,11 @@ constexpr int KX = 256;          // input-projection columns per XCD (Talker hid
 constexpr int MAXL = 5;          // CodePredictor layers supported
 constexpr int P = 16;            // CodePredictor positions per frame
 constexpr int KVS = 132;         // LDS row stride of the K/V rows (padded against bank conflicts)
+// Row scales of the E4M3 matrices a workgroup uses, in LDS: per layer its q/k/v rows (16), output
+// rows (32), gate and up rows (12 each) and down rows (32); then the 15 heads' 8 rows; then the
+// input projection's 32 rows.
+constexpr int SCQ = 0, SCO = SCQ + QPER, SCG = SCO + HPER, SCU = SCG + FPER, SCD = SCU + FPER, SCL = SCD + HPER;
+constexpr int SCH = MAXL * SCL, SCP = SCH + 15 * VPER, SCN = SCP + HPER;
 // LDS row strides (bf16 elements) of the split inputs: 64 bytes past the row, so the parts of one
 // input row fall on different banks
 constexpr int SH = H + 32;
@@ -88,12 +93,25 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 //   dn   down rows 16 (w / 4) .. + 15 of the rank, K steps 3 (w % 4) .. + 2 (of 12)
 // (Each piece that is issued on its own is a variable of its own: a partial update of one array
 // would make the compiler copy the whole array.)
+// One K step's fragment of a lane: 8 bf16 weights (16 bytes) or 8 E4M3 codes (8 bytes, widened to
+// bf16 before the MFMA).
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+template <typename WT>
+struct Frag {
+  typedef u32x4 T;
+};
+template <>
+struct Frag<uint8_t> {
+  typedef u32x2 T;
+};
+template <typename WT>
 struct Wl {
-  u32x4 q[4];
-  u32x4 o[2];
-  u32x4 ga[2], gb[2];
-  u32x4 gc[4];
-  u32x4 dn[3];
+  typedef typename Frag<WT>::T F;
+  F q[4];
+  F o[2];
+  F ga[2], gb[2];
+  F gc[4];
+  F dn[3];
 };
 
 // The lane index from a fresh thread index: what is computed from it is recomputed where it is
@@ -125,81 +143,106 @@ template <typename T>
 __device__ __forceinline__ const GLB u32x4* units(const T* p) {
   return xtp::glb(reinterpret_cast<const u32x4*>(p));
 }
-// 16 bytes of a tile fragment: element row0 (a uniform row base) + (l % 16) ld + 8 (l / 16) + c of a
-// bf16 matrix with ld columns. The lane offset comes from a fresh thread index, so it is
-// recomputed at each issue instead of being kept live across the layer loop for every site.
-__device__ __forceinline__ u32x4 ld_frag(const void* m, int ld, int row0, int c) {
+// A lane's tile fragment: the 8 elements at row0 (a uniform row base) + (l % 16) ld + 8 (l / 16) + c
+// of a matrix of WT elements with ld columns (16 bytes of bf16, 8 of E4M3). The lane offset comes
+// from a fresh thread index, so it is recomputed at each issue instead of being kept live across
+// the layer loop for every site.
+template <typename WT>
+__device__ __forceinline__ typename Frag<WT>::T ld_frag(const void* m, int ld, int row0, int c) {
   const int l = xtp::fresh_tid() & 63;
-  const uint16_t* base = reinterpret_cast<const uint16_t*>(m) + (size_t)row0 * ld + c;
-  return *units(base + ((l & 15) * ld + 8 * (l >> 4)));
+  const WT* base = reinterpret_cast<const WT*>(m) + (size_t)row0 * ld + c;
+  return *xtp::glb(reinterpret_cast<const typename Frag<WT>::T*>(base + ((l & 15) * ld + 8 * (l >> 4))));
 }
 
 // the rank's q/k/v rows QPER r + l % 16 of XCD g's (query heads | key | value) rows; the 16 rows
 // lie in one of the three matrices (QPER divides D)
-__device__ __forceinline__ void issue_q(Wl& R, const KCONST CpDesc& Dd, int l, int g, int r) {
+template <typename WT>
+__device__ __forceinline__ void issue_q(Wl<WT>& R, const KCONST CpDesc& Dd, int l, int g, int r) {
   const KCONST LayerW& W = Dd.layer[l];
   const int w = xtp::wave_id(), q0 = QPER * r;
   const void* m = q0 < G * D ? W.wq : q0 < (G + 1) * D ? W.wk : W.wv;
   const int row0 = q0 < G * D ? G * D * g + q0 : q0 < (G + 1) * D ? D * g + q0 - G * D : D * g + q0 - (G + 1) * D;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) R.q[s] = ld_frag(m, H, row0, 32 * (4 * w + s));
+  for (int s = 0; s < 4; ++s) R.q[s] = ld_frag<WT>(m, H, row0, 32 * (4 * w + s));
 }
 // rows HPER r + 16 t + l % 16 (t = 0, 1), K step w of the 256 columns from c0, of a matrix with
 // ld columns (output projection; input projection)
-__device__ __forceinline__ void issue_narrow(u32x4 (&o)[2], const void* m, int ld, int c0, int r) {
+template <typename WT>
+__device__ __forceinline__ void issue_narrow(typename Frag<WT>::T (&o)[2], const void* m, int ld, int c0, int r) {
   const int w = xtp::wave_id();
 #pragma unroll
-  for (int t = 0; t < 2; ++t) o[t] = ld_frag(m, ld, HPER * r + 16 * t, c0 + 32 * w);
+  for (int t = 0; t < 2; ++t) o[t] = ld_frag<WT>(m, ld, HPER * r + 16 * t, c0 + 32 * w);
 }
-__device__ __forceinline__ void issue_o(Wl& R, const KCONST CpDesc& Dd, int l, int g, int r) {
-  issue_narrow(R.o, Dd.layer[l].wo, Dd.nq * D, G * D * g, r);
+template <typename WT>
+__device__ __forceinline__ void issue_o(Wl<WT>& R, const KCONST CpDesc& Dd, int l, int g, int r) {
+  issue_narrow<WT>(R.o, Dd.layer[l].wo, Dd.nq * D, G * D * g, r);
 }
 // A descriptor pointer as a wave-uniform value. Selecting per lane between two pointers read from
 // the descriptor would otherwise become a per-lane read of the descriptor (a vector load whose wait
 // drains every weight load in flight); read each with a scalar load first.
-__device__ __forceinline__ const uint16_t* uniform_ptr(const void* p) {
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
 }
 
 // gate/up rows q = l % 16 of the rank's gate rows 0..FPER-1, then up rows, of FFN units
 // [FX g + FPER r, +FPER) (lanes 12..15: up rows 0..3), K steps 4 w + s0, 4 w + s0 + 1
-__device__ __forceinline__ void issue_gu0(u32x4 (&t)[2], const KCONST CpDesc& Dd, int l, int g, int r, int s0) {
+template <typename WT>
+__device__ __forceinline__ void issue_gu0(typename Frag<WT>::T (&t)[2], const KCONST CpDesc& Dd, int l, int g, int r, int s0) {
   const KCONST LayerW& W = Dd.layer[l];
-  const uint16_t *wg = uniform_ptr(W.wg), *wu = uniform_ptr(W.wu);
+  const void *wg = uniform_ptr(W.wg), *wu = uniform_ptr(W.wu);
   const int w = xtp::wave_id(), f0 = FX * g + FPER * r;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const bool gate = (xtp::fresh_tid() & 15) < FPER;
-    t[s] = ld_frag(gate ? wg : wu, H, gate ? f0 : f0 - FPER, 32 * (4 * w + s0 + s));
+    t[s] = ld_frag<WT>(gate ? wg : wu, H, gate ? f0 : f0 - FPER, 32 * (4 * w + s0 + s));
   }
 }
 // Lanes l % 16 < 8: gate/up rows 16..23 (up rows 4..11). Lanes l % 16 >= 8: with head j >= 1,
 // that head's rows VPER blockIdx + l % 16 - 8 (the head tile of the step's last layer, used after
 // it); else the up rows again (columns of C that are never used). K steps 4 w .. 4 w + 3.
-__device__ __forceinline__ void issue_gu1(Wl& R, const KCONST CpDesc& Dd, int l, int g, int r, int j) {
+template <typename WT>
+__device__ __forceinline__ void issue_gu1(Wl<WT>& R, const KCONST CpDesc& Dd, int l, int g, int r, int j) {
   const int w = xtp::wave_id(), f0 = FX * g + FPER * r;
-  const uint16_t *wu = uniform_ptr(Dd.layer[l].wu), *hd = uniform_ptr(Dd.heads);
+  const void *wu = uniform_ptr(Dd.layer[l].wu), *hd = uniform_ptr(Dd.heads);
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const bool head = j > 0 && (xtp::fresh_tid() & 8);
-    R.gc[s] = ld_frag(head ? hd : wu, H, head ? (j - 1) * V + VPER * (int)blockIdx.x - 8 : f0 + (16 - FPER) - 8 * ((xtp::fresh_tid() >> 3) & 1),
+    R.gc[s] = ld_frag<WT>(head ? hd : wu, H, head ? (j - 1) * V + VPER * (int)blockIdx.x - 8 : f0 + (16 - FPER) - 8 * ((xtp::fresh_tid() >> 3) & 1),
                       32 * (4 * w + s));
   }
 }
 // down rows HPER r + 16 (w / 4) + l % 16, K steps 3 (w % 4) .. + 2 of XCD g's FFN columns
-__device__ __forceinline__ void issue_dn(Wl& R, const KCONST CpDesc& Dd, int l, int g, int r) {
+template <typename WT>
+__device__ __forceinline__ void issue_dn(Wl<WT>& R, const KCONST CpDesc& Dd, int l, int g, int r) {
   const int w = xtp::wave_id();
 #pragma unroll
-  for (int s = 0; s < 3; ++s) R.dn[s] = ld_frag(Dd.layer[l].wd, F, HPER * r + 16 * (w >> 2), FX * g + 32 * (3 * (w & 3) + s));
+  for (int s = 0; s < 3; ++s) R.dn[s] = ld_frag<WT>(Dd.layer[l].wd, F, HPER * r + 16 * (w >> 2), FX * g + 32 * (3 * (w & 3) + s));
 }
 // ---------------------------------------------------------------------------- matrix-core dots
 
 // NS K steps from ks0 of one weight tile against the split input sp (row stride st): lane l
 // supplies A row l % 16 = 4 m + p, part p of input row m (rows past the parts: zeros).
-template <int M, int NS>
-__device__ __forceinline__ f32x4 mfma_steps(const u32x4* wt, const uint16_t* sp, int st, int ks0, const uint16_t* zero,
+// A K step's B fragment: the bf16 weights as they are, or 8 E4M3 codes widened to bf16 (exactly:
+// every E4M3 value is a bf16 value, the upper half of its fp32 widening)
+__device__ __forceinline__ bf16x8 bfrag(const u32x4& f) { return __builtin_bit_cast(bf16x8, f); }
+__device__ __forceinline__ bf16x8 bfrag(const u32x2& f) {
+  const uint32_t w[2] = {f.x, f.y};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    o[2 * i] = (__float_as_uint(lo.x) >> 16) | (__float_as_uint(lo.y) & 0xffff0000u);
+    o[2 * i + 1] = (__float_as_uint(hi.x) >> 16) | (__float_as_uint(hi.y) & 0xffff0000u);
+  }
+  const u32x4 v = {o[0], o[1], o[2], o[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int M, int NS, typename FT>
+__device__ __forceinline__ f32x4 mfma_steps(const FT* wt, const uint16_t* sp, int st, int ks0, const uint16_t* zero,
                                             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}) {
   const int row = lane_id() & 15, m = row >> 2, p = row & 3;
   const bool live = p < 3 && m < M;
@@ -207,7 +250,7 @@ __device__ __forceinline__ f32x4 mfma_steps(const u32x4* wt, const uint16_t* sp,
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const bf16x8 a = *reinterpret_cast<const bf16x8*>(live ? base + 32 * (ks0 + s) + 8 * (lane_id() >> 4) : zero);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, wt[s]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bfrag(wt[s]), acc, 0, 0, 0);
   }
   return acc;
 }
@@ -240,6 +283,7 @@ struct Smem {
   __align__(16) uint16_t zero[8];
   __align__(16) uint16_t gn[2 * MAXL + 1][H];  // RMSNorm gains: layer l attention 2 l, MLP 2 l + 1, final 2 MAXL
   __align__(16) uint16_t gqk[MAXL][2][D];      // q-norm, k-norm gains per layer
+  float scl[SCN];                              // E4M3 row scales (unused for bf16 weights)
 };
 
 // ---------------------------------------------------------------------------- exchanges
@@ -317,10 +361,12 @@ struct Next {
   bool head;  // load head j's rows with the gc tiles (last layer of a step)
 };
 
-template <int M>
-__device__ __forceinline__ bool cp_layer(Ctx& c, Wl& R, int l, int j, int p0, Next nx) {
+template <typename WT, int M>
+__device__ __forceinline__ bool cp_layer(Ctx& c, Wl<WT>& R, int l, int j, int p0, Next nx) {
   const KCONST CpDesc& Dd = *c.Dd;
   Smem& S = *c.S;
+  constexpr bool E8 = sizeof(WT) == 1;  // E4M3 rows: each row sum times its scale
+  const float* sc = S.scl + l * SCL;
   const int lane = lane_id(), w = xtp::wave_id(), g = c.g, r = c.r;
   const float eps = Dd.eps;
   const uint16_t* gn_mlp = S.gn[2 * l + 1];
@@ -344,6 +390,7 @@ __device__ __forceinline__ bool cp_layer(Ctx& c, Wl& R, int l, int j, int p0, Ne
         float v = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) v += S.part[ww][0][lane];
+        if (E8) v *= sc[SCQ + (lane & 15)];
         xtp::st_l(buf + (lane >> 4) * QR + QPER * r + (lane & 15), xtp::pack(v * (lane < 16 ? sc0 : sc1), t));
       }
     }
@@ -441,7 +488,7 @@ __device__ __forceinline__ bool cp_layer(Ctx& c, Wl& R, int l, int j, int p0, Ne
               float v = 0.f;
 #pragma unroll
               for (int ww = 0; ww < NW; ++ww) v += S.part[ww][e >> 4][16 * m + (e & 15)];
-              emit(e, m, v);
+              emit(e, m, E8 ? v * sc[SCO + e] : v);
             }
           },
           [&] {
@@ -477,6 +524,10 @@ __device__ __forceinline__ bool cp_layer(Ctx& c, Wl& R, int l, int j, int p0, Ne
           gs += S.part[ww][0][16 * m + f];
           us += S.part[ww][qu >> 4][16 * m + (qu & 15)];
         }
+        if (E8) {
+          gs *= sc[SCG + f];
+          us *= sc[SCU + f];
+        }
         const float sc = m == 0 ? sc0 : sc1;
         xtp::st_l(buf + m * FX + FPER * r + f, xtp::pack(silu(gs * sc) * (us * sc), t));
       }
@@ -486,8 +537,8 @@ __device__ __forceinline__ bool cp_layer(Ctx& c, Wl& R, int l, int j, int p0, Ne
                                                [&](int i, float v) { put_split(S.hsp, SF, i / FX, i % FX, v); }))
       return false;
   }
-  if (nx.l >= 0) issue_gu0(R.ga, Dd, nx.l, g, r, 0);
-  if (nx.l >= 0) issue_gu0(R.gb, Dd, nx.l, g, r, 2);
+  if (nx.l >= 0) issue_gu0<WT>(R.ga, Dd, nx.l, g, r, 0);
+  if (nx.l >= 0) issue_gu0<WT>(R.gb, Dd, nx.l, g, r, 2);
   TTS_STAMP(16);
 
   // --- down-projection partials of the rank's 32 rows (this XCD's FFN columns), residual
@@ -505,7 +556,7 @@ __device__ __forceinline__ bool cp_layer(Ctx& c, Wl& R, int l, int j, int p0, Ne
               float v = 0.f;
 #pragma unroll
               for (int ww = 0; ww < 4; ++ww) v += S.part[w0 + ww][0][16 * m + (e & 15)];
-              emit(e, m, v);
+              emit(e, m, E8 ? v * sc[SCD + e] : v);
             }
           },
           [&] {
@@ -568,8 +619,8 @@ __device__ __forceinline__ int argmax_exchange(Ctx& c, float logit) {
 // XCDs (the resident tiles pj), then a reduce-scatter + all-gather; steps 2..15 read the row
 // P E_ac[j - 1][tok] of the projected table (a linear map of a table row is that row of the mapped
 // table), which saves that exchange. Without a projection the rows are read as they are.
-template <int M>
-__device__ __forceinline__ bool step_input(Ctx& c, const u32x4 (&pj)[2], int j, int tok) {
+template <typename WT, int M>
+__device__ __forceinline__ bool step_input(Ctx& c, const typename Frag<WT>::T (&pj)[2], int j, int tok) {
   const KCONST CpDesc& Dd = *c.Dd;
   Smem& S = *c.S;
   const int tid = xtp::fresh_tid(), lane = lane_id(), w = xtp::wave_id();
@@ -603,7 +654,7 @@ __device__ __forceinline__ bool step_input(Ctx& c, const u32x4 (&pj)[2], int j, 
             float v = 0.f;
 #pragma unroll
             for (int ww = 0; ww < NW; ++ww) v += S.part[ww][e >> 4][16 * m + (e & 15)];
-            emit(e, m, v);
+            emit(e, m, sizeof(WT) == 1 ? v * S.scl[SCP + e] : v);
           }
         },
         [] {});
@@ -629,22 +680,22 @@ __device__ __forceinline__ bool step_input(Ctx& c, const u32x4 (&pj)[2], int j, 
   return true;
 }
 
-template <int M>
-__device__ __forceinline__ bool cp_step(Ctx& c, const CpCall& C, Wl& R, const u32x4 (&pj)[2], int j, int& tok,
+template <typename WT, int M>
+__device__ __forceinline__ bool cp_step(Ctx& c, const CpCall& C, Wl<WT>& R, const typename Frag<WT>::T (&pj)[2], int j, int& tok,
                                         int frame) {
   const KCONST CpDesc& Dd = *c.Dd;
   Smem& S = *c.S;
   const int lane = lane_id(), w = xtp::wave_id();
   const int nl = Dd.n_layers;
   TTS_STAMP(40);
-  if (!step_input<M>(c, pj, j, tok)) return false;
+  if (!step_input<WT, M>(c, pj, j, tok)) return false;
   TTS_STAMP(41);
   const int p0 = (j == 1) ? 0 : j;
   for (int l = 0; l < nl; ++l) {
     Next nx;
     nx.l = l + 1 < nl ? l + 1 : (j < Dd.n_ac ? 0 : -1);
     nx.head = l + 1 == nl;
-    if (!cp_layer<M>(c, R, l, j, p0, nx)) return false;
+    if (!cp_layer<WT, M>(c, R, l, j, p0, nx)) return false;
   }
   // final RMSNorm of the last row (its parts times the final gain are in xsp), head j rows
   // VPER blockIdx + i (columns 8..15 of the gc tiles), argmax
@@ -658,6 +709,7 @@ __device__ __forceinline__ bool cp_step(Ctx& c, const CpCall& C, Wl& R, const u3
     float v = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) v += S.part[ww][0][16 * (M - 1) + VPER + (lane & (VPER - 1))];
+    if (sizeof(WT) == 1) v *= S.scl[SCH + (j - 1) * VPER + (lane & (VPER - 1))];
     logit = v * norm_scale(S.ss[c.xb] + (M - 1) * NR, Dd.eps);
     if (C.logits && lane < VPER) xtp::glb(C.logits)[(size_t)(j - 1) * V + VPER * blockIdx.x + lane] = logit;
   }
@@ -672,14 +724,15 @@ __device__ __forceinline__ bool cp_step(Ctx& c, const CpCall& C, Wl& R, const u3
   return true;
 }
 
+template <typename WT>
 __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   const KCONST CpDesc& Dd = *(const KCONST CpDesc*)C.desc;
   __shared__ Smem S;
   TTS_TRACE_BEGIN(0);
   TTS_STAMP(1);
   const int g = xtp::xcd_id(), r = blockIdx.x / NX, tid = threadIdx.x;
-  Wl R;
-  u32x4 pj[2];
+  Wl<WT> R;
+  typename Frag<WT>::T pj[2];
   // RMSNorm gains, q/k-norm gains and the RoPE factors into LDS
   {
     const int nl = Dd.n_layers;
@@ -698,14 +751,45 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
       S.rope[i / (D / 2)][1][i % (D / 2)] = xtp::glb(Dd.rope_sin)[i];
     }
     if (tid < 8) S.zero[tid] = 0;
+    if constexpr (sizeof(WT) == 1) {
+      // the row scales of this workgroup's rows (1 where a layer or the projection is absent)
+      for (int i = tid; i < SCN; i += NT) {
+        float v = 1.f;
+        if (i < SCH) {
+          const int l = i / SCL, k = i % SCL;
+          if (l < nl) {
+            const KCONST xtp::LayerS& Sc = Dd.scale[l];
+            if (k < SCO) {
+              const int q0 = QPER * r + k;
+              v = q0 < G * D ? xtp::glb(Sc.wq)[G * D * g + q0]
+                             : q0 < (G + 1) * D ? xtp::glb(Sc.wk)[D * g + q0 - G * D] : xtp::glb(Sc.wv)[D * g + q0 - (G + 1) * D];
+            } else if (k < SCG) {
+              v = xtp::glb(Sc.wo)[HPER * r + k - SCO];
+            } else if (k < SCU) {
+              v = xtp::glb(Sc.wg)[FX * g + FPER * r + k - SCG];
+            } else if (k < SCD) {
+              v = xtp::glb(Sc.wu)[FX * g + FPER * r + k - SCU];
+            } else {
+              v = xtp::glb(Sc.wd)[HPER * r + k - SCD];
+            }
+          }
+        } else if (i < SCP) {
+          const int jj = (i - SCH) / VPER, e = (i - SCH) % VPER;
+          v = xtp::glb(Dd.head_scale)[(size_t)jj * V + VPER * blockIdx.x + e];
+        } else if (Dd.proj_scale) {
+          v = xtp::glb(Dd.proj_scale)[HPER * r + i - SCP];
+        }
+        S.scl[i] = v;
+      }
+    }
   }
   // the first layer's weight tiles (and the resident input-projection tiles) after the small
   // loads above, which would otherwise wait behind them
-  if (Dd.proj) issue_narrow(pj, Dd.proj, Dd.Ht, KX * g, r);
+  if (Dd.proj) issue_narrow<WT>(pj, Dd.proj, Dd.Ht, KX * g, r);
   issue_q(R, Dd, 0, g, r);
   issue_o(R, Dd, 0, g, r);
-  issue_gu0(R.ga, Dd, 0, g, r, 0);
-  issue_gu0(R.gb, Dd, 0, g, r, 2);
+  issue_gu0<WT>(R.ga, Dd, 0, g, r, 0);
+  issue_gu0<WT>(R.gb, Dd, 0, g, r, 2);
   issue_gu1(R, Dd, 0, g, r, 0);
   issue_dn(R, Dd, 0, g, r);
   Ctx c{&Dd, &S, g, r, xtp::glb(Dd.st)->epoch, 0, 0, 0, 0, xtp::Xch{Dd.xin, Dd.xcr, Dd.err}};
@@ -715,8 +799,8 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   if (tok >= Dd.Vs) tok = Dd.Vs - 1;
   xtp::lds_barrier();
   TTS_STAMP(2);
-  bool ok = cp_step<2>(c, C, R, pj, 1, tok, frame);
-  for (int j = 2; ok && j <= Dd.n_ac; ++j) ok = cp_step<1>(c, C, R, pj, j, tok, frame);
+  bool ok = cp_step<WT, 2>(c, C, R, pj, 1, tok, frame);
+  for (int j = 2; ok && j <= Dd.n_ac; ++j) ok = cp_step<WT, 1>(c, C, R, pj, j, tok, frame);
   TTS_STAMP(3);
   if (blockIdx.x == 0 && tid == 0) {
     xtp::glb(Dd.st)->epoch = c.tag + 1;  // every workgroup has read the epoch: all took part in the last exchange

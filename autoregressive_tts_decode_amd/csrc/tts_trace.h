@@ -16,12 +16,14 @@ constexpr int kTracePer = 4096;   // stamps per workgroup
 __device__ long long g_trace[kTraceWg * kTracePer];
 __device__ int g_trace_on;
 __shared__ int g_trace_n;
-// base: first slot of this kernel's stamps (kernels of one frame write disjoint ranges)
+// base: first slot of this kernel's stamps (kernels of one frame write disjoint ranges). The
+// switch is read once here: while tracing is off the slot counter starts past the end, so a stamp
+// costs one LDS compare and no global load.
 #define TTS_TRACE_BEGIN(base) \
-  do { if (threadIdx.x == 0) g_trace_n = (base); } while (0)
+  do { if (threadIdx.x == 0) g_trace_n = g_trace_on && blockIdx.x < kTraceWg ? (base) : kTracePer; } while (0)
 #define TTS_STAMP(lbl)                                                                                        \
   do {                                                                                                        \
-    if (threadIdx.x == 0 && g_trace_on && g_trace_n < kTracePer && blockIdx.x < kTraceWg)                     \
+    if (threadIdx.x == 0 && g_trace_n < kTracePer)                                                            \
       g_trace[blockIdx.x * kTracePer + g_trace_n++] = ((long long)(lbl) << 48) | (long long)wall_clock64();   \
   } while (0)
 #else

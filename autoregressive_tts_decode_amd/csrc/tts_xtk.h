@@ -191,6 +191,7 @@ __device__ __forceinline__ f32x4 mfma_lds(const uint8_t* w, int ws, int t0, int 
   const int row = t0 + (lane & 15) < nrows ? t0 + (lane & 15) : t0;
   const uint8_t* wr = w + row * ws;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int s = s0; s < s0 + n; ++s) {
     bf16x8v bf;
     if constexpr (KE == 1) {
@@ -307,11 +308,16 @@ __device__ __forceinline__ float* tk_pt(TkSmem& S, int wave, int set) { return S
 // rows also the row scales of the rank's rows that thread tid emits: q/k/v row tid (sq), output
 // row tid (so), gate and up row tid (sg, su), down row tid (sd), and after the last layer the
 // semantic head row tid (sh); sg, su, sd are loaded one layer ahead into sgn, sun, sdn (the
-// current ones are still needed when the next layer's constants arrive).
+// current ones are still needed when the next layer's constants arrive). The gains are kept as
+// raw bf16 patterns and widened where they are used: widening them at the load would make the
+// loading wave wait there for the load, and with it for every row it issued before. For the same
+// reason every load here is unconditional, from a valid index (a thread whose element or row does
+// not exist never uses the value).
 struct TkConsts {
-  float an[4], mn[4], qk[2];
+  uint32_t an[4], mn[4], qk[2];
   float sq, so, sg, su, sd, sh, sgn, sun, sdn;
 };
+__device__ __forceinline__ float gain_f32(uint32_t raw) { return __uint_as_float(raw << 16); }
 
 template <typename WT>
 __device__ __forceinline__ void tk_load_consts(TkConsts& c, const KCONST TkDesc& D, int l, int g, int r) {
@@ -320,34 +326,28 @@ __device__ __forceinline__ void tk_load_consts(TkConsts& c, const KCONST TkDesc&
   const uint16_t* mn = reinterpret_cast<const uint16_t*>(W.mlp_norm);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const int i = threadIdx.x + k * NT;
-    c.an[k] = i < D.H ? to_f32(glb(an)[i]) : 0.f;
-    c.mn[k] = i < D.H ? to_f32(glb(mn)[i]) : 0.f;
+    const int i = min((int)threadIdx.x + k * NT, D.H - 1);
+    c.an[k] = glb(an)[i];
+    c.mn[k] = glb(mn)[i];
   }
+  // q-norm gains for waves 0, 1, k-norm gains for the others (used by wave 2 only)
   const int wave = wave_id(), lane = threadIdx.x & 63;
-  c.qk[0] = c.qk[1] = 1.f;
-  if (wave < 3) {
-    const uint16_t* gn = reinterpret_cast<const uint16_t*>(wave < 2 ? W.q_norm : W.k_norm);
-    c.qk[0] = to_f32(glb(gn)[lane]);
-    c.qk[1] = to_f32(glb(gn)[lane + 64]);
-  }
+  const uint16_t* gn = reinterpret_cast<const uint16_t*>(wave < 2 ? W.q_norm : W.k_norm);
+  c.qk[0] = glb(gn)[lane];
+  c.qk[1] = glb(gn)[lane + 64];
   c.sq = c.so = c.sgn = c.sun = c.sdn = c.sh = 1.f;
   if constexpr (TkW<WT>::ES == 1) {
     const KCONST LayerS& Sc = D.scale[l];
     const int tid = threadIdx.x, d = D.d, G = D.nq / D.nkv, qper = (G + 2) * d / NR, hper = D.H / NR;
     const int fx = D.F / NX, fper = fx / NR;
-    if (tid < qper) {
-      const int q = qper * r + tid;
-      c.sq = q < G * d ? glb(Sc.wq)[G * d * g + q] : q < (G + 1) * d ? glb(Sc.wk)[d * g + q - G * d] : glb(Sc.wv)[d * g + q - (G + 1) * d];
-    }
-    if (tid < hper) {
-      c.so = glb(Sc.wo)[hper * r + tid];
-      c.sdn = glb(Sc.wd)[hper * r + tid];
-    }
-    if (tid < fper) {
-      c.sgn = glb(Sc.wg)[fx * g + fper * r + tid];
-      c.sun = glb(Sc.wu)[fx * g + fper * r + tid];
-    }
+    // the rank's qper q/k/v rows lie in one of the three matrices (qper divides d)
+    const int q0 = qper * r, qi = min(tid, qper - 1);
+    const float* sqm = q0 < G * d ? Sc.wq + G * d * g + q0 : q0 < (G + 1) * d ? Sc.wk + d * g + q0 - G * d : Sc.wv + d * g + q0 - (G + 1) * d;
+    c.sq = glb(sqm)[qi];
+    c.so = glb(Sc.wo)[hper * r + min(tid, hper - 1)];
+    c.sdn = glb(Sc.wd)[hper * r + min(tid, hper - 1)];
+    c.sgn = glb(Sc.wg)[fx * g + fper * r + min(tid, fper - 1)];
+    c.sun = glb(Sc.wu)[fx * g + fper * r + min(tid, fper - 1)];
   }
 }
 
@@ -395,10 +395,10 @@ struct RowCopy {
 // Wait until every load this wave issued has landed (the LDS-direct rows included).
 __device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
-// x * rsqrt(mean(x^2) + eps) * gain over n <= 4 NT elements, in two parts into sp (row stride
+// x * rsqrt(mean(x^2) + eps) * gain (raw bf16 gains gr) over n <= 4 NT elements, in two parts into sp (row stride
 // XST); with out, also as fp32 (to global memory). ss: NR per-rank partial sums of squares (from
 // reduce_gather) or nullptr to reduce here.
-__device__ __forceinline__ void tk_rmsnorm(const float* x, int n, const float* gr, float eps, uint16_t* sp, float* red,
+__device__ __forceinline__ void tk_rmsnorm(const float* x, int n, const uint32_t* gr, float eps, uint16_t* sp, float* red,
                                            const float* ss, float* out = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float tot = 0.f;
@@ -426,7 +426,7 @@ __device__ __forceinline__ void tk_rmsnorm(const float* x, int n, const float* g
   for (int k = 0; k < 4; ++k) {
     const int i = tid + k * NT;
     if (i < n) {
-      const float y = x[i] * sc * gr[k];
+      const float y = x[i] * sc * gain_f32(gr[k]);
       put2(sp, XST, i, y);
       if (out) glb(out)[i] = y;
     }
@@ -450,8 +450,8 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
     const float* src = S.qkv + wave * d;
     float v0 = src[lane], v1 = src[lane + 64];
     const float sc = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) / (float)d + D.eps);
-    v0 *= sc * cn.qk[0];
-    v1 *= sc * cn.qk[1];
+    v0 *= sc * gain_f32(cn.qk[0]);
+    v1 *= sc * gain_f32(cn.qk[1]);
     float* dst = wave < 2 ? S.q[wave] : S.kp;
     const float a = v0 * rc - v1 * rs, b = v1 * rc + v0 * rs;
     dst[lane] = a;
@@ -607,10 +607,10 @@ __device__ __forceinline__ void tk_next_consts(TkConsts& c, const KCONST TkDesc&
   } else {
     const uint16_t* f = reinterpret_cast<const uint16_t*>(D.final_norm);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) c.an[k] = tid + k * NT < D.H ? to_f32(glb(f)[tid + k * NT]) : 0.f;
+    for (int k = 0; k < 4; ++k) c.an[k] = glb(f)[min(tid + k * NT, D.H - 1)];
     if constexpr (TkW<WT>::ES == 1) {
       const int vper = D.V / NWG;
-      c.sh = tid < vper ? glb(D.head_scale)[vper * blockIdx.x + tid] : 1.f;
+      c.sh = glb(D.head_scale)[vper * blockIdx.x + min(tid, vper - 1)];
     }
   }
 }
@@ -746,7 +746,6 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
       dn.begin(reinterpret_cast<const uint8_t*>(W.wd) + (size_t)ES * ((size_t)(hper * r) * D.F + fx * g), nullptr, hper,
                (long long)ES * D.F, hper, ES * fx / 16);
       dn.part(S.lw, dparts);
-      tk_next_consts<WT>(c, D, l, tid, g, r);
     } else {
       if (nd > nl) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -756,8 +755,10 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
       }
       if (!last) tk_issue_a<WT>(X0, D, D.layer[l + 1], 0, g, r);
       else tk_issue_f<WT>(X0, D, 0);
-      tk_next_consts<WT>(c, D, l, tid, g, r);
     }
+    // one load site for both roles (after each wave's own issue), so the constants need no copy
+    // where the two paths meet
+    tk_next_consts<WT>(c, D, l, tid, g, r);
     lds_barrier();
     TTS_STAMP(61);
     // gate/up row q: an LDS tile row below nl, else a row of the register tile

@@ -1660,7 +1660,7 @@ int tts_run_frames_noalloc(tts_ctx* ctx, int32_t n, const tts_sampling* sem, con
   const int B = ctx->batch;
   if (!use_xtp(ctx, B, *ac) || !use_xtk(ctx, B))
     return ctx->fail(TTS_E_UNSUPPORTED,
-                     "run_frames_noalloc: runs both persistent kernels only (batch 1, greedy acoustic tokens, bf16 weights, "
+                     "run_frames_noalloc: runs both persistent kernels only (batch 1, greedy acoustic tokens, bf16 or E4M3 weights, "
                      "persistent exec mode)");
   // the exchange buffers this call needs, against the array's fixed size
   if (ScratchLayout::total > kScratchBytes)

@@ -223,7 +223,7 @@ int tts_run_frames(tts_ctx* ctx, int32_t n, const tts_sampling* sem, const tts_s
  * size that each GPU the library runs on holds until the process ends, instead
  * of from the context's workspace. Same arguments, results and errors as
  * tts_run_frames, plus TTS_E_UNSUPPORTED unless both persistent kernels run
- * (batch 1, greedy acoustic tokens, bf16 weights, persistent exec mode) and
+ * (batch 1, greedy acoustic tokens, bf16 or E4M3 weights, persistent exec mode) and
  * TTS_E_CAPACITY if their exchange buffers would not fit the array. Calls no
  * allocating routine. The array keeps the last call's contents and is cleared
  * (by a kernel) at the start of every call; calls that overlap on one GPU,

@@ -1,8 +1,8 @@
 """The allocation-free frame loop: tts_run_frames_noalloc (exchange buffers in the library's static
 scratch array, frames launched one by one) against tts_run_frames (exchange buffers in the
 context's workspace, the captured frame graph), through the C ABI, on two calls in a row, the
-second with fewer frames. Both paths run the same kernels on the same inputs, so codes and the
-logits after them must be identical bit for bit."""
+second with fewer frames, for bf16 and E4M3 weights. Both paths run the same kernels on the same
+inputs, so codes and the logits after them must be identical bit for bit."""
 import ctypes
 
 import numpy as np
@@ -20,10 +20,11 @@ def _bits(a):
     return a.view(np.uint32) if a.dtype == np.float32 else a
 
 
-def test_noalloc_frames_equal_the_graph_frames():
+@pytest.mark.parametrize("name", ["1.7b", "1.7b-fp8"])
+def test_noalloc_frames_equal_the_graph_frames(name):
     assert torch.cuda.is_available(), "the gpu tests need a HIP device"
     d = torch.device("cuda:0")
-    model = config.MODELS["1.7b"]
+    model = config.MODELS[name]
     w = synth.make_weights(model, 0)
     dw = tts.weights_to_device(w, model, d)
     dec = tts.TTSDecoder(model, 1, 64, 32)
@@ -36,7 +37,7 @@ def test_noalloc_frames_equal_the_graph_frames():
     a = torch.zeros((1, 15), dtype=torch.int32, device=d)
     Va = model.codepred.vocab
     for F in (8, 3):  # two calls in a row, the second with fewer frames
-        print(f"1.7b frames {F}: graph", flush=True)
+        print(f"{name} frames {F}: graph", flush=True)
         ref = torch.full((1, 32, 16), -1, dtype=torch.int32, device=d)
         al_ref = torch.zeros((1, 15, Va), dtype=torch.float32, device=d)
         dec.prefill(ids)
@@ -44,7 +45,7 @@ def test_noalloc_frames_equal_the_graph_frames():
         dec.codepred_frame(probe, GREEDY, None, a, logits=al_ref)
         torch.cuda.synchronize()
         prog_ref = dec.progress()
-        print(f"1.7b frames {F}: noalloc", flush=True)
+        print(f"{name} frames {F}: noalloc", flush=True)
         got = torch.full((1, 32, 16), -1, dtype=torch.int32, device=d)
         al_got = torch.zeros((1, 15, Va), dtype=torch.float32, device=d)
         dec.prefill(ids)
@@ -67,3 +68,5 @@ def test_noalloc_frames_equal_the_graph_frames():
     assert lib.tts_run_frames_noalloc(dec.ctx, 1, ctypes.byref(greedy), ctypes.byref(greedy), None,
                                       got.data_ptr()) == tts.TTS_E_UNSUPPORTED
     dec.close()
+    del dw
+    torch.cuda.empty_cache()

@@ -182,27 +182,50 @@ __device__ __forceinline__ f32x4 mfma_regs(const WBuf& B, int n, const uint16_t*
   return acc;
 }
 // The 16-row tile at rows t0 .. t0 + 15 of the LDS rows w (row stride ws bytes; rows >= nrows
-// read row t0), K steps s0 .. s0 + n - 1, against the split input sp.
+// read row t0), K steps s0 .. s0 + n - 1 (n >= 1), against the split input sp. For bf16 rows step
+// s + 1's fragments are read before step s's MFMA issues, so the LDS reads overlap the MFMA chain.
+template <typename WT>
+struct LdsB {
+  typedef u32x4 T;
+};
+template <>
+struct LdsB<uint8_t> {
+  typedef uint2 T;
+};
+template <typename WT>
+__device__ __forceinline__ typename LdsB<WT>::T lds_braw(const uint8_t* wr, int s, int q) {
+  constexpr int ES = TkW<WT>::ES, KE = TkW<WT>::KE;
+  return *reinterpret_cast<const typename LdsB<WT>::T*>(wr + ES * kcol<KE>(s, q));
+}
+__device__ __forceinline__ bf16x8v lds_bwiden(const u32x4& r) { return __builtin_bit_cast(bf16x8v, r); }
+__device__ __forceinline__ bf16x8v lds_bwiden(const uint2& r) { return e4m3x8_bf16(r.x, r.y); }
 template <typename WT>
 __device__ __forceinline__ f32x4 mfma_lds(const uint8_t* w, int ws, int t0, int nrows, int s0, int n, const uint16_t* sp,
                                           int st, const uint16_t* zero) {
-  constexpr int ES = TkW<WT>::ES, KE = TkW<WT>::KE;
+  constexpr int KE = TkW<WT>::KE;
   const int lane = fresh_tid() & 63, q = lane >> 4;
   const int row = t0 + (lane & 15) < nrows ? t0 + (lane & 15) : t0;
   const uint8_t* wr = w + row * ws;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (KE == 2) {
+    // (pipelined E4M3 steps measured slower: the plain loop, scheduled by the compiler)
 #pragma unroll 4
-  for (int s = s0; s < s0 + n; ++s) {
-    bf16x8v bf;
-    if constexpr (KE == 1) {
-      bf = *reinterpret_cast<const bf16x8v*>(wr + ES * kcol<KE>(s, q));
-    } else {
+    for (int s = s0; s < s0 + n; ++s) {
       const uint2 c = *reinterpret_cast<const uint2*>(wr + kcol<KE>(s, q));
-      bf = e4m3x8_bf16(c.x, c.y);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_frag2<KE>(sp, st, s, zero), e4m3x8_bf16(c.x, c.y), acc, 0, 0, 0);
     }
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_frag2<KE>(sp, st, s, zero), bf, acc, 0, 0, 0);
+    return acc;
   }
-  return acc;
+  bf16x8v a = a_frag2<KE>(sp, st, s0, zero);
+  typename LdsB<WT>::T b = lds_braw<WT>(wr, s0, q);
+  for (int s = s0; s < s0 + n - 1; ++s) {
+    const bf16x8v an = a_frag2<KE>(sp, st, s + 1, zero);
+    const typename LdsB<WT>::T bn = lds_braw<WT>(wr, s + 1, q);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lds_bwiden(b), acc, 0, 0, 0);
+    a = an;
+    b = bn;
+  }
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lds_bwiden(b), acc, 0, 0, 0);
 }
 
 // The weight rows of a layer, per workgroup (H in {512, 1024, 2048}, 8 KV heads of dimension 128

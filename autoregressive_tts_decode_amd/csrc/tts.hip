@@ -237,7 +237,7 @@ std::string check_config(const tts_config* c) {
   return "";
 }
 
-// Whether the persistent XCD-tensor-parallel CodePredictor kernel handles this config: bf16 weights,
+// Whether the persistent XCD-tensor-parallel CodePredictor kernel handles this config: bf16 or E4M3 weights,
 // 8 KV heads of dimension 128 (one per XCD), and per-workgroup weight slices that fit its two
 // register buffers (rows per wave and 16-byte units per lane).
 bool xtp_capable(const tts_config& c) {
@@ -265,7 +265,7 @@ bool xtp_capable(const tts_config& c) {
   return true;
 }
 
-// Whether the lean persistent CodePredictor kernel (tts_xcp.h) handles this config: bf16 weights
+// Whether the lean persistent CodePredictor kernel (tts_xcp.h) handles this config: bf16 or E4M3 weights
 // and the CodePredictor shape it is specialised to (hidden 1024, FFN 3072, 16 query and 8 KV heads
 // of 128, vocabulary 2048, at most 5 layers, 15 codebooks), with no input projection or one from a
 // Talker hidden of 2048.
@@ -279,7 +279,7 @@ bool xcp_capable(const tts_config& c) {
   return c.talker.hidden == xcp::H || c.talker.hidden == xcp::NX * xcp::KX;
 }
 
-// Whether the persistent Talker step kernel handles this config: bf16 weights, an fp32 KV cache,
+// Whether the persistent Talker step kernel handles this config: bf16 or E4M3 weights, an fp32 KV cache,
 // 8 KV heads of dimension 128 with 2 query heads each, and weight slices that fit its chunk shapes
 // (see tts_xtk.h).
 bool xtk_capable(const tts_config& c) {
@@ -300,7 +300,7 @@ bool xtk_capable(const tts_config& c) {
 
 }  // namespace
 
-// Whether the GEMM prefill handles this config: bf16 weights, head dimension 128 and every GEMM
+// Whether the GEMM prefill handles this config: bf16 or E4M3 weights, head dimension 128 and every GEMM
 // dimension of the Talker a multiple of the 64 x 64 x 64 tile.
 bool prefill_gemm_capable(const tts_config& c) {
   const tts_stack_cfg& t = c.talker;

@@ -1,4 +1,4 @@
-// Persistent CodePredictor frame kernel, lean form (CDNA4, gfx950; bf16 weights).
+// Persistent CodePredictor frame kernel, lean form (CDNA4, gfx950; bf16 or E4M3 weights).
 //
 // The 15 sequential CodePredictor steps of a frame ("Running Qwen3-TTS on an AMD R9700", section
 // "Running Qwen3-TTS": the small decoder runs once per acoustic codebook after the Talker step)

@@ -13,17 +13,21 @@
 //   * the waves of a workgroup split by role: four front waves poll the exchanges and run the
 //     attention, four back waves stream the weight rows (the loads of one wave return in order, so
 //     a poll never waits behind weight rows in flight);
-//   * the weight slices are large (up to 192 KB per workgroup and phase): the q/k/v, output and
-//     gate/up rows stream in chunks of at most 32 KB through two 32-register buffers of the back
-//     waves, each chunk issued as soon as the one two back has been consumed, while the down rows
-//     (up to 96 KB) are copied straight into LDS during the attention;
+//   * the weight slices are large (up to 192 KB per workgroup and phase): the q/k/v and output
+//     rows, the gate/up rows past the first 32 and the semantic head go through two 32-register
+//     buffers of the back waves, each chunk issued as soon as the one before it has been
+//     consumed, while the first gate/up rows and later the down rows are copied straight into
+//     LDS (up to 128 KB) in parts spread over the layer;
 //   * the row dots run on the matrix cores: a 16-row tile of weight rows is the B operand of
 //     v_mfma_f32_16x16x32_bf16 (registers hold B fragments: lane l row l % 16, columns 32 s +
 //     8 (l / 16) of K step s; LDS rows are padded by 16 bytes so a fragment's 16 rows fall on
 //     different banks), the A operand the input row cut into two bf16 parts, hi (the fp32
 //     pattern with its low 16 bits cleared) and mid (x - hi rounded to bf16): hi + mid is x to
 //     within 2^-17 |x|, and the products are exact in fp32. The K range of a tile is split over
-//     waves, whose partial sums are added in wave order.
+//     waves, whose partial sums are added in wave order;
+//   * E4M3 weights (WT = uint8_t): a 16-byte lane load carries two K steps of codes (the input
+//     fragments use the same column order), widened exactly to bf16 before each MFMA; each row's
+//     sum is multiplied by its fp32 scale where the row is emitted.
 #pragma once
 
 #include "tts_trace.h"

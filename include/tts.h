@@ -123,9 +123,9 @@ int tts_create(const tts_config* cfg, void* hip_stream, void* workspace, size_t 
  * tensor must be present with the exact shape, the config's dtype and
  * 16-byte alignment; FP8 configs add one "<matrix>.scale" per matrix (fp32)
  * and give gains and embeddings as bf16. Pointers are borrowed until
- * tts_destroy. FP8 configs run the persistent CodePredictor frame kernel, the
- * MFMA GEMM routes and the per-op kernels; the persistent Talker step kernel
- * needs bf16 weights (FP8 Talker steps use the per-op kernels). */
+ * tts_destroy. FP8 configs run both persistent kernels (E4M3 tiles widened
+ * to bf16 for the matrix cores, each row sum times its scale), the MFMA GEMM
+ * routes and the per-op kernels. */
 int tts_load_weights(tts_ctx* ctx, int32_t n, const char* const* names, void* const* dev_ptrs,
                      const int64_t* shapes, const int32_t* ranks, const int32_t* dtypes);
 
@@ -248,8 +248,9 @@ int tts_set_text_stream(tts_ctx* ctx, const int32_t* text_ids, int32_t n_text, i
  *    exchange tagged values instead of ending kernels. One runs all 15
  *    CodePredictor steps of a frame (batch 1, greedy acoustic tokens, bf16 or
  *    E4M3 weights, a CodePredictor with 8 KV heads of dimension 128); one runs
- *    a whole Talker step (batch 1, bf16 weights, 8 KV heads of dimension 128
- *    with 2 query heads each). Both need a device that keeps all their 256
+ *    a whole Talker step (batch 1, bf16 or E4M3 weights, hidden 512, 1024 or
+ *    2048, 8 KV heads of dimension 128 with 2 query heads each, an fp32 KV
+ *    cache). Both need a device that keeps all their 256
  *    workgroups resident at once (tts_persistent_allowed). Other calls use the
  *    per-op kernels. The prompt pass never uses them (see tts_set_prefill_mode).
  *  TTS_EXEC_KERNELS: one kernel per op.
@@ -264,7 +265,7 @@ int tts_get_exec_mode(const tts_ctx* ctx, int32_t* mode, int32_t* persistent_sup
 
 /* How tts_prefill runs the prompt ("Running Qwen3-TTS on an AMD R9700",
  * section "Running Qwen3-TTS": the prompt pass before the frame loop):
- *  TTS_PREFILL_GEMM (default where supported: bf16 weights, head dimension
+ *  TTS_PREFILL_GEMM (default where supported: bf16 or E4M3 weights, head dimension
  *    128, Talker dimensions multiples of 64): chunks of up to 64 positions
  *    per stream as MFMA GEMMs over all streams' rows, causal attention over
  *    the KV cache. fp32 activations enter each GEMM as three bf16 parts

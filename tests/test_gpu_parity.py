@@ -930,11 +930,13 @@ def _bits(a):
     return a.view(np.uint32) if a.dtype == np.float32 else a
 
 
-def test_1p7b_persistent_decode_is_bitwise_reproducible():
-    """Two runs of the same 1.7B batch-1 work give identical bits: the MFMA prompt pass, eight frames
-    of the captured graph on both persistent kernels, then an eager CodePredictor frame and Talker
-    step (every sum has a fixed order; split-K partials are added in slice order)."""
-    model = config.MODELS["1.7b"]
+@pytest.mark.parametrize("name", ["1.7b", "1.7b-fp8"])
+def test_1p7b_persistent_decode_is_bitwise_reproducible(name):
+    """Two runs of the same 1.7B batch-1 work give identical bits, with bf16 and with E4M3 weights:
+    the MFMA prompt pass, eight frames of the captured graph on both persistent kernels, then an
+    eager CodePredictor frame and Talker step (every sum has a fixed order; split-K partials are
+    added in slice order)."""
+    model = config.MODELS[name]
     w = synth.make_weights(model, 0)
     dec, dw = make_decoder(model, 1, 64, 16, w)
     assert dec.exec_mode()[0] == tts.EXEC_PERSISTENT and dec.prefill_mode() == tts.PREFILL_GEMM

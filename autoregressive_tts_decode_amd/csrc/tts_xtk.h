@@ -550,15 +550,33 @@ __device__ __forceinline__ bool tk_attention(const KCONST TkDesc& D, const Xch& 
         o[h][1] *= corr;
         m[h] = mn;
       }
-      // outputs: lane owns dimensions lane, lane + 64 of both heads
-      for (int tt = 0; tt < npass; ++tt) {
-        const int tp = base + tt;
-        const float w0 = readlane_f(w[0], 4 * tt), w1 = readlane_f(w[1], 4 * tt);
-        float v0, v1;
-        if (tp == p) { v0 = S.vp[lane]; v1 = S.vp[lane + 64]; }
-        else { v0 = glb(vg)[(size_t)tp * d + lane]; v1 = glb(vg)[(size_t)tp * d + lane + 64]; }
-        o[0][0] = fmaf(w0, v0, o[0][0]); o[0][1] = fmaf(w0, v1, o[0][1]);
-        o[1][0] = fmaf(w1, v0, o[1][0]); o[1][1] = fmaf(w1, v1, o[1][1]);
+      // outputs: lane owns dimensions lane, lane + 64 of both heads. The pass's v rows are loaded
+      // in batches of 8, all of a batch's loads in flight together; rows past the pass are not
+      // loaded (their weight is 0). The step's own row, not yet in the cache, comes from LDS.
+#pragma unroll
+      for (int h8 = 0; h8 < 16; h8 += 8) {
+        if (h8 < npass) {
+          float va[8], vb[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            va[k] = 0.f;
+            vb[k] = 0.f;
+            if (h8 + k < npass) {
+              const int tp = base + h8 + k;
+              va[k] = glb(vg)[(size_t)tp * d + lane];
+              vb[k] = glb(vg)[(size_t)tp * d + lane + 64];
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int tt = h8 + k;
+            const bool own = base + tt == p;
+            const float v0 = own ? S.vp[lane] : va[k], v1 = own ? S.vp[lane + 64] : vb[k];
+            const float w0 = readlane_f(w[0], 4 * tt), w1 = readlane_f(w[1], 4 * tt);
+            o[0][0] = fmaf(w0, v0, o[0][0]); o[0][1] = fmaf(w0, v1, o[0][1]);
+            o[1][0] = fmaf(w1, v0, o[1][0]); o[1][1] = fmaf(w1, v1, o[1][1]);
+          }
+        }
       }
     }
 #pragma unroll

@@ -117,6 +117,9 @@ WORKLOADS = {
     "0.6b": Workload("0.6b", M06B, batch=1, prefill_len=64, frames=240),
     "1.7b": Workload("1.7b", M17B, batch=1, prefill_len=64, frames=240),
     "1.7b-long": Workload("1.7b-long", M17B, batch=1, prefill_len=256, frames=2000),
+    # the 1.7B batch-1 decode with the pages' default sampling of both token kinds
+    "1.7b-sampled": Workload("1.7b-sampled", M17B, batch=1, prefill_len=64, frames=240,
+                             semantic=SEMANTIC_SAMPLED, acoustic=ACOUSTIC_SAMPLED),
     "1.7b-x32": Workload("1.7b-x32", M17B, batch=32, prefill_len=64, frames=240,
                          semantic=SEMANTIC_SAMPLED, acoustic=ACOUSTIC_SAMPLED),
     "0.6b-fp8": Workload("0.6b-fp8", M06B_FP8, batch=1, prefill_len=64, frames=240),

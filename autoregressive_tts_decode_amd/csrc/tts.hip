@@ -962,12 +962,25 @@ int sample(tts_ctx* ctx, const float* logits, int l_stride, int B, int V, const 
 // stream. Acoustic token j of stream b goes to out (refs with offset j-1);
 // logits (optional) to logits_out + b*15*Va + (j-1)*Va. u: uniform refs with
 // offset of acoustic 1 (incremented per step). forced: [B][15] or nullptr.
-// The persistent CodePredictor kernel handles batch 1 with greedy acoustic tokens.
-bool use_xtp(tts_ctx* ctx, int B, const tts_sampling& ac) { return ctx->xtp_ok && ctx->exec_mode == 1 && B == 1 && !ac.do_sample; }
+// The persistent CodePredictor kernels handle batch 1 with greedy acoustic tokens; the hidden-1024
+// one also draws sampled acoustic tokens in-kernel for top_k in 1..64 (others: per-op kernels).
+bool use_xtp(tts_ctx* ctx, int B, const tts_sampling& ac) {
+  if (!ctx->xtp_ok || ctx->exec_mode != TTS_EXEC_PERSISTENT || B != 1) return false;
+  return !ac.do_sample || (ctx->xcp_ok && ac.top_k >= 1 && ac.top_k <= xcp::KS);
+}
 
+// u: the uniforms of acoustic 1 of the frame at u[u_offset + (use_frame ? frame * u_f_stride : 0)],
+// then one per step (read only when ac samples).
 int codepred_frame_xtp(tts_ctx* ctx, const int32_t* semantic, const int32_t* forced, int32_t* codes, int f_stride, int use_frame,
-                       float* logits_out) {
+                       float* logits_out, const tts_sampling& ac, const float* u, int u_f_stride, int u_offset) {
   xtp::CpCall call;
+  call.do_sample = ac.do_sample ? 1 : 0;
+  call.top_k = ac.top_k;
+  call.top_p = ac.top_p;
+  call.temperature = ac.temperature;
+  call.u = u;
+  call.u_f_stride = u_f_stride;
+  call.u_offset = u_offset;
   call.desc = ctx->use_scratch ? ctx->cpdesc_s : ctx->cpdesc;
   call.semantic = semantic;
   call.forced = forced;
@@ -1096,7 +1109,7 @@ int enqueue_frame(tts_ctx* ctx, const tts_sampling& sem, const tts_sampling& ac,
                       c.talker.vocab, 1, codes, fs, 16, 0, 1, ctx->sem_tok, nullptr, 0, 0))
     return rc;
   if (use_xtp(ctx, B, ac)) {
-    if (int rc = codepred_frame_xtp(ctx, ctx->sem_tok, nullptr, codes + 1, 16, 1, nullptr)) return rc;
+    if (int rc = codepred_frame_xtp(ctx, ctx->sem_tok, nullptr, codes + 1, 16, 1, nullptr, ac, u, uf, 1)) return rc;
   } else if (int rc = codepred_frame(ctx, B, tokref(ctx->sem_tok, 1, 0, 0, 0), ac, uref(u, ub, uf, u == ctx->hT ? 0 : 1, 1), nullptr,
                                      codes, fs, 16, 1, 1, nullptr)) {
     return rc;
@@ -1576,7 +1589,7 @@ int tts_codepred_frame(tts_ctx* ctx, const int32_t* semantic, const tts_sampling
   const int B = ctx->batch;
   URef ur = uref(u ? u : ctx->hT, u ? 15 : 0, 0, 0, 0);
   if (use_xtp(ctx, B, *ac)) {
-    if (int rc = codepred_frame_xtp(ctx, semantic, forced, codes, 0, 0, logits)) return rc;
+    if (int rc = codepred_frame_xtp(ctx, semantic, forced, codes, 0, 0, logits, *ac, u, 0, 0)) return rc;
   } else if (int rc = codepred_frame(ctx, B, tokref(semantic, 1, 0, 0, 0), *ac, ur, forced, codes, 15, 0, 0, 0, logits)) {
     return rc;
   }
@@ -1658,7 +1671,7 @@ int tts_run_frames_noalloc(tts_ctx* ctx, int32_t n, const tts_sampling* sem, con
     return ctx->fail(TTS_E_CAPACITY, "run_frames_noalloc: %d + %d positions exceed max_cache_steps %d", ctx->pos, n,
                      ctx->cfg.max_cache_steps);
   const int B = ctx->batch;
-  if (!use_xtp(ctx, B, *ac) || !use_xtk(ctx, B))
+  if (ac->do_sample || !use_xtp(ctx, B, *ac) || !use_xtk(ctx, B))
     return ctx->fail(TTS_E_UNSUPPORTED,
                      "run_frames_noalloc: runs both persistent kernels only (batch 1, greedy acoustic tokens, bf16 or E4M3 weights, "
                      "persistent exec mode)");

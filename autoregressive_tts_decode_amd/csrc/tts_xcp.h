@@ -270,9 +270,14 @@ __device__ __forceinline__ float norm_scale(const float* ss, float eps) {
 struct Smem {
   float xo[2][2][HPER];          // this rank's elements of the residual rows [buffer][row]
   float ss[2][2 * NR];           // per-rank sums of squares of the residual rows [buffer][row NR + rank]
-  float xn[NX * 2 * HPER];       // reduce-scatter partials: partner x, row m at (x M + m) HPER
-  float qkv[2 * QR];             // this XCD's q/k/v rows (row m at m QR)
-  float kq[4][D];                // normed, rotated q of each attention wave
+  union {
+    struct {
+      float xn[NX * 2 * HPER];   // reduce-scatter partials: partner x, row m at (x M + m) HPER
+      float qkv[2 * QR];         // this XCD's q/k/v rows (row m at m QR)
+      float kq[4][D];            // normed, rotated q of each attention wave
+    };
+    __align__(16) float sv[V];   // sampled ids: the step's logits over the temperature (after the last layer)
+  };
   float part[NW][2][32];         // per-wave partial dots [wave][tile][16 m + row]
   float cand[2 * NWG];           // argmax candidates (value, id bits)
   float rope[P][2][D / 2];       // cos, sin of positions 0..15
@@ -284,7 +289,12 @@ struct Smem {
   __align__(16) uint16_t gn[2 * MAXL + 1][H];  // RMSNorm gains: layer l attention 2 l, MLP 2 l + 1, final 2 MAXL
   __align__(16) uint16_t gqk[MAXL][2][D];      // q-norm, k-norm gains per layer
   float scl[SCN];                              // E4M3 row scales (unused for bf16 weights)
+  __align__(16) uint32_t bins[4][256];         // sampled ids: radix-select histograms, one per key byte
+  u64 ckey[64];                                // sampled ids: the kept keys
+  int ncand;                                   // sampled ids: kept keys so far
+  int wsum[NW];                                // sampled ids: per-wave counts of keys tied at the cut
 };
+static_assert(sizeof(float) * (NX * 2 * HPER + 2 * QR + 4 * D) == sizeof(float) * V, "sampled logits fill the layer temporaries");
 
 // ---------------------------------------------------------------------------- exchanges
 
@@ -613,6 +623,149 @@ __device__ __forceinline__ int argmax_exchange(Ctx& c, float logit) {
   return best < V ? best : 0;
 }
 
+// ---------------------------------------------------------------------------- sampled ids
+
+constexpr int KS = 64;  // largest top_k of the in-kernel sampler: the kept ids fit one wave
+
+// v shifted n lanes up within its row of 16 lanes (0 below the row's first lane), by DPP row_shr.
+template <int N>
+__device__ __forceinline__ int shr_i(int v) { return __builtin_amdgcn_update_dpp(0, v, 0x110 + N, 0xF, 0xF, false); }
+template <int N>
+__device__ __forceinline__ float shr_f(float v) { return __int_as_float(shr_i<N>(__float_as_int(v))); }
+
+// Inclusive prefix sums over the wave in lane order: within each row of 16 lanes by DPP row
+// shifts, then the totals of the earlier rows added (a fixed order, the same in every wave).
+__device__ __forceinline__ int wave_scan_i(int v) {
+  v += shr_i<1>(v); v += shr_i<2>(v); v += shr_i<4>(v); v += shr_i<8>(v);
+  const int lane = lane_id();
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31), r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (lane >= 16 ? r0 : 0) + (lane >= 32 ? r1 : 0) + (lane >= 48 ? r2 : 0);
+}
+__device__ __forceinline__ float wave_scan_f(float v) {
+  v += shr_f<1>(v); v += shr_f<2>(v); v += shr_f<4>(v); v += shr_f<8>(v);
+  const int lane = lane_id();
+  const float r0 = rl(v, 15), r1 = rl(v, 31), r2 = rl(v, 47);
+  if (lane >= 16) v += r0;
+  if (lane >= 32) v += r1;
+  if (lane >= 48) v += r2;
+  return v;
+}
+
+// The float whose orderable key is o (the inverse of tts::orderable).
+__device__ __forceinline__ float from_orderable(uint32_t o) { return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o); }
+
+// Radix-select step, in every wave: from the histogram h of one key byte over the keys that match
+// the bytes chosen so far, the byte value holding the need-th largest of them; need becomes its
+// rank among the keys with that byte. Lane l reads bytes 255 - 4 l down to 252 - 4 l.
+__device__ __forceinline__ uint32_t select_byte(const uint32_t* h, int& need) {
+  const int lane = lane_id();
+  const uint4 b = *reinterpret_cast<const uint4*>(h + 252 - 4 * lane);
+  const int c[4] = {(int)b.w, (int)b.z, (int)b.y, (int)b.x};
+  const int tot = c[0] + c[1] + c[2] + c[3];
+  const int incl = wave_scan_i(tot), excl = incl - tot;
+  const unsigned long long hit = __ballot(excl < need && need <= incl);
+  const int L = hit ? __builtin_ctzll(hit) : 63;  // need never exceeds the keys counted
+  int e = excl, q = 3;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    if (q == 3 && e + c[i] >= need) q = i;
+    if (q == 3) e += c[i];
+  }
+  need -= __builtin_amdgcn_readlane(e, L);
+  return (uint32_t)(255 - 4 * L - __builtin_amdgcn_readlane(q, L));
+}
+
+// Sampled id of a step from the logits of every workgroup's VPER head rows (lanes 0..VPER-1 of
+// wave 0 hold this workgroup's). The acoustic sampler has no repetition penalty: the logits are
+// divided by the temperature; top-k keeps the k largest in the order (logit descending, id
+// ascending), found by a radix select over the orderable 32-bit keys; top-p keeps the shortest
+// prefix of that order whose probability mass reaches top_p; the id is the first whose running sum
+// of exp(l - l_max) exceeds u times the sum, else the last kept. Each workgroup gathers all V
+// logits and every wave computes the same id from them, so no further exchange follows.
+// Returns the id, or -1 on failure.
+__device__ __forceinline__ int sample_exchange(Ctx& c, const CpCall& C, float logit, float u) {
+  const int lane = lane_id(), w = xtp::wave_id(), tid = xtp::fresh_tid();
+  Smem& S = *c.S;
+  ++c.tag;
+  static_assert(xtp::CAND == VPER && V == 4 * NT, "one candidate line per workgroup; four logits per thread");
+  u64* cb = c.Dd->cand + (size_t)(c.apar & 1) * NWG * xtp::CAND;
+  if (w == 0 && lane < VPER) xtp::st_c(cb + blockIdx.x * VPER + lane, xtp::pack(logit, c.tag));
+  // histograms and the kept count start at zero (ordered before their use by the gather's barrier)
+  for (int i = tid; i < 4 * 256; i += NT) (&S.bins[0][0])[i] = 0u;
+  if (tid == 0) S.ncand = 0;
+  const float temp = C.temperature;
+  if (!xtp::get_each<V / NT>(V, c.tag, c.X.err, [&](int i) -> const u64* { return cb + i; },
+                             [&](int i, float v) { S.sv[i] = v / temp; }))
+    return -1;
+  ++c.apar;
+  // thread t holds ids 4 t .. 4 t + 3
+  const float4 x4 = *reinterpret_cast<const float4*>(&S.sv[4 * tid]);
+  const uint32_t o[4] = {orderable(x4.x), orderable(x4.y), orderable(x4.z), orderable(x4.w)};
+  const int k = C.top_k;
+  uint32_t T = 0, mask = 0;
+  int need = k;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int shift = 24 - 8 * q;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if ((o[i] & mask) == T) atomicAdd(&S.bins[q][(o[i] >> shift) & 255u], 1u);
+    xtp::lds_barrier();
+    T |= select_byte(S.bins[q], need) << shift;
+    mask |= 0xffu << shift;
+  }
+  // T: the k-th largest key; every key above it is kept, and the need lowest ids of those equal to it
+  int before = 0;  // keys equal to T at lower ids than this thread's
+  if (need < (int)S.bins[3][T & 255u]) {  // a tie at the cut (the same branch in every wave)
+    const int e = (o[0] == T) + (o[1] == T) + (o[2] == T) + (o[3] == T);
+    const int incl = wave_scan_i(e);
+    if (lane == 63) S.wsum[w] = incl;
+    xtp::lds_barrier();
+    before = incl - e;
+    for (int ww = 0; ww < w; ++ww) before += S.wsum[ww];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bool take = o[i] > T;
+    if (o[i] == T) take = before++ < need;
+    if (take) {
+      const int slot = atomicAdd(&S.ncand, 1);
+      if (slot < KS) S.ckey[slot] = ((u64)(~o[i]) << 32) | (uint32_t)(4 * tid + i);
+    }
+  }
+  xtp::lds_barrier();
+  // every wave: the kept keys sorted ascending over its lanes (bitonic), i.e. logit descending
+  u64 key = lane < k ? S.ckey[lane] : ~0ull;
+#pragma unroll
+  for (int kk = 2; kk <= 64; kk <<= 1) {
+#pragma unroll
+    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)key, jj), hi = __shfl_xor((uint32_t)(key >> 32), jj);
+      const u64 other = ((u64)hi << 32) | lo;
+      const bool keep_min = ((lane & jj) == 0) == ((lane & kk) == 0);
+      key = keep_min ? (other < key ? other : key) : (other > key ? other : key);
+    }
+  }
+  const float v = from_orderable(~(uint32_t)(key >> 32));
+  const int id = (int)(uint32_t)key;
+  const float l0 = rl(v, 0);
+  float wt = lane < k ? expf(v - l0) : 0.f;
+  int kept = k;
+  if (C.top_p < 1.0f) {
+    const float tot = rl(wave_scan_f(wt), 63);
+    const float cp = wave_scan_f(wt / tot);
+    const unsigned long long m = __ballot(lane < k && cp >= C.top_p);
+    kept = m ? __builtin_ctzll(m) + 1 : k;
+    if (lane >= kept) wt = 0.f;
+  }
+  const float cum = wave_scan_f(wt);
+  const float target = u * rl(cum, kept - 1);
+  const unsigned long long hit = __ballot(lane < kept && cum > target);
+  const int pick = hit ? __builtin_ctzll(hit) : kept - 1;
+  const int best = __builtin_amdgcn_readlane(id, pick);
+  return (unsigned)best < (unsigned)V ? best : 0;
+}
+
 // Step j's input rows: this rank's elements into xo[xb], the sums of squares into ss[xb], and the
 // rows times the first layer's attention gain, in parts, into xsp. M = 2 at step 1 (h_T and
 // E_sem[tok]), else E_ac[j - 1][tok]. With an input projection P, step 1 splits its K across the
@@ -714,7 +867,8 @@ __device__ __forceinline__ bool cp_step(Ctx& c, const CpCall& C, Wl<WT>& R, cons
     if (C.logits && lane < VPER) xtp::glb(C.logits)[(size_t)(j - 1) * V + VPER * blockIdx.x + lane] = logit;
   }
   TTS_STAMP(42);
-  const int best = argmax_exchange(c, logit);
+  const int best = C.do_sample ? sample_exchange(c, C, logit, xtp::glb(C.u)[C.u_offset + (C.use_frame ? frame * C.u_f_stride : 0) + j - 1])
+                               : argmax_exchange(c, logit);
   TTS_STAMP(43);
   if (best < 0) return false;
   if (blockIdx.x == 0 && threadIdx.x == 0) xtp::glb(C.codes)[(C.use_frame ? (long)frame * C.f_stride : 0) + j - 1] = best;

@@ -111,6 +111,12 @@ struct CpCall {
   int32_t f_stride, use_frame;
   float* logits;            // [15][V] or nullptr
   int32_t* next_tok;        // optional: last token fed forward (unused by the frame loop)
+  // sampled acoustic ids (the hidden-1024 CodePredictor kernel only; 0 = greedy): top_k in
+  // 1..64, top_p, temperature; step j draws at u[u_offset + (use_frame ? frame * u_f_stride : 0) + j - 1]
+  int32_t do_sample, top_k;
+  float top_p, temperature;
+  const float* u;
+  int32_t u_f_stride, u_offset;
 };
 
 // Wave index as a wave-uniform (scalar) value, so row addresses derived from it stay scalar.

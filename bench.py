@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=16, help="untimed frames before the timed ones")
     p.add_argument("--reps", type=int, default=5, help="timed runs (prefill + warmup + timed); median and max reported")
     p.add_argument("--workload", default="1.7b")
-    p.add_argument("--extra", default="0.6b,1.7b-x32,1.7b-long",
+    p.add_argument("--extra", default="0.6b,1.7b-sampled,1.7b-x32,1.7b-long",
                    help="comma-separated workloads also timed, each on its own frame count ('' for none)")
     p.add_argument("--cpu-frames", type=int, default=200, help="frames of the oracle CPU baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")

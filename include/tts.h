@@ -188,7 +188,7 @@ int tts_talker_step_text(tts_ctx* ctx, const int32_t* prev_codes, const int32_t*
  * per-frame cost counts it 15 times; "qwen3-tts-hip" README, section "Library
  * Usage": the subtalker sampling controls), conditioned on the pending Talker
  * hidden and on semantic [B]. ac: acoustic sampling; u [B, 15] uniforms
- * (ignored when greedy; may be NULL then). forced [B, 15] or NULL: when given,
+ * (ignored when greedy; may be NULL then; u[b][j-1] is step j's draw). forced [B, 15] or NULL: when given,
  * forced[b][j-1] replaces the drawn a_j as the input of step j+1 (teacher
  * forcing); the drawn tokens are still written to codes [B, 15] and the
  * logits to logits [B, 15, Va] when non-NULL. */
@@ -247,7 +247,11 @@ int tts_set_text_stream(tts_ctx* ctx, const int32_t* text_ids, int32_t n_text, i
  *    workgroups split each layer across the 8 XCDs tensor-parallel and
  *    exchange tagged values instead of ending kernels. One runs all 15
  *    CodePredictor steps of a frame (batch 1, greedy acoustic tokens, bf16 or
- *    E4M3 weights, a CodePredictor with 8 KV heads of dimension 128); one runs
+ *    E4M3 weights, a CodePredictor with 8 KV heads of dimension 128); for the
+ *    pages' CodePredictor shape (hidden 1024, FFN 3072, 16 query heads,
+ *    vocab 2048) it also draws sampled acoustic tokens itself when top_k is
+ *    in 1..64 (the logits gathered by every workgroup; same controls and
+ *    decision precision as tts_sample); one runs
  *    a whole Talker step (batch 1, bf16 or E4M3 weights, hidden 512, 1024 or
  *    2048, 8 KV heads of dimension 128 with 2 query heads each, an fp32 KV
  *    cache). Both need a device that keeps all their 256

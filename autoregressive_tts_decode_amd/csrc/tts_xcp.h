@@ -698,6 +698,7 @@ __device__ __forceinline__ int sample_exchange(Ctx& c, const CpCall& C, float lo
                              [&](int i, float v) { S.sv[i] = v / temp; }))
     return -1;
   ++c.apar;
+  TTS_STAMP(44);
   // thread t holds ids 4 t .. 4 t + 3
   const float4 x4 = *reinterpret_cast<const float4*>(&S.sv[4 * tid]);
   const uint32_t o[4] = {orderable(x4.x), orderable(x4.y), orderable(x4.z), orderable(x4.w)};
@@ -714,6 +715,7 @@ __device__ __forceinline__ int sample_exchange(Ctx& c, const CpCall& C, float lo
     T |= select_byte(S.bins[q], need) << shift;
     mask |= 0xffu << shift;
   }
+  TTS_STAMP(45);
   // T: the k-th largest key; every key above it is kept, and the need lowest ids of those equal to it
   int before = 0;  // keys equal to T at lower ids than this thread's
   if (need < (int)S.bins[3][T & 255u]) {  // a tie at the cut (the same branch in every wave)
@@ -734,6 +736,7 @@ __device__ __forceinline__ int sample_exchange(Ctx& c, const CpCall& C, float lo
     }
   }
   xtp::lds_barrier();
+  TTS_STAMP(46);
   // every wave: the kept keys sorted ascending over its lanes (bitonic), i.e. logit descending
   u64 key = lane < k ? S.ckey[lane] : ~0ull;
 #pragma unroll

@@ -30,7 +30,8 @@ CP_LABELS = {
     1: "start", 2: "constants+tiles issued", 3: "end",
     40: "step", 41: "step input", 10: "layer", 11: "q/k/v published", 13: "q/k/v gathered", 14: "attention",
     15: "gate/up published", 16: "SwiGLU gathered", 20: "reduce published", 21: "after-publish issue",
-    22: "reduce-scatter got", 23: "all-gather published", 24: "all-gather got", 42: "head dot", 43: "argmax",
+    22: "reduce-scatter got", 23: "all-gather published", 24: "all-gather got", 42: "head dot", 43: "token",
+    44: "logits gathered", 45: "top-k bound found", 46: "kept keys placed",
 }
 TALKER_LABELS = {
     49: "start", 50: "layer", 51: "q/k/v dots", 52: "q/k/v gathered", 53: "q/k prepared", 54: "attention chunk",

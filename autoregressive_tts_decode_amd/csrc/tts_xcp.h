@@ -890,55 +890,114 @@ __global__ __launch_bounds__(NT) void k_cp_frame(CpCall C) {
   const int g = xtp::xcd_id(), r = blockIdx.x / NX, tid = threadIdx.x;
   Wl<WT> R;
   typename Frag<WT>::T pj[2];
-  // RMSNorm gains, q/k-norm gains and the RoPE factors into LDS
+  // RMSNorm gains, q/k-norm gains, the RoPE factors (and the E4M3 row scales) into LDS. Each wave
+  // copies whole vectors, so the pointers it reads from the descriptor are wave-uniform (scalar
+  // loads; a per-lane read of the descriptor is a vector load that waits for every load before
+  // it), and every load is issued before the first store, so they are in flight together.
   {
-    const int nl = Dd.n_layers;
-    for (int i = tid; i < (2 * nl + 1) * (H / 8); i += NT) {
-      const int v = i / (H / 8), u = i % (H / 8);
-      const void* src = v == 2 * nl ? Dd.final_norm : (v & 1) ? Dd.layer[v >> 1].mlp_norm : Dd.layer[v >> 1].attn_norm;
-      *reinterpret_cast<u32x4*>(&S.gn[v == 2 * nl ? 2 * MAXL : v][8 * u]) = units(reinterpret_cast<const uint16_t*>(src))[u];
-    }
-    for (int i = tid; i < nl * 2 * (D / 8); i += NT) {
-      const int l = i / (2 * (D / 8)), k = (i / (D / 8)) & 1, u = i % (D / 8);
-      const void* src = k ? Dd.layer[l].k_norm : Dd.layer[l].q_norm;
-      *reinterpret_cast<u32x4*>(&S.gqk[l][k][8 * u]) = units(reinterpret_cast<const uint16_t*>(src))[u];
-    }
-    for (int i = tid; i < P * (D / 2); i += NT) {
-      S.rope[i / (D / 2)][0][i % (D / 2)] = xtp::glb(Dd.rope_cos)[i];
-      S.rope[i / (D / 2)][1][i % (D / 2)] = xtp::glb(Dd.rope_sin)[i];
-    }
-    if (tid < 8) S.zero[tid] = 0;
-    if constexpr (sizeof(WT) == 1) {
-      // the row scales of this workgroup's rows (1 where a layer or the projection is absent)
-      for (int i = tid; i < SCN; i += NT) {
-        float v = 1.f;
-        if (i < SCH) {
-          const int l = i / SCL, k = i % SCL;
-          if (l < nl) {
-            const KCONST xtp::LayerS& Sc = Dd.scale[l];
-            if (k < SCO) {
-              const int q0 = QPER * r + k;
-              v = q0 < G * D ? xtp::glb(Sc.wq)[G * D * g + q0]
-                             : q0 < (G + 1) * D ? xtp::glb(Sc.wk)[D * g + q0 - G * D] : xtp::glb(Sc.wv)[D * g + q0 - (G + 1) * D];
-            } else if (k < SCG) {
-              v = xtp::glb(Sc.wo)[HPER * r + k - SCO];
-            } else if (k < SCU) {
-              v = xtp::glb(Sc.wg)[FX * g + FPER * r + k - SCG];
-            } else if (k < SCD) {
-              v = xtp::glb(Sc.wu)[FX * g + FPER * r + k - SCU];
-            } else {
-              v = xtp::glb(Sc.wd)[HPER * r + k - SCD];
-            }
-          }
-        } else if (i < SCP) {
-          const int jj = (i - SCH) / VPER, e = (i - SCH) % VPER;
-          v = xtp::glb(Dd.head_scale)[(size_t)jj * V + VPER * blockIdx.x + e];
-        } else if (Dd.proj_scale) {
-          v = xtp::glb(Dd.proj_scale)[HPER * r + i - SCP];
-        }
-        S.scl[i] = v;
+    const int nl = Dd.n_layers, w = xtp::wave_id(), lane = lane_id();
+    static_assert(H / 8 == 128 && D / 8 == 16 && P * (D / 2) == 2 * NT && SCL <= 128 && 15 * VPER <= 128 && HPER <= 64,
+                  "prologue copy shapes");
+    // norm gains: vector v (layer v / 2's attention or MLP gain, the final gain at v = 2 nl) on wave v % NW
+    constexpr int NGV = (2 * MAXL + 1 + NW - 1) / NW;
+    u32x4 gv[NGV][2];
+#pragma unroll
+    for (int k = 0; k < NGV; ++k) {
+      const int v = w + NW * k;
+      if (v <= 2 * nl) {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(
+            v == 2 * nl ? Dd.final_norm : (v & 1) ? Dd.layer[v >> 1].mlp_norm : Dd.layer[v >> 1].attn_norm);
+        gv[k][0] = units(src)[lane];
+        gv[k][1] = units(src)[lane + 64];
       }
     }
+    // q/k-norm gains: vector 2 l + k (k = 1: the k-norm) on wave (2 l + k) % NW, lanes 0..15
+    constexpr int NQV = (2 * MAXL + NW - 1) / NW;
+    u32x4 qv[NQV];
+#pragma unroll
+    for (int k = 0; k < NQV; ++k) {
+      const int v = w + NW * k;
+      if (v < 2 * nl && lane < D / 8) {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>((v & 1) ? Dd.layer[v >> 1].k_norm : Dd.layer[v >> 1].q_norm);
+        qv[k] = units(src)[lane];
+      }
+    }
+    float rcs[2], rsn[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      rcs[k] = xtp::glb(Dd.rope_cos)[tid + NT * k];
+      rsn[k] = xtp::glb(Dd.rope_sin)[tid + NT * k];
+    }
+    // E4M3 row scales of this workgroup's rows (1 where a layer or the projection is absent): wave
+    // l < MAXL the layer's SCL, wave MAXL the 15 heads' VPER each, wave MAXL + 1 the projection's
+    float sv2[2] = {1.f, 1.f};
+    if constexpr (sizeof(WT) == 1) {
+      if (w < MAXL) {
+        if (w < nl) {
+          const KCONST xtp::LayerS& Sc = Dd.scale[w];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int k = lane + 64 * h;
+            if (k < SCO) {
+              const int q0 = QPER * r + k;
+              sv2[h] = q0 < G * D ? xtp::glb(Sc.wq)[G * D * g + q0]
+                                  : q0 < (G + 1) * D ? xtp::glb(Sc.wk)[D * g + q0 - G * D] : xtp::glb(Sc.wv)[D * g + q0 - (G + 1) * D];
+            } else if (k < SCG) {
+              sv2[h] = xtp::glb(Sc.wo)[HPER * r + k - SCO];
+            } else if (k < SCU) {
+              sv2[h] = xtp::glb(Sc.wg)[FX * g + FPER * r + k - SCG];
+            } else if (k < SCD) {
+              sv2[h] = xtp::glb(Sc.wu)[FX * g + FPER * r + k - SCU];
+            } else if (k < SCL) {
+              sv2[h] = xtp::glb(Sc.wd)[HPER * r + k - SCD];
+            }
+          }
+        }
+      } else if (w == MAXL) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e = lane + 64 * h;
+          if (e < 15 * VPER) sv2[h] = xtp::glb(Dd.head_scale)[(size_t)(e / VPER) * V + VPER * blockIdx.x + e % VPER];
+        }
+      } else if (w == MAXL + 1 && Dd.proj_scale && lane < HPER) {
+        sv2[0] = xtp::glb(Dd.proj_scale)[HPER * r + lane];
+      }
+    }
+    // the stores
+#pragma unroll
+    for (int k = 0; k < NGV; ++k) {
+      const int v = w + NW * k;
+      if (v <= 2 * nl) {
+        uint16_t* dst = S.gn[v == 2 * nl ? 2 * MAXL : v];
+        *reinterpret_cast<u32x4*>(&dst[8 * lane]) = gv[k][0];
+        *reinterpret_cast<u32x4*>(&dst[8 * (lane + 64)]) = gv[k][1];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NQV; ++k) {
+      const int v = w + NW * k;
+      if (v < 2 * nl && lane < D / 8) *reinterpret_cast<u32x4*>(&S.gqk[v >> 1][v & 1][8 * lane]) = qv[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + NT * k;
+      S.rope[i / (D / 2)][0][i % (D / 2)] = rcs[k];
+      S.rope[i / (D / 2)][1][i % (D / 2)] = rsn[k];
+    }
+    if constexpr (sizeof(WT) == 1) {
+      if (w < MAXL) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (lane + 64 * h < SCL) S.scl[w * SCL + lane + 64 * h] = sv2[h];
+      } else if (w == MAXL) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (lane + 64 * h < 15 * VPER) S.scl[SCH + lane + 64 * h] = sv2[h];
+      } else if (w == MAXL + 1 && lane < HPER) {
+        S.scl[SCP + lane] = sv2[0];
+      }
+    }
+    if (tid < 8) S.zero[tid] = 0;
   }
   // the first layer's weight tiles (and the resident input-projection tiles) after the small
   // loads above, which would otherwise wait behind them

@@ -697,6 +697,11 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
   };
   RowCopy<true> dn;  // the down rows, by the front waves, in two parts
   WBuf X0, X1;
+  // the step's input row before the weight tiles (a wave's loads return in order: issued behind
+  // the tiles it would wait for them), four elements per thread
+  static_assert(THMAX <= 4 * NT, "one 16-byte load per thread holds the input row");
+  f32x4 xin = {0.f, 0.f, 0.f, 0.f};
+  if (4 * tid < H) xin = *reinterpret_cast<const GLB f32x4*>(glb(D.x_in) + 4 * tid);
   tk_issue_a<WT>(X0, D, D.layer[0], 0, g, r);
   tk_issue_a<WT>(X1, D, D.layer[0], 1, g, r);
   gu_begin(D.layer[0]);
@@ -709,7 +714,7 @@ __global__ __launch_bounds__(NT) void k_talker_step(TkCall C) {
     rs = glb(D.rope_sin)[(size_t)p * 64 + lane];
   }
   int iring = 0, cpar = 0, apar = 0;
-  for (int i = tid; i < H; i += NT) S.xs[i] = glb(D.x_in)[i];
+  if (4 * tid < H) *reinterpret_cast<f32x4*>(&S.xs[4 * tid]) = xin;
   if (tid < 8) S.zero[tid] = 0;
   lds_barrier();
   float* xn = reinterpret_cast<float*>(S.xnp);  // cross-reduce partials (the split row is dead by then)

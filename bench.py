@@ -14,7 +14,9 @@ at 5 runs) is reported beside it, with the GPU clock and temperature read
 after every run. The other configs named in --extra run the same protocol on
 their own workloads (W = 16, K = the rest of their frames) and are reported
 under ``extra``. Prints one JSON line. The oracle (plain NumPy) is timed on a
-bounded sample of the same workload on the host cores as ``cpu_baseline``.
+bounded sample of the same workload on the host cores as ``cpu_baseline``. Each roofline fraction
+is also given against the box's measured device-copy bandwidth (``copy_bandwidth``,
+``frac_of_copy``).
 """
 from __future__ import annotations
 
@@ -143,6 +145,29 @@ def cpu_baseline(wl, weights, frames: int) -> dict:
 
 
 # ---------------------------------------------------------------------------- GPU runs
+
+def copy_bandwidth(mib: int = 1024, reps: int = 10) -> dict:
+    """The box's device-to-device copy rate, the practical HBM ceiling beside the 8 TB/s peak: one
+    buffer of `mib` MiB copied `reps` times by torch's copy kernel, HIP events around the copies on
+    the current stream; bytes moved = bytes read + bytes written."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbs": round(2 * n * 4 / t / 1e9, 1), "bytes_per_copy": 2 * n * 4, "reps": reps,
+            "note": "torch device copy; read + written bytes over HIP-event time"}
+
 
 def time_workload(name: str, K: int, W: int, reps: int, smi: Smi, args, weights=None, dominant: bool = False) -> dict:
     """The protocol on one workload: a discarded full run, then `reps` timed runs."""
@@ -304,6 +329,9 @@ def main():
     }
     if "prompt_lengths" in head:
         out["config"]["prompt_lengths"] = head["prompt_lengths"]
+    cbw = copy_bandwidth()
+    out["copy_bandwidth"] = cbw
+    out["frame_roofline"]["frac_of_copy"] = round(out["frame_roofline"]["achieved"] / cbw["gbs"], 4)
     if head["dom"] is not None:
         dom_s, dom_bytes = head["dom"]
         a_gbs = dom_bytes / dom_s / 1e9
@@ -312,7 +340,8 @@ def main():
         out["roofline"] = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": peak, "unit": "GB/s",
                            "frac": round(a_gbs / peak, 4), "traffic": traffic,
                            "kernel": "k_cp_frame (persistent CodePredictor frame: 15 steps)",
-                           "avg_launch_us": round(dom_s * 1e6, 2), "algorithmic_bytes_per_launch": int(dom_bytes)}
+                           "avg_launch_us": round(dom_s * 1e6, 2), "algorithmic_bytes_per_launch": int(dom_bytes),
+                           "frac_of_copy": round(a_gbs / cbw["gbs"], 4)}
     else:
         out["roofline"] = dict(head["frame_roofline"], traffic=None)
     extra = {}

@@ -24,7 +24,7 @@ from autoregressive_tts_decode_amd import config, synth, tts
 from oracle import OracleModel
 from oracle.decoder import linear
 from oracle.sampler import sample_token
-from parity_util import (rowwise_rel_err, greedy_agreement, top2_margin, sample_exempt, check_free_running,
+from parity_util import (MIN_CHECKED, rowwise_rel_err, greedy_agreement, top2_margin, sample_exempt, check_free_running,
                          check_stop_masking)
 
 pytestmark = pytest.mark.gpu
@@ -208,7 +208,7 @@ def test_tiny_sampled_frames_teacher_forced(tiny):
                 checked += 1
                 assert got_ac[j] == codes[0, t, 1 + j], f"acoustic draw {j + 1} differs at frame {t}"
         hist_np[0, codes[0, t, 0]] = True
-    assert checked > 0.9 * (checked + exempt)
+    assert checked > MIN_CHECKED * (checked + exempt)
     print(f"tiny sampled: {checked} draws equal, {exempt} exempt")
 
 
@@ -878,18 +878,19 @@ def test_1p7b_x32_sampled_streams_teacher_forced():
     dec.close()
     del dw
     torch.cuda.empty_cache()
-    assert checked > 0.9 * (checked + exempt)
+    assert checked > MIN_CHECKED * (checked + exempt)
     print(f"1.7b x32 sampled: logits rel err <= {worst:.2e}; {checked} draws equal, {exempt} exempt")
 
 
-@pytest.mark.parametrize("name", ["0.6b", "1.7b", "0.6b-fp8"])
-def test_gemm_prefill_matches_step_prefill_and_oracle(name):
-    """The prompt pass as MFMA GEMMs (chunks of 64 positions, 2 streams, a ragged last chunk) against
-    the one-position-at-a-time path and the oracle: logits after the prompt and after one Talker step
-    on the same codes (which reads the KV cache both prefills wrote)."""
+@pytest.mark.parametrize("name,B", [("0.6b", 2), ("1.7b", 2), ("0.6b-fp8", 2), ("1.7b", 1), ("1.7b-fp8", 1)])
+def test_gemm_prefill_matches_step_prefill_and_oracle(name, B):
+    """The prompt pass as MFMA GEMMs (chunks of 64 positions, a ragged last chunk) against the
+    one-position-at-a-time path and the oracle: logits after the prompt and after one Talker step on
+    the same codes (which reads the KV cache both prefills wrote). 2 streams: chunks of 128 and 72
+    rows (row tiles); 1 stream: chunks of 64 and 36 rows (the split-K route of few rows)."""
     model = config.MODELS[name]
     w = synth.make_weights(model, 0)
-    B, n = 2, 100
+    n = 100
     ids = synth.random_ids(n, model.text_vocab, seed=11, batch=B)
     codes = np.concatenate([synth.random_ids(1, model.talker.vocab, seed=12, batch=B),
                             synth.random_ids(15, model.codepred.vocab, seed=13, batch=B)], axis=1)
@@ -918,9 +919,9 @@ def test_gemm_prefill_matches_step_prefill_and_oracle(name):
         for g, r in ((g0, ref0), (g1, ref1)):
             n_, ex, bad = greedy_agreement(np.argmax(g, axis=-1), r)
             assert not bad, (mode, bad)
-        print(f"{name} prefill mode {mode}: rel err after prompt {e0:.2e}, after one step {e1:.2e}")
+        print(f"{name} x{B} prefill mode {mode}: rel err after prompt {e0:.2e}, after one step {e1:.2e}")
     e = rowwise_rel_err(got[tts.PREFILL_GEMM][1], got[tts.PREFILL_STEPS][1]).max()
-    print(f"{name}: GEMM vs step prefill, step logits rel diff {e:.2e}")
+    print(f"{name} x{B}: GEMM vs step prefill, step logits rel diff {e:.2e}")
 
 
 # ----------------------------------------------------------------------------- reproducibility

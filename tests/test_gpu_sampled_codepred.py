@@ -10,7 +10,8 @@ Three kinds of check:
     sum); ties of equal logits at the top-k cut are not exempt, so rows of a head made identical
     check that the lowest ids are kept;
   * logits and draws against the oracle model, teacher-forced (logits within the bf16 bar, draws
-    equal wherever the oracle's draw is not within 1e-4 of a boundary);
+    equal wherever the oracle's draw is not within 1e-4 of a boundary or of a near tie in the kept
+    order, see parity_util.sample_exempt);
   * a free-running sampled frame graph checked by the oracle along its own codes, and run twice
     with equal codes.
 """
@@ -21,7 +22,7 @@ import torch
 from autoregressive_tts_decode_amd import config, synth, tts
 from oracle.decoder import OracleModel
 from oracle.sampler import sample_token
-from parity_util import rowwise_rel_err, sample_exempt
+from parity_util import MIN_CHECKED, rowwise_rel_err, sample_exempt
 
 pytestmark = pytest.mark.gpu
 SEM = config.SEMANTIC_SAMPLED.as_dict()
@@ -168,7 +169,7 @@ def test_sampled_codepred_teacher_forced_against_the_oracle(name):
             else:
                 checked += 1
                 assert got[j] == codes[0, t, 1 + j], f"frame {t}: acoustic draw {j + 1} differs from the oracle's"
-    assert checked > 0.9 * (checked + exempt)
+    assert checked > MIN_CHECKED * (checked + exempt)
     print(f"{name}: logits rel err <= {worst:.2e}; {checked} draws equal to the oracle's, {exempt} exempt; "
           f"{own_eq} equal to the oracle sampler on the kernel's logits")
     dec.close()
@@ -222,5 +223,5 @@ def test_sampled_frame_graph_checked_by_the_oracle_and_reproducible():
                 checked += 1
                 assert got[0, t, 1 + j] == ref["codes"][0, t, 1 + j], f"frame {t}: acoustic draw {j + 1} differs"
         hist[got[0, t, 0]] = True
-    assert checked > 0.9 * (checked + exempt)
+    assert checked > MIN_CHECKED * (checked + exempt)
     print(f"1.7b sampled frame graph: {checked} draws equal to the oracle's, {exempt} exempt; two runs equal")

@@ -154,10 +154,10 @@ Layout make_layout(const tts_config& c) {
     L.ph = take(Mp * t.ffn * 4);
     L.ps = take(Mp * 4);
     // split-K partial tiles: a split GEMM has at most kGemmWgs (row tile, column tile, K slice)
-    // workgroups, each writing one 64 x 64 fp32 tile; the decode GEMM (rows <= 64) writes
-    // slices x rows x N
+    // workgroups, each writing one 64 x 64 fp32 tile; the decode GEMM (rows <= 64: decode steps and
+    // prompt chunks of few streams) writes slices x rows x N
     size_t pks = (size_t)kGemmWgs * kGBM * kGBN * 4;
-    const int mdec = (int)std::min<size_t>(rows, 64);
+    const int mdec = (int)std::min<size_t>(std::max(rows, Mp), 64);  // decode rows, or a prompt chunk of <= 64 rows
     const size_t qkvt = (size_t)(t.n_q_heads + 2 * t.n_kv_heads) * t.head_dim, qkvc = (size_t)(p.n_q_heads + 2 * p.n_kv_heads) * p.head_dim;
     const size_t shapes[][2] = {{qkvt, (size_t)t.hidden}, {(size_t)t.hidden, (size_t)t.n_q_heads * t.head_dim},
                                 {2 * (size_t)t.ffn, (size_t)t.hidden}, {(size_t)t.hidden, (size_t)t.ffn}, {(size_t)t.vocab, (size_t)t.hidden},
@@ -851,15 +851,32 @@ int prefill_gemm(tts_ctx* ctx, const int32_t* ids, int B, int n) {
   };
   for (int p0 = 0; p0 < n; p0 += kPrefillChunk) {
     const int P = std::min(kPrefillChunk, n - p0), M = B * P;
+    // A chunk of 16..64 rows (a prompt of one or a few streams) takes the batched decode's split-K
+    // route (proj_gemm): one 64-row tile per 64 weight rows would leave most CUs idle, while K
+    // slices let about 256 workgroups stream each matrix, and the slices are added in order.
+    // Wider chunks fill the chip with row tiles.
+    const bool split = M >= kGemmMinRows && M <= 64;
     hipLaunchKernelGGL(k_embed_rows<uint16_t>, dim3(M), dim3(256), 0, ctx->stream, ids, n, p0, P, c.text_vocab, ctx->embed_text, H, X);
     HIP_LAUNCH_CHECK();
+    ctx->ssq_x = nullptr;  // X holds fresh rows: no sums of squares are known for them
     for (int l = 0; l < t.n_layers; ++l) {
       const Layer& W = ctx->talker.layers[l];
       char* kc = w + ctx->L.tk + l * layer_cache;
       char* vc = w + ctx->L.tv + l * layer_cache;
-      hipLaunchKernelGGL(k_rowscale, dim3((M + 3) / 4), dim3(256), 0, ctx->stream, X, H, M, H, c.rms_eps, RS);
-      HIP_LAUNCH_CHECK();
-      if (int rc = gemm(X, H, RS, W.attn_norm, {{W.wq, qd}, {W.wk, kd}, {W.wv, kd}}, QKV, nqkv, H, M, 0)) return rc;
+      if (split) {
+        GemvArgs a = gemv_args(ctx);
+        a.ssq_in = l > 0;  // the previous layer's down projection left X's sums of squares
+        a.w[0] = W.wq; a.w[1] = W.wk; a.w[2] = W.wv;
+        a.seg_rows[0] = qd; a.seg_rows[1] = kd; a.seg_rows[2] = kd;
+        a.nseg = 3; a.N = nqkv; a.K = H; a.M = M;
+        a.src = SRC_VEC; a.x = X; a.x_stride = H; a.gain = W.attn_norm;
+        a.y = QKV; a.y_stride = nqkv; a.epi = EPI_STORE;
+        if (int rc = proj_gemm(ctx, a)) return rc;
+      } else {
+        hipLaunchKernelGGL(k_rowscale, dim3((M + 3) / 4), dim3(256), 0, ctx->stream, X, H, M, H, c.rms_eps, RS);
+        HIP_LAUNCH_CHECK();
+        if (int rc = gemm(X, H, RS, W.attn_norm, {{W.wq, qd}, {W.wk, kd}, {W.wv, kd}}, QKV, nqkv, H, M, 0)) return rc;
+      }
       QkArgs q;
       std::memset(&q, 0, sizeof q);
       q.qkv = QKV; q.q = Q; q.kc = kc; q.vc = vc; q.q_norm = W.q_norm; q.k_norm = W.k_norm;
@@ -875,19 +892,42 @@ int prefill_gemm(tts_ctx* ctx, const int32_t* ids, int B, int n) {
       pa.kvstart = ctx->kvstart;
       hipLaunchKernelGGL(k_prefill_attn<float>, dim3((P + 3) / 4, t.n_q_heads, B), dim3(256), 0, ctx->stream, pa);
       HIP_LAUNCH_CHECK();
-      if (int rc = gemm(O, qd, nullptr, nullptr, {{W.wo, H}}, X, H, qd, M, 1)) return rc;
-      hipLaunchKernelGGL(k_rowscale, dim3((M + 3) / 4), dim3(256), 0, ctx->stream, X, H, M, H, c.rms_eps, RS);
-      HIP_LAUNCH_CHECK();
-      if (int rc = gemm(X, H, RS, W.mlp_norm, {{W.wg, F}, {W.wu, F}}, GU, 2 * F, H, M, 0)) return rc;
-      hipLaunchKernelGGL(k_swiglu_rows, dim3(std::min((M * F + 255) / 256, 4096)), dim3(256), 0, ctx->stream, GU, M, F, Hh);
-      HIP_LAUNCH_CHECK();
-      if (int rc = gemm(Hh, F, nullptr, nullptr, {{W.wd, H}}, X, H, F, M, 1)) return rc;
+      if (split) {
+        // output projection + residual (leaves X's sums of squares), RMSNorm + gate/up + SwiGLU,
+        // down projection + residual (leaves them again)
+        GemvArgs a = gemv_args(ctx);
+        a.w[0] = W.wo; a.seg_rows[0] = H; a.N = H; a.K = qd; a.M = M;
+        a.src = SRC_VEC; a.x = O; a.x_stride = qd;
+        a.y = X; a.y_stride = H; a.res = X; a.res_stride = H; a.epi = EPI_RESID; a.ssq_out = 1;
+        if (int rc = proj_gemm(ctx, a)) return rc;
+        a = gemv_args(ctx);
+        a.ssq_in = 1;
+        a.w[0] = W.wg; a.w[1] = W.wu; a.seg_rows[0] = F; a.seg_rows[1] = F; a.nseg = 2;
+        a.N = F; a.K = H; a.M = M;
+        a.src = SRC_VEC; a.x = X; a.x_stride = H; a.gain = W.mlp_norm;
+        a.y = Hh; a.y_stride = F; a.epi = EPI_SWIGLU;
+        if (int rc = proj_gemm(ctx, a)) return rc;
+        a = gemv_args(ctx);
+        a.w[0] = W.wd; a.seg_rows[0] = H; a.N = H; a.K = F; a.M = M;
+        a.src = SRC_VEC; a.x = Hh; a.x_stride = F;
+        a.y = X; a.y_stride = H; a.res = X; a.res_stride = H; a.epi = EPI_RESID; a.ssq_out = 1;
+        if (int rc = proj_gemm(ctx, a)) return rc;
+      } else {
+        if (int rc = gemm(O, qd, nullptr, nullptr, {{W.wo, H}}, X, H, qd, M, 1)) return rc;
+        hipLaunchKernelGGL(k_rowscale, dim3((M + 3) / 4), dim3(256), 0, ctx->stream, X, H, M, H, c.rms_eps, RS);
+        HIP_LAUNCH_CHECK();
+        if (int rc = gemm(X, H, RS, W.mlp_norm, {{W.wg, F}, {W.wu, F}}, GU, 2 * F, H, M, 0)) return rc;
+        hipLaunchKernelGGL(k_swiglu_rows, dim3(std::min((M * F + 255) / 256, 4096)), dim3(256), 0, ctx->stream, GU, M, F, Hh);
+        HIP_LAUNCH_CHECK();
+        if (int rc = gemm(Hh, F, nullptr, nullptr, {{W.wd, H}}, X, H, F, M, 1)) return rc;
+      }
     }
     if (p0 + P == n) {
       hipLaunchKernelGGL(k_last_rows, dim3(B), dim3(256), 0, ctx->stream, X, P, H, ctx->x);
       HIP_LAUNCH_CHECK();
     }
   }
+  ctx->ssq_x = nullptr;  // the staging rows' sums of squares are of no later GEMM's input
   return TTS_OK;
 }
 

@@ -88,11 +88,21 @@ size_t kv_bytes(const tts_config&) { return 4; }
 
 bool xcp_capable(const tts_config& c);
 
-// K split of the decode GEMM (k_gemm_dec) for N output rows, K columns and M input rows: slices of
-// at most 256 columns (128 past 32 rows: the LDS holds the slice's A rows in three parts), more
-// of them while the grid has fewer than 256 workgroups; returns the slice count.
-int dec_split(int N, int K, int M, int* kslice) {
-  const int kmax = M <= 32 ? 256 : 128, tiles = N / 64;
+// Weight row tiles of 64 per decode-GEMM workgroup: 4 past 32 input rows (the staged A slice then
+// serves 256 weight rows) when every segment is a whole number of 256-row blocks, else 1.
+int dec_rw(int M, const int* seg_rows, int nseg) {
+  if (M <= 32) return 1;
+  for (int s = 0; s < nseg; ++s)
+    if (seg_rows[s] % 256) return 1;
+  return 4;
+}
+
+// K split of the decode GEMM (k_gemm_dec) for N output rows, K columns, M input rows and rw row
+// tiles per workgroup: slices of at most 256 columns (128 past 32 rows: the LDS holds the slice's A
+// rows in three parts), more of them while the grid has fewer than 256 workgroups; returns the
+// slice count.
+int dec_split(int N, int K, int M, int rw, int* kslice) {
+  const int kmax = M <= 32 ? 256 : 128, tiles = N / (64 * rw);
   const int ks_min = (K + kmax - 1) / kmax;
   const int want = std::max(1, (256 + tiles - 1) / tiles);
   int ks = std::max(ks_min, std::min(want, K / 64));
@@ -166,9 +176,11 @@ Layout make_layout(const tts_config& c) {
                                 {(size_t)p.hidden, (size_t)t.hidden}};
     for (const auto& sh : shapes) {
       if (sh[0] % 64 || sh[1] % 64) continue;
-      int ksl = 0;
-      const int ks = dec_split((int)sh[0], (int)sh[1], mdec, &ksl);
-      pks = std::max(pks, (size_t)ks * mdec * sh[0] * 4);
+      for (const int rw : {1, 4}) {  // either row-tile choice (segments decide it at launch)
+        int ksl = 0;
+        const int ks = dec_split((int)sh[0], (int)sh[1], mdec, rw, &ksl);
+        pks = std::max(pks, (size_t)ks * mdec * sh[0] * 4);
+      }
     }
     L.pks = take(pks);
     // per-row, per-256-column chunk sums of squares a residual GEMM leaves for the next RMSNorm
@@ -626,10 +638,11 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
   // first for a residual epilogue), so results do not depend on workgroup timing.
   // Few rows (decode): k_gemm_dec, each workgroup's weight fragments loaded straight to registers.
   const bool dec = ctx->bf16() && a.M <= 64;
+  const int rw = dec ? dec_rw(a.M, a.seg_rows, a.nseg) : 1;
   const int tiles = (N / kGBN) * ((a.M + kGBM - 1) / kGBM);
   int ks = 1, kslice = a.K;
   if (dec) {
-    ks = dec_split(N, a.K, a.M, &kslice);
+    ks = dec_split(N, a.K, a.M, rw, &kslice);
   } else {
     ks = std::max(1, std::min(a.K / kGBK, kGemmWgs / tiles));
     kslice = ((a.K / kGBK + ks - 1) / ks) * kGBK;
@@ -652,9 +665,10 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
     }
   }
   if (dec) {
-    if (a.M <= 16) hipLaunchKernelGGL((k_gemm_dec<1, 256>), dim3(N / 64, 1, ks), dim3(256), 0, ctx->stream, g);
-    else if (a.M <= 32) hipLaunchKernelGGL((k_gemm_dec<2, 256>), dim3(N / 64, 1, ks), dim3(256), 0, ctx->stream, g);
-    else hipLaunchKernelGGL((k_gemm_dec<4, 128>), dim3(N / 64, 1, ks), dim3(256), 0, ctx->stream, g);
+    if (a.M <= 16) hipLaunchKernelGGL((k_gemm_dec<1, 256, 1>), dim3(N / 64, 1, ks), dim3(256), 0, ctx->stream, g);
+    else if (a.M <= 32) hipLaunchKernelGGL((k_gemm_dec<2, 256, 1>), dim3(N / 64, 1, ks), dim3(256), 0, ctx->stream, g);
+    else if (rw == 4) hipLaunchKernelGGL((k_gemm_dec<4, 128, 4>), dim3(N / 256, 1, ks), dim3(256), 0, ctx->stream, g);
+    else hipLaunchKernelGGL((k_gemm_dec<4, 128, 1>), dim3(N / 64, 1, ks), dim3(256), 0, ctx->stream, g);
   } else if (int rc = launch_gemm(ctx, g, dim3(N / kGBN, (a.M + kGBM - 1) / kGBM, ks))) {
     return rc;
   }

@@ -181,29 +181,33 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
 }
 
 // Decode GEMM for few rows (M <= 16 MT; bf16 weights): C = RMSNorm-scaled A [M][K] times the
-// weight rows W [N][K]^T. A workgroup (4 waves) owns 64 weight rows and one K slice of at most KSM
-// columns: wave w loads its 16 rows' B fragments for the whole slice into registers at once (lane
-// l: row l % 16, columns 32 s + 8 (l / 16) of K step s), while the workgroup stages the slice of
-// the A rows (times the row scale and the gain) in LDS as three bf16 parts (hi, mid, lo; their
-// sum is the fp32 value exactly, as in k_gemm_bf16); each K step is then MT x 3 MFMAs per wave,
-// the smallest part first. With several slices each writes its partial tile to part (slice z at
+// weight rows W [N][K]^T. A workgroup (4 waves) owns 64 RW weight rows (all in one segment) and one
+// K slice of at most KSM columns: wave w loads the B fragments of rows 64 t + 16 w + l % 16
+// (t < RW) for the whole slice into registers at once (lane l: columns 32 s + 8 (l / 16) of K
+// step s), while the workgroup stages the slice of the A rows (times the row scale and the gain) in
+// LDS as three bf16 parts (hi, mid, lo; their sum is the fp32 value exactly, as in k_gemm_bf16);
+// each K step is then MT x RW x 3 MFMAs per wave, the smallest part first, every A fragment read
+// once for the RW tiles. With several slices each writes its partial tile to part (slice z at
 // part + z M N) and a pass of its own adds them in slice order.
-template <int MT, int KSM>
+template <int MT, int KSM, int RW>
 __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
   constexpr int MR = 16 * MT;
   constexpr int LD = KSM + 8;  // LDS row stride (bf16)
   __shared__ __align__(16) __bf16 As[3][MR][LD];
   __shared__ float srs[MR];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 64;
+  const int n0 = blockIdx.x * 64 * RW;
   int seg = 0, nrel = n0;
   while (seg + 1 < a.nseg && nrel >= a.seg_rows[seg]) { nrel -= a.seg_rows[seg]; ++seg; }
   const int kbeg = blockIdx.z * a.kslice, kn = min(a.kslice, a.K - kbeg), nks = kn / 32;
   const uint16_t* wrow = reinterpret_cast<const uint16_t*>(a.w[seg]) + (size_t)(nrel + 16 * wave + (lane & 15)) * a.K + kbeg +
                          8 * (lane >> 4);
-  u32x4 b[KSM / 32];
+  u32x4 b[RW][KSM / 32];
 #pragma unroll
-  for (int s = 0; s < KSM / 32; ++s) b[s] = s < nks ? *reinterpret_cast<const u32x4*>(wrow + 32 * s) : (u32x4){0u, 0u, 0u, 0u};
+  for (int t2 = 0; t2 < RW; ++t2)
+#pragma unroll
+    for (int s = 0; s < KSM / 32; ++s)
+      b[t2][s] = s < nks ? *reinterpret_cast<const u32x4*>(wrow + (size_t)64 * t2 * a.K + 32 * s) : (u32x4){0u, 0u, 0u, 0u};
   if (tid < MR) {
     float sc = 1.f;
     if (tid < a.M) {
@@ -243,38 +247,44 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
     }
   }
   __syncthreads();
-  f32x4v acc[MT];
+  f32x4v acc[RW][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = (f32x4v){0.f, 0.f, 0.f, 0.f};
+  for (int t2 = 0; t2 < RW; ++t2)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t2][t] = (f32x4v){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < KSM / 32; ++s) {
     if (s < nks) {
-      const bf16x8 bw = __builtin_bit_cast(bf16x8, b[s]);
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
         for (int p = 2; p >= 0; --p) {
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(&As[p][16 * t + (lane & 15)][32 * s + 8 * (lane >> 4)]);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, acc[t], 0, 0, 0);
+#pragma unroll
+          for (int t2 = 0; t2 < RW; ++t2)
+            acc[t2][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, b[t2][s]), acc[t2][t], 0, 0, 0);
         }
     }
   }
   const bool split = a.kslice < a.K;
-  const int n = n0 + 16 * wave + (lane & 15);
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
+  for (int t2 = 0; t2 < RW; ++t2) {
+    const int n = n0 + 64 * t2 + 16 * wave + (lane & 15);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = 16 * t + 4 * (lane >> 4) + r;
-      if (m < a.M) {
-        if (split) {
-          a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[t][r];
-        } else {
-          float* c = a.C + (size_t)m * a.ldc + n;
-          *c = a.add ? *c + acc[t][r] : acc[t][r];
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = 16 * t + 4 * (lane >> 4) + r;
+        if (m < a.M) {
+          if (split) {
+            a.part[((size_t)blockIdx.z * a.M + m) * a.N + n] = acc[t2][t][r];
+          } else {
+            float* c = a.C + (size_t)m * a.ldc + n;
+            *c = a.add ? *c + acc[t2][t][r] : acc[t2][t][r];
+          }
         }
       }
-    }
+  }
 }
 
 // Rows of a bf16 table E [R][K] through a bias-free bf16 projection P [N][K]: T[a][i] =

@@ -506,11 +506,24 @@ __global__ __launch_bounds__(256) void k_prefill_attn(PAttnArgs a) {
     o0 *= corr;
     o1 *= corr;
     m = mn;
+    // the pass's v rows, all loads in flight together (rows past the pass are not loaded; their
+    // weight is 0), then the sums in position order
     const int np = min(16, pos + 1 - base);
-    for (int tt = 0; tt < np; ++tt) {
+    float va[16], vb[16];
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+      va[tt] = 0.f;
+      vb[tt] = 0.f;
+      if (tt < np) {
+        va[tt] = to_f32(vc[(size_t)(base + tt) * d + lane]);
+        vb[tt] = to_f32(vc[(size_t)(base + tt) * d + lane + 64]);
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
       const float wt = __shfl(w, 4 * tt);
-      o0 = fmaf(wt, to_f32(vc[(size_t)(base + tt) * d + lane]), o0);
-      o1 = fmaf(wt, to_f32(vc[(size_t)(base + tt) * d + lane + 64]), o1);
+      o0 = fmaf(wt, va[tt], o0);
+      o1 = fmaf(wt, vb[tt], o1);
     }
   }
   float* o = a.out + (size_t)row * a.nq * d + (size_t)h * d;

@@ -722,6 +722,54 @@ __device__ __forceinline__ int block_incl_scan256(int v, int* ws) {
   return v + add;
 }
 
+// Inclusive prefix sum of v over the 64 lanes of a wave, in lane order (Hillis-Steele steps).
+__device__ __forceinline__ float wave_incl_sum(float v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// The draw from k <= 64 kept keys ((~orderable value) << 32 | id, in any order; vals[id] the
+// scaled logit), by one whole wave with no block barrier: the keys sorted ascending across its
+// lanes (logit descending, then id ascending) by a bitonic network on lane exchanges; top-p keeps
+// the shortest prefix whose probability mass reaches top_p; the id is the first whose running sum
+// of exp(l - l_max) exceeds u times the sum, else the last kept. The sums are prefix sums over the
+// lanes (a fixed order). Returns the id in every lane.
+__device__ __forceinline__ int draw_wave(const unsigned long long* cand, int k, const float* vals, float top_p, float u) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long key = lane < k ? cand[lane] : ~0ull;
+#pragma unroll
+  for (int kk = 2; kk <= 64; kk <<= 1) {
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      const unsigned lo = __shfl_xor((unsigned)key, j), hi = __shfl_xor((unsigned)(key >> 32), j);
+      const unsigned long long other = ((unsigned long long)hi << 32) | lo;
+      const bool keep_min = ((lane & j) == 0) == ((lane & kk) == 0);
+      key = keep_min ? (other < key ? other : key) : (other > key ? other : key);
+    }
+  }
+  const int id = (int)(uint32_t)key;
+  const float v = lane < k ? vals[id] : 0.f;
+  const float l0 = __shfl(v, 0);
+  float w = lane < k ? expf(v - l0) : 0.f;
+  int kept = k;
+  if (top_p < 1.0f) {
+    const float tot = __shfl(wave_incl_sum(w), 63);
+    const float cp = wave_incl_sum(w / tot);
+    const unsigned long long m = __ballot(lane < k && cp >= top_p);
+    kept = m ? __builtin_ctzll(m) + 1 : k;
+    if (lane >= kept) w = 0.f;
+  }
+  const float cum = wave_incl_sum(w);
+  const float target = u * __shfl(cum, kept - 1);
+  const unsigned long long hit = __ballot(lane < kept && cum > target);
+  return __shfl(id, hit ? __builtin_ctzll(hit) : kept - 1);
+}
+
 // One block (256 threads) per stream.
 __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -750,6 +798,7 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   } else {
     __shared__ unsigned long long keys[kSortMax];
     __shared__ float vals[kSortMax];
+    bool drawn = false;  // the draw was made by one wave (top_k <= 64)
     const uint8_t* hist = a.history ? a.history + (size_t)b * a.h_stride : nullptr;
     if (a.top_k >= 1 && a.top_k <= kTopKMax && a.top_k <= a.V) {
       // Top-k without sorting all V: the order wanted is (logit desc, id asc), i.e. ascending
@@ -802,26 +851,35 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
         if (o == T) take = rank++ < need;
         if (take) cand[atomicAdd(&ncand, 1)] = ((unsigned long long)(~o) << 32) | (uint32_t)i;
       }
-      int n2k = 1;
-      while (n2k < k) n2k <<= 1;
       __syncthreads();
-      for (int i = k + tid; i < n2k; i += 256) cand[i] = ~0ull;
-      __syncthreads();
-      for (int kk = 2; kk <= n2k; kk <<= 1) {
-        for (int j = kk >> 1; j > 0; j >>= 1) {
-          for (int i = tid; i < n2k; i += 256) {
-            const int ixj = i ^ j;
-            if (ixj > i) {
-              const unsigned long long x = cand[i], y = cand[ixj];
-              const bool up = (i & kk) == 0;
-              if ((x > y) == up) { cand[i] = y; cand[ixj] = x; }
-            }
-          }
-          __syncthreads();
+      if (k <= 64) {
+        // the kept keys fit one wave: it orders them and draws (no block barrier per sort stage)
+        if (tid < 64) {
+          const int t = draw_wave(cand, k, vals, a.top_p, u_at(a.u, a.st, b));
+          if (tid == 0) chosen = t;
         }
+        drawn = true;
+      } else {
+        int n2k = 1;
+        while (n2k < k) n2k <<= 1;
+        for (int i = k + tid; i < n2k; i += 256) cand[i] = ~0ull;
+        __syncthreads();
+        for (int kk = 2; kk <= n2k; kk <<= 1) {
+          for (int j = kk >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < n2k; i += 256) {
+              const int ixj = i ^ j;
+              if (ixj > i) {
+                const unsigned long long x = cand[i], y = cand[ixj];
+                const bool up = (i & kk) == 0;
+                if ((x > y) == up) { cand[i] = y; cand[ixj] = x; }
+              }
+            }
+            __syncthreads();
+          }
+        }
+        for (int i = tid; i < k; i += 256) keys[i] = cand[i];
+        __syncthreads();
       }
-      for (int i = tid; i < k; i += 256) keys[i] = cand[i];
-      __syncthreads();
     } else {
     int n2 = 1;
     while (n2 < a.V) n2 <<= 1;
@@ -852,7 +910,7 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
       }
     }
     }
-    if (tid == 0) {
+    if (tid == 0 && !drawn) {
       int kk = (a.top_k <= 0 || a.top_k > a.V) ? a.V : a.top_k;
       const float l0 = vals[(uint32_t)keys[0]];
       if (a.top_p < 1.0f) {

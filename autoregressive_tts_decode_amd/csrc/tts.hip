@@ -33,15 +33,18 @@ namespace {
 constexpr int kCpPositions = 16;   // CodePredictor positions 0..15 per frame
 constexpr int kAttnChunk = 32;     // Talker positions per attention split (the partial buffer's unit)
 
-// Positions per attention block for B streams of nkv KV heads: kAttnChunk while the (stream, head)
-// pairs alone give the chip few blocks, up to 4 kAttnChunk once they give 4 per CU. A block pays a
-// fixed q/k norm, combine and merge cost; with 32 streams x 8 heads at ~300 positions, 32-position
-// splits made 2560 blocks of 32 KB of K/V each. A multiple of kAttnChunk keeps the partial
-// buffer's layout: split i of the larger chunk is its slot i, and the slots past the last used
-// split are never written or read.
-int attn_chunk(int B, int nkv) {
+// Positions per attention block for B streams of nkv KV heads and a cache of cap positions:
+// kAttnChunk while the (stream, head) pairs alone give the chip few blocks, 2 kAttnChunk at 128
+// pairs, and the whole cache (one block per pair, no split) once the pairs alone fill the chip
+// (256). A block pays a fixed q/k norm and combine cost, and split blocks the merge: its
+// device-scope fences write back the XCD's L2 (32 streams x 8 heads at ~270 positions: a frame
+// of 14.0 ms with 128-position splits, 8.8 ms with one block per pair). A multiple of kAttnChunk
+// keeps the partial buffer's layout: split i of the larger chunk is its slot i, and the slots past
+// the last used split are never written or read.
+int attn_chunk(int B, int nkv, int cap) {
   const int pairs = B * nkv;
-  return pairs >= 256 ? 4 * kAttnChunk : pairs >= 128 ? 2 * kAttnChunk : kAttnChunk;
+  if (pairs >= 256) return (cap + kAttnChunk - 1) / kAttnChunk * kAttnChunk;
+  return pairs >= 128 ? 2 * kAttnChunk : kAttnChunk;
 }
 constexpr int kMaxGemvM = 8;       // input rows per GEMV launch
 constexpr int kGemmMinRows = 16;   // batched projections with at least this many rows run as MFMA GEMMs
@@ -801,7 +804,7 @@ int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_c
     t.rope_cos = rc; t.rope_sin = rs;
     t.pos_const = pos_const; t.pos_from_state = pos_from_state;
     t.kc = (char*)kc + l * layer_cache; t.vc = (char*)vc + l * layer_cache;
-    t.cap = cap; t.chunk = nsplit == 1 ? cap : attn_chunk(B, c.n_kv_heads); t.nsplit = nsplit;
+    t.cap = cap; t.chunk = nsplit == 1 ? cap : attn_chunk(B, c.n_kv_heads, cap); t.nsplit = nsplit;
     t.out = ctx->attn; t.out_stride = qd; t.part = ctx->part; t.counters = ctx->counters; t.st = ctx->st;
     t.kvstart = kvstart;
     if (int rc_ = attention(ctx, t, B)) return rc_;

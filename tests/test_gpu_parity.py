@@ -242,10 +242,11 @@ def test_tiny_64_streams_take_64_position_attention_splits():
     dec.close()
 
 
-def test_0p6b_32_streams_take_128_position_attention_splits():
-    """32 streams of 8 KV heads (256 pairs) run 128-position decode attention splits; after a
-    132-id prompt the first decode step attends over two of them. Logits of both frames of every
-    stream within the bf16 bar of the oracle."""
+def test_0p6b_32_streams_attend_past_128_positions_in_one_block_per_pair():
+    """32 streams of 8 KV heads (256 pairs, enough blocks to fill the chip) attend in one block per
+    (stream, KV head) over the whole context, with no split and no merge; after a 132-id prompt the
+    decode steps attend over 133 and 134 positions. Logits of both frames of every stream within
+    the bf16 bar of the oracle. (Splits and their merge: the 64-stream and long-context tests.)"""
     model = config.MODELS["0.6b"]
     w = synth.make_weights(model, 0)
     B, F = 32, 2

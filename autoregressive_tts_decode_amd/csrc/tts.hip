@@ -347,6 +347,9 @@ struct tts_ctx {
   // rows whose chunk sums of squares sit in the ssq buffer (the last ssq_out GEMM's output), or null
   const float* ssq_x = nullptr;
   int ssq_stride = 0, ssq_rows = 0, ssq_K = 0;
+  // the split-K slices of the last defer_reduce GEMM, left for its reader to add, or null
+  const float* dpart = nullptr;
+  int dks = 0, drows = 0, dn = 0;
   // streaming text of the frame loop (tts_set_text_stream): ids [B, text_n], borrowed
   const int32_t* text_ids = nullptr;
   int text_n = 0, text_next = 0;
@@ -685,6 +688,9 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
     else
       hipLaunchKernelGGL(k_swiglu_rows, dim3(std::min((a.M * a.N + 255) / 256, 4096)), dim3(256), 0, ctx->stream, GU, a.M, a.N, a.y);
     HIP_LAUNCH_CHECK();
+  } else if (ks > 1 && a.defer_reduce && a.epi == EPI_STORE && !ssq_out) {
+    // the reader adds the slices itself (in the same order)
+    ctx->dpart = g.part; ctx->dks = ks; ctx->drows = a.M; ctx->dn = N;
   } else if (ks > 1 || ssq_out) {
     // slices added in order (with the residual first); a residual GEMM also leaves the new rows'
     // sums of squares for the RMSNorm of the GEMM that reads them next
@@ -794,11 +800,17 @@ int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_c
     a.src = SRC_VEC; a.x = x; a.x_stride = c.hidden;
     a.gain = W.attn_norm;
     a.y = ctx->qkv; a.y_stride = qkv_n; a.epi = EPI_STORE; a.nontemporal = nontemporal;
+    a.defer_reduce = 1;  // the attention adds a split GEMM's slices itself
+    ctx->dpart = nullptr;
     if (int rc_ = proj(ctx, a)) return rc_;
     // q/k norm + RoPE + KV append + attention
     AttnArgs t;
     std::memset(&t, 0, sizeof t);
     t.qkv = ctx->qkv; t.qkv_stride = qkv_n; t.M = Mp;
+    if (ctx->dpart) {
+      t.qkv_part = ctx->dpart; t.qkv_ks = ctx->dks; t.qkv_rows = ctx->drows; t.qkv_n = ctx->dn;
+      ctx->dpart = nullptr;
+    }
     t.nq = c.n_q_heads; t.nkv = c.n_kv_heads; t.d = c.head_dim;
     t.q_norm = W.q_norm; t.k_norm = W.k_norm; t.eps = ctx->cfg.rms_eps;
     t.rope_cos = rc; t.rope_sin = rs;

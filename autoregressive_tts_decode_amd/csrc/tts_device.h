@@ -185,6 +185,7 @@ struct GemvArgs {
   int32_t nontemporal;      // stream the weights past the caches (read once per frame)
   int32_t ssq_out;          // EPI_RESID GEMM: also leave the new rows' chunk sums of squares
   int32_t ssq_in;           // RMSNorm GEMM whose input rows are the last ssq_out rows, unchanged
+  int32_t defer_reduce;     // EPI_STORE split-K GEMM: leave the slices for the reader to add (no pass)
   int32_t bump_pos, bump_frame;  // added to the device counters by block 0 (it reads no counter)
   DevState* st;
 };
@@ -425,6 +426,10 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
 struct AttnArgs {
   const float* qkv;         // rows (stream-major, M per stream) of [q (nq*d) | k (nkv*d) | v (nkv*d)]
   int32_t qkv_stride;
+  // or, when qkv_part is set, those rows as qkv_ks split-K slices [slice][qkv_rows][qkv_n], added
+  // here in slice order
+  const float* qkv_part;
+  int32_t qkv_ks, qkv_rows, qkv_n;
   int32_t M;                // new positions per stream
   int32_t nq, nkv, d;
   const void* q_norm;       // [d] weight dtype
@@ -509,13 +514,22 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   for (int vi = wave; vi < M * (G + 2); vi += 4) {
     const int m = vi / (G + 2), j = vi % (G + 2);  // j < G: q head; G: k; G + 1: v
     const int p = p0 + m;
-    const float* rowp = a.qkv + (size_t)(row0 + m) * a.qkv_stride;
-    const float* src = (j < G) ? rowp + (size_t)(g * G + j) * D
-                     : (j == G) ? rowp + (size_t)a.nq * D + (size_t)g * D
-                                : rowp + (size_t)(a.nq + a.nkv) * D + (size_t)g * D;
+    const size_t col0 = (j < G) ? (size_t)(g * G + j) * D
+                      : (j == G) ? (size_t)a.nq * D + (size_t)g * D : (size_t)(a.nq + a.nkv) * D + (size_t)g * D;
     float v[PL];
+    if (a.qkv_part) {  // the projection's K slices, added in slice order (as the reduction pass would)
 #pragma unroll
-    for (int i = 0; i < PL; ++i) v[i] = src[lane + 64 * i];
+      for (int i = 0; i < PL; ++i) v[i] = 0.f;
+      for (int z = 0; z < a.qkv_ks; ++z) {
+        const float* sp = a.qkv_part + ((size_t)z * a.qkv_rows + row0 + m) * a.qkv_n + col0;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) v[i] += sp[lane + 64 * i];
+      }
+    } else {
+      const float* src = a.qkv + (size_t)(row0 + m) * a.qkv_stride + col0;
+#pragma unroll
+      for (int i = 0; i < PL; ++i) v[i] = src[lane + 64 * i];
+    }
     if (j <= G) {
       float ss = 0.f;
 #pragma unroll

@@ -200,50 +200,74 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
   int seg = 0, nrel = n0;
   while (seg + 1 < a.nseg && nrel >= a.seg_rows[seg]) { nrel -= a.seg_rows[seg]; ++seg; }
   const int kbeg = blockIdx.z * a.kslice, kn = min(a.kslice, a.K - kbeg), nks = kn / 32;
+  // Every load is issued before any is waited on, in the order of use: the row sums of squares
+  // (or row scales), the A slice and its gains, then the weight fragments. Addresses are clamped
+  // into range instead of predicated (a predicated load leaves a branch whose join waits for it);
+  // what a clamped load brings in past the slice or the rows is never used.
+  constexpr int Q4 = KSM / 4, AI = MR * Q4 / 256, CB = 24;  // A float4 per thread; chunk sums
+  static_assert(AI * 256 == MR * Q4 && 256 % Q4 == 0, "A slice share");
+  const int mr = min(tid & (MR - 1), a.M - 1);
+  const int nch = a.ssq ? a.nchunk : 1;
+  const float* sq = a.ssq ? a.ssq + (size_t)mr * nch : (a.rs ? a.rs + mr : a.A);
+  float qv[CB];
+#pragma unroll
+  for (int c = 0; c < CB; ++c) qv[c] = sq[min(c, nch - 1)];
+  const int ca = 4 * (tid % Q4), ma = tid / Q4, cl = min(ca, kn - 4);  // thread's columns (all its rows)
+  float4 xa[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i)
+    xa[i] = *reinterpret_cast<const float4*>(a.A + (size_t)min(ma + i * (256 / Q4), a.M - 1) * a.lda + kbeg + cl);
+  const uint16_t* gp = reinterpret_cast<const uint16_t*>(a.gain);
+  const uint16_t* gq = gp ? gp + kbeg + cl : reinterpret_cast<const uint16_t*>(a.A);
+  uint16_t graw[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) graw[k] = gq[k];
   const uint16_t* wrow = reinterpret_cast<const uint16_t*>(a.w[seg]) + (size_t)(nrel + 16 * wave + (lane & 15)) * a.K + kbeg +
                          8 * (lane >> 4);
   u32x4 b[RW][KSM / 32];
 #pragma unroll
   for (int t2 = 0; t2 < RW; ++t2)
 #pragma unroll
-    for (int s = 0; s < KSM / 32; ++s)
-      b[t2][s] = s < nks ? *reinterpret_cast<const u32x4*>(wrow + (size_t)64 * t2 * a.K + 32 * s) : (u32x4){0u, 0u, 0u, 0u};
+    for (int s = 0; s < KSM / 32; ++s) b[t2][s] = *reinterpret_cast<const u32x4*>(wrow + (size_t)64 * t2 * a.K + 32 * min(s, nks - 1));
   if (tid < MR) {
     float sc = 1.f;
     if (tid < a.M) {
-      if (a.ssq) {
+      if (a.ssq) {  // chunk sums added in chunk order
         float q = 0.f;
-        for (int c = 0; c < a.nchunk; ++c) q += a.ssq[(size_t)tid * a.nchunk + c];
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+          if (c < nch) q += qv[c];
+        for (int c = CB; c < nch; ++c) q += sq[c];
         sc = 1.0f / sqrtf(q / (float)a.K + a.eps);
       } else if (a.rs) {
-        sc = a.rs[tid];
+        sc = qv[0];
       }
     }
     srs[tid] = sc;
   }
   __syncthreads();
-  const uint16_t* gp = reinterpret_cast<const uint16_t*>(a.gain);
-  const int q4 = kn / 4;
-  for (int e = tid; e < MR * q4; e += 256) {
-    const int m = e / q4, c = 4 * (e % q4);
-    float x[4] = {0.f, 0.f, 0.f, 0.f};
-    if (m < a.M) {
-      const float4 v = *reinterpret_cast<const float4*>(a.A + (size_t)m * a.lda + kbeg + c);
-      const float sc = srs[m];
-      x[0] = v.x * sc; x[1] = v.y * sc; x[2] = v.z * sc; x[3] = v.w * sc;
-      if (gp) {
+  if (ca < kn) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] *= to_f32(gp[kbeg + c + i]);
+    for (int i = 0; i < AI; ++i) {
+      const int m = ma + i * (256 / Q4);
+      float x[4] = {0.f, 0.f, 0.f, 0.f};
+      if (m < a.M) {
+        const float sc = srs[m];
+        x[0] = xa[i].x * sc; x[1] = xa[i].y * sc; x[2] = xa[i].z * sc; x[3] = xa[i].w * sc;
+        if (gp) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) x[k] *= to_f32(graw[k]);
+        }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const __bf16 hi = (__bf16)x[i];
-      const float r1 = x[i] - (float)hi;
-      const __bf16 mid = (__bf16)r1;
-      As[0][m][c + i] = hi;
-      As[1][m][c + i] = mid;
-      As[2][m][c + i] = (__bf16)(r1 - (float)mid);
+      for (int k = 0; k < 4; ++k) {
+        const __bf16 hi = (__bf16)x[k];
+        const float r1 = x[k] - (float)hi;
+        const __bf16 mid = (__bf16)r1;
+        As[0][m][ca + k] = hi;
+        As[1][m][ca + k] = mid;
+        As[2][m][ca + k] = (__bf16)(r1 - (float)mid);
+      }
     }
   }
   __syncthreads();
@@ -340,8 +364,24 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(float* C, int ldc, const 
   const int m = blockIdx.y, n = blockIdx.x * 256 + threadIdx.x;
   float v = 0.f;
   if (n < N) {
-    v = add ? C[(size_t)m * ldc + n] : 0.f;
-    for (int z = 0; z < ks; ++z) v += part[((size_t)z * M + m) * N + n];
+    const float* pp = part + (size_t)m * N + n;
+    const size_t zs = (size_t)M * N;
+    if (ks > 0) {
+      // C and the slices loaded together (indices clamped, not predicated, so no load waits on
+      // another), then added in slice order
+      const float c0 = C[(size_t)m * ldc + n];
+      constexpr int ZB = 16;
+      float t[ZB];
+#pragma unroll
+      for (int z = 0; z < ZB; ++z) t[z] = pp[min(z, ks - 1) * zs];
+      v = add ? c0 : 0.f;
+#pragma unroll
+      for (int z = 0; z < ZB; ++z)
+        if (z < ks) v += t[z];
+      for (int z = ZB; z < ks; ++z) v += pp[z * zs];
+    } else {
+      v = add ? C[(size_t)m * ldc + n] : 0.f;
+    }
     C[(size_t)m * ldc + n] = v;
   }
   if (ssq) {
@@ -359,10 +399,21 @@ __global__ __launch_bounds__(256) void k_splitk_swiglu(const float* part, int M,
   for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < n; idx += (size_t)gridDim.x * blockDim.x) {
     const size_t m = idx / F, f = idx % F;
     float g = 0.f, u = 0.f;
-    for (int z = 0; z < ks; ++z) {
-      const float* row = part + ((size_t)z * M + m) * 2 * F;
-      g += row[f];
-      u += row[F + f];
+    const float* row = part + m * 2 * F + f;
+    const size_t zs = (size_t)M * 2 * F;
+    constexpr int ZB = 8;  // slices loaded together (indices clamped), then added in slice order
+    float tg[ZB], tu[ZB];
+#pragma unroll
+    for (int z = 0; z < ZB; ++z) {
+      tg[z] = row[min(z, ks - 1) * zs];
+      tu[z] = row[min(z, ks - 1) * zs + F];
+    }
+#pragma unroll
+    for (int z = 0; z < ZB; ++z)
+      if (z < ks) { g += tg[z]; u += tu[z]; }
+    for (int z = ZB; z < ks; ++z) {
+      g += row[z * zs];
+      u += row[z * zs + F];
     }
     h[m * ldh + f] = silu(g) * u;
   }

@@ -102,12 +102,14 @@ int dec_rw(int M, const int* seg_rows, int nseg) {
 
 // K split of the decode GEMM (k_gemm_dec) for N output rows, K columns, M input rows and rw row
 // tiles per workgroup: slices of at most 256 columns (128 past 32 rows: the LDS holds the slice's A
-// rows in three parts), more of them while the grid has fewer than 256 workgroups; returns the
+// rows in three parts), more of them only while the grid has fewer than 64 workgroups (each slice
+// adds a partial tile that the following pass reads back; with every load of a workgroup issued at
+// once, fewer and longer slices measured faster than filling all 256 compute units); returns the
 // slice count.
 int dec_split(int N, int K, int M, int rw, int* kslice) {
   const int kmax = M <= 32 ? 256 : 128, tiles = N / (64 * rw);
   const int ks_min = (K + kmax - 1) / kmax;
-  const int want = std::max(1, (256 + tiles - 1) / tiles);
+  const int want = std::max(1, (64 + tiles - 1) / tiles);
   int ks = std::max(ks_min, std::min(want, K / 64));
   const int ksl = ((K / 64 + ks - 1) / ks) * 64;
   *kslice = ksl;

@@ -2,10 +2,15 @@
 
     python -m autoregressive_tts_decode_amd.prof_summary <prefix> [--frames K]
     python -m autoregressive_tts_decode_amd.prof_summary <prefix> --pmc COUNTER [--kernel NAME]
+    python -m autoregressive_tts_decode_amd.prof_summary <prefix> --shapes --run-frames F [--exclude A,B]
 
 With --pmc, <prefix>_counter_collection.csv of a rocprofv3 --pmc run is read instead and the
 per-dispatch average of COUNTER is printed for every kernel (or the kernels whose name contains
 NAME).
+
+With --shapes, the kernel trace is grouped by kernel and launch shape (grid threads in x and
+the grid's z extent, which for the split-K GEMMs is the slice count): launches and kernel time
+per frame over the run's F frames, kernels named in --exclude (the prompt pass's) left out.
 
 <prefix> is the path prefix rocprofv3 wrote (…/bench): it reads
 <prefix>_kernel_stats.csv and <prefix>_kernel_trace.csv. The frame loop is
@@ -28,7 +33,27 @@ def main():
     ap.add_argument("--top", type=int, default=16)
     ap.add_argument("--pmc", default="")
     ap.add_argument("--kernel", default="")
+    ap.add_argument("--shapes", action="store_true")
+    ap.add_argument("--run-frames", type=int, default=0, help="frames in the whole run (--shapes)")
+    ap.add_argument("--exclude", default="", help="comma-separated kernel name parts to leave out (--shapes)")
     a = ap.parse_args()
+    if a.shapes:
+        if a.run_frames <= 0:
+            raise SystemExit("--shapes needs --run-frames")
+        skip = [x for x in a.exclude.split(",") if x]
+        busy, cnt = defaultdict(float), defaultdict(int)
+        for r in csv.DictReader(open(a.prefix + "_kernel_trace.csv")):
+            if any(x in r["Kernel_Name"] for x in skip):
+                continue
+            key = (r["Kernel_Name"].replace("tts::", "")[:44], int(r["Grid_Size_X"]), int(r["Grid_Size_Z"]))
+            busy[key] += int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            cnt[key] += 1
+        F = a.run_frames
+        print(f"per frame over {F} frames: {sum(cnt.values()) / F:.0f} launches, {sum(busy.values()) / F / 1e3:.1f} us of kernels")
+        print(f"{'kernel':44s} {'grid x':>8s} {'z':>3s} {'per frame':>9s} {'avg us':>7s} {'us/frame':>9s}")
+        for k in sorted(busy, key=lambda k: -busy[k]):
+            print(f"{k[0]:44s} {k[1]:8d} {k[2]:3d} {cnt[k] / F:9.1f} {busy[k] / cnt[k] / 1e3:7.2f} {busy[k] / F / 1e3:9.1f}")
+        return
     if a.pmc:
         vals = defaultdict(list)
         for r in csv.DictReader(open(a.prefix + "_counter_collection.csv")):

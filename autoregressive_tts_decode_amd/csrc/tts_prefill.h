@@ -209,9 +209,6 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
   const int mr = min(tid & (MR - 1), a.M - 1);
   const int nch = a.ssq ? a.nchunk : 1;
   const float* sq = a.ssq ? a.ssq + (size_t)mr * nch : (a.rs ? a.rs + mr : a.A);
-  float qv[CB];
-#pragma unroll
-  for (int c = 0; c < CB; ++c) qv[c] = sq[min(c, nch - 1)];
   const int ca = 4 * (tid % Q4), ma = tid / Q4, cl = min(ca, kn - 4);  // thread's columns (all its rows)
   float4 xa[AI];
 #pragma unroll
@@ -229,7 +226,12 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
   for (int t2 = 0; t2 < RW; ++t2)
 #pragma unroll
     for (int s = 0; s < KSM / 32; ++s) b[t2][s] = *reinterpret_cast<const u32x4*>(wrow + (size_t)64 * t2 * a.K + 32 * min(s, nks - 1));
-  if (tid < MR) {
+  static_assert(MR <= 64, "row scales from wave 0");
+  if (wave == 0) {  // the row scales: only wave 0's lanes load the chunk sums
+    float qv[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) qv[c] = sq[min(c, nch - 1)];
+   if (tid < MR) {
     float sc = 1.f;
     if (tid < a.M) {
       if (a.ssq) {  // chunk sums added in chunk order
@@ -244,6 +246,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
       }
     }
     srs[tid] = sc;
+   }
   }
   __syncthreads();
   if (ca < kn) {

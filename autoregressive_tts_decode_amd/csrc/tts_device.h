@@ -387,9 +387,20 @@ __global__ __launch_bounds__(256) void k_embed_sum(EmbedArgs a) {
   __syncthreads();
   const int ttok = toks[16];
   for (int k = blockIdx.x * 256 + threadIdx.x; k < a.H; k += gridDim.x * 256) {
-    float s = to_f32(reinterpret_cast<const WT*>(a.table[0])[(size_t)toks[0] * a.H + k]);
-    for (int t = 1; t < a.ntab; ++t) s += to_f32(reinterpret_cast<const WT*>(a.table[t])[(size_t)toks[t] * a.H + k]);
-    if (ttok >= 0) s += to_f32(reinterpret_cast<const WT*>(a.text_table)[(size_t)ttok * a.H + k]);
+    // every table's element loaded together (table index clamped to the last, a text row read
+    // from row 0 when there is none), then summed in table order
+    WT e[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int tt = min(t, a.ntab - 1);
+      e[t] = reinterpret_cast<const WT*>(a.table[tt])[(size_t)toks[tt] * a.H + k];
+    }
+    const WT et = a.text_table ? reinterpret_cast<const WT*>(a.text_table)[(size_t)max(ttok, 0) * a.H + k] : e[0];
+    float s = to_f32(e[0]);
+#pragma unroll
+    for (int t = 1; t < 16; ++t)
+      if (t < a.ntab) s += to_f32(e[t]);
+    if (ttok >= 0) s += to_f32(et);
     a.x[(size_t)b * a.x_stride + k] = s;
   }
 }
@@ -794,9 +805,17 @@ __global__ __launch_bounds__(256) void k_sample(SampleArgs a) {
   if (!a.do_sample) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int i = tid; i < a.V; i += 256) {
-      const float v = l[i];
-      if (bi == 0x7fffffff || v > bv) { bv = v; bi = i; }
+    // up to LB logits per thread loaded together (indices clamped), then compared in id order
+    constexpr int LB = 16;
+    for (int i0 = tid; i0 < a.V; i0 += 256 * LB) {
+      float lv[LB];
+#pragma unroll
+      for (int c = 0; c < LB; ++c) lv[c] = l[min(i0 + 256 * c, a.V - 1)];
+#pragma unroll
+      for (int c = 0; c < LB; ++c) {
+        const int i = i0 + 256 * c;
+        if (i < a.V && (bi == 0x7fffffff || lv[c] > bv)) { bv = lv[c]; bi = i; }
+      }
     }
     red_v[tid] = bv; red_i[tid] = bi;
     __syncthreads();

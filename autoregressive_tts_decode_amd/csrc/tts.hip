@@ -101,8 +101,8 @@ int dec_rw(int M, const int* seg_rows, int nseg) {
 }
 
 // K split of the decode GEMM (k_gemm_dec) for N output rows, K columns, M input rows and rw row
-// tiles per workgroup: slices of at most 256 columns (128 past 32 rows: the LDS holds the slice's A
-// rows in three parts), more of them only while the grid has fewer than 64 workgroups (each slice
+// tiles per workgroup: slices of at most 256 columns (128 past 32 rows, which measured faster for
+// 64-row prompt chunks), more of them only while the grid has fewer than 64 workgroups (each slice
 // adds a partial tile that the following pass reads back; with every load of a workgroup issued at
 // once, fewer and longer slices measured faster than filling all 256 compute units); returns the
 // slice count.

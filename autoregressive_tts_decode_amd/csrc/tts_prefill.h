@@ -3,10 +3,12 @@
 // pass before the frame loop). Positions are processed in chunks of at most kPrefillChunk per
 // stream, M = B x chunk rows per GEMM; causal attention of a chunk reads the KV cache, which holds
 // every earlier position. The same GEMM serves batched decode steps (many streams' rows).
-// Activations stay fp32: each GEMM splits its fp32 input a into three bf16 parts, hi = bf16(a),
-// mid = bf16(a - hi), lo = bf16(a - hi - mid), whose sum is a exactly for normal values (each
-// remainder is exact in fp32 and the last fits 8 mantissa bits), and accumulates W hi + W mid +
-// W lo in fp32 (W is bf16 already): the product is the fp32 one up to accumulation order.
+// Activations stay fp32: the tiled GEMM (k_gemm_bf16) splits its fp32 input a into three bf16
+// parts, hi = bf16(a), mid = bf16(a - hi), lo = bf16(a - hi - mid), whose sum is a exactly for
+// normal values (each remainder is exact in fp32 and the last fits 8 mantissa bits), and
+// accumulates W hi + W mid + W lo in fp32 (W is bf16 already): the product is the fp32 one up to
+// accumulation order. The decode GEMM (k_gemm_dec, at most 64 rows) keeps two parts, hi and
+// bf16(a - hi), about 17 significant bits of a, as the persistent Talker kernel does.
 #pragma once
 
 #include "tts_device.h"
@@ -185,15 +187,16 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(GemmArgs a) {
 // K slice of at most KSM columns: wave w loads the B fragments of rows 64 t + 16 w + l % 16
 // (t < RW) for the whole slice into registers at once (lane l: columns 32 s + 8 (l / 16) of K
 // step s), while the workgroup stages the slice of the A rows (times the row scale and the gain) in
-// LDS as three bf16 parts (hi, mid, lo; their sum is the fp32 value exactly, as in k_gemm_bf16);
-// each K step is then MT x RW x 3 MFMAs per wave, the smallest part first, every A fragment read
-// once for the RW tiles. With several slices each writes its partial tile to part (slice z at
+// LDS as two bf16 parts (hi = bf16(x), lo = bf16(x - hi): their sum holds x to about 17
+// significant bits, a relative error near 2^-17, as the persistent Talker kernel's activations;
+// the products with bf16 weights are exact in the fp32 accumulator); each K step is then
+// MT x RW x 2 MFMAs per wave, the smaller part first, every A fragment read once for the RW tiles. With several slices each writes its partial tile to part (slice z at
 // part + z M N) and a pass of its own adds them in slice order.
 template <int MT, int KSM, int RW>
 __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
   constexpr int MR = 16 * MT;
   constexpr int LD = KSM + 8;  // LDS row stride (bf16)
-  __shared__ __align__(16) __bf16 As[3][MR][LD];
+  __shared__ __align__(16) __bf16 As[2][MR][LD];
   __shared__ float srs[MR];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 64 * RW;
@@ -265,11 +268,8 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const __bf16 hi = (__bf16)x[k];
-        const float r1 = x[k] - (float)hi;
-        const __bf16 mid = (__bf16)r1;
         As[0][m][ca + k] = hi;
-        As[1][m][ca + k] = mid;
-        As[2][m][ca + k] = (__bf16)(r1 - (float)mid);
+        As[1][m][ca + k] = (__bf16)(x[k] - (float)hi);
       }
     }
   }
@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void k_gemm_dec(GemmArgs a) {
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int p = 2; p >= 0; --p) {
+        for (int p = 1; p >= 0; --p) {
           const bf16x8 av = *reinterpret_cast<const bf16x8*>(&As[p][16 * t + (lane & 15)][32 * s + 8 * (lane >> 4)]);
 #pragma unroll
           for (int t2 = 0; t2 < RW; ++t2)

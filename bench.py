@@ -282,7 +282,7 @@ def time_workload(name: str, K: int, W: int, reps: int, smi: Smi, args, weights=
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build decodes on one GPU: a batch-1 frame does not shard usefully and "
+        print(json.dumps({"error": "the library decodes on one GPU: a batch-1 frame does not shard usefully and "
                                    "independent streams are data parallel with no exchange; run with --gpus 1"}))
         sys.exit(2)
 

@@ -50,7 +50,7 @@ enum tts_status {
   TTS_E_CAPACITY = -3,   /* KV positions or frames would exceed the configured capacity */
   TTS_E_STATE = -4,      /* call out of order (e.g. a step before weights or prefill) */
   TTS_E_HIP = -5,        /* a HIP runtime call failed; tts_last_error has its text */
-  TTS_E_UNSUPPORTED = -6, /* valid request outside what this build implements */
+  TTS_E_UNSUPPORTED = -6, /* valid request outside what the library implements */
   TTS_E_DEVICE = -7      /* a persistent kernel launched by an earlier call timed out in an exchange:
                             outputs since the last clean call are invalid; nothing was enqueued;
                             reported by every call that may launch them until tts_reset */

@@ -592,7 +592,7 @@ int gemv(tts_ctx* ctx, GemvArgs a) {
 // and the gain applied while A is loaded; the residual as C += result; SwiGLU through a staging
 // buffer; gathered input rows staged first). Needs bf16 weights and 64-multiple row segments.
 int gather(tts_ctx* ctx, int src, int M, int H, const float* vec, int vec_stride, const void* table, int table_rows, TokRef tok,
-           float* out, int out_stride, bool f32_table = false);
+           float* out, int out_stride, bool f32_table = false, bool want_ssq = false);
 
 bool gemm_routes(const tts_ctx* ctx, const GemvArgs& a) {
   if (!ctx->pgemm_ok || !(ctx->bf16() || ctx->fp8()) || a.M < kGemmMinRows || a.K % kGBK) return false;
@@ -783,19 +783,21 @@ GemvArgs gemv_args(tts_ctx* ctx) {
 // kvstart: per-stream first visible cache position (ragged Talker prompts), or nullptr.
 int stack_step(tts_ctx* ctx, const StackW& S, float* x, int B, int Mp, int pos_const, int pos_from_state, void* kc,
                void* vc, int cap, int nsplit, const float* rc, const float* rs, bool nontemporal,
-               const int32_t* kvstart = nullptr) {
+               const int32_t* kvstart = nullptr, bool in_ssq = false) {
   const tts_stack_cfg& c = S.c;
   const int rows = B * Mp;
   const int qd = c.n_q_heads * c.head_dim, kd = c.n_kv_heads * c.head_dim;
   const int qkv_n = qd + 2 * kd;
   // per-layer cache stride uses the allocated stream capacity, not the live batch
   const size_t layer_cache = (size_t)ctx->cfg.max_batch * c.n_kv_heads * cap * c.head_dim * ctx->kvb();
-  ctx->ssq_x = nullptr;  // x was written outside this stack
+  // x was written outside this stack; in_ssq: by a gather that left its rows' sums of squares
+  // (proj_gemm still checks that they describe these rows)
+  if (!in_ssq) ctx->ssq_x = nullptr;
   for (int l = 0; l < c.n_layers; ++l) {
     const Layer& W = S.layers[l];
     // RMSNorm + QKV (after layer 0 the previous down projection left x's sums of squares)
     GemvArgs a = gemv_args(ctx);
-    a.ssq_in = l > 0;
+    a.ssq_in = l > 0 || in_ssq;
     a.w[0] = W.wq; a.w[1] = W.wk; a.w[2] = W.wv;
     a.seg_rows[0] = qd; a.seg_rows[1] = kd; a.seg_rows[2] = kd;
     a.nseg = 3; a.N = qkv_n; a.K = c.hidden; a.M = rows;
@@ -1000,16 +1002,22 @@ int embed_sum(tts_ctx* ctx, int B, const TokRef* refs, const TokRef* text = null
 }
 
 int gather(tts_ctx* ctx, int src, int M, int H, const float* vec, int vec_stride, const void* table, int table_rows, TokRef tok,
-           float* out, int out_stride, bool f32_table) {
+           float* out, int out_stride, bool f32_table, bool want_ssq) {
   GatherArgs g;
   std::memset(&g, 0, sizeof g);
   g.src = src; g.M = M; g.H = H; g.vec = vec; g.vec_stride = vec_stride; g.table = table; g.table_rows = table_rows; g.tok = tok;
   g.x = out; g.x_stride = out_stride; g.st = ctx->st;
   if (out == ctx->ssq_x) ctx->ssq_x = nullptr;
   const int gx = (H + 255) / 256;
+  // the rows' chunk sums of squares (into the buffer sized for max_batch x kPrefillChunk rows of
+  // the widest hidden size), for the RMSNorm of the GEMM that reads them next
+  if (want_ssq && H % 256 == 0 && (size_t)M <= (size_t)ctx->cfg.max_batch * kPrefillChunk) g.ssq = (float*)(ctx->ws + ctx->L.ssq);
   if (ctx->tab16() && !f32_table) hipLaunchKernelGGL(k_gather<uint16_t>, dim3(gx, M), dim3(256), 0, ctx->stream, g);
   else hipLaunchKernelGGL(k_gather<float>, dim3(gx, M), dim3(256), 0, ctx->stream, g);
   HIP_LAUNCH_CHECK();
+  if (g.ssq) {
+    ctx->ssq_x = out; ctx->ssq_stride = out_stride; ctx->ssq_rows = M; ctx->ssq_K = H;
+  }
   return TTS_OK;
 }
 
@@ -1093,6 +1101,7 @@ int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac,
   void* vc = ctx->ws + ctx->L.cv;
   for (int j = 1; j <= c.n_acoustic; ++j) {
     const int Mp = (j == 1) ? 2 : 1;
+    bool gathered = false;  // the input rows came from a gather that left their sums of squares
     // CodePredictor input rows
     if (j == 1) {
       if (ctx->proj) {
@@ -1102,9 +1111,11 @@ int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac,
         a.tok = semantic;
         a.y = ctx->cx; a.y_stride = Hc; a.epi = EPI_STORE;
         if (int rc = proj(ctx, a)) return rc;
-      } else if (int rc = gather(ctx, SRC_VEC_THEN_TABLE, 2 * B, Hc, ctx->hT, Ht, ctx->embed_sem, c.talker.vocab, semantic, ctx->cx,
-                                 Hc)) {
-        return rc;
+      } else {
+        if (int rc = gather(ctx, SRC_VEC_THEN_TABLE, 2 * B, Hc, ctx->hT, Ht, ctx->embed_sem, c.talker.vocab, semantic, ctx->cx, Hc,
+                            false, true))
+          return rc;
+        gathered = true;
       }
     } else {
       const void* table = (const char*)ctx->embed_ac + (size_t)(j - 2) * ac_table;
@@ -1112,20 +1123,23 @@ int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac,
       if (ctx->ptab) {
         // the projected row P E_ac[j - 2][a] from the table (a linear map of a row is that row of
         // the mapped table)
-        if (int rc = gather(ctx, SRC_TABLE, B, Hc, nullptr, 0, ctx->ptab + (size_t)(j - 2) * Va * Hc, Va, prev, ctx->cx, Hc, true))
+        if (int rc = gather(ctx, SRC_TABLE, B, Hc, nullptr, 0, ctx->ptab + (size_t)(j - 2) * Va * Hc, Va, prev, ctx->cx, Hc, true,
+                            true))
           return rc;
+        gathered = true;
       } else if (ctx->proj) {
         GemvArgs a = gemv_args(ctx);
         a.w[0] = ctx->proj; a.seg_rows[0] = Hc; a.N = Hc; a.K = Ht; a.M = B;
         a.src = SRC_TABLE; a.table = table; a.table_rows = Va; a.tok = prev;
         a.y = ctx->cx; a.y_stride = Hc; a.epi = EPI_STORE;
         if (int rc = proj(ctx, a)) return rc;
-      } else if (int rc = gather(ctx, SRC_TABLE, B, Hc, nullptr, 0, table, Va, prev, ctx->cx, Hc)) {
-        return rc;
+      } else {
+        if (int rc = gather(ctx, SRC_TABLE, B, Hc, nullptr, 0, table, Va, prev, ctx->cx, Hc, false, true)) return rc;
+        gathered = true;
       }
     }
     if (int rc = stack_step(ctx, ctx->cp, ctx->cx, B, Mp, j == 1 ? 0 : j, 0, kc, vc, kCpPositions, 1, ctx->ccos, ctx->csin,
-                            false))
+                            false, nullptr, gathered))
       return rc;
     // final norm + head j on the last position of each stream
     GemvArgs a = gemv_args(ctx);

@@ -417,6 +417,9 @@ struct GatherArgs {
   float* x;
   int32_t x_stride;
   const DevState* st;
+  // optional: the sums of squares of each row's 256-column chunks, ssq[m * gridDim.x + chunk] (the
+  // grid then covers H with one column per thread), for the RMSNorm of the GEMM that reads x
+  float* ssq;
 };
 
 template <typename WT>
@@ -425,10 +428,19 @@ __global__ __launch_bounds__(256) void k_gather(GatherArgs a) {
   const int stream = (a.src == SRC_VEC_THEN_TABLE) ? (m >> 1) : m;
   const bool from_table = (a.src == SRC_TABLE) || (a.src == SRC_VEC_THEN_TABLE && (m & 1));
   const int t = from_table ? clamp_tok(tok_at(a.tok, a.st, stream), a.table_rows) : 0;
+  float q = 0.f;
   for (int k = blockIdx.x * 256 + threadIdx.x; k < a.H; k += gridDim.x * 256) {
     float v = from_table ? to_f32(reinterpret_cast<const WT*>(a.table)[(size_t)t * a.H + k])
                          : a.vec[(size_t)stream * a.vec_stride + k];
     a.x[(size_t)m * a.x_stride + k] = v;
+    q += v * v;
+  }
+  if (a.ssq) {  // the same fixed order as the split-K reduction's sums of squares
+    __shared__ float wsum[4];
+    const float s = wave_sum(q);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) a.ssq[(size_t)m * gridDim.x + blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
   }
 }
 

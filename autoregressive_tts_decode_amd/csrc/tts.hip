@@ -681,7 +681,9 @@ int proj_gemm(tts_ctx* ctx, const GemvArgs& a) {
     return rc;
   }
   HIP_LAUNCH_CHECK();
-  const bool ssq_out = a.ssq_out && a.epi == EPI_RESID;
+  // ssq_out: a residual GEMM, or a plain store (the CodePredictor's input projection), also leaves
+  // the written rows' 256-column chunk sums of squares
+  const bool ssq_out = a.ssq_out && (a.epi == EPI_RESID || a.epi == EPI_STORE) && N % 256 == 0;
   if (a.epi == EPI_SWIGLU) {
     // the slices' gate and up sums meet in the SwiGLU pass (no separate reduction)
     if (ks > 1)
@@ -1110,7 +1112,9 @@ int codepred_frame(tts_ctx* ctx, int B, TokRef semantic, const tts_sampling& ac,
         a.src = SRC_VEC_THEN_TABLE; a.x = ctx->hT; a.x_stride = Ht; a.table = ctx->embed_sem; a.table_rows = c.talker.vocab;
         a.tok = semantic;
         a.y = ctx->cx; a.y_stride = Hc; a.epi = EPI_STORE;
+        a.ssq_out = 1;  // the rows' sums of squares for the first RMSNorm (on the GEMM route)
         if (int rc = proj(ctx, a)) return rc;
+        gathered = true;
       } else {
         if (int rc = gather(ctx, SRC_VEC_THEN_TABLE, 2 * B, Hc, ctx->hT, Ht, ctx->embed_sem, c.talker.vocab, semantic, ctx->cx, Hc,
                             false, true))
